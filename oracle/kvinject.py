@@ -1,0 +1,102 @@
+"""KV-injection (DFlash / DSpark) block drafter, float64 oracle (test infrastructure only).
+
+Follows page "mlx-bun 0.4.0 -> 1.0.0", src/spec/dspark/module-dflash.ts: the file header (DSpark Eq 2 and Eq 3),
+#buildContext, #buildBlock, #layer, #backbone, projectContextRows and #baseLogits.
+
+  Eq 2   H_ctx = RMSNorm(W_c [H^l1; ...; H^lm])
+  Eq 3   K_i = [W_i^K n(H_ctx); W_i^K n(H_d)], V_i likewise, Q_i = W_i^Q n(H_d), n = the layer's attn_norm applied to
+         context and block alike; the block attends bidirectionally over [context ++ block].
+
+Readings: no RoPE, no q/k norm, no mask (batch of one); the head output is not cast before the lm_head; the Markov
+correction is zero at its initialisation (W2 = 0) and is omitted; the lm_head table E is also the embedding table.
+The activation the page calls geluApprox is read as the tanh form (parity unpinned beyond that formula).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import prims as P
+from .flowmap import ContextFull
+
+
+class KVInjectOracle:
+    def __init__(self, cfg: dict, weights: dict):
+        self.cfg = cfg
+        self.raw = weights
+        self._w: dict[str, np.ndarray] = {}
+        d, L = cfg["dim"], cfg["layers"]
+        self.K = [np.zeros((cfg["max_ctx"], d)) for _ in range(L)]
+        self.V = [np.zeros((cfg["max_ctx"], d)) for _ in range(L)]
+        self.length = 0
+
+    def w(self, name: str) -> np.ndarray:
+        if name not in self._w:
+            self._w[name] = P.weight_f64(self.raw[name])
+        return self._w[name]
+
+    def build_context(self, taps: np.ndarray) -> np.ndarray:
+        """Eq 2: H_ctx = RMSNorm(W_c taps; ctx_norm)."""
+        return P.rmsnorm(P.linear(taps, self.w("W_c")), self.w("ctx_norm"), self.cfg["rms_eps"])
+
+    def context_append(self, taps: np.ndarray, start: int):
+        """Retained context projection (projectContextRows): per layer K = W_k RMSNorm(H_ctx; attn_norm), V likewise,
+        written at rows start .. start + n - 1."""
+        cfg = self.cfg
+        n = taps.shape[0]
+        if start < 0 or start > self.length:
+            raise ValueError("start beyond the current context length")
+        if start + n + cfg["block"] > cfg["max_ctx"]:
+            raise ContextFull("context full")
+        hc = self.build_context(taps)
+        for i in range(cfg["layers"]):
+            nc = P.rmsnorm(hc, self.w(f"bb.{i}.attn_norm"), cfg["rms_eps"])
+            self.K[i][start:start + n] = P.linear(nc, self.w(f"bb.{i}.k"))
+            self.V[i][start:start + n] = P.linear(nc, self.w(f"bb.{i}.v"))
+        self.length = start + n
+        return hc
+
+    def build_block(self, anchor: int) -> np.ndarray:
+        """H_d[0] = tok_proj(E[anchor]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]."""
+        e = self.w("lm_head.weight")[anchor][None, :]
+        bp = self.w("block_pos")
+        first = P.linear(e, self.w("tok_proj")) + bp[0]
+        return np.concatenate([first, self.w("mask_emb") + bp[1:]], axis=0)
+
+    def _layer(self, i: int, hd_x: np.ndarray, kc: np.ndarray, vc: np.ndarray) -> np.ndarray:
+        cfg = self.cfg
+        H, hdim = cfg["heads"], cfg["head_dim"]
+        n = P.rmsnorm(hd_x, self.w(f"bb.{i}.attn_norm"), cfg["rms_eps"])
+        q = P.linear(n, self.w(f"bb.{i}.q"))
+        keys = np.concatenate([kc, P.linear(n, self.w(f"bb.{i}.k"))], axis=0)
+        vals = np.concatenate([vc, P.linear(n, self.w(f"bb.{i}.v"))], axis=0)
+        a = P.attention(q, keys, vals, H, hdim ** -0.5)
+        x = hd_x + P.linear(a, self.w(f"bb.{i}.o"))
+        n2 = P.rmsnorm(x, self.w(f"bb.{i}.ff_norm"), cfg["rms_eps"])
+        m = P.gelu_tanh(P.linear(n2, self.w(f"bb.{i}.gate"))) * P.linear(n2, self.w(f"bb.{i}.up"))
+        return x + P.linear(m, self.w(f"bb.{i}.down"))
+
+    def draft_block(self, anchor: int):
+        """Block output out_proj(RMSNorm(H_d; out_norm)) [gamma, Ht] over the retained context rows [0, length)."""
+        cfg = self.cfg
+        x = self.build_block(anchor)
+        xs = []
+        for i in range(cfg["layers"]):
+            x = self._layer(i, x, self.K[i][:self.length], self.V[i][:self.length])
+            xs.append(x.copy())
+        out = P.linear(P.rmsnorm(x, self.w("out_norm"), cfg["rms_eps"]), self.w("out_proj"))
+        return out, xs
+
+    def draft_block_reproject(self, taps_all: np.ndarray, anchor: int) -> np.ndarray:
+        """The same block with the context re-projected inside every layer from all tap rows (the page's route
+        without a retained context); equal to draft_block when the cache holds exactly those rows."""
+        cfg = self.cfg
+        hc = self.build_context(taps_all)
+        x = self.build_block(anchor)
+        for i in range(cfg["layers"]):
+            nc = P.rmsnorm(hc, self.w(f"bb.{i}.attn_norm"), cfg["rms_eps"])
+            x = self._layer(i, x, P.linear(nc, self.w(f"bb.{i}.k")), P.linear(nc, self.w(f"bb.{i}.v")))
+        return P.linear(P.rmsnorm(x, self.w("out_norm"), cfg["rms_eps"]), self.w("out_proj"))
+
+    def lm_argmax(self, hidden: np.ndarray):
+        z = P.linear(hidden, self.w("lm_head.weight"))
+        return P.argmax_rows(z), z

@@ -1,0 +1,301 @@
+"""Pins of the three drafter oracles: a loop-only second implementation at micro shapes, structural invariants
+the pages fix, special cases with closed forms, and the pages' own shape constants."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from inputs import configs, gen
+from oracle import flowmap, kvinject, loops, mtp
+from oracle import prims as P
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")))
+
+FM_MICRO = dict(variant="flowmap", dim=16, heads=2, head_dim=8, kv_heads=2, layers=2, ffn=32, block=4, target_dim=12,
+                n_taps=2, vocab=20, max_ctx=16, rope="interleaved", rope_dims=8, rope_theta=1e4, ln_eps=1e-6,
+                rms_eps=1e-6, qk_eps=1e-5, mlp="gelu_erf", kv_dtype="f16", wtype="bf16", ctx_rows=5, name="fm_micro")
+KV_MICRO = dict(variant="kvinject", dim=16, heads=2, head_dim=8, kv_heads=2, layers=2, ffn=24, block=3, target_dim=12,
+                n_taps=2, vocab=20, max_ctx=16, rope="none", rope_dims=0, rope_theta=0.0, ln_eps=1e-6, rms_eps=1e-6,
+                qk_eps=1e-6, mlp="geglu_tanh", kv_dtype="f32", wtype="bf16", ctx_rows=6, name="kv_micro")
+MTP_MICRO = dict(variant="mtp", dim=32, heads=4, head_dim=8, kv_heads=2, layers=1, ffn=64, block=4, target_dim=32,
+                 n_taps=2, vocab=20, max_ctx=16, rope="neox", rope_dims=4, rope_theta=1e7, ln_eps=1e-6, rms_eps=1e-6,
+                 qk_eps=1e-6, mlp="swiglu", kv_dtype="f32", wtype="q8_0", ctx_rows=16, name="mtp_micro")
+
+
+def _decoded(cfg, W):
+    return {k: P.weight_f64(v) for k, v in W.items()}
+
+
+def _bump_gates(W, cfg, value=None):
+    """A copy of the weights whose modulation gates are all `value` (None: keep)."""
+    W = dict(W)
+    m = W["mod"].copy().reshape(-1, 3, cfg["dim"])
+    if value is not None:
+        m[:, 2, :] = value
+    W["mod"] = m.reshape(-1)
+    return W
+
+
+# ── flow-map ────────────────────────────────────────────────────────────────────────────────────
+
+def _fm(cfg=FM_MICRO, seed=0):
+    W = gen.make_weights(cfg, seed)
+    o = flowmap.FlowMapOracle(cfg, W)
+    return o, W
+
+
+def test_flowmap_matches_loop_implementation():
+    cfg = FM_MICRO
+    o, W = _fm()
+    taps = gen.taps(cfg, "micro", cfg["ctx_rows"])
+    o.context_append(taps, 0)
+    out, _ = o.draft_block(anchor=7, pos=cfg["ctx_rows"])
+    tok, z = o.lm_argmax(out)
+    ref_out, ref_z = loops.flowmap_forward(cfg, _decoded(cfg, W), taps, 7, cfg["ctx_rows"])
+    assert np.allclose(out, ref_out, rtol=1e-11, atol=1e-12)
+    assert np.allclose(z, ref_z, rtol=1e-11, atol=1e-12)
+    assert list(tok) == [int(np.argmax(r)) for r in ref_z]
+
+
+def test_flowmap_draft_at_earlier_pos_matches_loops():
+    # pos < length: keys are rows [0, pos]; the anchor overwrites row pos
+    cfg = FM_MICRO
+    o, W = _fm()
+    taps = gen.taps(cfg, "micro", cfg["ctx_rows"])
+    o.context_append(taps, 0)
+    out, _ = o.draft_block(anchor=3, pos=2)
+    ref_out, _ = loops.flowmap_forward(cfg, _decoded(cfg, W), taps, 3, 2)
+    assert np.allclose(out, ref_out, rtol=1e-11, atol=1e-12)
+
+
+def test_flowmap_slots_identical_without_rope():
+    # Zero noise: every slot starts from the same row; with no positional signal the T slots stay identical.
+    cfg = FM_MICRO
+    o, _ = _fm()
+    o.context_append(gen.taps(cfg, "micro", 5), 0)
+    out, xs = o.draft_block(anchor=1, pos=5, rope=False)
+    assert np.allclose(out, np.tile(out[:1], (cfg["block"], 1)), atol=1e-13)
+    # with RoPE they diverge only through positions: the same position for every slot makes them identical again
+    out2, _ = o.draft_block(anchor=1, pos=5, slot_pos=np.full(cfg["block"], 9))
+    assert np.allclose(out2, np.tile(out2[:1], (cfg["block"], 1)), atol=1e-13)
+    out3, _ = o.draft_block(anchor=1, pos=5)
+    assert np.max(np.abs(out3 - out3[:1])) > 1e-6
+
+
+def test_flowmap_slot_permutation_equivariance():
+    # Self-attention is unmasked: permuting the slot positions permutes the outputs.
+    cfg = FM_MICRO
+    o, _ = _fm()
+    o.context_append(gen.taps(cfg, "micro", 5), 0)
+    sp = np.array([6, 7, 8, 9])
+    perm = np.array([2, 0, 3, 1])
+    a, _ = o.draft_block(anchor=4, pos=5, slot_pos=sp)
+    b, _ = o.draft_block(anchor=4, pos=5, slot_pos=sp[perm])
+    assert np.allclose(b, a[perm], atol=1e-12)
+
+
+def test_flowmap_zero_gates_reduce_to_head_of_h0():
+    # All gates 0: every branch is switched off, the residual stream stays h0, and the output is the head applied to
+    # the final modulation of h0 -- independent of context and anchor.
+    cfg = FM_MICRO
+    W = _bump_gates(gen.make_weights(cfg), cfg, 0.0)
+    o = flowmap.FlowMapOracle(cfg, W)
+    o.context_append(gen.taps(cfg, "micro", 5), 0)
+    out, _ = o.draft_block(anchor=2, pos=5)
+    D = cfg["dim"]
+    Wd = _decoded(cfg, W)
+    E = Wd["lm_head.weight"]
+    h0 = P.rmsnorm(E.mean(axis=0)[None], Wd["state_norm.weight"], 1e-6) @ Wd["x_embed.weight"].T + Wd["x_embed.bias"]
+    m = Wd["mod"].reshape(-1, 3, D)[-1]
+    ref = P.ln_mod(h0, m[0], m[1], 1e-6) @ Wd["head.weight"].T + Wd["head.bias"]
+    assert np.allclose(out, np.tile(ref, (cfg["block"], 1)), atol=1e-12)
+
+
+def test_flowmap_cross_attention_sees_only_rows_up_to_pos():
+    cfg = FM_MICRO
+    o, W = _fm()
+    o.context_append(gen.taps(cfg, "micro", 8), 0)
+    a, _ = o.draft_block(anchor=5, pos=4)
+    o.K[0][5:8] += 100.0
+    o.V[1][6] -= 50.0
+    b, _ = o.draft_block(anchor=5, pos=4)
+    assert np.array_equal(a, b)
+
+
+def test_flowmap_append_chunking_and_overwrite():
+    cfg = FM_MICRO
+    taps = gen.taps(cfg, "chunk", 9)
+    o1, W = _fm()
+    o1.context_append(taps, 0)
+    o2 = flowmap.FlowMapOracle(cfg, W)
+    o2.context_append(taps[:4], 0)
+    o2.context_append(taps[4:5], 4)
+    o2.context_append(taps[5:], 5)
+    for l in range(cfg["layers"]):
+        assert np.allclose(o1.K[l][:9], o2.K[l][:9], atol=1e-14)
+        assert np.allclose(o1.V[l][:9], o2.V[l][:9], atol=1e-14)
+    # rewrite from an earlier start (a rewind), then the tail again: the cache equals a fresh append
+    o2.context_append(gen.taps(cfg, "other", 3), 2)
+    o2.context_append(taps[2:], 2)
+    assert o2.length == 9
+    for l in range(cfg["layers"]):
+        assert np.allclose(o1.K[l][:9], o2.K[l][:9], atol=1e-14)
+
+
+def test_flowmap_context_full_and_bad_positions():
+    cfg = FM_MICRO
+    o, _ = _fm()
+    with pytest.raises(flowmap.ContextFull):
+        o.context_append(gen.taps(cfg, "x", 12), 0)          # 12 + 4 + 1 > 16
+    o.context_append(gen.taps(cfg, "x", 3), 0)
+    with pytest.raises(ValueError):
+        o.context_append(gen.taps(cfg, "x", 1), 5)           # start beyond length
+    with pytest.raises(ValueError):
+        o.draft_block(anchor=0, pos=4)                         # pos beyond length
+
+
+def test_flowmap_param_count_matches_page():
+    # The page's drafter has 475M parameters (bf16 file of 949,897,866 bytes).  Our flow-map shape replaces the
+    # time-conditioning MLPs by a constant table; adding back the per-norm adaLN linears (cond 256 -> 3*dim, 19 norms)
+    # and the time / jump embedders (256 -> 256 -> 256, two each) must land within 0.5% of the page's count.
+    c = configs.get("flashmap")
+    fc = GOLD["flashmap_cfg"]
+    assert (c["dim"], c["heads"], c["head_dim"], c["layers"], c["ffn"], c["block"], c["target_dim"], c["n_taps"]) == (
+        fc["dim"], fc["heads"], fc["hd"], fc["layers"], fc["ff"], fc["block"], fc["targetDim"], len(fc["taps"]))
+    n = sum(int(np.prod(s)) for name, s, k in gen.flowmap_weight_specs(c) if name not in ("mod", "lm_head.weight"))
+    cond = fc["cond"]
+    n += (3 * c["layers"] + 1) * (cond * 3 * c["dim"] + 3 * c["dim"])
+    n += 2 * 2 * (cond * cond + cond)
+    assert abs(n - GOLD["flashmap_size"]["params"]) / GOLD["flashmap_size"]["params"] < 0.005
+    assert abs(2 * n - GOLD["flashmap_size"]["file_bytes"]) / GOLD["flashmap_size"]["file_bytes"] < 0.005
+
+
+# ── KV-injection ────────────────────────────────────────────────────────────────────────────────
+
+def test_kvinject_matches_loop_implementation():
+    cfg = KV_MICRO
+    W = gen.make_weights(cfg)
+    o = kvinject.KVInjectOracle(cfg, W)
+    taps = gen.taps(cfg, "micro", cfg["ctx_rows"])
+    o.context_append(taps, 0)
+    out, _ = o.draft_block(anchor=11)
+    tok, z = o.lm_argmax(out)
+    ref_out, ref_z = loops.kvinject_forward(cfg, _decoded(cfg, W), taps, 11)
+    assert np.allclose(out, ref_out, rtol=1e-11, atol=1e-12)
+    assert np.allclose(z, ref_z, rtol=1e-11, atol=1e-12)
+
+
+def test_kvinject_cached_route_equals_reprojection():
+    # The page: the context projection is independent of the block and can be retained.
+    cfg = KV_MICRO
+    W = gen.make_weights(cfg)
+    o = kvinject.KVInjectOracle(cfg, W)
+    taps = gen.taps(cfg, "micro", 6)
+    o.context_append(taps[:2], 0)
+    o.context_append(taps[2:], 2)
+    a, _ = o.draft_block(anchor=4)
+    b = o.draft_block_reproject(taps, anchor=4)
+    assert np.allclose(a, b, atol=1e-13)
+
+
+def test_kvinject_mask_slot_permutation_equivariance():
+    # No positions and no mask: permuting the mask-token slots (1..gamma-1, their block_pos rows with them) permutes
+    # those outputs and leaves slot 0 unchanged.
+    cfg = KV_MICRO
+    W = gen.make_weights(cfg)
+    o = kvinject.KVInjectOracle(cfg, W)
+    o.context_append(gen.taps(cfg, "micro", 6), 0)
+    a, _ = o.draft_block(anchor=4)
+    W2 = dict(W)
+    W2["mask_emb"] = W["mask_emb"][::-1].copy()
+    bp = W["block_pos"].copy()
+    bp[1:] = bp[1:][::-1]
+    W2["block_pos"] = bp
+    o2 = kvinject.KVInjectOracle(cfg, W2)
+    o2.context_append(gen.taps(cfg, "micro", 6), 0)
+    b, _ = o2.draft_block(anchor=4)
+    assert np.allclose(b[0], a[0], atol=1e-13)
+    assert np.allclose(b[1:], a[1:][::-1], atol=1e-13)
+
+
+def test_dflash_defaults_match_page():
+    c = configs.get("kvinject")
+    d = GOLD["dflash_defaults"]
+    assert (c["block"], c["dim"], c["layers"], c["heads"], c["ffn"] // c["dim"], c["n_taps"]) == (
+        d["gamma"], d["dDraft"], d["nLayers"], d["nHeads"], d["ffMult"], len(d["tapLayers"]))
+
+
+# ── MTP ─────────────────────────────────────────────────────────────────────────────────────────
+
+def _mtp(seed=0):
+    cfg = MTP_MICRO
+    W = gen.make_weights(cfg, seed)
+    o = mtp.MTPOracle(cfg, W)
+    return cfg, W, o
+
+
+def test_mtp_matches_loop_implementation():
+    cfg, W, o = _mtp()
+    pos0, M, kv_lo = 9, 3, 2
+    kc, vc = gen.mtp_cache_rows(cfg, pos0)
+    o.set_cache_rows(kc, vc)
+    e, h = gen.mtp_inputs(cfg, M)
+    out = o.forward(e, h, pos0, kv_lo)
+    tok, z = o.lm_argmax(out)
+    ref_out, ref_z = loops.mtp_forward(cfg, _decoded(cfg, W), e, h, kc, vc, pos0, kv_lo)
+    assert np.allclose(out, ref_out, rtol=1e-11, atol=1e-12)
+    assert np.allclose(z, ref_z, rtol=1e-11, atol=1e-12)
+
+
+def test_mtp_rows_at_once_equal_rows_one_by_one():
+    # Causal attention over the head's own cache: M rows in one pass equal M single-row passes at consecutive
+    # positions (each pass writes its row's K/V before the next reads it).
+    cfg, W, o = _mtp()
+    pos0, M = 6, 4
+    kc, vc = gen.mtp_cache_rows(cfg, pos0)
+    o.set_cache_rows(kc, vc)
+    e, h = gen.mtp_inputs(cfg, M)
+    all_rows = o.forward(e, h, pos0, 0)
+    o2 = mtp.MTPOracle(cfg, W)
+    o2.set_cache_rows(kc, vc)
+    one = np.concatenate([o2.forward(e[m:m + 1], h[m:m + 1], pos0 + m, 0) for m in range(M)])
+    assert np.allclose(all_rows, one, atol=1e-13)
+
+
+def test_mtp_kv_lo_hides_earlier_rows():
+    cfg, W, o = _mtp()
+    kc, vc = gen.mtp_cache_rows(cfg, 8)
+    o.set_cache_rows(kc, vc)
+    e, h = gen.mtp_inputs(cfg, 2)
+    a = o.forward(e, h, 8, 3)
+    kc2 = kc.copy(); kc2[:3] += 10.0
+    o.set_cache_rows(kc2, vc)
+    b = o.forward(e, h, 8, 3)
+    assert np.array_equal(a, b)
+    c = o.forward(e, h, 8, 0)
+    assert np.max(np.abs(c - a)) > 1e-6
+
+
+def test_mtp_shapes_match_page_tensor_map():
+    # The page's tensor map gives [offset, type, ne0 = K, ne1 = N]; a Q8_0 tensor occupies N * K/32 * 34 bytes, and
+    # consecutive offsets must agree with those sizes for our [N][K] shapes.
+    c = configs.get("mtp")
+    mc = GOLD["mcfg"]
+    assert (c["dim"], c["ffn"], c["heads"], c["kv_heads"], c["head_dim"], c["rope_dims"], c["rope_theta"],
+            c["vocab"], c["block"]) == (mc["H"], mc["I"], mc["NH"], mc["NKV"], mc["HD"], mc["ROT"], mc["THETA"],
+                                          mc["VOCAB"], mc["MAXM"])
+    t = GOLD["mtp_tensors"]["tensors"]
+    ours = {name: shape for name, shape, kind in gen.mtp_weight_specs(c)}
+    items = sorted(t.items(), key=lambda kv: kv[1][0])
+    end = GOLD["mtp_tensors"]["head_block"][0] + GOLD["mtp_tensors"]["head_block"][1]
+    for i, (name, (off, typ, ne0, ne1)) in enumerate(items):
+        if name == "output_norm" or off < GOLD["mtp_tensors"]["head_block"][0]:
+            continue
+        nxt = items[i + 1][1][0] if i + 1 < len(items) else end
+        if typ == 8:
+            assert ours[name] == (ne1, ne0)
+            assert nxt - off == ne1 * ne0 // 32 * 34
+        else:
+            assert ours[name] == (ne0,)
+            assert nxt - off == ne0 * 4
