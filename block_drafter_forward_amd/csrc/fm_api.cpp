@@ -1,0 +1,846 @@
+// fm_api.cpp — the C ABI (include/fm.h): host-side validation, the device workspace plan and the launch sequence
+// of every call. All validation happens before anything is enqueued; nothing here allocates device memory or
+// synchronises a stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/fm.h"
+#include "fm_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fm_status fail(fm_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define HIPCHK(expr)                                                                                \
+    do {                                                                                            \
+        hipError_t e_ = (expr);                                                                     \
+        if (e_ != hipSuccess) return fail(FM_E_HIP, "%s: %s", #expr, hipGetErrorString(e_));        \
+    } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int TMAX = 16;          // rows of one skinny activation matrix
+constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
+
+// k-split of a partial-output skinny GEMM: the smallest S dividing K/128 with tiles*S >= TARGET_WGS.
+int pick_split(int M_total, int K) {
+    const int n4 = K / 128, tiles = M_total / 16;
+    for (int S = 1; S <= n4; ++S)
+        if (n4 % S == 0 && (tiles * S >= TARGET_WGS || n4 / S <= 2)) return S;
+    return n4;
+}
+
+int attn_chunk(int L) { return L >= 4096 ? 256 : (L >= 1024 ? 128 : 64); }
+
+// ── workspace plan ──────────────────────────────────────────────────────────────────────────────
+struct Plan {
+    size_t best, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx, pctxn,
+        qout, total;
+    size_t part_floats;      // capacity of the partial buffer
+    int rope_rows, rope_dims;
+    int nchunk_max;
+    int colR;
+};
+
+int kmax_frag(const fm_config& c) {
+    int k = std::max({c.dim, c.target_dim, c.ffn, c.heads * c.head_dim, c.n_taps * c.target_dim});
+    if (c.variant == FM_VARIANT_MTP) k = std::max(k, 2 * c.dim);
+    return k;
+}
+
+int part_need(const fm_config& c) {   // floats per split slab row-set: max over partial uses of S * M
+    int need = 0;
+    auto use = [&](int M, int K) { need = std::max(need, pick_split(M, K) * M); };
+    const int D = c.dim, Ht = c.target_dim;
+    if (c.variant == FM_VARIANT_FLOWMAP) {
+        use(D, c.n_taps * Ht); use(D, Ht); use(D, D); use(D, c.ffn);
+    } else if (c.variant == FM_VARIANT_KVINJECT) {
+        use(D, c.n_taps * Ht); use(D, Ht); use(D, D); use(D, c.ffn);
+    } else {
+        use(D, 2 * D); use(D, c.heads * c.head_dim); use(D, c.ffn);
+    }
+    return need;
+}
+
+Plan make_plan(const fm_config& c) {
+    Plan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    const int D = c.dim;
+    p.best = take(16 * sizeof(unsigned long long));
+    p.rope_dims = c.rope == FM_ROPE_NEOX ? c.rope_dims : c.head_dim;
+    p.rope_rows = c.max_ctx + c.block + 2;
+    p.rope = take(c.rope == FM_ROPE_NONE ? 0 : (size_t)p.rope_rows * p.rope_dims * 4);
+    const size_t fragK = (size_t)kmax_frag(c) * 64;   // 2 KB per 32 k
+    p.fragA = take(fragK);
+    p.fragH = take(fragK);
+    p.fragO = take(fragK);
+    p.fragU = take(fragK);
+    p.x = take((size_t)TMAX * D * 4);
+    p.part_floats = (size_t)TMAX * part_need(c);
+    p.part = take(p.part_floats * 4);
+    int qkvw = 3 * D;
+    if (c.variant == FM_VARIANT_MTP) qkvw = c.heads * 2 * c.head_dim + 2 * c.kv_heads * c.head_dim;
+    p.qkv = take((size_t)TMAX * qkvw * 4);
+    const int Lmax = c.max_ctx + c.block + 1;
+    p.nchunk_max = (Lmax + 63) / 64;
+    p.attnp = take((size_t)c.heads * p.nchunk_max * TMAX * (c.head_dim + 2) * 4);
+    p.stage = take((size_t)2 * c.layers * TMAX * D * 4);
+    p.h0 = take((size_t)D * 4);
+    p.colR = 64;
+    p.colsc = take(c.variant == FM_VARIANT_FLOWMAP ? (size_t)p.colR * c.target_dim * 4 : 0);
+    p.cmean = take((size_t)c.target_dim * 4);
+    p.hc = take((size_t)TMAX * D * 4);
+    const bool prefill = c.variant != FM_VARIANT_MTP;
+    p.pctx = take(prefill ? (size_t)c.max_ctx * D * 4 : 0);
+    p.pctxn = take(prefill ? (size_t)(c.variant == FM_VARIANT_KVINJECT ? c.layers : 1) * c.max_ctx * D * 2 : 0);
+    p.qout = take(c.variant == FM_VARIANT_MTP ? (size_t)TMAX * c.heads * c.head_dim * 4 : 0);
+    p.total = off;
+    return p;
+}
+
+fm_status validate_config(const fm_config* c) {
+    if (!c) return fail(FM_E_INVALID, "null config");
+    if (c->variant < 0 || c->variant > 2) return fail(FM_E_INVALID, "unknown variant %d", c->variant);
+    if (c->dim <= 0 || c->heads <= 0 || c->head_dim <= 0 || c->layers <= 0 || c->ffn <= 0 || c->block <= 0 ||
+        c->target_dim <= 0 || c->vocab <= 0 || c->max_ctx <= 0 || c->kv_heads <= 0)
+        return fail(FM_E_INVALID, "non-positive size in config");
+    if (c->block > TMAX) return fail(FM_E_INVALID, "block %d exceeds %d rows", c->block, TMAX);
+    if (c->layers > 16) return fail(FM_E_INVALID, "more than 16 layers");
+    if (c->heads % c->kv_heads) return fail(FM_E_INVALID, "heads %% kv_heads != 0");
+    if (c->variant != FM_VARIANT_MTP && c->dim != c->heads * c->head_dim)
+        return fail(FM_E_INVALID, "dim %d != heads * head_dim", c->dim);
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+        return fail(FM_E_UNSUPPORTED, "head_dim %d (64, 128 or 256 supported)", c->head_dim);
+    if (c->dim % 256 || c->target_dim % 256 || c->ffn % 128)
+        return fail(FM_E_INVALID, "dim and target_dim must be multiples of 256, ffn of 128");
+    if (c->vocab % 16) return fail(FM_E_INVALID, "vocab must be a multiple of 16");
+    if (c->dim > 8 * 256 * 3) return fail(FM_E_UNSUPPORTED, "dim too large for the row kernels");
+    switch (c->variant) {
+    case FM_VARIANT_FLOWMAP:
+        if (c->rope != FM_ROPE_INTERLEAVED || c->mlp != FM_MLP_GELU_ERF || c->wtype != FM_W_BF16 ||
+            c->kv_dtype != FM_KV_F16 || c->head_dim > 128)
+            return fail(FM_E_UNSUPPORTED, "flow-map needs interleaved RoPE, exact GELU, bf16, f16 cache, hd <= 128");
+        if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
+        break;
+    case FM_VARIANT_KVINJECT:
+        if (c->rope != FM_ROPE_NONE || c->mlp != FM_MLP_GEGLU_TANH || c->wtype != FM_W_BF16 ||
+            c->kv_dtype != FM_KV_F32 || c->head_dim > 128)
+            return fail(FM_E_UNSUPPORTED, "KV-inject needs no RoPE, tanh GeGLU, bf16, f32 cache, hd <= 128");
+        if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
+        break;
+    case FM_VARIANT_MTP:
+        if (c->rope != FM_ROPE_NEOX || c->mlp != FM_MLP_SWIGLU || c->wtype != FM_W_Q8_0 || c->kv_dtype != FM_KV_F32)
+            return fail(FM_E_UNSUPPORTED, "MTP needs NEOX RoPE, SwiGLU, Q8_0, f32 cache");
+        if (c->rope_dims <= 0 || c->rope_dims > c->head_dim || c->rope_dims % 2)
+            return fail(FM_E_INVALID, "rope_dims");
+        if (c->target_dim != c->dim) return fail(FM_E_INVALID, "MTP target_dim must equal dim");
+        if ((c->heads * c->head_dim) % 128 || (c->kv_heads * c->head_dim) % 16)
+            return fail(FM_E_INVALID, "MTP head widths");
+        break;
+    }
+    return FM_OK;
+}
+
+}  // namespace
+
+// ── handle ──────────────────────────────────────────────────────────────────────────────────────
+struct fm_drafter {
+    fm_config c;
+    Plan p;
+    std::map<std::string, const void*> w;
+    uint8_t* ws;
+    uint8_t* kv;
+    int length;
+
+    template <class T> T* at(size_t off) const { return (T*)(ws + off); }
+    const void* W(const std::string& n) const { auto it = w.find(n); return it == w.end() ? nullptr : it->second; }
+    const uint16_t* B(const std::string& n) const { return (const uint16_t*)W(n); }
+    const float* F(const std::string& n) const { return (const float*)W(n); }
+    size_t kv_es() const { return c.kv_dtype == FM_KV_F16 ? 2 : 4; }
+    void* kv_layer(int l, int which) const {   // which 0: K, 1: V
+        return kv + ((size_t)(2 * l + which) * c.max_ctx * c.dim) * kv_es();
+    }
+};
+
+namespace {
+
+std::vector<std::string> required_names(const fm_config& c) {
+    std::vector<std::string> n;
+    char b[128];
+    if (c.variant == FM_VARIANT_FLOWMAP) {
+        n = {"fc.weight", "hidden_norm.weight", "anchor_proj.weight", "anchor_proj.bias", "anchor_norm.weight",
+             "state_norm.weight", "x_embed.weight", "x_embed.bias", "head.weight", "head.bias", "lm_head.weight", "mod"};
+        for (int l = 0; l < c.layers; ++l) {
+            for (const char* br : {"self_attn", "cross_attn"}) {
+                for (const char* p : {"q_proj", "k_proj", "v_proj", "o_proj", "q_norm", "k_norm"}) {
+                    snprintf(b, sizeof b, "layers.%d.%s.%s.weight", l, br, p);
+                    n.push_back(b);
+                }
+            }
+            for (const char* p : {"mlp.fc1.weight", "mlp.fc1.bias", "mlp.fc2.weight", "mlp.fc2.bias"}) {
+                snprintf(b, sizeof b, "layers.%d.%s", l, p);
+                n.push_back(b);
+            }
+        }
+    } else if (c.variant == FM_VARIANT_KVINJECT) {
+        n = {"W_c", "ctx_norm", "tok_proj", "mask_emb", "block_pos", "out_norm", "out_proj", "lm_head.weight"};
+        for (int i = 0; i < c.layers; ++i)
+            for (const char* p : {"attn_norm", "q", "k", "v", "o", "ff_norm", "gate", "up", "down"}) {
+                snprintf(b, sizeof b, "bb.%d.%s", i, p);
+                n.push_back(b);
+            }
+    } else {
+        for (const char* p : {"eh_proj", "attn_q", "attn_k", "attn_v", "attn_output", "ffn_gate", "ffn_up", "ffn_down",
+                              "lm_head"}) {
+            n.push_back(std::string(p) + ".q");
+            n.push_back(std::string(p) + ".d");
+        }
+        for (const char* p : {"attn_norm", "attn_q_norm", "attn_k_norm", "post_attention_norm", "shared_head_norm",
+                              "enorm", "hnorm"})
+            n.push_back(p);
+    }
+    return n;
+}
+
+// ── skinny GEMM helper ──────────────────────────────────────────────────────────────────────────
+struct SkGroupDesc {
+    const void* W;
+    const void* Wd;
+    const void* W2;
+    const void* W2d;
+    const uint16_t* bias;
+    const uint8_t* X;
+    void* out;
+    int M;
+    int ld;
+};
+
+// Enqueue one skinny launch. For SK_PARTIAL the k-split is chosen here (returned through S_out); every other mode
+// runs with S = 1 (the whole k-range in one work-group).
+fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K, int T, int mode, int S_force,
+                 int* S_out, hipStream_t st) {
+    if (gs.empty() || gs.size() > SK_MAX_GROUPS) return fail(FM_E_INVALID, "skinny: %zu groups", gs.size());
+    if (K % 128) return fail(FM_E_INVALID, "skinny: K %d not a multiple of 128", K);
+    SkinnyArgs a{};
+    int tiles_total = 0;
+    for (auto& g : gs) tiles_total += g.M / 16;
+    int S = 1;
+    if (mode == SK_PARTIAL) S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K);
+    a.ngroups = (int)gs.size();
+    a.K = K;
+    a.T = T;
+    a.S = S;
+    a.KW = K / 128 / S;
+    a.mode = mode;
+    int begin = 0;
+    size_t part_use = 0;
+    for (size_t i = 0; i < gs.size(); ++i) {
+        const auto& g = gs[i];
+        if (g.M % 16) return fail(FM_E_INVALID, "skinny: M %d not a multiple of 16", g.M);
+        a.g[i] = SkinnyGroup{g.W, g.Wd, g.W2, g.W2d, g.bias, g.X, g.out, g.M, g.ld, begin, 0};
+        begin += (g.M / 16) * S;
+        part_use = std::max(part_use, (size_t)S * TMAX * g.M);
+    }
+    if (mode == SK_PARTIAL) {
+        a.part_stride = (long long)TMAX * gs[0].M;
+        if (part_use > d->p.part_floats) return fail(FM_E_INVALID, "skinny: partial buffer too small");
+    }
+    if (S_out) *S_out = S;
+    HIPCHK(launch_skinny(a, d->c.wtype == FM_W_Q8_0 ? SKW_Q8_0 : SKW_BF16, begin, st));
+    return FM_OK;
+}
+
+RowArgs rows_base(int D, int T) {
+    RowArgs r{};
+    r.D = D;
+    r.T = T;
+    return r;
+}
+
+fm_status rows(const RowArgs& r, hipStream_t st) {
+    HIPCHK(launch_rows(r, st));
+    return FM_OK;
+}
+
+#define CHK(x)                        \
+    do {                              \
+        fm_status s_ = (x);           \
+        if (s_ != FM_OK) return s_;   \
+    } while (0)
+
+// ── flow-map ────────────────────────────────────────────────────────────────────────────────────
+std::string LW(int l, const char* s) {
+    char b[128];
+    snprintf(b, sizeof b, "layers.%d.%s", l, s);
+    return b;
+}
+
+// c rows (fragments in fragH, T rows) -> every layer's K/V at rows start.. (skinny path, T <= 16)
+fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim;
+    std::vector<SkGroupDesc> gs;
+    float* stage = d->at<float>(d->p.stage);
+    for (int l = 0; l < c.layers; ++l) {
+        gs.push_back({d->W(LW(l, "cross_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr,
+                      d->at<uint8_t>(d->p.fragH), stage + (size_t)(2 * l) * T * D, D, D});
+        gs.push_back({d->W(LW(l, "cross_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr,
+                      d->at<uint8_t>(d->p.fragH), stage + (size_t)(2 * l + 1) * T * D, D, D});
+    }
+    // at most 12 groups per launch
+    for (size_t i = 0; i < gs.size(); i += SK_MAX_GROUPS) {
+        std::vector<SkGroupDesc> sub(gs.begin() + i, gs.begin() + std::min(gs.size(), i + SK_MAX_GROUPS));
+        CHK(skinny(d, sub, D, T, SK_F32, 0, nullptr, st));
+    }
+    KVFinalArgs k{};
+    k.stage = stage;
+    k.n = T;
+    k.D = D;
+    k.heads = c.heads;
+    k.hd = c.head_dim;
+    k.layers = c.layers;
+    for (int l = 0; l < c.layers; ++l) k.knorm[l] = d->B(LW(l, "cross_attn.k_norm.weight"));
+    k.eps = c.qk_eps;
+    k.rope_tab = d->at<float>(d->p.rope);
+    k.rope_dims = d->p.rope_dims;
+    k.start = start;
+    k.cache = d->kv;
+    k.max_ctx = c.max_ctx;
+    k.kv_dtype = c.kv_dtype;
+    HIPCHK(launch_kv_final(k, st));
+    return FM_OK;
+}
+
+fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim, KT = c.n_taps * c.target_dim;
+    if (n <= TMAX) {
+        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), st));
+        int S = 0;
+        float* part = d->at<float>(d->p.part);
+        CHK(skinny(d, {{d->W("fc.weight"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}},
+                   KT, n, SK_PARTIAL, 0, &S, st));
+        RowArgs r = rows_base(D, n);
+        r.part = part;
+        r.S = S;
+        r.part_stride = (long long)TMAX * D;
+        r.norm = ROW_RMS;
+        r.w_bf16 = d->B("hidden_norm.weight");
+        r.eps = c.rms_eps;
+        r.frag_out = d->at<uint8_t>(d->p.fragH);
+        CHK(rows(r, st));
+        return fm_kv_rows_small(d, n, start, st);
+    }
+    // prefill: MFMA GEMMs
+    float* ctx = d->at<float>(d->p.pctx);
+    uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
+    const int mt = (n + 127) / 128;
+    {
+        PrefillArgs a{};
+        a.ngroups = 1;
+        a.g[0] = PrefillGroup{nullptr, d->B("fc.weight"), nullptr, ctx, PF_F32, 0};
+        a.A = taps;
+        a.a_f32 = 1;
+        a.rows = n;
+        a.N = D;
+        a.K = KT;
+        a.ld = D;
+        a.m_tiles = mt;
+        a.n_tiles = D / 128;
+        HIPCHK(launch_prefill(a, mt * a.n_tiles, st));
+    }
+    HIPCHK(launch_rms_f16(ctx, n, D, d->B("hidden_norm.weight"), c.rms_eps, ctxn, st));
+    for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
+        PrefillArgs a{};
+        const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
+        const int per = mt * (D / 128);
+        for (int j = 0; j < nl; ++j) {
+            const int l = l0 + j;
+            a.g[2 * j] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.k_proj.weight")),
+                                      d->B(LW(l, "cross_attn.k_norm.weight")), d->kv_layer(l, 0), PF_CACHE_K,
+                                      (2 * j) * per};
+            a.g[2 * j + 1] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.v_proj.weight")), nullptr, d->kv_layer(l, 1),
+                                          PF_CACHE_V, (2 * j + 1) * per};
+        }
+        a.ngroups = 2 * nl;
+        a.A = ctxn;
+        a.a_f32 = 0;
+        a.rows = n;
+        a.N = D;
+        a.K = D;
+        a.ld = D;
+        a.hd = c.head_dim;
+        a.eps = c.qk_eps;
+        a.rope_tab = d->at<float>(d->p.rope);
+        a.rope_dims = d->p.rope_dims;
+        a.start = start;
+        a.kv_dtype = c.kv_dtype;
+        a.m_tiles = mt;
+        a.n_tiles = D / 128;
+        HIPCHK(launch_prefill(a, 2 * nl * per, st));
+    }
+    return FM_OK;
+}
+
+fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim, T = c.block, Ht = c.target_dim, H = c.heads, hd = c.head_dim;
+    const int pos = ba->pos;
+    float* part = d->at<float>(d->p.part);
+    float* x = d->at<float>(d->p.x);
+    const float* mod = d->F("mod");
+    uint8_t* fragA = d->at<uint8_t>(d->p.fragA);
+    uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
+    uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
+    uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
+    float* qkv = d->at<float>(d->p.qkv);
+    const float* rope = d->at<float>(d->p.rope);
+    const long long pstr = (long long)TMAX * D;
+
+    // anchor slot: anchor_norm(anchor_proj(E[anchor])) through every layer's k/v path at pos
+    HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, fragA, st));
+    int S = 0;
+    CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, 1,
+               SK_PARTIAL, 0, &S, st));
+    {
+        RowArgs r = rows_base(D, 1);
+        r.part = part;
+        r.S = S;
+        r.part_stride = pstr;
+        r.bias = d->B("anchor_proj.bias");
+        r.norm = ROW_RMS;
+        r.w_bf16 = d->B("anchor_norm.weight");
+        r.eps = c.rms_eps;
+        r.frag_out = fragH;
+        CHK(rows(r, st));
+    }
+    CHK(fm_kv_rows_small(d, 1, pos, st));
+
+    const int L = pos + 1;
+    const int chunk = attn_chunk(L);
+    const int nchunks = (L + chunk - 1) / chunk;
+    int S_prev = 0;           // split count of the pending residual update (fc2 of the previous layer)
+    for (int l = 0; l < c.layers; ++l) {
+        const float* m_sa = mod + (size_t)(3 * l) * 3 * D;
+        const float* m_ca = mod + (size_t)(3 * l + 1) * 3 * D;
+        const float* m_ml = mod + (size_t)(3 * l + 2) * 3 * D;
+        // residual (previous layer's MLP) + self-attention modulation
+        {
+            RowArgs r = rows_base(D, T);
+            r.x = x;
+            if (l == 0) {
+                r.init = d->at<float>(d->p.h0);
+            } else {
+                r.part = part;
+                r.S = S_prev;
+                r.part_stride = pstr;
+                r.bias = d->B(LW(l - 1, "mlp.fc2.bias"));
+                r.gate = mod + (size_t)(3 * (l - 1) + 2) * 3 * D + 2 * D;
+                if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)(l - 1) * T * D;
+            }
+            r.norm = ROW_LN_MOD;
+            r.scale = m_sa;
+            r.shift = m_sa + D;
+            r.eps = c.ln_eps;
+            r.frag_out = fragH;
+            CHK(rows(r, st));
+        }
+        CHK(skinny(d,
+                   {{d->W(LW(l, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, 3 * D},
+                    {d->W(LW(l, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
+                    {d->W(LW(l, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D, D,
+                     3 * D}},
+                   D, T, SK_F32, 0, nullptr, st));
+        {
+            SelfAttnArgs a{};
+            a.qkv = qkv;
+            a.T = T;
+            a.D = D;
+            a.heads = H;
+            a.hd = hd;
+            a.qn = d->B(LW(l, "self_attn.q_norm.weight"));
+            a.kn = d->B(LW(l, "self_attn.k_norm.weight"));
+            a.eps = c.qk_eps;
+            a.rope_tab = rope;
+            a.pos_base = pos + 1;
+            a.scale = 1.f / sqrtf((float)hd);
+            a.o_frag = fragO;
+            HIPCHK(launch_self_attn(a, st));
+        }
+        CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
+                   D, T, SK_PARTIAL, 0, &S, st));
+        {
+            RowArgs r = rows_base(D, T);
+            r.x = x;
+            r.part = part;
+            r.S = S;
+            r.part_stride = pstr;
+            r.gate = m_sa + 2 * D;
+            r.norm = ROW_LN_MOD;
+            r.scale = m_ca;
+            r.shift = m_ca + D;
+            r.eps = c.ln_eps;
+            r.frag_out = fragH;
+            CHK(rows(r, st));
+        }
+        // cross-attention over cache rows [0, pos]
+        int Sq = 0;
+        CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, part, D, D}},
+                   D, T, SK_PARTIAL, 0, &Sq, st));
+        {
+            AttnArgs a{};
+            a.qp.part = part;
+            a.qp.S = Sq;
+            a.qp.part_stride = pstr;
+            a.qp.q_ld = D;
+            a.qp.q_hs = hd;
+            a.qp.norm_bf16 = d->B(LW(l, "cross_attn.q_norm.weight"));
+            a.qp.eps = c.qk_eps;
+            a.qp.rope = 1;
+            a.qp.rope_dims = d->p.rope_dims;
+            a.qp.rope_tab = rope;
+            a.qp.pos_base = pos + 1;
+            a.nq = T;
+            a.kc = d->kv_layer(l, 0);
+            a.vc = d->kv_layer(l, 1);
+            a.kv_ld = D;
+            a.kv_dtype = c.kv_dtype;
+            a.key_lo = 0;
+            a.key_hi = L;
+            a.heads = H;
+            a.kv_heads = H;
+            a.hd = hd;
+            a.causal_base = -1;
+            a.scale = 1.f / sqrtf((float)hd);
+            a.chunk = chunk;
+            a.nchunks = nchunks;
+            a.part = d->at<float>(d->p.attnp);
+            HIPCHK(launch_attn_split(a, st));
+            MergeArgs m{};
+            m.part = a.part;
+            m.heads = H;
+            m.nchunks = nchunks;
+            m.nq = T;
+            m.hd = hd;
+            m.o_frag = fragO;
+            HIPCHK(launch_attn_merge(m, st));
+        }
+        CHK(skinny(d, {{d->W(LW(l, "cross_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
+                   D, T, SK_PARTIAL, 0, &S, st));
+        {
+            RowArgs r = rows_base(D, T);
+            r.x = x;
+            r.part = part;
+            r.S = S;
+            r.part_stride = pstr;
+            r.gate = m_ca + 2 * D;
+            r.norm = ROW_LN_MOD;
+            r.scale = m_ml;
+            r.shift = m_ml + D;
+            r.eps = c.ln_eps;
+            r.frag_out = fragH;
+            CHK(rows(r, st));
+        }
+        // MLP: fc1 + exact GELU (fused), fc2 (its residual is applied by the next row kernel)
+        CHK(skinny(d, {{d->W(LW(l, "mlp.fc1.weight")), nullptr, nullptr, nullptr, d->B(LW(l, "mlp.fc1.bias")), fragH,
+                        fragU, c.ffn, 0}},
+                   D, T, SK_FRAG_GELU, 0, nullptr, st));
+        CHK(skinny(d, {{d->W(LW(l, "mlp.fc2.weight")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
+                   SK_PARTIAL, 0, &S_prev, st));
+    }
+    {
+        const float* m_f = mod + (size_t)(3 * c.layers) * 3 * D;
+        RowArgs r = rows_base(D, T);
+        r.x = x;
+        r.part = part;
+        r.S = S_prev;
+        r.part_stride = pstr;
+        r.bias = d->B(LW(c.layers - 1, "mlp.fc2.bias"));
+        r.gate = mod + (size_t)(3 * (c.layers - 1) + 2) * 3 * D + 2 * D;
+        if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)(c.layers - 1) * T * D;
+        r.norm = ROW_LN_MOD;
+        r.scale = m_f;
+        r.shift = m_f + D;
+        r.eps = c.ln_eps;
+        r.frag_out = fragH;
+        CHK(rows(r, st));
+    }
+    CHK(skinny(d, {{d->W("head.weight"), nullptr, nullptr, nullptr, d->B("head.bias"), fragH, hidden_out, Ht, Ht}}, D, T,
+               SK_F32, 0, nullptr, st));
+    return FM_OK;
+}
+
+fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
+    const auto& c = d->c;
+    const int Ht = c.target_dim, D = c.dim;
+    // zero-noise slot input h0 = x_embed(state_norm(mean row of E)) + b
+    HIPCHK(launch_colmean(d->B("lm_head.weight"), c.vocab, Ht, d->at<float>(d->p.colsc), d->p.colR,
+                          d->at<float>(d->p.cmean), st));
+    RowArgs r = rows_base(Ht, 1);
+    r.init = d->at<float>(d->p.cmean);
+    r.norm = ROW_RMS;
+    r.w_bf16 = d->B("state_norm.weight");
+    r.eps = c.rms_eps;
+    r.frag_out = d->at<uint8_t>(d->p.fragA);
+    CHK(rows(r, st));
+    CHK(skinny(d, {{d->W("x_embed.weight"), nullptr, nullptr, nullptr, d->B("x_embed.bias"), d->at<uint8_t>(d->p.fragA),
+                    d->at<float>(d->p.h0), D, D}},
+               Ht, 1, SK_F32, 0, nullptr, st));
+    return FM_OK;
+}
+
+// ── KV-injection ────────────────────────────────────────────────────────────────────────────────
+std::string BB(int i, const char* s) {
+    char b[64];
+    snprintf(b, sizeof b, "bb.%d.%s", i, s);
+    return b;
+}
+
+fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim, KT = c.n_taps * c.target_dim;
+    if (n <= TMAX) {
+        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), st));
+        int S = 0;
+        float* part = d->at<float>(d->p.part);
+        CHK(skinny(d, {{d->W("W_c"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}}, KT, n,
+                   SK_PARTIAL, 0, &S, st));
+        float* hc = d->at<float>(d->p.hc);
+        RowArgs r = rows_base(D, n);
+        r.part = part;
+        r.S = S;
+        r.part_stride = (long long)TMAX * D;
+        r.norm = ROW_RMS;
+        r.w_bf16 = d->B("ctx_norm");
+        r.eps = c.rms_eps;
+        r.f32_out = hc;
+        r.out_ld = D;
+        CHK(rows(r, st));
+        // per layer: RMSNorm(H_ctx; attn_norm) -> K, V written straight into the f32 cache rows
+        for (int i = 0; i < c.layers; ++i) {
+            uint8_t* fr = i % 2 ? d->at<uint8_t>(d->p.fragO) : d->at<uint8_t>(d->p.fragH);
+            RowArgs q = rows_base(D, n);
+            q.in_rows = hc;
+            q.in_ld = D;
+            q.norm = ROW_RMS;
+            q.w_bf16 = d->B(BB(i, "attn_norm"));
+            q.eps = c.rms_eps;
+            q.frag_out = fr;
+            CHK(rows(q, st));
+            CHK(skinny(d,
+                       {{d->W(BB(i, "k")), nullptr, nullptr, nullptr, nullptr, fr,
+                         (float*)d->kv_layer(i, 0) + (size_t)start * D, D, D},
+                        {d->W(BB(i, "v")), nullptr, nullptr, nullptr, nullptr, fr,
+                         (float*)d->kv_layer(i, 1) + (size_t)start * D, D, D}},
+                       D, n, SK_F32, 0, nullptr, st));
+        }
+        return FM_OK;
+    }
+    float* ctx = d->at<float>(d->p.pctx);
+    uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
+    const int mt = (n + 127) / 128;
+    {
+        PrefillArgs a{};
+        a.ngroups = 1;
+        a.g[0] = PrefillGroup{nullptr, d->B("W_c"), nullptr, ctx, PF_F32, 0};
+        a.A = taps;
+        a.a_f32 = 1;
+        a.rows = n;
+        a.N = D;
+        a.K = KT;
+        a.ld = D;
+        a.m_tiles = mt;
+        a.n_tiles = D / 128;
+        HIPCHK(launch_prefill(a, mt * a.n_tiles, st));
+    }
+    // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32), then per layer RMSNorm(H_ctx; attn_norm) -> f16
+    {
+        RowArgs r = rows_base(D, n);
+        r.x = ctx;
+        r.norm = ROW_RMS;
+        r.w_bf16 = d->B("ctx_norm");
+        r.eps = c.rms_eps;
+        r.f32_out = ctx;
+        r.out_ld = D;
+        CHK(rows(r, st));
+    }
+    for (int i = 0; i < c.layers; ++i)
+        HIPCHK(launch_rms_f16(ctx, n, D, d->B(BB(i, "attn_norm")), c.rms_eps, ctxn + (size_t)i * c.max_ctx * D, st));
+    const int per = mt * (D / 128);
+    for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
+        PrefillArgs a{};
+        const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
+        for (int j = 0; j < nl; ++j) {
+            const int i = l0 + j;
+            const uint16_t* Ai = ctxn + (size_t)i * c.max_ctx * D;
+            a.g[2 * j] = PrefillGroup{Ai, d->B(BB(i, "k")), nullptr, d->kv_layer(i, 0), PF_CACHE_V, (2 * j) * per};
+            a.g[2 * j + 1] = PrefillGroup{Ai, d->B(BB(i, "v")), nullptr, d->kv_layer(i, 1), PF_CACHE_V, (2 * j + 1) * per};
+        }
+        a.ngroups = 2 * nl;
+        a.a_f32 = 0;
+        a.rows = n;
+        a.N = D;
+        a.K = D;
+        a.ld = D;
+        a.hd = c.head_dim;
+        a.start = start;
+        a.kv_dtype = c.kv_dtype;
+        a.m_tiles = mt;
+        a.n_tiles = D / 128;
+        HIPCHK(launch_prefill(a, 2 * nl * per, st));
+    }
+    return FM_OK;
+}
+
+fm_status kvinject_draft(fm_drafter*, const fm_block_args*, float*, hipStream_t) {
+    return fail(FM_E_UNSUPPORTED, "KV-inject draft not built yet");
+}
+
+fm_status kvinject_create(fm_drafter*, hipStream_t) { return FM_OK; }
+
+}  // namespace
+
+// ── C ABI ───────────────────────────────────────────────────────────────────────────────────────
+extern "C" {
+
+size_t fm_kv_bytes(const fm_config* cfg) {
+    if (validate_config(cfg) != FM_OK) return 0;
+    const fm_config& c = *cfg;
+    if (c.variant == FM_VARIANT_MTP) return 2 * (size_t)c.max_ctx * c.kv_heads * c.head_dim * 4;
+    const size_t es = c.kv_dtype == FM_KV_F16 ? 2 : 4;
+    return 2 * (size_t)c.layers * c.max_ctx * c.dim * es;
+}
+
+size_t fm_workspace_bytes(const fm_config* cfg) {
+    if (validate_config(cfg) != FM_OK) return 0;
+    return make_plan(*cfg).total;
+}
+
+fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* names, const void* const* ptrs,
+                    void* kv_cache, void* workspace, void* stream, fm_drafter** out) {
+    g_err.clear();
+    if (!out) return fail(FM_E_INVALID, "null output handle pointer");
+    *out = nullptr;
+    CHK(validate_config(cfg));
+    if (!kv_cache || !workspace) return fail(FM_E_INVALID, "null kv_cache or workspace");
+    if (((uintptr_t)kv_cache & 255) || ((uintptr_t)workspace & 255))
+        return fail(FM_E_INVALID, "kv_cache and workspace must be 256-byte aligned");
+    if (n_weights < 0 || (n_weights > 0 && (!names || !ptrs))) return fail(FM_E_INVALID, "bad weight table");
+    auto* d = new fm_drafter();
+    d->c = *cfg;
+    d->p = make_plan(*cfg);
+    d->ws = (uint8_t*)workspace;
+    d->kv = (uint8_t*)kv_cache;
+    d->length = 0;
+    for (int i = 0; i < n_weights; ++i) {
+        if (!names[i]) { delete d; return fail(FM_E_INVALID, "null weight name at %d", i); }
+        if (!ptrs[i]) { delete d; return fail(FM_E_INVALID, "null pointer for weight %s", names[i]); }
+        d->w[names[i]] = ptrs[i];
+    }
+    for (const auto& n : required_names(*cfg))
+        if (!d->W(n)) {
+            delete d;
+            return fail(FM_E_MISSING_WEIGHT, "missing weight '%s'", n.c_str());
+        }
+    if (cfg->variant == FM_VARIANT_KVINJECT && cfg->block < 1) { delete d; return fail(FM_E_INVALID, "gamma"); }
+    hipStream_t st = (hipStream_t)stream;
+    fm_status s = FM_OK;
+    do {
+        if (launch_fill_u32(d->at<uint32_t>(d->p.best), 32, 0u, st) != hipSuccess) { s = fail(FM_E_HIP, "fill"); break; }
+        if (cfg->rope != FM_ROPE_NONE) {
+            hipError_t e = launch_rope_table(d->at<float>(d->p.rope), d->p.rope_rows, d->p.rope_dims, cfg->rope_theta, st);
+            if (e != hipSuccess) { s = fail(FM_E_HIP, "rope table: %s", hipGetErrorString(e)); break; }
+        }
+        if (cfg->variant == FM_VARIANT_FLOWMAP) s = flowmap_create(d, st);
+        else if (cfg->variant == FM_VARIANT_KVINJECT) s = kvinject_create(d, st);
+    } while (0);
+    if (s != FM_OK) { delete d; return s; }
+    *out = d;
+    return FM_OK;
+}
+
+fm_status fm_context_append(fm_drafter* d, const float* taps, int32_t n, int32_t start, void* stream) {
+    g_err.clear();
+    if (!d) return fail(FM_E_INVALID, "null handle");
+    if (d->c.variant == FM_VARIANT_MTP) return fail(FM_E_INVALID, "the MTP head has no context append");
+    if (!taps) return fail(FM_E_INVALID, "null taps");
+    if (n < 1) return fail(FM_E_INVALID, "n = %d < 1", n);
+    if (start < 0 || start > d->length) return fail(FM_E_INVALID, "start %d outside [0, length %d]", start, d->length);
+    if ((long long)start + n + d->c.block + 1 > d->c.max_ctx)
+        return fail(FM_E_CONTEXT_FULL, "context full: start %d + n %d + block %d + 1 > max_ctx %d", start, n,
+                    d->c.block, d->c.max_ctx);
+    hipStream_t st = (hipStream_t)stream;
+    fm_status s = d->c.variant == FM_VARIANT_FLOWMAP ? flowmap_append(d, taps, n, start, st)
+                                                     : kvinject_append(d, taps, n, start, st);
+    if (s == FM_OK) d->length = start + n;
+    return s;
+}
+
+fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_out, void* stream) {
+    g_err.clear();
+    if (!d || !a || !hidden_out) return fail(FM_E_INVALID, "null argument");
+    hipStream_t st = (hipStream_t)stream;
+    const auto& c = d->c;
+    if (c.variant == FM_VARIANT_FLOWMAP) {
+        if (!a->anchor) return fail(FM_E_INVALID, "null anchor");
+        if (a->pos < 0 || a->pos > d->length) return fail(FM_E_INVALID, "pos %d outside [0, length %d]", a->pos, d->length);
+        if ((long long)a->pos + c.block + 1 > c.max_ctx) return fail(FM_E_CONTEXT_FULL, "pos %d + block + 1 > max_ctx", a->pos);
+        return flowmap_draft(d, a, hidden_out, st);
+    }
+    if (c.variant == FM_VARIANT_KVINJECT) {
+        if (!a->anchor) return fail(FM_E_INVALID, "null anchor");
+        if (d->length < 1) return fail(FM_E_INVALID, "empty context");
+        return kvinject_draft(d, a, hidden_out, st);
+    }
+    return fail(FM_E_UNSUPPORTED, "MTP draft not built yet");
+}
+
+fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits, void* stream) {
+    g_err.clear();
+    if (!d || !hidden || !tokens) return fail(FM_E_INVALID, "null argument");
+    if (rows < 1 || rows > d->c.block) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, d->c.block);
+    hipStream_t st = (hipStream_t)stream;
+    const int K = d->c.target_dim;
+    uint8_t* fr = d->at<uint8_t>(d->p.fragH);
+    HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
+    LmArgs a{};
+    const bool q8 = d->c.wtype == FM_W_Q8_0;
+    a.E = q8 ? d->W("lm_head.q") : d->W("lm_head.weight");
+    a.Ed = q8 ? d->W("lm_head.d") : nullptr;
+    a.X = fr;
+    a.V = d->c.vocab;
+    a.K = K;
+    a.T = rows;
+    a.best = d->at<unsigned long long>(d->p.best);
+    a.tokens = tokens;
+    a.logits = logits;
+    HIPCHK(launch_lm_argmax(a, q8 ? 1 : 0, st));
+    return FM_OK;
+}
+
+int32_t fm_context_length(const fm_drafter* d) { return d ? d->length : -1; }
+
+void fm_destroy(fm_drafter* d) { delete d; }
+
+const char* fm_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

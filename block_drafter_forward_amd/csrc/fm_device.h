@@ -1,0 +1,89 @@
+// fm_device.h — device-side helpers shared by the gfx950 kernels: storage-format conversions, the MFMA
+// activation-fragment layout, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ── bf16 / f16 ─────────────────────────────────────────────────────────────────────────────────
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, h);
+    return (float)v;
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    _Float16 v = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, v);
+}
+
+// ── activation fragments ───────────────────────────────────────────────────────────────────────
+// A skinny activation matrix X[T <= 16][K] (K a multiple of 32) is stored as the B operand of
+// v_mfma_f32_16x16x32_bf16, split into two bf16 terms x = hi + lo (|x - hi - lo| <= 2^-17 |x|):
+//   for k-step s (k = 32 s .. 32 s + 31): 2048 bytes = hi[64 lanes][8 bf16] then lo[64 lanes][8 bf16];
+//   lane l = t + 16 g holds row t = l % 16, elements k = 32 s + 8 g + e for e = 0..7.
+// Rows t >= T are never read back by any consumer (MFMA columns are independent), so they need no clearing.
+#define FRAG_STEP_BYTES 2048
+
+__device__ __forceinline__ size_t frag_offset(int t, int k) {   // byte offset of element (t, k), k % 8 == 0
+    int s = k >> 5, g = (k & 31) >> 3;
+    return (size_t)s * FRAG_STEP_BYTES + (size_t)(t + 16 * g) * 16;
+}
+
+// Store 8 consecutive values x[t][k .. k+7] (k % 8 == 0) as their hi/lo bf16 fragments.
+__device__ __forceinline__ void frag_store8(uint8_t* frag, int t, int k, const float* v) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+        uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
+        uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
+        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    uint8_t* p = frag + frag_offset(t, k);
+    *(uint4*)p = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *(uint4*)(p + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+// ── reductions ─────────────────────────────────────────────────────────────────────────────────
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+// Sum over the 256 threads of a block; `red` is __shared__ float[4]. Every thread gets the result.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+    v = wave_sum(v);
+    int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ── math ───────────────────────────────────────────────────────────────────────────────────────
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float c = 0.7978845608028654f;   // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigmoidf(x); }

@@ -1,0 +1,226 @@
+// fm_kernels.h — argument blocks and host launchers of the gfx950 kernels (internal to libfm).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// ── K1: skinny-T weight-streaming GEMM ─────────────────────────────────────────────────────────
+// Y[t][m] = sum_k X[t][k] W[m][k] for t < T <= 16: weights streamed once from HBM straight into the A operand of
+// v_mfma_f32_16x16x32_bf16 (16 rows x 32 k per step), activations read as hi/lo bf16 fragments (fm_device.h).
+// A work-group is 4 waves on one 16-row tile, each wave a quarter of the group's k-range; the 4 partial tiles are
+// summed in LDS. S > 1 splits k across work-groups; those write partial slabs the consumer sums in order.
+enum SkinnyOut {
+    SK_F32 = 0,        // out[t*ld + m] = acc + bias[m]
+    SK_PARTIAL = 1,    // out[split*part_stride + t*ld + m] = acc
+    SK_FRAG_GELU = 2,  // frag(out)[t][m] = gelu_erf(acc + bias[m])
+    SK_FRAG_GEGLU = 3, // frag(out)[t][m] = gelu_tanh(acc_gate) * acc_up        (two weight tiles)
+    SK_FRAG_SWIGLU = 4 // frag(out)[t][m] = silu(acc_gate) * acc_up             (two weight tiles)
+};
+enum SkinnyWType { SKW_BF16 = 0, SKW_Q8_0 = 1 };
+
+#define SK_MAX_GROUPS 12
+struct SkinnyGroup {
+    const void* W;        // bf16 [M][K], or Q8_0 codes int8 [M][K]
+    const void* Wd;       // Q8_0 scales f16 [M][K/32] (else null)
+    const void* W2;       // second weight tile (GLU "up"), same format, or null
+    const void* W2d;
+    const uint16_t* bias; // bf16 [M] or null
+    const uint8_t* X;     // activation fragments, K/32 steps
+    void* out;
+    int M;                // rows (multiple of 16)
+    int ld;               // output row stride (elements)
+    int tile_begin;       // first work-group of this group
+    int pad;
+};
+struct SkinnyArgs {
+    SkinnyGroup g[SK_MAX_GROUPS];
+    int ngroups;
+    int K;
+    int T;
+    int S;                // k-splits across work-groups
+    int KW;               // k-steps per wave (K / 32 == S * 4 * KW), any value >= 1
+    int mode;
+    long long part_stride;
+};
+hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int n_workgroups, hipStream_t st);
+
+// ── K3: row kernels (residual update + norm + fragment store) ─────────────────────────────────
+enum RowNorm { ROW_NONE = 0, ROW_LN_MOD = 1, ROW_RMS = 2 };
+struct RowArgs {
+    float* x;              // residual stream [T][D] updated in place (or null)
+    const float* init;     // if set, the row's base value is init[i] (broadcast over rows) instead of x
+    const float* in_rows;  // if set, base value is in_rows[t*in_ld + i]
+    int in_ld;
+    const float* part;     // split partials [S][T][D] added (or null)
+    long long part_stride;
+    int S;
+    const uint16_t* bias;  // bf16 [D] added with the partials (or null)
+    const float* gate;     // f32 [D]: x = base + gate * update (null: gate 1)
+    int norm;              // RowNorm
+    const float* scale;    // LN-mod: LN(x) * (1 + scale) + shift
+    const float* shift;
+    const uint16_t* w_bf16;// RMSNorm weight (bf16) or
+    const float* w_f32;    //   (f32)
+    float eps;
+    uint8_t* frag_out;     // normalised row -> fragments at k offset frag_koff (or null)
+    int frag_koff;
+    float* f32_out;        // normalised row as f32 [T][out_ld] (or null)
+    int out_ld;
+    float* debug_x;        // copy of the updated stream [T][D] (or null)
+    int D;
+    int T;
+};
+hipError_t launch_rows(const RowArgs& a, hipStream_t st);
+
+// f32 rows [T][K] (row stride ld) -> fragments. T <= 16, K % 32 == 0.
+hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st);
+// bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
+hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, hipStream_t st);
+// bf16 row E[*idx] -> f32 [K] (+ optional bf16 row added); ids are clamped to [0, V).
+hipError_t launch_gather_f32(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add_bf16, float* out,
+                             hipStream_t st);
+
+// ── create-time kernels ────────────────────────────────────────────────────────────────────────
+// Column mean of a bf16 table [V][H] -> f32 [H] (two deterministic stages; scratch holds R*H floats).
+hipError_t launch_colmean(const uint16_t* E, int V, int H, float* scratch, int R, float* out, hipStream_t st);
+// RoPE table rows p < P: [cos r/2 | sin r/2] of angle p * theta^(-2i/r), built in f64, stored f32.
+hipError_t launch_rope_table(float* tab, int P, int r, double theta, hipStream_t st);
+// Fill n 32-bit words with v.
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
+
+// ── K4: attention ──────────────────────────────────────────────────────────────────────────────
+struct QPrep {             // how a work-group builds its query rows for one head
+    const float* q;        // q rows: q[t*q_ld + h*q_hs + d] ...
+    int q_ld;
+    int q_hs;
+    const float* part;     // ... or the sum of S partial slabs [S][T][q_ld] (same indexing)
+    long long part_stride;
+    int S;
+    const uint16_t* norm_bf16;  // head RMSNorm weight (bf16 or f32) or null
+    const float* norm_f32;
+    float eps;
+    int rope;              // 0 none, 1 interleaved, 2 NEOX partial
+    int rope_dims;
+    const float* rope_tab; // rows [cos rope_dims/2 | sin rope_dims/2]
+    int pos_base;          // query t sits at position pos_base + t
+};
+// Flow-map self-attention over the T slots (one work-group per head); writes o as fragments.
+struct SelfAttnArgs {
+    const float* qkv;      // [T][3D]: q | k | v
+    int T, D, heads, hd;
+    const uint16_t* qn;    // q_norm, k_norm (bf16 [hd])
+    const uint16_t* kn;
+    float eps;
+    const float* rope_tab;
+    int pos_base;
+    float scale;
+    uint8_t* o_frag;
+};
+hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st);
+
+struct AttnArgs {
+    QPrep qp;
+    int nq;                // query rows (<= 16)
+    const void* kc;        // cache keys / values: row j at kc + j*kv_ld (element type by kv_dtype)
+    const void* vc;
+    int kv_ld;
+    int kv_dtype;          // 0 f16, 1 f32
+    int key_lo, key_hi;    // cache rows [key_lo, key_hi)
+    const float* kx;       // extra keys / values (f32 rows [nx][x_ld]) after the cache rows
+    const float* vx;
+    int nx, x_ld;
+    int heads, kv_heads, hd;
+    int causal_base;       // >= 0: query t sees cache row j only if j <= causal_base + t
+    float scale;
+    int chunk;             // keys per work-group
+    int nchunks;
+    float* part;           // [heads][nchunks][nq][hd + 2]: unnormalised o, running max, sum
+};
+hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st);
+
+struct MergeArgs {
+    const float* part;
+    int heads, nchunks, nq, hd;
+    const float* gate;     // optional: o *= sigmoid(gate[t*gate_ld + h*gate_hs + d])
+    int gate_ld, gate_hs;
+    uint8_t* o_frag;       // o row t, k = h*hd + d
+};
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st);
+
+// K/V rows -> cache: per group (layer) g: k rows from kbuf[g] (head RMSNorm + RoPE), v rows from vbuf[g];
+// written at cache rows start .. start+n-1 as f16 or f32.
+struct KVFinalArgs {
+    const float* stage;    // [2*layers][n][D]: k of layer l at group 2l, v at 2l+1
+    int n, D, heads, hd, layers;
+    const uint16_t* knorm[16];     // per layer bf16 [hd] head-norm weight of K (null: no norm, no RoPE)
+    float eps;
+    const float* rope_tab;
+    int rope_dims;
+    int start;
+    void* cache;           // layer l: K at l*2*max_ctx*D, V at (2l+1)*max_ctx*D (elements)
+    int max_ctx;
+    int kv_dtype;
+};
+hipError_t launch_kv_final(const KVFinalArgs& a, hipStream_t st);
+
+// MTP: q/k head-norm + NEOX RoPE, K/V cache write at pos0 + m; q written to qout [M][NH*HD].
+struct MtpPrepArgs {
+    const float* qf; const float* kt; const float* vt;
+    int M, NH, NKV, HD, rot;
+    const float* qn; const float* kn;
+    float eps;
+    const float* rope_tab;
+    int pos0;
+    float* qout;
+    float* kc; float* vc;  // [max_ctx][NKV*HD]
+};
+hipError_t launch_mtp_prep(const MtpPrepArgs& a, hipStream_t st);
+
+// ── K5: lm_head + argmax ───────────────────────────────────────────────────────────────────────
+struct LmArgs {
+    const void* E;         // bf16 [V][K] or Q8_0 codes
+    const void* Ed;        // Q8_0 scales or null
+    const uint8_t* X;      // fragments of the rows
+    int V, K, T;
+    unsigned long long* best;  // [16] packed (value, index) maxima, zero between calls
+    unsigned int* counter;     // work-groups done, zero between calls
+    int32_t* tokens;
+    float* logits;         // optional [T][V]
+    int n_wg;
+};
+hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
+
+// ── K2: MFMA prefill GEMM (f16 operands, f32 accumulate) ──────────────────────────────────────
+// C[r][n] = sum_k A[r][k] B[n][k]; A f32 or f16 rows, B bf16 weights converted to f16 on the way into LDS.
+enum PrefillEpi {
+    PF_F32 = 0,     // C f32 [rows][ld]
+    PF_CACHE_K = 1, // head RMSNorm + RoPE at position start + r, stored to the cache (f16/f32)
+    PF_CACHE_V = 2  // stored to the cache
+};
+struct PrefillGroup {
+    const void* A;         // this group's A rows (null: PrefillArgs.A)
+    const uint16_t* B;     // bf16 [N][K]
+    const uint16_t* knorm; // bf16 [hd] (PF_CACHE_K)
+    void* out;             // f32 C or the cache row 0 of this layer's K or V
+    int epi;
+    int tile_begin;
+};
+#define PF_MAX_GROUPS 12
+struct PrefillArgs {
+    PrefillGroup g[PF_MAX_GROUPS];
+    int ngroups;
+    const void* A;         // [rows][K]
+    int a_f32;             // 1: A is f32, 0: A is f16
+    int rows, N, K, ld;
+    int hd;
+    float eps;
+    const float* rope_tab;
+    int rope_dims;
+    int start;
+    int kv_dtype;
+    int m_tiles, n_tiles;
+};
+hipError_t launch_prefill(const PrefillArgs& a, int n_workgroups, hipStream_t st);
+
+// Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context).
+hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out,
+                          hipStream_t st);

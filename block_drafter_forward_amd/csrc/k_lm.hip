@@ -1,0 +1,197 @@
+// k_lm.hip — K5: the lm_head GEMM fused with a per-row argmax.
+//
+// z[t][v] = sum_k X[t][k] E[v][k] over the whole vocabulary, for the T <= 16 rows of one draft, and
+// tok[t] = argmax_v z[t][v] (lowest index on ties). The flow-map page runs the target's verify-block matvec
+// ("one read of the table") and then argmaxRows over materialised logits; here the logits never leave registers:
+//   * a wave owns 32 vocabulary rows (two 16-row A tiles of v_mfma_f32_16x16x32_bf16) over the full K and streams
+//     them once from HBM (non-temporal, software-pipelined in chunks of 4 k-steps); the 16 draft rows are the MFMA's
+//     N, as hi/lo bf16 fragments (read through L2 by every wave);
+//   * the wave's best (value, index) per row is reduced across lanes with shuffles, then across the work-group's
+//     4 waves in LDS, then across work-groups with one 64-bit atomicMax per row on an order-preserving key
+//     (value bits, ~index), so ties resolve to the lowest index independent of scheduling;
+//   * a one-work-group finalize kernel turns the keys into token ids and clears them for the next call.
+// Q8_0 tables (the MTP head's lm_head): each k-step is one Q8_0 block; codes go exactly through the bf16 MFMA and
+// the per-row scale multiplies the step's product.
+#include "fm_device.h"
+#include "fm_kernels.h"
+
+namespace {
+
+constexpr int CH = 4;   // k-steps per pipeline stage
+
+__device__ __forceinline__ uint32_t nt32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint4 ldg_nt(const void* p) {
+    const uint32_t* q = (const uint32_t*)p;
+    return make_uint4(nt32(q), nt32(q + 1), nt32(q + 2), nt32(q + 3));
+}
+__device__ __forceinline__ uint2 ldg_nt2(const void* p) {
+    const uint32_t* q = (const uint32_t*)p;
+    return make_uint2(nt32(q), nt32(q + 1));
+}
+__device__ __forceinline__ bf16x8_t as_bf(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint4 i8x8_bf16(uint2 c) {
+    uint32_t w[2] = {c.x, c.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int b0 = ((int)(w[i] << (24 - 16 * j))) >> 24;
+            int b1 = ((int)(w[i] << (16 - 16 * j))) >> 24;
+            o[2 * i + j] = (__float_as_uint((float)b0) >> 16) | (__float_as_uint((float)b1) & 0xffff0000u);
+        }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int WT>
+struct Stage {
+    uint4 a[2][CH];      // bf16 weights, or (WT == 1) codes in .x/.y
+    uint4 bh[CH], bl[CH];
+    float sc[2][CH][4];
+};
+
+template <int WT>
+__device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v0, int s, int r, int g, int lane,
+                                           bool tile1) {
+    const int K = a.K;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const uint8_t* xb = a.X + (size_t)(s + i) * FRAG_STEP_BYTES + lane * 16;
+        st.bh[i] = *(const uint4*)xb;
+        st.bl[i] = *(const uint4*)(xb + 1024);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        if (n == 1 && !tile1) continue;
+        const size_t row = (size_t)(v0 + 16 * n + r);
+        if constexpr (WT == 0) {
+            const uint16_t* E = (const uint16_t*)a.E + row * K + (size_t)s * 32 + g * 8;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) st.a[n][i] = ldg_nt(E + i * 32);
+        } else {
+            const int8_t* C = (const int8_t*)a.E + row * K + (size_t)s * 32 + g * 8;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                uint2 c = ldg_nt2(C + i * 32);
+                st.a[n][i] = make_uint4(c.x, c.y, 0, 0);
+            }
+            const int nb = K >> 5;
+            const uint16_t* Dd = (const uint16_t*)a.Ed;
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    st.sc[n][i][j] = f16_to_f32(Dd[(size_t)(v0 + 16 * n + 4 * g + j) * nb + s + i]);
+        }
+    }
+}
+
+template <int WT>
+__device__ __forceinline__ void compute_stage(const Stage<WT>& st, f32x4_t* acc, bool tile1) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            if (n == 1 && !tile1) continue;
+            if constexpr (WT == 0) {
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(st.a[n][i]), as_bf(st.bh[i]), acc[n], 0, 0, 0);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(st.a[n][i]), as_bf(st.bl[i]), acc[n], 0, 0, 0);
+            } else {
+                const bf16x8_t A = as_bf(i8x8_bf16(make_uint2(st.a[n][i].x, st.a[n][i].y)));
+                f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf(st.bh[i]), p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf(st.bl[i]), p, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[n][j] += st.sc[n][i][j] * p[j];
+            }
+        }
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(256) void lm_argmax_kernel(LmArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int v0 = (blockIdx.x * 4 + wave) * 32;
+    const bool active = v0 < a.V;
+    const bool tile1 = v0 + 16 < a.V;
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    if (active) {
+        const int nsteps = a.K >> 5;
+        Stage<WT> s0, s1;
+        load_stage<WT>(s0, a, v0, 0, r, g, lane, tile1);
+        for (int s = 0; s < nsteps; s += 2 * CH) {
+            if (s + CH < nsteps) load_stage<WT>(s1, a, v0, s + CH, r, g, lane, tile1);
+            compute_stage<WT>(s0, acc, tile1);
+            if (s + 2 * CH < nsteps) load_stage<WT>(s0, a, v0, s + 2 * CH, r, g, lane, tile1);
+            if (s + CH < nsteps) compute_stage<WT>(s1, acc, tile1);
+        }
+    }
+    // lane holds z[t = lane % 16][v0 + 16 n + 4 g + j]
+    const int t = lane & 15;
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    if (active) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            if (n == 1 && !tile1) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int v = v0 + 16 * n + 4 * g + j;
+                const float z = acc[n][j];
+                if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
+                if (z > best) { best = z; bidx = v; }   // v increases with (n, j): first max kept
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        const float ob = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bidx, o, 64);
+        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+    }
+    __shared__ float wb[4][16];
+    __shared__ int wi[4][16];
+    if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
+    __syncthreads();
+    if (threadIdx.x < 16 && threadIdx.x < a.T) {
+        const int tt = threadIdx.x;
+        float b = wb[0][tt];
+        int bi = wi[0][tt];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (wb[w][tt] > b || (wb[w][tt] == b && wi[w][tt] < bi)) { b = wb[w][tt]; bi = wi[w][tt]; }
+        if (bi != 0x7fffffff) {
+            const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
+            atomicMax(&a.best[tt], key);
+        }
+    }
+}
+
+__global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tokens) {
+    const int t = threadIdx.x;
+    if (t < T) {
+        const unsigned long long k = best[t];
+        tokens[t] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
+        best[t] = 0ull;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
+    if ((a.K >> 5) % (2 * CH) != 0 || a.T > 16) return hipErrorInvalidValue;
+    const int nwg = (a.V + 127) / 128;
+    if (wtype == 0) lm_argmax_kernel<0><<<nwg, 256, 0, st>>>(a);
+    else lm_argmax_kernel<1><<<nwg, 256, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    lm_finalize_kernel<<<1, 64, 0, st>>>(a.best, a.T, a.tokens);
+    return hipGetLastError();
+}

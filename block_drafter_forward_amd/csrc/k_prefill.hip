@@ -1,0 +1,208 @@
+// k_prefill.hip — K2: the MFMA GEMM of context prefill, C[r][n] = sum_k A[r][k] B[n][k].
+//
+// The one truly dense contraction of the path: the fusion of many context rows (fc / W_c over the concatenated
+// taps, flashmap_drafter.js extendContext; module-dflash.ts #buildContext) and the per-layer K/V projections of the
+// fused rows. Operands are f16 on v_mfma_f32_16x16x32_f16 with f32 accumulation: the f32 taps are rounded to f16 on
+// their way into LDS (2^-11 relative, four times finer than bf16), the bf16 weights are widened to f16 exactly (up
+// to f16's subnormal range, |error| <= 2^-25). Tiles: 128 x 128 per work-group of 4 waves (2 x 2, 64 x 64 each,
+// 16 accumulators of 16x16), k-stages of 32 double-buffered in LDS with a 16-byte row pad (conflict-free fragment
+// reads), the next stage's global loads in flight while the current one computes. Work-groups are remapped so
+// each XCD owns a contiguous run of tiles (consecutive n-tiles of the same row block share their A rows in that
+// XCD's L2).
+// Epilogues: f32 rows; a cache store (f16 / f32) at rows start + r; or, for K, the per-head RMSNorm over the tile's
+// columns (a head is 64 or 128 columns of the 128-wide tile) and interleaved RoPE at position start + r before the
+// store -- the page's headNormRope + kvWrite, fused.
+#include "fm_device.h"
+#include "fm_kernels.h"
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 32, LDP = BK + 8;
+
+__device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+}
+
+template <int AF32>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
+    __shared__ float nred[2][BM];
+
+    int lin = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    int gi = 0;
+#pragma unroll 1
+    for (int i = 1; i < a.ngroups; ++i)
+        if (lin >= a.g[i].tile_begin) gi = i;
+    const PrefillGroup& G = a.g[gi];
+    const int local = lin - G.tile_begin;
+    const int mt = local / a.n_tiles, nt = local - mt * a.n_tiles;
+    const int r0 = mt * BM, n0 = nt * BN;
+    const void* Ap = G.A ? G.A : a.A;
+    const int K = a.K;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int ldrow = tid >> 1, kofs = (tid & 1) * 16;
+    const bool avalid = r0 + ldrow < a.rows;
+
+    float4 ra[4];
+    uint4 rah[2], rb[2];
+    auto gload = [&](int kt) {
+        const int k = kt * BK + kofs;
+        if constexpr (AF32) {
+            if (avalid) {
+                const float4* p = (const float4*)((const float*)Ap + (size_t)(r0 + ldrow) * K + k);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ra[i] = p[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        } else {
+            if (avalid) {
+                const uint4* p = (const uint4*)((const uint16_t*)Ap + (size_t)(r0 + ldrow) * K + k);
+                rah[0] = p[0];
+                rah[1] = p[1];
+            } else {
+                rah[0] = rah[1] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        const uint4* pb = (const uint4*)(G.B + (size_t)(n0 + ldrow) * K + k);
+        rb[0] = pb[0];
+        rb[1] = pb[1];
+    };
+    auto lstore = [&](int buf) {
+        uint4 h0, h1;
+        if constexpr (AF32) {
+            h0 = make_uint4(pack_f16x2(ra[0].x, ra[0].y), pack_f16x2(ra[0].z, ra[0].w),
+                            pack_f16x2(ra[1].x, ra[1].y), pack_f16x2(ra[1].z, ra[1].w));
+            h1 = make_uint4(pack_f16x2(ra[2].x, ra[2].y), pack_f16x2(ra[2].z, ra[2].w),
+                            pack_f16x2(ra[3].x, ra[3].y), pack_f16x2(ra[3].z, ra[3].w));
+        } else {
+            h0 = rah[0];
+            h1 = rah[1];
+        }
+        *(uint4*)&As[buf][ldrow][kofs] = h0;
+        *(uint4*)&As[buf][ldrow][kofs + 8] = h1;
+        uint32_t w[8] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w, rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = pack_f16x2(bf16_lo(w[i]), bf16_hi(w[i]));
+        *(uint4*)&Bs[buf][ldrow][kofs] = make_uint4(o[0], o[1], o[2], o[3]);
+        *(uint4*)&Bs[buf][ldrow][kofs + 8] = make_uint4(o[4], o[5], o[6], o[7]);
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        f16x8_t af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = as_f16x8(*(const uint4*)&As[buf][wm * 64 + i * 16 + fr][fk]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bfr[j] = as_f16x8(*(const uint4*)&Bs[buf][wn * 64 + j * 16 + fr][fk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        if (kt + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // acc[i][j][q] = C[r0 + wm*64 + 16 i + 4 (lane/16) + q][n0 + wn*64 + 16 j + lane%16]
+    const int rq = 4 * (lane >> 4), cl = lane & 15;
+    if (G.epi == PF_CACHE_K && G.knorm) {
+        const int hd = a.hd;
+        float ssq[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s += acc[i][j][q] * acc[i][j][q];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+                ssq[i][q] = s;
+            }
+        if (hd == 128) {
+            if (cl == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) nred[wn][wm * 64 + 16 * i + rq + q] = ssq[i][q];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = wm * 64 + 16 * i + rq + q;
+                    ssq[i][q] = nred[0][rl] + nred[1][rl];
+                }
+        }
+        const int half = a.rope_dims >> 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + wm * 64 + 16 * i + rq + q;
+                const float rs = 1.f / sqrtf(ssq[i][q] / (float)hd + a.eps);
+                const int pos = a.start + (r < a.rows ? r : 0);
+                const float* tr = a.rope_tab + (size_t)pos * a.rope_dims;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn * 64 + 16 * j + cl;
+                    const int d = n % hd;
+                    const float v = acc[i][j][q] * rs * bf16_to_f32(G.knorm[d]);
+                    const float p = __shfl_xor(v, 1, 64);
+                    const float c = tr[d >> 1], s = tr[half + (d >> 1)];
+                    acc[i][j][q] = (d & 1) ? v * c + p * s : v * c - p * s;
+                }
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + wm * 64 + 16 * i + rq + q;
+            if (r >= a.rows) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + wn * 64 + 16 * j + cl;
+                const float v = acc[i][j][q];
+                if (G.epi == PF_F32) {
+                    ((float*)G.out)[(size_t)r * a.ld + n] = v;
+                } else {
+                    const size_t off = (size_t)(a.start + r) * a.ld + n;
+                    if (a.kv_dtype == 0) ((uint16_t*)G.out)[off] = f32_to_f16(v);
+                    else ((float*)G.out)[off] = v;
+                }
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int nwg, hipStream_t st) {
+    if (a.K % BK || a.N % BN) return hipErrorInvalidValue;
+    if (a.a_f32) prefill_kernel<1><<<nwg, 256, 0, st>>>(a);
+    else prefill_kernel<0><<<nwg, 256, 0, st>>>(a);
+    return hipGetLastError();
+}

@@ -1,0 +1,264 @@
+// k_rows.hip — K3 row kernels and K7 small kernels.
+//
+// rows_kernel: one work-group per activation row. It finishes the previous phase (base + gate * (sum of split-K
+// partial slabs + bias): the gated residual of the flow-map page's gateAdd, or a plain residual), optionally keeps
+// the updated residual stream, then normalises the row -- adaLN LayerNorm-modulation (lnMod) or RMSNorm
+// (rmsRows / WG_NORM) -- and stores it as the hi/lo bf16 fragments the next skinny GEMM reads. Values stay in
+// registers between the passes; reductions are wave shuffles plus one LDS exchange, in a fixed order.
+#include "fm_device.h"
+#include "fm_kernels.h"
+
+namespace {
+
+template <int NS>
+__global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
+    const int t = blockIdx.x;
+    const int D = a.D;
+    const int nslot = D >> 3;
+    __shared__ float red[4];
+    float v[NS][8];
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int slot = threadIdx.x + j * 256;
+        if (slot < nslot) {
+            const int i0 = slot * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = i0 + e;
+                float base = 0.f;
+                if (a.init) base = a.init[i];
+                else if (a.in_rows) base = a.in_rows[(size_t)t * a.in_ld + i];
+                else if (a.x) base = a.x[(size_t)t * D + i];
+                float u = 0.f;
+                for (int s = 0; s < a.S; ++s) u += a.part[(size_t)s * a.part_stride + (size_t)t * D + i];
+                if (a.bias) u += bf16_to_f32(a.bias[i]);
+                const float gv = a.gate ? a.gate[i] : 1.f;
+                const float val = base + gv * u;
+                v[j][e] = val;
+                sum += val;
+            }
+            if (a.x) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a.x[(size_t)t * D + i0 + e] = v[j][e];
+            }
+            if (a.debug_x) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a.debug_x[(size_t)t * D + i0 + e] = v[j][e];
+            }
+        }
+    }
+    if (a.norm == ROW_NONE && !a.frag_out && !a.f32_out) return;
+
+    float r = 1.f, mean = 0.f;
+    if (a.norm == ROW_LN_MOD) {
+        mean = block_sum256(sum, red) / (float)D;
+        float q = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            if (threadIdx.x + j * 256 < nslot)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { const float d = v[j][e] - mean; q += d * d; }
+        const float var = block_sum256(q, red) / (float)D;
+        r = 1.f / sqrtf(var + a.eps);
+    } else if (a.norm == ROW_RMS) {
+        float q = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            if (threadIdx.x + j * 256 < nslot)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q += v[j][e] * v[j][e];
+        const float ms = block_sum256(q, red) / (float)D;
+        r = 1.f / sqrtf(ms + a.eps);
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int slot = threadIdx.x + j * 256;
+        if (slot < nslot) {
+            const int i0 = slot * 8;
+            float h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = i0 + e;
+                if (a.norm == ROW_LN_MOD) h[e] = (v[j][e] - mean) * r * (1.f + a.scale[i]) + a.shift[i];
+                else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * (a.w_bf16 ? bf16_to_f32(a.w_bf16[i]) : a.w_f32[i]);
+                else h[e] = v[j][e];
+            }
+            if (a.frag_out) frag_store8(a.frag_out, t, a.frag_koff + i0, h);
+            if (a.f32_out) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a.f32_out[(size_t)t * a.out_ld + i0 + e] = h[e];
+            }
+        }
+    }
+}
+
+__global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag) {
+    const int t = blockIdx.y;
+    const int slot = blockIdx.x * 256 + threadIdx.x;
+    if (slot * 8 >= K) return;
+    float v[8];
+    const float* p = x + (size_t)t * ld + slot * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = p[e];
+    frag_store8(frag, t, slot * 8, v);
+}
+
+// Token ids outside [0, V) are clamped into the table (a device-side id cannot be validated by the host).
+__device__ __forceinline__ size_t clamp_row(int32_t id, int V) { return (size_t)(id < 0 ? 0 : (id >= V ? V - 1 : id)); }
+
+__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag) {
+    const int slot = blockIdx.x * 256 + threadIdx.x;
+    if (slot * 8 >= K) return;
+    const size_t row = clamp_row(idx[0], V);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(E[row * K + slot * 8 + e]);
+    frag_store8(frag, 0, slot * 8, v);
+}
+
+__global__ void gather_f32_kernel(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add,
+                                  float* out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= K) return;
+    const size_t row = clamp_row(idx[0], V);
+    float v = bf16_to_f32(E[row * K + i]);
+    if (add) v += bf16_to_f32(add[i]);
+    out[i] = v;
+}
+
+__global__ void colmean_stage1(const uint16_t* E, int V, int H, int R, float* scratch) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= H) return;
+    const int per = (V + R - 1) / R;
+    const int r0 = blockIdx.y * per, r1 = min(V, r0 + per);
+    float s = 0.f;
+    for (int r = r0; r < r1; ++r) s += bf16_to_f32(E[(size_t)r * H + col]);
+    scratch[(size_t)blockIdx.y * H + col] = s;
+}
+
+__global__ void colmean_stage2(const float* scratch, int V, int H, int R, float* out) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= H) return;
+    double s = 0.0;
+    for (int r = 0; r < R; ++r) s += (double)scratch[(size_t)r * H + col];
+    out[col] = (float)(s / (double)V);
+}
+
+__global__ void rope_table_kernel(float* tab, int P, int rdim, double theta) {
+    const int half = rdim >> 1;
+    const size_t n = (size_t)P * half;
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= n) return;
+    const int p = (int)(id / half), i = (int)(id % half);
+    const double a = (double)p * pow(theta, -2.0 * (double)i / (double)rdim);
+    tab[(size_t)p * rdim + i] = (float)cos(a);
+    tab[(size_t)p * rdim + half + i] = (float)sin(a);
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+template <int NS>
+__global__ __launch_bounds__(256) void rms_f16_kernel(const float* x, int D, const uint16_t* w, float eps,
+                                                      uint16_t* out) {
+    const int t = blockIdx.x;
+    const int nslot = D >> 3;
+    __shared__ float red[4];
+    float v[NS][8];
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int slot = threadIdx.x + j * 256;
+        if (slot < nslot) {
+            const float4* p = (const float4*)(x + (size_t)t * D + slot * 8);
+            float4 a0 = p[0], a1 = p[1];
+            v[j][0] = a0.x; v[j][1] = a0.y; v[j][2] = a0.z; v[j][3] = a0.w;
+            v[j][4] = a1.x; v[j][5] = a1.y; v[j][6] = a1.z; v[j][7] = a1.w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q += v[j][e] * v[j][e];
+        }
+    }
+    const float r = 1.f / sqrtf(block_sum256(q, red) / (float)D + eps);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int slot = threadIdx.x + j * 256;
+        if (slot < nslot) {
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = slot * 8 + 2 * e;
+                o[e] = (uint32_t)f32_to_f16(v[j][2 * e] * r * bf16_to_f32(w[i])) |
+                       ((uint32_t)f32_to_f16(v[j][2 * e + 1] * r * bf16_to_f32(w[i + 1])) << 16);
+            }
+            *(uint4*)(out + (size_t)t * D + slot * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
+    const int nslot = a.D / 8;
+    const int ns = (nslot + 255) / 256;
+    dim3 grid(a.T), block(256);
+    switch (ns) {
+    case 1: rows_kernel<1><<<grid, block, 0, st>>>(a); break;
+    case 2: rows_kernel<2><<<grid, block, 0, st>>>(a); break;
+    case 3: rows_kernel<3><<<grid, block, 0, st>>>(a); break;
+    case 4: rows_kernel<4><<<grid, block, 0, st>>>(a); break;
+    case 5: rows_kernel<5><<<grid, block, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st) {
+    dim3 grid((K / 8 + 255) / 256, T);
+    f32_to_frag_kernel<<<grid, 256, 0, st>>>(x, ld, K, frag);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, hipStream_t st) {
+    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_f32(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add, float* out,
+                             hipStream_t st) {
+    gather_f32_kernel<<<(K + 255) / 256, 256, 0, st>>>(E, V, K, idx, add, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_colmean(const uint16_t* E, int V, int H, float* scratch, int R, float* out, hipStream_t st) {
+    colmean_stage1<<<dim3((H + 255) / 256, R), 256, 0, st>>>(E, V, H, R, scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    colmean_stage2<<<(H + 255) / 256, 256, 0, st>>>(scratch, V, H, R, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* tab, int P, int rdim, double theta, hipStream_t st) {
+    const size_t n = (size_t)P * (rdim / 2);
+    rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(tab, P, rdim, theta);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    fill_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, hipStream_t st) {
+    const int ns = (D / 8 + 255) / 256;
+    switch (ns) {
+    case 1: rms_f16_kernel<1><<<n, 256, 0, st>>>(x, D, w, eps, out); break;
+    case 2: rms_f16_kernel<2><<<n, 256, 0, st>>>(x, D, w, eps, out); break;
+    case 3: rms_f16_kernel<3><<<n, 256, 0, st>>>(x, D, w, eps, out); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}

@@ -1,0 +1,220 @@
+// k_skinny.hip — K1: skinny-T (T <= 16) weight-streaming GEMM on the bf16 matrix cores of gfx950.
+//
+// Computes Y[t][m] = sum_k X[t][k] W[m][k] for the draft's 16 slots (or fewer rows), the product the flow-map page's
+// gemvT17 / gemvT1 kernels and the MTP page's WG_Q8 compute: every weight byte is read from HBM exactly once.
+// Design for CDNA4:
+//   * the weight tile (16 rows x 32 k, 1 KB) is loaded straight into the A operand of v_mfma_f32_16x16x32_bf16:
+//     lane l reads 16 contiguous bytes of row l % 16, so a wave reads 16 rows x 64 contiguous bytes per step;
+//     loads are non-temporal (streamed, never reused);
+//   * the activations are the B operand (16 slots = the MFMA's N), pre-split into bf16 hi + lo fragments by their
+//     producer, so one k-step is two MFMAs and the f32 activations keep ~17 significant bits;
+//   * a work-group is 4 waves on one 16-row tile, each wave a contiguous quarter of the k-range, streamed in stages
+//     of 4 k-steps with the next stage's loads in flight; the four 16x16 partial tiles are summed in LDS in a fixed
+//     order (deterministic), then the epilogue runs per element;
+//   * k is split across S work-groups when M alone gives too few work-groups to fill 256 CUs; the S partial slabs
+//     are summed by the consumer kernel in a fixed order.
+// Q8_0 weights (int8 codes + one f16 scale per 32 codes): a k-step is exactly one Q8_0 block, so the codes go
+// through the MFMA exactly (int8 is exact in bf16) and each row's scale multiplies that step's partial product.
+#include "fm_device.h"
+#include "fm_kernels.h"
+
+namespace {
+
+__device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
+    uint4 v;
+    v.x = __builtin_nontemporal_load(&((const uint32_t*)p)[0]);
+    v.y = __builtin_nontemporal_load(&((const uint32_t*)p)[1]);
+    v.z = __builtin_nontemporal_load(&((const uint32_t*)p)[2]);
+    v.w = __builtin_nontemporal_load(&((const uint32_t*)p)[3]);
+    return v;
+}
+__device__ __forceinline__ uint2 ldg_nt2(const uint2* p) {
+    uint2 v;
+    v.x = __builtin_nontemporal_load(&((const uint32_t*)p)[0]);
+    v.y = __builtin_nontemporal_load(&((const uint32_t*)p)[1]);
+    return v;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 8 int8 codes -> 8 bf16 (exact).
+__device__ __forceinline__ uint4 i8x8_to_bf16x8(uint2 c) {
+    uint32_t w[2] = {c.x, c.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int b0 = ((int)(w[i] << (24 - 16 * j))) >> 24;
+            int b1 = ((int)(w[i] << (16 - 16 * j))) >> 24;
+            uint32_t f0 = __float_as_uint((float)b0) >> 16;
+            uint32_t f1 = __float_as_uint((float)b1) & 0xffff0000u;
+            o[2 * i + j] = f0 | f1;
+        }
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+constexpr int SKC = 4;   // k-steps per pipeline stage
+
+template <int NT, int WT>
+struct SkStage {
+    uint4 a[NT][SKC];    // bf16 weights; Q8_0 codes in .x/.y
+    uint4 bh[SKC], bl[SKC];
+    float sc[NT][SKC][4];
+};
+
+template <int NT, int WT>
+__device__ __forceinline__ void sk_load(SkStage<NT, WT>& st, const SkinnyGroup& G, int K, int m0, int s, int n_left,
+                                        int r, int g, int lane) {
+    const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
+#pragma unroll
+    for (int i = 0; i < SKC; ++i) {
+        if (i < n_left) {
+            st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
+            st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        if constexpr (WT == SKW_BF16) {
+            const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2);
+            const uint4* wp = (const uint4*)(W + (size_t)(m0 + r) * K + (size_t)s * 32 + g * 8);
+#pragma unroll
+            for (int i = 0; i < SKC; ++i)
+                if (i < n_left) st.a[n][i] = ldg_nt(wp + i * 4);
+        } else {
+            const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2);
+            const uint16_t* Dd = (const uint16_t*)(n == 0 ? G.Wd : G.W2d);
+            const uint2* cp = (const uint2*)(C + (size_t)(m0 + r) * K + (size_t)s * 32 + g * 8);
+            const int nb = K >> 5;
+#pragma unroll
+            for (int i = 0; i < SKC; ++i) {
+                if (i < n_left) {
+                    const uint2 c = ldg_nt2(cp + i * 4);
+                    st.a[n][i] = make_uint4(c.x, c.y, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) st.sc[n][i][j] = f16_to_f32(Dd[(size_t)(m0 + 4 * g + j) * nb + s + i]);
+                }
+            }
+        }
+    }
+}
+
+template <int NT, int WT>
+__device__ __forceinline__ void sk_compute(const SkStage<NT, WT>& st, f32x4_t* acc, int n_left) {
+#pragma unroll
+    for (int i = 0; i < SKC; ++i) {
+        if (i >= n_left) continue;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            if constexpr (WT == SKW_BF16) {
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[n][i]), as_bf16x8(st.bh[i]), acc[n], 0, 0, 0);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[n][i]), as_bf16x8(st.bl[i]), acc[n], 0, 0, 0);
+            } else {
+                const bf16x8_t A = as_bf16x8(i8x8_to_bf16x8(make_uint2(st.a[n][i].x, st.a[n][i].y)));
+                f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bh[i]), p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bl[i]), p, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[n][j] += st.sc[n][i][j] * p[j];
+            }
+        }
+    }
+}
+
+template <int NT, int WT>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
+    const int bid = blockIdx.x;
+    int gi = 0;
+#pragma unroll 1
+    for (int i = 1; i < a.ngroups; ++i)
+        if (bid >= a.g[i].tile_begin) gi = i;
+    const SkinnyGroup& G = a.g[gi];
+    const int local = bid - G.tile_begin;
+    const int rt = local / a.S;
+    const int split = local - rt * a.S;
+    const int m0 = rt * 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int KW = a.KW;
+    const int s0 = (split * 4 + wave) * KW;   // first k-step of this wave
+    const int r = lane & 15, g = lane >> 4;
+    const int K = a.K;
+
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // software pipeline over stages of SKC k-steps: stage i+1's loads are in flight while stage i computes
+    SkStage<NT, WT> st0, st1;
+    sk_load<NT, WT>(st0, G, K, m0, s0, KW, r, g, lane);
+    for (int s = 0; s < KW; s += 2 * SKC) {
+        if (s + SKC < KW) sk_load<NT, WT>(st1, G, K, m0, s0 + s + SKC, KW - s - SKC, r, g, lane);
+        sk_compute<NT, WT>(st0, acc, KW - s);
+        if (s + 2 * SKC < KW) sk_load<NT, WT>(st0, G, K, m0, s0 + s + 2 * SKC, KW - s - 2 * SKC, r, g, lane);
+        if (s + SKC < KW) sk_compute<NT, WT>(st1, acc, KW - s - SKC);
+    }
+
+    // ── sum the four waves' tiles (fixed order) ──
+    __shared__ f32x4_t red[NT][4][64];
+    __shared__ float tile[16][17];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) red[n][wave][lane] = acc[n];
+    __syncthreads();
+    const int el = threadIdx.x & 63, rr = threadIdx.x >> 6;
+    float v[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+        v[n] = ((red[n][0][el][rr] + red[n][1][el][rr]) + red[n][2][el][rr]) + red[n][3][el][rr];
+    const int ml = 4 * (el >> 4) + rr;   // row of the tile
+    const int t = el & 15;               // activation row (slot)
+    const int m = m0 + ml;
+
+    switch (a.mode) {
+    case SK_F32:
+        if (t < a.T) {
+            float b = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
+            ((float*)G.out)[(size_t)t * G.ld + m] = v[0] + b;
+        }
+        return;
+    case SK_PARTIAL:
+        if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)t * G.ld + m] = v[0];
+        return;
+    default: break;
+    }
+    float o;
+    if (a.mode == SK_FRAG_GELU) {
+        float b = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
+        o = gelu_erf(v[0] + b);
+    } else if (a.mode == SK_FRAG_GEGLU) {
+        o = gelu_tanh(v[0]) * v[NT - 1];
+    } else {
+        o = silu(v[0]) * v[NT - 1];
+    }
+    tile[t][ml] = o;
+    __syncthreads();
+    if (threadIdx.x < 32) {
+        const int tt = threadIdx.x >> 1, h = threadIdx.x & 1;
+        if (tt < a.T) {
+            float vals[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vals[e] = tile[tt][8 * h + e];
+            frag_store8((uint8_t*)G.out, tt, m0 + 8 * h, vals);
+        }
+    }
+}
+
+template <int NT, int WT>
+hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
+    if (a.KW < 1) return hipErrorInvalidValue;
+    skinny_kernel<NT, WT><<<nwg, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st) {
+    const bool glu = (a.mode == SK_FRAG_GEGLU || a.mode == SK_FRAG_SWIGLU);
+    if (wtype == SKW_BF16) return glu ? launch_nt<2, SKW_BF16>(a, nwg, st) : launch_nt<1, SKW_BF16>(a, nwg, st);
+    return glu ? launch_nt<2, SKW_Q8_0>(a, nwg, st) : launch_nt<1, SKW_Q8_0>(a, nwg, st);
+}

@@ -1,0 +1,165 @@
+/*
+ * fm.h — C ABI of the MI355X (gfx950) block drafter forward.
+ *
+ * One drafter handle drives three calls, in the order a speculative-decoding loop makes them:
+ *
+ *   fm_context_append   tapped target hidden states -> fused context -> per-layer K/V rows in the cache
+ *   fm_draft_block      one single-pass block forward (16 flow-map slots, gamma KV-injection slots or M MTP rows)
+ *   fm_lm_argmax        lm_head GEMM fused with a per-row argmax
+ *
+ * Sources (page title, unit on the page):
+ *   flow-map   "diskformer 0.5.4 -> 0.6.6", engines/flashmap_drafter.js: FlashMapDrafter.extendContext,
+ *              FlashMapDrafter.draft, the file header
+ *   KV-inject  "mlx-bun 0.4.0 -> 1.0.0", src/spec/dspark/module-dflash.ts: projectContextRows, forwardRows,
+ *              #backbone / #layer (DSpark Eq 2 and Eq 3)
+ *   MTP        "diskformer 0.5.3 -> 0.6.4", engines/ternary_bonsai_2_mtp.js: MTPHead.forward, the file header
+ *
+ * Conventions
+ *   - Every data pointer is DEVICE memory owned by the caller (weights, caches, workspace, inputs, outputs). The
+ *     library never allocates or frees device memory and never synchronises a stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only enqueues work on it;
+ *     results are valid once the caller synchronises that stream.
+ *   - Every argument is validated on the host BEFORE anything is enqueued; on error nothing is launched and the
+ *     call returns a non-zero fm_status with a message in fm_last_error().
+ *   - A handle is not thread-safe; one handle is used from one host thread and one stream at a time.
+ *   - Weights: bf16 matrices row-major [out][in]; Q8_0 matrices as an int8 code array [out][in] plus an f16 scale
+ *     array [out][in/32] (one scale per 32 consecutive codes of a row). Norm weights bf16 (flow-map, KV-inject) or
+ *     f32 (MTP).
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fm_status {
+    FM_OK = 0,
+    FM_E_INVALID = 1,        /* bad argument: null pointer, out-of-range size/position, inconsistent config */
+    FM_E_CONTEXT_FULL = 2,   /* the append (or draft) would run past max_ctx */
+    FM_E_HIP = 3,            /* a HIP runtime call failed (message holds hipGetErrorString) */
+    FM_E_UNSUPPORTED = 4,    /* a config combination this build does not implement */
+    FM_E_MISSING_WEIGHT = 5  /* a weight the variant needs is not in the name table */
+} fm_status;
+
+enum fm_variant { FM_VARIANT_FLOWMAP = 0, FM_VARIANT_KVINJECT = 1, FM_VARIANT_MTP = 2 };
+enum fm_rope { FM_ROPE_NONE = 0, FM_ROPE_INTERLEAVED = 1, FM_ROPE_NEOX = 2 };
+enum fm_mlp { FM_MLP_GELU_ERF = 0, FM_MLP_GEGLU_TANH = 1, FM_MLP_SWIGLU = 2 };
+enum fm_kv_dtype { FM_KV_F16 = 0, FM_KV_F32 = 1 };
+enum fm_wtype { FM_W_BF16 = 0, FM_W_Q8_0 = 1 };
+
+/* Shape and constants of one drafter.
+ *   dim        D, the drafter width (flow-map CFG.dim, DflashConfig.dDraft, MCFG.H)
+ *   heads      query heads; head_dim hd; kv_heads K/V heads (== heads except grouped-query MTP)
+ *   layers     drafter layers (MTP: 1)
+ *   ffn        MLP width (F)
+ *   block      rows per draft: flow-map slots (16), KV-inject gamma, MTP maximum M (8); at most 16
+ *   target_dim Ht, width of a tapped target layer, of the head output and of the lm_head rows
+ *   n_taps     tapped target layers concatenated on the feature axis (flow-map / KV-inject context input)
+ *   vocab      lm_head rows
+ *   max_ctx    cache rows (positions) held per layer
+ *   rope       FM_ROPE_*; rope_dims rotated dims per head (NEOX partial); rope_theta the base
+ *   ln_eps / rms_eps / qk_eps   LayerNorm, RMSNorm and q/k head-norm epsilons
+ *   mlp        FM_MLP_*; kv_dtype FM_KV_* (cache element type); wtype FM_W_* (matrix storage)           */
+typedef struct fm_config {
+    int32_t variant;
+    int32_t dim;
+    int32_t heads;
+    int32_t head_dim;
+    int32_t kv_heads;
+    int32_t layers;
+    int32_t ffn;
+    int32_t block;
+    int32_t target_dim;
+    int32_t n_taps;
+    int32_t vocab;
+    int32_t max_ctx;
+    int32_t rope;
+    int32_t rope_dims;
+    double rope_theta;
+    float ln_eps;
+    float rms_eps;
+    float qk_eps;
+    int32_t mlp;
+    int32_t kv_dtype;
+    int32_t wtype;
+} fm_config;
+
+typedef struct fm_drafter fm_drafter;
+
+/* Bytes of the K/V cache the caller allocates for `cfg` (0 if cfg is invalid).
+ * Flow-map / KV-inject layout: for layer l, K rows at byte offset 2*l*max_ctx*dim*es and V rows right after
+ * (es = 2 for F16, 4 for F32), each [max_ctx][dim]. MTP layout: K [max_ctx][kv_heads*head_dim] f32, then V. */
+size_t fm_kv_bytes(const fm_config* cfg);
+
+/* Bytes of the device workspace the caller allocates for `cfg` (0 if cfg is invalid): activations, split-K
+ * partials, the RoPE table, the zero-noise slot row, argmax scratch. Owned by the caller; reserved for one handle. */
+size_t fm_workspace_bytes(const fm_config* cfg);
+
+/* Create a drafter. `names` / `ptrs` is a table of n_weights (name, device pointer) pairs naming every tensor the
+ * variant needs (the parameter names of the pages; Q8_0 matrices as "<name>.q" codes and "<name>.d" scales).
+ * Borrowed: the library keeps the pointers, never frees them; they must outlive the handle. kv_cache and
+ * workspace must be at least fm_kv_bytes / fm_workspace_bytes and 256-byte aligned.
+ * Enqueues the create-time work on `stream`: clearing the workspace's counters, the RoPE table (angles in f64,
+ * stored f32) and, for the flow-map, the zero-noise slot input x_embed(state_norm(mean row of lm_head)) + bias
+ * (flashmap_drafter.js, init). Context length starts at 0.
+ * Errors: FM_E_INVALID (null pointer, dim % heads, sizes not multiples of 32/256, block > 16 ...),
+ * FM_E_MISSING_WEIGHT, FM_E_UNSUPPORTED, FM_E_HIP. */
+fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* names, const void* const* ptrs,
+                    void* kv_cache, void* workspace, void* stream, fm_drafter** out);
+
+/* Append n rows of tapped features taps[n][n_taps*target_dim] (f32, device) as context positions
+ * start .. start+n-1 (flashmap_drafter.js extendContext; module-dflash.ts projectContextRows):
+ *   flow-map   c = RMSNorm(fc(taps); hidden_norm), per layer K = RoPE(headRMSNorm(k_proj c; k_norm)), V = v_proj c
+ *   KV-inject  c = RMSNorm(W_c taps; ctx_norm), per layer K = W_k RMSNorm(c; attn_norm), V likewise
+ * written to the cache (f16 or f32). Any start <= current length may be rewritten (a rewind); the length becomes
+ * start + n. Errors: FM_E_INVALID (n < 1, start < 0, start > length, null taps, MTP handle),
+ * FM_E_CONTEXT_FULL when start + n + block + 1 > max_ctx (extendContext's own check). */
+fm_status fm_context_append(fm_drafter* d, const float* taps, int32_t n, int32_t start, void* stream);
+
+/* Per-call arguments of a draft. */
+typedef struct fm_block_args {
+    const int32_t* anchor;    /* device: the anchor token id (flow-map, KV-inject); unused by MTP */
+    int32_t pos;              /* flow-map: the anchor's context position (slots sit at pos+1 ..); MTP: pos0 */
+    int32_t rows;             /* MTP: M in [1, block]; ignored by the other variants (block rows) */
+    int32_t kv_lo;            /* MTP: first cache row attended to; ignored otherwise */
+    const float* embed_rows;  /* MTP: device [M][dim] f32 embedding rows e */
+    const float* prev_hidden; /* MTP: device [M][dim] f32 normed trunk rows h */
+    float* debug_layers;      /* nullable device [layers][rows][dim] f32: the residual stream after each layer */
+} fm_block_args;
+
+/* One block forward; writes hidden_out[rows][target_dim] (f32, device), the rows that go to the lm_head.
+ *   flow-map  (flashmap_drafter.js draft): writes the anchor's context slot at `pos` into the cache (side effect),
+ *             then the T zero-noise slots through every DiT layer (adaLN self-attention over the slots,
+ *             cross-attention over cache rows [0, pos], GELU MLP), final modulation and head. Needs pos <= length.
+ *   KV-inject (module-dflash.ts forwardRows / #backbone): block = [tok_proj(E[anchor]) + block_pos[0];
+ *             mask_emb + block_pos[1..]], every layer attends over [cache rows [0, length) ++ block], out_proj.
+ *   MTP       (ternary_bonsai_2_mtp.js MTPHead.forward): rows M at positions pos .. pos+M-1, writes their K/V to
+ *             the cache there, causal grouped-query attention over rows [kv_lo, pos+m]; output shared_head_norm(x).
+ * Anchor ids outside [0, vocab) are clamped into the table (a device-side id cannot be checked by the host).
+ * Errors: FM_E_INVALID (null pointers, pos > length, rows out of range, kv_lo > pos), FM_E_CONTEXT_FULL
+ * (pos + rows (+1) > max_ctx). */
+fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_out, void* stream);
+
+/* tokens[r] = argmax_v (hidden[r] . lm_head[v]) for r < rows (ties to the lowest index), int32 on the device.
+ * logits, if not NULL, receives the full [rows][vocab] f32 logits (a debug path; the fused path never writes them).
+ * Errors: FM_E_INVALID (rows < 1 or > block, null hidden / tokens). */
+fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits,
+                       void* stream);
+
+/* Current context length (rows appended and not rewound), or -1 for a null handle. */
+int32_t fm_context_length(const fm_drafter* d);
+
+/* Free the handle's host-side state; device memory stays with the caller. NULL is ignored. */
+void fm_destroy(fm_drafter* d);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* fm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FM_H */

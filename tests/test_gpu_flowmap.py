@@ -1,0 +1,163 @@
+"""GPU parity of the flow-map drafter (the HIP path through the C ABI) against the float64 oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from inputs import configs, gen
+from oracle import flowmap
+from tests.parity import assert_rows_close, assert_tokens_match, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(f"[gpu-flowmap] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _setup(cfg, seed=0):
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    W = gen.make_weights(cfg, seed)
+    dw = fm.upload_weights(W)
+    d = fm.Drafter(cfg, dw)
+    o = flowmap.FlowMapOracle(cfg, W)
+    return fm, d, o
+
+
+def _cache_rows(d, l, which, r0, r1):
+    return d.kv_layer(l, which)[r0:r1].float().cpu().numpy()
+
+
+def _check_cache(d, o, cfg, r0, r1, what):
+    worst = 0.0
+    for l in range(cfg["layers"]):
+        worst = max(worst, assert_rows_close(_cache_rows(d, l, 0, r0, r1), o.K[l][r0:r1], what=f"{what} K{l}"))
+        worst = max(worst, assert_rows_close(_cache_rows(d, l, 1, r0, r1), o.V[l][r0:r1], what=f"{what} V{l}"))
+    return worst
+
+
+def _draft(fm, d, cfg, anchor, pos, debug=True):
+    T, D, Ht = cfg["block"], cfg["dim"], cfg["target_dim"]
+    a = torch.tensor([anchor], dtype=torch.int32, device="cuda")
+    hid = torch.empty(T, Ht, dtype=torch.float32, device="cuda")
+    dbg = torch.empty(cfg["layers"], T, D, dtype=torch.float32, device="cuda") if debug else None
+    d.fm_draft_block(hid, anchor=a, pos=pos, debug_layers=dbg)
+    tok = torch.empty(T, dtype=torch.int32, device="cuda")
+    logits = torch.empty(T, cfg["vocab"], dtype=torch.float32, device="cuda")
+    d.fm_lm_argmax(hid, T, tok, logits)
+    torch.cuda.synchronize()
+    return (hid.cpu().numpy(), tok.cpu().numpy(), logits.cpu().numpy(),
+            dbg.cpu().numpy() if debug else None)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = configs.get("tiny")
+    _say("tiny: setup")
+    fm, d, o = _setup(cfg)
+    return cfg, fm, d, o
+
+
+def test_tiny_prefill_cache(tiny):
+    cfg, fm, d, o = tiny
+    _say("tiny: 64-row prefill (MFMA path)")
+    taps = gen.taps(cfg, "prefill", cfg["ctx_rows"])
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    torch.cuda.synchronize()
+    assert d.length == cfg["ctx_rows"]
+    w = _check_cache(d, o, cfg, 0, cfg["ctx_rows"], "prefill")
+    _say(f"tiny prefill cache worst row err {w:.2e}")
+
+
+def test_tiny_draft_block(tiny):
+    cfg, fm, d, o = tiny
+    pos = cfg["ctx_rows"]
+    _say(f"tiny: draft at pos {pos}")
+    hid, tok, logits, dbg = _draft(fm, d, cfg, anchor=1234, pos=pos)
+    out, xs = o.draft_block(1234, pos)
+    _, z = o.lm_argmax(out)
+    # the anchor slot written at pos
+    _check_cache(d, o, cfg, pos, pos + 1, "anchor slot")
+    for l in range(cfg["layers"]):
+        assert_rows_close(dbg[l], xs[l], what=f"x after layer {l}")
+    e = assert_rows_close(hid, out, what="hidden")
+    assert_rows_close(logits, z, what="logits")
+    n = assert_tokens_match(tok, z)
+    _say(f"tiny draft hidden err {e:.2e}, tokens checked exactly on {n}/{cfg['block']} rows")
+
+
+def test_tiny_small_append_then_draft(tiny):
+    # skinny append path (n <= 16) at start = pos (overwrites the anchor slot), then a second draft
+    cfg, fm, d, o = tiny
+    pos = cfg["ctx_rows"]
+    _say("tiny: 7-row append at the anchor position, then draft")
+    taps = gen.taps(cfg, "append1", 7)
+    o.context_append(taps, pos)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), pos)
+    torch.cuda.synchronize()
+    _check_cache(d, o, cfg, pos, pos + 7, "small append")
+    pos2 = pos + 7
+    hid, tok, logits, _ = _draft(fm, d, cfg, anchor=77, pos=pos2, debug=False)
+    out, _ = o.draft_block(77, pos2)
+    _, z = o.lm_argmax(out)
+    assert_rows_close(hid, out, what="hidden")
+    assert_tokens_match(tok, z)
+
+
+def test_tiny_draft_is_deterministic(tiny):
+    cfg, fm, d, o = tiny
+    pos = d.length
+    h1, t1, _, _ = _draft(fm, d, cfg, anchor=5, pos=pos, debug=False)
+    h2, t2, _, _ = _draft(fm, d, cfg, anchor=5, pos=pos, debug=False)
+    assert np.array_equal(h1, h2) and np.array_equal(t1, t2)
+
+
+def test_tiny_rewind_and_errors(tiny):
+    cfg, fm, d, o = tiny
+    with pytest.raises(fm.FmError) as e:
+        d.fm_context_append(torch.zeros(4, cfg["n_taps"] * cfg["target_dim"], device="cuda"), d.length + 1)
+    assert e.value.status == fm.FM_E_INVALID
+    with pytest.raises(fm.FmError) as e:
+        d.fm_context_append(torch.zeros(cfg["max_ctx"], cfg["n_taps"] * cfg["target_dim"], device="cuda"), 0)
+    assert e.value.status == fm.FM_E_CONTEXT_FULL
+    hid = torch.empty(cfg["block"], cfg["target_dim"], device="cuda")
+    with pytest.raises(fm.FmError) as e:
+        d.fm_draft_block(hid, anchor=torch.zeros(1, dtype=torch.int32, device="cuda"), pos=d.length + 1)
+    assert e.value.status == fm.FM_E_INVALID
+
+
+@pytest.fixture(scope="module")
+def flashmap():
+    cfg = configs.get("flashmap")
+    _say("flashmap: generating weights")
+    fm, d, o = _setup(cfg)
+    return cfg, fm, d, o
+
+
+def test_flashmap_prefill_and_draft(flashmap):
+    cfg, fm, d, o = flashmap
+    n = cfg["ctx_rows"]
+    _say(f"flashmap: {n}-row prefill")
+    taps = gen.taps(cfg, "prefill", n)
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    torch.cuda.synchronize()
+    w = _check_cache(d, o, cfg, 0, n, "prefill")
+    _say(f"flashmap prefill cache worst row err {w:.2e}")
+    an = int(gen.anchors(cfg, "flashmap", 1)[0])
+    _say(f"flashmap: draft at pos {n}, anchor {an}")
+    hid, tok, logits, dbg = _draft(fm, d, cfg, anchor=an, pos=n)
+    out, xs = o.draft_block(an, n)
+    _, z = o.lm_argmax(out)
+    for l in range(cfg["layers"]):
+        assert_rows_close(dbg[l], xs[l], what=f"x after layer {l}")
+    e = assert_rows_close(hid, out, what="hidden")
+    assert_rows_close(logits, z, what="logits")
+    k = assert_tokens_match(tok, z)
+    _say(f"flashmap draft hidden err {e:.2e}; tokens exact on {k}/{cfg['block']} rows")
