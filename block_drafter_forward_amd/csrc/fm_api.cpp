@@ -40,15 +40,28 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int TMAX = 16;          // rows of one skinny activation matrix
 constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
 
-// k-split of a partial-output skinny GEMM: the smallest S dividing K/128 with tiles*S >= TARGET_WGS.
-int pick_split(int M_total, int K) {
-    const int n4 = K / 128, tiles = M_total / 16;
-    for (int S = 1; S <= n4; ++S)
-        if (n4 % S == 0 && (tiles * S >= TARGET_WGS || n4 / S <= 2)) return S;
-    return n4;
+// k-steps per wave the skinny kernel is built for: up to 16 loaded at once, longer ranges in even stages.
+bool kw_ok(int kw) {
+    return kw == 1 || kw == 2 || kw == 3 || kw == 4 || kw == 5 || kw == 6 || kw == 8 || kw == 10 || kw == 12 ||
+           kw == 16 || (kw > 16 && kw % 2 == 0);
 }
 
-int attn_chunk(int L) { return L >= 4096 ? 256 : (L >= 1024 ? 128 : 64); }
+// k-split of a partial-output skinny GEMM (at most 8 slabs, the consumers' limit): the smallest S with
+// tiles * S >= TARGET_WGS and a per-wave range loaded at once (<= 16 k-steps); else the smallest S with enough
+// work-groups; else the largest supported S.
+int pick_split(int M_total, int K) {
+    const int n4 = K / 128, tiles = M_total / 16;
+    int any_enough = -1, largest = -1;
+    for (int S = 1; S <= std::min(8, n4); ++S) {
+        if (n4 % S || !kw_ok(n4 / S)) continue;
+        largest = S;
+        if (tiles * S >= TARGET_WGS) {
+            if (n4 / S <= 16) return S;
+            if (any_enough < 0) any_enough = S;
+        }
+    }
+    return any_enough > 0 ? any_enough : largest;
+}
 
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
@@ -101,7 +114,7 @@ Plan make_plan(const fm_config& c) {
     if (c.variant == FM_VARIANT_MTP) qkvw = c.heads * 2 * c.head_dim + 2 * c.kv_heads * c.head_dim;
     p.qkv = take((size_t)TMAX * qkvw * 4);
     const int Lmax = c.max_ctx + c.block + 1;
-    p.nchunk_max = (Lmax + 63) / 64;
+    p.nchunk_max = (Lmax + 15) / 16;
     p.attnp = take((size_t)c.heads * p.nchunk_max * TMAX * (c.head_dim + 2) * 4);
     p.stage = take((size_t)2 * c.layers * TMAX * D * 4);
     p.h0 = take((size_t)D * 4);
@@ -245,6 +258,8 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     for (auto& g : gs) tiles_total += g.M / 16;
     int S = 1;
     if (mode == SK_PARTIAL) S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K);
+    if (S < 1 || (K / 128) % S || !kw_ok(K / 128 / S))
+        return fail(FM_E_UNSUPPORTED, "skinny: no supported k-split for K %d (S %d)", K, S);
     a.ngroups = (int)gs.size();
     a.K = K;
     a.T = T;
@@ -277,6 +292,7 @@ RowArgs rows_base(int D, int T) {
 }
 
 fm_status rows(const RowArgs& r, hipStream_t st) {
+    if (r.S > 8) return fail(FM_E_UNSUPPORTED, "row kernel: more than 8 partial slabs");
     HIPCHK(launch_rows(r, st));
     return FM_OK;
 }
@@ -436,7 +452,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     CHK(fm_kv_rows_small(d, 1, pos, st));
 
     const int L = pos + 1;
-    const int chunk = attn_chunk(L);
+    const int chunk = attn_chunk_size(hd, c.kv_dtype);
     const int nchunks = (L + chunk - 1) / chunk;
     int S_prev = 0;           // split count of the pending residual update (fc2 of the previous layer)
     for (int l = 0; l < c.layers; ++l) {

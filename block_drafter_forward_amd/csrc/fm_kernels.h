@@ -131,10 +131,12 @@ struct AttnArgs {
     int heads, kv_heads, hd;
     int causal_base;       // >= 0: query t sees cache row j only if j <= causal_base + t
     float scale;
-    int chunk;             // keys per work-group
+    int chunk;             // keys per work-group: attn_chunk_size(hd, kv_dtype)
     int nchunks;
     float* part;           // [heads][nchunks][nq][hd + 2]: unnormalised o, running max, sum
 };
+// Keys per work-group of the split kernel for a head width and cache type (the host sizes nchunks with it).
+int attn_chunk_size(int hd, int kv_dtype);
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st);
 
 struct MergeArgs {

@@ -15,6 +15,8 @@
 #include "fm_device.h"
 #include "fm_kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 __device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
@@ -22,45 +24,77 @@ __device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
 }
 
 // ── self-attention ───────────────────────────────────────────────────────────────────────────────
+// All global loads (q, k, v of the head, the two norm weights, the slots' RoPE rows) are issued before the first
+// use, so the work-group pays one memory round trip.
 __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     const int h = blockIdx.x;
     const int T = a.T, hd = a.hd, D = a.D;
     __shared__ float X[3][16][129];   // q, k, v rows of this head (hd <= 128)
     __shared__ float P[16][17];
+    __shared__ float NW[2][128];
+    __shared__ float RT[16][128];     // RoPE rows [cos hd/2 | sin hd/2] of the T slots
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < 3 * T * hd; i += 256) {
-        const int w = i / (T * hd), r = i % (T * hd), t = r / hd, d = r % hd;
-        X[w][t][d] = a.qkv[(size_t)t * 3 * D + (size_t)w * D + (size_t)h * hd + d];
+    const int q4 = hd >> 2;           // float4 per row
+    const int n4 = 3 * T * q4;
+    float4 xv[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        const int i = tid + 256 * j;
+        const int ii = i < n4 ? i : n4 - 1;
+        const int w = ii / (T * q4), r = ii % (T * q4), t = r / q4, d4 = r % q4;
+        xv[j] = *(const float4*)(a.qkv + (size_t)t * 3 * D + (size_t)w * D + (size_t)h * hd + 4 * d4);
+    }
+    float nw = 0.f;
+    if (tid < 2 * hd) nw = bf16_to_f32((tid < hd ? a.qn : a.kn)[tid % hd]);
+    float rt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = tid + 256 * j;
+        const int ii = i < T * hd ? i : T * hd - 1;
+        rt[j] = a.rope_tab[(size_t)(a.pos_base + ii / hd) * hd + ii % hd];
+    }
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        const int i = tid + 256 * j;
+        if (i < n4) {
+            const int w = i / (T * q4), r = i % (T * q4), t = r / q4, d4 = r % q4;
+            X[w][t][4 * d4] = xv[j].x; X[w][t][4 * d4 + 1] = xv[j].y;
+            X[w][t][4 * d4 + 2] = xv[j].z; X[w][t][4 * d4 + 3] = xv[j].w;
+        }
+    }
+    if (tid < 2 * hd) NW[tid / hd][tid % hd] = nw;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = tid + 256 * j;
+        if (i < T * hd) RT[i / hd][i % hd] = rt[j];
     }
     __syncthreads();
     // head RMSNorm of the q and k rows (one wave per row)
     for (int row = wave; row < 2 * T; row += 4) {
         const int w = row / T, t = row % T;
-        const uint16_t* nw = w == 0 ? a.qn : a.kn;
         float ss = 0.f;
         for (int d = lane; d < hd; d += 64) ss += X[w][t][d] * X[w][t][d];
         ss = wave_sum(ss);
         const float r = 1.f / sqrtf(ss / (float)hd + a.eps);
-        for (int d = lane; d < hd; d += 64) X[w][t][d] = X[w][t][d] * (bf16_to_f32(nw[d]) * r);
+        for (int d = lane; d < hd; d += 64) X[w][t][d] = X[w][t][d] * (NW[w][d] * r);
     }
     __syncthreads();
     // interleaved RoPE: pairs (2i, 2i+1) at position pos_base + t
     const int half = hd >> 1;
     for (int i = tid; i < 2 * T * half; i += 256) {
         const int row = i / half, pi = i % half, w = row / T, t = row % T;
-        const float* tr = a.rope_tab + (size_t)(a.pos_base + t) * hd;
-        const float c = tr[pi], s = tr[half + pi];
+        const float c = RT[t][pi], sn = RT[t][half + pi];
         const float x0 = X[w][t][2 * pi], x1 = X[w][t][2 * pi + 1];
-        X[w][t][2 * pi] = x0 * c - x1 * s;
-        X[w][t][2 * pi + 1] = x1 * c + x0 * s;
+        X[w][t][2 * pi] = x0 * c - x1 * sn;
+        X[w][t][2 * pi + 1] = x1 * c + x0 * sn;
     }
     __syncthreads();
     {
         const int t = tid >> 4, u = tid & 15;
         if (t < T && u < T) {
-            float s = 0.f;
-            for (int d = 0; d < hd; ++d) s += X[0][t][d] * X[1][u][d];
-            P[t][u] = s * a.scale;
+            float sc = 0.f;
+            for (int d = 0; d < hd; ++d) sc += X[0][t][d] * X[1][u][d];
+            P[t][u] = sc * a.scale;
         }
     }
     __syncthreads();
@@ -88,31 +122,117 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     }
 }
 
-// ── query preparation shared by the split kernel ─────────────────────────────────────────────────
-template <int HD>
-__device__ void prep_queries(const QPrep& qp, int h, int nq, float (*qs)[HD]) {
+// ── split-L attention ────────────────────────────────────────────────────────────────────────────
+// Keys per work-group: K and V chunks of C rows each take 16 KB in LDS in their storage type.
+template <int HD, int KVT>
+struct SplitShape {
+    static constexpr int ES = KVT == 0 ? 2 : 4;
+    static constexpr int C = 16384 / (HD * ES);          // 64 (f16, 128), 128 (f16, 64), 32 (f32, 128), 16 (f32, 256)
+    static constexpr int PAD = 16 / ES;                   // one 16-byte pad per row: conflict-free row reads
+    static constexpr int ROW = HD + PAD;                  // elements per LDS row
+    static constexpr int V16 = HD * ES / 16;              // 16-byte pieces per key row
+    static constexpr int LD16 = C * V16 / 256;            // 16-byte pieces per thread per tensor
+    static constexpr int NTG = 256 / C;                   // query groups in the score pass
+    static constexpr int G = 256 / HD;                    // key groups in the P.V pass
+};
+
+// Every global load (queries or their split-K partials, the head-norm weight, the queries' RoPE rows, the chunk's
+// K and V rows) is issued before the first use: one memory round trip per work-group; the rest runs from LDS.
+template <int HD, int KVT>
+__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
+    using SS = SplitShape<HD, KVT>;
+    constexpr int C = SS::C, ROW = SS::ROW;
+    typedef typename std::conditional<KVT == 0, uint16_t, float>::type kv_t;
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int nq = a.nq;
+    const int kh = h / (a.heads / a.kv_heads);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < nq * HD; i += 256) {
+    __shared__ float qs[16][HD];
+    __shared__ __attribute__((aligned(16))) kv_t Ks[C * ROW];
+    __shared__ __attribute__((aligned(16))) kv_t Vs[C * ROW];
+    __shared__ float sc[16][C];
+    __shared__ float mrow[16], lrow[16];
+    const QPrep& qp = a.qp;
+
+    const int ncache = a.key_hi - a.key_lo;
+    const int ntot = ncache + a.nx;
+    const int k0 = c * C;
+    const int cnt = min(C, ntot - k0);
+
+    // 1. prefetch
+    constexpr int QPT = 16 * HD / 256;          // query values per thread (nq <= 16)
+    float qv[QPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + 256 * j;
         const int t = i / HD, d = i % HD;
-        const size_t off = (size_t)t * qp.q_ld + (size_t)h * qp.q_hs + d;
+        const int tt = t < nq ? t : 0;
+        const size_t off = (size_t)tt * qp.q_ld + (size_t)h * qp.q_hs + d;
         float v;
         if (qp.part) {
-            v = 0.f;
-            for (int s = 0; s < qp.S; ++s) v += qp.part[(size_t)s * qp.part_stride + off];
+            v = qp.part[off];
+#pragma unroll
+            for (int s2 = 1; s2 < 8; ++s2)
+                if (s2 < qp.S) v += qp.part[(size_t)s2 * qp.part_stride + off];
         } else {
             v = qp.q[off];
         }
-        qs[t][d] = v;
+        qv[j] = v;
+    }
+    float nwv = 0.f;
+    if (tid < HD && (qp.norm_bf16 || qp.norm_f32)) nwv = qp.norm_bf16 ? bf16_to_f32(qp.norm_bf16[tid]) : qp.norm_f32[tid];
+    float ropev[QPT];
+    if (qp.rope) {
+        const int rd = qp.rope_dims;
+#pragma unroll
+        for (int j = 0; j < QPT; ++j) {
+            const int i = tid + 256 * j;
+            const int t = i / HD, d = i % HD;
+            const int tt = t < nq ? t : 0;
+            ropev[j] = d < rd ? qp.rope_tab[(size_t)(qp.pos_base + tt) * rd + d] : 0.f;
+        }
+    }
+    uint4 kr[SS::LD16], vr[SS::LD16];
+#pragma unroll
+    for (int j = 0; j < SS::LD16; ++j) {
+        const int u = tid + 256 * j;
+        const int row = u / SS::V16, p16 = u % SS::V16;
+        int kidx = k0 + row;
+        kidx = kidx < ntot ? kidx : ntot - 1;
+        const bool fc = kidx < ncache;
+        const kv_t* kb = fc ? (const kv_t*)a.kc + (size_t)(a.key_lo + kidx) * a.kv_ld
+                            : (const kv_t*)a.kx + (size_t)(kidx - ncache) * a.x_ld;
+        const kv_t* vb = fc ? (const kv_t*)a.vc + (size_t)(a.key_lo + kidx) * a.kv_ld
+                            : (const kv_t*)a.vx + (size_t)(kidx - ncache) * a.x_ld;
+        kr[j] = *((const uint4*)(kb + (size_t)kh * HD) + p16);
+        vr[j] = *((const uint4*)(vb + (size_t)kh * HD) + p16);
+    }
+    // 2. to LDS
+    constexpr int RTW = HD <= 128 ? HD : 128;   // RoPE'd dims of a query head (NEOX rotates at most 128 here)
+    __shared__ float nws[HD], rts[16][RTW];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + 256 * j;
+        qs[i / HD][i % HD] = qv[j];
+        if (qp.rope && i % HD < RTW) rts[i / HD][i % HD] = ropev[j];
+    }
+    if (tid < HD) nws[tid] = nwv;
+#pragma unroll
+    for (int j = 0; j < SS::LD16; ++j) {
+        const int u = tid + 256 * j;
+        const int row = u / SS::V16, p16 = u % SS::V16;
+        *((uint4*)(Ks + row * ROW) + p16) = kr[j];
+        *((uint4*)(Vs + row * ROW) + p16) = vr[j];
     }
     __syncthreads();
+    // 3. query head-norm and RoPE in LDS
     if (qp.norm_bf16 || qp.norm_f32) {
         for (int t = wave; t < nq; t += 4) {
             float ss = 0.f;
             for (int d = lane; d < HD; d += 64) ss += qs[t][d] * qs[t][d];
             ss = wave_sum(ss);
             const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
-            for (int d = lane; d < HD; d += 64)
-                qs[t][d] *= (qp.norm_bf16 ? bf16_to_f32(qp.norm_bf16[d]) : qp.norm_f32[d]) * r;
+            for (int d = lane; d < HD; d += 64) qs[t][d] *= nws[d] * r;
         }
         __syncthreads();
     }
@@ -120,109 +240,78 @@ __device__ void prep_queries(const QPrep& qp, int h, int nq, float (*qs)[HD]) {
         const int half = HD / 2;
         for (int i = tid; i < nq * half; i += 256) {
             const int t = i / half, pi = i % half;
-            const float* tr = qp.rope_tab + (size_t)(qp.pos_base + t) * qp.rope_dims;
-            const float c = tr[pi], s = tr[half + pi];
+            const float cs = rts[t][pi], sn = rts[t][half + pi];
             const float x0 = qs[t][2 * pi], x1 = qs[t][2 * pi + 1];
-            qs[t][2 * pi] = x0 * c - x1 * s;
-            qs[t][2 * pi + 1] = x1 * c + x0 * s;
+            qs[t][2 * pi] = x0 * cs - x1 * sn;
+            qs[t][2 * pi + 1] = x1 * cs + x0 * sn;
         }
         __syncthreads();
     } else if (qp.rope == 2) {
         const int half = qp.rope_dims / 2;
         for (int i = tid; i < nq * half; i += 256) {
             const int t = i / half, pi = i % half;
-            const float* tr = qp.rope_tab + (size_t)(qp.pos_base + t) * qp.rope_dims;
-            const float c = tr[pi], s = tr[half + pi];
+            const float cs = rts[t][pi], sn = rts[t][half + pi];
             const float x0 = qs[t][pi], x1 = qs[t][pi + half];
-            qs[t][pi] = x0 * c - x1 * s;
-            qs[t][pi + half] = x1 * c + x0 * s;
+            qs[t][pi] = x0 * cs - x1 * sn;
+            qs[t][pi + half] = x1 * cs + x0 * sn;
         }
         __syncthreads();
     }
-}
-
-// ── split-L attention ────────────────────────────────────────────────────────────────────────────
-template <int HD>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
-    constexpr int G = 256 / HD;            // key groups in the P·V pass
-    const int c = blockIdx.x, h = blockIdx.y;
-    const int nq = a.nq;
-    const int kh = h / (a.heads / a.kv_heads);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    __shared__ float qs[16][HD];
-    __shared__ float sc[16][256];
-    __shared__ float red[G][16][HD];
-    __shared__ float mrow[16], lrow[16];
-
-    prep_queries<HD>(a.qp, h, nq, qs);
-
-    const int ncache = a.key_hi - a.key_lo;
-    const int ntot = ncache + a.nx;
-    const int k0 = c * a.chunk;
-    const int cnt = min(a.chunk, ntot - k0);
-
-    // scores: thread j owns key k0 + j
+    // 4. scores: thread (key j, query group tg)
     {
-        float s[16];
+        const int j = tid % C, tg = tid / C;
+        const bool valid = j < cnt;
+        const int kidx = k0 + j;
+        const bool from_cache = kidx < ncache;
+        float acc[16 / SS::NTG];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) s[t] = 0.f;
-        const bool valid = tid < cnt;
-        if (valid) {
-            const int kidx = k0 + tid;
-            const bool from_cache = kidx < ncache;
-            const size_t base = from_cache ? (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD
-                                           : (size_t)(kidx - ncache) * a.x_ld + (size_t)kh * HD;
-            for (int d = 0; d < HD; d += 8) {
-                float kk[8];
-                if (from_cache) {
-                    if (a.kv_dtype == 0) {
-                        const uint4 raw = *(const uint4*)((const uint16_t*)a.kc + base + d);
-                        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int q = 0; q < 16 / SS::NTG; ++q) acc[q] = 0.f;
+        for (int d0 = 0; d0 < HD; d0 += 8) {
+            float kk[8];
+            if constexpr (KVT == 0) {
+                const uint4 raw = *(const uint4*)(Ks + j * ROW + d0);
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            kk[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
-                            kk[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
-                        }
-                    } else {
-                        const float4* p = (const float4*)((const float*)a.kc + base + d);
-                        const float4 x0 = p[0], x1 = p[1];
-                        kk[0] = x0.x; kk[1] = x0.y; kk[2] = x0.z; kk[3] = x0.w;
-                        kk[4] = x1.x; kk[5] = x1.y; kk[6] = x1.z; kk[7] = x1.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kk[e] = a.kx[base + d + e];
+                for (int e = 0; e < 4; ++e) {
+                    kk[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
+                    kk[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
                 }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    if (t < nq) {
-                        float acc = s[t];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc += qs[t][d + e] * kk[e];
-                        s[t] = acc;
-                    }
-                }
+            } else {
+                const float4 x0 = *(const float4*)(Ks + j * ROW + d0);
+                const float4 x1 = *(const float4*)(Ks + j * ROW + d0 + 4);
+                kk[0] = x0.x; kk[1] = x0.y; kk[2] = x0.z; kk[3] = x0.w;
+                kk[4] = x1.x; kk[5] = x1.y; kk[6] = x1.z; kk[7] = x1.w;
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                s[t] *= a.scale;
-                if (a.causal_base >= 0 && from_cache && a.key_lo + kidx > a.causal_base + t) s[t] = -INFINITY;
+            for (int q = 0; q < 16 / SS::NTG; ++q) {
+                const int t = tg + q * SS::NTG;
+                if (t < nq) {
+                    float s2 = acc[q];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s2 += qs[t][d0 + e] * kk[e];
+                    acc[q] = s2;
+                }
             }
         }
-        if (tid < 256) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
-                if (t < nq) sc[t][tid] = valid ? s[t] : -INFINITY;
+        for (int q = 0; q < 16 / SS::NTG; ++q) {
+            const int t = tg + q * SS::NTG;
+            if (t < nq) {
+                float v = acc[q] * a.scale;
+                if (!valid) v = -INFINITY;
+                if (a.causal_base >= 0 && from_cache && a.key_lo + kidx > a.causal_base + t) v = -INFINITY;
+                sc[t][j] = v;
+            }
         }
     }
     __syncthreads();
-    // per-query max and exp-sum over the chunk (one wave per query row)
+    // 5. per-query max and exp-sum over the chunk (one wave per query row)
     for (int t = wave; t < nq; t += 4) {
         float m = -INFINITY;
-        for (int j = lane; j < a.chunk; j += 64) m = fmaxf(m, sc[t][j]);
+        for (int j = lane; j < C; j += 64) m = fmaxf(m, sc[t][j]);
         m = wave_max(m);
         float l = 0.f;
-        for (int j = lane; j < a.chunk; j += 64) {
+        for (int j = lane; j < C; j += 64) {
             const float p = (m == -INFINITY) ? 0.f : expf(sc[t][j] - m);
             sc[t][j] = p;
             l += p;
@@ -231,24 +320,28 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         if (lane == 0) { mrow[t] = m; lrow[t] = l; }
     }
     __syncthreads();
-    // P·V: thread (d, key group kg)
+    // 6. P.V: thread (d, key group kg)
+    float o[16];
     {
         const int d = tid % HD, kg = tid / HD;
-        float o[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) o[t] = 0.f;
-        for (int j = kg; j < cnt; j += G) {
-            const int kidx = k0 + j;
+        for (int j = kg; j < C; j += SS::G) {
             float vv;
-            if (kidx < ncache) vv = ld_kv(a.vc, (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD + d, a.kv_dtype);
-            else vv = a.vx[(size_t)(kidx - ncache) * a.x_ld + (size_t)kh * HD + d];
+            if constexpr (KVT == 0) vv = f16_to_f32(Vs[j * ROW + d]);
+            else vv = Vs[j * ROW + d];
 #pragma unroll
             for (int t = 0; t < 16; ++t)
                 if (t < nq) o[t] += sc[t][j] * vv;
         }
+    }
+    __syncthreads();   // Ks is reused below for the key-group reduction
+    float* red = (float*)Ks;   // [G][16][HD]
+    {
+        const int d = tid % HD, kg = tid / HD;
 #pragma unroll
         for (int t = 0; t < 16; ++t)
-            if (t < nq) red[kg][t][d] = o[t];
+            if (t < nq) red[(kg * 16 + t) * HD + d] = o[t];
     }
     __syncthreads();
     float* out = a.part + ((size_t)h * a.nchunks + c) * nq * (HD + 2);
@@ -256,7 +349,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         const int t = i / HD, d = i % HD;
         float v = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) v += red[g][t][d];
+        for (int g = 0; g < SS::G; ++g) v += red[(g * 16 + t) * HD + d];
         out[(size_t)t * (HD + 2) + d] = v;
     }
     if (tid < nq) {
@@ -389,14 +482,26 @@ hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+int attn_chunk_size(int hd, int kv_dtype) { return 16384 / (hd * (kv_dtype == 0 ? 2 : 4)); }
+
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
-    if (a.chunk > 256 || a.nq > 16) return hipErrorInvalidValue;
+    if (a.nq > 16 || a.chunk != attn_chunk_size(a.hd, a.kv_dtype)) return hipErrorInvalidValue;
+    if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
     dim3 grid(a.nchunks, a.heads);
-    switch (a.hd) {
-    case 64: attn_split_kernel<64><<<grid, 256, 0, st>>>(a); break;
-    case 128: attn_split_kernel<128><<<grid, 256, 0, st>>>(a); break;
-    case 256: attn_split_kernel<256><<<grid, 256, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
+    if (a.kv_dtype == 0) {
+        switch (a.hd) {
+        case 64: attn_split_kernel<64, 0><<<grid, 256, 0, st>>>(a); break;
+        case 128: attn_split_kernel<128, 0><<<grid, 256, 0, st>>>(a); break;
+        case 256: attn_split_kernel<256, 0><<<grid, 256, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (a.hd) {
+        case 64: attn_split_kernel<64, 1><<<grid, 256, 0, st>>>(a); break;
+        case 128: attn_split_kernel<128, 1><<<grid, 256, 0, st>>>(a); break;
+        case 256: attn_split_kernel<256, 1><<<grid, 256, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }

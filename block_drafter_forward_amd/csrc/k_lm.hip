@@ -56,9 +56,10 @@ struct Stage {
     float sc[2][CH][4];
 };
 
+// Loads are unconditional (rows past the table are clamped to its last row and discarded later): a conditional
+// load would make the compiler wait for every outstanding load before the next MFMA.
 template <int WT>
-__device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v0, int s, int r, int g, int lane,
-                                           bool tile1) {
+__device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v0, int s, int r, int g, int lane) {
     const int K = a.K;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -68,8 +69,7 @@ __device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        if (n == 1 && !tile1) continue;
-        const size_t row = (size_t)(v0 + 16 * n + r);
+        const size_t row = (size_t)min(v0 + 16 * n + r, a.V - 1);
         if constexpr (WT == 0) {
             const uint16_t* E = (const uint16_t*)a.E + row * K + (size_t)s * 32 + g * 8;
 #pragma unroll
@@ -87,18 +87,17 @@ __device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v
             for (int i = 0; i < CH; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    st.sc[n][i][j] = f16_to_f32(Dd[(size_t)(v0 + 16 * n + 4 * g + j) * nb + s + i]);
+                    st.sc[n][i][j] = f16_to_f32(Dd[(size_t)min(v0 + 16 * n + 4 * g + j, a.V - 1) * nb + s + i]);
         }
     }
 }
 
 template <int WT>
-__device__ __forceinline__ void compute_stage(const Stage<WT>& st, f32x4_t* acc, bool tile1) {
+__device__ __forceinline__ void compute_stage(const Stage<WT>& st, f32x4_t* acc) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            if (n == 1 && !tile1) continue;
             if constexpr (WT == 0) {
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(st.a[n][i]), as_bf(st.bh[i]), acc[n], 0, 0, 0);
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(st.a[n][i]), as_bf(st.bl[i]), acc[n], 0, 0, 0);
@@ -123,15 +122,19 @@ __global__ __launch_bounds__(256) void lm_argmax_kernel(LmArgs a) {
     const bool tile1 = v0 + 16 < a.V;
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     if (active) {
-        const int nsteps = a.K >> 5;
+        const int nsteps = a.K >> 5;   // a multiple of 2 * CH
         Stage<WT> s0, s1;
-        load_stage<WT>(s0, a, v0, 0, r, g, lane, tile1);
-        for (int s = 0; s < nsteps; s += 2 * CH) {
-            if (s + CH < nsteps) load_stage<WT>(s1, a, v0, s + CH, r, g, lane, tile1);
-            compute_stage<WT>(s0, acc, tile1);
-            if (s + 2 * CH < nsteps) load_stage<WT>(s0, a, v0, s + 2 * CH, r, g, lane, tile1);
-            if (s + CH < nsteps) compute_stage<WT>(s1, acc, tile1);
+        load_stage<WT>(s0, a, v0, 0, r, g, lane);
+        int s = 0;
+        for (; s + 2 * CH < nsteps; s += 2 * CH) {
+            load_stage<WT>(s1, a, v0, s + CH, r, g, lane);
+            compute_stage<WT>(s0, acc);
+            load_stage<WT>(s0, a, v0, s + 2 * CH, r, g, lane);
+            compute_stage<WT>(s1, acc);
         }
+        load_stage<WT>(s1, a, v0, s + CH, r, g, lane);
+        compute_stage<WT>(s0, acc);
+        compute_stage<WT>(s1, acc);
     }
     // lane holds z[t = lane % 16][v0 + 16 n + 4 g + j]
     const int t = lane & 15;

@@ -10,42 +10,82 @@
 
 namespace {
 
+__device__ __forceinline__ void ld8(const float* p, float* v) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void ld8_bf16(const uint16_t* p, float* v) {
+    const uint4 a = *(const uint4*)p;
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+}
+__device__ __forceinline__ void st8(float* p, const float* v) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Every global load of the row (base, partial slabs, bias, gate, and the norm's own parameters) is issued before
+// the first arithmetic, so the work-group pays one memory round trip; S <= 8 partial slabs.
 template <int NS>
 __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     const int t = blockIdx.x;
     const int D = a.D;
     const int nslot = D >> 3;
     __shared__ float red[4];
-    float v[NS][8];
+    float v[NS][8], u[NS][8], gv[NS][8], p0[NS][8], p1[NS][8];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int slot = threadIdx.x + j * 256;
+        const int i0 = (slot < nslot ? slot : 0) * 8;
+        if (a.init) ld8(a.init + i0, v[j]);
+        else if (a.in_rows) ld8(a.in_rows + (size_t)t * a.in_ld + i0, v[j]);
+        else if (a.x) ld8(a.x + (size_t)t * D + i0, v[j]);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[j][e] = 0.f;
+        if (a.S > 0) ld8(a.part + (size_t)t * D + i0, u[j]);
+#pragma unroll
+        for (int s = 1; s < 8; ++s) {
+            if (s < a.S) {
+                float w[8];
+                ld8(a.part + (size_t)s * a.part_stride + (size_t)t * D + i0, w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[j][e] += w[e];
+            }
+        }
+        if (a.bias) {
+            float w[8];
+            ld8_bf16(a.bias + i0, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[j][e] += w[e];
+        }
+        if (a.gate) ld8(a.gate + i0, gv[j]);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[j][e] = 1.f;
+        }
+        if (a.norm == ROW_LN_MOD) {
+            ld8(a.scale + i0, p0[j]);
+            ld8(a.shift + i0, p1[j]);
+        } else if (a.norm == ROW_RMS) {
+            if (a.w_bf16) ld8_bf16(a.w_bf16 + i0, p0[j]);
+            else ld8(a.w_f32 + i0, p0[j]);
+        }
+    }
     float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int slot = threadIdx.x + j * 256;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] += gv[j][e] * u[j][e];
         if (slot < nslot) {
-            const int i0 = slot * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = i0 + e;
-                float base = 0.f;
-                if (a.init) base = a.init[i];
-                else if (a.in_rows) base = a.in_rows[(size_t)t * a.in_ld + i];
-                else if (a.x) base = a.x[(size_t)t * D + i];
-                float u = 0.f;
-                for (int s = 0; s < a.S; ++s) u += a.part[(size_t)s * a.part_stride + (size_t)t * D + i];
-                if (a.bias) u += bf16_to_f32(a.bias[i]);
-                const float gv = a.gate ? a.gate[i] : 1.f;
-                const float val = base + gv * u;
-                v[j][e] = val;
-                sum += val;
-            }
-            if (a.x) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a.x[(size_t)t * D + i0 + e] = v[j][e];
-            }
-            if (a.debug_x) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a.debug_x[(size_t)t * D + i0 + e] = v[j][e];
-            }
+            for (int e = 0; e < 8; ++e) sum += v[j][e];
+            if (a.x) st8(a.x + (size_t)t * D + slot * 8, v[j]);
+            if (a.debug_x) st8(a.debug_x + (size_t)t * D + slot * 8, v[j]);
         }
     }
     if (a.norm == ROW_NONE && !a.frag_out && !a.f32_out) return;
@@ -79,16 +119,12 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
             float h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int i = i0 + e;
-                if (a.norm == ROW_LN_MOD) h[e] = (v[j][e] - mean) * r * (1.f + a.scale[i]) + a.shift[i];
-                else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * (a.w_bf16 ? bf16_to_f32(a.w_bf16[i]) : a.w_f32[i]);
+                if (a.norm == ROW_LN_MOD) h[e] = (v[j][e] - mean) * r * (1.f + p0[j][e]) + p1[j][e];
+                else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * p0[j][e];
                 else h[e] = v[j][e];
             }
             if (a.frag_out) frag_store8(a.frag_out, t, a.frag_koff + i0, h);
-            if (a.f32_out) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a.f32_out[(size_t)t * a.out_ld + i0 + e] = h[e];
-            }
+            if (a.f32_out) st8(a.f32_out + (size_t)t * a.out_ld + i0, h);
         }
     }
 }

@@ -8,9 +8,10 @@
 //     loads are non-temporal (streamed, never reused);
 //   * the activations are the B operand (16 slots = the MFMA's N), pre-split into bf16 hi + lo fragments by their
 //     producer, so one k-step is two MFMAs and the f32 activations keep ~17 significant bits;
-//   * a work-group is 4 waves on one 16-row tile, each wave a contiguous quarter of the k-range, streamed in stages
-//     of 4 k-steps with the next stage's loads in flight; the four 16x16 partial tiles are summed in LDS in a fixed
-//     order (deterministic), then the epilogue runs per element;
+//   * a work-group is 4 waves on one 16-row tile, each wave a contiguous quarter of the k-range; up to 16 k-steps
+//     a wave loads its whole range at once (all of it in flight), longer ranges stream in double-buffered stages;
+//     the four 16x16 partial tiles are summed in LDS in a fixed order (deterministic), then the epilogue runs per
+//     element;
 //   * k is split across S work-groups when M alone gives too few work-groups to fill 256 CUs; the S partial slabs
 //     are summed by the consumer kernel in a fixed order.
 // Q8_0 weights (int8 codes + one f16 scale per 32 codes): a k-step is exactly one Q8_0 block, so the codes go
@@ -55,25 +56,23 @@ __device__ __forceinline__ uint4 i8x8_to_bf16x8(uint2 c) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-constexpr int SKC = 4;   // k-steps per pipeline stage
-
-template <int NT, int WT>
+// One pipeline stage: SKC k-steps of the wave's A tiles and B fragments, loaded without any condition (a
+// conditional load makes the compiler wait for every outstanding load before the next MFMA).
+template <int NT, int WT, int SKC>
 struct SkStage {
     uint4 a[NT][SKC];    // bf16 weights; Q8_0 codes in .x/.y
     uint4 bh[SKC], bl[SKC];
     float sc[NT][SKC][4];
 };
 
-template <int NT, int WT>
-__device__ __forceinline__ void sk_load(SkStage<NT, WT>& st, const SkinnyGroup& G, int K, int m0, int s, int n_left,
-                                        int r, int g, int lane) {
+template <int NT, int WT, int SKC>
+__device__ __forceinline__ void sk_load(SkStage<NT, WT, SKC>& st, const SkinnyGroup& G, int K, int m0, int s, int r,
+                                        int g, int lane) {
     const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
 #pragma unroll
     for (int i = 0; i < SKC; ++i) {
-        if (i < n_left) {
-            st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
-            st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
-        }
+        st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
+        st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -81,8 +80,7 @@ __device__ __forceinline__ void sk_load(SkStage<NT, WT>& st, const SkinnyGroup& 
             const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2);
             const uint4* wp = (const uint4*)(W + (size_t)(m0 + r) * K + (size_t)s * 32 + g * 8);
 #pragma unroll
-            for (int i = 0; i < SKC; ++i)
-                if (i < n_left) st.a[n][i] = ldg_nt(wp + i * 4);
+            for (int i = 0; i < SKC; ++i) st.a[n][i] = ldg_nt(wp + i * 4);
         } else {
             const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2);
             const uint16_t* Dd = (const uint16_t*)(n == 0 ? G.Wd : G.W2d);
@@ -90,22 +88,19 @@ __device__ __forceinline__ void sk_load(SkStage<NT, WT>& st, const SkinnyGroup& 
             const int nb = K >> 5;
 #pragma unroll
             for (int i = 0; i < SKC; ++i) {
-                if (i < n_left) {
-                    const uint2 c = ldg_nt2(cp + i * 4);
-                    st.a[n][i] = make_uint4(c.x, c.y, 0, 0);
+                const uint2 c = ldg_nt2(cp + i * 4);
+                st.a[n][i] = make_uint4(c.x, c.y, 0, 0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) st.sc[n][i][j] = f16_to_f32(Dd[(size_t)(m0 + 4 * g + j) * nb + s + i]);
-                }
+                for (int j = 0; j < 4; ++j) st.sc[n][i][j] = f16_to_f32(Dd[(size_t)(m0 + 4 * g + j) * nb + s + i]);
             }
         }
     }
 }
 
-template <int NT, int WT>
-__device__ __forceinline__ void sk_compute(const SkStage<NT, WT>& st, f32x4_t* acc, int n_left) {
+template <int NT, int WT, int SKC>
+__device__ __forceinline__ void sk_compute(const SkStage<NT, WT, SKC>& st, f32x4_t* acc) {
 #pragma unroll
     for (int i = 0; i < SKC; ++i) {
-        if (i >= n_left) continue;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             if constexpr (WT == SKW_BF16) {
@@ -123,7 +118,10 @@ __device__ __forceinline__ void sk_compute(const SkStage<NT, WT>& st, f32x4_t* a
     }
 }
 
-template <int NT, int WT>
+// UP = 1: the wave's whole k-range (SKC == KW steps) is loaded at once, then multiplied -- every byte of the wave
+// in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
+// stage i computes), with the last pair peeled so the loop body carries no conditions.
+template <int NT, int WT, int UP, int SKC>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
     const int bid = blockIdx.x;
     int gi = 0;
@@ -145,14 +143,23 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // software pipeline over stages of SKC k-steps: stage i+1's loads are in flight while stage i computes
-    SkStage<NT, WT> st0, st1;
-    sk_load<NT, WT>(st0, G, K, m0, s0, KW, r, g, lane);
-    for (int s = 0; s < KW; s += 2 * SKC) {
-        if (s + SKC < KW) sk_load<NT, WT>(st1, G, K, m0, s0 + s + SKC, KW - s - SKC, r, g, lane);
-        sk_compute<NT, WT>(st0, acc, KW - s);
-        if (s + 2 * SKC < KW) sk_load<NT, WT>(st0, G, K, m0, s0 + s + 2 * SKC, KW - s - 2 * SKC, r, g, lane);
-        if (s + SKC < KW) sk_compute<NT, WT>(st1, acc, KW - s - SKC);
+    if constexpr (UP) {
+        SkStage<NT, WT, SKC> st;
+        sk_load<NT, WT, SKC>(st, G, K, m0, s0, r, g, lane);
+        sk_compute<NT, WT, SKC>(st, acc);
+    } else {
+        SkStage<NT, WT, SKC> st0, st1;
+        sk_load<NT, WT, SKC>(st0, G, K, m0, s0, r, g, lane);
+        int s = 0;
+        for (; s + 2 * SKC < KW; s += 2 * SKC) {
+            sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane);
+            sk_compute<NT, WT, SKC>(st0, acc);
+            sk_load<NT, WT, SKC>(st0, G, K, m0, s0 + s + 2 * SKC, r, g, lane);
+            sk_compute<NT, WT, SKC>(st1, acc);
+        }
+        sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane);
+        sk_compute<NT, WT, SKC>(st0, acc);
+        sk_compute<NT, WT, SKC>(st1, acc);
     }
 
     // ── sum the four waves' tiles (fixed order) ──
@@ -206,8 +213,19 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 
 template <int NT, int WT>
 hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
-    if (a.KW < 1) return hipErrorInvalidValue;
-    skinny_kernel<NT, WT><<<nwg, 256, 0, st>>>(a);
+    const int KW = a.KW;
+    dim3 grid(nwg), block(256);
+#define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n><<<grid, block, 0, st>>>(a); return hipGetLastError();
+    switch (KW) {
+        SK_UP(1) SK_UP(2) SK_UP(3) SK_UP(4) SK_UP(5) SK_UP(6) SK_UP(8) SK_UP(10) SK_UP(12) SK_UP(16)
+    default: break;
+    }
+#undef SK_UP
+    if (KW % 16 == 0) skinny_kernel<NT, WT, 0, 8><<<grid, block, 0, st>>>(a);
+    else if (KW % 8 == 0) skinny_kernel<NT, WT, 0, 4><<<grid, block, 0, st>>>(a);
+    else if (KW % 4 == 0) skinny_kernel<NT, WT, 0, 2><<<grid, block, 0, st>>>(a);
+    else if (KW % 2 == 0) skinny_kernel<NT, WT, 0, 1><<<grid, block, 0, st>>>(a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
