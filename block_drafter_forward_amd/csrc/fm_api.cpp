@@ -68,6 +68,7 @@ struct Plan {
     size_t best, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx, pctxn,
         qout, total;
     size_t part_floats;      // capacity of the partial buffer
+    size_t attnp_bytes;      // capacity of the attention partial buffer
     int rope_rows, rope_dims;
     int nchunk_max;
     int colR;
@@ -115,7 +116,8 @@ Plan make_plan(const fm_config& c) {
     p.qkv = take((size_t)TMAX * qkvw * 4);
     const int Lmax = c.max_ctx + c.block + 1;
     p.nchunk_max = (Lmax + 15) / 16;
-    p.attnp = take((size_t)c.heads * p.nchunk_max * TMAX * (c.head_dim + 2) * 4);
+    p.attnp_bytes = (size_t)c.heads * p.nchunk_max * TMAX * (c.head_dim + 2) * 4;
+    p.attnp = take(p.attnp_bytes);
     p.stage = take((size_t)2 * c.layers * TMAX * D * 4);
     p.h0 = take((size_t)D * 4);
     p.colR = 64;
@@ -727,8 +729,254 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     return FM_OK;
 }
 
-fm_status kvinject_draft(fm_drafter*, const fm_block_args*, float*, hipStream_t) {
-    return fail(FM_E_UNSUPPORTED, "KV-inject draft not built yet");
+// Attention of nq query rows over cache rows [key_lo, key_hi) (+ nx extra f32 rows), merged into o fragments.
+fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_lo, int key_hi, const float* kx,
+                 const float* vx, int nx, int x_ld, int causal_base, float scale, const float* gate, int gate_ld,
+                 int gate_hs, uint8_t* o_frag, hipStream_t st) {
+    const auto& c = d->c;
+    AttnArgs a{};
+    a.qp = qp;
+    a.nq = nq;
+    a.kv_dtype = c.kv_dtype;
+    if (c.variant == FM_VARIANT_MTP) {
+        const size_t w = (size_t)c.kv_heads * c.head_dim;
+        a.kc = d->kv;
+        a.vc = (const float*)d->kv + (size_t)c.max_ctx * w;
+        a.kv_ld = (int)w;
+    } else {
+        a.kc = d->kv_layer(layer_kv, 0);
+        a.vc = d->kv_layer(layer_kv, 1);
+        a.kv_ld = c.dim;
+    }
+    a.key_lo = key_lo;
+    a.key_hi = key_hi;
+    a.kx = kx;
+    a.vx = vx;
+    a.nx = nx;
+    a.x_ld = x_ld;
+    a.heads = c.heads;
+    a.kv_heads = c.kv_heads;
+    a.hd = c.head_dim;
+    a.causal_base = causal_base;
+    a.scale = scale;
+    a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype);
+    const int ntot = key_hi - key_lo + nx;
+    a.nchunks = (ntot + a.chunk - 1) / a.chunk;
+    if ((size_t)c.heads * a.nchunks * TMAX * (c.head_dim + 2) * 4 > d->p.attnp_bytes)
+        return fail(FM_E_INVALID, "attention partial buffer too small");
+    a.part = d->at<float>(d->p.attnp);
+    HIPCHK(launch_attn_split(a, st));
+    MergeArgs m{};
+    m.part = a.part;
+    m.heads = c.heads;
+    m.nchunks = a.nchunks;
+    m.nq = nq;
+    m.hd = c.head_dim;
+    m.gate = gate;
+    m.gate_ld = gate_ld;
+    m.gate_hs = gate_hs;
+    m.o_frag = o_frag;
+    HIPCHK(launch_attn_merge(m, st));
+    return FM_OK;
+}
+
+fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim, T = c.block, Ht = c.target_dim, hd = c.head_dim;
+    float* part = d->at<float>(d->p.part);
+    float* x = d->at<float>(d->p.x);
+    uint8_t* fragA = d->at<uint8_t>(d->p.fragA);
+    uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
+    uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
+    uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
+    float* qkv = d->at<float>(d->p.qkv);
+    const long long pstr = (long long)TMAX * D;
+    const int Lc = d->length;
+
+    // block rows: H_d[0] = tok_proj(E[anchor]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]
+    HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, fragA, st));
+    int S = 0;
+    CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, 1, SK_PARTIAL, 0,
+               &S, st));
+    {
+        RowArgs r = rows_base(D, T);
+        r.x = x;
+        r.base_zero = 1;
+        r.part = part;
+        r.S = S;
+        r.part_stride = pstr;
+        r.part_rows = 1;
+        r.base_bf16 = d->B("mask_emb");
+        r.base_from = 1;
+        r.row_bias_bf16 = d->B("block_pos");
+        r.norm = ROW_RMS;
+        r.w_bf16 = d->B(BB(0, "attn_norm"));
+        r.eps = c.rms_eps;
+        r.frag_out = fragH;
+        CHK(rows(r, st));
+    }
+    const float scale = 1.f / sqrtf((float)hd);
+    for (int i = 0; i < c.layers; ++i) {
+        CHK(skinny(d,
+                   {{d->W(BB(i, "q")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, 3 * D},
+                    {d->W(BB(i, "k")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
+                    {d->W(BB(i, "v")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D, D, 3 * D}},
+                   D, T, SK_F32, 0, nullptr, st));
+        // bidirectional attention over [context rows ++ block rows]
+        QPrep qp{};
+        qp.q = qkv;
+        qp.q_ld = 3 * D;
+        qp.q_hs = hd;
+        CHK(attend(d, qp, T, i, 0, Lc, qkv + D, qkv + 2 * D, T, 3 * D, -1, scale, nullptr, 0, 0, fragO, st));
+        CHK(skinny(d, {{d->W(BB(i, "o")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}}, D, T, SK_PARTIAL, 0,
+                   &S, st));
+        {
+            RowArgs r = rows_base(D, T);
+            r.x = x;
+            r.part = part;
+            r.S = S;
+            r.part_stride = pstr;
+            r.norm = ROW_RMS;
+            r.w_bf16 = d->B(BB(i, "ff_norm"));
+            r.eps = c.rms_eps;
+            r.frag_out = fragH;
+            CHK(rows(r, st));
+        }
+        CHK(skinny(d, {{d->W(BB(i, "gate")), nullptr, d->W(BB(i, "up")), nullptr, nullptr, fragH, fragU, c.ffn, 0}},
+                   D, T, SK_FRAG_GEGLU, 0, nullptr, st));
+        CHK(skinny(d, {{d->W(BB(i, "down")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
+                   SK_PARTIAL, 0, &S, st));
+        {
+            RowArgs r = rows_base(D, T);
+            r.x = x;
+            r.part = part;
+            r.S = S;
+            r.part_stride = pstr;
+            if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)i * T * D;
+            r.norm = ROW_RMS;
+            r.w_bf16 = i + 1 < c.layers ? d->B(BB(i + 1, "attn_norm")) : d->B("out_norm");
+            r.eps = c.rms_eps;
+            r.frag_out = fragH;
+            CHK(rows(r, st));
+        }
+    }
+    CHK(skinny(d, {{d->W("out_proj"), nullptr, nullptr, nullptr, nullptr, fragH, hidden_out, Ht, Ht}}, D, T, SK_F32, 0,
+               nullptr, st));
+    return FM_OK;
+}
+
+// ── MTP ─────────────────────────────────────────────────────────────────────────────────────────
+fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    const auto& c = d->c;
+    const int H = c.dim, M = ba->rows, NH = c.heads, NKV = c.kv_heads, HD = c.head_dim;
+    const int qw = NH * 2 * HD, kw = NKV * HD, qkvw = qw + 2 * kw;
+    float* part = d->at<float>(d->p.part);
+    float* x = d->at<float>(d->p.x);
+    uint8_t* fragA = d->at<uint8_t>(d->p.fragA);
+    uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
+    uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
+    uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
+    float* qkv = d->at<float>(d->p.qkv);
+    float* qout = d->at<float>(d->p.qout);
+    const long long pstr = (long long)TMAX * H;
+    auto Q = [&](const char* n) { return d->W(std::string(n) + ".q"); };
+    auto Dd = [&](const char* n) { return d->W(std::string(n) + ".d"); };
+
+    // x = eh_proj([enorm(e); hnorm(h)])
+    for (int side = 0; side < 2; ++side) {
+        RowArgs r = rows_base(H, M);
+        r.in_rows = side == 0 ? ba->embed_rows : ba->prev_hidden;
+        r.in_ld = H;
+        r.norm = ROW_RMS;
+        r.w_f32 = d->F(side == 0 ? "enorm" : "hnorm");
+        r.eps = c.rms_eps;
+        r.frag_out = fragA;
+        r.frag_koff = side * H;
+        CHK(rows(r, st));
+    }
+    int S = 0;
+    CHK(skinny(d, {{Q("eh_proj"), Dd("eh_proj"), nullptr, nullptr, nullptr, fragA, part, H, H}}, 2 * H, M, SK_PARTIAL,
+               0, &S, st));
+    {
+        RowArgs r = rows_base(H, M);
+        r.x = x;
+        r.base_zero = 1;
+        r.part = part;
+        r.S = S;
+        r.part_stride = pstr;
+        r.norm = ROW_RMS;
+        r.w_f32 = d->F("attn_norm");
+        r.eps = c.rms_eps;
+        r.frag_out = fragH;
+        CHK(rows(r, st));
+    }
+    CHK(skinny(d,
+               {{Q("attn_q"), Dd("attn_q"), nullptr, nullptr, nullptr, fragH, qkv, qw, qkvw},
+                {Q("attn_k"), Dd("attn_k"), nullptr, nullptr, nullptr, fragH, qkv + qw, kw, qkvw},
+                {Q("attn_v"), Dd("attn_v"), nullptr, nullptr, nullptr, fragH, qkv + qw + kw, kw, qkvw}},
+               H, M, SK_F32, 0, nullptr, st));
+    {
+        MtpPrepArgs p{};
+        p.qf = qkv;
+        p.kt = qkv + qw;
+        p.vt = qkv + qw + kw;
+        p.qf_ld = p.kt_ld = p.vt_ld = qkvw;
+        p.M = M;
+        p.NH = NH;
+        p.NKV = NKV;
+        p.HD = HD;
+        p.rot = c.rope_dims;
+        p.qn = d->F("attn_q_norm");
+        p.kn = d->F("attn_k_norm");
+        p.eps = c.rms_eps;
+        p.rope_tab = d->at<float>(d->p.rope);
+        p.pos0 = ba->pos;
+        p.qout = qout;
+        p.kc = (float*)d->kv;
+        p.vc = (float*)d->kv + (size_t)c.max_ctx * kw;
+        HIPCHK(launch_mtp_prep(p, st));
+    }
+    {
+        QPrep qp{};
+        qp.q = qout;
+        qp.q_ld = NH * HD;
+        qp.q_hs = HD;
+        CHK(attend(d, qp, M, 0, ba->kv_lo, ba->pos + M, nullptr, nullptr, 0, 0, ba->pos, 1.f / sqrtf((float)HD),
+                   qkv + HD, qkvw, 2 * HD, fragO, st));
+    }
+    CHK(skinny(d, {{Q("attn_output"), Dd("attn_output"), nullptr, nullptr, nullptr, fragO, part, H, H}}, NH * HD, M,
+               SK_PARTIAL, 0, &S, st));
+    {
+        RowArgs r = rows_base(H, M);
+        r.x = x;
+        r.part = part;
+        r.S = S;
+        r.part_stride = pstr;
+        r.norm = ROW_RMS;
+        r.w_f32 = d->F("post_attention_norm");
+        r.eps = c.rms_eps;
+        r.frag_out = fragH;
+        CHK(rows(r, st));
+    }
+    CHK(skinny(d, {{Q("ffn_gate"), Dd("ffn_gate"), Q("ffn_up"), Dd("ffn_up"), nullptr, fragH, fragU, c.ffn, 0}}, H, M,
+               SK_FRAG_SWIGLU, 0, nullptr, st));
+    CHK(skinny(d, {{Q("ffn_down"), Dd("ffn_down"), nullptr, nullptr, nullptr, fragU, part, H, H}}, c.ffn, M,
+               SK_PARTIAL, 0, &S, st));
+    {
+        RowArgs r = rows_base(H, M);
+        r.x = x;
+        r.part = part;
+        r.S = S;
+        r.part_stride = pstr;
+        if (ba->debug_layers) r.debug_x = ba->debug_layers;
+        r.norm = ROW_RMS;
+        r.w_f32 = d->F("shared_head_norm");
+        r.eps = c.rms_eps;
+        r.f32_out = hidden_out;
+        r.out_ld = H;
+        CHK(rows(r, st));
+    }
+    return FM_OK;
 }
 
 fm_status kvinject_create(fm_drafter*, hipStream_t) { return FM_OK; }
@@ -824,10 +1072,15 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
     }
     if (c.variant == FM_VARIANT_KVINJECT) {
         if (!a->anchor) return fail(FM_E_INVALID, "null anchor");
-        if (d->length < 1) return fail(FM_E_INVALID, "empty context");
         return kvinject_draft(d, a, hidden_out, st);
     }
-    return fail(FM_E_UNSUPPORTED, "MTP draft not built yet");
+    if (!a->embed_rows || !a->prev_hidden) return fail(FM_E_INVALID, "null embed_rows / prev_hidden");
+    if (a->rows < 1 || a->rows > c.block) return fail(FM_E_INVALID, "rows %d outside [1, %d]", a->rows, c.block);
+    if (a->pos < 0 || a->kv_lo < 0 || a->kv_lo > a->pos)
+        return fail(FM_E_INVALID, "need 0 <= kv_lo (%d) <= pos (%d)", a->kv_lo, a->pos);
+    if ((long long)a->pos + a->rows > c.max_ctx)
+        return fail(FM_E_CONTEXT_FULL, "pos %d + rows %d > KV cache rows %d", a->pos, a->rows, c.max_ctx);
+    return mtp_draft(d, a, hidden_out, st);
 }
 
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits, void* stream) {

@@ -68,6 +68,11 @@ struct RowArgs {
     float* debug_x;        // copy of the updated stream [T][D] (or null)
     int D;
     int T;
+    int base_zero;         // base value 0 even when x is set (x is then only written)
+    int part_rows;         // rows t >= part_rows take no partials (0: every row)
+    const uint16_t* base_bf16;  // rows t >= base_from take their base from these bf16 rows [(t - base_from)][D]
+    int base_from;
+    const uint16_t* row_bias_bf16;  // bf16 [T][D] added to row t (or null)
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
@@ -167,6 +172,7 @@ hipError_t launch_kv_final(const KVFinalArgs& a, hipStream_t st);
 // MTP: q/k head-norm + NEOX RoPE, K/V cache write at pos0 + m; q written to qout [M][NH*HD].
 struct MtpPrepArgs {
     const float* qf; const float* kt; const float* vt;
+    int qf_ld, kt_ld, vt_ld;   // row strides (elements)
     int M, NH, NKV, HD, rot;
     const float* qn; const float* kn;
     float eps;

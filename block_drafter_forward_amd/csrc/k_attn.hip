@@ -448,13 +448,13 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
     __shared__ float sh[256];
     if (j >= NH + NKV) {
         const int vh = j - NH - NKV;
-        if (tid < HD) a.vc[(size_t)pos * NKV * HD + vh * HD + tid] = a.vt[(size_t)m * NKV * HD + vh * HD + tid];
+        if (tid < HD) a.vc[(size_t)pos * NKV * HD + vh * HD + tid] = a.vt[(size_t)m * a.vt_ld + vh * HD + tid];
         return;
     }
     float x = 0.f, w = 0.f;
     if (tid < HD) {
-        if (j < NH) { x = a.qf[(size_t)m * NH * 2 * HD + (size_t)j * 2 * HD + tid]; w = a.qn[tid]; }
-        else { x = a.kt[(size_t)m * NKV * HD + (size_t)(j - NH) * HD + tid]; w = a.kn[tid]; }
+        if (j < NH) { x = a.qf[(size_t)m * a.qf_ld + (size_t)j * 2 * HD + tid]; w = a.qn[tid]; }
+        else { x = a.kt[(size_t)m * a.kt_ld + (size_t)(j - NH) * HD + tid]; w = a.kn[tid]; }
     }
     const float ss = block_sum256(x * x, red);
     const float y = x * (1.f / sqrtf(ss / (float)HD + a.eps)) * w;

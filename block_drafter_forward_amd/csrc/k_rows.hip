@@ -37,19 +37,21 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     for (int j = 0; j < NS; ++j) {
         const int slot = threadIdx.x + j * 256;
         const int i0 = (slot < nslot ? slot : 0) * 8;
-        if (a.init) ld8(a.init + i0, v[j]);
+        if (a.base_bf16 && t >= a.base_from) ld8_bf16(a.base_bf16 + (size_t)(t - a.base_from) * D + i0, v[j]);
+        else if (a.init) ld8(a.init + i0, v[j]);
         else if (a.in_rows) ld8(a.in_rows + (size_t)t * a.in_ld + i0, v[j]);
-        else if (a.x) ld8(a.x + (size_t)t * D + i0, v[j]);
+        else if (a.x && !a.base_zero) ld8(a.x + (size_t)t * D + i0, v[j]);
         else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) u[j][e] = 0.f;
-        if (a.S > 0) ld8(a.part + (size_t)t * D + i0, u[j]);
+        const int S = (a.part_rows > 0 && t >= a.part_rows) ? 0 : a.S;
+        if (S > 0) ld8(a.part + (size_t)t * D + i0, u[j]);
 #pragma unroll
         for (int s = 1; s < 8; ++s) {
-            if (s < a.S) {
+            if (s < S) {
                 float w[8];
                 ld8(a.part + (size_t)s * a.part_stride + (size_t)t * D + i0, w);
 #pragma unroll
@@ -59,6 +61,12 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
         if (a.bias) {
             float w[8];
             ld8_bf16(a.bias + i0, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[j][e] += w[e];
+        }
+        if (a.row_bias_bf16) {
+            float w[8];
+            ld8_bf16(a.row_bias_bf16 + (size_t)t * D + i0, w);
 #pragma unroll
             for (int e = 0; e < 8; ++e) u[j][e] += w[e];
         }

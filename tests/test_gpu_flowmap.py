@@ -161,3 +161,40 @@ def test_flashmap_prefill_and_draft(flashmap):
     assert_rows_close(logits, z, what="logits")
     k = assert_tokens_match(tok, z)
     _say(f"flashmap draft hidden err {e:.2e}; tokens exact on {k}/{cfg['block']} rows")
+
+
+def test_longctx_workload(flashmap):
+    """8192-row prefill on the MFMA path, then 64 draft steps, each followed by an append of U{1..16} rows at the
+    anchor position (the long-context workload's own schedule)."""
+    from block_drafter_forward_amd import fm as fmod
+    cfg0, _, _, o0 = flashmap
+    cfg = configs.get("longctx")
+    d = fmod.Drafter(cfg, fmod.upload_weights(o0.raw))
+    o = flowmap.FlowMapOracle(cfg, o0.raw)
+    o._w = o0._w                      # share the decoded float64 weights
+    n = cfg["ctx_rows"]
+    _say(f"longctx: {n}-row prefill")
+    taps = gen.taps(cfg, "prefill", n)
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    torch.cuda.synchronize()
+    for l in (0, cfg["layers"] - 1):
+        rows = np.r_[0:64, n - 64:n]
+        assert_rows_close(d.kv_layer(l, 0)[rows].float().cpu().numpy(), o.K[l][rows], what=f"prefill K{l}")
+        assert_rows_close(d.kv_layer(l, 1)[rows].float().cpu().numpy(), o.V[l][rows], what=f"prefill V{l}")
+    worst = 0.0
+    exact = 0
+    for s, (an, pos, ns) in enumerate(gen.longctx_schedule(cfg)):
+        hid, tok, _, _ = _draft(fmod, d, cfg, anchor=an, pos=pos, debug=False)
+        out, _ = o.draft_block(an, pos)
+        _, z = o.lm_argmax(out)
+        worst = max(worst, assert_rows_close(hid, out, what=f"step {s} hidden"))
+        exact += assert_tokens_match(tok, z)
+        t2 = gen.taps(cfg, f"step{s}", ns)
+        o.context_append(t2, pos)
+        d.fm_context_append(torch.from_numpy(t2).cuda(), pos)
+        if s % 16 == 0:
+            _say(f"longctx: step {s} pos {pos} (L={pos + 1}) ok, worst hidden err so far {worst:.2e}")
+    torch.cuda.synchronize()
+    assert d.length == o.length
+    _say(f"longctx: 64 steps, worst hidden err {worst:.2e}, tokens exact on {exact}/{64 * cfg['block']} rows")

@@ -1,0 +1,81 @@
+"""GPU parity of the MTP head (Q8_0 weights, grouped-query causal attention over its own cache) against the
+float64 oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from inputs import configs, gen
+from oracle import mtp
+from tests.parity import assert_rows_close, assert_tokens_match
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+SMALL = dict(variant="mtp", dim=512, heads=4, head_dim=256, kv_heads=2, layers=1, ffn=1024, block=8,
+             target_dim=512, n_taps=2, vocab=4096, max_ctx=300, rope="neox", rope_dims=64, rope_theta=1e7,
+             ln_eps=1e-6, rms_eps=1e-6, qk_eps=1e-6, mlp="swiglu", kv_dtype="f32", wtype="q8_0", ctx_rows=300,
+             name="mtp_small")
+
+
+def _say(msg):
+    print(f"[gpu-mtp] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("name", ["small", "mtp"])
+def test_mtp_rows(name):
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL if name == "small" else configs.get("mtp")
+    _say(f"{name}: generating Q8_0 weights")
+    W = gen.make_weights(cfg)
+    d = fm.Drafter(cfg, fm.upload_weights(W))
+    o = mtp.MTPOracle(cfg, W)
+    kc, vc = gen.mtp_cache_rows(cfg, cfg["max_ctx"])
+    H = cfg["dim"]
+    for M in (1, 2, 4, 8):
+        pos0 = cfg["max_ctx"] - M
+        kv_lo = 0 if M != 4 else pos0 // 3
+        _say(f"{name}: M={M} pos0={pos0} kv_lo={kv_lo}")
+        o.set_cache_rows(kc[:pos0], vc[:pos0])
+        d.kv_layer(0, 0)[:pos0].copy_(torch.from_numpy(kc[:pos0]))
+        d.kv_layer(0, 1)[:pos0].copy_(torch.from_numpy(vc[:pos0]))
+        e, h = gen.mtp_inputs(cfg, M)
+        hid = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        dbg = torch.empty(1, M, H, dtype=torch.float32, device="cuda")
+        d.fm_draft_block(hid, pos=pos0, rows=M, kv_lo=kv_lo, embed_rows=torch.from_numpy(e).cuda(),
+                         prev_hidden=torch.from_numpy(h).cuda(), debug_layers=dbg)
+        tok = torch.empty(M, dtype=torch.int32, device="cuda")
+        logits = torch.empty(M, cfg["vocab"], dtype=torch.float32, device="cuda")
+        d.fm_lm_argmax(hid, M, tok, logits)
+        torch.cuda.synchronize()
+        out = o.forward(e, h, pos0, kv_lo)
+        _, z = o.lm_argmax(out)
+        # the rows' own K/V were appended to the cache at pos0 .. pos0 + M - 1
+        assert_rows_close(d.kv_layer(0, 0)[pos0:pos0 + M].cpu().numpy(), o.Kc[pos0:pos0 + M], what="new K rows")
+        assert_rows_close(d.kv_layer(0, 1)[pos0:pos0 + M].cpu().numpy(), o.Vc[pos0:pos0 + M], what="new V rows")
+        err = assert_rows_close(hid.cpu().numpy(), out, what=f"hidden M={M}")
+        assert_rows_close(logits.cpu().numpy(), z, what=f"logits M={M}")
+        k = assert_tokens_match(tok.cpu().numpy(), z)
+        _say(f"{name}: M={M} hidden err {err:.2e}; tokens exact on {k}/{M}")
+
+
+def test_mtp_bad_rows():
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL
+    W = gen.make_weights(cfg)
+    d = fm.Drafter(cfg, fm.upload_weights(W))
+    e = torch.zeros(9, cfg["dim"], device="cuda")
+    hid = torch.empty(9, cfg["dim"], device="cuda")
+    for rows, pos, kv_lo, st in [(9, 0, 0, fm.FM_E_INVALID), (0, 0, 0, fm.FM_E_INVALID),
+                                 (4, cfg["max_ctx"] - 3, 0, fm.FM_E_CONTEXT_FULL), (2, 5, 6, fm.FM_E_INVALID)]:
+        with pytest.raises(fm.FmError) as ex:
+            d.fm_draft_block(hid, pos=pos, rows=rows, kv_lo=kv_lo, embed_rows=e, prev_hidden=e)
+        assert ex.value.status == st
+    with pytest.raises(fm.FmError) as ex:
+        d.fm_context_append(e, 0)
+    assert ex.value.status == fm.FM_E_INVALID
