@@ -65,8 +65,9 @@ int pick_split(int M_total, int K) {
 
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
-    size_t best, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx, pctxn,
-        qout, total;
+    size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
+        pctxn, qout, apart, afrag, cfrag, total;
+    size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
     int rope_rows, rope_dims;
@@ -100,6 +101,8 @@ Plan make_plan(const fm_config& c) {
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     const int D = c.dim;
     p.best = take(16 * sizeof(unsigned long long));
+    p.zeros_bytes = (size_t)std::max({kmax_frag(c), 2 * c.dim, c.target_dim, 256}) * 4;
+    p.zeros = take(p.zeros_bytes);
     p.rope_dims = c.rope == FM_ROPE_NEOX ? c.rope_dims : c.head_dim;
     p.rope_rows = c.max_ctx + c.block + 2;
     p.rope = take(c.rope == FM_ROPE_NONE ? 0 : (size_t)p.rope_rows * p.rope_dims * 4);
@@ -128,6 +131,11 @@ Plan make_plan(const fm_config& c) {
     p.pctx = take(prefill ? (size_t)c.max_ctx * D * 4 : 0);
     p.pctxn = take(prefill ? (size_t)(c.variant == FM_VARIANT_KVINJECT ? c.layers : 1) * c.max_ctx * D * 2 : 0);
     p.qout = take(c.variant == FM_VARIANT_MTP ? (size_t)TMAX * c.heads * c.head_dim * 4 : 0);
+    // the flow-map anchor path runs on a side stream next to the first layer: it has buffers of its own
+    const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
+    p.apart = take(fmv ? p.part_floats * 4 : 0);
+    p.afrag = take(fmv ? (size_t)c.target_dim * 64 : 0);
+    p.cfrag = take(fmv ? (size_t)c.dim * 64 : 0);
     p.total = off;
     return p;
 }
@@ -185,6 +193,8 @@ struct fm_drafter {
     uint8_t* ws;
     uint8_t* kv;
     int length;
+    hipStream_t side = nullptr;        // default-priority stream for work that overlaps the caller's stream
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
     template <class T> T* at(size_t off) const { return (T*)(ws + off); }
     const void* W(const std::string& n) const { auto it = w.find(n); return it == w.end() ? nullptr : it->second; }
@@ -286,10 +296,11 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     return FM_OK;
 }
 
-RowArgs rows_base(int D, int T) {
+RowArgs rows_base(const fm_drafter* d, int D, int T) {
     RowArgs r{};
     r.D = D;
     r.T = T;
+    r.zeros = d->at<float>(d->p.zeros);
     return r;
 }
 
@@ -305,6 +316,58 @@ fm_status rows(const RowArgs& r, hipStream_t st) {
         if (s_ != FM_OK) return s_;   \
     } while (0)
 
+// Attention of nq query rows over cache rows [key_lo, key_hi) (+ nx extra f32 rows), merged into o fragments.
+fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_lo, int key_hi, const float* kx,
+                 const float* vx, int nx, int x_ld, int causal_base, float scale, const float* gate, int gate_ld,
+                 int gate_hs, uint8_t* o_frag, hipStream_t st) {
+    const auto& c = d->c;
+    AttnArgs a{};
+    a.qp = qp;
+    a.qp.zeros = d->at<float>(d->p.zeros);
+    a.nq = nq;
+    a.kv_dtype = c.kv_dtype;
+    if (c.variant == FM_VARIANT_MTP) {
+        const size_t w = (size_t)c.kv_heads * c.head_dim;
+        a.kc = d->kv;
+        a.vc = (const float*)d->kv + (size_t)c.max_ctx * w;
+        a.kv_ld = (int)w;
+    } else {
+        a.kc = d->kv_layer(layer_kv, 0);
+        a.vc = d->kv_layer(layer_kv, 1);
+        a.kv_ld = c.dim;
+    }
+    a.key_lo = key_lo;
+    a.key_hi = key_hi;
+    a.kx = kx;
+    a.vx = vx;
+    a.nx = nx;
+    a.x_ld = x_ld;
+    a.heads = c.heads;
+    a.kv_heads = c.kv_heads;
+    a.hd = c.head_dim;
+    a.causal_base = causal_base;
+    a.scale = scale;
+    a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype);
+    const int ntot = key_hi - key_lo + nx;
+    a.nchunks = (ntot + a.chunk - 1) / a.chunk;
+    if ((size_t)c.heads * a.nchunks * TMAX * (c.head_dim + 2) * 4 > d->p.attnp_bytes)
+        return fail(FM_E_INVALID, "attention partial buffer too small");
+    a.part = d->at<float>(d->p.attnp);
+    HIPCHK(launch_attn_split(a, st));
+    MergeArgs m{};
+    m.part = a.part;
+    m.heads = c.heads;
+    m.nchunks = a.nchunks;
+    m.nq = nq;
+    m.hd = c.head_dim;
+    m.gate = gate;
+    m.gate_ld = gate_ld;
+    m.gate_hs = gate_hs;
+    m.o_frag = o_frag;
+    HIPCHK(launch_attn_merge(m, st));
+    return FM_OK;
+}
+
 // ── flow-map ────────────────────────────────────────────────────────────────────────────────────
 std::string LW(int l, const char* s) {
     char b[128];
@@ -313,16 +376,16 @@ std::string LW(int l, const char* s) {
 }
 
 // c rows (fragments in fragH, T rows) -> every layer's K/V at rows start.. (skinny path, T <= 16)
-fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, hipStream_t st) {
+fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, const uint8_t* cfrag, hipStream_t st) {
     const auto& c = d->c;
     const int D = c.dim;
     std::vector<SkGroupDesc> gs;
     float* stage = d->at<float>(d->p.stage);
     for (int l = 0; l < c.layers; ++l) {
-        gs.push_back({d->W(LW(l, "cross_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr,
-                      d->at<uint8_t>(d->p.fragH), stage + (size_t)(2 * l) * T * D, D, D});
-        gs.push_back({d->W(LW(l, "cross_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr,
-                      d->at<uint8_t>(d->p.fragH), stage + (size_t)(2 * l + 1) * T * D, D, D});
+        gs.push_back({d->W(LW(l, "cross_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, cfrag,
+                      stage + (size_t)(2 * l) * T * D, D, D});
+        gs.push_back({d->W(LW(l, "cross_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, cfrag,
+                      stage + (size_t)(2 * l + 1) * T * D, D, D});
     }
     // at most 12 groups per launch
     for (size_t i = 0; i < gs.size(); i += SK_MAX_GROUPS) {
@@ -344,6 +407,7 @@ fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, hipStream_t st) {
     k.cache = d->kv;
     k.max_ctx = c.max_ctx;
     k.kv_dtype = c.kv_dtype;
+    k.zeros = d->at<float>(d->p.zeros);
     HIPCHK(launch_kv_final(k, st));
     return FM_OK;
 }
@@ -357,7 +421,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         float* part = d->at<float>(d->p.part);
         CHK(skinny(d, {{d->W("fc.weight"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}},
                    KT, n, SK_PARTIAL, 0, &S, st));
-        RowArgs r = rows_base(D, n);
+        RowArgs r = rows_base(d, D, n);
         r.part = part;
         r.S = S;
         r.part_stride = (long long)TMAX * D;
@@ -366,7 +430,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         r.eps = c.rms_eps;
         r.frag_out = d->at<uint8_t>(d->p.fragH);
         CHK(rows(r, st));
-        return fm_kv_rows_small(d, n, start, st);
+        return fm_kv_rows_small(d, n, start, d->at<uint8_t>(d->p.fragH), st);
     }
     // prefill: MFMA GEMMs
     float* ctx = d->at<float>(d->p.pctx);
@@ -434,28 +498,35 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     const float* rope = d->at<float>(d->p.rope);
     const long long pstr = (long long)TMAX * D;
 
-    // anchor slot: anchor_norm(anchor_proj(E[anchor])) through every layer's k/v path at pos
-    HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, fragA, st));
-    int S = 0;
-    CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, 1,
-               SK_PARTIAL, 0, &S, st));
+    // anchor slot: anchor_norm(anchor_proj(E[anchor])) through every layer's k/v path at pos. It only has to be in
+    // the cache before the first cross-attention, so it runs on the side stream next to layer 0's self-attention
+    // branch (fork / join events; inside a graph capture these become parallel branches).
     {
-        RowArgs r = rows_base(D, 1);
-        r.part = part;
-        r.S = S;
+        hipStream_t as = d->side;
+        HIPCHK(hipEventRecord(d->ev_fork, st));
+        HIPCHK(hipStreamWaitEvent(as, d->ev_fork, 0));
+        uint8_t* afrag = d->at<uint8_t>(d->p.afrag);
+        uint8_t* cfrag = d->at<uint8_t>(d->p.cfrag);
+        float* apart = d->at<float>(d->p.apart);
+        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, afrag, as));
+        int Sa = 0;
+        CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, afrag, apart, D, D}}, Ht, 1,
+                   SK_PARTIAL, 0, &Sa, as));
+        RowArgs r = rows_base(d, D, 1);
+        r.part = apart;
+        r.S = Sa;
         r.part_stride = pstr;
         r.bias = d->B("anchor_proj.bias");
         r.norm = ROW_RMS;
         r.w_bf16 = d->B("anchor_norm.weight");
         r.eps = c.rms_eps;
-        r.frag_out = fragH;
-        CHK(rows(r, st));
+        r.frag_out = cfrag;
+        CHK(rows(r, as));
+        CHK(fm_kv_rows_small(d, 1, pos, cfrag, as));
+        HIPCHK(hipEventRecord(d->ev_join, as));
     }
-    CHK(fm_kv_rows_small(d, 1, pos, st));
-
+    int S = 0;
     const int L = pos + 1;
-    const int chunk = attn_chunk_size(hd, c.kv_dtype);
-    const int nchunks = (L + chunk - 1) / chunk;
     int S_prev = 0;           // split count of the pending residual update (fc2 of the previous layer)
     for (int l = 0; l < c.layers; ++l) {
         const float* m_sa = mod + (size_t)(3 * l) * 3 * D;
@@ -463,7 +534,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         const float* m_ml = mod + (size_t)(3 * l + 2) * 3 * D;
         // residual (previous layer's MLP) + self-attention modulation
         {
-            RowArgs r = rows_base(D, T);
+            RowArgs r = rows_base(d, D, T);
             r.x = x;
             if (l == 0) {
                 r.init = d->at<float>(d->p.h0);
@@ -507,7 +578,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
                    D, T, SK_PARTIAL, 0, &S, st));
         {
-            RowArgs r = rows_base(D, T);
+            RowArgs r = rows_base(d, D, T);
             r.x = x;
             r.part = part;
             r.S = S;
@@ -520,52 +591,28 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
             r.frag_out = fragH;
             CHK(rows(r, st));
         }
-        // cross-attention over cache rows [0, pos]
-        int Sq = 0;
-        CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, part, D, D}},
-                   D, T, SK_PARTIAL, 0, &Sq, st));
+        // cross-attention over cache rows [0, pos]: q = cross q_proj(h) (whole k-range per work-group), then
+        // per-head q_norm + RoPE inside the attention kernel
+        CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, D}},
+                   D, T, SK_F32, 0, nullptr, st));
+        if (l == 0) HIPCHK(hipStreamWaitEvent(st, d->ev_join, 0));   // the anchor slot is in the cache
         {
-            AttnArgs a{};
-            a.qp.part = part;
-            a.qp.S = Sq;
-            a.qp.part_stride = pstr;
-            a.qp.q_ld = D;
-            a.qp.q_hs = hd;
-            a.qp.norm_bf16 = d->B(LW(l, "cross_attn.q_norm.weight"));
-            a.qp.eps = c.qk_eps;
-            a.qp.rope = 1;
-            a.qp.rope_dims = d->p.rope_dims;
-            a.qp.rope_tab = rope;
-            a.qp.pos_base = pos + 1;
-            a.nq = T;
-            a.kc = d->kv_layer(l, 0);
-            a.vc = d->kv_layer(l, 1);
-            a.kv_ld = D;
-            a.kv_dtype = c.kv_dtype;
-            a.key_lo = 0;
-            a.key_hi = L;
-            a.heads = H;
-            a.kv_heads = H;
-            a.hd = hd;
-            a.causal_base = -1;
-            a.scale = 1.f / sqrtf((float)hd);
-            a.chunk = chunk;
-            a.nchunks = nchunks;
-            a.part = d->at<float>(d->p.attnp);
-            HIPCHK(launch_attn_split(a, st));
-            MergeArgs m{};
-            m.part = a.part;
-            m.heads = H;
-            m.nchunks = nchunks;
-            m.nq = T;
-            m.hd = hd;
-            m.o_frag = fragO;
-            HIPCHK(launch_attn_merge(m, st));
+            QPrep qp{};
+            qp.q = qkv;
+            qp.q_ld = D;
+            qp.q_hs = hd;
+            qp.norm_bf16 = d->B(LW(l, "cross_attn.q_norm.weight"));
+            qp.eps = c.qk_eps;
+            qp.rope = 1;
+            qp.rope_dims = d->p.rope_dims;
+            qp.rope_tab = rope;
+            qp.pos_base = pos + 1;
+            CHK(attend(d, qp, T, l, 0, L, nullptr, nullptr, 0, 0, -1, 1.f / sqrtf((float)hd), nullptr, 0, 0, fragO, st));
         }
         CHK(skinny(d, {{d->W(LW(l, "cross_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
                    D, T, SK_PARTIAL, 0, &S, st));
         {
-            RowArgs r = rows_base(D, T);
+            RowArgs r = rows_base(d, D, T);
             r.x = x;
             r.part = part;
             r.S = S;
@@ -587,7 +634,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     }
     {
         const float* m_f = mod + (size_t)(3 * c.layers) * 3 * D;
-        RowArgs r = rows_base(D, T);
+        RowArgs r = rows_base(d, D, T);
         r.x = x;
         r.part = part;
         r.S = S_prev;
@@ -613,7 +660,7 @@ fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     // zero-noise slot input h0 = x_embed(state_norm(mean row of E)) + b
     HIPCHK(launch_colmean(d->B("lm_head.weight"), c.vocab, Ht, d->at<float>(d->p.colsc), d->p.colR,
                           d->at<float>(d->p.cmean), st));
-    RowArgs r = rows_base(Ht, 1);
+    RowArgs r = rows_base(d, Ht, 1);
     r.init = d->at<float>(d->p.cmean);
     r.norm = ROW_RMS;
     r.w_bf16 = d->B("state_norm.weight");
@@ -643,7 +690,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
         CHK(skinny(d, {{d->W("W_c"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}}, KT, n,
                    SK_PARTIAL, 0, &S, st));
         float* hc = d->at<float>(d->p.hc);
-        RowArgs r = rows_base(D, n);
+        RowArgs r = rows_base(d, D, n);
         r.part = part;
         r.S = S;
         r.part_stride = (long long)TMAX * D;
@@ -656,7 +703,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
         // per layer: RMSNorm(H_ctx; attn_norm) -> K, V written straight into the f32 cache rows
         for (int i = 0; i < c.layers; ++i) {
             uint8_t* fr = i % 2 ? d->at<uint8_t>(d->p.fragO) : d->at<uint8_t>(d->p.fragH);
-            RowArgs q = rows_base(D, n);
+            RowArgs q = rows_base(d, D, n);
             q.in_rows = hc;
             q.in_ld = D;
             q.norm = ROW_RMS;
@@ -692,7 +739,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     }
     // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32), then per layer RMSNorm(H_ctx; attn_norm) -> f16
     {
-        RowArgs r = rows_base(D, n);
+        RowArgs r = rows_base(d, D, n);
         r.x = ctx;
         r.norm = ROW_RMS;
         r.w_bf16 = d->B("ctx_norm");
@@ -729,57 +776,6 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     return FM_OK;
 }
 
-// Attention of nq query rows over cache rows [key_lo, key_hi) (+ nx extra f32 rows), merged into o fragments.
-fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_lo, int key_hi, const float* kx,
-                 const float* vx, int nx, int x_ld, int causal_base, float scale, const float* gate, int gate_ld,
-                 int gate_hs, uint8_t* o_frag, hipStream_t st) {
-    const auto& c = d->c;
-    AttnArgs a{};
-    a.qp = qp;
-    a.nq = nq;
-    a.kv_dtype = c.kv_dtype;
-    if (c.variant == FM_VARIANT_MTP) {
-        const size_t w = (size_t)c.kv_heads * c.head_dim;
-        a.kc = d->kv;
-        a.vc = (const float*)d->kv + (size_t)c.max_ctx * w;
-        a.kv_ld = (int)w;
-    } else {
-        a.kc = d->kv_layer(layer_kv, 0);
-        a.vc = d->kv_layer(layer_kv, 1);
-        a.kv_ld = c.dim;
-    }
-    a.key_lo = key_lo;
-    a.key_hi = key_hi;
-    a.kx = kx;
-    a.vx = vx;
-    a.nx = nx;
-    a.x_ld = x_ld;
-    a.heads = c.heads;
-    a.kv_heads = c.kv_heads;
-    a.hd = c.head_dim;
-    a.causal_base = causal_base;
-    a.scale = scale;
-    a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype);
-    const int ntot = key_hi - key_lo + nx;
-    a.nchunks = (ntot + a.chunk - 1) / a.chunk;
-    if ((size_t)c.heads * a.nchunks * TMAX * (c.head_dim + 2) * 4 > d->p.attnp_bytes)
-        return fail(FM_E_INVALID, "attention partial buffer too small");
-    a.part = d->at<float>(d->p.attnp);
-    HIPCHK(launch_attn_split(a, st));
-    MergeArgs m{};
-    m.part = a.part;
-    m.heads = c.heads;
-    m.nchunks = a.nchunks;
-    m.nq = nq;
-    m.hd = c.head_dim;
-    m.gate = gate;
-    m.gate_ld = gate_ld;
-    m.gate_hs = gate_hs;
-    m.o_frag = o_frag;
-    HIPCHK(launch_attn_merge(m, st));
-    return FM_OK;
-}
-
 fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
     const auto& c = d->c;
     const int D = c.dim, T = c.block, Ht = c.target_dim, hd = c.head_dim;
@@ -799,7 +795,7 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
     CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, 1, SK_PARTIAL, 0,
                &S, st));
     {
-        RowArgs r = rows_base(D, T);
+        RowArgs r = rows_base(d, D, T);
         r.x = x;
         r.base_zero = 1;
         r.part = part;
@@ -831,7 +827,7 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
         CHK(skinny(d, {{d->W(BB(i, "o")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}}, D, T, SK_PARTIAL, 0,
                    &S, st));
         {
-            RowArgs r = rows_base(D, T);
+            RowArgs r = rows_base(d, D, T);
             r.x = x;
             r.part = part;
             r.S = S;
@@ -847,7 +843,7 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
         CHK(skinny(d, {{d->W(BB(i, "down")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
                    SK_PARTIAL, 0, &S, st));
         {
-            RowArgs r = rows_base(D, T);
+            RowArgs r = rows_base(d, D, T);
             r.x = x;
             r.part = part;
             r.S = S;
@@ -884,7 +880,7 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
 
     // x = eh_proj([enorm(e); hnorm(h)])
     for (int side = 0; side < 2; ++side) {
-        RowArgs r = rows_base(H, M);
+        RowArgs r = rows_base(d, H, M);
         r.in_rows = side == 0 ? ba->embed_rows : ba->prev_hidden;
         r.in_ld = H;
         r.norm = ROW_RMS;
@@ -898,7 +894,7 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
     CHK(skinny(d, {{Q("eh_proj"), Dd("eh_proj"), nullptr, nullptr, nullptr, fragA, part, H, H}}, 2 * H, M, SK_PARTIAL,
                0, &S, st));
     {
-        RowArgs r = rows_base(H, M);
+        RowArgs r = rows_base(d, H, M);
         r.x = x;
         r.base_zero = 1;
         r.part = part;
@@ -947,7 +943,7 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
     CHK(skinny(d, {{Q("attn_output"), Dd("attn_output"), nullptr, nullptr, nullptr, fragO, part, H, H}}, NH * HD, M,
                SK_PARTIAL, 0, &S, st));
     {
-        RowArgs r = rows_base(H, M);
+        RowArgs r = rows_base(d, H, M);
         r.x = x;
         r.part = part;
         r.S = S;
@@ -963,7 +959,7 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
     CHK(skinny(d, {{Q("ffn_down"), Dd("ffn_down"), nullptr, nullptr, nullptr, fragU, part, H, H}}, c.ffn, M,
                SK_PARTIAL, 0, &S, st));
     {
-        RowArgs r = rows_base(H, M);
+        RowArgs r = rows_base(d, H, M);
         r.x = x;
         r.part = part;
         r.S = S;
@@ -1029,7 +1025,17 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
     hipStream_t st = (hipStream_t)stream;
     fm_status s = FM_OK;
     do {
+        if (cfg->variant == FM_VARIANT_FLOWMAP) {
+            hipError_t e = hipStreamCreateWithFlags(&d->side, hipStreamNonBlocking);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_fork, hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_join, hipEventDisableTiming);
+            if (e != hipSuccess) { s = fail(FM_E_HIP, "side stream: %s", hipGetErrorString(e)); break; }
+        }
         if (launch_fill_u32(d->at<uint32_t>(d->p.best), 32, 0u, st) != hipSuccess) { s = fail(FM_E_HIP, "fill"); break; }
+        if (launch_fill_u32(d->at<uint32_t>(d->p.zeros), d->p.zeros_bytes / 4, 0u, st) != hipSuccess) {
+            s = fail(FM_E_HIP, "fill");
+            break;
+        }
         if (cfg->rope != FM_ROPE_NONE) {
             hipError_t e = launch_rope_table(d->at<float>(d->p.rope), d->p.rope_rows, d->p.rope_dims, cfg->rope_theta, st);
             if (e != hipSuccess) { s = fail(FM_E_HIP, "rope table: %s", hipGetErrorString(e)); break; }
@@ -1037,7 +1043,7 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
         if (cfg->variant == FM_VARIANT_FLOWMAP) s = flowmap_create(d, st);
         else if (cfg->variant == FM_VARIANT_KVINJECT) s = kvinject_create(d, st);
     } while (0);
-    if (s != FM_OK) { delete d; return s; }
+    if (s != FM_OK) { fm_destroy(d); return s; }
     *out = d;
     return FM_OK;
 }
@@ -1108,7 +1114,13 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
 
 int32_t fm_context_length(const fm_drafter* d) { return d ? d->length : -1; }
 
-void fm_destroy(fm_drafter* d) { delete d; }
+void fm_destroy(fm_drafter* d) {
+    if (!d) return;
+    if (d->ev_fork) (void)hipEventDestroy(d->ev_fork);
+    if (d->ev_join) (void)hipEventDestroy(d->ev_join);
+    if (d->side) (void)hipStreamDestroy(d->side);
+    delete d;
+}
 
 const char* fm_last_error(void) { return g_err.c_str(); }
 

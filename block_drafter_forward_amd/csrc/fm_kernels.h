@@ -73,6 +73,7 @@ struct RowArgs {
     const uint16_t* base_bf16;  // rows t >= base_from take their base from these bf16 rows [(t - base_from)][D]
     int base_from;
     const uint16_t* row_bias_bf16;  // bf16 [T][D] added to row t (or null)
+    const float* zeros;    // a zero row of >= D floats (absent inputs read it; required)
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
@@ -94,12 +95,10 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 
 // ── K4: attention ──────────────────────────────────────────────────────────────────────────────
 struct QPrep {             // how a work-group builds its query rows for one head
-    const float* q;        // q rows: q[t*q_ld + h*q_hs + d] ...
+    const float* q;        // q rows: q[t*q_ld + h*q_hs + d]
     int q_ld;
     int q_hs;
-    const float* part;     // ... or the sum of S partial slabs [S][T][q_ld] (same indexing)
-    long long part_stride;
-    int S;
+    const float* zeros;    // a zero row of >= 256 floats (absent inputs read it; required)
     const uint16_t* norm_bf16;  // head RMSNorm weight (bf16 or f32) or null
     const float* norm_f32;
     float eps;
@@ -166,6 +165,7 @@ struct KVFinalArgs {
     void* cache;           // layer l: K at l*2*max_ctx*D, V at (2l+1)*max_ctx*D (elements)
     int max_ctx;
     int kv_dtype;
+    const float* zeros;    // zero row (absent norm weights / RoPE read it)
 };
 hipError_t launch_kv_final(const KVFinalArgs& a, hipStream_t st);
 

@@ -2,9 +2,11 @@
 //
 //  self_attn     flow-map self-attention over the T slots (one work-group per head): per-head q/k RMSNorm,
 //                interleaved RoPE at the slots' positions, softmax(q kᵀ / sqrt(hd)) v with no mask
-//                (flashmap_drafter.js: headNormRope, attnF32); o leaves as fragments for the o_proj GEMM.
+//                (flashmap_drafter.js: headNormRope, attnF32), both products on f16 MFMA with hi/lo splits;
+//                o leaves as fragments for the o_proj GEMM.
 //  attn_split    up to 16 query rows of one head against one chunk of keys (cache rows, then optional extra f32
-//                rows): scores, chunk max, exp-sum and the unnormalised P·V, written as a partial. Splitting the key
+//                rows): scores, chunk max, exp-sum and the unnormalised P·V, written as a partial; f16 caches run
+//                both products on the matrix cores, f32 caches on the vector ALU. Splitting the key
 //                range across work-groups (flash-decoding) removes the page's 4096-key shared-memory cap and gives
 //                long contexts enough work-groups; the queries' own head-norm + RoPE (or the sum of their split-K
 //                partials) is rebuilt per work-group so it needs no extra launch.
@@ -24,17 +26,22 @@ __device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
 }
 
 // ── self-attention ───────────────────────────────────────────────────────────────────────────────
-// All global loads (q, k, v of the head, the two norm weights, the slots' RoPE rows) are issued before the first
-// use, so the work-group pays one memory round trip.
-__global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
+// Self-attention with both products on the matrix cores (one work-group per head): after the f32 head-norm and
+// RoPE, q, k and v are split into f16 hi + lo; scores take three MFMAs per 32-dim step (hi·hi + hi·lo + lo·hi, the
+// dropped lo·lo term is below 2^-22 relative), P·V likewise with the 16 keys padded to the MFMA's 32.
+__global__ __launch_bounds__(256) void self_attn_mfma_kernel(SelfAttnArgs a) {
     const int h = blockIdx.x;
     const int T = a.T, hd = a.hd, D = a.D;
-    __shared__ float X[3][16][129];   // q, k, v rows of this head (hd <= 128)
+    constexpr int XR = 129, FR = 136, VR = 40;   // pitches: f32 rows, f16 rows (hd <= 128), transposed V rows
+    __shared__ float X[3][16][XR];
     __shared__ float P[16][17];
     __shared__ float NW[2][128];
-    __shared__ float RT[16][128];     // RoPE rows [cos hd/2 | sin hd/2] of the T slots
+    __shared__ float RT[16][128];
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[16 * FR], Ql[16 * FR], Kh[16 * FR], Kl[16 * FR];
+    __shared__ __attribute__((aligned(16))) _Float16 Vh[128 * VR], Vl[128 * VR];
+    __shared__ __attribute__((aligned(16))) _Float16 Ph[16 * VR], Pl[16 * VR];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int q4 = hd >> 2;           // float4 per row
+    const int q4 = hd >> 2;
     const int n4 = 3 * T * q4;
     float4 xv[6];
 #pragma unroll
@@ -44,8 +51,8 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         const int w = ii / (T * q4), r = ii % (T * q4), t = r / q4, d4 = r % q4;
         xv[j] = *(const float4*)(a.qkv + (size_t)t * 3 * D + (size_t)w * D + (size_t)h * hd + 4 * d4);
     }
-    float nw = 0.f;
-    if (tid < 2 * hd) nw = bf16_to_f32((tid < hd ? a.qn : a.kn)[tid % hd]);
+    const int nwi = tid < 2 * hd ? tid : 0;
+    const float nw = bf16_to_f32((nwi < hd ? a.qn : a.kn)[nwi % hd]);
     float rt[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -53,6 +60,8 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         const int ii = i < T * hd ? i : T * hd - 1;
         rt[j] = a.rope_tab[(size_t)(a.pos_base + ii / hd) * hd + ii % hd];
     }
+    for (int i = tid; i < 3 * 16 * XR; i += 256) (&X[0][0][0])[i] = 0.f;
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
         const int i = tid + 256 * j;
@@ -69,7 +78,6 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         if (i < T * hd) RT[i / hd][i % hd] = rt[j];
     }
     __syncthreads();
-    // head RMSNorm of the q and k rows (one wave per row)
     for (int row = wave; row < 2 * T; row += 4) {
         const int w = row / T, t = row % T;
         float ss = 0.f;
@@ -79,7 +87,6 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         for (int d = lane; d < hd; d += 64) X[w][t][d] = X[w][t][d] * (NW[w][d] * r);
     }
     __syncthreads();
-    // interleaved RoPE: pairs (2i, 2i+1) at position pos_base + t
     const int half = hd >> 1;
     for (int i = tid; i < 2 * T * half; i += 256) {
         const int row = i / half, pi = i % half, w = row / T, t = row % T;
@@ -89,22 +96,61 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         X[w][t][2 * pi + 1] = x1 * c + x0 * sn;
     }
     __syncthreads();
-    {
-        const int t = tid >> 4, u = tid & 15;
-        if (t < T && u < T) {
-            float sc = 0.f;
-            for (int d = 0; d < hd; ++d) sc += X[0][t][d] * X[1][u][d];
-            P[t][u] = sc * a.scale;
+    // f16 hi/lo splits; V transposed (dim-major), keys T..31 zero
+    for (int i = tid; i < 16 * hd; i += 256) {
+        const int t = i / hd, d = i % hd;
+        const float q = X[0][t][d], k = X[1][t][d], v = X[2][t][d];
+        const _Float16 qh = (_Float16)q, kh = (_Float16)k, vh = (_Float16)v;
+        Qh[t * FR + d] = qh; Ql[t * FR + d] = (_Float16)(q - (float)qh);
+        Kh[t * FR + d] = kh; Kl[t * FR + d] = (_Float16)(k - (float)kh);
+        Vh[d * VR + t] = vh; Vl[d * VR + t] = (_Float16)(v - (float)vh);
+        Vh[d * VR + 16 + t] = (_Float16)0.f; Vl[d * VR + 16 + t] = (_Float16)0.f;
+    }
+    __syncthreads();
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    if (wave == 0) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < hd / 32; ++s) {
+            const f16x8_t A = *(const f16x8_t*)(Kh + fr * FR + s * 32 + fk);
+            const f16x8_t Al = *(const f16x8_t*)(Kl + fr * FR + s * 32 + fk);
+            const f16x8_t B = *(const f16x8_t*)(Qh + fr * FR + s * 32 + fk);
+            const f16x8_t Bl = *(const f16x8_t*)(Ql + fr * FR + s * 32 + fk);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, acc, 0, 0, 0);
+        }
+        // lane holds S[t = lane % 16][u = 4 (lane / 16) + i]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P[fr][4 * (lane >> 4) + i] = acc[i] * a.scale;
+    }
+    __syncthreads();
+    if (tid < 16) {
+        const int t = tid;
+        float m = -INFINITY;
+        for (int u = 0; u < T; ++u) m = fmaxf(m, P[t][u]);
+        float z = 0.f, e[16];
+        for (int u = 0; u < 16; ++u) { e[u] = (u < T && t < T) ? expf(P[t][u] - m) : 0.f; z += e[u]; }
+        const float iz = z > 0.f ? 1.f / z : 0.f;
+        for (int u = 0; u < 32; ++u) {
+            const float p = u < 16 ? e[u] * iz : 0.f;
+            const _Float16 ph = (_Float16)p;
+            Ph[t * VR + u] = ph;
+            Pl[t * VR + u] = (_Float16)(p - (float)ph);
         }
     }
     __syncthreads();
-    if (tid < T) {
-        float m = -INFINITY;
-        for (int u = 0; u < T; ++u) m = fmaxf(m, P[tid][u]);
-        float z = 0.f;
-        for (int u = 0; u < T; ++u) { const float e = expf(P[tid][u] - m); P[tid][u] = e; z += e; }
-        const float iz = 1.f / z;
-        for (int u = 0; u < T; ++u) P[tid][u] *= iz;
+    // O[t][d]: wave w owns dim tiles w, w + 4; result staged in X[0] for the fragment store
+    for (int dt = wave; dt < hd / 16; dt += 4) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const f16x8_t A = *(const f16x8_t*)(Ph + fr * VR + fk);
+        const f16x8_t Al = *(const f16x8_t*)(Pl + fr * VR + fk);
+        const f16x8_t B = *(const f16x8_t*)(Vh + (dt * 16 + fr) * VR + fk);
+        const f16x8_t Bl = *(const f16x8_t*)(Vl + (dt * 16 + fr) * VR + fk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[0][4 * (lane >> 4) + i][dt * 16 + fr] = acc[i];
     }
     __syncthreads();
     const int per = hd >> 3;
@@ -112,12 +158,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         const int t = slot / per, d0 = (slot % per) * 8;
         float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
-        for (int u = 0; u < T; ++u) {
-            const float p = P[t][u];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += p * X[2][u][d0 + e];
-        }
+        for (int e = 0; e < 8; ++e) o[e] = X[0][t][d0 + e];
         frag_store8(a.o_frag, t, h * hd + d0, o);
     }
 }
@@ -159,39 +200,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     const int k0 = c * C;
     const int cnt = min(C, ntot - k0);
 
-    // 1. prefetch
-    constexpr int QPT = 16 * HD / 256;          // query values per thread (nq <= 16)
-    float qv[QPT];
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + 256 * j;
-        const int t = i / HD, d = i % HD;
-        const int tt = t < nq ? t : 0;
-        const size_t off = (size_t)tt * qp.q_ld + (size_t)h * qp.q_hs + d;
-        float v;
-        if (qp.part) {
-            v = qp.part[off];
-#pragma unroll
-            for (int s2 = 1; s2 < 8; ++s2)
-                if (s2 < qp.S) v += qp.part[(size_t)s2 * qp.part_stride + off];
-        } else {
-            v = qp.q[off];
-        }
-        qv[j] = v;
-    }
-    float nwv = 0.f;
-    if (tid < HD && (qp.norm_bf16 || qp.norm_f32)) nwv = qp.norm_bf16 ? bf16_to_f32(qp.norm_bf16[tid]) : qp.norm_f32[tid];
-    float ropev[QPT];
-    if (qp.rope) {
-        const int rd = qp.rope_dims;
-#pragma unroll
-        for (int j = 0; j < QPT; ++j) {
-            const int i = tid + 256 * j;
-            const int t = i / HD, d = i % HD;
-            const int tt = t < nq ? t : 0;
-            ropev[j] = d < rd ? qp.rope_tab[(size_t)(qp.pos_base + tt) * rd + d] : 0.f;
-        }
-    }
+    // 1. prefetch: the chunk's K and V rows first, then the queries (every load unconditional; absent inputs
+    //    read the zero row), all in flight before the first use
     uint4 kr[SS::LD16], vr[SS::LD16];
 #pragma unroll
     for (int j = 0; j < SS::LD16; ++j) {
@@ -207,6 +217,23 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         kr[j] = *((const uint4*)(kb + (size_t)kh * HD) + p16);
         vr[j] = *((const uint4*)(vb + (size_t)kh * HD) + p16);
     }
+    constexpr int QPT = 16 * HD / 256;          // query values per thread (nq <= 16)
+    float qv[QPT], ropev[QPT];
+    const float* ropep = qp.rope ? qp.rope_tab : qp.zeros;
+    const int rd = qp.rope ? qp.rope_dims : 0;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + 256 * j;
+        const int t = i / HD, d = i % HD;
+        const int tt = t < nq ? t : 0;
+        qv[j] = qp.q[(size_t)tt * qp.q_ld + (size_t)h * qp.q_hs + d];
+        const int dd = d < rd ? d : 0;
+        ropev[j] = ropep[(size_t)(qp.rope ? qp.pos_base + tt : 0) * rd + dd];
+    }
+    const bool has_norm = qp.norm_bf16 || qp.norm_f32;
+    const float nw16 = bf16_to_f32((qp.norm_bf16 ? qp.norm_bf16 : (const uint16_t*)qp.zeros)[tid % HD]);
+    const float nw32 = (qp.norm_f32 ? qp.norm_f32 : qp.zeros)[tid % HD];
+    const float nwv = qp.norm_bf16 ? nw16 : nw32;
     // 2. to LDS
     constexpr int RTW = HD <= 128 ? HD : 128;   // RoPE'd dims of a query head (NEOX rotates at most 128 here)
     __shared__ float nws[HD], rts[16][RTW];
@@ -217,6 +244,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         if (qp.rope && i % HD < RTW) rts[i / HD][i % HD] = ropev[j];
     }
     if (tid < HD) nws[tid] = nwv;
+    (void)has_norm;
 #pragma unroll
     for (int j = 0; j < SS::LD16; ++j) {
         const int u = tid + 256 * j;
@@ -358,30 +386,261 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     }
 }
 
+// ── split-L attention on the matrix cores (f16 cache) ────────────────────────────────────────────
+// One work-group = one head x one chunk of C keys (16 KB of K and 16 KB of V), 4 waves:
+//   scores  Sᵀ[j][t] = sum_d K[j][d] q[t][d] on v_mfma_f32_16x16x32_f16: A = K rows straight from LDS (exact f16),
+//           B = the queries split q = hi + lo in f16 (two MFMAs, ~22 significant bits);
+//   softmax per query row over the chunk (max, exp, sum) in f32;
+//   P.V     O[t][d] = sum_j P[t][j] V[j][d]: A = P split hi/lo in f16, B = V read from a transposed LDS copy
+//           (dim-major) so each lane's 8 keys are one 16-byte read.
+// All global loads (K, V, queries, norm weight, RoPE rows) are issued before the first use.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
+    constexpr int C = 16384 / (HD * 2);        // keys per chunk: 64 (HD 128), 128 (HD 64)
+    constexpr int KROW = HD + 8;               // LDS row pitches (halfs), 16-byte pad
+    constexpr int VROW = C + 8;
+    constexpr int PROW = C + 8;
+    constexpr int QROW = HD + 8;
+    constexpr int V16 = HD * 2 / 16;           // 16-byte pieces per key row
+    constexpr int LD16 = C * V16 / 256;
+    constexpr int QPT = 16 * HD / 256;
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int nq = a.nq;
+    const int kh = h / (a.heads / a.kv_heads);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const QPrep& qp = a.qp;
+    __shared__ __attribute__((aligned(16))) _Float16 Ks[C * KROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Vt[HD * VROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[16 * QROW], Ql[16 * QROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Ph[16 * PROW], Pl[16 * PROW];
+    __shared__ float qs[16][HD];
+    __shared__ float S[16][C + 1];
+    __shared__ float nws[HD], rts[16][HD];
+    __shared__ float mrow[16], lrow[16];
+
+    const int ncache = a.key_hi - a.key_lo;
+    const int k0 = c * C;
+    const int cnt = min(C, ncache - k0);
+
+    // 1. prefetch
+    uint4 kr[LD16], vr[LD16];
+#pragma unroll
+    for (int j = 0; j < LD16; ++j) {
+        const int u = tid + 256 * j;
+        const int row = u / V16, p16 = u % V16;
+        const int kidx = min(k0 + row, ncache - 1);
+        const size_t off = (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD;
+        kr[j] = *((const uint4*)((const uint16_t*)a.kc + off) + p16);
+        vr[j] = *((const uint4*)((const uint16_t*)a.vc + off) + p16);
+    }
+    float qv[QPT], ropev[QPT];
+    const float* ropep = qp.rope ? qp.rope_tab : qp.zeros;
+    const int rd = qp.rope ? qp.rope_dims : 0;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + 256 * j;
+        const int t = i / HD, d = i % HD;
+        const int tt = t < nq ? t : 0;
+        qv[j] = qp.q[(size_t)tt * qp.q_ld + (size_t)h * qp.q_hs + d];
+        const int dd = d < rd ? d : 0;
+        ropev[j] = ropep[(size_t)(qp.rope ? qp.pos_base + tt : 0) * rd + dd];
+    }
+    const bool has_norm = qp.norm_bf16 || qp.norm_f32;
+    const float nw16 = bf16_to_f32((qp.norm_bf16 ? qp.norm_bf16 : (const uint16_t*)qp.zeros)[tid % HD]);
+    const float nw32 = (qp.norm_f32 ? qp.norm_f32 : qp.zeros)[tid % HD];
+
+    // 2. to LDS: K row-major, V transposed (dim-major), queries f32
+#pragma unroll
+    for (int j = 0; j < LD16; ++j) {
+        const int u = tid + 256 * j;
+        const int row = u / V16, p16 = u % V16;
+        *(uint4*)(Ks + row * KROW + p16 * 8) = kr[j];
+        const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Vt[(p16 * 8 + 2 * e) * VROW + row] = __builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xffffu));
+            Vt[(p16 * 8 + 2 * e + 1) * VROW + row] = __builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + 256 * j;
+        qs[i / HD][i % HD] = (i / HD) < nq ? qv[j] : 0.f;
+        rts[i / HD][i % HD] = ropev[j];
+    }
+    if (tid < HD) nws[tid] = qp.norm_bf16 ? nw16 : nw32;
+    __syncthreads();
+    // 3. query head-norm + RoPE (f32), then the hi/lo f16 split
+    if (has_norm) {
+        for (int t = wave; t < nq; t += 4) {
+            float ss = 0.f;
+            for (int d = lane; d < HD; d += 64) ss += qs[t][d] * qs[t][d];
+            ss = wave_sum(ss);
+            const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
+            for (int d = lane; d < HD; d += 64) qs[t][d] *= nws[d] * r;
+        }
+        __syncthreads();
+    }
+    if (qp.rope == 1) {
+        const int half = HD / 2;
+        for (int i = tid; i < nq * half; i += 256) {
+            const int t = i / half, pi = i % half;
+            const float cs = rts[t][pi], sn = rts[t][half + pi];
+            const float x0 = qs[t][2 * pi], x1 = qs[t][2 * pi + 1];
+            qs[t][2 * pi] = x0 * cs - x1 * sn;
+            qs[t][2 * pi + 1] = x1 * cs + x0 * sn;
+        }
+        __syncthreads();
+    } else if (qp.rope == 2) {
+        const int half = qp.rope_dims / 2;
+        for (int i = tid; i < nq * half; i += 256) {
+            const int t = i / half, pi = i % half;
+            const float cs = rts[t][pi], sn = rts[t][half + pi];
+            const float x0 = qs[t][pi], x1 = qs[t][pi + half];
+            qs[t][pi] = x0 * cs - x1 * sn;
+            qs[t][pi + half] = x1 * cs + x0 * sn;
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < 16 * HD; i += 256) {
+        const int t = i / HD, d = i % HD;
+        const float x = qs[t][d];
+        const _Float16 hi = (_Float16)x;
+        Qh[t * QROW + d] = hi;
+        Ql[t * QROW + d] = (_Float16)(x - (float)hi);
+    }
+    __syncthreads();
+    // 4. scores: wave w owns key tiles w, w+4, ...
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    for (int kt = wave; kt < C / 16; kt += 4) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < HD / 32; ++s) {
+            const f16x8_t A = *(const f16x8_t*)(Ks + (kt * 16 + fr) * KROW + s * 32 + fk);
+            const f16x8_t Bh = *(const f16x8_t*)(Qh + fr * QROW + s * 32 + fk);
+            const f16x8_t Bl = *(const f16x8_t*)(Ql + fr * QROW + s * 32 + fk);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+        }
+        // lane holds keys j = 16 kt + 4 (lane / 16) + i for query t = lane % 16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = kt * 16 + 4 * (lane >> 4) + i;
+            const int kidx = k0 + j;
+            float v = acc[i] * a.scale;
+            if (j >= cnt) v = -INFINITY;
+            if (a.causal_base >= 0 && a.key_lo + kidx > a.causal_base + fr) v = -INFINITY;
+            S[fr][j] = v;
+        }
+    }
+    __syncthreads();
+    // 5. softmax statistics per query row; P = exp(S - m) split hi/lo in f16
+    for (int t = wave; t < 16; t += 4) {
+        float m = -INFINITY;
+        for (int j = lane; j < C; j += 64) m = fmaxf(m, S[t][j]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int j = lane; j < C; j += 64) {
+            const float p = (m == -INFINITY || t >= nq) ? 0.f : expf(S[t][j] - m);
+            const _Float16 hi = (_Float16)p;
+            Ph[t * PROW + j] = hi;
+            Pl[t * PROW + j] = (_Float16)(p - (float)hi);
+            l += p;
+        }
+        l = wave_sum(l);
+        if (lane == 0) { mrow[t] = m; lrow[t] = l; }
+    }
+    __syncthreads();
+    // 6. O = P V: wave w owns dim tiles w, w+4, ...
+    float* out = a.part + ((size_t)h * a.nchunks + c) * nq * (HD + 2);
+    for (int dt = wave; dt < HD / 16; dt += 4) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < C / 32; ++s) {
+            const f16x8_t Ah = *(const f16x8_t*)(Ph + fr * PROW + s * 32 + fk);
+            const f16x8_t Al = *(const f16x8_t*)(Pl + fr * PROW + s * 32 + fk);
+            const f16x8_t B = *(const f16x8_t*)(Vt + (dt * 16 + fr) * VROW + s * 32 + fk);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, acc, 0, 0, 0);
+        }
+        // lane holds O[t = 4 (lane / 16) + i][d = 16 dt + lane % 16]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * (lane >> 4) + i;
+            if (t < nq) out[(size_t)t * (HD + 2) + dt * 16 + fr] = acc[i];
+        }
+    }
+    if (tid < nq) {
+        out[(size_t)tid * (HD + 2) + HD] = mrow[tid];
+        out[(size_t)tid * (HD + 2) + HD + 1] = lrow[tid];
+    }
+}
+
+// One work-group per (head, query row): thread (4-dim group, chunk group) folds its chunks with the online
+// rescale, four chunks' loads in flight at a time; the chunk groups are then folded in LDS.
+template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-    const int h = blockIdx.x;
-    const int HD = a.hd, per = HD >> 3;
-    const float* base = a.part + (size_t)h * a.nchunks * a.nq * (HD + 2);
-    for (int slot = threadIdx.x; slot < a.nq * per; slot += 256) {
-        const int t = slot / per, d0 = (slot % per) * 8;
-        float M = -INFINITY;
-        for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, base[((size_t)c * a.nq + t) * (HD + 2) + HD]);
-        float l = 0.f, o[8];
+    constexpr int DV = HD / 4, G = 256 / DV;
+    const int h = blockIdx.x, t = blockIdx.y;
+    const int d4 = threadIdx.x % DV, cg = threadIdx.x / DV;
+    const int nc = a.nchunks;
+    const float* base = a.part + (size_t)h * nc * a.nq * (HD + 2) + (size_t)t * (HD + 2);
+    const size_t cstride = (size_t)a.nq * (HD + 2);
+    float M = -INFINITY, Ls = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = cg; c0 < nc; c0 += 4 * G) {
+        float4 o[4];
+        float m[4], l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * G;
+            const int cc = c < nc ? c : cg;
+            const float* p = base + (size_t)cc * cstride;
+            o[u] = *(const float4*)(p + 4 * d4);
+            m[u] = c < nc ? p[HD] : -INFINITY;
+            l[u] = p[HD + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (m[u] == -INFINITY) continue;
+            const float Mn = fmaxf(M, m[u]);
+            const float a0 = (M == -INFINITY) ? 0.f : expf(M - Mn), a1 = expf(m[u] - Mn);
+            Ls = Ls * a0 + l[u] * a1;
+            O.x = O.x * a0 + o[u].x * a1; O.y = O.y * a0 + o[u].y * a1;
+            O.z = O.z * a0 + o[u].z * a1; O.w = O.w * a0 + o[u].w * a1;
+            M = Mn;
+        }
+    }
+    __shared__ float sm[G], sl[G];
+    __shared__ float so[G][HD];
+    if (d4 == 0) { sm[cg] = M; sl[cg] = Ls; }
+    so[cg][4 * d4] = O.x; so[cg][4 * d4 + 1] = O.y; so[cg][4 * d4 + 2] = O.z; so[cg][4 * d4 + 3] = O.w;
+    __syncthreads();
+    const int per = HD / 8;
+    if (threadIdx.x < per) {
+        const int d0 = threadIdx.x * 8;
+        float MM = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < G; ++g) MM = fmaxf(MM, sm[g]);
+        float L = 0.f, o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.f;
-        for (int c = 0; c < a.nchunks; ++c) {
-            const float* p = base + ((size_t)c * a.nq + t) * (HD + 2);
-            const float mc = p[HD];
-            const float w = (mc == -INFINITY) ? 0.f : expf(mc - M);
-            l += w * p[HD + 1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += w * p[d0 + e];
+        for (int g = 0; g < G; ++g) {
+            const float w = sm[g] == -INFINITY ? 0.f : expf(sm[g] - MM);
+            L += w * sl[g];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += w * so[g][d0 + e];
         }
-        const float il = 1.f / l;
+        const float il = 1.f / L;
+        float gt[8];
+        const float* gp = a.gate ? a.gate + (size_t)t * a.gate_ld + (size_t)h * a.gate_hs + d0 : nullptr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gt[e] = gp ? gp[e] : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             o[e] *= il;
-            if (a.gate) o[e] *= sigmoidf(a.gate[(size_t)t * a.gate_ld + (size_t)h * a.gate_hs + d0 + e]);
+            if (gp) o[e] *= sigmoidf(gt[e]);
         }
         frag_store8(a.o_frag, t, h * HD + d0, o);
     }
@@ -397,11 +656,16 @@ __global__ __launch_bounds__(256) void kv_final_kernel(KVFinalArgs a) {
     const size_t kbase = (size_t)(2 * l) * a.max_ctx * D + row;
     const size_t vbase = (size_t)(2 * l + 1) * a.max_ctx * D + row;
     const uint16_t* nw = a.knorm[l];
+    const uint16_t* nwp = nw ? nw : (const uint16_t*)a.zeros;
+    const float* tr = nw ? a.rope_tab + (size_t)(a.start + t) * a.rope_dims : a.zeros;
     for (int slot = threadIdx.x; slot < D / 8; slot += 256) {
         const int i0 = slot * 8, d0 = i0 % hd;
-        float k[8], v[8];
+        float k[8], v[8], wn[8], cs[4], sn[4];
+        const int half = nw ? a.rope_dims >> 1 : 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { k[e] = krow[i0 + e]; v[e] = vrow[i0 + e]; }
+        for (int e = 0; e < 8; ++e) { k[e] = krow[i0 + e]; v[e] = vrow[i0 + e]; wn[e] = bf16_to_f32(nwp[d0 + e]); }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { cs[e] = tr[(d0 >> 1) + e]; sn[e] = tr[half + (d0 >> 1) + e]; }
         if (nw) {
             float ss = 0.f;
 #pragma unroll
@@ -409,13 +673,10 @@ __global__ __launch_bounds__(256) void kv_final_kernel(KVFinalArgs a) {
             for (int o = 1; o < per; o <<= 1) ss += __shfl_xor(ss, o, 64);
             const float r = 1.f / sqrtf(ss / (float)hd + a.eps);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) k[e] *= bf16_to_f32(nw[d0 + e]) * r;
-            const float* tr = a.rope_tab + (size_t)(a.start + t) * a.rope_dims;
-            const int half = a.rope_dims >> 1;
+            for (int e = 0; e < 8; ++e) k[e] *= wn[e] * r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int pi = (d0 >> 1) + e;
-                const float c = tr[pi], s = tr[half + pi];
+                const float c = cs[e], s = sn[e];
                 const float x0 = k[2 * e], x1 = k[2 * e + 1];
                 k[2 * e] = x0 * c - x1 * s;
                 k[2 * e + 1] = x1 * c + x0 * s;
@@ -478,21 +739,21 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
 
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
     if (a.hd > 128 || a.T > 16) return hipErrorInvalidValue;
-    self_attn_kernel<<<a.heads, 256, 0, st>>>(a);
+    self_attn_mfma_kernel<<<a.heads, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
 int attn_chunk_size(int hd, int kv_dtype) { return 16384 / (hd * (kv_dtype == 0 ? 2 : 4)); }
 
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
-    if (a.nq > 16 || a.chunk != attn_chunk_size(a.hd, a.kv_dtype)) return hipErrorInvalidValue;
+    if (a.nq > 16 || a.chunk != attn_chunk_size(a.hd, a.kv_dtype) || !a.qp.zeros || !a.qp.q) return hipErrorInvalidValue;
+    if (a.qp.rope && a.qp.rope_dims > (a.hd <= 128 ? a.hd : 128)) return hipErrorInvalidValue;
     if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
     dim3 grid(a.nchunks, a.heads);
     if (a.kv_dtype == 0) {
         switch (a.hd) {
-        case 64: attn_split_kernel<64, 0><<<grid, 256, 0, st>>>(a); break;
-        case 128: attn_split_kernel<128, 0><<<grid, 256, 0, st>>>(a); break;
-        case 256: attn_split_kernel<256, 0><<<grid, 256, 0, st>>>(a); break;
+        case 64: attn_split_mfma_kernel<64><<<grid, 256, 0, st>>>(a); break;
+        case 128: attn_split_mfma_kernel<128><<<grid, 256, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     } else {
@@ -507,7 +768,13 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st) {
-    attn_merge_kernel<<<a.heads, 256, 0, st>>>(a);
+    dim3 grid(a.heads, a.nq);
+    switch (a.hd) {
+    case 64: attn_merge_kernel<64><<<grid, 256, 0, st>>>(a); break;
+    case 128: attn_merge_kernel<128><<<grid, 256, 0, st>>>(a); break;
+    case 256: attn_merge_kernel<256><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -24,63 +24,63 @@ __device__ __forceinline__ void st8(float* p, const float* v) {
     *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Every global load of the row (base, partial slabs, bias, gate, and the norm's own parameters) is issued before
-// the first arithmetic, so the work-group pays one memory round trip; S <= 8 partial slabs.
-template <int NS>
+// Every global load of the row (base, S partial slabs, bias, per-row bias, gate, and the norm's parameters) is
+// unconditional -- absent inputs read the workspace's zero row and are masked arithmetically -- and issued before
+// the first arithmetic. (A load inside a data-dependent branch makes the compiler wait for all outstanding loads
+// at the branch, which turned this kernel into a chain of serial memory round trips.)
+template <int NS, int S>
 __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     const int t = blockIdx.x;
     const int D = a.D;
     const int nslot = D >> 3;
     __shared__ float red[4];
+    const float* zf = a.zeros;
+    const uint16_t* zb = (const uint16_t*)a.zeros;
+    // base: bf16 rows for t >= base_from, else f32 (init broadcast / in_rows / x / zero)
+    const bool use_b16 = a.base_bf16 != nullptr && t >= a.base_from;
+    const float* basef;
+    size_t base_ld;
+    if (a.init) { basef = a.init; base_ld = 0; }
+    else if (a.in_rows) { basef = a.in_rows; base_ld = a.in_ld; }
+    else if (a.x && !a.base_zero) { basef = a.x; base_ld = D; }
+    else { basef = zf; base_ld = 0; }
+    const uint16_t* baseb = a.base_bf16 ? a.base_bf16 + (size_t)(use_b16 ? t - a.base_from : 0) * D : zb;
+    const bool has_part = !(a.part_rows > 0 && t >= a.part_rows);
+    const uint16_t* biasp = a.bias ? a.bias : zb;
+    const uint16_t* rbias = a.row_bias_bf16 ? a.row_bias_bf16 + (size_t)t * D : zb;
+    const float* gatep = a.gate ? a.gate : zf;
+    const float* p0f = a.norm == ROW_LN_MOD ? a.scale : (a.w_f32 ? a.w_f32 : zf);
+    const float* p1f = a.norm == ROW_LN_MOD ? a.shift : zf;
+    const uint16_t* wb = a.w_bf16 ? a.w_bf16 : zb;
+    const bool w_is_b16 = a.norm == ROW_RMS && a.w_bf16 != nullptr;
+
     float v[NS][8], u[NS][8], gv[NS][8], p0[NS][8], p1[NS][8];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int slot = threadIdx.x + j * 256;
         const int i0 = (slot < nslot ? slot : 0) * 8;
-        if (a.base_bf16 && t >= a.base_from) ld8_bf16(a.base_bf16 + (size_t)(t - a.base_from) * D + i0, v[j]);
-        else if (a.init) ld8(a.init + i0, v[j]);
-        else if (a.in_rows) ld8(a.in_rows + (size_t)t * a.in_ld + i0, v[j]);
-        else if (a.x && !a.base_zero) ld8(a.x + (size_t)t * D + i0, v[j]);
-        else {
+        float bf[8], bb[8], pp[S > 0 ? S : 1][8], bi[8], rb[8], w16[8];
+        ld8(basef + (size_t)t * base_ld + i0, bf);
+        ld8_bf16(baseb + i0, bb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
-        }
+        for (int s = 0; s < S; ++s) ld8(a.part + (size_t)s * a.part_stride + (size_t)t * D + i0, pp[s]);
+        ld8_bf16(biasp + i0, bi);
+        ld8_bf16(rbias + i0, rb);
+        ld8(gatep + i0, gv[j]);
+        ld8(p0f + i0, p0[j]);
+        ld8(p1f + i0, p1[j]);
+        ld8_bf16(wb + i0, w16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u[j][e] = 0.f;
-        const int S = (a.part_rows > 0 && t >= a.part_rows) ? 0 : a.S;
-        if (S > 0) ld8(a.part + (size_t)t * D + i0, u[j]);
+        for (int e = 0; e < 8; ++e) {
+            float uu = bi[e] + rb[e];
+            if (has_part) {
 #pragma unroll
-        for (int s = 1; s < 8; ++s) {
-            if (s < S) {
-                float w[8];
-                ld8(a.part + (size_t)s * a.part_stride + (size_t)t * D + i0, w);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) u[j][e] += w[e];
+                for (int s = 0; s < S; ++s) uu += pp[s][e];
             }
-        }
-        if (a.bias) {
-            float w[8];
-            ld8_bf16(a.bias + i0, w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[j][e] += w[e];
-        }
-        if (a.row_bias_bf16) {
-            float w[8];
-            ld8_bf16(a.row_bias_bf16 + (size_t)t * D + i0, w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[j][e] += w[e];
-        }
-        if (a.gate) ld8(a.gate + i0, gv[j]);
-        else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gv[j][e] = 1.f;
-        }
-        if (a.norm == ROW_LN_MOD) {
-            ld8(a.scale + i0, p0[j]);
-            ld8(a.shift + i0, p1[j]);
-        } else if (a.norm == ROW_RMS) {
-            if (a.w_bf16) ld8_bf16(a.w_bf16 + i0, p0[j]);
-            else ld8(a.w_f32 + i0, p0[j]);
+            u[j][e] = uu;
+            v[j][e] = use_b16 ? bb[e] : bf[e];
+            if (!a.gate) gv[j][e] = 1.f;
+            if (w_is_b16) p0[j][e] = w16[e];
         }
     }
     float sum = 0.f;
@@ -244,19 +244,33 @@ __global__ __launch_bounds__(256) void rms_f16_kernel(const float* x, int D, con
 
 }  // namespace
 
-hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
-    const int nslot = a.D / 8;
-    const int ns = (nslot + 255) / 256;
+template <int NS>
+hipError_t launch_rows_ns(const RowArgs& a, hipStream_t st) {
     dim3 grid(a.T), block(256);
-    switch (ns) {
-    case 1: rows_kernel<1><<<grid, block, 0, st>>>(a); break;
-    case 2: rows_kernel<2><<<grid, block, 0, st>>>(a); break;
-    case 3: rows_kernel<3><<<grid, block, 0, st>>>(a); break;
-    case 4: rows_kernel<4><<<grid, block, 0, st>>>(a); break;
-    case 5: rows_kernel<5><<<grid, block, 0, st>>>(a); break;
+    switch (a.S) {
+    case 0: rows_kernel<NS, 0><<<grid, block, 0, st>>>(a); break;
+    case 1: rows_kernel<NS, 1><<<grid, block, 0, st>>>(a); break;
+    case 2: rows_kernel<NS, 2><<<grid, block, 0, st>>>(a); break;
+    case 3: rows_kernel<NS, 3><<<grid, block, 0, st>>>(a); break;
+    case 4: rows_kernel<NS, 4><<<grid, block, 0, st>>>(a); break;
+    case 5: rows_kernel<NS, 5><<<grid, block, 0, st>>>(a); break;
+    case 6: rows_kernel<NS, 6><<<grid, block, 0, st>>>(a); break;
+    case 7: rows_kernel<NS, 7><<<grid, block, 0, st>>>(a); break;
+    case 8: rows_kernel<NS, 8><<<grid, block, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
+    if (!a.zeros) return hipErrorInvalidValue;
+    const int ns = (a.D / 8 + 255) / 256;
+    switch (ns) {
+    case 1: return launch_rows_ns<1>(a, st);
+    case 2: return launch_rows_ns<2>(a, st);
+    case 3: return launch_rows_ns<3>(a, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st) {
