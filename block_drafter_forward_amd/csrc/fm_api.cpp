@@ -46,9 +46,9 @@ bool kw_ok(int kw) {
            kw == 16 || (kw > 16 && kw % 2 == 0);
 }
 
-// k-split of a partial-output skinny GEMM (at most 8 slabs, the consumers' limit): the smallest S with
-// tiles * S >= TARGET_WGS and a per-wave range loaded at once (<= 16 k-steps); else the smallest S with enough
-// work-groups; else the largest supported S.
+// k-split of a partial-output skinny GEMM (at most 8 slabs, the consumers' limit). Preference: enough work-groups
+// (tiles * S >= TARGET_WGS) with a per-wave range that is a whole number of row-staged chunks (KW % 8 == 0);
+// then enough work-groups with any supported range; else the largest supported S.
 int pick_split(int M_total, int K) {
     const int n4 = K / 128, tiles = M_total / 16;
     int any_enough = -1, largest = -1;
@@ -56,7 +56,7 @@ int pick_split(int M_total, int K) {
         if (n4 % S || !kw_ok(n4 / S)) continue;
         largest = S;
         if (tiles * S >= TARGET_WGS) {
-            if (n4 / S <= 16) return S;
+            if ((n4 / S) % 8 == 0) return S;
             if (any_enough < 0) any_enough = S;
         }
     }
@@ -153,8 +153,8 @@ fm_status validate_config(const fm_config* c) {
         return fail(FM_E_INVALID, "dim %d != heads * head_dim", c->dim);
     if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
         return fail(FM_E_UNSUPPORTED, "head_dim %d (64, 128 or 256 supported)", c->head_dim);
-    if (c->dim % 256 || c->target_dim % 256 || c->ffn % 128)
-        return fail(FM_E_INVALID, "dim and target_dim must be multiples of 256, ffn of 128");
+    if (c->dim % 256 || c->target_dim % 256 || c->ffn % (c->wtype == FM_W_BF16 ? 256 : 128))
+        return fail(FM_E_INVALID, "dim and target_dim must be multiples of 256, ffn of 256 (bf16) or 128 (Q8_0)");
     if (c->vocab % 16) return fail(FM_E_INVALID, "vocab must be a multiple of 16");
     if (c->dim > 8 * 256 * 3) return fail(FM_E_UNSUPPORTED, "dim too large for the row kernels");
     switch (c->variant) {
@@ -193,6 +193,7 @@ struct fm_drafter {
     uint8_t* ws;
     uint8_t* kv;
     int length;
+    int perm;                          // k order of activation fragments (fm_device.h); natural (0) everywhere
     hipStream_t side = nullptr;        // default-priority stream for work that overlaps the caller's stream
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
@@ -278,6 +279,7 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     a.S = S;
     a.KW = K / 128 / S;
     a.mode = mode;
+    a.perm = d->perm;
     int begin = 0;
     size_t part_use = 0;
     for (size_t i = 0; i < gs.size(); ++i) {
@@ -301,6 +303,7 @@ RowArgs rows_base(const fm_drafter* d, int D, int T) {
     r.D = D;
     r.T = T;
     r.zeros = d->at<float>(d->p.zeros);
+    r.frag_perm = d->perm;
     return r;
 }
 
@@ -364,6 +367,7 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
     m.gate_ld = gate_ld;
     m.gate_hs = gate_hs;
     m.o_frag = o_frag;
+    m.perm = d->perm;
     HIPCHK(launch_attn_merge(m, st));
     return FM_OK;
 }
@@ -416,7 +420,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     const auto& c = d->c;
     const int D = c.dim, KT = c.n_taps * c.target_dim;
     if (n <= TMAX) {
-        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), st));
+        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), d->perm, st));
         int S = 0;
         float* part = d->at<float>(d->p.part);
         CHK(skinny(d, {{d->W("fc.weight"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}},
@@ -508,7 +512,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         uint8_t* afrag = d->at<uint8_t>(d->p.afrag);
         uint8_t* cfrag = d->at<uint8_t>(d->p.cfrag);
         float* apart = d->at<float>(d->p.apart);
-        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, afrag, as));
+        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, afrag, d->perm, as));
         int Sa = 0;
         CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, afrag, apart, D, D}}, Ht, 1,
                    SK_PARTIAL, 0, &Sa, as));
@@ -573,6 +577,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
             a.pos_base = pos + 1;
             a.scale = 1.f / sqrtf((float)hd);
             a.o_frag = fragO;
+            a.perm = d->perm;
             HIPCHK(launch_self_attn(a, st));
         }
         CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
@@ -684,7 +689,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     const auto& c = d->c;
     const int D = c.dim, KT = c.n_taps * c.target_dim;
     if (n <= TMAX) {
-        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), st));
+        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), d->perm, st));
         int S = 0;
         float* part = d->at<float>(d->p.part);
         CHK(skinny(d, {{d->W("W_c"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}}, KT, n,
@@ -790,7 +795,7 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
     const int Lc = d->length;
 
     // block rows: H_d[0] = tok_proj(E[anchor]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]
-    HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, fragA, st));
+    HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, fragA, d->perm, st));
     int S = 0;
     CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, 1, SK_PARTIAL, 0,
                &S, st));
@@ -1011,6 +1016,7 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
     d->ws = (uint8_t*)workspace;
     d->kv = (uint8_t*)kv_cache;
     d->length = 0;
+    d->perm = 0;
     for (int i = 0; i < n_weights; ++i) {
         if (!names[i]) { delete d; return fail(FM_E_INVALID, "null weight name at %d", i); }
         if (!ptrs[i]) { delete d; return fail(FM_E_INVALID, "null pointer for weight %s", names[i]); }
@@ -1096,7 +1102,7 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     hipStream_t st = (hipStream_t)stream;
     const int K = d->c.target_dim;
     uint8_t* fr = d->at<uint8_t>(d->p.fragH);
-    HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
+    HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, d->perm, st));
     LmArgs a{};
     const bool q8 = d->c.wtype == FM_W_Q8_0;
     a.E = q8 ? d->W("lm_head.q") : d->W("lm_head.weight");
@@ -1108,6 +1114,7 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     a.best = d->at<unsigned long long>(d->p.best);
     a.tokens = tokens;
     a.logits = logits;
+    a.perm = d->perm;
     HIPCHK(launch_lm_argmax(a, q8 ? 1 : 0, st));
     return FM_OK;
 }

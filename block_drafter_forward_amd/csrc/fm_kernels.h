@@ -40,6 +40,7 @@ struct SkinnyArgs {
     int KW;               // k-steps per wave (K / 32 == S * 4 * KW), any value >= 1
     int mode;
     long long part_stride;
+    int perm;             // k order of the fragments and weight loads (fm_device.h)
 };
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int n_workgroups, hipStream_t st);
 
@@ -74,13 +75,15 @@ struct RowArgs {
     int base_from;
     const uint16_t* row_bias_bf16;  // bf16 [T][D] added to row t (or null)
     const float* zeros;    // a zero row of >= D floats (absent inputs read it; required)
+    int frag_perm;         // k order of frag_out
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
 // f32 rows [T][K] (row stride ld) -> fragments. T <= 16, K % 32 == 0.
-hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st);
+hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, int perm, hipStream_t st);
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
-hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, hipStream_t st);
+hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
+                              hipStream_t st);
 // bf16 row E[*idx] -> f32 [K] (+ optional bf16 row added); ids are clamped to [0, V).
 hipError_t launch_gather_f32(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add_bf16, float* out,
                              hipStream_t st);
@@ -118,6 +121,7 @@ struct SelfAttnArgs {
     int pos_base;
     float scale;
     uint8_t* o_frag;
+    int perm;
 };
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st);
 
@@ -149,6 +153,7 @@ struct MergeArgs {
     const float* gate;     // optional: o *= sigmoid(gate[t*gate_ld + h*gate_hs + d])
     int gate_ld, gate_hs;
     uint8_t* o_frag;       // o row t, k = h*hd + d
+    int perm;
 };
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st);
 
@@ -194,6 +199,7 @@ struct LmArgs {
     int32_t* tokens;
     float* logits;         // optional [T][V]
     int n_wg;
+    int perm;
 };
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
 

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void self_attn_mfma_kernel(SelfAttnArgs a) {
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = X[0][t][d0 + e];
-        frag_store8(a.o_frag, t, h * hd + d0, o);
+        frag_store8(a.o_frag, t, h * hd + d0, o, a.perm);
     }
 }
 
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
             o[e] *= il;
             if (gp) o[e] *= sigmoidf(gt[e]);
         }
-        frag_store8(a.o_frag, t, h * HD + d0, o);
+        frag_store8(a.o_frag, t, h * HD + d0, o, a.perm);
     }
 }
 

@@ -71,9 +71,9 @@ __device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v
     for (int n = 0; n < 2; ++n) {
         const size_t row = (size_t)min(v0 + 16 * n + r, a.V - 1);
         if constexpr (WT == 0) {
-            const uint16_t* E = (const uint16_t*)a.E + row * K + (size_t)s * 32 + g * 8;
+            const uint16_t* E = (const uint16_t*)a.E + row * K;
 #pragma unroll
-            for (int i = 0; i < CH; ++i) st.a[n][i] = ldg_nt(E + i * 32);
+            for (int i = 0; i < CH; ++i) st.a[n][i] = ldg_nt(E + kcol(s + i, g, a.perm));
         } else {
             const int8_t* C = (const int8_t*)a.E + row * K + (size_t)s * 32 + g * 8;
 #pragma unroll
@@ -177,6 +177,108 @@ __global__ __launch_bounds__(256) void lm_argmax_kernel(LmArgs a) {
     }
 }
 
+// bf16 tables, row-staged: a wave owns 16 vocabulary rows. Each chunk of 8 k-steps (256 columns) is read as
+// 8 row-contiguous instructions (2 rows x 512 bytes), parked in a wave-private LDS tile and read back in the MFMA A
+// layout -- whole cache lines per instruction instead of the A layout's 16 half lines. The next chunk (weights and
+// activation fragments) is in flight while the current one multiplies.
+constexpr int RS_PITCH = 33;   // uint4 per LDS row: 32 + 1 pad (conflict-free A reads)
+
+struct RsChunk {
+    uint4 a[8];
+    uint4 bh[8], bl[8];
+};
+
+__device__ __forceinline__ void rs_load(RsChunk& c, const LmArgs& a, int v0, int s, int lane) {
+    const uint8_t* xb = a.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        c.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
+        c.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
+    }
+    // V is a multiple of 16, so a wave's 16 rows are all inside the table
+    const uint16_t* E = (const uint16_t*)a.E + (size_t)(v0 + (lane >> 5)) * a.K + s * 32 + (lane & 31) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c.a[i] = ldg_nt(E + (size_t)(2 * i) * a.K);
+}
+
+__device__ __forceinline__ void rs_compute(const RsChunk& c, uint4* lds, f32x4_t& acc, int lane) {
+    const int hr = lane >> 5, piece = lane & 31, r = lane & 15, g = lane >> 4;
+    __builtin_amdgcn_wave_barrier();   // the previous chunk's LDS reads stay before these writes
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds[(2 * i + hr) * RS_PITCH + piece] = c.a[i];
+    __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 av = lds[r * RS_PITCH + 4 * i + g];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(c.bh[i]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(c.bl[i]), acc, 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256) void lm_argmax_rs_kernel(LmArgs a) {
+    __shared__ uint4 rs_lds[4][16 * RS_PITCH];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int v0 = (blockIdx.x * 4 + wave) * 16;
+    const bool active = v0 < a.V;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (active) {
+        uint4* lds = rs_lds[wave];
+        const int nch = a.K >> 8;   // chunks of 8 k-steps
+        RsChunk c0, c1;
+        rs_load(c0, a, v0, 0, lane);
+        int ch = 0;
+        for (; ch + 2 < nch; ch += 2) {
+            rs_load(c1, a, v0, 8 * (ch + 1), lane);
+            rs_compute(c0, lds, acc, lane);
+            rs_load(c0, a, v0, 8 * (ch + 2), lane);
+            rs_compute(c1, lds, acc, lane);
+        }
+        if (ch + 1 < nch) {
+            rs_load(c1, a, v0, 8 * (ch + 1), lane);
+            rs_compute(c0, lds, acc, lane);
+            rs_compute(c1, lds, acc, lane);
+        } else {
+            rs_compute(c0, lds, acc, lane);
+        }
+    }
+    // lane holds z[t = lane % 16][v0 + 4 g + j]
+    const int t = lane & 15;
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int v = v0 + 4 * g + j;
+            const float z = acc[j];
+            if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
+            if (z > best) { best = z; bidx = v; }
+        }
+    }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        const float ob = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bidx, o, 64);
+        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+    }
+    __shared__ float wb[4][16];
+    __shared__ int wi[4][16];
+    if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
+    __syncthreads();
+    if (threadIdx.x < 16 && threadIdx.x < a.T) {
+        const int tt = threadIdx.x;
+        float b = wb[0][tt];
+        int bi = wi[0][tt];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (wb[w][tt] > b || (wb[w][tt] == b && wi[w][tt] < bi)) { b = wb[w][tt]; bi = wi[w][tt]; }
+        if (bi != 0x7fffffff) {
+            const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
+            atomicMax(&a.best[tt], key);
+        }
+    }
+}
+
 __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tokens) {
     const int t = threadIdx.x;
     if (t < T) {
@@ -189,10 +291,15 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
 }  // namespace
 
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
-    if ((a.K >> 5) % (2 * CH) != 0 || a.T > 16) return hipErrorInvalidValue;
-    const int nwg = (a.V + 127) / 128;
-    if (wtype == 0) lm_argmax_kernel<0><<<nwg, 256, 0, st>>>(a);
-    else lm_argmax_kernel<1><<<nwg, 256, 0, st>>>(a);
+    if (a.T > 16) return hipErrorInvalidValue;
+    if (wtype == 0 && a.perm == 0 && a.K % 256 == 0) {
+        lm_argmax_rs_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
+    } else {
+        if ((a.K >> 5) % (2 * CH) != 0) return hipErrorInvalidValue;
+        const int nwg = (a.V + 127) / 128;
+        if (wtype == 0) lm_argmax_kernel<0><<<nwg, 256, 0, st>>>(a);
+        else lm_argmax_kernel<1><<<nwg, 256, 0, st>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     lm_finalize_kernel<<<1, 64, 0, st>>>(a.best, a.T, a.tokens);

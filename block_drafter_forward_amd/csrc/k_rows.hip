@@ -131,13 +131,13 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
                 else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * p0[j][e];
                 else h[e] = v[j][e];
             }
-            if (a.frag_out) frag_store8(a.frag_out, t, a.frag_koff + i0, h);
+            if (a.frag_out) frag_store8(a.frag_out, t, a.frag_koff + i0, h, a.frag_perm);
             if (a.f32_out) st8(a.f32_out + (size_t)t * a.out_ld + i0, h);
         }
     }
 }
 
-__global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag) {
+__global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag, int perm) {
     const int t = blockIdx.y;
     const int slot = blockIdx.x * 256 + threadIdx.x;
     if (slot * 8 >= K) return;
@@ -145,20 +145,20 @@ __global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag)
     const float* p = x + (size_t)t * ld + slot * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = p[e];
-    frag_store8(frag, t, slot * 8, v);
+    frag_store8(frag, t, slot * 8, v, perm);
 }
 
 // Token ids outside [0, V) are clamped into the table (a device-side id cannot be validated by the host).
 __device__ __forceinline__ size_t clamp_row(int32_t id, int V) { return (size_t)(id < 0 ? 0 : (id >= V ? V - 1 : id)); }
 
-__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag) {
+__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm) {
     const int slot = blockIdx.x * 256 + threadIdx.x;
     if (slot * 8 >= K) return;
     const size_t row = clamp_row(idx[0], V);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(E[row * K + slot * 8 + e]);
-    frag_store8(frag, 0, slot * 8, v);
+    frag_store8(frag, 0, slot * 8, v, perm);
 }
 
 __global__ void gather_f32_kernel(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add,
@@ -273,14 +273,15 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
     }
 }
 
-hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st) {
+hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, int perm, hipStream_t st) {
     dim3 grid((K / 8 + 255) / 256, T);
-    f32_to_frag_kernel<<<grid, 256, 0, st>>>(x, ld, K, frag);
+    f32_to_frag_kernel<<<grid, 256, 0, st>>>(x, ld, K, frag, perm);
     return hipGetLastError();
 }
 
-hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, hipStream_t st) {
-    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag);
+hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
+                              hipStream_t st) {
+    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, perm);
     return hipGetLastError();
 }
 
