@@ -350,8 +350,8 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
     a.hd = c.head_dim;
     a.causal_base = causal_base;
     a.scale = scale;
-    a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype);
     const int ntot = key_hi - key_lo + nx;
+    a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype, ntot, c.heads);
     a.nchunks = (ntot + a.chunk - 1) / a.chunk;
     if ((size_t)c.heads * a.nchunks * TMAX * (c.head_dim + 2) * 4 > d->p.attnp_bytes)
         return fail(FM_E_INVALID, "attention partial buffer too small");

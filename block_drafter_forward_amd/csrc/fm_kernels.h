@@ -143,8 +143,9 @@ struct AttnArgs {
     int nchunks;
     float* part;           // [heads][nchunks][nq][hd + 2]: unnormalised o, running max, sum
 };
-// Keys per work-group of the split kernel for a head width and cache type (the host sizes nchunks with it).
-int attn_chunk_size(int hd, int kv_dtype);
+// Keys per work-group of the split kernel for a head width, cache type, key count and head count (the host sizes
+// nchunks with it; the launcher checks that the two agree).
+int attn_chunk_size(int hd, int kv_dtype, int nkeys, int heads);
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st);
 
 struct MergeArgs {

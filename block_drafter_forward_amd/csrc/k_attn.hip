@@ -2,7 +2,7 @@
 //
 //  self_attn     flow-map self-attention over the T slots (one work-group per head): per-head q/k RMSNorm,
 //                interleaved RoPE at the slots' positions, softmax(q kᵀ / sqrt(hd)) v with no mask
-//                (flashmap_drafter.js: headNormRope, attnF32), both products on f16 MFMA with hi/lo splits;
+//                (flashmap_drafter.js: headNormRope, attnF32), in f32 registers with two LDS exchanges;
 //                o leaves as fragments for the o_proj GEMM.
 //  attn_split    up to 16 query rows of one head against one chunk of keys (cache rows, then optional extra f32
 //                rows): scores, chunk max, exp-sum and the unnormalised P·V, written as a partial; f16 caches run
@@ -26,140 +26,101 @@ __device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
 }
 
 // ── self-attention ───────────────────────────────────────────────────────────────────────────────
-// Self-attention with both products on the matrix cores (one work-group per head): after the f32 head-norm and
-// RoPE, q, k and v are split into f16 hi + lo; scores take three MFMAs per 32-dim step (hi·hi + hi·lo + lo·hi, the
-// dropped lo·lo term is below 2^-22 relative), P·V likewise with the 16 keys padded to the MFMA's 32.
-__global__ __launch_bounds__(256) void self_attn_mfma_kernel(SelfAttnArgs a) {
-    const int h = blockIdx.x;
-    const int T = a.T, hd = a.hd, D = a.D;
-    constexpr int XR = 129, FR = 136, VR = 40;   // pitches: f32 rows, f16 rows (hd <= 128), transposed V rows
-    __shared__ float X[3][16][XR];
-    __shared__ float P[16][17];
-    __shared__ float NW[2][128];
-    __shared__ float RT[16][128];
-    __shared__ __attribute__((aligned(16))) _Float16 Qh[16 * FR], Ql[16 * FR], Kh[16 * FR], Kl[16 * FR];
-    __shared__ __attribute__((aligned(16))) _Float16 Vh[128 * VR], Vl[128 * VR];
-    __shared__ __attribute__((aligned(16))) _Float16 Ph[16 * VR], Pl[16 * VR];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int q4 = hd >> 2;
-    const int n4 = 3 * T * q4;
-    float4 xv[6];
+// One work-group per head, built for latency (the whole op is 16 x 16 x hd): every global load (q, k, v rows, the
+// norm weights and the slots' RoPE rows) is issued up front; thread (row, segment) holds hd/8 consecutive values of
+// one q or k row, so the head-RMSNorm is an 8-lane shuffle reduction and the interleaved RoPE pairs stay inside the
+// thread; then one LDS exchange for the scores (thread = (query, key), 16-lane softmax by shuffles) and one for
+// P·V, whose 8 consecutive outputs per thread go straight out as fragments. All arithmetic in f32.
+template <int HD>
+__global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
+    constexpr int SEG = HD / 8, VPT = HD / 16, QP = HD + 4;
+    __shared__ __attribute__((aligned(16))) float QK[32 * QP];
+    __shared__ __attribute__((aligned(16))) float Vs[16 * QP];
+    __shared__ float Ps[16][17];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int T = a.T, D = a.D;
+    const int row = tid >> 3, seg = tid & 7;            // q rows 0..15, k rows 16..31
+    const int w = row >> 4, t = row & 15, tc = min(t, T - 1);
+    float x[SEG], cs[SEG / 2], sn[SEG / 2], nw[SEG], v[VPT];
+    {
+        const float* src = a.qkv + (size_t)tc * 3 * D + (size_t)w * D + (size_t)h * HD + seg * SEG;
 #pragma unroll
-    for (int j = 0; j < 6; ++j) {
-        const int i = tid + 256 * j;
-        const int ii = i < n4 ? i : n4 - 1;
-        const int w = ii / (T * q4), r = ii % (T * q4), t = r / q4, d4 = r % q4;
-        xv[j] = *(const float4*)(a.qkv + (size_t)t * 3 * D + (size_t)w * D + (size_t)h * hd + 4 * d4);
-    }
-    const int nwi = tid < 2 * hd ? tid : 0;
-    const float nw = bf16_to_f32((nwi < hd ? a.qn : a.kn)[nwi % hd]);
-    float rt[8];
+        for (int j = 0; j < SEG / 4; ++j) {
+            const float4 f = ((const float4*)src)[j];
+            x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+        }
+        const float* rt = a.rope_tab + (size_t)(a.pos_base + tc) * HD + seg * (SEG / 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int i = tid + 256 * j;
-        const int ii = i < T * hd ? i : T * hd - 1;
-        rt[j] = a.rope_tab[(size_t)(a.pos_base + ii / hd) * hd + ii % hd];
-    }
-    for (int i = tid; i < 3 * 16 * XR; i += 256) (&X[0][0][0])[i] = 0.f;
-    __syncthreads();
+        for (int j = 0; j < SEG / 8; ++j) {
+            const float4 c = ((const float4*)rt)[j], sv = ((const float4*)(rt + HD / 2))[j];
+            cs[4 * j] = c.x; cs[4 * j + 1] = c.y; cs[4 * j + 2] = c.z; cs[4 * j + 3] = c.w;
+            sn[4 * j] = sv.x; sn[4 * j + 1] = sv.y; sn[4 * j + 2] = sv.z; sn[4 * j + 3] = sv.w;
+        }
+        const uint16_t* n = (w ? a.kn : a.qn) + seg * SEG;
 #pragma unroll
-    for (int j = 0; j < 6; ++j) {
-        const int i = tid + 256 * j;
-        if (i < n4) {
-            const int w = i / (T * q4), r = i % (T * q4), t = r / q4, d4 = r % q4;
-            X[w][t][4 * d4] = xv[j].x; X[w][t][4 * d4 + 1] = xv[j].y;
-            X[w][t][4 * d4 + 2] = xv[j].z; X[w][t][4 * d4 + 3] = xv[j].w;
+        for (int j = 0; j < SEG; ++j) nw[j] = bf16_to_f32(n[j]);
+        const int vt = min(tid >> 4, T - 1), vp = tid & 15;
+        const float* vs = a.qkv + (size_t)vt * 3 * D + 2 * (size_t)D + (size_t)h * HD + vp * VPT;
+#pragma unroll
+        for (int j = 0; j < VPT / 4; ++j) {
+            const float4 f = ((const float4*)vs)[j];
+            v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
         }
     }
-    if (tid < 2 * hd) NW[tid / hd][tid % hd] = nw;
+    float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int i = tid + 256 * j;
-        if (i < T * hd) RT[i / hd][i % hd] = rt[j];
+    for (int j = 0; j < SEG; ++j) ss += x[j] * x[j];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    const float r = 1.f / sqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+    for (int j = 0; j < SEG / 2; ++j) {
+        const float x0 = x[2 * j] * (nw[2 * j] * r), x1 = x[2 * j + 1] * (nw[2 * j + 1] * r);
+        x[2 * j] = x0 * cs[j] - x1 * sn[j];
+        x[2 * j + 1] = x1 * cs[j] + x0 * sn[j];
     }
+#pragma unroll
+    for (int j = 0; j < SEG / 4; ++j)
+        *(float4*)(QK + row * QP + seg * SEG + 4 * j) = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+#pragma unroll
+    for (int j = 0; j < VPT / 4; ++j)
+        *(float4*)(Vs + (tid >> 4) * QP + (tid & 15) * VPT + 4 * j) =
+            make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
     __syncthreads();
-    for (int row = wave; row < 2 * T; row += 4) {
-        const int w = row / T, t = row % T;
-        float ss = 0.f;
-        for (int d = lane; d < hd; d += 64) ss += X[w][t][d] * X[w][t][d];
-        ss = wave_sum(ss);
-        const float r = 1.f / sqrtf(ss / (float)hd + a.eps);
-        for (int d = lane; d < hd; d += 64) X[w][t][d] = X[w][t][d] * (NW[w][d] * r);
-    }
-    __syncthreads();
-    const int half = hd >> 1;
-    for (int i = tid; i < 2 * T * half; i += 256) {
-        const int row = i / half, pi = i % half, w = row / T, t = row % T;
-        const float c = RT[t][pi], sn = RT[t][half + pi];
-        const float x0 = X[w][t][2 * pi], x1 = X[w][t][2 * pi + 1];
-        X[w][t][2 * pi] = x0 * c - x1 * sn;
-        X[w][t][2 * pi + 1] = x1 * c + x0 * sn;
-    }
-    __syncthreads();
-    // f16 hi/lo splits; V transposed (dim-major), keys T..31 zero
-    for (int i = tid; i < 16 * hd; i += 256) {
-        const int t = i / hd, d = i % hd;
-        const float q = X[0][t][d], k = X[1][t][d], v = X[2][t][d];
-        const _Float16 qh = (_Float16)q, kh = (_Float16)k, vh = (_Float16)v;
-        Qh[t * FR + d] = qh; Ql[t * FR + d] = (_Float16)(q - (float)qh);
-        Kh[t * FR + d] = kh; Kl[t * FR + d] = (_Float16)(k - (float)kh);
-        Vh[d * VR + t] = vh; Vl[d * VR + t] = (_Float16)(v - (float)vh);
-        Vh[d * VR + 16 + t] = (_Float16)0.f; Vl[d * VR + 16 + t] = (_Float16)0.f;
-    }
-    __syncthreads();
-    const int fr = lane & 15, fk = 8 * (lane >> 4);
-    if (wave == 0) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < hd / 32; ++s) {
-            const f16x8_t A = *(const f16x8_t*)(Kh + fr * FR + s * 32 + fk);
-            const f16x8_t Al = *(const f16x8_t*)(Kl + fr * FR + s * 32 + fk);
-            const f16x8_t B = *(const f16x8_t*)(Qh + fr * FR + s * 32 + fk);
-            const f16x8_t Bl = *(const f16x8_t*)(Ql + fr * FR + s * 32 + fk);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, acc, 0, 0, 0);
+    {
+        const int qt = tid >> 4, u = tid & 15;
+        const float* q = QK + qt * QP;
+        const float* k = QK + (16 + u) * QP;
+        float s = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < HD; d += 4) {
+            const float4 qa = *(const float4*)(q + d), kb = *(const float4*)(k + d);
+            s += qa.x * kb.x + qa.y * kb.y + qa.z * kb.z + qa.w * kb.w;
         }
-        // lane holds S[t = lane % 16][u = 4 (lane / 16) + i]
+        s = u < T ? s * a.scale : -INFINITY;
+        float m = s;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) P[fr][4 * (lane >> 4) + i] = acc[i] * a.scale;
-    }
-    __syncthreads();
-    if (tid < 16) {
-        const int t = tid;
-        float m = -INFINITY;
-        for (int u = 0; u < T; ++u) m = fmaxf(m, P[t][u]);
-        float z = 0.f, e[16];
-        for (int u = 0; u < 16; ++u) { e[u] = (u < T && t < T) ? expf(P[t][u] - m) : 0.f; z += e[u]; }
-        const float iz = z > 0.f ? 1.f / z : 0.f;
-        for (int u = 0; u < 32; ++u) {
-            const float p = u < 16 ? e[u] * iz : 0.f;
-            const _Float16 ph = (_Float16)p;
-            Ph[t * VR + u] = ph;
-            Pl[t * VR + u] = (_Float16)(p - (float)ph);
-        }
-    }
-    __syncthreads();
-    // O[t][d]: wave w owns dim tiles w, w + 4; result staged in X[0] for the fragment store
-    for (int dt = wave; dt < hd / 16; dt += 4) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const f16x8_t A = *(const f16x8_t*)(Ph + fr * VR + fk);
-        const f16x8_t Al = *(const f16x8_t*)(Pl + fr * VR + fk);
-        const f16x8_t B = *(const f16x8_t*)(Vh + (dt * 16 + fr) * VR + fk);
-        const f16x8_t Bl = *(const f16x8_t*)(Vl + (dt * 16 + fr) * VR + fk);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, acc, 0, 0, 0);
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        const float e = u < T ? expf(s - m) : 0.f;
+        float z = e;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[0][4 * (lane >> 4) + i][dt * 16 + fr] = acc[i];
+        for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+        Ps[qt][u] = e / z;
     }
     __syncthreads();
-    const int per = hd >> 3;
-    for (int slot = tid; slot < T * per; slot += 256) {
-        const int t = slot / per, d0 = (slot % per) * 8;
+    if (tid < 2 * HD) {
+        const int ot = tid / (HD / 8), d0 = (tid % (HD / 8)) * 8;
         float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = X[0][t][d0 + e];
-        frag_store8(a.o_frag, t, h * hd + d0, o, a.perm);
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        for (int u = 0; u < T; ++u) {
+            const float p = Ps[ot][u];
+            const float4 v0 = *(const float4*)(Vs + u * QP + d0), v1 = *(const float4*)(Vs + u * QP + d0 + 4);
+            o[0] += p * v0.x; o[1] += p * v0.y; o[2] += p * v0.z; o[3] += p * v0.w;
+            o[4] += p * v1.x; o[5] += p * v1.y; o[6] += p * v1.z; o[7] += p * v1.w;
+        }
+        if (ot < T) frag_store8(a.o_frag, ot, h * HD + d0, o, a.perm);
     }
 }
 
@@ -387,23 +348,27 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 }
 
 // ── split-L attention on the matrix cores (f16 cache) ────────────────────────────────────────────
-// One work-group = one head x one chunk of C keys (16 KB of K and 16 KB of V), 4 waves:
+// One work-group = one head x one chunk of C keys, 4 waves, three LDS exchanges:
+//   prep    every global load first (the chunk's K and V rows, the queries, norm weight, RoPE rows); thread
+//           (query t, segment) holds hd/16 consecutive query values, so the head-RMSNorm is a 16-lane shuffle
+//           reduction and the interleaved RoPE pairs stay in the thread; queries leave split q = hi + lo in f16;
 //   scores  Sᵀ[j][t] = sum_d K[j][d] q[t][d] on v_mfma_f32_16x16x32_f16: A = K rows straight from LDS (exact f16),
-//           B = the queries split q = hi + lo in f16 (two MFMAs, ~22 significant bits);
-//   softmax per query row over the chunk (max, exp, sum) in f32;
+//           B = the query hi and lo halves (two MFMAs, ~22 significant bits);
+//   softmax 16 threads per query row over the chunk (max, exp, sum by shuffles) in f32;
 //   P.V     O[t][d] = sum_j P[t][j] V[j][d]: A = P split hi/lo in f16, B = V read from a transposed LDS copy
 //           (dim-major) so each lane's 8 keys are one 16-byte read.
-// All global loads (K, V, queries, norm weight, RoPE rows) are issued before the first use.
-template <int HD>
+// C is 64 or 32 keys (hd 128) so that short contexts still spread over enough work-groups.
+template <int HD, int C>
 __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
-    constexpr int C = 16384 / (HD * 2);        // keys per chunk: 64 (HD 128), 128 (HD 64)
     constexpr int KROW = HD + 8;               // LDS row pitches (halfs), 16-byte pad
     constexpr int VROW = C + 8;
     constexpr int PROW = C + 8;
     constexpr int QROW = HD + 8;
     constexpr int V16 = HD * 2 / 16;           // 16-byte pieces per key row
     constexpr int LD16 = C * V16 / 256;
-    constexpr int QPT = 16 * HD / 256;
+    constexpr int QS = HD / 16;                // query values per thread
+    constexpr int CPT = C / 16;                // scores per thread in the softmax
+    static_assert(LD16 >= 1 && C % 32 == 0, "chunk shape");
     const int c = blockIdx.x, h = blockIdx.y;
     const int nq = a.nq;
     const int kh = h / (a.heads / a.kv_heads);
@@ -413,16 +378,13 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 Vt[HD * VROW];
     __shared__ __attribute__((aligned(16))) _Float16 Qh[16 * QROW], Ql[16 * QROW];
     __shared__ __attribute__((aligned(16))) _Float16 Ph[16 * PROW], Pl[16 * PROW];
-    __shared__ float qs[16][HD];
     __shared__ float S[16][C + 1];
-    __shared__ float nws[HD], rts[16][HD];
-    __shared__ float mrow[16], lrow[16];
 
     const int ncache = a.key_hi - a.key_lo;
     const int k0 = c * C;
     const int cnt = min(C, ncache - k0);
 
-    // 1. prefetch
+    // 1. every global load up front
     uint4 kr[LD16], vr[LD16];
 #pragma unroll
     for (int j = 0; j < LD16; ++j) {
@@ -433,23 +395,50 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
         kr[j] = *((const uint4*)((const uint16_t*)a.kc + off) + p16);
         vr[j] = *((const uint4*)((const uint16_t*)a.vc + off) + p16);
     }
-    float qv[QPT], ropev[QPT];
-    const float* ropep = qp.rope ? qp.rope_tab : qp.zeros;
-    const int rd = qp.rope ? qp.rope_dims : 0;
+    const int qt = tid >> 4, qseg = tid & 15, tq = min(qt, nq - 1);
+    float q[QS], nw[QS], cs[QS / 2], sn[QS / 2];
+    {
+        const float* src = qp.q + (size_t)tq * qp.q_ld + (size_t)h * qp.q_hs + qseg * QS;
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + 256 * j;
-        const int t = i / HD, d = i % HD;
-        const int tt = t < nq ? t : 0;
-        qv[j] = qp.q[(size_t)tt * qp.q_ld + (size_t)h * qp.q_hs + d];
-        const int dd = d < rd ? d : 0;
-        ropev[j] = ropep[(size_t)(qp.rope ? qp.pos_base + tt : 0) * rd + dd];
+        for (int j = 0; j < QS / 4; ++j) {
+            const float4 f = ((const float4*)src)[j];
+            q[4 * j] = f.x; q[4 * j + 1] = f.y; q[4 * j + 2] = f.z; q[4 * j + 3] = f.w;
+        }
+        const float* rt = qp.rope ? qp.rope_tab + (size_t)(qp.pos_base + tq) * HD + qseg * (QS / 2) : qp.zeros;
+        const float* rs = qp.rope ? rt + HD / 2 : qp.zeros;
+#pragma unroll
+        for (int j = 0; j < QS / 2; ++j) { cs[j] = rt[j]; sn[j] = rs[j]; }
+        const uint16_t* nb = qp.norm_bf16 ? qp.norm_bf16 + qseg * QS : (const uint16_t*)qp.zeros;
+        const float* nf = qp.norm_f32 ? qp.norm_f32 + qseg * QS : qp.zeros;
+#pragma unroll
+        for (int j = 0; j < QS; ++j) nw[j] = qp.norm_bf16 ? bf16_to_f32(nb[j]) : nf[j];
     }
-    const bool has_norm = qp.norm_bf16 || qp.norm_f32;
-    const float nw16 = bf16_to_f32((qp.norm_bf16 ? qp.norm_bf16 : (const uint16_t*)qp.zeros)[tid % HD]);
-    const float nw32 = (qp.norm_f32 ? qp.norm_f32 : qp.zeros)[tid % HD];
-
-    // 2. to LDS: K row-major, V transposed (dim-major), queries f32
+    // 2. query head-norm + RoPE in registers, hi/lo split; K row-major and V transposed into LDS
+    if (qp.norm_bf16 || qp.norm_f32) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < QS; ++j) ss += q[j] * q[j];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
+#pragma unroll
+        for (int j = 0; j < QS; ++j) q[j] *= nw[j] * r;
+    }
+    if (qp.rope) {
+#pragma unroll
+        for (int j = 0; j < QS / 2; ++j) {
+            const float x0 = q[2 * j], x1 = q[2 * j + 1];
+            q[2 * j] = x0 * cs[j] - x1 * sn[j];
+            q[2 * j + 1] = x1 * cs[j] + x0 * sn[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < QS; ++j) {
+        const float x = qt < nq ? q[j] : 0.f;
+        const _Float16 hi = (_Float16)x;
+        Qh[qt * QROW + qseg * QS + j] = hi;
+        Ql[qt * QROW + qseg * QS + j] = (_Float16)(x - (float)hi);
+    }
 #pragma unroll
     for (int j = 0; j < LD16; ++j) {
         const int u = tid + 256 * j;
@@ -462,55 +451,8 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
             Vt[(p16 * 8 + 2 * e + 1) * VROW + row] = __builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
         }
     }
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + 256 * j;
-        qs[i / HD][i % HD] = (i / HD) < nq ? qv[j] : 0.f;
-        rts[i / HD][i % HD] = ropev[j];
-    }
-    if (tid < HD) nws[tid] = qp.norm_bf16 ? nw16 : nw32;
     __syncthreads();
-    // 3. query head-norm + RoPE (f32), then the hi/lo f16 split
-    if (has_norm) {
-        for (int t = wave; t < nq; t += 4) {
-            float ss = 0.f;
-            for (int d = lane; d < HD; d += 64) ss += qs[t][d] * qs[t][d];
-            ss = wave_sum(ss);
-            const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
-            for (int d = lane; d < HD; d += 64) qs[t][d] *= nws[d] * r;
-        }
-        __syncthreads();
-    }
-    if (qp.rope == 1) {
-        const int half = HD / 2;
-        for (int i = tid; i < nq * half; i += 256) {
-            const int t = i / half, pi = i % half;
-            const float cs = rts[t][pi], sn = rts[t][half + pi];
-            const float x0 = qs[t][2 * pi], x1 = qs[t][2 * pi + 1];
-            qs[t][2 * pi] = x0 * cs - x1 * sn;
-            qs[t][2 * pi + 1] = x1 * cs + x0 * sn;
-        }
-        __syncthreads();
-    } else if (qp.rope == 2) {
-        const int half = qp.rope_dims / 2;
-        for (int i = tid; i < nq * half; i += 256) {
-            const int t = i / half, pi = i % half;
-            const float cs = rts[t][pi], sn = rts[t][half + pi];
-            const float x0 = qs[t][pi], x1 = qs[t][pi + half];
-            qs[t][pi] = x0 * cs - x1 * sn;
-            qs[t][pi + half] = x1 * cs + x0 * sn;
-        }
-        __syncthreads();
-    }
-    for (int i = tid; i < 16 * HD; i += 256) {
-        const int t = i / HD, d = i % HD;
-        const float x = qs[t][d];
-        const _Float16 hi = (_Float16)x;
-        Qh[t * QROW + d] = hi;
-        Ql[t * QROW + d] = (_Float16)(x - (float)hi);
-    }
-    __syncthreads();
-    // 4. scores: wave w owns key tiles w, w+4, ...
+    // 3. scores: wave w owns key tiles w, w+4, ...
     const int fr = lane & 15, fk = 8 * (lane >> 4);
     for (int kt = wave; kt < C / 16; kt += 4) {
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -526,33 +468,40 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int j = kt * 16 + 4 * (lane >> 4) + i;
-            const int kidx = k0 + j;
             float v = acc[i] * a.scale;
             if (j >= cnt) v = -INFINITY;
-            if (a.causal_base >= 0 && a.key_lo + kidx > a.causal_base + fr) v = -INFINITY;
+            if (a.causal_base >= 0 && a.key_lo + k0 + j > a.causal_base + fr) v = -INFINITY;
             S[fr][j] = v;
         }
     }
     __syncthreads();
-    // 5. softmax statistics per query row; P = exp(S - m) split hi/lo in f16
-    for (int t = wave; t < 16; t += 4) {
+    // 4. softmax statistics: 16 threads per query row, CPT keys each; P = exp(S - m) split hi/lo in f16
+    float* out = a.part + ((size_t)h * a.nchunks + c) * nq * (HD + 2);
+    {
+        float sv[CPT];
         float m = -INFINITY;
-        for (int j = lane; j < C; j += 64) m = fmaxf(m, S[t][j]);
-        m = wave_max(m);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) { sv[i] = S[qt][qseg + 16 * i]; m = fmaxf(m, sv[i]); }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
         float l = 0.f;
-        for (int j = lane; j < C; j += 64) {
-            const float p = (m == -INFINITY || t >= nq) ? 0.f : expf(S[t][j] - m);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const float p = (m == -INFINITY || qt >= nq) ? 0.f : expf(sv[i] - m);
             const _Float16 hi = (_Float16)p;
-            Ph[t * PROW + j] = hi;
-            Pl[t * PROW + j] = (_Float16)(p - (float)hi);
+            Ph[qt * PROW + qseg + 16 * i] = hi;
+            Pl[qt * PROW + qseg + 16 * i] = (_Float16)(p - (float)hi);
             l += p;
         }
-        l = wave_sum(l);
-        if (lane == 0) { mrow[t] = m; lrow[t] = l; }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+        if (qseg == 0 && qt < nq) {
+            out[(size_t)qt * (HD + 2) + HD] = m;
+            out[(size_t)qt * (HD + 2) + HD + 1] = l;
+        }
     }
     __syncthreads();
-    // 6. O = P V: wave w owns dim tiles w, w+4, ...
-    float* out = a.part + ((size_t)h * a.nchunks + c) * nq * (HD + 2);
+    // 5. O = P V: wave w owns dim tiles w, w+4, ...
     for (int dt = wave; dt < HD / 16; dt += 4) {
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -569,10 +518,6 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
             const int t = 4 * (lane >> 4) + i;
             if (t < nq) out[(size_t)t * (HD + 2) + dt * 16 + fr] = acc[i];
         }
-    }
-    if (tid < nq) {
-        out[(size_t)tid * (HD + 2) + HD] = mrow[tid];
-        out[(size_t)tid * (HD + 2) + HD + 1] = lrow[tid];
     }
 }
 
@@ -738,22 +683,42 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
 }  // namespace
 
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
-    if (a.hd > 128 || a.T > 16) return hipErrorInvalidValue;
-    self_attn_mfma_kernel<<<a.heads, 256, 0, st>>>(a);
+    if (a.T < 1 || a.T > 16) return hipErrorInvalidValue;
+    switch (a.hd) {
+    case 64: self_attn_kernel<64><<<a.heads, 256, 0, st>>>(a); break;
+    case 128: self_attn_kernel<128><<<a.heads, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
-int attn_chunk_size(int hd, int kv_dtype) { return 16384 / (hd * (kv_dtype == 0 ? 2 : 4)); }
+int attn_chunk_size(int hd, int kv_dtype, int nkeys, int heads) {
+    const int big = 16384 / (hd * (kv_dtype == 0 ? 2 : 4));
+    if (kv_dtype != 0) return big;
+    // f16 caches: halve the chunk while the big one leaves the 256 CUs short of work-groups
+    return (long)heads * ((nkeys + big - 1) / big) < 256 ? big / 2 : big;
+}
 
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
-    if (a.nq > 16 || a.chunk != attn_chunk_size(a.hd, a.kv_dtype) || !a.qp.zeros || !a.qp.q) return hipErrorInvalidValue;
+    const int nkeys = a.key_hi - a.key_lo + a.nx;
+    if (a.nq < 1 || a.nq > 16 || a.chunk != attn_chunk_size(a.hd, a.kv_dtype, nkeys, a.heads) || !a.qp.zeros ||
+        !a.qp.q)
+        return hipErrorInvalidValue;
     if (a.qp.rope && a.qp.rope_dims > (a.hd <= 128 ? a.hd : 128)) return hipErrorInvalidValue;
     if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
     dim3 grid(a.nchunks, a.heads);
     if (a.kv_dtype == 0) {
+        if (a.qp.rope == 2 || (a.qp.rope == 1 && a.qp.rope_dims != a.hd)) return hipErrorInvalidValue;
+        const bool big = a.chunk == 16384 / (a.hd * 2);
         switch (a.hd) {
-        case 64: attn_split_mfma_kernel<64><<<grid, 256, 0, st>>>(a); break;
-        case 128: attn_split_mfma_kernel<128><<<grid, 256, 0, st>>>(a); break;
+        case 64:
+            if (big) attn_split_mfma_kernel<64, 128><<<grid, 256, 0, st>>>(a);
+            else attn_split_mfma_kernel<64, 64><<<grid, 256, 0, st>>>(a);
+            break;
+        case 128:
+            if (big) attn_split_mfma_kernel<128, 64><<<grid, 256, 0, st>>>(a);
+            else attn_split_mfma_kernel<128, 32><<<grid, 256, 0, st>>>(a);
+            break;
         default: return hipErrorInvalidValue;
         }
     } else {

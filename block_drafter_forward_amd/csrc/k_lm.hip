@@ -279,6 +279,113 @@ __global__ __launch_bounds__(256) void lm_argmax_rs_kernel(LmArgs a) {
     }
 }
 
+// bf16 tables, row-staged weights + work-group-shared activations: the 4 waves of a work-group own 4 adjacent
+// 16-row vocabulary tiles and walk the k-range in lockstep, so each chunk's activation fragments (8 k-steps,
+// 16 KB) are read from L2 once per work-group (each thread one quarter of it) into a double-buffered LDS slab
+// instead of once per wave. Weights and fragments of the next two chunks are in flight while one multiplies.
+struct WsRegs {
+    uint4 a[8];   // this wave's 16 rows x 256 columns
+    uint4 b[4];   // this thread's quarter of the chunk's fragments
+};
+
+__device__ __forceinline__ void ws_load(WsRegs& r, const LmArgs& a, int v0, int ch, int tid) {
+    const int lane = tid & 63;
+    const uint16_t* E = (const uint16_t*)a.E + (size_t)(v0 + (lane >> 5)) * a.K + ch * 256 + (lane & 31) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.a[i] = ldg_nt(E + (size_t)(2 * i) * a.K);
+    const uint4* xb = (const uint4*)(a.X + (size_t)ch * 8 * FRAG_STEP_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = xb[tid + 256 * j];
+}
+
+__device__ __forceinline__ void ws_stage(const WsRegs& r, uint4* alds, uint4* blds, int tid) {
+    const int lane = tid & 63;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) alds[(2 * i + (lane >> 5)) * RS_PITCH + (lane & 31)] = r.a[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) blds[tid + 256 * j] = r.b[j];
+}
+
+__device__ __forceinline__ void ws_compute(const uint4* alds, const uint4* blds, f32x4_t& acc, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 av = alds[r * RS_PITCH + 4 * i + g];
+        const uint4 bh = blds[i * 128 + lane], bl = blds[i * 128 + 64 + lane];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bh), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bl), acc, 0, 0, 0);
+    }
+}
+
+// K % 512 == 0 (an even number of chunks), V % 64 == 0 or the tail work-group's extra rows clamped.
+__global__ __launch_bounds__(256) void lm_argmax_ws_kernel(LmArgs a) {
+    __shared__ uint4 alds_all[4][16 * RS_PITCH];
+    __shared__ uint4 blds_all[2][1024];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4;
+    const int v0 = min((blockIdx.x * 4 + wave) * 16, a.V - 16);   // tail waves redo the last tile (discarded)
+    const bool own = (blockIdx.x * 4 + wave) * 16 < a.V;
+    uint4* alds = alds_all[wave];
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nch = a.K >> 8;
+    WsRegs r0, r1;
+    ws_load(r0, a, v0, 0, tid);
+    ws_load(r1, a, v0, 1, tid);
+    int ch = 0;
+    for (; ch + 2 < nch; ch += 2) {
+        ws_stage(r0, alds, blds_all[0], tid);
+        ws_load(r0, a, v0, ch + 2, tid);
+        __syncthreads();
+        ws_compute(alds, blds_all[0], acc, lane);
+        ws_stage(r1, alds, blds_all[1], tid);
+        ws_load(r1, a, v0, ch + 3, tid);
+        __syncthreads();
+        ws_compute(alds, blds_all[1], acc, lane);
+    }
+    ws_stage(r0, alds, blds_all[0], tid);
+    __syncthreads();
+    ws_compute(alds, blds_all[0], acc, lane);
+    ws_stage(r1, alds, blds_all[1], tid);
+    __syncthreads();
+    ws_compute(alds, blds_all[1], acc, lane);
+
+    // lane holds z[t = lane % 16][v0 + 4 g + j]
+    const int t = lane & 15;
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    if (own) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int v = v0 + 4 * g + j;
+            const float z = acc[j];
+            if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
+            if (z > best) { best = z; bidx = v; }
+        }
+    }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        const float ob = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bidx, o, 64);
+        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+    }
+    __shared__ float wb[4][16];
+    __shared__ int wi[4][16];
+    if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
+    __syncthreads();
+    if (tid < 16 && tid < a.T) {
+        float b = wb[0][tid];
+        int bi = wi[0][tid];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (wb[w][tid] > b || (wb[w][tid] == b && wi[w][tid] < bi)) { b = wb[w][tid]; bi = wi[w][tid]; }
+        if (bi != 0x7fffffff) {
+            const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
+            atomicMax(&a.best[tid], key);
+        }
+    }
+}
+
 __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tokens) {
     const int t = threadIdx.x;
     if (t < T) {
@@ -292,7 +399,9 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
 
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
     if (a.T > 16) return hipErrorInvalidValue;
-    if (wtype == 0 && a.perm == 0 && a.K % 256 == 0) {
+    if (wtype == 0 && a.perm == 0 && a.K % 512 == 0) {
+        lm_argmax_ws_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
+    } else if (wtype == 0 && a.perm == 0 && a.K % 256 == 0) {
         lm_argmax_rs_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
     } else {
         if ((a.K >> 5) % (2 * CH) != 0) return hipErrorInvalidValue;

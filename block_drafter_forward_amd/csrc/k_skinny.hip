@@ -117,58 +117,57 @@ __device__ __forceinline__ void sk_compute(const SkStage<NT, WT, SKC>& st, f32x4
     }
 }
 
-// Row-staged variant (bf16, KW a multiple of 8): the MFMA A-operand pattern (16 rows x 64 bytes per load
-// instruction) streams from HBM at about a third of the rate of row-contiguous reads. So each chunk of 8 k-steps
-// (256 columns) of the wave's 16-row tile is loaded as 8 row-contiguous instructions (2 rows x 512 bytes each),
-// parked in a wave-private LDS tile (row pitch padded by 16 bytes) and read back in the A layout; the next
-// chunk's weights and activation fragments are in flight while the current one multiplies.
-constexpr int RS_PITCH = 33;   // uint4 per LDS row: 32 + 1 pad
-
-template <int NT>
+// Row-staged variant (bf16, KW a multiple of RC = 8 or 4): the MFMA A-operand pattern (16 rows x 64 bytes per load
+// instruction) streams from HBM at about a third of the rate of row-contiguous reads. So each chunk of RC k-steps
+// (32 RC columns) of the wave's 16-row tile is loaded as RC row-contiguous instructions (16 / RC rows x 64 RC bytes
+// each: whole cache lines), parked in a wave-private LDS tile (row pitch padded by 16 bytes) and read back in the
+// A layout; the next chunk's weights and activation fragments are in flight while the current one multiplies.
+template <int NT, int RC>
 struct RsStage {
-    uint4 a[NT][8];
-    uint4 bh[8], bl[8];
+    uint4 a[NT][RC];
+    uint4 bh[RC], bl[RC];
 };
 
-template <int NT>
-__device__ __forceinline__ void rs_load(RsStage<NT>& st, const SkinnyGroup& G, int K, int m0, int s, int lane) {
+template <int NT, int RC>
+__device__ __forceinline__ void rs_load(RsStage<NT, RC>& st, const SkinnyGroup& G, int K, int m0, int s, int lane) {
     const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RC; ++i) {
         st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
         st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
     }
-    const int hr = lane >> 5, piece = lane & 31;
+    constexpr int RPI = 16 / RC, LPR = 64 / RPI;   // rows per instruction, lanes per row
+    const int sub = lane / LPR, piece = lane % LPR;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2);
+        const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + sub) * K + s * 32 + piece * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            st.a[n][i] = ldg_nt((const uint4*)(W + (size_t)(m0 + 2 * i + hr) * K + (size_t)s * 32) + piece);
+        for (int i = 0; i < RC; ++i) st.a[n][i] = ldg_nt((const uint4*)(W + (size_t)(RPI * i) * K));
     }
 }
 
-template <int NT>
-__device__ __forceinline__ void rs_compute(const RsStage<NT>& st, uint4* lds, f32x4_t* acc, int lane) {
-    const int hr = lane >> 5, piece = lane & 31, r = lane & 15, g = lane >> 4;
+template <int NT, int RC>
+__device__ __forceinline__ void rs_compute(const RsStage<NT, RC>& st, uint4* lds, f32x4_t* acc, int lane) {
+    constexpr int RPI = 16 / RC, LPR = 64 / RPI, PITCH = 4 * RC + 1;
+    const int sub = lane / LPR, piece = lane % LPR, r = lane & 15, g = lane >> 4;
     __builtin_amdgcn_wave_barrier();   // the previous chunk's LDS reads stay before these writes
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds[(n * 16 + 2 * i + hr) * RS_PITCH + piece] = st.a[n][i];
+        for (int i = 0; i < RC; ++i) lds[(n * 16 + RPI * i + sub) * PITCH + piece] = st.a[n][i];
     __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RC; ++i) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            const uint4 av = lds[(n * 16 + r) * RS_PITCH + 4 * i + g];
+            const uint4 av = lds[(n * 16 + r) * PITCH + 4 * i + g];
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(st.bh[i]), acc[n], 0, 0, 0);
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(st.bl[i]), acc[n], 0, 0, 0);
         }
     }
 }
 
-// UP = 2: row-staged chunks of 8 k-steps (bf16, KW % 8 == 0), double-buffered, last chunk peeled.
+// UP = 2: row-staged chunks of SKC (8 or 4) k-steps (bf16, KW % SKC == 0), double-buffered, last chunk peeled.
 // UP = 1: the wave's whole k-range (SKC == KW steps) is loaded at once, then multiplied -- every byte of the wave
 // in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
 // stage i computes), with the last pair peeled so the loop body carries no conditions.
@@ -195,24 +194,24 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
     for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     if constexpr (UP == 2) {
-        __shared__ uint4 rs_lds[4][NT * 16 * RS_PITCH];
+        __shared__ uint4 rs_lds[4][NT * 16 * (4 * SKC + 1)];
         uint4* lds = rs_lds[wave];
-        RsStage<NT> c0, c1;
-        const int nch = KW >> 3;
-        rs_load<NT>(c0, G, K, m0, s0, lane);
+        RsStage<NT, SKC> c0, c1;
+        const int nch = KW / SKC;
+        rs_load<NT, SKC>(c0, G, K, m0, s0, lane);
         int ch = 0;
         for (; ch + 2 < nch; ch += 2) {
-            rs_load<NT>(c1, G, K, m0, s0 + 8 * (ch + 1), lane);
-            rs_compute<NT>(c0, lds, acc, lane);
-            rs_load<NT>(c0, G, K, m0, s0 + 8 * (ch + 2), lane);
-            rs_compute<NT>(c1, lds, acc, lane);
+            rs_load<NT, SKC>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
+            rs_compute<NT, SKC>(c0, lds, acc, lane);
+            rs_load<NT, SKC>(c0, G, K, m0, s0 + SKC * (ch + 2), lane);
+            rs_compute<NT, SKC>(c1, lds, acc, lane);
         }
         if (ch + 1 < nch) {
-            rs_load<NT>(c1, G, K, m0, s0 + 8 * (ch + 1), lane);
-            rs_compute<NT>(c0, lds, acc, lane);
-            rs_compute<NT>(c1, lds, acc, lane);
+            rs_load<NT, SKC>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
+            rs_compute<NT, SKC>(c0, lds, acc, lane);
+            rs_compute<NT, SKC>(c1, lds, acc, lane);
         } else {
-            rs_compute<NT>(c0, lds, acc, lane);
+            rs_compute<NT, SKC>(c0, lds, acc, lane);
         }
     } else if constexpr (UP == 1) {
         SkStage<NT, WT, SKC> st;
@@ -286,8 +285,9 @@ template <int NT, int WT>
 hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
     const int KW = a.KW;
     dim3 grid(nwg), block(256);
-    if (WT == SKW_BF16 && a.perm == 0 && KW % 8 == 0) {
-        skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
+    if (WT == SKW_BF16 && a.perm == 0 && KW % 4 == 0) {
+        if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
+        else skinny_kernel<NT, WT, 2, 4><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }
 #define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n><<<grid, block, 0, st>>>(a); return hipGetLastError();
