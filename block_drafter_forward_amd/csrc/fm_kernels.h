@@ -109,10 +109,14 @@ struct QPrep {             // how a work-group builds its query rows for one hea
     int rope_dims;
     const float* rope_tab; // rows [cos rope_dims/2 | sin rope_dims/2]
     int pos_base;          // query t sits at position pos_base + t
+    int parts;             // q is the sum of this many split-K slabs (0 or 1: one), slab i at q + i * pstride
+    long long pstride;     //   (honoured by the f16-cache kernel; the f32-cache kernel takes one slab)
 };
 // Flow-map self-attention over the T slots (one work-group per head); writes o as fragments.
 struct SelfAttnArgs {
-    const float* qkv;      // [T][3D]: q | k | v
+    const float* qkv;      // [T][3D]: q | k | v, the sum of `parts` split-K slabs pstride floats apart
+    int parts;
+    long long pstride;
     int T, D, heads, hd;
     const uint16_t* qn;    // q_norm, k_norm (bf16 [hd])
     const uint16_t* kn;

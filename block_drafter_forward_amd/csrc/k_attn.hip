@@ -21,6 +21,8 @@
 
 namespace {
 
+constexpr int MAX_QSLABS = 4;   // split-K slabs of q (and of the self-attention's k, v) summed in the prologue
+
 __device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
     return dt == 0 ? f16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
@@ -45,9 +47,15 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     {
         const float* src = a.qkv + (size_t)tc * 3 * D + (size_t)w * D + (size_t)h * HD + seg * SEG;
 #pragma unroll
-        for (int j = 0; j < SEG / 4; ++j) {
-            const float4 f = ((const float4*)src)[j];
-            x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+        for (int j = 0; j < SEG; ++j) x[j] = 0.f;
+#pragma unroll
+        for (int p = 0; p < MAX_QSLABS; ++p) {   // every slab load issued together; absent slabs re-read slab 0
+            const float m = p < a.parts ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < SEG / 4; ++j) {
+                const float4 f = ((const float4*)(src + (p < a.parts ? p : 0) * a.pstride))[j];
+                x[4 * j] += m * f.x; x[4 * j + 1] += m * f.y; x[4 * j + 2] += m * f.z; x[4 * j + 3] += m * f.w;
+            }
         }
         const float* rt = a.rope_tab + (size_t)(a.pos_base + tc) * HD + seg * (SEG / 2);
 #pragma unroll
@@ -62,9 +70,15 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         const int vt = min(tid >> 4, T - 1), vp = tid & 15;
         const float* vs = a.qkv + (size_t)vt * 3 * D + 2 * (size_t)D + (size_t)h * HD + vp * VPT;
 #pragma unroll
-        for (int j = 0; j < VPT / 4; ++j) {
-            const float4 f = ((const float4*)vs)[j];
-            v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+        for (int j = 0; j < VPT; ++j) v[j] = 0.f;
+#pragma unroll
+        for (int p = 0; p < MAX_QSLABS; ++p) {
+            const float m = p < a.parts ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < VPT / 4; ++j) {
+                const float4 f = ((const float4*)(vs + (p < a.parts ? p : 0) * a.pstride))[j];
+                v[4 * j] += m * f.x; v[4 * j + 1] += m * f.y; v[4 * j + 2] += m * f.z; v[4 * j + 3] += m * f.w;
+            }
         }
     }
     float ss = 0.f;
@@ -399,10 +413,17 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
     float q[QS], nw[QS], cs[QS / 2], sn[QS / 2];
     {
         const float* src = qp.q + (size_t)tq * qp.q_ld + (size_t)h * qp.q_hs + qseg * QS;
+        const int parts = qp.parts > 1 ? qp.parts : 1;
 #pragma unroll
-        for (int j = 0; j < QS / 4; ++j) {
-            const float4 f = ((const float4*)src)[j];
-            q[4 * j] = f.x; q[4 * j + 1] = f.y; q[4 * j + 2] = f.z; q[4 * j + 3] = f.w;
+        for (int j = 0; j < QS; ++j) q[j] = 0.f;
+#pragma unroll
+        for (int p = 0; p < MAX_QSLABS; ++p) {   // every slab load issued together; absent slabs re-read slab 0
+            const float m = p < parts ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < QS / 4; ++j) {
+                const float4 f = ((const float4*)(src + (p < parts ? p : 0) * qp.pstride))[j];
+                q[4 * j] += m * f.x; q[4 * j + 1] += m * f.y; q[4 * j + 2] += m * f.z; q[4 * j + 3] += m * f.w;
+            }
         }
         const float* rt = qp.rope ? qp.rope_tab + (size_t)(qp.pos_base + tq) * HD + qseg * (QS / 2) : qp.zeros;
         const float* rs = qp.rope ? rt + HD / 2 : qp.zeros;
@@ -683,7 +704,7 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
 }  // namespace
 
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
-    if (a.T < 1 || a.T > 16) return hipErrorInvalidValue;
+    if (a.T < 1 || a.T > 16 || a.parts < 1 || a.parts > MAX_QSLABS) return hipErrorInvalidValue;
     switch (a.hd) {
     case 64: self_attn_kernel<64><<<a.heads, 256, 0, st>>>(a); break;
     case 128: self_attn_kernel<128><<<a.heads, 256, 0, st>>>(a); break;
@@ -706,6 +727,7 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
         return hipErrorInvalidValue;
     if (a.qp.rope && a.qp.rope_dims > (a.hd <= 128 ? a.hd : 128)) return hipErrorInvalidValue;
     if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
+    if (a.qp.parts > MAX_QSLABS || (a.kv_dtype != 0 && a.qp.parts > 1)) return hipErrorInvalidValue;
     dim3 grid(a.nchunks, a.heads);
     if (a.kv_dtype == 0) {
         if (a.qp.rope == 2 || (a.qp.rope == 1 && a.qp.rope_dims != a.hd)) return hipErrorInvalidValue;

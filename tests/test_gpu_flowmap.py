@@ -182,6 +182,16 @@ def test_longctx_workload(flashmap):
         rows = np.r_[0:64, n - 64:n]
         assert_rows_close(d.kv_layer(l, 0)[rows].float().cpu().numpy(), o.K[l][rows], what=f"prefill K{l}")
         assert_rows_close(d.kv_layer(l, 1)[rows].float().cpu().numpy(), o.V[l][rows], what=f"prefill V{l}")
+    # drafts over short prefixes of the cache: one key, a ragged chunk, and both sides of the split kernel's chunk
+    # switch (960 keys: 32-key chunks, as 16 heads x 15 64-key chunks would leave CUs idle; 961 keys: 64-key chunks)
+    for pos in (0, 16, 959, 960):
+        an = 1000 + pos
+        hid, tok, _, _ = _draft(fmod, d, cfg, anchor=an, pos=pos, debug=False)
+        out, _ = o.draft_block(an, pos)
+        _, z = o.lm_argmax(out)
+        e = assert_rows_close(hid, out, what=f"draft at pos {pos} hidden")
+        assert_tokens_match(tok, z)
+        _say(f"longctx: draft over L={pos + 1} keys ok, hidden err {e:.2e}")
     worst = 0.0
     exact = 0
     for s, (an, pos, ns) in enumerate(gen.longctx_schedule(cfg)):
