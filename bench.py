@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--graph", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for a rocprofv3 --pmc pass: set up, run fm_lm_argmax 5 times and one elementwise kernel that "
+                         "reads 1 GiB and writes 1 GiB (the counters' scale reference), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -122,6 +125,18 @@ def main():
     def step():
         d.fm_draft_block(hidden, anchor=anchor, pos=n)
         d.fm_lm_argmax(hidden, T, tokens)
+
+    if args.pmc_probe:
+        step()
+        for _ in range(5):
+            d.fm_lm_argmax(hidden, T, tokens)
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.mul(src, 2.0, out=dst)   # one elementwise kernel: 1 GiB read, 1 GiB written
+        torch.cuda.synchronize()
+        print("[bench] pmc probe done: 5 x fm_lm_argmax, one 1 GiB elementwise pass", file=sys.stderr, flush=True)
+        return
 
     stream = torch.cuda.current_stream()
     graph = None
