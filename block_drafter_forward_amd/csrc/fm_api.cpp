@@ -453,7 +453,6 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     // prefill: MFMA GEMMs
     float* ctx = d->at<float>(d->p.pctx);
     uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
-    const int mt = (n + 127) / 128;
     {
         PrefillArgs a{};
         a.ngroups = 1;
@@ -464,15 +463,18 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         a.N = D;
         a.K = KT;
         a.ld = D;
-        a.m_tiles = mt;
-        a.n_tiles = D / 128;
-        HIPCHK(launch_prefill(a, mt * a.n_tiles, st));
+        const int tile = prefill_tile(n, D, 1);
+        a.m_tiles = (n + tile - 1) / tile;
+        a.n_tiles = D / tile;
+        HIPCHK(launch_prefill(a, a.m_tiles * a.n_tiles, st));
     }
     HIPCHK(launch_rms_f16(ctx, n, D, d->B("hidden_norm.weight"), c.rms_eps, ctxn, st));
     for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
         PrefillArgs a{};
         const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
-        const int per = mt * (D / 128);
+        const int tile = prefill_tile(n, D, 2 * nl);
+        const int mt = (n + tile - 1) / tile;
+        const int per = mt * (D / tile);
         for (int j = 0; j < nl; ++j) {
             const int l = l0 + j;
             a.g[2 * j] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.k_proj.weight")),
@@ -495,7 +497,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         a.start = start;
         a.kv_dtype = c.kv_dtype;
         a.m_tiles = mt;
-        a.n_tiles = D / 128;
+        a.n_tiles = D / tile;
         HIPCHK(launch_prefill(a, 2 * nl * per, st));
     }
     return FM_OK;
@@ -746,7 +748,6 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     }
     float* ctx = d->at<float>(d->p.pctx);
     uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
-    const int mt = (n + 127) / 128;
     {
         PrefillArgs a{};
         a.ngroups = 1;
@@ -757,9 +758,10 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
         a.N = D;
         a.K = KT;
         a.ld = D;
-        a.m_tiles = mt;
-        a.n_tiles = D / 128;
-        HIPCHK(launch_prefill(a, mt * a.n_tiles, st));
+        const int tile = prefill_tile(n, D, 1);
+        a.m_tiles = (n + tile - 1) / tile;
+        a.n_tiles = D / tile;
+        HIPCHK(launch_prefill(a, a.m_tiles * a.n_tiles, st));
     }
     // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32), then per layer RMSNorm(H_ctx; attn_norm) -> f16
     {
@@ -774,10 +776,12 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     }
     for (int i = 0; i < c.layers; ++i)
         HIPCHK(launch_rms_f16(ctx, n, D, d->B(BB(i, "attn_norm")), c.rms_eps, ctxn + (size_t)i * c.max_ctx * D, st));
-    const int per = mt * (D / 128);
     for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
         PrefillArgs a{};
         const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
+        const int tile = prefill_tile(n, D, 2 * nl);
+        const int mt = (n + tile - 1) / tile;
+        const int per = mt * (D / tile);
         for (int j = 0; j < nl; ++j) {
             const int i = l0 + j;
             const uint16_t* Ai = ctxn + (size_t)i * c.max_ctx * D;
@@ -794,7 +798,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
         a.start = start;
         a.kv_dtype = c.kv_dtype;
         a.m_tiles = mt;
-        a.n_tiles = D / 128;
+        a.n_tiles = D / tile;
         HIPCHK(launch_prefill(a, 2 * nl * per, st));
     }
     return FM_OK;

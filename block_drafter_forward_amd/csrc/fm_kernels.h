@@ -238,6 +238,9 @@ struct PrefillArgs {
     int kv_dtype;
     int m_tiles, n_tiles;
 };
+// Tile edge (128 or 256) the launcher uses for rows x N x ngroups; the host sizes m_tiles, n_tiles and the
+// groups' tile_begin with it.
+int prefill_tile(int rows, int N, int ngroups);
 hipError_t launch_prefill(const PrefillArgs& a, int n_workgroups, hipStream_t st);
 
 // Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context).

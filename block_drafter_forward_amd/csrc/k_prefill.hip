@@ -4,9 +4,10 @@
 // taps, flashmap_drafter.js extendContext; module-dflash.ts #buildContext) and the per-layer K/V projections of the
 // fused rows. Operands are f16 on v_mfma_f32_16x16x32_f16 with f32 accumulation: the f32 taps are rounded to f16 on
 // their way into LDS (2^-11 relative, four times finer than bf16), the bf16 weights are widened to f16 exactly (up
-// to f16's subnormal range, |error| <= 2^-25). Tiles: 128 x 128 per work-group of 4 waves (2 x 2, 64 x 64 each,
-// 16 accumulators of 16x16), k-stages of 32 double-buffered in LDS with a 16-byte row pad (conflict-free fragment
-// reads), the next stage's global loads in flight while the current one computes. Work-groups are remapped so
+// to f16's subnormal range, |error| <= 2^-25). Tiles: 256 x 256 per work-group of 8 waves (2 x 4, 128 x 64 each,
+// 32 accumulators of 16x16) when the problem has enough of them, else 128 x 128 per 4 waves; k-stages of 32
+// double-buffered in LDS with a 16-byte row pad (conflict-free fragment reads), the next stage's global loads in
+// flight while the current one computes. The larger tile halves the L2 traffic per flop. Work-groups are remapped so
 // each XCD owns a contiguous run of tiles (consecutive n-tiles of the same row block share their A rows in that
 // XCD's L2).
 // Epilogues: f32 rows; a cache store (f16 / f32) at rows start + r; or, for K, the per-head RMSNorm over the tile's
@@ -17,7 +18,7 @@
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, LDP = BK + 8;
+constexpr int BK = 32, LDP = BK + 8;
 
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
 
@@ -25,11 +26,14 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
 }
 
-template <int AF32>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+// Tile T x T (T = 128: 4 waves as 2 x 2 of 64 x 64; T = 256: 8 waves as 2 x 4 of 128 x 64). Every thread stages
+// 16 k-values of one A row and one B row per k-stage; rows past the end of A are clamped (their results dropped).
+template <int AF32, int T>
+__global__ __launch_bounds__(T * 2) void prefill_kernel(PrefillArgs a) {
+    constexpr int BM = T, BN = T, NWN = T / 64, TI = T == 128 ? 4 : 8, TJ = 4;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
-    __shared__ float nred[2][BM];
+    __shared__ float nred[NWN][BM];
 
     int lin = blockIdx.x;
     const int total = gridDim.x;
@@ -46,31 +50,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int K = a.K;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / NWN, wn = wave % NWN;
     const int ldrow = tid >> 1, kofs = (tid & 1) * 16;
-    const bool avalid = r0 + ldrow < a.rows;
+    const int arow = min(r0 + ldrow, a.rows - 1);
 
     float4 ra[4];
     uint4 rah[2], rb[2];
     auto gload = [&](int kt) {
         const int k = kt * BK + kofs;
         if constexpr (AF32) {
-            if (avalid) {
-                const float4* p = (const float4*)((const float*)Ap + (size_t)(r0 + ldrow) * K + k);
+            const float4* p = (const float4*)((const float*)Ap + (size_t)arow * K + k);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ra[i] = p[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            for (int i = 0; i < 4; ++i) ra[i] = p[i];
         } else {
-            if (avalid) {
-                const uint4* p = (const uint4*)((const uint16_t*)Ap + (size_t)(r0 + ldrow) * K + k);
-                rah[0] = p[0];
-                rah[1] = p[1];
-            } else {
-                rah[0] = rah[1] = make_uint4(0, 0, 0, 0);
-            }
+            const uint4* p = (const uint4*)((const uint16_t*)Ap + (size_t)arow * K + k);
+            rah[0] = p[0];
+            rah[1] = p[1];
         }
         const uint4* pb = (const uint4*)(G.B + (size_t)(n0 + ldrow) * K + k);
         rb[0] = pb[0];
@@ -97,11 +92,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         *(uint4*)&Bs[buf][ldrow][kofs + 8] = make_uint4(o[4], o[5], o[6], o[7]);
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / BK;
     gload(0);
@@ -110,81 +105,81 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int fr = lane & 15, fk = 8 * (lane >> 4);
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        f16x8_t af[4], bfr[4];
+        gload(kt + 1 < nk ? kt + 1 : kt);   // the last stage re-reads itself: no conditional load
+        f16x8_t af[TI], bfr[TJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = as_f16x8(*(const uint4*)&As[buf][wm * 64 + i * 16 + fr][fk]);
+        for (int i = 0; i < TI; ++i) af[i] = as_f16x8(*(const uint4*)&As[buf][wm * (TI * 16) + i * 16 + fr][fk]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[j] = as_f16x8(*(const uint4*)&Bs[buf][wn * 64 + j * 16 + fr][fk]);
+        for (int j = 0; j < TJ; ++j) bfr[j] = as_f16x8(*(const uint4*)&Bs[buf][wn * 64 + j * 16 + fr][fk]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < TJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        if (kt + 1 < nk) lstore(buf ^ 1);
+        lstore(buf ^ 1);
         __syncthreads();
     }
 
-    // acc[i][j][q] = C[r0 + wm*64 + 16 i + 4 (lane/16) + q][n0 + wn*64 + 16 j + lane%16]
+    // acc[i][j][q] = C[r0 + wm*16*TI + 16 i + 4 (lane/16) + q][n0 + wn*64 + 16 j + lane%16]
     const int rq = 4 * (lane >> 4), cl = lane & 15;
     if (G.epi == PF_CACHE_K && G.knorm) {
         const int hd = a.hd;
-        float ssq[4][4];
+        float ssq[TI][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s += acc[i][j][q] * acc[i][j][q];
+                for (int j = 0; j < TJ; ++j) s += acc[i][j][q] * acc[i][j][q];
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
                 ssq[i][q] = s;
             }
-        if (hd == 128) {
+        if (hd == 128) {   // a head spans two waves along n
             if (cl == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < TI; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) nred[wn][wm * 64 + 16 * i + rq + q] = ssq[i][q];
+                    for (int q = 0; q < 4; ++q) nred[wn][wm * TI * 16 + 16 * i + rq + q] = ssq[i][q];
             }
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int rl = wm * 64 + 16 * i + rq + q;
-                    ssq[i][q] = nred[0][rl] + nred[1][rl];
+                    const int rl = wm * TI * 16 + 16 * i + rq + q;
+                    ssq[i][q] = nred[wn & ~1][rl] + nred[wn | 1][rl];
                 }
         }
         const int half = a.rope_dims >> 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int r = r0 + wm * 64 + 16 * i + rq + q;
+                const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
                 const float rs = 1.f / sqrtf(ssq[i][q] / (float)hd + a.eps);
                 const int pos = a.start + (r < a.rows ? r : 0);
                 const float* tr = a.rope_tab + (size_t)pos * a.rope_dims;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TJ; ++j) {
                     const int n = n0 + wn * 64 + 16 * j + cl;
                     const int d = n % hd;
                     const float v = acc[i][j][q] * rs * bf16_to_f32(G.knorm[d]);
                     const float p = __shfl_xor(v, 1, 64);
-                    const float c = tr[d >> 1], s = tr[half + (d >> 1)];
-                    acc[i][j][q] = (d & 1) ? v * c + p * s : v * c - p * s;
+                    const float c = tr[d >> 1], sn = tr[half + (d >> 1)];
+                    acc[i][j][q] = (d & 1) ? v * c + p * sn : v * c - p * sn;
                 }
             }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int r = r0 + wm * 64 + 16 * i + rq + q;
+            const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
             if (r >= a.rows) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TJ; ++j) {
                 const int n = n0 + wn * 64 + 16 * j + cl;
                 const float v = acc[i][j][q];
                 if (G.epi == PF_F32) {
@@ -200,9 +195,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
+int prefill_tile(int rows, int N, int ngroups) {
+    const long big_tiles = (long)((rows + 255) / 256) * (N / 256) * ngroups;
+    return (N % 256 == 0 && big_tiles >= 256) ? 256 : 128;   // at least one 256-tile per CU
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, int nwg, hipStream_t st) {
-    if (a.K % BK || a.N % BN) return hipErrorInvalidValue;
-    if (a.a_f32) prefill_kernel<1><<<nwg, 256, 0, st>>>(a);
-    else prefill_kernel<0><<<nwg, 256, 0, st>>>(a);
+    const int T = prefill_tile(a.rows, a.N, a.ngroups);
+    if (a.K % BK || a.N % T || a.rows < 1 || a.n_tiles != a.N / T || a.m_tiles != (a.rows + T - 1) / T)
+        return hipErrorInvalidValue;
+    if (T == 256) {
+        if (a.a_f32) prefill_kernel<1, 256><<<nwg, 512, 0, st>>>(a);
+        else prefill_kernel<0, 256><<<nwg, 512, 0, st>>>(a);
+    } else {
+        if (a.a_f32) prefill_kernel<1, 128><<<nwg, 256, 0, st>>>(a);
+        else prefill_kernel<0, 128><<<nwg, 256, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
