@@ -57,6 +57,147 @@ def draft_step_bytes(cfg, L: int) -> int:
     return b + 2 * Lyr * L * D * 2
 
 
+def weight_bytes(W, names) -> int:
+    """Bytes of the named tensors in their storage format (a Q8_0 tensor is its codes plus its f16 scales)."""
+    tot = 0
+    for n in names:
+        v = W[n]
+        tot += sum(x.nbytes for x in v) if isinstance(v, tuple) else v.nbytes
+    return tot
+
+
+def _graph_of(torch, fn):
+    """fn captured into a HIP graph after one eager run on a side stream; plain fn if capture fails."""
+    try:
+        cur = torch.cuda.current_stream()
+        s = torch.cuda.Stream()
+        s.wait_stream(cur)
+        with torch.cuda.stream(s):
+            fn()
+        cur.wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g.replay
+    except Exception as e:
+        print(f"[bench] graph capture failed ({e}); plain launches", file=sys.stderr, flush=True)
+        return fn
+
+
+def _time_ms(torch, run, warmup: int, reps: int) -> float:
+    """Mean ms of run() over reps calls after warmup calls, HIP events on torch's current stream (the stream the
+    library launches on)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _hbm_row(what, ms, nbytes, unit="per s"):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"what": what, "value": 1e3 / ms, "unit": unit, "us": ms * 1e3, "algorithmic_bytes": nbytes,
+            "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def _mfma_row(what, ms, rows, flop):
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"what": what, "value": rows / (ms * 1e-3), "unit": "tokens/s", "ms": ms, "flop": flop,
+            "achieved_tflops": tf, "mfma_frac": tf / MFMA_F16_PEAK_TFLOPS}
+
+
+def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
+    """The remaining measured rows of the hot-path table: long-context draft and 16-row append, the 512-row
+    prefill, the KV-injection draft and prefill, and the MTP pass at M = 1, 2, 4, 8."""
+    rows = {}
+    cfg, lcfg = configs.get("flashmap"), configs.get("longctx")
+    D, Ht, T, Lyr = cfg["dim"], cfg["target_dim"], cfg["block"], cfg["layers"]
+    hid = torch.empty(T, Ht, dtype=torch.float32, device="cuda")
+    tok = torch.empty(T, dtype=torch.int32, device="cuda")
+    an = torch.tensor([int(gen.anchors(cfg, "bench", 1)[0])], dtype=torch.int32, device="cuda")
+
+    # long context: draft at pos = 8192 (L = 8193) after the 8192-row prefill, then 16-row appends at 8192
+    P = lcfg["ctx_rows"]
+
+    def lstep():
+        dl.fm_draft_block(hid, anchor=an, pos=P)
+        dl.fm_lm_argmax(hid, T, tok)
+    ms = _time_ms(torch, _graph_of(torch, lstep), 5, reps)
+    rows["longctx_draft_L8193"] = _hbm_row("flow-map draft block + lm_head argmax at L = 8193", ms,
+                                           draft_step_bytes(lcfg, P + 1), "draft blocks/s")
+    t16 = torch.from_numpy(gen.taps(lcfg, "bench-append", 16)).cuda()
+    ms = _time_ms(torch, lambda: dl.fm_context_append(t16, P), 5, reps)
+    app_w = ["fc.weight", "hidden_norm.weight"] + [f"layers.{l}.cross_attn.{m}" for l in range(Lyr)
+                                                    for m in ("k_proj.weight", "v_proj.weight", "k_norm.weight")]
+    rows["longctx_append_16"] = _hbm_row("16-row context append (fc, RMSNorm, 12 K/V projections, f16 cache)", ms,
+                                         weight_bytes(W, app_w) + t16.numel() * 4 + 2 * Lyr * 16 * D * 2,
+                                         "appends/s")
+    dl.fm_context_append(t16, P)   # leave the context at 8192 + 16 rows
+
+    # 512-row prefill on the FlashMap shape
+    n = cfg["ctx_rows"]
+    tp = torch.from_numpy(gen.taps(cfg, "prefill", n)).cuda()
+    ms = _time_ms(torch, lambda: d.fm_context_append(tp, 0), 2, 10)
+    rows["flashmap_prefill_512"] = _mfma_row("512-row context prefill", ms, n,
+                                             2.0 * n * D * (cfg["n_taps"] * Ht + 2 * Lyr * D))
+
+    # KV-injection: 2048-row prefill, then the gamma = 5 draft + lm_head argmax
+    kc = configs.get("kvinject")
+    print("[bench] KV-injection weights", file=sys.stderr, flush=True)
+    Wk = gen.make_weights(kc)
+    dk = fm.Drafter(kc, fm.upload_weights(Wk))
+    nk, Dk, Htk, g = kc["ctx_rows"], kc["dim"], kc["target_dim"], kc["block"]
+    tk = torch.from_numpy(gen.taps(kc, "prefill", nk)).cuda()
+    ms = _time_ms(torch, lambda: dk.fm_context_append(tk, 0), 2, 10)
+    rows["kvinject_prefill_2048"] = _mfma_row("2048-row context prefill (KV-injection)", ms, nk,
+                                              2.0 * nk * Dk * (kc["n_taps"] * Htk + 2 * kc["layers"] * Dk))
+    hk = torch.empty(g, Htk, dtype=torch.float32, device="cuda")
+    tkk = torch.empty(g, dtype=torch.int32, device="cuda")
+    ak = torch.tensor([int(gen.anchors(kc, "bench", 1)[0])], dtype=torch.int32, device="cuda")
+
+    def kstep():
+        dk.fm_draft_block(hk, anchor=ak)
+        dk.fm_lm_argmax(hk, g, tkk)
+    ms = _time_ms(torch, _graph_of(torch, kstep), 5, reps)
+    kw = [nm for nm, _, _ in gen.kvinject_weight_specs(kc) if nm not in ("W_c", "ctx_norm")]
+    rows["kvinject_draft"] = _hbm_row("KV-injection draft (gamma 5) + lm_head argmax", ms,
+                                      weight_bytes(Wk, kw) + 2 * kc["layers"] * nk * Dk * 4,
+                                      "draft blocks/s")
+    del dk, Wk
+
+    # MTP head: M rows at pos0 = 4096 - M over the 4096-row cache, + the Q8_0 lm_head argmax
+    mc = configs.get("mtp")
+    print("[bench] MTP weights", file=sys.stderr, flush=True)
+    Wm = gen.make_weights(mc)
+    dm = fm.Drafter(mc, fm.upload_weights(Wm))
+    H, NKV, HD = mc["dim"], mc["kv_heads"], mc["head_dim"]
+    dm.kv_layer(0, 0).normal_()
+    dm.kv_layer(0, 1).normal_()
+    mw = weight_bytes(Wm, [nm for nm, _, _ in gen.mtp_weight_specs(mc)])
+    for M in (1, 2, 4, 8):
+        pos0 = mc["max_ctx"] - M
+        e, h = gen.mtp_inputs(mc, M)
+        e, h = torch.from_numpy(e).cuda(), torch.from_numpy(h).cuda()
+        hm = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        tm = torch.empty(M, dtype=torch.int32, device="cuda")
+
+        def mstep():
+            dm.fm_draft_block(hm, pos=pos0, rows=M, embed_rows=e, prev_hidden=h)
+            dm.fm_lm_argmax(hm, M, tm)
+        ms = _time_ms(torch, _graph_of(torch, mstep), 5, reps)
+        rows[f"mtp_pass_M{M}"] = _hbm_row(f"MTP pass, M = {M} rows + Q8_0 lm_head argmax", ms,
+                                          mw + 2 * (pos0 + M) * NKV * HD * 4, "passes/s")
+    del dm, Wm
+    return rows
+
+
 def cpu_baseline(cfg, W, budget_s: float):
     """The oracle (float64 NumPy) on the host cores: draft block + lm_head argmax at the same position."""
     from inputs import gen
@@ -95,6 +236,7 @@ def main():
     ap.add_argument("--graph", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline, lm_head and 8192-row prefill only")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for a rocprofv3 --pmc pass: set up, run fm_lm_argmax 5 times and one elementwise kernel that "
                          "reads 1 GiB and writes 1 GiB (the counters' scale reference), then exit")
@@ -220,6 +362,9 @@ def main():
                                  "unit": "TFLOP/s", "frac": pf_tflops / MFMA_F16_PEAK_TFLOPS, "flop": pf_flop,
                                  "dtype": "f16 operands, f32 accumulate"}},
     }
+    if not args.quick:
+        print("[bench] remaining workloads", file=sys.stderr, flush=True)
+        res["rows"] = other_rows(torch, fm, configs, gen, W, d, dl, max(20, args.steps // 4))
     if not args.no_cpu:
         print("[bench] oracle on the host cores", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, args.cpu_budget)
