@@ -15,6 +15,8 @@
 #include "fm_device.h"
 #include "fm_kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int CH = 4;   // k-steps per pipeline stage
@@ -318,37 +320,115 @@ __device__ __forceinline__ void ws_compute(const uint4* alds, const uint4* blds,
     }
 }
 
-// K % 512 == 0 (an even number of chunks), V % 64 == 0 or the tail work-group's extra rows clamped.
+// Q8_0 tables, same structure: a chunk of 8 k-steps is 8 Q8_0 blocks per row, 256 code bytes (4 rows per
+// 1 KB load instruction) and 8 f16 scales per row (one 16-byte load by lanes 0-15). Codes go to a wave-private LDS
+// tile and come back as the A operand (8 codes = 8 bytes per lane, widened exactly to bf16); scales go to a
+// transposed [step][row] LDS slab so a lane reads its 4 output rows' scales of a step in one 8-byte read; each step's
+// product is scaled per row before it is accumulated.
+constexpr int Q8_PITCH = 17;   // uint4 per LDS code row: 16 + 1 pad
+
+struct WsRegsQ8 {
+    uint4 a[4];   // 16 rows x 256 codes
+    uint4 sc;     // lanes 0-15: row lane's 8 scales
+    uint4 b[4];
+};
+
+__device__ __forceinline__ void ws_load_q8(WsRegsQ8& r, const LmArgs& a, int v0, int ch, int tid) {
+    const int lane = tid & 63;
+    const int8_t* C = (const int8_t*)a.E + (size_t)(v0 + (lane >> 4)) * a.K + ch * 256 + (lane & 15) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.a[i] = ldg_nt(C + (size_t)(4 * i) * a.K);
+    const int nb = a.K >> 5;
+    r.sc = ldg_nt((const uint16_t*)a.Ed + (size_t)(v0 + (lane & 15)) * nb + ch * 8);
+    const uint4* xb = (const uint4*)(a.X + (size_t)ch * 8 * FRAG_STEP_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = xb[tid + 256 * j];
+}
+
+__device__ __forceinline__ void ws_stage_q8(const WsRegsQ8& r, uint4* alds, uint16_t* slds, uint4* blds, int tid) {
+    const int lane = tid & 63;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) alds[(4 * i + (lane >> 4)) * Q8_PITCH + (lane & 15)] = r.a[i];
+    if (lane < 16) {
+        const uint32_t w[4] = {r.sc.x, r.sc.y, r.sc.z, r.sc.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            slds[(2 * e) * 16 + lane] = (uint16_t)(w[e] & 0xffffu);
+            slds[(2 * e + 1) * 16 + lane] = (uint16_t)(w[e] >> 16);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) blds[tid + 256 * j] = r.b[j];
+}
+
+__device__ __forceinline__ void ws_compute_q8(const uint4* alds, const uint16_t* slds, const uint4* blds, f32x4_t& acc,
+                                              int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint2 cv = ((const uint2*)(alds + r * Q8_PITCH))[4 * i + g];
+        const bf16x8_t A = as_bf(i8x8_bf16(cv));
+        const uint4 bh = blds[i * 128 + lane], bl = blds[i * 128 + 64 + lane];
+        f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf(bh), p, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf(bl), p, 0, 0, 0);
+        const uint2 sv = *(const uint2*)(slds + i * 16 + 4 * g);
+        acc[0] += f16_to_f32((uint16_t)(sv.x & 0xffffu)) * p[0];
+        acc[1] += f16_to_f32((uint16_t)(sv.x >> 16)) * p[1];
+        acc[2] += f16_to_f32((uint16_t)(sv.y & 0xffffu)) * p[2];
+        acc[3] += f16_to_f32((uint16_t)(sv.y >> 16)) * p[3];
+    }
+}
+
+// K % 512 == 0 (an even number of chunks), V % 16 == 0 (a tail work-group's extra waves redo the last tile).
+template <int WT>
 __global__ __launch_bounds__(256) void lm_argmax_ws_kernel(LmArgs a) {
-    __shared__ uint4 alds_all[4][16 * RS_PITCH];
+    constexpr int APITCH = WT == 0 ? RS_PITCH : Q8_PITCH;
+    __shared__ uint4 alds_all[4][16 * APITCH];
+    __shared__ uint16_t slds_all[4][8 * 16];
     __shared__ uint4 blds_all[2][1024];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4;
     const int v0 = min((blockIdx.x * 4 + wave) * 16, a.V - 16);   // tail waves redo the last tile (discarded)
     const bool own = (blockIdx.x * 4 + wave) * 16 < a.V;
     uint4* alds = alds_all[wave];
+    uint16_t* slds = slds_all[wave];
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int nch = a.K >> 8;
-    WsRegs r0, r1;
-    ws_load(r0, a, v0, 0, tid);
-    ws_load(r1, a, v0, 1, tid);
+    using Regs = typename std::conditional<WT == 0, WsRegs, WsRegsQ8>::type;
+    auto load = [&](Regs& r, int ch) {
+        if constexpr (WT == 0) ws_load(r, a, v0, ch, tid);
+        else ws_load_q8(r, a, v0, ch, tid);
+    };
+    auto stage = [&](const Regs& r, int buf) {
+        if constexpr (WT == 0) ws_stage(r, alds, blds_all[buf], tid);
+        else ws_stage_q8(r, alds, slds, blds_all[buf], tid);
+    };
+    auto compute = [&](int buf) {
+        if constexpr (WT == 0) ws_compute(alds, blds_all[buf], acc, lane);
+        else ws_compute_q8(alds, slds, blds_all[buf], acc, lane);
+    };
+    Regs r0, r1;
+    load(r0, 0);
+    load(r1, 1);
     int ch = 0;
     for (; ch + 2 < nch; ch += 2) {
-        ws_stage(r0, alds, blds_all[0], tid);
-        ws_load(r0, a, v0, ch + 2, tid);
+        stage(r0, 0);
+        load(r0, ch + 2);
         __syncthreads();
-        ws_compute(alds, blds_all[0], acc, lane);
-        ws_stage(r1, alds, blds_all[1], tid);
-        ws_load(r1, a, v0, ch + 3, tid);
+        compute(0);
+        stage(r1, 1);
+        load(r1, ch + 3);
         __syncthreads();
-        ws_compute(alds, blds_all[1], acc, lane);
+        compute(1);
     }
-    ws_stage(r0, alds, blds_all[0], tid);
+    stage(r0, 0);
     __syncthreads();
-    ws_compute(alds, blds_all[0], acc, lane);
-    ws_stage(r1, alds, blds_all[1], tid);
+    compute(0);
+    stage(r1, 1);
     __syncthreads();
-    ws_compute(alds, blds_all[1], acc, lane);
+    compute(1);
 
     // lane holds z[t = lane % 16][v0 + 4 g + j]
     const int t = lane & 15;
@@ -399,8 +479,9 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
 
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
     if (a.T > 16) return hipErrorInvalidValue;
-    if (wtype == 0 && a.perm == 0 && a.K % 512 == 0) {
-        lm_argmax_ws_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
+    if (a.perm == 0 && a.K % 512 == 0) {
+        if (wtype == 0) lm_argmax_ws_kernel<0><<<(a.V + 63) / 64, 256, 0, st>>>(a);
+        else lm_argmax_ws_kernel<1><<<(a.V + 63) / 64, 256, 0, st>>>(a);
     } else if (wtype == 0 && a.perm == 0 && a.K % 256 == 0) {
         lm_argmax_rs_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
     } else {

@@ -167,6 +167,74 @@ __device__ __forceinline__ void rs_compute(const RsStage<NT, RC>& st, uint4* lds
     }
 }
 
+// Q8_0 row staging (KW a multiple of 8): a chunk of 8 k-steps is 8 Q8_0 blocks per row -- 256 code bytes (4 rows
+// per 1 KB load instruction) and 8 f16 scales per row (lanes 0-15, one 16-byte load). Codes return from a
+// wave-private LDS tile as the A operand (8 bytes per lane, widened exactly to bf16); the scales sit transposed
+// [step][row] so a lane reads the scales of its 4 output rows for a step in one 8-byte read.
+constexpr int Q8_PITCH = 17;   // uint4 per LDS code row: 16 + 1 pad
+
+template <int NT>
+struct RsStageQ8 {
+    uint4 a[NT][4];
+    uint4 sc[NT];
+    uint4 bh[8], bl[8];
+};
+
+template <int NT>
+__device__ __forceinline__ void rs_load_q8(RsStageQ8<NT>& st, const SkinnyGroup& G, int K, int m0, int s, int lane) {
+    const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
+        st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
+    }
+    const int nb = K >> 5;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + (lane >> 4)) * K + s * 32 + (lane & 15) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.a[n][i] = ldg_nt((const uint4*)(C + (size_t)(4 * i) * K));
+        st.sc[n] = ldg_nt((const uint4*)((const uint16_t*)(n == 0 ? G.Wd : G.W2d) + (size_t)(m0 + (lane & 15)) * nb + s));
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void rs_compute_q8(const RsStageQ8<NT>& st, uint4* lds, uint16_t* slds, f32x4_t* acc,
+                                              int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    __builtin_amdgcn_wave_barrier();   // the previous chunk's LDS reads stay before these writes
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds[(n * 16 + 4 * i + (lane >> 4)) * Q8_PITCH + (lane & 15)] = st.a[n][i];
+        if (lane < 16) {
+            const uint32_t w[4] = {st.sc[n].x, st.sc[n].y, st.sc[n].z, st.sc[n].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                slds[(n * 8 + 2 * e) * 16 + lane] = (uint16_t)(w[e] & 0xffffu);
+                slds[(n * 8 + 2 * e + 1) * 16 + lane] = (uint16_t)(w[e] >> 16);
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const uint2 cv = ((const uint2*)(lds + (n * 16 + r) * Q8_PITCH))[4 * i + g];
+            const bf16x8_t A = as_bf16x8(i8x8_to_bf16x8(cv));
+            f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bh[i]), p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bl[i]), p, 0, 0, 0);
+            const uint2 sv = *(const uint2*)(slds + (n * 8 + i) * 16 + 4 * g);
+            acc[n][0] += f16_to_f32((uint16_t)(sv.x & 0xffffu)) * p[0];
+            acc[n][1] += f16_to_f32((uint16_t)(sv.x >> 16)) * p[1];
+            acc[n][2] += f16_to_f32((uint16_t)(sv.y & 0xffffu)) * p[2];
+            acc[n][3] += f16_to_f32((uint16_t)(sv.y >> 16)) * p[3];
+        }
+    }
+}
+
 // UP = 2: row-staged chunks of SKC (8 or 4) k-steps (bf16, KW % SKC == 0), double-buffered, last chunk peeled.
 // UP = 1: the wave's whole k-range (SKC == KW steps) is loaded at once, then multiplied -- every byte of the wave
 // in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
@@ -193,7 +261,29 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (UP == 2) {
+    if constexpr (UP == 2 && WT == SKW_Q8_0) {
+        __shared__ uint4 q8_lds[4][NT * 16 * Q8_PITCH];
+        __shared__ uint16_t q8_slds[4][NT * 8 * 16];
+        uint4* lds = q8_lds[wave];
+        uint16_t* slds = q8_slds[wave];
+        RsStageQ8<NT> c0, c1;
+        const int nch = KW / 8;
+        rs_load_q8<NT>(c0, G, K, m0, s0, lane);
+        int ch = 0;
+        for (; ch + 2 < nch; ch += 2) {
+            rs_load_q8<NT>(c1, G, K, m0, s0 + 8 * (ch + 1), lane);
+            rs_compute_q8<NT>(c0, lds, slds, acc, lane);
+            rs_load_q8<NT>(c0, G, K, m0, s0 + 8 * (ch + 2), lane);
+            rs_compute_q8<NT>(c1, lds, slds, acc, lane);
+        }
+        if (ch + 1 < nch) {
+            rs_load_q8<NT>(c1, G, K, m0, s0 + 8 * (ch + 1), lane);
+            rs_compute_q8<NT>(c0, lds, slds, acc, lane);
+            rs_compute_q8<NT>(c1, lds, slds, acc, lane);
+        } else {
+            rs_compute_q8<NT>(c0, lds, slds, acc, lane);
+        }
+    } else if constexpr (UP == 2) {
         __shared__ uint4 rs_lds[4][NT * 16 * (4 * SKC + 1)];
         uint4* lds = rs_lds[wave];
         RsStage<NT, SKC> c0, c1;
@@ -288,6 +378,10 @@ hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
     if (WT == SKW_BF16 && a.perm == 0 && KW % 4 == 0) {
         if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
         else skinny_kernel<NT, WT, 2, 4><<<grid, block, 0, st>>>(a);
+        return hipGetLastError();
+    }
+    if (WT == SKW_Q8_0 && a.perm == 0 && KW % 8 == 0) {
+        skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }
 #define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n><<<grid, block, 0, st>>>(a); return hipGetLastError();
