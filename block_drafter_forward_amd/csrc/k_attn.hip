@@ -542,6 +542,169 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
     }
 }
 
+// ── split-L attention on the matrix cores (f32 cache, grouped queries) ─────────────────────────────
+// One work-group = one kv head x one chunk of 32 keys (cache rows, then the optional extra f32 rows), 4 waves, for
+// all G = heads / kv_heads query heads of the group at once (G * nq <= 16 QT rows, row t = head-in-group * nq + m),
+// so each K/V element is read once per chunk. K and V are split f32 -> f16 hi + lo on their way into LDS (V
+// transposed), the queries likewise; scores take K_hi q_hi + K_hi q_lo + K_lo q_hi on v_mfma_f32_16x16x32_f16
+// (the lo * lo term is below 2^-22 relative), P.V likewise with P split hi + lo. Queries arrive ready (no head-norm,
+// no RoPE: the MTP queries are prepared by mtp_prep, the KV-injection has neither). Writes the same per-chunk
+// (o, max, sum) partials as the other split kernels.
+template <int HD, int QT>
+__global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
+    constexpr int C = 32;
+    constexpr int KROW = HD + 8, VROW = C + 8, QROW = HD + 8, PROW = C + 8;
+    constexpr int NQR = 16 * QT;                 // query rows held
+    constexpr int V4 = HD / 4;                   // float4 per key row
+    constexpr int LDK = C * V4 / 256;            // float4 of K (and of V) per thread
+    constexpr int LDQ = NQR * V4 / 256;          // float4 of q per thread
+    static_assert(LDK >= 1 && LDQ >= 1, "shape");
+    const int c = blockIdx.x, kh = blockIdx.y;
+    const int nq = a.nq;
+    const int G = a.heads / a.kv_heads;
+    const int Q = G * nq;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const QPrep& qp = a.qp;
+    __shared__ __attribute__((aligned(16))) _Float16 Kh[C * KROW], Kl[C * KROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Vth[HD * VROW], Vtl[HD * VROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[NQR * QROW], Ql[NQR * QROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Ph[NQR * PROW], Pl[NQR * PROW];
+    __shared__ float S[NQR][C + 1];
+
+    const int ncache = a.key_hi - a.key_lo;
+    const int ntot = ncache + a.nx;
+    const int k0 = c * C;
+
+    // 1. every global load up front
+    float4 kr[LDK], vr[LDK], qr[LDQ];
+#pragma unroll
+    for (int i = 0; i < LDK; ++i) {
+        const int u = tid + 256 * i, row = u / V4, c4 = u % V4;
+        const int kidx = min(k0 + row, ntot - 1);
+        const bool fc = kidx < ncache;
+        const float* kb = fc ? (const float*)a.kc + (size_t)(a.key_lo + kidx) * a.kv_ld
+                             : a.kx + (size_t)(kidx - ncache) * a.x_ld;
+        const float* vb = fc ? (const float*)a.vc + (size_t)(a.key_lo + kidx) * a.kv_ld
+                             : a.vx + (size_t)(kidx - ncache) * a.x_ld;
+        kr[i] = *((const float4*)(kb + (size_t)kh * HD) + c4);
+        vr[i] = *((const float4*)(vb + (size_t)kh * HD) + c4);
+    }
+#pragma unroll
+    for (int i = 0; i < LDQ; ++i) {
+        const int u = tid + 256 * i, t = u / V4, c4 = u % V4;
+        const int hl = t / nq, m = t - hl * nq;
+        const float* src = t < Q ? qp.q + (size_t)m * qp.q_ld + (size_t)(kh * G + hl) * qp.q_hs : qp.zeros;
+        qr[i] = *((const float4*)src + c4);
+    }
+    // 2. hi/lo f16 splits into LDS: K row-major, V transposed (dim-major), queries row-major
+#pragma unroll
+    for (int i = 0; i < LDK; ++i) {
+        const int u = tid + 256 * i, row = u / V4, d = 4 * (u % V4);
+        const float kv[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+        const float vv[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const _Float16 hk = (_Float16)kv[e], hv = (_Float16)vv[e];
+            Kh[row * KROW + d + e] = hk;
+            Kl[row * KROW + d + e] = (_Float16)(kv[e] - (float)hk);
+            Vth[(d + e) * VROW + row] = hv;
+            Vtl[(d + e) * VROW + row] = (_Float16)(vv[e] - (float)hv);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < LDQ; ++i) {
+        const int u = tid + 256 * i, t = u / V4, d = 4 * (u % V4);
+        const float qv[4] = {qr[i].x, qr[i].y, qr[i].z, qr[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = t < Q ? qv[e] : 0.f;
+            const _Float16 h = (_Float16)x;
+            Qh[t * QROW + d + e] = h;
+            Ql[t * QROW + d + e] = (_Float16)(x - (float)h);
+        }
+    }
+    __syncthreads();
+    // 3. scores Sᵀ[j][t]: (key tile, query tile) pairs over the waves
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    for (int pr = wave; pr < 2 * QT; pr += 4) {
+        const int kt = pr & 1, qt = pr >> 1;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < HD / 32; ++s) {
+            const f16x8_t Ah = *(const f16x8_t*)(Kh + (kt * 16 + fr) * KROW + s * 32 + fk);
+            const f16x8_t Al = *(const f16x8_t*)(Kl + (kt * 16 + fr) * KROW + s * 32 + fk);
+            const f16x8_t Bh = *(const f16x8_t*)(Qh + (qt * 16 + fr) * QROW + s * 32 + fk);
+            const f16x8_t Bl = *(const f16x8_t*)(Ql + (qt * 16 + fr) * QROW + s * 32 + fk);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, acc, 0, 0, 0);
+        }
+        // lane holds keys j = 16 kt + 4 (lane / 16) + i for query row t = 16 qt + lane % 16
+        const int t = qt * 16 + fr;
+        const int m = t % nq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = kt * 16 + 4 * (lane >> 4) + i;
+            const int kidx = k0 + j;
+            float v = acc[i] * a.scale;
+            if (kidx >= ntot) v = -INFINITY;
+            if (a.causal_base >= 0 && kidx < ncache && a.key_lo + kidx > a.causal_base + m) v = -INFINITY;
+            S[t][j] = v;
+        }
+    }
+    __syncthreads();
+    // 4. softmax statistics: 4 threads per query row, 8 keys each; P = exp(S - m) split hi/lo
+    {
+        const int t = tid >> 2, q4 = tid & 3;
+        if (t < NQR) {
+            float sv[C / 4], mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < C / 4; ++i) { sv[i] = S[t][q4 * (C / 4) + i]; mx = fmaxf(mx, sv[i]); }
+            mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+            float l = 0.f;
+#pragma unroll
+            for (int i = 0; i < C / 4; ++i) {
+                const float p = (mx == -INFINITY || t >= Q) ? 0.f : expf(sv[i] - mx);
+                const _Float16 h = (_Float16)p;
+                Ph[t * PROW + q4 * (C / 4) + i] = h;
+                Pl[t * PROW + q4 * (C / 4) + i] = (_Float16)(p - (float)h);
+                l += p;
+            }
+            l += __shfl_xor(l, 1, 64);
+            l += __shfl_xor(l, 2, 64);
+            if (q4 == 0 && t < Q) {
+                const int hl = t / nq, m = t - hl * nq;
+                float* out = a.part + (((size_t)(kh * G + hl) * a.nchunks + c) * nq + m) * (HD + 2);
+                out[HD] = mx;
+                out[HD + 1] = l;
+            }
+        }
+    }
+    __syncthreads();
+    // 5. O = P V: (query tile, dim tile) pairs over the waves, one 32-key step each
+    for (int pr = wave; pr < QT * (HD / 16); pr += 4) {
+        const int qt = pr / (HD / 16), dt = pr % (HD / 16);
+        const f16x8_t Ah = *(const f16x8_t*)(Ph + (qt * 16 + fr) * PROW + fk);
+        const f16x8_t Al = *(const f16x8_t*)(Pl + (qt * 16 + fr) * PROW + fk);
+        const f16x8_t Bh = *(const f16x8_t*)(Vth + (dt * 16 + fr) * VROW + fk);
+        const f16x8_t Bl = *(const f16x8_t*)(Vtl + (dt * 16 + fr) * VROW + fk);
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, acc, 0, 0, 0);
+        // lane holds O[t = 16 qt + 4 (lane / 16) + i][d = 16 dt + lane % 16]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = qt * 16 + 4 * (lane >> 4) + i;
+            if (t < Q) {
+                const int hl = t / nq, m = t - hl * nq;
+                a.part[(((size_t)(kh * G + hl) * a.nchunks + c) * nq + m) * (HD + 2) + dt * 16 + fr] = acc[i];
+            }
+        }
+    }
+}
+
 // One work-group per (head, query row): thread (4-dim group, chunk group) folds its chunks with the online
 // rescale, four chunks' loads in flight at a time; the chunk groups are then folded in LDS.
 template <int HD>
@@ -713,9 +876,16 @@ hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The f32-cache matrix-core kernel: head widths 128 / 256, queries ready-made, G * nq <= 48.
+static bool f32_mfma_fits(const AttnArgs& a) {
+    const int G = a.heads / a.kv_heads;
+    return a.kv_dtype == 1 && (a.hd == 128 || a.hd == 256) && !a.qp.norm_bf16 && !a.qp.norm_f32 && !a.qp.rope &&
+           a.qp.parts <= 1 && G * a.nq <= 48;
+}
+
 int attn_chunk_size(int hd, int kv_dtype, int nkeys, int heads) {
     const int big = 16384 / (hd * (kv_dtype == 0 ? 2 : 4));
-    if (kv_dtype != 0) return big;
+    if (kv_dtype != 0) return (hd == 128 || hd == 256) ? 32 : big;
     // f16 caches: halve the chunk while the big one leaves the 256 CUs short of work-groups
     return (long)heads * ((nkeys + big - 1) / big) < 256 ? big / 2 : big;
 }
@@ -743,11 +913,22 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
             break;
         default: return hipErrorInvalidValue;
         }
+    } else if (f32_mfma_fits(a)) {
+        const int rows = (a.heads / a.kv_heads) * a.nq;
+        dim3 g2(a.nchunks, a.kv_heads);
+        if (a.hd == 128) {
+            if (rows <= 16) attn_split_f32_mfma_kernel<128, 1><<<g2, 256, 0, st>>>(a);
+            else if (rows <= 32) attn_split_f32_mfma_kernel<128, 2><<<g2, 256, 0, st>>>(a);
+            else attn_split_f32_mfma_kernel<128, 3><<<g2, 256, 0, st>>>(a);
+        } else {
+            if (rows <= 16) attn_split_f32_mfma_kernel<256, 1><<<g2, 256, 0, st>>>(a);
+            else if (rows <= 32) attn_split_f32_mfma_kernel<256, 2><<<g2, 256, 0, st>>>(a);
+            else attn_split_f32_mfma_kernel<256, 3><<<g2, 256, 0, st>>>(a);
+        }
     } else {
+        if (a.hd == 256 || a.hd == 128) return hipErrorInvalidValue;   // the vector-ALU kernel's chunk is not 32
         switch (a.hd) {
         case 64: attn_split_kernel<64, 1><<<grid, 256, 0, st>>>(a); break;
-        case 128: attn_split_kernel<128, 1><<<grid, 256, 0, st>>>(a); break;
-        case 256: attn_split_kernel<256, 1><<<grid, 256, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     }

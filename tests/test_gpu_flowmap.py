@@ -163,6 +163,31 @@ def test_flashmap_prefill_and_draft(flashmap):
     _say(f"flashmap draft hidden err {e:.2e}; tokens exact on {k}/{cfg['block']} rows")
 
 
+def test_flashmap_ragged_prefill(flashmap):
+    """A 1000-row prefill: the fusion GEMM on 128-row tiles, the 12 K/V projections on 256-row tiles whose last
+    row block is ragged (1000 = 3 x 256 + 232)."""
+    from block_drafter_forward_amd import fm as fmod
+    cfg, _, _, o0 = flashmap
+    d = fmod.Drafter(cfg, fmod.upload_weights(o0.raw))
+    o = flowmap.FlowMapOracle(cfg, o0.raw)
+    o._w = o0._w
+    n = 1000
+    _say(f"flashmap: {n}-row ragged prefill")
+    taps = gen.taps(cfg, "ragged", n)
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    torch.cuda.synchronize()
+    rows = np.r_[0:8, 250:262, 760:776, n - 40:n]
+    worst = 0.0
+    for l in range(cfg["layers"]):
+        worst = max(worst, assert_rows_close(d.kv_layer(l, 0)[rows].float().cpu().numpy(), o.K[l][rows],
+                                             what=f"ragged K{l}"))
+        worst = max(worst, assert_rows_close(d.kv_layer(l, 1)[rows].float().cpu().numpy(), o.V[l][rows],
+                                             what=f"ragged V{l}"))
+    assert d.length == n
+    _say(f"flashmap ragged prefill worst row err {worst:.2e}")
+
+
 def test_longctx_workload(flashmap):
     """8192-row prefill on the MFMA path, then 64 draft steps, each followed by an append of U{1..16} rows at the
     anchor position (the long-context workload's own schedule)."""
