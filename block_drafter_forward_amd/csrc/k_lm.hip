@@ -290,6 +290,7 @@ struct WsRegs {
     uint4 b[4];   // this thread's quarter of the chunk's fragments
 };
 
+template <int NW>
 __device__ __forceinline__ void ws_load(WsRegs& r, const LmArgs& a, int v0, int ch, int tid) {
     const int lane = tid & 63;
     const uint16_t* E = (const uint16_t*)a.E + (size_t)(v0 + (lane >> 5)) * a.K + ch * 256 + (lane & 31) * 8;
@@ -297,16 +298,17 @@ __device__ __forceinline__ void ws_load(WsRegs& r, const LmArgs& a, int v0, int 
     for (int i = 0; i < 8; ++i) r.a[i] = ldg_nt(E + (size_t)(2 * i) * a.K);
     const uint4* xb = (const uint4*)(a.X + (size_t)ch * 8 * FRAG_STEP_BYTES);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.b[j] = xb[tid + 256 * j];
+    for (int j = 0; j < 16 / NW; ++j) r.b[j] = xb[tid + 64 * NW * j];
 }
 
+template <int NW>
 __device__ __forceinline__ void ws_stage(const WsRegs& r, uint4* alds, uint4* blds, int tid) {
     const int lane = tid & 63;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 8; ++i) alds[(2 * i + (lane >> 5)) * RS_PITCH + (lane & 31)] = r.a[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) blds[tid + 256 * j] = r.b[j];
+    for (int j = 0; j < 16 / NW; ++j) blds[tid + 64 * NW * j] = r.b[j];
 }
 
 __device__ __forceinline__ void ws_compute(const uint4* alds, const uint4* blds, f32x4_t& acc, int lane) {
@@ -333,18 +335,21 @@ struct WsRegsQ8 {
     uint4 b[4];
 };
 
+template <int NW>
 __device__ __forceinline__ void ws_load_q8(WsRegsQ8& r, const LmArgs& a, int v0, int ch, int tid) {
     const int lane = tid & 63;
     const int8_t* C = (const int8_t*)a.E + (size_t)(v0 + (lane >> 4)) * a.K + ch * 256 + (lane & 15) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.a[i] = ldg_nt(C + (size_t)(4 * i) * a.K);
     const int nb = a.K >> 5;
-    r.sc = ldg_nt((const uint16_t*)a.Ed + (size_t)(v0 + (lane & 15)) * nb + ch * 8);
+    // scales with an ordinary load: a 128-byte line of them serves 8 chunks and must stay in L2 meanwhile
+    r.sc = *(const uint4*)((const uint16_t*)a.Ed + (size_t)(v0 + (lane & 15)) * nb + ch * 8);
     const uint4* xb = (const uint4*)(a.X + (size_t)ch * 8 * FRAG_STEP_BYTES);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.b[j] = xb[tid + 256 * j];
+    for (int j = 0; j < 16 / NW; ++j) r.b[j] = xb[tid + 64 * NW * j];
 }
 
+template <int NW>
 __device__ __forceinline__ void ws_stage_q8(const WsRegsQ8& r, uint4* alds, uint16_t* slds, uint4* blds, int tid) {
     const int lane = tid & 63;
     __builtin_amdgcn_wave_barrier();
@@ -359,7 +364,7 @@ __device__ __forceinline__ void ws_stage_q8(const WsRegsQ8& r, uint4* alds, uint
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) blds[tid + 256 * j] = r.b[j];
+    for (int j = 0; j < 16 / NW; ++j) blds[tid + 64 * NW * j] = r.b[j];
 }
 
 __device__ __forceinline__ void ws_compute_q8(const uint4* alds, const uint16_t* slds, const uint4* blds, f32x4_t& acc,
@@ -382,28 +387,28 @@ __device__ __forceinline__ void ws_compute_q8(const uint4* alds, const uint16_t*
 }
 
 // K % 512 == 0 (an even number of chunks), V % 16 == 0 (a tail work-group's extra waves redo the last tile).
-template <int WT>
-__global__ __launch_bounds__(256) void lm_argmax_ws_kernel(LmArgs a) {
+template <int WT, int NW>
+__global__ __launch_bounds__(NW * 64) void lm_argmax_ws_kernel(LmArgs a) {
     constexpr int APITCH = WT == 0 ? RS_PITCH : Q8_PITCH;
-    __shared__ uint4 alds_all[4][16 * APITCH];
-    __shared__ uint16_t slds_all[4][8 * 16];
+    __shared__ uint4 alds_all[NW][16 * APITCH];
+    __shared__ uint16_t slds_all[NW][8 * 16];
     __shared__ uint4 blds_all[2][1024];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4;
-    const int v0 = min((blockIdx.x * 4 + wave) * 16, a.V - 16);   // tail waves redo the last tile (discarded)
-    const bool own = (blockIdx.x * 4 + wave) * 16 < a.V;
+    const int v0 = min((blockIdx.x * NW + wave) * 16, a.V - 16);   // tail waves redo the last tile (discarded)
+    const bool own = (blockIdx.x * NW + wave) * 16 < a.V;
     uint4* alds = alds_all[wave];
     uint16_t* slds = slds_all[wave];
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int nch = a.K >> 8;
     using Regs = typename std::conditional<WT == 0, WsRegs, WsRegsQ8>::type;
     auto load = [&](Regs& r, int ch) {
-        if constexpr (WT == 0) ws_load(r, a, v0, ch, tid);
-        else ws_load_q8(r, a, v0, ch, tid);
+        if constexpr (WT == 0) ws_load<NW>(r, a, v0, ch, tid);
+        else ws_load_q8<NW>(r, a, v0, ch, tid);
     };
     auto stage = [&](const Regs& r, int buf) {
-        if constexpr (WT == 0) ws_stage(r, alds, blds_all[buf], tid);
-        else ws_stage_q8(r, alds, slds, blds_all[buf], tid);
+        if constexpr (WT == 0) ws_stage<NW>(r, alds, blds_all[buf], tid);
+        else ws_stage_q8<NW>(r, alds, slds, blds_all[buf], tid);
     };
     auto compute = [&](int buf) {
         if constexpr (WT == 0) ws_compute(alds, blds_all[buf], acc, lane);
@@ -449,15 +454,15 @@ __global__ __launch_bounds__(256) void lm_argmax_ws_kernel(LmArgs a) {
         const int oi = __shfl_xor(bidx, o, 64);
         if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
     }
-    __shared__ float wb[4][16];
-    __shared__ int wi[4][16];
+    __shared__ float wb[NW][16];
+    __shared__ int wi[NW][16];
     if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
     __syncthreads();
     if (tid < 16 && tid < a.T) {
         float b = wb[0][tid];
         int bi = wi[0][tid];
 #pragma unroll
-        for (int w = 1; w < 4; ++w)
+        for (int w = 1; w < NW; ++w)
             if (wb[w][tid] > b || (wb[w][tid] == b && wi[w][tid] < bi)) { b = wb[w][tid]; bi = wi[w][tid]; }
         if (bi != 0x7fffffff) {
             const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
@@ -480,8 +485,8 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
     if (a.T > 16) return hipErrorInvalidValue;
     if (a.perm == 0 && a.K % 512 == 0) {
-        if (wtype == 0) lm_argmax_ws_kernel<0><<<(a.V + 63) / 64, 256, 0, st>>>(a);
-        else lm_argmax_ws_kernel<1><<<(a.V + 63) / 64, 256, 0, st>>>(a);
+        if (wtype == 0) lm_argmax_ws_kernel<0, 4><<<(a.V + 63) / 64, 256, 0, st>>>(a);
+        else lm_argmax_ws_kernel<1, 8><<<(a.V + 127) / 128, 512, 0, st>>>(a);
     } else if (wtype == 0 && a.perm == 0 && a.K % 256 == 0) {
         lm_argmax_rs_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
     } else {

@@ -194,7 +194,8 @@ __device__ __forceinline__ void rs_load_q8(RsStageQ8<NT>& st, const SkinnyGroup&
         const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + (lane >> 4)) * K + s * 32 + (lane & 15) * 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.a[n][i] = ldg_nt((const uint4*)(C + (size_t)(4 * i) * K));
-        st.sc[n] = ldg_nt((const uint4*)((const uint16_t*)(n == 0 ? G.Wd : G.W2d) + (size_t)(m0 + (lane & 15)) * nb + s));
+        // scales with an ordinary load: a 128-byte line of them serves 8 chunks and must stay in L2 meanwhile
+        st.sc[n] = *(const uint4*)((const uint16_t*)(n == 0 ? G.Wd : G.W2d) + (size_t)(m0 + (lane & 15)) * nb + s);
     }
 }
 
