@@ -132,9 +132,10 @@ hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st);
 struct AttnArgs {
     QPrep qp;
     int nq;                // query rows (<= 16)
-    const void* kc;        // cache keys / values: row j at kc + j*kv_ld (element type by kv_dtype)
-    const void* vc;
+    const void* kc;        // cache keys: row j at kc + j*kv_ld (element type by kv_dtype)
+    const void* vc;        // cache values: f32 rows like the keys; f16 transposed, dim d at vc + d*vt_ld
     int kv_ld;
+    int vt_ld;
     int kv_dtype;          // 0 f16, 1 f32
     int key_lo, key_hi;    // cache rows [key_lo, key_hi)
     const float* kx;       // extra keys / values (f32 rows [nx][x_ld]) after the cache rows
@@ -143,8 +144,9 @@ struct AttnArgs {
     int heads, kv_heads, hd;
     int causal_base;       // >= 0: query t sees cache row j only if j <= causal_base + t
     float scale;
-    int chunk;             // keys per work-group: attn_chunk_size(hd, kv_dtype)
-    int nchunks;
+    int chunk;             // keys per chunk: attn_chunk_size(hd, kv_dtype, keys, heads)
+    int cpw;               // chunks per work-group (f16-cache kernel; the others take 1)
+    int nchunks;           // work-groups per head = partials per head
     float* part;           // [heads][nchunks][nq][hd + 2]: unnormalised o, running max, sum
 };
 // Keys per work-group of the split kernel for a head width, cache type, key count and head count (the host sizes
@@ -172,7 +174,7 @@ struct KVFinalArgs {
     const float* rope_tab;
     int rope_dims;
     int start;
-    void* cache;           // layer l: K at l*2*max_ctx*D, V at (2l+1)*max_ctx*D (elements)
+    void* cache;           // layer l: K at l*2*max_ctx*D, V at (2l+1)*max_ctx*D (elements; f16 V transposed)
     int max_ctx;
     int kv_dtype;
     const float* zeros;    // zero row (absent norm weights / RoPE read it)
@@ -213,7 +215,8 @@ hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
 enum PrefillEpi {
     PF_F32 = 0,     // C f32 [rows][ld]
     PF_CACHE_K = 1, // head RMSNorm + RoPE at position start + r, stored to the cache (f16/f32)
-    PF_CACHE_V = 2  // stored to the cache
+    PF_CACHE_V = 2, // stored to the cache
+    PF_CACHE_VT = 3 // stored transposed: out[n * vt_ld + start + r] (f16 V cache)
 };
 struct PrefillGroup {
     const void* A;         // this group's A rows (null: PrefillArgs.A)
@@ -236,6 +239,7 @@ struct PrefillArgs {
     int rope_dims;
     int start;
     int kv_dtype;
+    int vt_ld;             // PF_CACHE_VT: positions per transposed row (the cache's max_ctx)
     int m_tiles, n_tiles;
 };
 // Tile edge (128 or 256) the launcher uses for rows x N x ngroups; the host sizes m_tiles, n_tiles and the

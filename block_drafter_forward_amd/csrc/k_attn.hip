@@ -23,6 +23,9 @@ namespace {
 
 constexpr int MAX_QSLABS = 4;   // split-K slabs of q (and of the self-attention's k, v) summed in the prologue
 
+// native 4 x u32 vector: arrays of it stay in registers where arrays of the HIP uint4 class may not
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
     return dt == 0 ? f16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
@@ -362,56 +365,83 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 }
 
 // ── split-L attention on the matrix cores (f16 cache) ────────────────────────────────────────────
-// One work-group = one head x one chunk of C keys, 4 waves, three LDS exchanges:
-//   prep    every global load first (the chunk's K and V rows, the queries, norm weight, RoPE rows); thread
-//           (query t, segment) holds hd/16 consecutive query values, so the head-RMSNorm is a 16-lane shuffle
-//           reduction and the interleaved RoPE pairs stay in the thread; queries leave split q = hi + lo in f16;
-//   scores  Sᵀ[j][t] = sum_d K[j][d] q[t][d] on v_mfma_f32_16x16x32_f16: A = K rows straight from LDS (exact f16),
-//           B = the query hi and lo halves (two MFMAs, ~22 significant bits);
-//   softmax 16 threads per query row over the chunk (max, exp, sum by shuffles) in f32;
-//   P.V     O[t][d] = sum_j P[t][j] V[j][d]: A = P split hi/lo in f16, B = V read from a transposed LDS copy
-//           (dim-major) so each lane's 8 keys are one 16-byte read.
-// C is 64 or 32 keys (hd 128) so that short contexts still spread over enough work-groups.
+// One work-group = one head x a run of cpw chunks of C keys, 4 waves; the queries are built once, then per chunk:
+//   stage   the chunk's K (row-major) and V (transposed, dim-major) into LDS while the next chunk's loads fly;
+//   scores  Sᵀ[j][t] = sum_d K[j][d] q[t][d] on v_mfma_f32_16x16x32_f16: A = K rows (exact f16), B = the query hi
+//           and lo halves (two MFMAs, ~22 significant bits);
+//   softmax 16 threads per query row keep its running max and sum (online softmax across the run) and publish
+//           the rescale factor of the chunk;
+//   P.V     O[t][d] += P[t][j] V[j][d] with P split hi/lo, after rescaling O; V's transposed copy gives each lane
+//           its 8 keys in one 16-byte read.
+// The queries are built in registers: thread (query t, segment) holds hd/16 consecutive values (the sum of up to
+// 4 split-K slabs), head-RMSNorm by a 16-lane shuffle reduction, interleaved RoPE pairs in the thread, f16 hi/lo.
+// C is 64 or 32 keys (hd 128) so that short contexts still spread over enough work-groups; long contexts give
+// each work-group several chunks (fewer partials to merge, loads overlapped with the previous chunk's math).
 template <int HD, int C>
 __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
     constexpr int KROW = HD + 8;               // LDS row pitches (halfs), 16-byte pad
-    constexpr int VROW = C + 8;
     constexpr int PROW = C + 8;
     constexpr int QROW = HD + 8;
     constexpr int V16 = HD * 2 / 16;           // 16-byte pieces per key row
     constexpr int LD16 = C * V16 / 256;
     constexpr int QS = HD / 16;                // query values per thread
     constexpr int CPT = C / 16;                // scores per thread in the softmax
-    static_assert(LD16 >= 1 && C % 32 == 0, "chunk shape");
-    const int c = blockIdx.x, h = blockIdx.y;
+    constexpr int NDT = HD / 64;               // dim tiles per wave in P.V
+    constexpr int NVS = C / 32;                // 32-key steps per chunk in P.V
+    static_assert(LD16 >= 1 && C % 32 == 0 && NDT >= 1, "chunk shape");
+    const int wg = blockIdx.x, h = blockIdx.y;
     const int nq = a.nq;
     const int kh = h / (a.heads / a.kv_heads);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const QPrep& qp = a.qp;
     __shared__ __attribute__((aligned(16))) _Float16 Ks[C * KROW];
-    __shared__ __attribute__((aligned(16))) _Float16 Vt[HD * VROW];
     __shared__ __attribute__((aligned(16))) _Float16 Qh[16 * QROW], Ql[16 * QROW];
     __shared__ __attribute__((aligned(16))) _Float16 Ph[16 * PROW], Pl[16 * PROW];
     __shared__ float S[16][C + 1];
+    __shared__ float alpha_s[16];
 
     const int ncache = a.key_hi - a.key_lo;
-    const int k0 = c * C;
-    const int cnt = min(C, ncache - k0);
+    const int c_first = wg * a.cpw;
+    const int c_last = min(c_first + a.cpw, (ncache + C - 1) / C) - 1;
 
-    // 1. every global load up front
-    uint4 kr[LD16], vr[LD16];
+    // K rows (row-major, through LDS) and this wave's V operands: the cache holds V dimension-major, so the 8 keys a
+    // lane needs for one dimension are 16 contiguous bytes. Keys past the end read a valid address; their values
+    // are zeroed (their probabilities are zero too, but the cache there may hold anything).
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    u32x4_t kr[LD16], vb[NDT][NVS];
+    auto load_kv = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < LD16; ++j) {
-        const int u = tid + 256 * j;
-        const int row = u / V16, p16 = u % V16;
-        const int kidx = min(k0 + row, ncache - 1);
-        const size_t off = (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD;
-        kr[j] = *((const uint4*)((const uint16_t*)a.kc + off) + p16);
-        vr[j] = *((const uint4*)((const uint16_t*)a.vc + off) + p16);
-    }
+        for (int j = 0; j < LD16; ++j) {
+            const int u = tid + 256 * j;
+            const int row = u / V16, p16 = u % V16;
+            const int kidx = min(c * C + row, ncache - 1);
+            const size_t off = (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD;
+            kr[j] = *((const u32x4_t*)((const uint16_t*)a.kc + off) + p16);
+        }
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+            for (int s = 0; s < NVS; ++s) {
+                const int g0 = c * C + s * 32 + fk;   // first of the lane's 8 keys
+                const size_t d = (size_t)kh * HD + (wave + 4 * n) * 16 + fr;
+                u32x4_t v = *(const u32x4_t*)((const uint16_t*)a.vc + d * a.vt_ld + a.key_lo + (g0 < ncache ? g0 : 0));
+                if (g0 + 8 > ncache) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = g0 + 2 * e < ncache ? 0xffffu : 0u;
+                        const uint32_t hi = g0 + 2 * e + 1 < ncache ? 0xffff0000u : 0u;
+                        v[e] &= lo | hi;
+                    }
+                }
+                vb[n][s] = v;
+            }
+    };
+    load_kv(c_first);
+
+    // queries (once per work-group)
     const int qt = tid >> 4, qseg = tid & 15, tq = min(qt, nq - 1);
-    float q[QS], nw[QS], cs[QS / 2], sn[QS / 2];
     {
+        float q[QS], nw[QS], cs[QS / 2], sn[QS / 2];
         const float* src = qp.q + (size_t)tq * qp.q_ld + (size_t)h * qp.q_hs + qseg * QS;
         const int parts = qp.parts > 1 ? qp.parts : 1;
 #pragma unroll
@@ -433,112 +463,138 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
         const float* nf = qp.norm_f32 ? qp.norm_f32 + qseg * QS : qp.zeros;
 #pragma unroll
         for (int j = 0; j < QS; ++j) nw[j] = qp.norm_bf16 ? bf16_to_f32(nb[j]) : nf[j];
-    }
-    // 2. query head-norm + RoPE in registers, hi/lo split; K row-major and V transposed into LDS
-    if (qp.norm_bf16 || qp.norm_f32) {
-        float ss = 0.f;
+        if (qp.norm_bf16 || qp.norm_f32) {
+            float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < QS; ++j) ss += q[j] * q[j];
+            for (int j = 0; j < QS; ++j) ss += q[j] * q[j];
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
-        const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
+            for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
+            const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
 #pragma unroll
-        for (int j = 0; j < QS; ++j) q[j] *= nw[j] * r;
-    }
-    if (qp.rope) {
-#pragma unroll
-        for (int j = 0; j < QS / 2; ++j) {
-            const float x0 = q[2 * j], x1 = q[2 * j + 1];
-            q[2 * j] = x0 * cs[j] - x1 * sn[j];
-            q[2 * j + 1] = x1 * cs[j] + x0 * sn[j];
+            for (int j = 0; j < QS; ++j) q[j] *= nw[j] * r;
         }
-    }
+        if (qp.rope) {
 #pragma unroll
-    for (int j = 0; j < QS; ++j) {
-        const float x = qt < nq ? q[j] : 0.f;
-        const _Float16 hi = (_Float16)x;
-        Qh[qt * QROW + qseg * QS + j] = hi;
-        Ql[qt * QROW + qseg * QS + j] = (_Float16)(x - (float)hi);
-    }
-#pragma unroll
-    for (int j = 0; j < LD16; ++j) {
-        const int u = tid + 256 * j;
-        const int row = u / V16, p16 = u % V16;
-        *(uint4*)(Ks + row * KROW + p16 * 8) = kr[j];
-        const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            Vt[(p16 * 8 + 2 * e) * VROW + row] = __builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xffffu));
-            Vt[(p16 * 8 + 2 * e + 1) * VROW + row] = __builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
-        }
-    }
-    __syncthreads();
-    // 3. scores: wave w owns key tiles w, w+4, ...
-    const int fr = lane & 15, fk = 8 * (lane >> 4);
-    for (int kt = wave; kt < C / 16; kt += 4) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < HD / 32; ++s) {
-            const f16x8_t A = *(const f16x8_t*)(Ks + (kt * 16 + fr) * KROW + s * 32 + fk);
-            const f16x8_t Bh = *(const f16x8_t*)(Qh + fr * QROW + s * 32 + fk);
-            const f16x8_t Bl = *(const f16x8_t*)(Ql + fr * QROW + s * 32 + fk);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
-        }
-        // lane holds keys j = 16 kt + 4 (lane / 16) + i for query t = lane % 16
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = kt * 16 + 4 * (lane >> 4) + i;
-            float v = acc[i] * a.scale;
-            if (j >= cnt) v = -INFINITY;
-            if (a.causal_base >= 0 && a.key_lo + k0 + j > a.causal_base + fr) v = -INFINITY;
-            S[fr][j] = v;
-        }
-    }
-    __syncthreads();
-    // 4. softmax statistics: 16 threads per query row, CPT keys each; P = exp(S - m) split hi/lo in f16
-    float* out = a.part + ((size_t)h * a.nchunks + c) * nq * (HD + 2);
-    {
-        float sv[CPT];
-        float m = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) { sv[i] = S[qt][qseg + 16 * i]; m = fmaxf(m, sv[i]); }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        float l = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const float p = (m == -INFINITY || qt >= nq) ? 0.f : expf(sv[i] - m);
-            const _Float16 hi = (_Float16)p;
-            Ph[qt * PROW + qseg + 16 * i] = hi;
-            Pl[qt * PROW + qseg + 16 * i] = (_Float16)(p - (float)hi);
-            l += p;
+            for (int j = 0; j < QS / 2; ++j) {
+                const float x0 = q[2 * j], x1 = q[2 * j + 1];
+                q[2 * j] = x0 * cs[j] - x1 * sn[j];
+                q[2 * j + 1] = x1 * cs[j] + x0 * sn[j];
+            }
         }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
-        if (qseg == 0 && qt < nq) {
-            out[(size_t)qt * (HD + 2) + HD] = m;
-            out[(size_t)qt * (HD + 2) + HD + 1] = l;
+        for (int j = 0; j < QS; ++j) {
+            const float x = qt < nq ? q[j] : 0.f;
+            const _Float16 hi = (_Float16)x;
+            Qh[qt * QROW + qseg * QS + j] = hi;
+            Ql[qt * QROW + qseg * QS + j] = (_Float16)(x - (float)hi);
         }
     }
-    __syncthreads();
-    // 5. O = P V: wave w owns dim tiles w, w+4, ...
-    for (int dt = wave; dt < HD / 16; dt += 4) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    float m_run = -INFINITY, l_run = 0.f;   // of query row qt (replicated over its 16 threads)
+    f32x4_t o[NDT];
 #pragma unroll
-        for (int s = 0; s < C / 32; ++s) {
-            const f16x8_t Ah = *(const f16x8_t*)(Ph + fr * PROW + s * 32 + fk);
-            const f16x8_t Al = *(const f16x8_t*)(Pl + fr * PROW + s * 32 + fk);
-            const f16x8_t B = *(const f16x8_t*)(Vt + (dt * 16 + fr) * VROW + s * 32 + fk);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, acc, 0, 0, 0);
+    for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = c_first; c <= c_last; ++c) {
+        const int k0 = c * C;
+        const int cnt = min(C, ncache - k0);
+        // stage K row-major and V transposed, then put the next chunk's loads in flight (the run's last chunk
+        // re-reads itself: no conditional load)
+#pragma unroll
+        for (int j = 0; j < LD16; ++j) {
+            const int u = tid + 256 * j;
+            const int row = u / V16, p16 = u % V16;
+            *(u32x4_t*)(Ks + row * KROW + p16 * 8) = kr[j];
         }
-        // lane holds O[t = 4 (lane / 16) + i][d = 16 dt + lane % 16]
+        u32x4_t vcur[NDT][NVS];
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+            for (int s = 0; s < NVS; ++s) vcur[n][s] = vb[n][s];
+        load_kv(min(c + 1, c_last));
+        __syncthreads();
+        // scores: wave w owns key tiles w, w+4, ...
+        for (int kt = wave; kt < C / 16; kt += 4) {
+            f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < HD / 32; ++s) {
+                const f16x8_t A = *(const f16x8_t*)(Ks + (kt * 16 + fr) * KROW + s * 32 + fk);
+                const f16x8_t Bh = *(const f16x8_t*)(Qh + fr * QROW + s * 32 + fk);
+                const f16x8_t Bl = *(const f16x8_t*)(Ql + fr * QROW + s * 32 + fk);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+            }
+            // lane holds keys j = 16 kt + 4 (lane / 16) + i for query t = lane % 16
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = kt * 16 + 4 * (lane >> 4) + i;
+                float v = acc[i] * a.scale;
+                if (j >= cnt) v = -INFINITY;
+                if (a.causal_base >= 0 && a.key_lo + k0 + j > a.causal_base + fr) v = -INFINITY;
+                S[fr][j] = v;
+            }
+        }
+        __syncthreads();
+        // online softmax: 16 threads per query row, CPT keys each
+        {
+            float sv[CPT];
+            float cm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) { sv[i] = S[qt][qseg + 16 * i]; cm = fmaxf(cm, sv[i]); }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 64));
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
+            float l = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const float p = (m_new == -INFINITY || qt >= nq) ? 0.f : expf(sv[i] - m_new);
+                const _Float16 hi = (_Float16)p;
+                Ph[qt * PROW + qseg + 16 * i] = hi;
+                Pl[qt * PROW + qseg + 16 * i] = (_Float16)(p - (float)hi);
+                l += p;
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off, 64);
+            l_run = l_run * alpha + l;
+            m_run = m_new;
+            if (qseg == 0) alpha_s[qt] = alpha;
+        }
+        __syncthreads();
+        // O = alpha O + P V: wave w owns dim tiles w, w+4, ...
+        {
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = alpha_s[4 * (lane >> 4) + i];
+#pragma unroll
+            for (int n = 0; n < NDT; ++n) {
+        #pragma unroll
+                for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
+#pragma unroll
+                for (int s = 0; s < NVS; ++s) {
+                    const f16x8_t Ah = *(const f16x8_t*)(Ph + fr * PROW + s * 32 + fk);
+                    const f16x8_t Al = *(const f16x8_t*)(Pl + fr * PROW + s * 32 + fk);
+                    const f16x8_t B = __builtin_bit_cast(f16x8_t, vcur[n][s]);
+                    o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, o[n], 0, 0, 0);
+                    o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, o[n], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();   // the next chunk overwrites K, V, S and P
+    }
+    // the run's partial: unnormalised o, running max, running sum
+    float* out = a.part + ((size_t)h * a.nchunks + wg) * nq * (HD + 2);
+#pragma unroll
+    for (int n = 0; n < NDT; ++n) {
+        const int dt = wave + 4 * n;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * (lane >> 4) + i;
-            if (t < nq) out[(size_t)t * (HD + 2) + dt * 16 + fr] = acc[i];
+            if (t < nq) out[(size_t)t * (HD + 2) + dt * 16 + fr] = o[n][i];
         }
+    }
+    if (qseg == 0 && qt < nq) {
+        out[(size_t)qt * (HD + 2) + HD] = m_run;
+        out[(size_t)qt * (HD + 2) + HD + 1] = l_run;
     }
 }
 
@@ -819,7 +875,10 @@ __global__ __launch_bounds__(256) void kv_final_kernel(KVFinalArgs a) {
                 vw[e] = (uint32_t)f32_to_f16(v[2 * e]) | ((uint32_t)f32_to_f16(v[2 * e + 1]) << 16);
             }
             *(uint4*)((uint16_t*)a.cache + kbase + i0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-            *(uint4*)((uint16_t*)a.cache + vbase + i0) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+            // f16 V is dimension-major: dim i0 + e of position start + t
+            uint16_t* vt = (uint16_t*)a.cache + (size_t)(2 * l + 1) * a.max_ctx * D + (size_t)i0 * a.max_ctx + a.start + t;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[(size_t)e * a.max_ctx] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
         } else {
             float* kc = (float*)a.cache + kbase + i0;
             float* vc = (float*)a.cache + vbase + i0;
@@ -893,8 +952,10 @@ int attn_chunk_size(int hd, int kv_dtype, int nkeys, int heads) {
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
     const int nkeys = a.key_hi - a.key_lo + a.nx;
     if (a.nq < 1 || a.nq > 16 || a.chunk != attn_chunk_size(a.hd, a.kv_dtype, nkeys, a.heads) || !a.qp.zeros ||
-        !a.qp.q)
+        !a.qp.q || nkeys < 1)
         return hipErrorInvalidValue;
+    const int tc = (nkeys + a.chunk - 1) / a.chunk;
+    if (a.cpw < 1 || (a.kv_dtype != 0 && a.cpw != 1) || a.nchunks != (tc + a.cpw - 1) / a.cpw) return hipErrorInvalidValue;
     if (a.qp.rope && a.qp.rope_dims > (a.hd <= 128 ? a.hd : 128)) return hipErrorInvalidValue;
     if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
     if (a.qp.parts > MAX_QSLABS || (a.kv_dtype != 0 && a.qp.parts > 1)) return hipErrorInvalidValue;

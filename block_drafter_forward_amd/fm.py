@@ -190,5 +190,7 @@ class Drafter:
             t = self.kv.view(torch.float32).view(2, c["max_ctx"], w)
             return t[which]
         dt = torch.float16 if c["kv_dtype"] == "f16" else torch.float32
-        t = self.kv.view(dt).view(c["layers"], 2, c["max_ctx"], c["dim"])
-        return t[l, which]
+        t = self.kv.view(dt).view(c["layers"], 2, c["max_ctx"] * c["dim"])[l, which]
+        if c["kv_dtype"] == "f16" and which == 1:   # the f16 V cache is dimension-major: present it [pos][dim]
+            return t.view(c["dim"], c["max_ctx"]).t()
+        return t.view(c["max_ctx"], c["dim"])

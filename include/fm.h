@@ -91,8 +91,11 @@ typedef struct fm_config {
 typedef struct fm_drafter fm_drafter;
 
 /* Bytes of the K/V cache the caller allocates for `cfg` (0 if cfg is invalid).
- * Flow-map / KV-inject layout: for layer l, K rows at byte offset 2*l*max_ctx*dim*es and V rows right after
- * (es = 2 for F16, 4 for F32), each [max_ctx][dim]. MTP layout: K [max_ctx][kv_heads*head_dim] f32, then V. */
+ * Flow-map / KV-inject layout: for layer l, K at byte offset 2*l*max_ctx*dim*es and V right after (es = 2 for F16,
+ * 4 for F32), each max_ctx*dim elements. K is [max_ctx][dim] (position-major). V is [max_ctx][dim] in an F32 cache
+ * and [dim][max_ctx] (dimension-major, transposed) in an F16 cache, so that attention reads each dimension's run
+ * of consecutive positions as the matrix-core operand directly; an F16 cache needs max_ctx % 8 == 0.
+ * MTP layout: K [max_ctx][kv_heads*head_dim] f32, then V likewise. */
 size_t fm_kv_bytes(const fm_config* cfg);
 
 /* Bytes of the device workspace the caller allocates for `cfg` (0 if cfg is invalid): activations, split-K
