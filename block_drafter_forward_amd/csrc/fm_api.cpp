@@ -176,7 +176,7 @@ fm_status validate_config(const fm_config* c) {
             c->kv_dtype != FM_KV_F16 || c->head_dim > 128)
             return fail(FM_E_UNSUPPORTED, "flow-map needs interleaved RoPE, exact GELU, bf16, f16 cache, hd <= 128");
         if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
-        if (c->max_ctx % 8) return fail(FM_E_INVALID, "an f16 cache needs max_ctx %% 8 == 0 (V is dimension-major)");
+        if (c->max_ctx % 32) return fail(FM_E_INVALID, "an f16 cache needs max_ctx %% 32 == 0 (V is tiled by 32)");
         break;
     case FM_VARIANT_KVINJECT:
         if (c->rope != FM_ROPE_NONE || c->mlp != FM_MLP_GEGLU_TANH || c->wtype != FM_W_BF16 ||
@@ -353,7 +353,7 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
         a.kc = d->kv_layer(layer_kv, 0);
         a.vc = d->kv_layer(layer_kv, 1);
         a.kv_ld = c.dim;
-        a.vt_ld = c.max_ctx;   // f16 V is dimension-major
+        a.vt_ld = c.dim;   // f16 V is tiled [pos / 32][dim][32]
     }
     a.key_lo = key_lo;
     a.key_hi = key_hi;
@@ -369,9 +369,14 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
     const int ntot = key_hi - key_lo + nx;
     a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype, ntot, c.heads);
     const int tc = (ntot + a.chunk - 1) / a.chunk;
-    // f16 caches: long contexts give each work-group a run of chunks, keeping ~2 work-groups per CU
-    a.cpw = c.kv_dtype == FM_KV_F16 ? std::max(1, tc * c.heads / (2 * TARGET_WGS)) : 1;
-    a.nchunks = (tc + a.cpw - 1) / a.cpw;
+    if (c.kv_dtype == FM_KV_F16) {
+        // one run of 32-key steps per wave; long contexts lengthen the runs to keep ~4 waves per CU
+        a.cpw = std::max(1, tc * c.heads / (4 * TARGET_WGS));
+        a.nchunks = ((tc + a.cpw - 1) / a.cpw + 3) / 4 * 4;
+    } else {
+        a.cpw = 1;
+        a.nchunks = tc;
+    }
     if ((size_t)c.heads * a.nchunks * TMAX * (c.head_dim + 2) * 4 > d->p.attnp_bytes)
         return fail(FM_E_INVALID, "attention partial buffer too small");
     a.part = d->at<float>(d->p.attnp);
@@ -501,7 +506,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         a.rope_dims = d->p.rope_dims;
         a.start = start;
         a.kv_dtype = c.kv_dtype;
-        a.vt_ld = c.max_ctx;
+        a.vt_ld = D;
         a.m_tiles = mt;
         a.n_tiles = D / tile;
         HIPCHK(launch_prefill(a, 2 * nl * per, st));

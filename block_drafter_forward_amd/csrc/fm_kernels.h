@@ -133,7 +133,7 @@ struct AttnArgs {
     QPrep qp;
     int nq;                // query rows (<= 16)
     const void* kc;        // cache keys: row j at kc + j*kv_ld (element type by kv_dtype)
-    const void* vc;        // cache values: f32 rows like the keys; f16 transposed, dim d at vc + d*vt_ld
+    const void* vc;        // cache values: f32 rows like the keys; f16 tiled [pos/32][vt_ld dims][32]
     int kv_ld;
     int vt_ld;
     int kv_dtype;          // 0 f16, 1 f32
@@ -174,7 +174,7 @@ struct KVFinalArgs {
     const float* rope_tab;
     int rope_dims;
     int start;
-    void* cache;           // layer l: K at l*2*max_ctx*D, V at (2l+1)*max_ctx*D (elements; f16 V transposed)
+    void* cache;           // layer l: K at l*2*max_ctx*D, V at (2l+1)*max_ctx*D (elements; f16 V tiled by 32)
     int max_ctx;
     int kv_dtype;
     const float* zeros;    // zero row (absent norm weights / RoPE read it)
@@ -216,7 +216,7 @@ enum PrefillEpi {
     PF_F32 = 0,     // C f32 [rows][ld]
     PF_CACHE_K = 1, // head RMSNorm + RoPE at position start + r, stored to the cache (f16/f32)
     PF_CACHE_V = 2, // stored to the cache
-    PF_CACHE_VT = 3 // stored transposed: out[n * vt_ld + start + r] (f16 V cache)
+    PF_CACHE_VT = 3 // f16 V cache, tiled: position p, dim n at out[((p / 32) * vt_ld + n) * 32 + p % 32]
 };
 struct PrefillGroup {
     const void* A;         // this group's A rows (null: PrefillArgs.A)
@@ -239,7 +239,7 @@ struct PrefillArgs {
     int rope_dims;
     int start;
     int kv_dtype;
-    int vt_ld;             // PF_CACHE_VT: positions per transposed row (the cache's max_ctx)
+    int vt_ld;             // PF_CACHE_VT: dims per 32-position tile (the cache row width)
     int m_tiles, n_tiles;
 };
 // Tile edge (128 or 256) the launcher uses for rows x N x ngroups; the host sizes m_tiles, n_tiles and the

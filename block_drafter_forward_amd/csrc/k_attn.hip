@@ -364,94 +364,82 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     }
 }
 
-// ── split-L attention on the matrix cores (f16 cache) ────────────────────────────────────────────
-// One work-group = one head x a run of cpw chunks of C keys, 4 waves; the queries are built once, then per chunk:
-//   stage   the chunk's K (row-major) and V (transposed, dim-major) into LDS while the next chunk's loads fly;
-//   scores  Sᵀ[j][t] = sum_d K[j][d] q[t][d] on v_mfma_f32_16x16x32_f16: A = K rows (exact f16), B = the query hi
-//           and lo halves (two MFMAs, ~22 significant bits);
-//   softmax 16 threads per query row keep its running max and sum (online softmax across the run) and publish
-//           the rescale factor of the chunk;
-//   P.V     O[t][d] += P[t][j] V[j][d] with P split hi/lo, after rescaling O; V's transposed copy gives each lane
-//           its 8 keys in one 16-byte read.
-// The queries are built in registers: thread (query t, segment) holds hd/16 consecutive values (the sum of up to
-// 4 split-K slabs), head-RMSNorm by a 16-lane shuffle reduction, interleaved RoPE pairs in the thread, f16 hi/lo.
-// C is 64 or 32 keys (hd 128) so that short contexts still spread over enough work-groups; long contexts give
-// each work-group several chunks (fewer partials to merge, loads overlapped with the previous chunk's math).
-template <int HD, int C>
-__global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
-    constexpr int KROW = HD + 8;               // LDS row pitches (halfs), 16-byte pad
-    constexpr int PROW = C + 8;
-    constexpr int QROW = HD + 8;
-    constexpr int V16 = HD * 2 / 16;           // 16-byte pieces per key row
-    constexpr int LD16 = C * V16 / 256;
-    constexpr int QS = HD / 16;                // query values per thread
-    constexpr int CPT = C / 16;                // scores per thread in the softmax
-    constexpr int NDT = HD / 64;               // dim tiles per wave in P.V
-    constexpr int NVS = C / 32;                // 32-key steps per chunk in P.V
-    static_assert(LD16 >= 1 && C % 32 == 0 && NDT >= 1, "chunk shape");
-    const int wg = blockIdx.x, h = blockIdx.y;
+// ── split-L attention on the matrix cores, one key run per wave (f16 cache, V tiled by 32 positions) ─
+// A work-group of 4 waves builds the head's queries once (thread (query t, segment) holds hd/16 consecutive values:
+// the sum of up to 4 split-K slabs, head-RMSNorm by a 16-lane shuffle, interleaved RoPE in the thread, f16 hi + lo
+// into LDS); after one barrier each wave works alone on its own run of 32-key steps, with no further barrier:
+//   loads   32 K rows and the head's block of the 32-position V tile (contiguous in the tiled cache) as whole 1 KB
+//           instructions, one step ahead, parked in the wave's LDS tiles (keys past the end zeroed);
+//   scores  Sᵀ[j][t] on v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = the queries' hi and lo halves (kept in
+//           registers for the whole run);
+//   softmax online over the run: lanes of one query reduce by shuffles; the score accumulator of lane (t, g) holds
+//           keys 4g..4g+3 and 16+4g..16+4g+3 of the step, exactly the 8 values the A operand of the 32-key P.V
+//           product needs in that key order, so P never leaves registers (hi + lo halves);
+//   P.V     B = V read from the wave's LDS tile in the same key order (two 8-byte reads per dimension tile).
+// Each wave writes its run's (o, max, sum) partial; runs past the end write an empty one (max = -inf).
+template <int HD>
+__global__ __launch_bounds__(256) void attn_wave_kernel(AttnArgs a) {
+    constexpr int QROW = HD + 8;                 // q LDS row (halfs)
+    constexpr int KP = HD / 8 + 1;               // uint4 per LDS K row (+1 pad)
+    constexpr int VP = 5;                        // uint4 per LDS V dimension row: 32 keys = 4, +1 pad
+    constexpr int NS = HD / 32;                  // score k-steps
+    constexpr int ND = HD / 16;                  // dimension tiles
+    constexpr int RPI = 512 / HD;                // K rows per 1 KB load instruction
+    constexpr int LPR = 64 / RPI;                // lanes per K row
+    constexpr int KLD = 32 / RPI;                // K load instructions per step
+    constexpr int VLD = HD / 16;                 // V load instructions per step (16 dimensions each)
+    constexpr int QS = HD / 16;
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
     const int nq = a.nq;
     const int kh = h / (a.heads / a.kv_heads);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const QPrep& qp = a.qp;
-    __shared__ __attribute__((aligned(16))) _Float16 Ks[C * KROW];
-    __shared__ __attribute__((aligned(16))) _Float16 Qh[16 * QROW], Ql[16 * QROW];
-    __shared__ __attribute__((aligned(16))) _Float16 Ph[16 * PROW], Pl[16 * PROW];
-    __shared__ float S[16][C + 1];
-    __shared__ float alpha_s[16];
+    __shared__ u32x4_t Klds_all[4][32 * KP];
+    __shared__ u32x4_t Vlds_all[4][HD * VP];
+    static_assert(2 * 16 * QROW * 2 <= (int)sizeof(Klds_all), "q rows alias the K tiles");
+    _Float16* Qh = (_Float16*)&Klds_all[0][0];   // the queries live in the K tiles until every wave holds them
+    _Float16* Ql = Qh + 16 * QROW;
+    u32x4_t* Klds = Klds_all[wave];
+    u32x4_t* Vlds = Vlds_all[wave];
 
     const int ncache = a.key_hi - a.key_lo;
-    const int c_first = wg * a.cpw;
-    const int c_last = min(c_first + a.cpw, (ncache + C - 1) / C) - 1;
+    const int nsteps = (ncache + 31) >> 5;
+    const int run = blockIdx.x * 4 + wave;
+    const int s_first = run * a.cpw;
+    const int s_end = min(s_first + a.cpw, nsteps);   // may be <= s_first: an empty run
 
-    // K rows (row-major, through LDS) and this wave's V operands: the cache holds V dimension-major, so the 8 keys a
-    // lane needs for one dimension are 16 contiguous bytes. Keys past the end read a valid address; their values
-    // are zeroed (their probabilities are zero too, but the cache there may hold anything).
-    const int fr = lane & 15, fk = 8 * (lane >> 4);
-    u32x4_t kr[LD16], vb[NDT][NVS];
-    auto load_kv = [&](int c) {
+    u32x4_t kr[KLD], vr[VLD];
+    auto load_step = [&](int st) {
+        const int k0 = st * 32;
 #pragma unroll
-        for (int j = 0; j < LD16; ++j) {
-            const int u = tid + 256 * j;
-            const int row = u / V16, p16 = u % V16;
-            const int kidx = min(c * C + row, ncache - 1);
-            const size_t off = (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD;
-            kr[j] = *((const u32x4_t*)((const uint16_t*)a.kc + off) + p16);
+        for (int i = 0; i < KLD; ++i) {
+            const int row = i * RPI + lane / LPR;
+            const int kidx = min(k0 + row, ncache - 1);
+            kr[i] = *((const u32x4_t*)((const uint16_t*)a.kc + (size_t)(a.key_lo + kidx) * a.kv_ld + (size_t)kh * HD) +
+                      lane % LPR);
         }
+        // V: the step's 32-position tile, this head's HD dimensions x 64 bytes, contiguous (16 dims per instruction)
+        const uint16_t* vt = (const uint16_t*)a.vc + ((size_t)((a.key_lo + k0) >> 5) * a.vt_ld + (size_t)kh * HD) * 32;
 #pragma unroll
-        for (int n = 0; n < NDT; ++n)
-#pragma unroll
-            for (int s = 0; s < NVS; ++s) {
-                const int g0 = c * C + s * 32 + fk;   // first of the lane's 8 keys
-                const size_t d = (size_t)kh * HD + (wave + 4 * n) * 16 + fr;
-                u32x4_t v = *(const u32x4_t*)((const uint16_t*)a.vc + d * a.vt_ld + a.key_lo + (g0 < ncache ? g0 : 0));
-                if (g0 + 8 > ncache) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = g0 + 2 * e < ncache ? 0xffffu : 0u;
-                        const uint32_t hi = g0 + 2 * e + 1 < ncache ? 0xffff0000u : 0u;
-                        v[e] &= lo | hi;
-                    }
-                }
-                vb[n][s] = v;
-            }
+        for (int i = 0; i < VLD; ++i) vr[i] = *((const u32x4_t*)(vt + (16 * i) * 32) + lane);
     };
-    load_kv(c_first);
+    load_step(min(s_first, nsteps - 1));
 
     // queries (once per work-group)
-    const int qt = tid >> 4, qseg = tid & 15, tq = min(qt, nq - 1);
     {
+        const int qt = tid >> 4, qseg = tid & 15, tq = min(qt, nq - 1);
         float q[QS], nw[QS], cs[QS / 2], sn[QS / 2];
         const float* src = qp.q + (size_t)tq * qp.q_ld + (size_t)h * qp.q_hs + qseg * QS;
         const int parts = qp.parts > 1 ? qp.parts : 1;
 #pragma unroll
         for (int j = 0; j < QS; ++j) q[j] = 0.f;
 #pragma unroll
-        for (int p = 0; p < MAX_QSLABS; ++p) {   // every slab load issued together; absent slabs re-read slab 0
-            const float m = p < parts ? 1.f : 0.f;
+        for (int pp = 0; pp < MAX_QSLABS; ++pp) {   // every slab load issued together; absent slabs re-read slab 0
+            const float m = pp < parts ? 1.f : 0.f;
 #pragma unroll
             for (int j = 0; j < QS / 4; ++j) {
-                const float4 f = ((const float4*)(src + (p < parts ? p : 0) * qp.pstride))[j];
+                const float4 f = ((const float4*)(src + (pp < parts ? pp : 0) * qp.pstride))[j];
                 q[4 * j] += m * f.x; q[4 * j + 1] += m * f.y; q[4 * j + 2] += m * f.z; q[4 * j + 3] += m * f.w;
             }
         }
@@ -469,9 +457,9 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
             for (int j = 0; j < QS; ++j) ss += q[j] * q[j];
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
-            const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
+            const float rr = 1.f / sqrtf(ss / (float)HD + qp.eps);
 #pragma unroll
-            for (int j = 0; j < QS; ++j) q[j] *= nw[j] * r;
+            for (int j = 0; j < QS; ++j) q[j] *= nw[j] * rr;
         }
         if (qp.rope) {
 #pragma unroll
@@ -489,112 +477,110 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
             Ql[qt * QROW + qseg * QS + j] = (_Float16)(x - (float)hi);
         }
     }
+    __syncthreads();
+    f16x8_t qh[NS], ql[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        qh[s] = *(const f16x8_t*)(Qh + r * QROW + 32 * s + 8 * g);
+        ql[s] = *(const f16x8_t*)(Ql + r * QROW + 32 * s + 8 * g);
+    }
+    __syncthreads();   // every wave holds its query operands: the K tiles are free
 
-    float m_run = -INFINITY, l_run = 0.f;   // of query row qt (replicated over its 16 threads)
-    f32x4_t o[NDT];
+    float m_run = -INFINITY, l_run = 0.f;   // of query t = r (replicated over g)
+    f32x4_t o[ND];
 #pragma unroll
-    for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int c = c_first; c <= c_last; ++c) {
-        const int k0 = c * C;
-        const int cnt = min(C, ncache - k0);
-        // stage K row-major and V transposed, then put the next chunk's loads in flight (the run's last chunk
-        // re-reads itself: no conditional load)
+    for (int i = 0; i < ND; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int st = s_first; st < s_end; ++st) {
+        const int k0 = st * 32;
+        // park this step's K rows and V dimension rows (keys past the end zeroed) in the wave's LDS tiles
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int j = 0; j < LD16; ++j) {
-            const int u = tid + 256 * j;
-            const int row = u / V16, p16 = u % V16;
-            *(u32x4_t*)(Ks + row * KROW + p16 * 8) = kr[j];
-        }
-        u32x4_t vcur[NDT][NVS];
+        for (int i = 0; i < KLD; ++i) Klds[(i * RPI + lane / LPR) * KP + lane % LPR] = kr[i];
+        {
+            const int p = k0 + (lane & 3) * 8;
+            u32x4_t msk = u32x4_t{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+            if (p + 8 > ncache) {
 #pragma unroll
-        for (int n = 0; n < NDT; ++n)
-#pragma unroll
-            for (int s = 0; s < NVS; ++s) vcur[n][s] = vb[n][s];
-        load_kv(min(c + 1, c_last));
-        __syncthreads();
-        // scores: wave w owns key tiles w, w+4, ...
-        for (int kt = wave; kt < C / 16; kt += 4) {
-            f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < HD / 32; ++s) {
-                const f16x8_t A = *(const f16x8_t*)(Ks + (kt * 16 + fr) * KROW + s * 32 + fk);
-                const f16x8_t Bh = *(const f16x8_t*)(Qh + fr * QROW + s * 32 + fk);
-                const f16x8_t Bl = *(const f16x8_t*)(Ql + fr * QROW + s * 32 + fk);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+                for (int e = 0; e < 4; ++e)
+                    msk[e] = (p + 2 * e < ncache ? 0xffffu : 0u) | (p + 2 * e + 1 < ncache ? 0xffff0000u : 0u);
             }
-            // lane holds keys j = 16 kt + 4 (lane / 16) + i for query t = lane % 16
+#pragma unroll
+            for (int i = 0; i < VLD; ++i) Vlds[(16 * i + (lane >> 2)) * VP + (lane & 3)] = vr[i] & msk;
+        }
+        __builtin_amdgcn_wave_barrier();
+        load_step(min(st + 1, s_end - 1));   // the run's last step re-reads itself: no conditional load
+        // scores of the step's two 16-key tiles
+        f32x4_t sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            sc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const f16x8_t A = __builtin_bit_cast(f16x8_t, Klds[(16 * kt + r) * KP + 4 * s + g]);
+                sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[s], sc[kt], 0, 0, 0);
+                sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[s], sc[kt], 0, 0, 0);
+            }
+        }
+        // online softmax of query r over the step's keys 16 kt + 4 g + i
+        float sv[2][4], cm = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = kt * 16 + 4 * (lane >> 4) + i;
-                float v = acc[i] * a.scale;
-                if (j >= cnt) v = -INFINITY;
-                if (a.causal_base >= 0 && a.key_lo + k0 + j > a.causal_base + fr) v = -INFINITY;
-                S[fr][j] = v;
+                const int kidx = k0 + 16 * kt + 4 * g + i;
+                float v = sc[kt][i] * a.scale;
+                if (kidx >= ncache) v = -INFINITY;
+                if (a.causal_base >= 0 && a.key_lo + kidx > a.causal_base + r) v = -INFINITY;
+                sv[kt][i] = v;
+                cm = fmaxf(cm, v);
             }
-        }
-        __syncthreads();
-        // online softmax: 16 threads per query row, CPT keys each
-        {
-            float sv[CPT];
-            float cm = -INFINITY;
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float m_new = fmaxf(m_run, cm);
+        const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
+        f16x8_t ph, pl;
+        float ls = 0.f;
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) { sv[i] = S[qt][qseg + 16 * i]; cm = fmaxf(cm, sv[i]); }
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 64));
-            const float m_new = fmaxf(m_run, cm);
-            const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
-            float l = 0.f;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const float p = (m_new == -INFINITY || qt >= nq) ? 0.f : expf(sv[i] - m_new);
-                const _Float16 hi = (_Float16)p;
-                Ph[qt * PROW + qseg + 16 * i] = hi;
-                Pl[qt * PROW + qseg + 16 * i] = (_Float16)(p - (float)hi);
-                l += p;
+            for (int i = 0; i < 4; ++i) {
+                const float pv = (m_new == -INFINITY) ? 0.f : expf(sv[kt][i] - m_new);
+                const _Float16 hi = (_Float16)pv;
+                ph[4 * kt + i] = hi;
+                pl[4 * kt + i] = (_Float16)(pv - (float)hi);
+                ls += pv;
             }
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+        float al[4];
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off, 64);
-            l_run = l_run * alpha + l;
-            m_run = m_new;
-            if (qseg == 0) alpha_s[qt] = alpha;
-        }
-        __syncthreads();
-        // O = alpha O + P V: wave w owns dim tiles w, w+4, ...
-        {
-            float al[4];
+        for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 4 * g + j, 64);
+        // O = alpha O + P V, V from the LDS tile in the same key order as P
 #pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = alpha_s[4 * (lane >> 4) + i];
+        for (int dt = 0; dt < ND; ++dt) {
+            const uint2* vrow = (const uint2*)(Vlds + (16 * dt + r) * VP);
+            const uint2 v0 = vrow[g], v1 = vrow[4 + g];
+            const f16x8_t B = __builtin_bit_cast(f16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
-            for (int n = 0; n < NDT; ++n) {
-        #pragma unroll
-                for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
-#pragma unroll
-                for (int s = 0; s < NVS; ++s) {
-                    const f16x8_t Ah = *(const f16x8_t*)(Ph + fr * PROW + s * 32 + fk);
-                    const f16x8_t Al = *(const f16x8_t*)(Pl + fr * PROW + s * 32 + fk);
-                    const f16x8_t B = __builtin_bit_cast(f16x8_t, vcur[n][s]);
-                    o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, o[n], 0, 0, 0);
-                    o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, o[n], 0, 0, 0);
-                }
-            }
-        }
-        __syncthreads();   // the next chunk overwrites K, V, S and P
-    }
-    // the run's partial: unnormalised o, running max, running sum
-    float* out = a.part + ((size_t)h * a.nchunks + wg) * nq * (HD + 2);
-#pragma unroll
-    for (int n = 0; n < NDT; ++n) {
-        const int dt = wave + 4 * n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * (lane >> 4) + i;
-            if (t < nq) out[(size_t)t * (HD + 2) + dt * 16 + fr] = o[n][i];
+            for (int j = 0; j < 4; ++j) o[dt][j] *= al[j];
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, B, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, o[dt], 0, 0, 0);
         }
     }
-    if (qseg == 0 && qt < nq) {
-        out[(size_t)qt * (HD + 2) + HD] = m_run;
-        out[(size_t)qt * (HD + 2) + HD + 1] = l_run;
+    // the run's partial: unnormalised o, running max, running sum (an empty run: max -inf, sum 0, o 0)
+    float* out = a.part + ((size_t)h * a.nchunks + run) * nq * (HD + 2);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 4 * g + j;
+            if (t < nq) out[(size_t)t * (HD + 2) + 16 * dt + r] = o[dt][j];
+        }
+    if (g == 0 && r < nq) {
+        out[(size_t)r * (HD + 2) + HD] = m_run;
+        out[(size_t)r * (HD + 2) + HD + 1] = l_run;
     }
 }
 
@@ -875,10 +861,12 @@ __global__ __launch_bounds__(256) void kv_final_kernel(KVFinalArgs a) {
                 vw[e] = (uint32_t)f32_to_f16(v[2 * e]) | ((uint32_t)f32_to_f16(v[2 * e + 1]) << 16);
             }
             *(uint4*)((uint16_t*)a.cache + kbase + i0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-            // f16 V is dimension-major: dim i0 + e of position start + t
-            uint16_t* vt = (uint16_t*)a.cache + (size_t)(2 * l + 1) * a.max_ctx * D + (size_t)i0 * a.max_ctx + a.start + t;
+            // f16 V is tiled [pos / 32][dim][32]: dims i0 .. i0 + 7 of position start + t
+            const int pos = a.start + t;
+            uint16_t* vt = (uint16_t*)a.cache + (size_t)(2 * l + 1) * a.max_ctx * D +
+                           ((size_t)(pos >> 5) * D + i0) * 32 + (pos & 31);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vt[(size_t)e * a.max_ctx] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < 8; ++e) vt[e * 32] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
         } else {
             float* kc = (float*)a.cache + kbase + i0;
             float* vc = (float*)a.cache + vbase + i0;
@@ -943,10 +931,10 @@ static bool f32_mfma_fits(const AttnArgs& a) {
 }
 
 int attn_chunk_size(int hd, int kv_dtype, int nkeys, int heads) {
-    const int big = 16384 / (hd * (kv_dtype == 0 ? 2 : 4));
-    if (kv_dtype != 0) return (hd == 128 || hd == 256) ? 32 : big;
-    // f16 caches: halve the chunk while the big one leaves the 256 CUs short of work-groups
-    return (long)heads * ((nkeys + big - 1) / big) < 256 ? big / 2 : big;
+    (void)nkeys;
+    (void)heads;
+    if (kv_dtype == 0) return 32;   // the wave kernel's 32-key step
+    return (hd == 128 || hd == 256) ? 32 : 16384 / (hd * 4);
 }
 
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
@@ -955,23 +943,23 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
         !a.qp.q || nkeys < 1)
         return hipErrorInvalidValue;
     const int tc = (nkeys + a.chunk - 1) / a.chunk;
-    if (a.cpw < 1 || (a.kv_dtype != 0 && a.cpw != 1) || a.nchunks != (tc + a.cpw - 1) / a.cpw) return hipErrorInvalidValue;
+    // f16 caches: nchunks = key runs per head rounded up to whole 4-wave work-groups; f32 caches: one chunk each
+    const int runs = (tc + a.cpw - 1) / a.cpw;
+    if (a.cpw < 1 || (a.kv_dtype != 0 && (a.cpw != 1 || a.nchunks != tc)) ||
+        (a.kv_dtype == 0 && a.nchunks != (runs + 3) / 4 * 4))
+        return hipErrorInvalidValue;
     if (a.qp.rope && a.qp.rope_dims > (a.hd <= 128 ? a.hd : 128)) return hipErrorInvalidValue;
     if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
     if (a.qp.parts > MAX_QSLABS || (a.kv_dtype != 0 && a.qp.parts > 1)) return hipErrorInvalidValue;
     dim3 grid(a.nchunks, a.heads);
     if (a.kv_dtype == 0) {
-        if (a.qp.rope == 2 || (a.qp.rope == 1 && a.qp.rope_dims != a.hd)) return hipErrorInvalidValue;
-        const bool big = a.chunk == 16384 / (a.hd * 2);
+        if (a.qp.rope == 2 || (a.qp.rope == 1 && a.qp.rope_dims != a.hd) || a.nx > 0 || (a.key_lo & 31))
+            return hipErrorInvalidValue;
+        dim3 gw((a.nchunks + 3) / 4, a.heads);
+        if (a.nchunks % 4) return hipErrorInvalidValue;
         switch (a.hd) {
-        case 64:
-            if (big) attn_split_mfma_kernel<64, 128><<<grid, 256, 0, st>>>(a);
-            else attn_split_mfma_kernel<64, 64><<<grid, 256, 0, st>>>(a);
-            break;
-        case 128:
-            if (big) attn_split_mfma_kernel<128, 64><<<grid, 256, 0, st>>>(a);
-            else attn_split_mfma_kernel<128, 32><<<grid, 256, 0, st>>>(a);
-            break;
+        case 64: attn_wave_kernel<64><<<gw, 256, 0, st>>>(a); break;
+        case 128: attn_wave_kernel<128><<<gw, 256, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
         }
     } else if (f32_mfma_fits(a)) {

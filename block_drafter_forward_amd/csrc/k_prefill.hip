@@ -12,8 +12,8 @@
 // load latency (measured: 30% -> 40% of the f16 peak on the 8192-row K/V projections). Work-groups are remapped so
 // each XCD owns a contiguous run of tiles (consecutive n-tiles of the same row block share their A rows in that
 // XCD's L2).
-// Epilogues: f32 rows; a cache store (f16 / f32) at rows start + r, or transposed (the f16 V cache, dimension-major,
-// 8-byte stores of 4 consecutive positions); or, for K, the per-head RMSNorm over the tile's
+// Epilogues: f32 rows; a cache store (f16 / f32) at rows start + r, or into the f16 V cache's 32-position tiles
+// (dimension-major inside a tile: 8-byte stores of 4 consecutive positions); or, for K, the per-head RMSNorm over the tile's
 // columns (a head is 64 or 128 columns of the 128-wide tile) and interleaved RoPE at position start + r before the
 // store -- the page's headNormRope + kvWrite, fused.
 #include "fm_device.h"
@@ -192,17 +192,20 @@ __global__ __launch_bounds__(T * 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
             const int rb = r0 + wm * TI * 16 + 16 * i + rq;
+            const int pb = a.start + rb;
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
                 const int n = n0 + wn * 64 + 16 * j + cl;
-                uint16_t* dst = (uint16_t*)G.out + (size_t)n * a.vt_ld + a.start + rb;
-                if (rb + 3 < a.rows && ((a.start + rb) & 3) == 0) {
+                uint16_t* dst = (uint16_t*)G.out + ((size_t)(pb >> 5) * a.vt_ld + n) * 32 + (pb & 31);
+                if (rb + 3 < a.rows && (pb & 3) == 0) {   // the 4 positions share a 32-position tile
                     *(uint2*)dst = make_uint2((uint32_t)f32_to_f16(acc[i][j][0]) | ((uint32_t)f32_to_f16(acc[i][j][1]) << 16),
                                               (uint32_t)f32_to_f16(acc[i][j][2]) | ((uint32_t)f32_to_f16(acc[i][j][3]) << 16));
                 } else {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        if (rb + q < a.rows) dst[q] = f32_to_f16(acc[i][j][q]);
+                        if (rb + q < a.rows)
+                            ((uint16_t*)G.out)[((size_t)((pb + q) >> 5) * a.vt_ld + n) * 32 + ((pb + q) & 31)] =
+                                f32_to_f16(acc[i][j][q]);
                 }
             }
         }

@@ -191,6 +191,6 @@ class Drafter:
             return t[which]
         dt = torch.float16 if c["kv_dtype"] == "f16" else torch.float32
         t = self.kv.view(dt).view(c["layers"], 2, c["max_ctx"] * c["dim"])[l, which]
-        if c["kv_dtype"] == "f16" and which == 1:   # the f16 V cache is dimension-major: present it [pos][dim]
-            return t.view(c["dim"], c["max_ctx"]).t()
+        if c["kv_dtype"] == "f16" and which == 1:   # the f16 V cache is tiled [pos/32][dim][32]: a [pos][dim] copy
+            return t.view(c["max_ctx"] // 32, c["dim"], 32).permute(0, 2, 1).reshape(c["max_ctx"], c["dim"])
         return t.view(c["max_ctx"], c["dim"])

@@ -93,8 +93,9 @@ typedef struct fm_drafter fm_drafter;
 /* Bytes of the K/V cache the caller allocates for `cfg` (0 if cfg is invalid).
  * Flow-map / KV-inject layout: for layer l, K at byte offset 2*l*max_ctx*dim*es and V right after (es = 2 for F16,
  * 4 for F32), each max_ctx*dim elements. K is [max_ctx][dim] (position-major). V is [max_ctx][dim] in an F32 cache
- * and [dim][max_ctx] (dimension-major, transposed) in an F16 cache, so that attention reads each dimension's run
- * of consecutive positions as the matrix-core operand directly; an F16 cache needs max_ctx % 8 == 0.
+ * and tiled [max_ctx/32][dim][32] in an F16 cache: each block of 32 positions is stored dimension-major, so that
+ * attention reads one dimension's 32 consecutive positions as the matrix-core operand, and a head's block of
+ * 32 positions as contiguous memory; an F16 cache needs max_ctx % 32 == 0.
  * MTP layout: K [max_ctx][kv_heads*head_dim] f32, then V likewise. */
 size_t fm_kv_bytes(const fm_config* cfg);
 
