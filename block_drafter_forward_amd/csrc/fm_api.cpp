@@ -77,7 +77,7 @@ int pick_split(int M_total, int K) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -143,6 +143,11 @@ Plan make_plan(const fm_config& c) {
     const bool prefill = c.variant != FM_VARIANT_MTP;
     p.pctx = take(prefill ? (size_t)c.max_ctx * D * 4 : 0);
     p.pctxn = take(prefill ? (size_t)(c.variant == FM_VARIANT_KVINJECT ? c.layers : 1) * c.max_ctx * D * 2 : 0);
+    // f16 copies of the prefill weights (the context projection, then K and V of every layer), made at create, and
+    // of the taps of one append: the 256-tile prefill GEMM streams f16 operands straight into LDS
+    const size_t KT = (size_t)c.n_taps * c.target_dim;
+    p.w16 = take(prefill ? (KT * D + 2ull * c.layers * D * D) * 2 : 0);
+    p.taps16 = take(prefill ? (size_t)c.max_ctx * KT * 2 : 0);
     p.qout = take(c.variant == FM_VARIANT_MTP ? (size_t)TMAX * c.heads * c.head_dim * 4 : 0);
     // the flow-map anchor path runs on a side stream next to the first layer: it has buffers of its own
     const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
@@ -218,6 +223,12 @@ struct fm_drafter {
     size_t kv_es() const { return c.kv_dtype == FM_KV_F16 ? 2 : 4; }
     void* kv_layer(int l, int which) const {   // which 0: K, 1: V
         return kv + ((size_t)(2 * l + which) * c.max_ctx * c.dim) * kv_es();
+    }
+    size_t tap_width() const { return (size_t)c.n_taps * c.target_dim; }
+    // f16 copies of the prefill weights: the context projection [dim][n_taps * target_dim], then per layer K, V [dim][dim]
+    const uint16_t* w16_ctx() const { return at<uint16_t>(p.w16); }
+    const uint16_t* w16_kv(int l, int which) const {
+        return at<uint16_t>(p.w16) + tap_width() * c.dim + (size_t)(2 * l + which) * c.dim * c.dim;
     }
 };
 
@@ -397,6 +408,40 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
 }
 
 // ── flow-map ────────────────────────────────────────────────────────────────────────────────────
+// A operand of the context projection: the f32 taps as they are for 128-tiles (rounded to f16 on the way into LDS),
+// an f16 copy for 256-tiles (which stream f16 operands straight into LDS; same rounding).
+fm_status prefill_taps(fm_drafter* d, const float* taps, int n, PrefillArgs& a, hipStream_t st) {
+    const size_t KT = d->tap_width();
+    if (prefill_tile(n, d->c.dim, 1) == 256) {
+        uint16_t* t16 = d->at<uint16_t>(d->p.taps16);
+        HIPCHK(launch_f32_to_f16(taps, (size_t)n * KT, t16, st));
+        a.A = t16;
+        a.a_f32 = 0;
+    } else {
+        a.A = taps;
+        a.a_f32 = 1;
+    }
+    return FM_OK;
+}
+
+std::string LW(int l, const char* s);
+std::string BB(int i, const char* s);
+
+// f16 copies of the prefill weights (bf16 -> f16 is exact down to f16's subnormal range)
+fm_status prefill_weight_copies(fm_drafter* d, hipStream_t st) {
+    const auto& c = d->c;
+    const size_t DD = (size_t)c.dim * c.dim;
+    const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
+    HIPCHK(launch_bf16_to_f16(d->B(fmv ? "fc.weight" : "W_c"), d->tap_width() * c.dim, (uint16_t*)d->w16_ctx(), st));
+    for (int l = 0; l < c.layers; ++l)
+        for (int w = 0; w < 2; ++w) {
+            const std::string nm = fmv ? LW(l, w ? "cross_attn.v_proj.weight" : "cross_attn.k_proj.weight")
+                                       : BB(l, w ? "v" : "k");
+            HIPCHK(launch_bf16_to_f16(d->B(nm), DD, (uint16_t*)d->w16_kv(l, w), st));
+        }
+    return FM_OK;
+}
+
 std::string LW(int l, const char* s) {
     char b[128];
     snprintf(b, sizeof b, "layers.%d.%s", l, s);
@@ -466,9 +511,8 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     {
         PrefillArgs a{};
         a.ngroups = 1;
-        a.g[0] = PrefillGroup{nullptr, d->B("fc.weight"), nullptr, ctx, PF_F32, 0};
-        a.A = taps;
-        a.a_f32 = 1;
+        a.g[0] = PrefillGroup{nullptr, d->B("fc.weight"), d->w16_ctx(), nullptr, ctx, PF_F32, 0};
+        CHK(prefill_taps(d, taps, n, a, st));
         a.rows = n;
         a.N = D;
         a.K = KT;
@@ -487,11 +531,11 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         const int per = mt * (D / tile);
         for (int j = 0; j < nl; ++j) {
             const int l = l0 + j;
-            a.g[2 * j] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.k_proj.weight")),
+            a.g[2 * j] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.k_proj.weight")), d->w16_kv(l, 0),
                                       d->B(LW(l, "cross_attn.k_norm.weight")), d->kv_layer(l, 0), PF_CACHE_K,
                                       (2 * j) * per};
-            a.g[2 * j + 1] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.v_proj.weight")), nullptr, d->kv_layer(l, 1),
-                                          PF_CACHE_VT, (2 * j + 1) * per};
+            a.g[2 * j + 1] = PrefillGroup{nullptr, d->B(LW(l, "cross_attn.v_proj.weight")), d->w16_kv(l, 1), nullptr,
+                                          d->kv_layer(l, 1), PF_CACHE_VT, (2 * j + 1) * per};
         }
         a.ngroups = 2 * nl;
         a.A = ctxn;
@@ -762,9 +806,8 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     {
         PrefillArgs a{};
         a.ngroups = 1;
-        a.g[0] = PrefillGroup{nullptr, d->B("W_c"), nullptr, ctx, PF_F32, 0};
-        a.A = taps;
-        a.a_f32 = 1;
+        a.g[0] = PrefillGroup{nullptr, d->B("W_c"), d->w16_ctx(), nullptr, ctx, PF_F32, 0};
+        CHK(prefill_taps(d, taps, n, a, st));
         a.rows = n;
         a.N = D;
         a.K = KT;
@@ -796,8 +839,10 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
         for (int j = 0; j < nl; ++j) {
             const int i = l0 + j;
             const uint16_t* Ai = ctxn + (size_t)i * c.max_ctx * D;
-            a.g[2 * j] = PrefillGroup{Ai, d->B(BB(i, "k")), nullptr, d->kv_layer(i, 0), PF_CACHE_V, (2 * j) * per};
-            a.g[2 * j + 1] = PrefillGroup{Ai, d->B(BB(i, "v")), nullptr, d->kv_layer(i, 1), PF_CACHE_V, (2 * j + 1) * per};
+            a.g[2 * j] = PrefillGroup{Ai, d->B(BB(i, "k")), d->w16_kv(i, 0), nullptr, d->kv_layer(i, 0), PF_CACHE_V,
+                                      (2 * j) * per};
+            a.g[2 * j + 1] = PrefillGroup{Ai, d->B(BB(i, "v")), d->w16_kv(i, 1), nullptr, d->kv_layer(i, 1), PF_CACHE_V,
+                                          (2 * j + 1) * per};
         }
         a.ngroups = 2 * nl;
         a.a_f32 = 0;
@@ -1079,6 +1124,10 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
         if (cfg->rope != FM_ROPE_NONE) {
             hipError_t e = launch_rope_table(d->at<float>(d->p.rope), d->p.rope_rows, d->p.rope_dims, cfg->rope_theta, st);
             if (e != hipSuccess) { s = fail(FM_E_HIP, "rope table: %s", hipGetErrorString(e)); break; }
+        }
+        if (cfg->variant != FM_VARIANT_MTP) {
+            s = prefill_weight_copies(d, st);
+            if (s != FM_OK) break;
         }
         if (cfg->variant == FM_VARIANT_FLOWMAP) s = flowmap_create(d, st);
         else if (cfg->variant == FM_VARIANT_KVINJECT) s = kvinject_create(d, st);

@@ -221,6 +221,7 @@ enum PrefillEpi {
 struct PrefillGroup {
     const void* A;         // this group's A rows (null: PrefillArgs.A)
     const uint16_t* B;     // bf16 [N][K]
+    const uint16_t* B16;   // the same matrix as f16 [N][K] (256-tiles read this one)
     const uint16_t* knorm; // bf16 [hd] (PF_CACHE_K)
     void* out;             // f32 C or the cache row 0 of this layer's K or V
     int epi;
@@ -243,9 +244,12 @@ struct PrefillArgs {
     int m_tiles, n_tiles;
 };
 // Tile edge (128 or 256) the launcher uses for rows x N x ngroups; the host sizes m_tiles, n_tiles and the
-// groups' tile_begin with it.
+// groups' tile_begin with it. 256-tiles need f16 A (a_f32 == 0), every group's B16, and K % 64 == 0.
 int prefill_tile(int rows, int N, int ngroups);
 hipError_t launch_prefill(const PrefillArgs& a, int n_workgroups, hipStream_t st);
+// y = f16(x) element-wise (round to nearest even), n % 4 == 0: f32 taps, bf16 weights.
+hipError_t launch_f32_to_f16(const float* x, size_t n, uint16_t* y, hipStream_t st);
+hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStream_t st);
 
 // Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context).
 hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out,

@@ -2,20 +2,27 @@
 //
 // The one truly dense contraction of the path: the fusion of many context rows (fc / W_c over the concatenated
 // taps, flashmap_drafter.js extendContext; module-dflash.ts #buildContext) and the per-layer K/V projections of the
-// fused rows. Operands are f16 on v_mfma_f32_16x16x32_f16 with f32 accumulation: the f32 taps are rounded to f16 on
-// their way into LDS (2^-11 relative, four times finer than bf16), the bf16 weights are widened to f16 exactly (up
-// to f16's subnormal range, |error| <= 2^-25). Tiles: 256 x 256 per work-group of 8 waves (2 x 4, 128 x 64 each,
-// 32 accumulators of 16x16) when the problem has enough of them, else 128 x 128 per 4 waves; k-stages of 32
-// double-buffered in LDS with a 16-byte row pad (conflict-free fragment reads), the next stage's global loads in
-// flight while the current one computes. The larger tile halves the L2 traffic per flop. Two k-stages of global
-// loads are in flight (registers) while a third multiplies from LDS: one stage of MFMAs alone does not cover the
-// load latency (measured: 30% -> 40% of the f16 peak on the 8192-row K/V projections). Work-groups are remapped so
-// each XCD owns a contiguous run of tiles (consecutive n-tiles of the same row block share their A rows in that
-// XCD's L2).
+// fused rows. Operands are f16 on v_mfma_f32_16x16x32_f16 with f32 accumulation: f32 taps are rounded to f16
+// (2^-11 relative, four times finer than bf16), bf16 weights are widened to f16 exactly (up to f16's subnormal
+// range, |error| <= 2^-25).
+//
+// Large problems (at least one 256 x 256 tile per CU) run prefill_dma_kernel: A and B are both f16 in HBM (the
+// weights converted once when the drafter is created, the taps by one pass before the product) and are streamed
+// into LDS by the LDS-direct load (global_load_lds_dwordx4: no registers, no conversion on the way). A k-stage is 64
+// k-values, so every row slice a load touches is one whole 128-byte line (measured: half-line slices moved half the
+// bytes per second); in LDS a row is 8 chunks of 16 bytes with chunk c at slot c ^ (row & 7), which makes the
+// 16 x 32 fragment reads conflict-free (measured with a read microbenchmark: 4 LDS cycles per 1 KB read). Two stage
+// buffers (128 KB); 8 waves as 2 x 4 of 128 x 64; each wave reads the fragments of the next 32-k substep while the
+// current one multiplies, so one barrier per stage is the only synchronisation.
+// Small problems run prefill_kernel: 128 x 128 tiles of 4 waves, operands staged through registers (f32 taps
+// rounded, bf16 weights widened on the way into LDS), two k-stages of loads in flight.
+// Work-groups are remapped so each XCD owns a contiguous run of tiles, taken 8 row tiles at a time (the 8 row
+// tiles of a group share B tiles and each A tile is shared by the group's column tiles, in that XCD's L2).
 // Epilogues: f32 rows; a cache store (f16 / f32) at rows start + r, or into the f16 V cache's 32-position tiles
-// (dimension-major inside a tile: 8-byte stores of 4 consecutive positions); or, for K, the per-head RMSNorm over the tile's
-// columns (a head is 64 or 128 columns of the 128-wide tile) and interleaved RoPE at position start + r before the
-// store -- the page's headNormRope + kvWrite, fused.
+// (dimension-major inside a tile: 8-byte stores of 4 consecutive positions); or, for K, the per-head RMSNorm over the
+// tile's columns (a head is 64 or 128 columns of the 256-wide tile) and interleaved RoPE at position start + r before
+// the store -- the page's headNormRope + kvWrite, fused.
+#include <algorithm>
 #include "fm_device.h"
 #include "fm_kernels.h"
 
@@ -27,6 +34,105 @@ __device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+}
+
+// acc[i][j][q] = C[r0 + wm*16*TI + 16 i + 4 (lane/16) + q][n0 + wn*64 + 16 j + lane%16]
+template <int T, int TI, int TJ, int NWN>
+__device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const PrefillArgs& a, const PrefillGroup& G,
+                                                 int r0, int n0, int wm, int wn, int lane, float (&nred)[NWN][T]) {
+    const int rq = 4 * (lane >> 4), cl = lane & 15;
+    if (G.epi == PF_CACHE_K && G.knorm) {
+        const int hd = a.hd;
+        float ssq[TI][4];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) s += acc[i][j][q] * acc[i][j][q];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+                ssq[i][q] = s;
+            }
+        if (hd == 128) {   // a head spans two waves along n
+            if (cl == 0) {
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) nred[wn][wm * TI * 16 + 16 * i + rq + q] = ssq[i][q];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = wm * TI * 16 + 16 * i + rq + q;
+                    ssq[i][q] = nred[wn & ~1][rl] + nred[wn | 1][rl];
+                }
+        }
+        const int half = a.rope_dims >> 1;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
+                const float rs = 1.f / sqrtf(ssq[i][q] / (float)hd + a.eps);
+                const int pos = a.start + (r < a.rows ? r : 0);
+                const float* tr = a.rope_tab + (size_t)pos * a.rope_dims;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) {
+                    const int n = n0 + wn * 64 + 16 * j + cl;
+                    const int d = n % hd;
+                    const float v = acc[i][j][q] * rs * bf16_to_f32(G.knorm[d]);
+                    const float p = __shfl_xor(v, 1, 64);
+                    const float c = tr[d >> 1], sn = tr[half + (d >> 1)];
+                    acc[i][j][q] = (d & 1) ? v * c + p * sn : v * c - p * sn;
+                }
+            }
+    }
+    if (G.epi == PF_CACHE_VT) {   // a lane's 4 consecutive rows are 4 consecutive positions of one V dimension
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const int rb = r0 + wm * TI * 16 + 16 * i + rq;
+            const int pb = a.start + rb;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int n = n0 + wn * 64 + 16 * j + cl;
+                uint16_t* dst = (uint16_t*)G.out + ((size_t)(pb >> 5) * a.vt_ld + n) * 32 + (pb & 31);
+                if (rb + 3 < a.rows && (pb & 3) == 0) {   // the 4 positions share a 32-position tile
+                    *(uint2*)dst = make_uint2((uint32_t)f32_to_f16(acc[i][j][0]) | ((uint32_t)f32_to_f16(acc[i][j][1]) << 16),
+                                              (uint32_t)f32_to_f16(acc[i][j][2]) | ((uint32_t)f32_to_f16(acc[i][j][3]) << 16));
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (rb + q < a.rows)
+                            ((uint16_t*)G.out)[((size_t)((pb + q) >> 5) * a.vt_ld + n) * 32 + ((pb + q) & 31)] =
+                                f32_to_f16(acc[i][j][q]);
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
+            if (r >= a.rows) continue;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int n = n0 + wn * 64 + 16 * j + cl;
+                const float v = acc[i][j][q];
+                if (G.epi == PF_F32) {
+                    ((float*)G.out)[(size_t)r * a.ld + n] = v;
+                } else {
+                    const size_t off = (size_t)(a.start + r) * a.ld + n;
+                    if (a.kv_dtype == 0) ((uint16_t*)G.out)[off] = f32_to_f16(v);
+                    else ((float*)G.out)[off] = v;
+                }
+            }
+        }
 }
 
 // Tile T x T (T = 128: 4 waves as 2 x 2 of 64 x 64; T = 256: 8 waves as 2 x 4 of 128 x 64). Every thread stages
@@ -136,100 +242,133 @@ __global__ __launch_bounds__(T * 2) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    // acc[i][j][q] = C[r0 + wm*16*TI + 16 i + 4 (lane/16) + q][n0 + wn*64 + 16 j + lane%16]
-    const int rq = 4 * (lane >> 4), cl = lane & 15;
-    if (G.epi == PF_CACHE_K && G.knorm) {
-        const int hd = a.hd;
-        float ssq[TI][4];
+    prefill_epilogue<T, TI, TJ, NWN>(acc, a, G, r0, n0, wm, wn, lane, nred);
+}
+
+// ── 256 x 256 tiles from f16 operands, LDS-direct loads ──────────────────────────────────────────────────────────
+
+// LDS-direct load of 16 bytes per lane: lane l's 16 bytes from g land at LDS byte lds + 16 l (lds is wave-uniform,
+// passed in m0). Written as inline asm so that the compiler's wait bookkeeping leaves it alone: it cannot tell the
+// two stage buffers apart and would otherwise wait for every load in flight before any LDS read; the kernel waits
+// for these loads explicitly (wait_vm). Nothing else in the kernel uses m0.
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+    const unsigned la =
+        __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((__attribute__((address_space(3))) void*)lds));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = n and the other counters at their maxima (gfx9 encoding), and with lgkmcnt = 0 only
+template <int N> __device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// A bare s_barrier: __syncthreads() adds a release fence, which makes the compiler wait for every LDS-direct load in
+// flight (vmcnt(0)) and would serialise the pipeline; the waits this kernel needs are explicit.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(512) void prefill_dma_kernel(PrefillArgs a) {
+    constexpr int TI = 8, TJ = 4, NWN = 4, GM = 8;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][256 * 128];   // [stage][A | B][row][128 B]
+    __shared__ float nred[NWN][256];
+
+    const int total = gridDim.x;
+    int lin = blockIdx.x;
+    if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    int gi = 0;
+#pragma unroll 1
+    for (int i = 1; i < a.ngroups; ++i)
+        if (lin >= a.g[i].tile_begin) gi = i;
+    const PrefillGroup& G = a.g[gi];
+    const int local = lin - G.tile_begin;
+    const int grp = local / (GM * a.n_tiles);
+    const int gm = min(GM, a.m_tiles - grp * GM);
+    const int within = local - grp * GM * a.n_tiles;
+    const int mt = grp * GM + within % gm, nt = within / gm;
+    const int r0 = mt * 256, n0 = nt * 256;
+    const uint16_t* Ap = (const uint16_t*)(G.A ? G.A : a.A);
+    const int K = a.K;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 2, wn = wave & 3;
+    // loads: wave w fills rows 32w .. 32w + 31 of the A and the B tile, 8 rows (1 KB of LDS) per instruction; lane l
+    // takes row l / 8 of those 8 and writes LDS slot l % 8 of it, which holds chunk (l % 8) ^ (l / 8)
+    const int lrow = lane >> 3, lch = (lane & 7) ^ lrow;
+    const uint16_t* ga[4];
+    const uint16_t* gb[4];
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < TJ; ++j) s += acc[i][j][q] * acc[i][j][q];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-                ssq[i][q] = s;
-            }
-        if (hd == 128) {   // a head spans two waves along n
-            if (cl == 0) {
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) nred[wn][wm * TI * 16 + 16 * i + rq + q] = ssq[i][q];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int rl = wm * TI * 16 + 16 * i + rq + q;
-                    ssq[i][q] = nred[wn & ~1][rl] + nred[wn | 1][rl];
-                }
-        }
-        const int half = a.rope_dims >> 1;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
-                const float rs = 1.f / sqrtf(ssq[i][q] / (float)hd + a.eps);
-                const int pos = a.start + (r < a.rows ? r : 0);
-                const float* tr = a.rope_tab + (size_t)pos * a.rope_dims;
-#pragma unroll
-                for (int j = 0; j < TJ; ++j) {
-                    const int n = n0 + wn * 64 + 16 * j + cl;
-                    const int d = n % hd;
-                    const float v = acc[i][j][q] * rs * bf16_to_f32(G.knorm[d]);
-                    const float p = __shfl_xor(v, 1, 64);
-                    const float c = tr[d >> 1], sn = tr[half + (d >> 1)];
-                    acc[i][j][q] = (d & 1) ? v * c + p * sn : v * c - p * sn;
-                }
-            }
+    for (int i = 0; i < 4; ++i) {
+        ga[i] = Ap + (size_t)min(r0 + 32 * wave + 8 * i + lrow, a.rows - 1) * K + 8 * lch;
+        gb[i] = G.B16 + (size_t)(n0 + 32 * wave + 8 * i + lrow) * K + 8 * lch;
     }
-    if (G.epi == PF_CACHE_VT) {   // a lane's 4 consecutive rows are 4 consecutive positions of one V dimension
+    auto issue = [&](int s, int buf) {
+        const int k0 = s * 64;
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const int rb = r0 + wm * TI * 16 + 16 * i + rq;
-            const int pb = a.start + rb;
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int n = n0 + wn * 64 + 16 * j + cl;
-                uint16_t* dst = (uint16_t*)G.out + ((size_t)(pb >> 5) * a.vt_ld + n) * 32 + (pb & 31);
-                if (rb + 3 < a.rows && (pb & 3) == 0) {   // the 4 positions share a 32-position tile
-                    *(uint2*)dst = make_uint2((uint32_t)f32_to_f16(acc[i][j][0]) | ((uint32_t)f32_to_f16(acc[i][j][1]) << 16),
-                                              (uint32_t)f32_to_f16(acc[i][j][2]) | ((uint32_t)f32_to_f16(acc[i][j][3]) << 16));
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (rb + q < a.rows)
-                            ((uint16_t*)G.out)[((size_t)((pb + q) >> 5) * a.vt_ld + n) * 32 + ((pb + q) & 31)] =
-                                f32_to_f16(acc[i][j][q]);
-                }
-            }
+        for (int i = 0; i < 4; ++i) {
+            lds_load16(ga[i] + k0, &lds[buf][0][(32 * wave + 8 * i) * 128]);
+            lds_load16(gb[i] + k0, &lds[buf][1][(32 * wave + 8 * i) * 128]);
         }
-        return;
-    }
+    };
+    // fragment of k-half h: row l % 16 of a 16-row block, chunk 4h + l / 16, at slot chunk ^ (row & 7)
+    const int fr = lane & 15, fq = lane >> 4;
+    const int fo0 = fr * 128 + 16 * (fq ^ (fr & 7)), fo1 = fr * 128 + 16 * ((4 + fq) ^ (fr & 7));
+    f32x4_t acc[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
-            if (r >= a.rows) continue;
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f16x8_t fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+    auto rd = [&](f16x8_t* fa, f16x8_t* fb, int buf, int fo) {
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int n = n0 + wn * 64 + 16 * j + cl;
-                const float v = acc[i][j][q];
-                if (G.epi == PF_F32) {
-                    ((float*)G.out)[(size_t)r * a.ld + n] = v;
-                } else {
-                    const size_t off = (size_t)(a.start + r) * a.ld + n;
-                    if (a.kv_dtype == 0) ((uint16_t*)G.out)[off] = f32_to_f16(v);
-                    else ((float*)G.out)[off] = v;
-                }
-            }
-        }
+        for (int i = 0; i < TI; ++i) fa[i] = *(const f16x8_t*)&lds[buf][0][(wm * 128 + 16 * i) * 128 + fo];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) fb[j] = *(const f16x8_t*)&lds[buf][1][(wn * 64 + 16 * j) * 128 + fo];
+    };
+    auto mm = [&](const f16x8_t* fa, const f16x8_t* fb) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Stage s lives in buffer s % 2. Iteration s: read substep 1's fragments of stage s, multiply substep 0; wait
+    // until this wave's reads are done and stage s + 1 has landed, barrier (now every wave is done with buffer s % 2
+    // and stage s + 1 is visible); load stage s + 2 into buffer s % 2, read stage s + 1's substep-0 fragments,
+    // multiply substep 1. Past the end the loads re-read the last stage into a buffer nobody reads again, so every
+    // iteration issues the same number of loads.
+    const int nk = K / 64;
+    issue(0, 0);
+    issue(min(1, nk - 1), 1);
+    wait_vm<8>();
+    bar();
+    rd(fa0, fb0, 0, fo0);
+    for (int s = 0; s < nk; ++s) {
+        const int buf = s & 1;
+        rd(fa1, fb1, buf, fo1);
+        mm(fa0, fb0);
+        wait_lgkm0();
+        wait_vm<0>();
+        bar();
+        issue(min(s + 2, nk - 1), buf);
+        rd(fa0, fb0, buf ^ 1, fo0);
+        mm(fa1, fb1);
+    }
+    wait_vm<0>();
+    prefill_epilogue<256, TI, TJ, NWN>(acc, a, G, r0, n0, wm, wn, lane, nred);
+}
+
+__global__ void f32_to_f16_kernel(const float* __restrict__ x, size_t n4, uint2* __restrict__ y) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        const float4 v = ((const float4*)x)[i];
+        y[i] = make_uint2(pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w));
+    }
+}
+
+__global__ void bf16_to_f16_kernel(const uint2* __restrict__ x, size_t n4, uint2* __restrict__ y) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        const uint2 w = x[i];
+        y[i] = make_uint2(pack_f16x2(bf16_lo(w.x), bf16_hi(w.x)), pack_f16x2(bf16_lo(w.y), bf16_hi(w.y)));
+    }
 }
 
 }  // namespace
@@ -241,14 +380,35 @@ int prefill_tile(int rows, int N, int ngroups) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int nwg, hipStream_t st) {
     const int T = prefill_tile(a.rows, a.N, a.ngroups);
-    if (a.K % BK || a.N % T || a.rows < 1 || a.n_tiles != a.N / T || a.m_tiles != (a.rows + T - 1) / T)
+    if (a.K % BK || a.N % T || a.rows < 1 || a.n_tiles != a.N / T || a.m_tiles != (a.rows + T - 1) / T ||
+        a.ngroups < 1 || a.ngroups > PF_MAX_GROUPS)
         return hipErrorInvalidValue;
-    if (T == 256) {
-        if (a.a_f32) prefill_kernel<1, 256><<<nwg, 512, 0, st>>>(a);
-        else prefill_kernel<0, 256><<<nwg, 512, 0, st>>>(a);
+    if (T == 256) {   // f16 A and f16 copies of every group's B; 64-k stages
+        if (a.a_f32 || a.K % 64) return hipErrorInvalidValue;
+        for (int i = 0; i < a.ngroups; ++i)
+            if (!a.g[i].B16) return hipErrorInvalidValue;
+        prefill_dma_kernel<<<nwg, 512, 0, st>>>(a);
     } else {
         if (a.a_f32) prefill_kernel<1, 128><<<nwg, 256, 0, st>>>(a);
         else prefill_kernel<0, 128><<<nwg, 256, 0, st>>>(a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_f32_to_f16(const float* x, size_t n, uint16_t* y, hipStream_t st) {
+    if (n % 4 || ((uintptr_t)x & 15) || ((uintptr_t)y & 7)) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    const size_t n4 = n / 4;
+    const int grid = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    f32_to_f16_kernel<<<grid, 256, 0, st>>>(x, n4, (uint2*)y);
+    return hipGetLastError();
+}
+
+hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStream_t st) {
+    if (n % 4 || ((uintptr_t)x & 7) || ((uintptr_t)y & 7)) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    const size_t n4 = n / 4;
+    const int grid = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    bf16_to_f16_kernel<<<grid, 256, 0, st>>>((const uint2*)x, n4, (uint2*)y);
     return hipGetLastError();
 }
