@@ -77,7 +77,7 @@ int pick_split(int M_total, int K) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -148,6 +148,8 @@ Plan make_plan(const fm_config& c) {
     const size_t KT = (size_t)c.n_taps * c.target_dim;
     p.w16 = take(prefill ? (KT * D + 2ull * c.layers * D * D) * 2 : 0);
     p.taps16 = take(prefill ? (size_t)c.max_ctx * KT * 2 : 0);
+    // the prefill K epilogue's copy of the RoPE table (flow-map): each lane's cos / sin as two 16-byte loads
+    p.rope_pf = take(c.variant == FM_VARIANT_FLOWMAP ? (size_t)p.rope_rows * p.rope_dims * 4 : 0);
     p.qout = take(c.variant == FM_VARIANT_MTP ? (size_t)TMAX * c.heads * c.head_dim * 4 : 0);
     // the flow-map anchor path runs on a side stream next to the first layer: it has buffers of its own
     const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
@@ -547,6 +549,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         a.hd = c.head_dim;
         a.eps = c.qk_eps;
         a.rope_tab = d->at<float>(d->p.rope);
+        a.rope_pf = d->at<float>(d->p.rope_pf);
         a.rope_dims = d->p.rope_dims;
         a.start = start;
         a.kv_dtype = c.kv_dtype;
@@ -1123,6 +1126,9 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
         }
         if (cfg->rope != FM_ROPE_NONE) {
             hipError_t e = launch_rope_table(d->at<float>(d->p.rope), d->p.rope_rows, d->p.rope_dims, cfg->rope_theta, st);
+            if (e == hipSuccess && cfg->variant == FM_VARIANT_FLOWMAP)
+                e = launch_rope_prefill(d->at<float>(d->p.rope), d->p.rope_rows, d->p.rope_dims,
+                                        d->at<float>(d->p.rope_pf), st);
             if (e != hipSuccess) { s = fail(FM_E_HIP, "rope table: %s", hipGetErrorString(e)); break; }
         }
         if (cfg->variant != FM_VARIANT_MTP) {

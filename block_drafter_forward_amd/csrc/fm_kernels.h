@@ -237,6 +237,7 @@ struct PrefillArgs {
     int hd;
     float eps;
     const float* rope_tab;
+    const float* rope_pf;  // PF_CACHE_K with knorm: the prefill copy of the RoPE table (launch_rope_prefill)
     int rope_dims;
     int start;
     int kv_dtype;
@@ -247,6 +248,9 @@ struct PrefillArgs {
 // groups' tile_begin with it. 256-tiles need f16 A (a_f32 == 0), every group's B16, and K % 64 == 0.
 int prefill_tile(int rows, int N, int ngroups);
 hipError_t launch_prefill(const PrefillArgs& a, int n_workgroups, hipStream_t st);
+// Prefill copy of the interleaved-RoPE table [P][rdim] (rdim % 64 == 0): per position, per block of 32 pairs, per
+// c = 0..7 the cos then the sin of pairs c, c + 8, c + 16, c + 24 of the block.
+hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hipStream_t st);
 // y = f16(x) element-wise (round to nearest even), n % 4 == 0: f32 taps, bf16 weights.
 hipError_t launch_f32_to_f16(const float* x, size_t n, uint16_t* y, hipStream_t st);
 hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStream_t st);

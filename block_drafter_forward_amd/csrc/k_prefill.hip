@@ -36,13 +36,74 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
 }
 
+// LDS-direct load of 16 bytes per lane: lane l's 16 bytes from g land at LDS byte lds + 16 l (lds is wave-uniform,
+// passed in m0). Written as inline asm so that the compiler's wait bookkeeping leaves it alone: it cannot tell the
+// two stage buffers apart and would otherwise wait for every load in flight before any LDS read; the kernel waits
+// for these loads explicitly (wait_vm). Nothing else in the kernel uses m0.
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+    const unsigned la =
+        __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((__attribute__((address_space(3))) void*)lds));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = n and the other counters at their maxima (gfx9 encoding), and with lgkmcnt = 0 only
+template <int N> __device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// v[q] = C[row q][column c0 + t] on lane t of a quad (t = lane % 4) -> o[c] = C[row t][column c0 + c]: two
+// exchanges between lane pairs (lane ^ 1, then lane ^ 2) by DPP quad permutations.
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+// sum over the 16 lanes of a DPP row: pairs, quads, then the two mirrors
+__device__ __forceinline__ float row16_sum(float s) {
+    s += quad_xor1(s);
+    s += quad_xor2(s);
+    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x140, 0xF, 0xF, true));
+    return s;
+}
+__device__ __forceinline__ void quad_transpose(const f32x4_t& v, int t, float (&o)[4]) {
+    const bool odd = t & 1, hi = t & 2;
+    // step 1: even lanes keep rows 0 and 2 and take the odd neighbour's (column + 1) values of those rows; odd lanes
+    // keep rows 1 and 3 and take the even neighbour's (column - 1) values
+    const float s0 = quad_xor1(odd ? v[0] : v[1]), s1 = quad_xor1(odd ? v[2] : v[3]);
+    const float a0 = odd ? s0 : v[0], a1 = odd ? v[1] : s0;   // row t & 1, columns 2 (t >> 1) + 0, 1
+    const float b0 = odd ? s1 : v[2], b1 = odd ? v[3] : s1;   // row (t & 1) + 2, same columns
+    // step 2: lanes t and t ^ 2 complete one row each: row t & 1 for t < 2, row (t & 1) + 2 for t >= 2
+    const float u0 = quad_xor2(hi ? a0 : b0), u1 = quad_xor2(hi ? a1 : b1);
+    if (hi) { o[0] = u0; o[1] = u1; o[2] = b0; o[3] = b1; }
+    else    { o[0] = a0; o[1] = a1; o[2] = u0; o[3] = u1; }
+}
+
 // acc[i][j][q] = C[r0 + wm*16*TI + 16 i + 4 (lane/16) + q][n0 + wn*64 + 16 j + lane%16]
-template <int T, int TI, int TJ, int NWN>
+// stage: null, or T * T * 2 bytes of LDS that no wave reads or loads into any more (f16 row tiles go out through it)
+template <int T, int TI, int TJ, int NWN, bool STAGED>
 __device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const PrefillArgs& a, const PrefillGroup& G,
-                                                 int r0, int n0, int wm, int wn, int lane, float (&nred)[NWN][T]) {
+                                                 int r0, int n0, int wm, int wn, int lane, float (&nred)[NWN][T],
+                                                 uint8_t* stage) {
     const int rq = 4 * (lane >> 4), cl = lane & 15;
     if (G.epi == PF_CACHE_K && G.knorm) {
         const int hd = a.hd;
+        // with LDS to spare, the tile's T table rows (consecutive positions, T * hd floats <= T * T * 2 bytes) are
+        // copied in one batch of loads instead of 4 * TI dependent rounds of loads from L2
+        if constexpr (STAGED) {
+            // one wave instruction moves 1 KB = 1024 / (4 hd) table rows; lane l takes 16 bytes of row l / (hd / 4)
+            const int wave = threadIdx.x >> 6, rpi = 256 / hd, c16 = hd / 4;
+            const int nins = T * hd * 4 / 1024, nw = blockDim.x >> 6;
+            for (int ins = wave; ins < nins; ins += nw) {
+                const int rl = ins * rpi + lane / c16, k = lane % c16;
+                const int pos = a.start + min(r0 + rl, a.rows - 1);
+                lds_load16(a.rope_pf + (size_t)pos * hd + 4 * k, stage + ins * 1024);
+            }
+            wait_vm<0>();
+            __syncthreads();
+        }
+        const float* rtab = STAGED ? (const float*)stage : a.rope_pf;
         float ssq[TI][4];
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -51,9 +112,7 @@ __device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const P
                 float s = 0.f;
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) s += acc[i][j][q] * acc[i][j][q];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-                ssq[i][q] = s;
+                ssq[i][q] = row16_sum(s);
             }
         if (hd == 128) {   // a head spans two waves along n
             if (cl == 0) {
@@ -71,23 +130,31 @@ __device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const P
                     ssq[i][q] = nred[wn & ~1][rl] + nred[wn | 1][rl];
                 }
         }
-        const int half = a.rope_dims >> 1;
+        // RoPE from the prefill copy of the table (rope_pf): per position, per 32-pair block b, per c = 0..7 the cos
+        // then the sin of pairs 32 b + c + 8 j, j = 0..3 -- exactly this lane's four columns, two 16-byte loads per row
+        const int dbase = (n0 + wn * 64) % hd;   // 0 or 64
+        const int nb = hd / 64;
+        float kw[TJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) kw[j] = bf16_to_f32(G.knorm[dbase + 16 * j + cl]);
+        const float inv_hd = 1.f / (float)hd;
+        const bool odd = cl & 1;
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
-                const float rs = 1.f / sqrtf(ssq[i][q] / (float)hd + a.eps);
-                const int pos = a.start + (r < a.rows ? r : 0);
-                const float* tr = a.rope_tab + (size_t)pos * a.rope_dims;
+                // v_rsq_f32 (~1 ulp): far below the f16 rounding of the cached K; 1 / hd is exact (hd = 64 or 128)
+                const float rs = __builtin_amdgcn_rsqf(ssq[i][q] * inv_hd + a.eps);
+                const size_t trow = STAGED ? (size_t)(r - r0) : (size_t)a.start + (r < a.rows ? r : 0);
+                const float* tp = rtab + ((trow * nb + dbase / 64) * 8 + (cl >> 1)) * 8;
+                const float4 cs = *(const float4*)tp, sn = *(const float4*)(tp + 4);
+                const float cj[4] = {cs.x, cs.y, cs.z, cs.w}, sj[4] = {sn.x, sn.y, sn.z, sn.w};
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) {
-                    const int n = n0 + wn * 64 + 16 * j + cl;
-                    const int d = n % hd;
-                    const float v = acc[i][j][q] * rs * bf16_to_f32(G.knorm[d]);
-                    const float p = __shfl_xor(v, 1, 64);
-                    const float c = tr[d >> 1], sn = tr[half + (d >> 1)];
-                    acc[i][j][q] = (d & 1) ? v * c + p * sn : v * c - p * sn;
+                    const float v = acc[i][j][q] * rs * kw[j];
+                    const float pv = quad_xor1(v);   // the other element of the pair (columns 2m, 2m + 1)
+                    acc[i][j][q] = odd ? v * cj[j] + pv * sj[j] : v * cj[j] - pv * sj[j];
                 }
             }
     }
@@ -114,23 +181,52 @@ __device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const P
         }
         return;
     }
+    // Row stores: a 4 x 4 transpose inside each quad of lanes turns "4 rows of one column" into "4 consecutive
+    // columns of one row", so each lane writes one 8-byte (f16) or 16-byte (f32) piece instead of four 2- or 4-byte
+    // ones (measured: 2-byte stores made the K/V projection 25% slower than 8-byte ones).
+    const int t = cl & 3, cq = cl & ~3;
+    if (STAGED && G.epi != PF_F32 && a.kv_dtype == 0) {
+        if (G.epi == PF_CACHE_K && G.knorm) __syncthreads();   // every wave is done with the table rows in LDS
+        // f16 rows: the tile goes through LDS (row rl at rl * 2T bytes, 16-byte chunk k at slot k ^ (rl % 32)) and
+        // out as whole row segments, 16 bytes per lane (measured: 32-byte pieces of rows 4 KB apart wrote slower than
+        // the V cache's contiguous tiles)
+        constexpr int RB = 2 * T, NCH = T / 8;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                float o[4];
+                quad_transpose(acc[i][j], t, o);
+                const int rl = wm * TI * 16 + 16 * i + rq + t, cl4 = wn * 64 + 16 * j + cq;
+                *(uint2*)(stage + rl * RB + (((cl4 >> 3) ^ (rl & 31)) << 4) + ((cl4 >> 2) & 1) * 8) =
+                    make_uint2(pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3]));
+            }
+        __syncthreads();
+        for (int c = threadIdx.x; c < T * NCH; c += blockDim.x) {
+            const int rl = c / NCH, k = c % NCH, r = r0 + rl;
+            if (r < a.rows)
+                *(uint4*)((uint16_t*)G.out + (size_t)(a.start + r) * a.ld + n0 + 8 * k) =
+                    *(const uint4*)(stage + rl * RB + ((k ^ (rl & 31)) << 4));
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = r0 + wm * TI * 16 + 16 * i + rq + q;
+        for (int j = 0; j < TJ; ++j) {
+            float o[4];
+            quad_transpose(acc[i][j], t, o);
+            const int r = r0 + wm * TI * 16 + 16 * i + rq + t;
+            const int n = n0 + wn * 64 + 16 * j + cq;
             if (r >= a.rows) continue;
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int n = n0 + wn * 64 + 16 * j + cl;
-                const float v = acc[i][j][q];
-                if (G.epi == PF_F32) {
-                    ((float*)G.out)[(size_t)r * a.ld + n] = v;
-                } else {
-                    const size_t off = (size_t)(a.start + r) * a.ld + n;
-                    if (a.kv_dtype == 0) ((uint16_t*)G.out)[off] = f32_to_f16(v);
-                    else ((float*)G.out)[off] = v;
-                }
+            if (G.epi == PF_F32) {
+                *(float4*)((float*)G.out + (size_t)r * a.ld + n) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+                const size_t off = (size_t)(a.start + r) * a.ld + n;
+                if (a.kv_dtype == 0)
+                    *(uint2*)((uint16_t*)G.out + off) = make_uint2(pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3]));
+                else
+                    *(float4*)((float*)G.out + off) = make_float4(o[0], o[1], o[2], o[3]);
             }
         }
 }
@@ -242,32 +338,18 @@ __global__ __launch_bounds__(T * 2) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    prefill_epilogue<T, TI, TJ, NWN>(acc, a, G, r0, n0, wm, wn, lane, nred);
+    prefill_epilogue<T, TI, TJ, NWN, false>(acc, a, G, r0, n0, wm, wn, lane, nred, nullptr);
 }
 
 // ── 256 x 256 tiles from f16 operands, LDS-direct loads ──────────────────────────────────────────────────────────
 
-// LDS-direct load of 16 bytes per lane: lane l's 16 bytes from g land at LDS byte lds + 16 l (lds is wave-uniform,
-// passed in m0). Written as inline asm so that the compiler's wait bookkeeping leaves it alone: it cannot tell the
-// two stage buffers apart and would otherwise wait for every load in flight before any LDS read; the kernel waits
-// for these loads explicitly (wait_vm). Nothing else in the kernel uses m0.
-__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
-    const unsigned la =
-        __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((__attribute__((address_space(3))) void*)lds));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory", "m0");
-}
-
-// s_waitcnt with vmcnt = n and the other counters at their maxima (gfx9 encoding), and with lgkmcnt = 0 only
-template <int N> __device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 // A bare s_barrier: __syncthreads() adds a release fence, which makes the compiler wait for every LDS-direct load in
 // flight (vmcnt(0)) and would serialise the pipeline; the waits this kernel needs are explicit.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
+template <int GM>
 __global__ __launch_bounds__(512) void prefill_dma_kernel(PrefillArgs a) {
-    constexpr int TI = 8, TJ = 4, NWN = 4, GM = 8;
+    constexpr int TI = 8, TJ = 4, NWN = 4;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][256 * 128];   // [stage][A | B][row][128 B]
     __shared__ float nred[NWN][256];
 
@@ -353,8 +435,23 @@ __global__ __launch_bounds__(512) void prefill_dma_kernel(PrefillArgs a) {
         rd(fa0, fb0, buf ^ 1, fo0);
         mm(fa1, fb1);
     }
-    wait_vm<0>();
-    prefill_epilogue<256, TI, TJ, NWN>(acc, a, G, r0, n0, wm, wn, lane, nred);
+    wait_vm<0>();   // this wave's loads have landed; the barrier below covers every wave's
+    __syncthreads();
+    prefill_epilogue<256, TI, TJ, NWN, true>(acc, a, G, r0, n0, wm, wn, lane, nred, &lds[0][0][0]);
+}
+
+// Prefill copy of the interleaved-RoPE table: tab[p][i] = cos, tab[p][rdim/2 + i] = sin of pair i ->
+// out[p][b][c][0..3] = cos of pairs 32 b + c + 8 j (j = 0..3), out[p][b][c][4..7] = their sin (values copied as is).
+__global__ void rope_prefill_kernel(const float* __restrict__ tab, int P, int rdim, float* __restrict__ out) {
+    const int half = rdim >> 1;
+    const size_t n = (size_t)P * half;
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= n) return;
+    const int p = (int)(id / half), i = (int)(id % half);
+    const int b = i >> 5, w = i & 31, j = w >> 3, c = w & 7;
+    float* o = out + (size_t)p * rdim + (size_t)(b * 8 + c) * 8;
+    o[j] = tab[(size_t)p * rdim + i];
+    o[4 + j] = tab[(size_t)p * rdim + half + i];
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, size_t n4, uint2* __restrict__ y) {
@@ -383,15 +480,25 @@ hipError_t launch_prefill(const PrefillArgs& a, int nwg, hipStream_t st) {
     if (a.K % BK || a.N % T || a.rows < 1 || a.n_tiles != a.N / T || a.m_tiles != (a.rows + T - 1) / T ||
         a.ngroups < 1 || a.ngroups > PF_MAX_GROUPS)
         return hipErrorInvalidValue;
+    for (int i = 0; i < a.ngroups; ++i)
+        if (a.g[i].epi == PF_CACHE_K && a.g[i].knorm && (!a.rope_pf || a.rope_dims != a.hd || a.hd % 64))
+            return hipErrorInvalidValue;
     if (T == 256) {   // f16 A and f16 copies of every group's B; 64-k stages
         if (a.a_f32 || a.K % 64) return hipErrorInvalidValue;
         for (int i = 0; i < a.ngroups; ++i)
             if (!a.g[i].B16) return hipErrorInvalidValue;
-        prefill_dma_kernel<<<nwg, 512, 0, st>>>(a);
+        prefill_dma_kernel<1><<<nwg, 512, 0, st>>>(a);
     } else {
         if (a.a_f32) prefill_kernel<1, 128><<<nwg, 256, 0, st>>>(a);
         else prefill_kernel<0, 128><<<nwg, 256, 0, st>>>(a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hipStream_t st) {
+    if (rdim % 64 || P < 1) return hipErrorInvalidValue;
+    const size_t n = (size_t)P * (rdim / 2);
+    rope_prefill_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(tab, P, rdim, out);
     return hipGetLastError();
 }
 
