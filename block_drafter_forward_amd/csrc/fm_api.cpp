@@ -1148,6 +1148,7 @@ fm_status fm_context_append(fm_drafter* d, const float* taps, int32_t n, int32_t
     if (!d) return fail(FM_E_INVALID, "null handle");
     if (d->c.variant == FM_VARIANT_MTP) return fail(FM_E_INVALID, "the MTP head has no context append");
     if (!taps) return fail(FM_E_INVALID, "null taps");
+    if ((uintptr_t)taps & 15) return fail(FM_E_INVALID, "taps must be 16-byte aligned");
     if (n < 1) return fail(FM_E_INVALID, "n = %d < 1", n);
     if (start < 0 || start > d->length) return fail(FM_E_INVALID, "start %d outside [0, length %d]", start, d->length);
     if ((long long)start + n + d->c.block + 1 > d->c.max_ctx)

@@ -100,7 +100,9 @@ typedef struct fm_drafter fm_drafter;
 size_t fm_kv_bytes(const fm_config* cfg);
 
 /* Bytes of the device workspace the caller allocates for `cfg` (0 if cfg is invalid): activations, split-K
- * partials, the RoPE table, the zero-noise slot row, argmax scratch. Owned by the caller; reserved for one handle. */
+ * partials, the RoPE table (and its prefill copy), the zero-noise slot row, argmax scratch, prefill buffers (an f16
+ * copy of one append's taps; f16 copies of the context-projection and K/V weights, made at create).
+ * Owned by the caller; reserved for one handle. */
 size_t fm_workspace_bytes(const fm_config* cfg);
 
 /* Create a drafter. `names` / `ptrs` is a table of n_weights (name, device pointer) pairs naming every tensor the
@@ -108,8 +110,10 @@ size_t fm_workspace_bytes(const fm_config* cfg);
  * Borrowed: the library keeps the pointers, never frees them; they must outlive the handle. kv_cache and
  * workspace must be at least fm_kv_bytes / fm_workspace_bytes and 256-byte aligned.
  * Enqueues the create-time work on `stream`: clearing the workspace's counters, the RoPE table (angles in f64,
- * stored f32) and, for the flow-map, the zero-noise slot input x_embed(state_norm(mean row of lm_head)) + bias
- * (flashmap_drafter.js, init). Context length starts at 0.
+ * stored f32, and its permuted prefill copy), f16 copies of the context-projection and per-layer K/V weights
+ * (flow-map and KV-inject) and, for the flow-map, the zero-noise slot input x_embed(state_norm(mean row of
+ * lm_head)) + bias (flashmap_drafter.js, init). The weights must keep their values while the handle lives.
+ * Context length starts at 0.
  * Errors: FM_E_INVALID (null pointer, dim % heads, sizes not multiples of 32/256, block > 16 ...),
  * FM_E_MISSING_WEIGHT, FM_E_UNSUPPORTED, FM_E_HIP. */
 fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* names, const void* const* ptrs,
@@ -120,7 +124,8 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
  *   flow-map   c = RMSNorm(fc(taps); hidden_norm), per layer K = RoPE(headRMSNorm(k_proj c; k_norm)), V = v_proj c
  *   KV-inject  c = RMSNorm(W_c taps; ctx_norm), per layer K = W_k RMSNorm(c; attn_norm), V likewise
  * written to the cache (f16 or f32). Any start <= current length may be rewritten (a rewind); the length becomes
- * start + n. Errors: FM_E_INVALID (n < 1, start < 0, start > length, null taps, MTP handle),
+ * start + n. taps must be 16-byte aligned (it is read in 16-byte pieces).
+ * Errors: FM_E_INVALID (n < 1, start < 0, start > length, null or misaligned taps, MTP handle),
  * FM_E_CONTEXT_FULL when start + n + block + 1 > max_ctx (extendContext's own check). */
 fm_status fm_context_append(fm_drafter* d, const float* taps, int32_t n, int32_t start, void* stream);
 
