@@ -165,7 +165,7 @@ def test_flashmap_prefill_and_draft(flashmap):
 
 def test_flashmap_ragged_prefill(flashmap):
     """A 1000-row prefill: the fusion GEMM on 128-row tiles, the 12 K/V projections on 256-row tiles whose last
-    row block is ragged (1000 = 3 x 256 + 232)."""
+    row block is ragged (1000 = 3 x 256 + 232); then a rewinding append of 600 rows at an unaligned start."""
     from block_drafter_forward_amd import fm as fmod
     cfg, _, _, o0 = flashmap
     d = fmod.Drafter(cfg, fmod.upload_weights(o0.raw))
@@ -186,6 +186,24 @@ def test_flashmap_ragged_prefill(flashmap):
                                              what=f"ragged V{l}"))
     assert d.length == n
     _say(f"flashmap ragged prefill worst row err {worst:.2e}")
+    # a rewinding 600-row append at start 301 (not a multiple of 4 or 32): the K/V projections still run on
+    # 256-row tiles, RoPE positions start at 301, V lands in the 32-position tiles 4 positions at a time only where
+    # they are aligned; rows before the start keep their values
+    s2, n2 = 301, 600
+    _say(f"flashmap: {n2}-row append at start {s2}")
+    t2 = gen.taps(cfg, "ragged-rewind", n2)
+    o.context_append(t2, s2)
+    d.fm_context_append(torch.from_numpy(t2).cuda(), s2)
+    torch.cuda.synchronize()
+    rows = np.r_[290:312, 316:324, 500:515, s2 + n2 - 24:s2 + n2]
+    worst = 0.0
+    for l in range(cfg["layers"]):
+        worst = max(worst, assert_rows_close(d.kv_layer(l, 0)[rows].float().cpu().numpy(), o.K[l][rows],
+                                             what=f"rewind K{l}"))
+        worst = max(worst, assert_rows_close(d.kv_layer(l, 1)[rows].float().cpu().numpy(), o.V[l][rows],
+                                             what=f"rewind V{l}"))
+    assert d.length == s2 + n2
+    _say(f"flashmap unaligned append worst row err {worst:.2e}")
 
 
 def test_longctx_workload(flashmap):
