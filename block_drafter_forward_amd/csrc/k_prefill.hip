@@ -233,8 +233,10 @@ __device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const P
 
 // Tile T x T (T = 128: 4 waves as 2 x 2 of 64 x 64; T = 256: 8 waves as 2 x 4 of 128 x 64). Every thread stages
 // 16 k-values of one A row and one B row per k-stage; rows past the end of A are clamped (their results dropped).
+// Two work-groups per CU (2 waves per SIMD, <= 256 registers a wave): without the bound the compiler keeps the
+// accumulators in AGPRs next to 151 VGPRs and the kernel runs at one wave per SIMD, 25% slower.
 template <int AF32, int T>
-__global__ __launch_bounds__(T * 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(T * 2, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int BM = T, BN = T, NWN = T / 64, TI = T == 128 ? 4 : 8, TJ = 4;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];

@@ -240,8 +240,10 @@ __device__ __forceinline__ void rs_compute_q8(const RsStageQ8<NT>& st, uint4* ld
 // UP = 1: the wave's whole k-range (SKC == KW steps) is loaded at once, then multiplied -- every byte of the wave
 // in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
 // stage i computes), with the last pair peeled so the loop body carries no conditions.
+// A single Q8_0 matrix fits two work-groups per CU (<= 256 registers a wave, no scratch); without the bound the
+// compiler spends AGPRs and runs one wave per SIMD. Two matrices at once would spill, so they keep one.
 template <int NT, int WT, int UP, int SKC>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skinny_kernel(SkinnyArgs a) {
     const int bid = blockIdx.x;
     int gi = 0;
 #pragma unroll 1
