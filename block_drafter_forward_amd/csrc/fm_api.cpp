@@ -383,8 +383,11 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
     a.chunk = attn_chunk_size(c.head_dim, c.kv_dtype, ntot, c.heads);
     const int tc = (ntot + a.chunk - 1) / a.chunk;
     if (c.kv_dtype == FM_KV_F16) {
-        // one run of 32-key steps per wave; long contexts lengthen the runs to keep ~4 waves per CU
-        a.cpw = std::max(1, tc * c.heads / (4 * TARGET_WGS));
+        // the fewest 32-key steps per wave that keep the launch within one round of work-groups (one per CU): a
+        // second partial round costs more than the longer runs (measured at L = 8193: 272 work-groups 791 us per
+        // draft, 208 work-groups 759 us); more runs also make the merge read more partials
+        a.cpw = 1;
+        while (a.cpw < tc && c.heads * (((tc + a.cpw - 1) / a.cpw + 3) / 4) > TARGET_WGS) ++a.cpw;
         a.nchunks = ((tc + a.cpw - 1) / a.cpw + 3) / 4 * 4;
     } else {
         a.cpw = 1;
