@@ -47,9 +47,6 @@ bool kw_ok(int kw) {
            kw == 16 || (kw > 16 && kw % 2 == 0);
 }
 
-// k-split of a partial-output skinny GEMM (at most 8 slabs, the consumers' limit). Preference: enough work-groups
-// (tiles * S >= TARGET_WGS) with a per-wave range that is a whole number of row-staged chunks (KW % 8 == 0);
-// then enough work-groups with any supported range; else the largest supported S.
 // k-split of a projection whose slabs the attention kernel sums itself (q, or the self-attention's q|k|v): the
 // largest S <= QKV_SLABS leaving each wave whole row-staged chunks (4 k-steps); measured on MI355X this streams a
 // 2048 x 2048 weight ~20% faster than the unsplit 128 work-groups.
@@ -60,13 +57,19 @@ int pick_qsplit(int K) {
     return 1;
 }
 
-int pick_split(int M_total, int K) {
+// k-split of a partial-output skinny GEMM (at most 8 slabs, the consumers' limit). Preference: enough work-groups
+// (tiles * S >= TARGET_WGS) with a per-wave range that is a whole number of row-staged chunks (KW % 8 == 0);
+// then enough work-groups with any supported range; else the largest supported S. Q8_0 weights (q8): the
+// single-matrix kernel runs two work-groups per CU, so twice the work-groups are wanted, and only whole chunks.
+int pick_split(int M_total, int K, bool q8 = false) {
+    const int target = q8 ? 2 * TARGET_WGS : TARGET_WGS;
     const int n4 = K / 128, tiles = M_total / 16;
     int any_enough = -1, largest = -1;
     for (int S = 1; S <= std::min(8, n4); ++S) {
         if (n4 % S || !kw_ok(n4 / S)) continue;
+        if (q8 && (n4 / S) % 8) continue;   // the row-staged Q8_0 path takes whole chunks of 8 k-steps
         largest = S;
-        if (tiles * S >= TARGET_WGS) {
+        if (tiles * S >= target) {
             if ((n4 / S) % 8 == 0) return S;
             if (any_enough < 0) any_enough = S;
         }
@@ -95,7 +98,8 @@ int kmax_frag(const fm_config& c) {
 
 int part_need(const fm_config& c) {   // floats per split slab row-set: max over partial uses of S * M
     int need = 0;
-    auto use = [&](int M, int K) { need = std::max(need, pick_split(M, K) * M); };
+    const bool q8 = c.wtype == FM_W_Q8_0;
+    auto use = [&](int M, int K) { need = std::max(need, pick_split(M, K, q8) * M); };
     const int D = c.dim, Ht = c.target_dim;
     if (c.variant == FM_VARIANT_FLOWMAP) {
         use(D, c.n_taps * Ht); use(D, Ht); use(D, D); use(D, c.ffn);
@@ -299,7 +303,8 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     int tiles_total = 0;
     for (auto& g : gs) tiles_total += g.M / 16;
     int S = 1;
-    if (mode == SK_PARTIAL) S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K);
+    if (mode == SK_PARTIAL)
+        S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K, d->c.wtype == FM_W_Q8_0);
     if (S < 1 || (K / 128) % S || !kw_ok(K / 128 / S))
         return fail(FM_E_UNSUPPORTED, "skinny: no supported k-split for K %d (S %d)", K, S);
     a.ngroups = (int)gs.size();
