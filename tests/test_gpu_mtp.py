@@ -79,3 +79,29 @@ def test_mtp_bad_rows():
     with pytest.raises(fm.FmError) as ex:
         d.fm_context_append(e, 0)
     assert ex.value.status == fm.FM_E_INVALID
+
+
+def test_mtp_lm_head_row_scales():
+    """The Q8_0 lm_head alone on rows whose magnitudes span 1e-30 .. 1e30 (each row is brought into the f16 range
+    by a power of two inside the library): logits within the row tolerance, tokens by the top-2 gap rule."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL
+    W = gen.make_weights(cfg)
+    d = fm.Drafter(cfg, fm.upload_weights(W))
+    o = mtp.MTPOracle(cfg, W)
+    rng = np.random.default_rng(7)
+    scales = np.array([1.0, 1e-30, 1e30, 3e-5, 7e4, 1.0, 0.5, 2.0 ** 20], dtype=np.float64)
+    h = (rng.standard_normal((8, cfg["target_dim"])) * scales[:, None]).astype(np.float32)
+    h[5, ::7] = 0.0                                   # a row with exact zeros in it
+    for M in (8, 3):
+        _say(f"lm_head row scales: M={M}")
+        hid = torch.from_numpy(h[:M].copy()).cuda()
+        tok = torch.empty(M, dtype=torch.int32, device="cuda")
+        logits = torch.empty(M, cfg["vocab"], dtype=torch.float32, device="cuda")
+        d.fm_lm_argmax(hid, M, tok, logits)
+        torch.cuda.synchronize()
+        _, z = o.lm_argmax(h[:M].astype(np.float64))
+        assert_rows_close(logits.cpu().numpy(), z, what=f"logits M={M}")
+        assert_tokens_match(tok.cpu().numpy(), z)
