@@ -40,6 +40,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int TMAX = 16;          // rows of one skinny activation matrix
 constexpr int QKV_SLABS = 4;      // split-K slabs the attention kernels sum while building q (and k, v)
 constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
+constexpr int PF_SPLIT_WGS = 512; // a k-split prefill launch stays within one round (two 128-tile work-groups per CU)
+constexpr int PF_SPLIT_ROWS = 4096;  // prefill context rows kept for k-split slabs
 
 // k-steps per wave the skinny kernel is built for: up to 16 loaded at once, longer ranges in even stages.
 bool kw_ok(int kw) {
@@ -88,6 +90,7 @@ struct Plan {
     int nchunk_max;
     size_t qkv_floats;
     int colR;
+    int pctx_rows;           // rows of the prefill context buffer (>= max_ctx)
 };
 
 int kmax_frag(const fm_config& c) {
@@ -145,7 +148,10 @@ Plan make_plan(const fm_config& c) {
     p.cmean = take((size_t)c.target_dim * 4);
     p.hc = take((size_t)TMAX * D * 4);
     const bool prefill = c.variant != FM_VARIANT_MTP;
-    p.pctx = take(prefill ? (size_t)c.max_ctx * D * 4 : 0);
+    // prefill context rows; small prefills split the context projection's k-range, whose partial slabs need
+    // up to PF_SPLIT_ROWS rows
+    p.pctx_rows = std::max(c.max_ctx, PF_SPLIT_ROWS);
+    p.pctx = take(prefill ? (size_t)p.pctx_rows * D * 4 : 0);
     p.pctxn = take(prefill ? (size_t)(c.variant == FM_VARIANT_KVINJECT ? c.layers : 1) * c.max_ctx * D * 2 : 0);
     // f16 copies of the prefill weights (the context projection, then K and V of every layer), made at create, and
     // of the taps of one append: the 256-tile prefill GEMM streams f16 operands straight into LDS
@@ -420,6 +426,12 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
 // ── flow-map ────────────────────────────────────────────────────────────────────────────────────
 // A operand of the context projection: the f32 taps as they are for 128-tiles (rounded to f16 on the way into LDS),
 // an f16 copy for 256-tiles (which stream f16 operands straight into LDS; same rounding).
+// The context projection [n][K] x [K][D]: 128-tiles that fill less than one round of work-groups (two per CU) split
+// their k-range over up to 4 work-groups per tile; the slabs go to ctx + s * n * D and the RMSNorm that follows
+// sums them. Returns the slab count.
+fm_status prefill_context(fm_drafter* d, const float* taps, int n, const uint16_t* w, const uint16_t* w16, float* ctx,
+                          int* nslab, hipStream_t st);
+
 fm_status prefill_taps(fm_drafter* d, const float* taps, int n, PrefillArgs& a, hipStream_t st) {
     const size_t KT = d->tap_width();
     if (prefill_tile(n, d->c.dim, 1) == 256) {
@@ -431,6 +443,32 @@ fm_status prefill_taps(fm_drafter* d, const float* taps, int n, PrefillArgs& a, 
         a.A = taps;
         a.a_f32 = 1;
     }
+    return FM_OK;
+}
+
+fm_status prefill_context(fm_drafter* d, const float* taps, int n, const uint16_t* w, const uint16_t* w16, float* ctx,
+                          int* nslab, hipStream_t st) {
+    const int D = d->c.dim, KT = (int)d->tap_width();
+    PrefillArgs a{};
+    a.ngroups = 1;
+    a.g[0] = PrefillGroup{nullptr, w, w16, nullptr, ctx, PF_F32, 0};
+    CHK(prefill_taps(d, taps, n, a, st));
+    a.rows = n;
+    a.N = D;
+    a.K = KT;
+    a.ld = D;
+    const int tile = prefill_tile(n, D, 1);
+    a.m_tiles = (n + tile - 1) / tile;
+    a.n_tiles = D / tile;
+    const int tiles = a.m_tiles * a.n_tiles;
+    int ks = 1;
+    if (tile == 128)
+        while (ks < 4 && 2 * ks * tiles <= PF_SPLIT_WGS && KT % (2 * ks * 32) == 0 && 2 * ks * n <= d->p.pctx_rows)
+            ks *= 2;
+    a.ksplit = ks;
+    a.slab_stride = (long long)n * D;
+    HIPCHK(launch_prefill(a, tiles * ks, st));
+    *nslab = ks;
     return FM_OK;
 }
 
@@ -518,21 +556,9 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     // prefill: MFMA GEMMs
     float* ctx = d->at<float>(d->p.pctx);
     uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
-    {
-        PrefillArgs a{};
-        a.ngroups = 1;
-        a.g[0] = PrefillGroup{nullptr, d->B("fc.weight"), d->w16_ctx(), nullptr, ctx, PF_F32, 0};
-        CHK(prefill_taps(d, taps, n, a, st));
-        a.rows = n;
-        a.N = D;
-        a.K = KT;
-        a.ld = D;
-        const int tile = prefill_tile(n, D, 1);
-        a.m_tiles = (n + tile - 1) / tile;
-        a.n_tiles = D / tile;
-        HIPCHK(launch_prefill(a, a.m_tiles * a.n_tiles, st));
-    }
-    HIPCHK(launch_rms_f16(ctx, n, D, d->B("hidden_norm.weight"), c.rms_eps, ctxn, st));
+    int nslab = 1;
+    CHK(prefill_context(d, taps, n, d->B("fc.weight"), d->w16_ctx(), ctx, &nslab, st));
+    HIPCHK(launch_rms_f16(ctx, n, D, d->B("hidden_norm.weight"), c.rms_eps, ctxn, nslab, (long long)n * D, st));
     for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
         PrefillArgs a{};
         const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
@@ -814,24 +840,19 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     }
     float* ctx = d->at<float>(d->p.pctx);
     uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
-    {
-        PrefillArgs a{};
-        a.ngroups = 1;
-        a.g[0] = PrefillGroup{nullptr, d->B("W_c"), d->w16_ctx(), nullptr, ctx, PF_F32, 0};
-        CHK(prefill_taps(d, taps, n, a, st));
-        a.rows = n;
-        a.N = D;
-        a.K = KT;
-        a.ld = D;
-        const int tile = prefill_tile(n, D, 1);
-        a.m_tiles = (n + tile - 1) / tile;
-        a.n_tiles = D / tile;
-        HIPCHK(launch_prefill(a, a.m_tiles * a.n_tiles, st));
-    }
-    // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32), then per layer RMSNorm(H_ctx; attn_norm) -> f16
+    int nslab = 1;
+    CHK(prefill_context(d, taps, n, d->B("W_c"), d->w16_ctx(), ctx, &nslab, st));
+    // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32; split slabs summed into slab 0's rows), then per layer
+    // RMSNorm(H_ctx; attn_norm) -> f16
     {
         RowArgs r = rows_base(d, D, n);
-        r.x = ctx;
+        if (nslab > 1) {
+            r.part = ctx;
+            r.S = nslab;
+            r.part_stride = (long long)n * D;
+        } else {
+            r.x = ctx;
+        }
         r.norm = ROW_RMS;
         r.w_bf16 = d->B("ctx_norm");
         r.eps = c.rms_eps;
@@ -840,7 +861,8 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
         CHK(rows(r, st));
     }
     for (int i = 0; i < c.layers; ++i)
-        HIPCHK(launch_rms_f16(ctx, n, D, d->B(BB(i, "attn_norm")), c.rms_eps, ctxn + (size_t)i * c.max_ctx * D, st));
+        HIPCHK(launch_rms_f16(ctx, n, D, d->B(BB(i, "attn_norm")), c.rms_eps, ctxn + (size_t)i * c.max_ctx * D, 1, 0,
+                              st));
     for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
         PrefillArgs a{};
         const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);

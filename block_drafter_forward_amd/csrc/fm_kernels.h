@@ -243,6 +243,8 @@ struct PrefillArgs {
     int kv_dtype;
     int vt_ld;             // PF_CACHE_VT: dims per 32-position tile (the cache row width)
     int m_tiles, n_tiles;
+    int ksplit;            // > 1 (128-tiles, PF_F32 groups only): the k-range is split over ksplit work-groups per
+    long long slab_stride; //   tile; split s writes its partial product to out + s * slab_stride (floats)
 };
 // Tile edge (128 or 256) the launcher uses for rows x N x ngroups; the host sizes m_tiles, n_tiles and the
 // groups' tile_begin with it. 256-tiles need f16 A (a_f32 == 0), every group's B16, and K % 64 == 0.
@@ -255,6 +257,7 @@ hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hi
 hipError_t launch_f32_to_f16(const float* x, size_t n, uint16_t* y, hipStream_t st);
 hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStream_t st);
 
-// Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context).
-hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out,
-                          hipStream_t st);
+// Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context); the rows are the sum of nslab (1, 2 or 4)
+// partial slabs slab_stride floats apart.
+hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, int nslab,
+                          long long slab_stride, hipStream_t st);

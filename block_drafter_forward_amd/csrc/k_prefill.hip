@@ -245,16 +245,22 @@ __global__ __launch_bounds__(T * 2, 2) void prefill_kernel(PrefillArgs a) {
     int lin = blockIdx.x;
     const int total = gridDim.x;
     if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    // k split over work-groups: split s takes k in [s K / ksplit, (s + 1) K / ksplit) of every tile
+    const int ks = a.ksplit > 1 ? a.ksplit : 1;
+    const int split = lin / (total / ks);
+    lin -= split * (total / ks);
     int gi = 0;
 #pragma unroll 1
     for (int i = 1; i < a.ngroups; ++i)
         if (lin >= a.g[i].tile_begin) gi = i;
-    const PrefillGroup& G = a.g[gi];
+    PrefillGroup G = a.g[gi];
+    if (ks > 1) G.out = (float*)G.out + (size_t)split * a.slab_stride;
     const int local = lin - G.tile_begin;
     const int mt = local / a.n_tiles, nt = local - mt * a.n_tiles;
     const int r0 = mt * BM, n0 = nt * BN;
     const void* Ap = G.A ? G.A : a.A;
-    const int K = a.K;
+    const int K = a.K;               // row stride of A and B
+    const int kb = split * (K / ks);  // first k of this split
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / NWN, wn = wave % NWN;
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(T * 2, 2) void prefill_kernel(PrefillArgs a) {
         uint4 rah[2], rb[2];
     };
     auto gload = [&](PStage& r, int kt) {
-        const int k = kt * BK + kofs;
+        const int k = kb + kt * BK + kofs;
         if constexpr (AF32) {
             const float4* p = (const float4*)((const float*)Ap + (size_t)arow * K + k);
 #pragma unroll
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(T * 2, 2) void prefill_kernel(PrefillArgs a) {
 
     // two k-stages in flight in registers while one multiplies from LDS; past the end a stage re-reads the
     // last one (no conditional load)
-    const int nk = K / BK;
+    const int nk = K / ks / BK;
     PStage s0, s1;
     gload(s0, 0);
     gload(s1, min(1, nk - 1));
@@ -482,6 +488,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int nwg, hipStream_t st) {
     if (a.K % BK || a.N % T || a.rows < 1 || a.n_tiles != a.N / T || a.m_tiles != (a.rows + T - 1) / T ||
         a.ngroups < 1 || a.ngroups > PF_MAX_GROUPS)
         return hipErrorInvalidValue;
+    if (a.ksplit > 1) {   // 128-tiles writing f32 partial slabs; nwg = tiles x ksplit
+        if (T != 128 || a.K % (a.ksplit * BK) || nwg % a.ksplit || a.slab_stride < (long long)a.rows * a.ld)
+            return hipErrorInvalidValue;
+        for (int i = 0; i < a.ngroups; ++i)
+            if (a.g[i].epi != PF_F32) return hipErrorInvalidValue;
+    }
     for (int i = 0; i < a.ngroups; ++i)
         if (a.g[i].epi == PF_CACHE_K && a.g[i].knorm && (!a.rope_pf || a.rope_dims != a.hd || a.hd % 64))
             return hipErrorInvalidValue;

@@ -205,9 +205,9 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
     if (i < n) p[i] = v;
 }
 
-template <int NS>
+template <int NS, int NSLAB>
 __global__ __launch_bounds__(256) void rms_f16_kernel(const float* x, int D, const uint16_t* w, float eps,
-                                                      uint16_t* out) {
+                                                      uint16_t* out, long long slab_stride) {
     const int t = blockIdx.x;
     const int nslot = D >> 3;
     __shared__ float red[4];
@@ -217,10 +217,15 @@ __global__ __launch_bounds__(256) void rms_f16_kernel(const float* x, int D, con
     for (int j = 0; j < NS; ++j) {
         const int slot = threadIdx.x + j * 256;
         if (slot < nslot) {
-            const float4* p = (const float4*)(x + (size_t)t * D + slot * 8);
-            float4 a0 = p[0], a1 = p[1];
-            v[j][0] = a0.x; v[j][1] = a0.y; v[j][2] = a0.z; v[j][3] = a0.w;
-            v[j][4] = a1.x; v[j][5] = a1.y; v[j][6] = a1.z; v[j][7] = a1.w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < NSLAB; ++sl) {   // partial slabs summed in a fixed order
+                const float4* p = (const float4*)(x + (size_t)sl * slab_stride + (size_t)t * D + slot * 8);
+                const float4 a0 = p[0], a1 = p[1];
+                v[j][0] += a0.x; v[j][1] += a0.y; v[j][2] += a0.z; v[j][3] += a0.w;
+                v[j][4] += a1.x; v[j][5] += a1.y; v[j][6] += a1.z; v[j][7] += a1.w;
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) q += v[j][e] * v[j][e];
         }
@@ -311,13 +316,26 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, hipStream_t st) {
+template <int NSLAB>
+hipError_t launch_rms_f16_s(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out,
+                            long long slab_stride, hipStream_t st) {
     const int ns = (D / 8 + 255) / 256;
     switch (ns) {
-    case 1: rms_f16_kernel<1><<<n, 256, 0, st>>>(x, D, w, eps, out); break;
-    case 2: rms_f16_kernel<2><<<n, 256, 0, st>>>(x, D, w, eps, out); break;
-    case 3: rms_f16_kernel<3><<<n, 256, 0, st>>>(x, D, w, eps, out); break;
+    case 1: rms_f16_kernel<1, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride); break;
+    case 2: rms_f16_kernel<2, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride); break;
+    case 3: rms_f16_kernel<3, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, int nslab,
+                          long long slab_stride, hipStream_t st) {
+    if (nslab > 1 && slab_stride < (long long)n * D) return hipErrorInvalidValue;
+    switch (nslab) {
+    case 1: return launch_rms_f16_s<1>(x, n, D, w, eps, out, 0, st);
+    case 2: return launch_rms_f16_s<2>(x, n, D, w, eps, out, slab_stride, st);
+    case 4: return launch_rms_f16_s<4>(x, n, D, w, eps, out, slab_stride, st);
+    default: return hipErrorInvalidValue;
+    }
 }
