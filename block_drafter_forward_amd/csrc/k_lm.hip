@@ -405,6 +405,10 @@ __global__ __launch_bounds__(NW * 64) void lm_argmax_ws_kernel(LmArgs a) {
     auto load = [&](Regs& r, int ch) {
         if constexpr (WT == 0) ws_load<NW>(r, a, v0, ch, tid);
         else ws_load_q8<NW>(r, a, v0, ch, tid);
+        // each chunk's loads stay together, in the prologue as in the loop: the wait before a chunk is staged is
+        // the stricter of the loop header's two entries, and a prologue that interleaves the two chunks' loads
+        // makes it wait for the next chunk's loads as well (vmcnt(1) instead of vmcnt(12))
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto stage = [&](const Regs& r, int buf) {
         if constexpr (WT == 0) ws_stage<NW>(r, alds, blds_all[buf], tid);
