@@ -11,6 +11,11 @@ MTPHead.forward and the WGSL kernels it dispatches (WG_NORM, WG_Q8, WG_QKPREP, W
 
 Each q head's projection is 512 wide: [query 256 | gate 256].  Row m sits at position pos0 + m, its K/V are
 written to the cache there, and it attends to keys kv_lo .. pos0 + m.  The attention scale is 1/sqrt(256).
+
+Chained depth (the file header: "Depth N chains the head"; MTPRunner's draft loop): every further single-row pass
+takes the embedding row of the previous draft token and the previous pass's output h' = shared_head_norm(x), one
+position later.  The embedding row of a token is the dequantised row of the Q8_0 lm_head table (the pages use the
+target's tied token table; the build's reading).
 """
 from __future__ import annotations
 
@@ -71,3 +76,24 @@ class MTPOracle:
     def lm_argmax(self, hidden: np.ndarray):
         z = P.linear(hidden, self.w("lm_head"))
         return P.argmax_rows(z), z
+
+    def embed_row(self, tok: int) -> np.ndarray:
+        """The embedding row of a token: row tok of the dequantised Q8_0 lm_head table (d * q per element)."""
+        return self.w("lm_head")[int(tok)]
+
+    def chain(self, tok0: int, h: np.ndarray, steps: int, pos: int, kv_lo: int = 0, follow=None):
+        """steps chained single-row passes from draft token tok0 and hidden row h (MTPRunner: drafts[d] comes from a
+        pass over [drafts[d - 1]] with the previous pass's output as h, at the next position).  Pass i runs at
+        position pos + i.  follow (optional): tokens to chain instead of this oracle's own argmax (a device run that
+        took the other side of a near-tie).  Returns (tokens [steps], hidden rows [steps][H], logits [steps][V])."""
+        toks, hs, zs = [], [], []
+        t, hp = int(tok0), np.asarray(h, np.float64)
+        for i in range(steps):
+            out = self.forward(self.embed_row(t)[None, :], hp[None, :], pos + i, kv_lo)
+            nt, z = self.lm_argmax(out)
+            t = int(nt[0]) if follow is None else int(follow[i])
+            toks.append(int(nt[0]))
+            hs.append(out[0])
+            zs.append(z[0])
+            hp = out[0]
+        return np.array(toks), np.stack(hs), np.stack(zs)

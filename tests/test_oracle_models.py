@@ -277,6 +277,50 @@ def test_mtp_kv_lo_hides_earlier_rows():
     assert np.max(np.abs(c - a)) > 1e-6
 
 
+def test_mtp_embed_row_is_scale_times_code():
+    # Q8_0: every element of a table row is its block's f16 scale times its int8 code (closed form, element by
+    # element, without the oracle's vectorised decode)
+    cfg, W, o = _mtp()
+    codes, scales = W["lm_head"]
+    for tok in (0, 7, cfg["vocab"] - 1):
+        row = o.embed_row(tok)
+        for k in range(cfg["dim"]):
+            d = float(np.frombuffer(np.uint16(scales[tok, k // 32]).tobytes(), dtype=np.float16)[0])
+            assert row[k] == d * int(codes[tok, k])
+
+
+def test_mtp_chain_equals_one_pass_over_the_chained_rows():
+    # Chained depth: step i runs at pos + i on (E[token i-1], h'_(i-1)). By causality and the cache rows each step
+    # writes, one M = steps pass over those same inputs gives the same rows, so the chain's plumbing (positions,
+    # which h and which token feed the next step, the cache rows it leaves) is pinned by the batched forward.
+    cfg, W, o = _mtp()
+    pos, steps, kv_lo = 7, 3, 1
+    kc, vc = gen.mtp_cache_rows(cfg, pos)
+    o.set_cache_rows(kc, vc)
+    _, h = gen.mtp_inputs(cfg, 1)
+    toks, hs, zs = o.chain(5, h[0], steps, pos, kv_lo)
+    assert toks.shape == (steps,) and hs.shape == (steps, cfg["dim"]) and zs.shape == (steps, cfg["vocab"])
+    assert np.array_equal(toks, np.argmax(zs, axis=1))
+    chain_K = o.Kc[pos:pos + steps].copy()
+    o2 = mtp.MTPOracle(cfg, W)
+    o2.set_cache_rows(kc, vc)
+    e_in = np.stack([o2.embed_row(t) for t in [5, *toks[:-1]]])
+    h_in = np.concatenate([h[:1], hs[:-1]])
+    batch = o2.forward(e_in, h_in, pos, kv_lo)
+    assert np.allclose(batch, hs, atol=1e-12)
+    assert np.allclose(o2.Kc[pos:pos + steps], chain_K, atol=1e-12)
+    # follow: chaining other tokens changes every later step, and re-chaining its own tokens changes nothing
+    o3 = mtp.MTPOracle(cfg, W)
+    o3.set_cache_rows(kc, vc)
+    t3, h3, _ = o3.chain(5, h[0], steps, pos, kv_lo, follow=toks)
+    assert np.array_equal(t3, toks) and np.array_equal(h3, hs)
+    o4 = mtp.MTPOracle(cfg, W)
+    o4.set_cache_rows(kc, vc)
+    other = (toks + 1) % cfg["vocab"]
+    _, h4, _ = o4.chain(5, h[0], steps, pos, kv_lo, follow=other)
+    assert np.array_equal(h4[0], hs[0]) and np.max(np.abs(h4[1] - hs[1])) > 1e-6
+
+
 def test_mtp_shapes_match_page_tensor_map():
     # The page's tensor map gives [offset, type, ne0 = K, ne1 = N]; a Q8_0 tensor occupies N * K/32 * 34 bytes, and
     # consecutive offsets must agree with those sizes for our [N][K] shapes.
