@@ -194,6 +194,20 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
         ms = _time_ms(torch, _graph_of(torch, mstep), 5, reps)
         rows[f"mtp_pass_M{M}"] = _hbm_row(f"MTP pass, M = {M} rows + Q8_0 lm_head argmax", ms,
                                           mw + 2 * (pos0 + M) * NKV * HD * 4, "passes/s")
+    # chained depth: 3 single-row passes, each on the previous draft's table row and h' (fm_mtp_chain)
+    steps = 3
+    posc = mc["max_ctx"] - steps
+    _, h1 = gen.mtp_inputs(mc, 1)
+    h1 = torch.from_numpy(h1[0].copy()).cuda()
+    tc = torch.tensor([7] + [0] * steps, dtype=torch.int32, device="cuda")
+    hc = torch.empty(steps, H, dtype=torch.float32, device="cuda")
+
+    def cstep():
+        dm.fm_mtp_chain(tc, h1, steps, posc, 0, hc)
+    ms = _time_ms(torch, _graph_of(torch, cstep), 5, reps)
+    cbytes = sum(mw + 2 * (posc + i + 1) * NKV * HD * 4 for i in range(steps))
+    rows["mtp_chain_3"] = _hbm_row("MTP chained depth: 3 single-row passes (table row gather + pass + Q8_0 lm_head "
+                                   "argmax each)", ms, cbytes, "chains/s")
     del dm, Wm
     return rows
 

@@ -82,7 +82,7 @@ int pick_split(int M_total, int K, bool q8 = false) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -166,6 +166,8 @@ Plan make_plan(const fm_config& c) {
     p.apart = take(fmv ? p.part_floats * 4 : 0);
     p.afrag = take(fmv ? (size_t)c.target_dim * 64 : 0);
     p.cfrag = take(fmv ? (size_t)c.dim * 64 : 0);
+    // MTP chained passes: the embedding row of the previous draft token
+    p.echain = take(c.variant == FM_VARIANT_MTP ? (size_t)c.dim * 4 : 0);
     p.total = off;
     return p;
 }
@@ -1236,6 +1238,39 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     a.logits = logits;
     a.perm = d->perm;
     HIPCHK(launch_lm_argmax(a, q8 ? 1 : 0, st));
+    return FM_OK;
+}
+
+fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t steps, int32_t pos, int32_t kv_lo,
+                       float* hidden_out, void* stream) {
+    g_err.clear();
+    if (!d || !tokens || !h || !hidden_out) return fail(FM_E_INVALID, "null argument");
+    const auto& c = d->c;
+    if (c.variant != FM_VARIANT_MTP) return fail(FM_E_INVALID, "fm_mtp_chain needs an MTP drafter");
+    if (steps < 1) return fail(FM_E_INVALID, "steps %d < 1", steps);
+    if (pos < 0 || kv_lo < 0 || kv_lo > pos) return fail(FM_E_INVALID, "need 0 <= kv_lo (%d) <= pos (%d)", kv_lo, pos);
+    if ((long long)pos + steps > c.max_ctx)
+        return fail(FM_E_CONTEXT_FULL, "pos %d + steps %d > KV cache rows %d", pos, steps, c.max_ctx);
+    hipStream_t st = (hipStream_t)stream;
+    const int H = c.dim;
+    float* e = d->at<float>(d->p.echain);
+    const bool q8 = c.wtype == FM_W_Q8_0;
+    for (int i = 0; i < steps; ++i) {
+        // e = the previous draft token's table row; h = the previous pass's output (the caller's row first)
+        if (q8)
+            HIPCHK(launch_gather_q8_f32((const int8_t*)d->W("lm_head.q"), (const uint16_t*)d->W("lm_head.d"), c.vocab,
+                                        H, tokens + i, e, st));
+        else
+            HIPCHK(launch_gather_f32(d->B("lm_head.weight"), c.vocab, H, tokens + i, nullptr, e, st));
+        fm_block_args a{};
+        a.rows = 1;
+        a.pos = pos + i;
+        a.kv_lo = kv_lo;
+        a.embed_rows = e;
+        a.prev_hidden = i == 0 ? h : hidden_out + (size_t)(i - 1) * H;
+        CHK(mtp_draft(d, &a, hidden_out + (size_t)i * H, st));
+        CHK(fm_lm_argmax(d, hidden_out + (size_t)i * H, 1, tokens + i + 1, nullptr, stream));
+    }
     return FM_OK;
 }
 

@@ -84,6 +84,9 @@ hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* fra
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
                               hipStream_t st);
+// Q8_0 row E[*idx] -> f32 [K] (scale times code); ids are clamped to [0, V).
+hipError_t launch_gather_q8_f32(const int8_t* q, const uint16_t* dsc, int V, int K, const int32_t* idx, float* out,
+                                hipStream_t st);
 // bf16 row E[*idx] -> f32 [K] (+ optional bf16 row added); ids are clamped to [0, V).
 hipError_t launch_gather_f32(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add_bf16, float* out,
                              hipStream_t st);

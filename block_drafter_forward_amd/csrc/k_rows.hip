@@ -171,6 +171,15 @@ __global__ void gather_f32_kernel(const uint16_t* E, int V, int K, const int32_t
     out[i] = v;
 }
 
+// Row E[*idx] of a Q8_0 table ([V][K] int8 codes, [V][K/32] f16 scales) -> f32: d * q per element (exact in f32).
+__global__ void gather_q8_f32_kernel(const int8_t* q, const uint16_t* dsc, int V, int K, const int32_t* idx,
+                                     float* out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= K) return;
+    const size_t row = clamp_row(idx[0], V);
+    out[i] = f16_to_f32(dsc[row * (K >> 5) + (i >> 5)]) * (float)q[row * K + i];
+}
+
 __global__ void colmean_stage1(const uint16_t* E, int V, int H, int R, float* scratch) {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= H) return;
@@ -287,6 +296,13 @@ hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* fra
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
                               hipStream_t st) {
     gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_q8_f32(const int8_t* q, const uint16_t* dsc, int V, int K, const int32_t* idx, float* out,
+                                hipStream_t st) {
+    if (K % 32 || V < 1) return hipErrorInvalidValue;
+    gather_q8_f32_kernel<<<(K + 255) / 256, 256, 0, st>>>(q, dsc, V, K, idx, out);
     return hipGetLastError();
 }
 

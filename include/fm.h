@@ -159,6 +159,19 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits,
                        void* stream);
 
+/* Chained MTP depth (ternary_bonsai_2_mtp.js: the file header's "Depth N chains the head", MTPRunner's draft loop):
+ * `steps` further single-row passes, pass i at position pos + i, each on the embedding row of the previous draft
+ * token (tokens[i]: the row of the lm_head table, dequantised) and the previous pass's output h' (h for pass 0),
+ * each followed by the lm_head argmax, all on the device with no host synchronisation.
+ *   tokens      device int32 [steps + 1]: tokens[0] is given (the draft the chain starts from); pass i writes
+ *               tokens[i + 1]
+ *   h           device f32 [dim]: the output row h' of the pass that drafted tokens[0]
+ *   hidden_out  device f32 [steps][dim]: pass i's output h'; each pass writes its K/V row into the cache at pos + i
+ * Errors: FM_E_INVALID (null pointers, not an MTP drafter, steps < 1, kv_lo > pos), FM_E_CONTEXT_FULL
+ * (pos + steps > max_ctx). Token ids outside [0, vocab) are clamped into the table. */
+fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t steps, int32_t pos, int32_t kv_lo,
+                       float* hidden_out, void* stream);
+
 /* Current context length (rows appended and not rewound), or -1 for a null handle. */
 int32_t fm_context_length(const fm_drafter* d);
 

@@ -105,3 +105,45 @@ def test_mtp_lm_head_row_scales():
         _, z = o.lm_argmax(h[:M].astype(np.float64))
         assert_rows_close(logits.cpu().numpy(), z, what=f"logits M={M}")
         assert_tokens_match(tok.cpu().numpy(), z)
+
+
+@pytest.mark.parametrize("name", ["small", "mtp"])
+def test_mtp_chain(name):
+    """Chained depth: 3 single-row passes on the device, each on the previous draft token's table row and the
+    previous output h'. The oracle chains the device's tokens (each checked by the top-2 gap rule first), so a
+    near-tie cannot make the two chains diverge; hidden rows and the new cache rows within the row tolerance."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL if name == "small" else configs.get("mtp")
+    W = gen.make_weights(cfg)
+    d = fm.Drafter(cfg, fm.upload_weights(W))
+    o = mtp.MTPOracle(cfg, W)
+    steps, H = 3, cfg["dim"]
+    pos = cfg["max_ctx"] - steps
+    kv_lo = 0 if name == "small" else pos // 4
+    kc, vc = gen.mtp_cache_rows(cfg, pos)
+    o.set_cache_rows(kc, vc)
+    d.kv_layer(0, 0)[:pos].copy_(torch.from_numpy(kc))
+    d.kv_layer(0, 1)[:pos].copy_(torch.from_numpy(vc))
+    _, h = gen.mtp_inputs(cfg, 1)
+    tok0 = 123 % cfg["vocab"]
+    _say(f"{name}: chain of {steps} from token {tok0} at pos {pos}, kv_lo {kv_lo}")
+    tokens = torch.tensor([tok0] + [0] * steps, dtype=torch.int32, device="cuda")
+    hid = torch.empty(steps, H, dtype=torch.float32, device="cuda")
+    d.fm_mtp_chain(tokens, torch.from_numpy(h[0].copy()).cuda(), steps, pos, kv_lo, hid)
+    torch.cuda.synchronize()
+    gt = tokens.cpu().numpy()
+    _, oh, oz = o.chain(tok0, h[0], steps, pos, kv_lo, follow=gt[1:])
+    for i in range(steps):
+        assert_tokens_match(gt[i + 1:i + 2], oz[i:i + 1])
+    err = assert_rows_close(hid.cpu().numpy(), oh, what="chained h'")
+    assert_rows_close(d.kv_layer(0, 0)[pos:pos + steps].cpu().numpy(), o.Kc[pos:pos + steps], what="chained K rows")
+    assert_rows_close(d.kv_layer(0, 1)[pos:pos + steps].cpu().numpy(), o.Vc[pos:pos + steps], what="chained V rows")
+    _say(f"{name}: chain tokens {gt[1:].tolist()}, h' err {err:.2e}")
+    with pytest.raises(fm.FmError) as ex:
+        d.fm_mtp_chain(tokens, hid[0], steps, cfg["max_ctx"] - 1, 0, hid)
+    assert ex.value.status == fm.FM_E_CONTEXT_FULL
+    with pytest.raises(fm.FmError) as ex:
+        d.fm_mtp_chain(tokens, hid[0], 0, 0, 0, hid)
+    assert ex.value.status == fm.FM_E_INVALID
