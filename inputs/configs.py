@@ -42,7 +42,7 @@ CONFIGS: dict[str, dict] = {
         variant="kvinject", dim=1024, heads=8, head_dim=128, kv_heads=8, layers=5, ffn=2048, block=5,
         target_dim=2560, n_taps=4, vocab=262144, max_ctx=2048 + 64, rope="none", rope_dims=0,
         rope_theta=0.0, ln_eps=1e-6, rms_eps=1e-6, qk_eps=1e-6, mlp="geglu_tanh", kv_dtype="f32",
-        wtype="bf16", ctx_rows=2048),
+        wtype="bf16", ctx_rows=2048, markov_rank=256),
     # MTP head (MCFG: H 5120, I 17408, 24 q heads, 4 kv heads, head dim 256, 64 rotated dims, theta 1e7,
     # eps 1e-6, vocab 248320, at most 8 rows); Q8_0 weights, 4096-position KV cache.
     "mtp": dict(

@@ -109,6 +109,13 @@ def kvinject_weight_specs(cfg: dict):
     s += [("W_c", (d, cfg["n_taps"] * Ht), "w"), ("ctx_norm", (d,), "n"), ("tok_proj", (d, Ht), "w"),
           ("mask_emb", (g - 1, d), "w"), ("block_pos", (g, d), "w"), ("out_norm", (d,), "n"),
           ("out_proj", (Ht, d), "w"), ("lm_head.weight", (cfg["vocab"], Ht), "w")]
+    r = cfg.get("markov_rank", 0)
+    if r:
+        # DSpark Markov head and confidence head in the page's own layouts: w1 [V][r] (rows gathered by token),
+        # w2 [r][V] (bias = e1 w2), conf.w [(dDraft + r)][1], conf.b [1]. The page zero-initialises w2 and conf.w
+        # (a pure parallel drafter at init); the synthetic set draws them N(0, .02) so that both heads act.
+        s += [("markov.w1", (cfg["vocab"], r), "w"), ("markov.w2", (r, cfg["vocab"]), "w"),
+              ("conf.w", (d + r, 1), "w"), ("conf.b", (1,), "b")]
     return s
 
 

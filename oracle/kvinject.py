@@ -7,9 +7,14 @@ Follows page "mlx-bun 0.4.0 -> 1.0.0", src/spec/dspark/module-dflash.ts: the fil
   Eq 3   K_i = [W_i^K n(H_ctx); W_i^K n(H_d)], V_i likewise, Q_i = W_i^Q n(H_d), n = the layer's attn_norm applied to
          context and block alike; the block attends bidirectionally over [context ++ block].
 
-Readings: no RoPE, no q/k norm, no mask (batch of one); the head output is not cast before the lm_head; the Markov
-correction is zero at its initialisation (W2 = 0) and is omitted; the lm_head table E is also the embedding table.
-The activation the page calls geluApprox is read as the tanh form (parity unpinned beyond that formula).
+Readings: no RoPE, no q/k norm, no mask (batch of one); the head output is not cast before the lm_head; the lm_head
+table E is also the embedding table. The activation the page calls geluApprox is read as the tanh form (parity
+unpinned beyond that formula).
+
+Markov decode (forwardRows' greedy loop with the Markov head, #markov, #confidence): with block = RMSNorm(H_d;
+out_norm) and base logits z = (block out_proj) E^T, step k takes e1 = w1[prev] (prev = the anchor, then the
+previous step's token), scores_k = z_k + e1 w2, token_k = argmax scores_k and conf_k = sigmoid([block_k; e1] conf.w
++ conf.b). draft_block/lm_argmax alone are the page's parallel route (w2 = 0, its initialisation).
 """
 from __future__ import annotations
 
@@ -83,7 +88,8 @@ class KVInjectOracle:
         for i in range(cfg["layers"]):
             x = self._layer(i, x, self.K[i][:self.length], self.V[i][:self.length])
             xs.append(x.copy())
-        out = P.linear(P.rmsnorm(x, self.w("out_norm"), cfg["rms_eps"]), self.w("out_proj"))
+        self.block_n = P.rmsnorm(x, self.w("out_norm"), cfg["rms_eps"])
+        out = P.linear(self.block_n, self.w("out_proj"))
         return out, xs
 
     def draft_block_reproject(self, taps_all: np.ndarray, anchor: int) -> np.ndarray:
@@ -100,3 +106,23 @@ class KVInjectOracle:
     def lm_argmax(self, hidden: np.ndarray):
         z = P.linear(hidden, self.w("lm_head.weight"))
         return P.argmax_rows(z), z
+
+    def markov_decode(self, block_n: np.ndarray, hidden: np.ndarray, anchor: int, follow=None):
+        """Greedy decode with the Markov correction and the confidence head over the rows of one block: block_n the
+        normed backbone rows [gamma][dDraft], hidden = out_proj(block_n) [gamma][Ht]. follow (optional): tokens to
+        condition the next step on instead of this oracle's own argmax (a device run that took the other side of a
+        near-tie). Returns (tokens, scores [gamma][V], conf [gamma])."""
+        z = P.linear(hidden, self.w("lm_head.weight"))
+        w1, w2 = self.w("markov.w1"), self.w("markov.w2")
+        cw, cb = self.w("conf.w")[:, 0], self.w("conf.b")[0]
+        prev = int(anchor)
+        toks, scores, conf = [], [], []
+        for k in range(z.shape[0]):
+            e1 = w1[prev]
+            s = z[k] + e1 @ w2
+            t = int(P.argmax_rows(s[None, :])[0])
+            toks.append(t)
+            scores.append(s)
+            conf.append(P.sigmoid(np.concatenate([block_n[k], e1]) @ cw + cb))
+            prev = t if follow is None else int(follow[k])
+        return np.array(toks), np.stack(scores), np.array(conf)

@@ -186,6 +186,70 @@ def test_kvinject_matches_loop_implementation():
     assert np.allclose(z, ref_z, rtol=1e-11, atol=1e-12)
 
 
+KV_MARKOV = dict(KV_MICRO, markov_rank=4, name="kv_markov")
+
+
+def _markov_setup(W=None):
+    cfg = KV_MARKOV
+    W = W if W is not None else gen.make_weights(cfg)
+    o = kvinject.KVInjectOracle(cfg, W)
+    o.context_append(gen.taps(cfg, "micro", cfg["ctx_rows"]), 0)
+    out, _ = o.draft_block(anchor=11)
+    return cfg, W, o, out
+
+
+def test_markov_decode_at_the_page_init_is_the_parallel_argmax():
+    # The page initialises w2 and conf.w to zero ("starts as pure parallel DFlash"): the tokens are the plain
+    # per-row argmax of the base logits and every confidence is sigmoid(conf.b) (closed form).
+    cfg, W, o, _ = _markov_setup()
+    W0 = dict(W)
+    W0["markov.w2"] = np.zeros_like(W["markov.w2"])
+    W0["conf.w"] = np.zeros_like(W["conf.w"])
+    cfg, W0, o0, out0 = _markov_setup(W0)
+    tok, z = o0.lm_argmax(out0)
+    t, sc, conf = o0.markov_decode(o0.block_n, out0, anchor=11)
+    assert np.array_equal(t, tok) and np.array_equal(sc, z)
+    b = float(P.bf16_to_f64(W["conf.b"])[0])
+    assert np.allclose(conf, 1.0 / (1.0 + np.exp(-b)), rtol=1e-15)
+
+
+def test_markov_decode_matches_plain_loops():
+    # Brute force: every score and the confidence dot product as explicit Python loops over the decoded weights.
+    cfg, W, o, out = _markov_setup()
+    t, sc, conf = o.markov_decode(o.block_n, out, anchor=11)
+    E = P.bf16_to_f64(W["lm_head.weight"])
+    w1, w2 = P.bf16_to_f64(W["markov.w1"]), P.bf16_to_f64(W["markov.w2"])
+    cw, cb = P.bf16_to_f64(W["conf.w"]), P.bf16_to_f64(W["conf.b"])
+    V, r, d = cfg["vocab"], cfg["markov_rank"], cfg["dim"]
+    prev = 11
+    for k in range(cfg["block"]):
+        s = []
+        for v in range(V):
+            zv = sum(out[k][j] * E[v][j] for j in range(cfg["target_dim"]))
+            s.append(zv + sum(w1[prev][j] * w2[j][v] for j in range(r)))
+        best = max(range(V), key=lambda v: (s[v], -v))
+        assert t[k] == best
+        assert np.allclose(sc[k], s, rtol=1e-12, atol=1e-14)
+        c = cb[0] + sum(o.block_n[k][j] * cw[j][0] for j in range(d)) + sum(w1[prev][j] * cw[d + j][0] for j in range(r))
+        assert abs(conf[k] - 1.0 / (1.0 + np.exp(-c))) < 1e-14
+        prev = best
+
+
+def test_markov_decode_identical_rows_remove_the_chain():
+    # If every w1 row is the same, the correction no longer depends on the previous token: each row's token is the
+    # argmax of its base logits plus one common bias, whatever the other rows chose (and whatever `follow` says).
+    cfg, W, o, out = _markov_setup()
+    W1 = dict(W)
+    W1["markov.w1"] = np.repeat(W["markov.w1"][3:4], cfg["vocab"], axis=0)
+    cfg, W1, o1, out1 = _markov_setup(W1)
+    t, sc, _ = o1.markov_decode(o1.block_n, out1, anchor=11)
+    bias = P.bf16_to_f64(W1["markov.w1"])[0] @ P.bf16_to_f64(W1["markov.w2"])
+    _, z = o1.lm_argmax(out1)
+    assert np.array_equal(t, np.argmax(z + bias, axis=1))
+    t2, sc2, _ = o1.markov_decode(o1.block_n, out1, anchor=11, follow=(t + 1) % cfg["vocab"])
+    assert np.array_equal(t2, t) and np.array_equal(sc2, sc)
+
+
 def test_kvinject_cached_route_equals_reprojection():
     # The page: the context projection is independent of the block and can be retained.
     cfg = KV_MICRO
