@@ -166,10 +166,22 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
         dk.fm_draft_block(hk, anchor=ak)
         dk.fm_lm_argmax(hk, g, tkk)
     ms = _time_ms(torch, _graph_of(torch, kstep), 5, reps)
-    kw = [nm for nm, _, _ in gen.kvinject_weight_specs(kc) if nm not in ("W_c", "ctx_norm")]
-    rows["kvinject_draft"] = _hbm_row("KV-injection draft (gamma 5) + lm_head argmax", ms,
-                                      weight_bytes(Wk, kw) + 2 * kc["layers"] * nk * Dk * 4,
-                                      "draft blocks/s")
+    kw = [nm for nm, _, _ in gen.kvinject_weight_specs(kc)
+          if nm not in ("W_c", "ctx_norm") and not nm.startswith(("markov.", "conf."))]
+    kbytes = weight_bytes(Wk, kw) + 2 * kc["layers"] * nk * Dk * 4
+    rows["kvinject_draft"] = _hbm_row("KV-injection draft (gamma 5) + lm_head argmax", ms, kbytes, "draft blocks/s")
+    # the same draft decoded with the DSpark Markov correction and confidence head (fm_markov_argmax): the base
+    # logits once (written and read back), then per row the rank x V correction table and the w1 row
+    rk, Vk = kc["markov_rank"], kc["vocab"]
+    cfk = torch.empty(g, dtype=torch.float32, device="cuda")
+
+    def mkstep():
+        dk.fm_draft_block(hk, anchor=ak)
+        dk.fm_markov_argmax(hk, g, ak, rk, tkk, cfk)
+    ms = _time_ms(torch, _graph_of(torch, mkstep), 5, reps)
+    rows["kvinject_draft_markov"] = _hbm_row("KV-injection draft + Markov-corrected greedy decode and confidence "
+                                             "(gamma 5, rank 256)", ms,
+                                             kbytes + g * (rk * Vk * 2 + 2 * Vk * 4 + rk * 2), "draft blocks/s")
     del dk, Wk
 
     # MTP head: M rows at pos0 = 4096 - M over the 4096-row cache, + the Q8_0 lm_head argmax

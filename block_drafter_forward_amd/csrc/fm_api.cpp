@@ -82,7 +82,7 @@ int pick_split(int M_total, int K, bool q8 = false) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -168,6 +168,11 @@ Plan make_plan(const fm_config& c) {
     p.cfrag = take(fmv ? (size_t)c.dim * 64 : 0);
     // MTP chained passes: the embedding row of the previous draft token
     p.echain = take(c.variant == FM_VARIANT_MTP ? (size_t)c.dim * 4 : 0);
+    // KV-injection: the normed backbone rows of the last draft (the confidence head's input) and the base logits
+    // of the Markov decode
+    const bool kvi = c.variant == FM_VARIANT_KVINJECT;
+    p.blockn = take(kvi ? (size_t)TMAX * c.dim * 4 : 0);
+    p.zbase = take(kvi ? (size_t)c.block * c.vocab * 4 : 0);
     p.total = off;
     return p;
 }
@@ -972,6 +977,10 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
             r.w_bf16 = i + 1 < c.layers ? d->B(BB(i + 1, "attn_norm")) : d->B("out_norm");
             r.eps = c.rms_eps;
             r.frag_out = fragH;
+            if (i + 1 == c.layers) {   // keep block = RMSNorm(H_d; out_norm) for the confidence head
+                r.f32_out = d->at<float>(d->p.blockn);
+                r.out_ld = D;
+            }
             CHK(rows(r, st));
         }
     }
@@ -1271,6 +1280,40 @@ fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t s
         CHK(mtp_draft(d, &a, hidden_out + (size_t)i * H, st));
         CHK(fm_lm_argmax(d, hidden_out + (size_t)i * H, 1, tokens + i + 1, nullptr, stream));
     }
+    return FM_OK;
+}
+
+fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, const int32_t* anchor, int32_t rank,
+                           int32_t* tokens, float* conf, float* scores, void* stream) {
+    g_err.clear();
+    if (!d || !hidden || !anchor || !tokens || !conf) return fail(FM_E_INVALID, "null argument");
+    const auto& c = d->c;
+    if (c.variant != FM_VARIANT_KVINJECT) return fail(FM_E_INVALID, "fm_markov_argmax needs a KV-injection drafter");
+    if (rows < 1 || rows > c.block) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, c.block);
+    if (rank < 1 || rank > MARKOV_MAX_RANK) return fail(FM_E_INVALID, "rank %d outside [1, %d]", rank, MARKOV_MAX_RANK);
+    if (c.vocab % 4) return fail(FM_E_UNSUPPORTED, "vocab %d not a multiple of 4", c.vocab);
+    for (const char* n : {"markov.w1", "markov.w2", "conf.w", "conf.b"})
+        if (!d->w.count(n)) return fail(FM_E_INVALID, "missing weight %s", n);
+    hipStream_t st = (hipStream_t)stream;
+    float* z = d->at<float>(d->p.zbase);
+    // base logits of every row (the fused lm_head with its logits output; its own tokens are overwritten below)
+    CHK(fm_lm_argmax(d, hidden, rows, tokens, z, stream));
+    MarkovArgs a{};
+    a.w1 = d->B("markov.w1");
+    a.w2 = d->B("markov.w2");
+    a.cw = d->B("conf.w");
+    a.cb = d->B("conf.b");
+    a.z = z;
+    a.block = d->at<float>(d->p.blockn);
+    a.anchor = anchor;
+    a.tokens = tokens;
+    a.conf = conf;
+    a.scores = scores;
+    a.key = d->at<unsigned long long>(d->p.best);
+    a.V = c.vocab;
+    a.r = rank;
+    a.D = c.dim;
+    for (int k = 0; k < rows; ++k) HIPCHK(launch_markov_step(a, k, st));
     return FM_OK;
 }
 

@@ -213,6 +213,25 @@ struct LmArgs {
 };
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
 
+// DSpark Markov decode step k (KV-injection drafter): scores = z_k + w1[prev] w2, argmax -> tokens[k], confidence
+// sigmoid([block_k; w1[prev]] conf.w + conf.b) -> conf[k]; prev = anchor (k = 0) or tokens[k - 1].
+#define MARKOV_MAX_RANK 1024
+struct MarkovArgs {
+    const uint16_t* w1;    // bf16 [V][r]
+    const uint16_t* w2;    // bf16 [r][V]
+    const uint16_t* cw;    // bf16 [D + r]
+    const uint16_t* cb;    // bf16 [1]
+    const float* z;        // base logits [rows][V]
+    const float* block;    // normed backbone rows [rows][D]
+    const int32_t* anchor; // device [1]
+    int32_t* tokens;       // device [rows]
+    float* conf;           // device [rows]
+    float* scores;         // optional [rows][V]
+    unsigned long long* key;  // [1], zero between steps
+    int V, r, D;
+};
+hipError_t launch_markov_step(const MarkovArgs& a, int k, hipStream_t st);
+
 // ── K2: MFMA prefill GEMM (f16 operands, f32 accumulate) ──────────────────────────────────────
 // C[r][n] = sum_k A[r][k] B[n][k]; A f32 or f16 rows, B bf16 weights converted to f16 on the way into LDS.
 enum PrefillEpi {

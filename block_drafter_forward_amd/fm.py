@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.fm_lm_argmax.restype = ctypes.c_int
         L.fm_mtp_chain.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         L.fm_mtp_chain.restype = ctypes.c_int
+        L.fm_markov_argmax.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp]
+        L.fm_markov_argmax.restype = ctypes.c_int
         L.fm_context_length.argtypes = [vp]
         L.fm_context_length.restype = i32
         L.fm_destroy.argtypes = [vp]
@@ -186,6 +188,11 @@ class Drafter:
     def fm_mtp_chain(self, tokens, h, steps: int, pos: int, kv_lo: int, hidden_out, stream=None):
         check(self.L.fm_mtp_chain(self.h, tokens.data_ptr(), h.data_ptr(), steps, pos, kv_lo, hidden_out.data_ptr(),
                                   _stream_ptr(stream)))
+
+    def fm_markov_argmax(self, hidden, rows: int, anchor, rank: int, tokens, conf, scores=None, stream=None):
+        check(self.L.fm_markov_argmax(self.h, hidden.data_ptr(), rows, anchor.data_ptr(), rank, tokens.data_ptr(),
+                                      conf.data_ptr(), scores.data_ptr() if scores is not None else None,
+                                      _stream_ptr(stream)))
 
     # views of the caller-owned cache (layout documented in include/fm.h)
     def kv_layer(self, l: int, which: int):

@@ -172,6 +172,20 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
 fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t steps, int32_t pos, int32_t kv_lo,
                        float* hidden_out, void* stream);
 
+/* Greedy decode of a KV-injection block with the DSpark Markov correction and confidence head (module-dflash.ts:
+ * forwardRows' loop with #markov and #confidence). For r < rows, in order: e1 = markov.w1[prev] (prev = *anchor for
+ * r = 0, else tokens[r - 1]), tokens[r] = argmax_v (hidden[r] . lm_head[v] + (e1 . markov.w2)[v]) (ties to the
+ * lowest index), conf[r] = sigmoid([block_r; e1] . conf.w + conf.b) with block_r = RMSNorm(H_d; out_norm) row r of
+ * the last fm_draft_block on this handle (hidden = that call's output).
+ *   weights (named at fm_create): markov.w1 bf16 [vocab][rank], markov.w2 bf16 [rank][vocab],
+ *            conf.w bf16 [dim + rank], conf.b bf16 [1]
+ *   anchor   device int32 [1]; tokens, conf device [rows]; scores nullable device f32 [rows][vocab] (debug)
+ * Confidence pruning (truncating the block where conf drops below a threshold) is the caller's decision.
+ * Errors: FM_E_INVALID (null pointers, not a KV-injection drafter, rows outside [1, block], rank outside [1, 1024],
+ * missing weights), FM_E_UNSUPPORTED (vocab % 4 != 0). */
+fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, const int32_t* anchor, int32_t rank,
+                           int32_t* tokens, float* conf, float* scores, void* stream);
+
 /* Current context length (rows appended and not rewound), or -1 for a null handle. */
 int32_t fm_context_length(const fm_drafter* d);
 

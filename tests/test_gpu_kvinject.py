@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 SMALL = dict(variant="kvinject", dim=256, heads=2, head_dim=128, kv_heads=2, layers=2, ffn=512, block=5,
              target_dim=512, n_taps=2, vocab=4096, max_ctx=160, rope="none", rope_dims=0, rope_theta=0.0,
              ln_eps=1e-6, rms_eps=1e-6, qk_eps=1e-6, mlp="geglu_tanh", kv_dtype="f32", wtype="bf16", ctx_rows=100,
-             name="kvinject_small")
+             markov_rank=64, name="kvinject_small")
 
 
 def _say(msg):
@@ -85,3 +85,40 @@ def test_kvinject_prefill_append_draft(name):
     _, z = o.lm_argmax(out)
     assert_rows_close(hid, out, what="hidden after append")
     assert_tokens_match(tok, z)
+
+
+@pytest.mark.parametrize("name", ["small", "kvinject"])
+def test_kvinject_markov_decode(name):
+    """DSpark Markov correction + confidence head after a draft: the oracle conditions each step on the device's
+    previous token (each checked by the top-2 gap rule on the oracle's scores), so a near-tie cannot make the two
+    decodes diverge; scores within the row tolerance, confidences within 1e-4."""
+    cfg = SMALL if name == "small" else configs.get("kvinject")
+    fm, d, o = _setup(cfg)
+    n = cfg["ctx_rows"]
+    taps = gen.taps(cfg, "prefill", n)
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    an = int(gen.anchors(cfg, name + "-markov", 1)[0])
+    _say(f"{name}: draft + Markov decode, anchor {an}, rank {cfg['markov_rank']}")
+    T, V = cfg["block"], cfg["vocab"]
+    a = torch.tensor([an], dtype=torch.int32, device="cuda")
+    hid = torch.empty(T, cfg["target_dim"], dtype=torch.float32, device="cuda")
+    d.fm_draft_block(hid, anchor=a)
+    tok = torch.empty(T, dtype=torch.int32, device="cuda")
+    conf = torch.empty(T, dtype=torch.float32, device="cuda")
+    scores = torch.empty(T, V, dtype=torch.float32, device="cuda")
+    d.fm_markov_argmax(hid, T, a, cfg["markov_rank"], tok, conf, scores)
+    torch.cuda.synchronize()
+    gt = tok.cpu().numpy()
+    out, _ = o.draft_block(an)
+    ot, osc, oconf = o.markov_decode(o.block_n, out, an, follow=gt)
+    k = assert_tokens_match(gt, osc)
+    e = assert_rows_close(scores.cpu().numpy(), osc, what="Markov scores")
+    assert np.max(np.abs(conf.cpu().numpy() - oconf)) < 1e-4, (conf.cpu().numpy(), oconf)
+    _say(f"{name}: tokens {gt.tolist()} (exact on {k}/{T}), scores err {e:.2e}, conf {np.round(oconf, 4).tolist()}")
+    # the correction acts: the Markov tokens differ from the plain argmax somewhere, or the scores do
+    _, z = o.lm_argmax(out)
+    assert np.max(np.abs(osc - z)) > 1e-4
+    with pytest.raises(fm.FmError) as ex:
+        d.fm_markov_argmax(hid, T + 1, a, cfg["markov_rank"], tok, conf)
+    assert ex.value.status == fm.FM_E_INVALID
