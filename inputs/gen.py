@@ -92,6 +92,18 @@ def flowmap_weight_specs(cfg: dict):
               (f"layers.{l}.mlp.fc2.weight", (D, F), "w"), (f"layers.{l}.mlp.fc2.bias", (D,), "b")]
     s += [("head.weight", (Ht, D), "w"), ("head.bias", (Ht,), "b"),
           ("lm_head.weight", (cfg["vocab"], Ht), "w"), ("mod", ((3 * L + 1) * 3 * D,), "mod")]
+    td, cd = cfg.get("time_dim", 0), cfg.get("cond_dim", 0)
+    if td:
+        # time conditioning (the page's timeConditioning): two time MLPs [cond x time_dim], [cond x cond] and one
+        # adaLN linear [3 D x cond] per norm, all with biases
+        for pre in ("time_embed", "jump_embed"):
+            s += [(f"{pre}.linear_1.weight", (cd, td), "w"), (f"{pre}.linear_1.bias", (cd,), "b"),
+                  (f"{pre}.linear_2.weight", (cd, cd), "w"), (f"{pre}.linear_2.bias", (cd,), "b")]
+        for l in range(L):
+            for n in ("self_attn", "cross_attn", "mlp"):
+                s += [(f"layers.{l}.{n}_adaln.linear.weight", (3 * D, cd), "w"),
+                      (f"layers.{l}.{n}_adaln.linear.bias", (3 * D,), "b")]
+        s += [("final_adaln.linear.weight", (3 * D, cd), "w"), ("final_adaln.linear.bias", (3 * D,), "b")]
     return s
 
 

@@ -11,6 +11,11 @@ Readings taken where the page leaves a step open:
   * cross-attention keys are cache rows [0, pos], the anchor slot at pos included (L = pos + 1);
   * self-attention is unmasked over the T slots; slot s sits at position pos + 1 + s;
   * RoPE angles are exact (float64), caches are float64.
+
+Time conditioning (timeConditioning, the page's FlashMapDraftModel.time_conditioning): the modulation table of a
+jump s -> t from the time MLPs. A time is embedded sinusoidally (frequencies and angles rounded to f32 as the page
+does, cos and sin of those angles), passed through linear_1, SiLU, linear_2 of time_embed (for s) or jump_embed
+(for t); cond = SiLU(sum of the two); each norm's [scale | shift | gate] is its adaLN linear of cond.
 """
 from __future__ import annotations
 
@@ -42,6 +47,29 @@ class FlowMapOracle:
 
     def lw(self, l: int, name: str) -> np.ndarray:
         return self.w(f"layers.{l}.{name}")
+
+    def time_conditioning(self, s: float, t: float) -> np.ndarray:
+        """The [(3 layers + 1) * 3 D] modulation table of the jump s -> t (norm order per layer: self, cross, mlp;
+        then the final norm), float64 arithmetic after the page's f32 angles."""
+        cfg = self.cfg
+        half = cfg["time_dim"] // 2
+
+        def embed(prefix, time):
+            i = np.arange(half, dtype=np.float64)
+            f = np.exp(-np.log(10000.0) * i / half).astype(np.float32)
+            a = (np.float32(np.float32(time) * np.float32(cfg["time_scale"])) * f).astype(np.float64)
+            e = np.concatenate([np.cos(a), np.sin(a)])
+            h = P.silu(P.linear(e[None, :], self.w(f"{prefix}.linear_1.weight"), self.w(f"{prefix}.linear_1.bias")))
+            return P.linear(h, self.w(f"{prefix}.linear_2.weight"), self.w(f"{prefix}.linear_2.bias"))[0]
+
+        cond = P.silu(embed("time_embed", s) + embed("jump_embed", t))
+        rows = [f"layers.{l}.{n}_adaln.linear" for l in range(cfg["layers"]) for n in ("self_attn", "cross_attn", "mlp")]
+        rows.append("final_adaln.linear")
+        return np.concatenate([P.linear(cond[None, :], self.w(f"{r}.weight"), self.w(f"{r}.bias"))[0] for r in rows])
+
+    def use_table(self, table: np.ndarray):
+        """Draft with this modulation table instead of the stored one."""
+        self._w["mod"] = np.asarray(table, np.float64)
 
     def mod(self, n: int):
         """Row n of the modulation table: (scale, shift, gate), each [D] (norm order per layer: self, cross, mlp;

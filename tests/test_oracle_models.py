@@ -171,6 +171,78 @@ def test_flowmap_param_count_matches_page():
     assert abs(2 * n - GOLD["flashmap_size"]["file_bytes"]) / GOLD["flashmap_size"]["file_bytes"] < 0.005
 
 
+# ── time conditioning ───────────────────────────────────────────────────────────────────────────
+
+FM_TC = dict(variant="flowmap", dim=8, heads=2, head_dim=4, kv_heads=2, layers=2, ffn=16, block=4, target_dim=8,
+             n_taps=2, vocab=12, max_ctx=32, rope="interleaved", rope_dims=4, rope_theta=1e4, ln_eps=1e-6,
+             rms_eps=1e-6, qk_eps=1e-5, mlp="gelu_erf", kv_dtype="f16", wtype="bf16", ctx_rows=4, time_dim=8,
+             cond_dim=6, time_scale=1000.0, name="fm_tc")
+
+
+def test_time_conditioning_matches_plain_loops():
+    # Brute force of the page's timeConditioning: sinusoid, two-layer time MLPs, SiLU of the sum, one linear per
+    # norm, as explicit Python loops over the decoded weights (frequencies and angles rounded to f32 as the page's
+    # Math.fround does)
+    import math
+    cfg = FM_TC
+    W = gen.make_weights(cfg)
+    o = flowmap.FlowMapOracle(cfg, W)
+    dec = {k: P.weight_f64(v) for k, v in W.items()}
+    half, cd, D = cfg["time_dim"] // 2, cfg["cond_dim"], cfg["dim"]
+    f32 = lambda x: float(np.float32(x))
+
+    def lin(name, x):
+        Wm, b = dec[name + ".weight"], dec[name + ".bias"]
+        return [b[m] + sum(Wm[m][k] * x[k] for k in range(len(x))) for m in range(Wm.shape[0])]
+
+    silu = lambda v: [u / (1.0 + math.exp(-u)) for u in v]
+
+    def embed(pre, time):
+        e = [0.0] * (2 * half)
+        for i in range(half):
+            fi = f32(math.exp(-math.log(10000.0) * i / half))
+            a = f32(f32(time * cfg["time_scale"]) * fi)
+            e[i], e[half + i] = math.cos(a), math.sin(a)
+        return lin(pre + ".linear_2", silu(lin(pre + ".linear_1", e)))
+
+    for s_, t_ in ((0.0, 1.0), (0.25, 0.75)):
+        ts, tj = embed("time_embed", s_), embed("jump_embed", t_)
+        cond = silu([ts[i] + tj[i] for i in range(cd)])
+        ref = []
+        for l in range(cfg["layers"]):
+            for n in ("self_attn", "cross_attn", "mlp"):
+                ref += lin(f"layers.{l}.{n}_adaln.linear", cond)
+        ref += lin("final_adaln.linear", cond)
+        assert np.allclose(o.time_conditioning(s_, t_), ref, rtol=1e-12, atol=1e-14)
+        assert len(ref) == (3 * cfg["layers"] + 1) * 3 * D
+
+
+def test_time_conditioning_closed_forms():
+    cfg = FM_TC
+    W = gen.make_weights(cfg)
+    # zero weights everywhere: every linear returns its bias, so the table is the adaLN biases
+    Wz = {k: (np.zeros_like(v) if k.endswith(".weight") and ("embed" in k or "adaln" in k) else v) for k, v in W.items()}
+    oz = flowmap.FlowMapOracle(cfg, Wz)
+    biases = np.concatenate([P.weight_f64(W[f"layers.{l}.{n}_adaln.linear.bias"]) for l in range(cfg["layers"])
+                             for n in ("self_attn", "cross_attn", "mlp")] + [P.weight_f64(W["final_adaln.linear.bias"])])
+    assert np.array_equal(oz.time_conditioning(0.0, 1.0), biases)
+    # at time 0 the sinusoid is [1 .. 1 | 0 .. 0] (cos 0, sin 0), so linear_1 of it is the sum of its first half of
+    # columns plus its bias; the jump 0 -> 0 built from that closed form must give the table's final-norm rows
+    o = flowmap.FlowMapOracle(cfg, W)
+    w1 = P.weight_f64(W["time_embed.linear_1.weight"])
+    half = cfg["time_dim"] // 2
+    h = w1[:, :half].sum(axis=1) + P.weight_f64(W["time_embed.linear_1.bias"])
+    ts = P.weight_f64(W["time_embed.linear_2.weight"]) @ P.silu(h) + P.weight_f64(W["time_embed.linear_2.bias"])
+    tab = o.time_conditioning(0.0, 1.0)
+    tab00 = o.time_conditioning(0.0, 0.0)
+    cond00 = P.silu(ts + (P.weight_f64(W["jump_embed.linear_2.weight"]) @ P.silu(
+        P.weight_f64(W["jump_embed.linear_1.weight"])[:, :half].sum(axis=1) + P.weight_f64(W["jump_embed.linear_1.bias"]))
+        + P.weight_f64(W["jump_embed.linear_2.bias"])))
+    fw, fb = P.weight_f64(W["final_adaln.linear.weight"]), P.weight_f64(W["final_adaln.linear.bias"])
+    assert np.allclose(tab00[-3 * cfg["dim"]:], fw @ cond00 + fb, rtol=1e-12, atol=1e-14)
+    assert not np.allclose(tab, tab00)
+
+
 # ── KV-injection ────────────────────────────────────────────────────────────────────────────────
 
 def test_kvinject_matches_loop_implementation():
