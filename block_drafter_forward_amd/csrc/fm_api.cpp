@@ -82,7 +82,7 @@ int pick_split(int M_total, int K, bool q8 = false) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -173,6 +173,7 @@ Plan make_plan(const fm_config& c) {
     const bool kvi = c.variant == FM_VARIANT_KVINJECT;
     p.blockn = take(kvi ? (size_t)TMAX * c.dim * 4 : 0);
     p.zbase = take(kvi ? (size_t)c.block * c.vocab * 4 : 0);
+    p.tcond = take(fmv ? (size_t)TC_MAX_DIM * 4 : 0);   // time conditioning: the cond vector
     p.total = off;
     return p;
 }
@@ -1314,6 +1315,53 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
     a.r = rank;
     a.D = c.dim;
     for (int k = 0; k < rows; ++k) HIPCHK(launch_markov_step(a, k, st));
+    return FM_OK;
+}
+
+fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, int32_t cond_dim, float time_scale,
+                            void* stream) {
+    g_err.clear();
+    if (!d) return fail(FM_E_INVALID, "null handle");
+    const auto& c = d->c;
+    if (c.variant != FM_VARIANT_FLOWMAP) return fail(FM_E_INVALID, "time conditioning needs a flow-map drafter");
+    if (time_dim < 2 || time_dim % 2 || time_dim > TC_MAX_DIM || cond_dim < 1 || cond_dim > TC_MAX_DIM)
+        return fail(FM_E_INVALID, "time_dim %d / cond_dim %d outside [2, %d] (time_dim even)", time_dim, cond_dim,
+                    TC_MAX_DIM);
+    const int nn = 3 * c.layers + 1;
+    if (nn > TC_MAX_NORMS) return fail(FM_E_UNSUPPORTED, "%d norms", nn);
+    TimeCondArgs a{};
+    const char* pre[2] = {"time_embed", "jump_embed"};
+    char b[128];
+    auto need = [&](const char* n) -> const uint16_t* {
+        auto it = d->w.find(n);
+        return it == d->w.end() ? nullptr : (const uint16_t*)it->second;
+    };
+    for (int w = 0; w < 2; ++w) {
+        snprintf(b, sizeof b, "%s.linear_1.weight", pre[w]); a.l1w[w] = need(b);
+        snprintf(b, sizeof b, "%s.linear_1.bias", pre[w]);   a.l1b[w] = need(b);
+        snprintf(b, sizeof b, "%s.linear_2.weight", pre[w]); a.l2w[w] = need(b);
+        snprintf(b, sizeof b, "%s.linear_2.bias", pre[w]);   a.l2b[w] = need(b);
+        if (!a.l1w[w] || !a.l1b[w] || !a.l2w[w] || !a.l2b[w]) return fail(FM_E_INVALID, "missing %s weights", pre[w]);
+    }
+    for (int n = 0; n < nn; ++n) {
+        static const char* br[3] = {"self_attn", "cross_attn", "mlp"};
+        if (n < 3 * c.layers) snprintf(b, sizeof b, "layers.%d.%s_adaln.linear.", n / 3, br[n % 3]);
+        else snprintf(b, sizeof b, "final_adaln.linear.");
+        const std::string base = b;
+        a.aw[n] = need((base + "weight").c_str());
+        a.ab[n] = need((base + "bias").c_str());
+        if (!a.aw[n] || !a.ab[n]) return fail(FM_E_INVALID, "missing %sweight / bias", b);
+    }
+    a.times[0] = s;
+    a.times[1] = t;
+    a.time_scale = time_scale;
+    a.td = time_dim;
+    a.cd = cond_dim;
+    a.rows = 3 * c.dim;
+    a.nnorm = nn;
+    a.cond = d->at<float>(d->p.tcond);
+    a.table = (float*)d->F("mod");   // the caller's modulation table, overwritten in place
+    HIPCHK(launch_time_condition(a, (hipStream_t)stream));
     return FM_OK;
 }
 

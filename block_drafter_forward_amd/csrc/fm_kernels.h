@@ -84,6 +84,21 @@ hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* fra
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
                               hipStream_t st);
+// Time conditioning of a jump s -> t: the modulation table [nnorm][rows] (rows = 3 D: scale | shift | gate) from the
+// time MLPs ([0] time_embed, [1] jump_embed: linear_1 bf16 [cd][td], linear_2 [cd][cd], biases) and one adaLN
+// linear per norm (bf16 [rows][cd] + bias [rows]). cond is a [cd] f32 scratch vector.
+#define TC_MAX_DIM 1024
+#define TC_MAX_NORMS 49
+struct TimeCondArgs {
+    const uint16_t* l1w[2]; const uint16_t* l1b[2]; const uint16_t* l2w[2]; const uint16_t* l2b[2];
+    const uint16_t* aw[TC_MAX_NORMS]; const uint16_t* ab[TC_MAX_NORMS];
+    float times[2];        // s, t
+    float time_scale;
+    int td, cd, rows, nnorm;
+    float* cond;
+    float* table;
+};
+hipError_t launch_time_condition(const TimeCondArgs& a, hipStream_t st);
 // Q8_0 row E[*idx] -> f32 [K] (scale times code); ids are clamped to [0, V).
 hipError_t launch_gather_q8_f32(const int8_t* q, const uint16_t* dsc, int V, int K, const int32_t* idx, float* out,
                                 hipStream_t st);

@@ -180,6 +180,51 @@ __global__ void gather_q8_f32_kernel(const int8_t* q, const uint16_t* dsc, int V
     out[i] = f16_to_f32(dsc[row * (K >> 5) + (i >> 5)]) * (float)q[row * K + i];
 }
 
+// Time conditioning of a jump s -> t (the flow-map page's timeConditioning), create-time work.
+// Stage 1, one work-group: the sinusoidal embeddings of s and t (frequencies exp in f64 rounded to f32, angles as
+// f32 products, cos / sin of those angles: the page's Math.fround steps), each through linear_1, SiLU, linear_2 of
+// its MLP ([0] time_embed for s, [1] jump_embed for t); cond = SiLU(sum of the two).
+__global__ __launch_bounds__(256) void tc_embed_kernel(TimeCondArgs a) {
+    __shared__ float e[2][TC_MAX_DIM], h[2][TC_MAX_DIM], y[2][TC_MAX_DIM];
+    const int tid = threadIdx.x, half = a.td / 2;
+    for (int i = tid; i < half; i += 256)
+        for (int w = 0; w < 2; ++w) {
+            const float f = (float)exp(-log(10000.0) * (double)i / (double)half);
+            const float ang = (a.times[w] * a.time_scale) * f;
+            e[w][i] = (float)cos((double)ang);
+            e[w][half + i] = (float)sin((double)ang);
+        }
+    __syncthreads();
+    for (int m = tid; m < a.cd; m += 256)
+        for (int w = 0; w < 2; ++w) {
+            float acc = bf16_to_f32(a.l1b[w][m]);
+            for (int k = 0; k < a.td; ++k) acc += bf16_to_f32(a.l1w[w][(size_t)m * a.td + k]) * e[w][k];
+            h[w][m] = silu(acc);
+        }
+    __syncthreads();
+    for (int m = tid; m < a.cd; m += 256)
+        for (int w = 0; w < 2; ++w) {
+            float acc = bf16_to_f32(a.l2b[w][m]);
+            for (int k = 0; k < a.cd; ++k) acc += bf16_to_f32(a.l2w[w][(size_t)m * a.cd + k]) * h[w][k];
+            y[w][m] = acc;
+        }
+    __syncthreads();
+    for (int m = tid; m < a.cd; m += 256) a.cond[m] = silu(y[0][m] + y[1][m]);
+}
+
+// Stage 2: table row n (norm n) entry m = adaLN bias[m] + sum_k W_n[m][k] cond[k], one thread per entry.
+__global__ __launch_bounds__(256) void tc_adaln_kernel(TimeCondArgs a) {
+    __shared__ float c[TC_MAX_DIM];
+    const int n = blockIdx.y, m = blockIdx.x * 256 + threadIdx.x;
+    for (int k = threadIdx.x; k < a.cd; k += 256) c[k] = a.cond[k];
+    __syncthreads();
+    if (m >= a.rows) return;
+    const uint16_t* wr = a.aw[n] + (size_t)m * a.cd;
+    float acc = bf16_to_f32(a.ab[n][m]);
+    for (int k = 0; k < a.cd; ++k) acc += bf16_to_f32(wr[k]) * c[k];
+    a.table[(size_t)n * a.rows + m] = acc;
+}
+
 __global__ void colmean_stage1(const uint16_t* E, int V, int H, int R, float* scratch) {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= H) return;
@@ -296,6 +341,17 @@ hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* fra
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
                               hipStream_t st) {
     gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_time_condition(const TimeCondArgs& a, hipStream_t st) {
+    if (a.td < 2 || a.td % 2 || a.td > TC_MAX_DIM || a.cd < 1 || a.cd > TC_MAX_DIM || a.rows < 1 || a.nnorm < 1 ||
+        a.nnorm > TC_MAX_NORMS)
+        return hipErrorInvalidValue;
+    tc_embed_kernel<<<1, 256, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    tc_adaln_kernel<<<dim3((a.rows + 255) / 256, a.nnorm), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

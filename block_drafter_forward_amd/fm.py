@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.fm_mtp_chain.restype = ctypes.c_int
         L.fm_markov_argmax.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp]
         L.fm_markov_argmax.restype = ctypes.c_int
+        L.fm_time_condition.argtypes = [vp, ctypes.c_float, ctypes.c_float, i32, i32, ctypes.c_float, vp]
+        L.fm_time_condition.restype = ctypes.c_int
         L.fm_context_length.argtypes = [vp]
         L.fm_context_length.restype = i32
         L.fm_destroy.argtypes = [vp]
@@ -193,6 +195,9 @@ class Drafter:
         check(self.L.fm_markov_argmax(self.h, hidden.data_ptr(), rows, anchor.data_ptr(), rank, tokens.data_ptr(),
                                       conf.data_ptr(), scores.data_ptr() if scores is not None else None,
                                       _stream_ptr(stream)))
+
+    def fm_time_condition(self, s: float, t: float, time_dim: int, cond_dim: int, time_scale: float, stream=None):
+        check(self.L.fm_time_condition(self.h, s, t, time_dim, cond_dim, time_scale, _stream_ptr(stream)))
 
     # views of the caller-owned cache (layout documented in include/fm.h)
     def kv_layer(self, l: int, which: int):

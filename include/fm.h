@@ -186,6 +186,19 @@ fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t s
 fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, const int32_t* anchor, int32_t rank,
                            int32_t* tokens, float* conf, float* scores, void* stream);
 
+/* Time conditioning of the flow-map jump s -> t (flashmap_drafter.js timeConditioning, the model's
+ * time_conditioning): sinusoidal embeddings of s and t (time_dim values, frequencies 10000^(-i / (time_dim / 2)),
+ * angles of time * time_scale rounded to f32 as the page rounds them) through the time_embed / jump_embed MLPs
+ * (linear_1 [cond_dim][time_dim], SiLU, linear_2 [cond_dim][cond_dim], bf16, with biases), cond = SiLU(sum), then
+ * every norm's [scale | shift | gate] = its adaLN linear (layers.<l>.{self_attn,cross_attn,mlp}_adaln.linear and
+ * final_adaln.linear, bf16 [3 dim][cond_dim] + bias) of cond. The table is written IN PLACE into the f32 buffer
+ * registered as "mod" at fm_create (the caller's memory), so later drafts use it. Create-time work: the page
+ * computes it once per jump (zero noise to tokens: s = 0, t = 1).
+ * Errors: FM_E_INVALID (not a flow-map drafter, missing weights, time_dim odd or outside [2, 1024], cond_dim
+ * outside [1, 1024]), FM_E_UNSUPPORTED (more than 49 norms). */
+fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, int32_t cond_dim, float time_scale,
+                            void* stream);
+
 /* Current context length (rows appended and not rewound), or -1 for a null handle. */
 int32_t fm_context_length(const fm_drafter* d);
 

@@ -251,3 +251,40 @@ def test_longctx_workload(flashmap):
     torch.cuda.synchronize()
     assert d.length == o.length
     _say(f"longctx: 64 steps, worst hidden err {worst:.2e}, tokens exact on {exact}/{64 * cfg['block']} rows")
+
+
+def test_tiny_time_conditioning():
+    """The adaLN table of a jump s -> t from the time MLPs, written into the drafter's modulation table: equal to
+    the oracle's (two jumps), then a prefill and a draft that use it, against the oracle drafting with its own
+    table."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = configs.get("tiny", time_dim=256, cond_dim=256, time_scale=1000.0)
+    W = gen.make_weights(cfg)
+    dw = fm.upload_weights(W)
+    d = fm.Drafter(cfg, dw)
+    o = flowmap.FlowMapOracle(cfg, W)
+    L, D = cfg["layers"], cfg["dim"]
+    for s_, t_ in ((0.25, 0.5), (0.0, 1.0)):
+        _say(f"tiny: time conditioning {s_} -> {t_}")
+        d.fm_time_condition(s_, t_, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"])
+        torch.cuda.synchronize()
+        got = dw["mod"].cpu().numpy().reshape(3 * L + 1, 3 * D)
+        ref = o.time_conditioning(s_, t_).reshape(3 * L + 1, 3 * D)
+        e = assert_rows_close(got, ref, tol=1e-4, what=f"table {s_}->{t_}")
+        _say(f"tiny: table err {e:.2e}")
+    o.use_table(ref.reshape(-1))
+    taps = gen.taps(cfg, "prefill", cfg["ctx_rows"])
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    pos = cfg["ctx_rows"]
+    hid, tok, logits, dbg = _draft(fm, d, cfg, anchor=321, pos=pos)
+    out, _ = o.draft_block(321, pos)
+    _, z = o.lm_argmax(out)
+    e = assert_rows_close(hid, out, what="hidden with the derived table")
+    k = assert_tokens_match(tok, z)
+    _say(f"tiny: draft with the derived table: hidden err {e:.2e}, tokens exact on {k}/{cfg['block']}")
+    with pytest.raises(fm.FmError) as ex:
+        d.fm_time_condition(0.0, 1.0, 255, 256, 1000.0)
+    assert ex.value.status == fm.FM_E_INVALID
