@@ -369,7 +369,7 @@ fm_status rows(const RowArgs& r, hipStream_t st) {
 // Attention of nq query rows over cache rows [key_lo, key_hi) (+ nx extra f32 rows), merged into o fragments.
 fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_lo, int key_hi, const float* kx,
                  const float* vx, int nx, int x_ld, int causal_base, float scale, const float* gate, int gate_ld,
-                 int gate_hs, uint8_t* o_frag, hipStream_t st) {
+                 int gate_hs, uint8_t* o_frag, hipStream_t st, int o_row0 = 0) {
     const auto& c = d->c;
     AttnArgs a{};
     a.qp = qp;
@@ -427,6 +427,7 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
     m.gate_hs = gate_hs;
     m.o_frag = o_frag;
     m.perm = d->perm;
+    m.row0 = o_row0;
     HIPCHK(launch_attn_merge(m, st));
     return FM_OK;
 }
@@ -901,9 +902,14 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     return FM_OK;
 }
 
-fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+// B requests in one pass (B = 1: fm_draft_block): handle ds[b] holds request b's context cache, handle ds[0]'s
+// workspace holds the B * block rows; every projection streams its weights once for all rows, each request attends
+// over its own cache rows ++ its own block rows.
+fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* anchors, float* hidden_out,
+                               float* debug_layers, hipStream_t st) {
+    fm_drafter* d = ds[0];
     const auto& c = d->c;
-    const int D = c.dim, T = c.block, Ht = c.target_dim, hd = c.head_dim;
+    const int D = c.dim, G = c.block, T = B * G, Ht = c.target_dim, hd = c.head_dim;
     float* part = d->at<float>(d->p.part);
     float* x = d->at<float>(d->p.x);
     uint8_t* fragA = d->at<uint8_t>(d->p.fragA);
@@ -912,18 +918,19 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
     uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
     float* qkv = d->at<float>(d->p.qkv);
     const long long pstr = (long long)TMAX * D;
-    const int Lc = d->length;
 
-    // block rows: H_d[0] = tok_proj(E[anchor]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]
-    HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, fragA, d->perm, st));
+    // block rows of request b: H_d[0] = tok_proj(E[anchor_b]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]
+    for (int b = 0; b < B; ++b)
+        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, anchors + b, fragA, d->perm, st, b));
     int S = 0;
-    CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, 1, SK_PARTIAL, 0,
+    CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, B, SK_PARTIAL, 0,
                &S, st));
-    {
-        RowArgs r = rows_base(d, D, T);
+    for (int b = 0; b < B; ++b) {
+        RowArgs r = rows_base(d, D, G);
+        r.row0 = b * G;
         r.x = x;
         r.base_zero = 1;
-        r.part = part;
+        r.part = part + (size_t)b * D;   // tok_proj output row b feeds the request's row 0 only
         r.S = S;
         r.part_stride = pstr;
         r.part_rows = 1;
@@ -943,12 +950,16 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
                     {d->W(BB(i, "k")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
                     {d->W(BB(i, "v")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D, D, 3 * D}},
                    D, T, SK_F32, 0, nullptr, st));
-        // bidirectional attention over [context rows ++ block rows]
-        QPrep qp{};
-        qp.q = qkv;
-        qp.q_ld = 3 * D;
-        qp.q_hs = hd;
-        CHK(attend(d, qp, T, i, 0, Lc, qkv + D, qkv + 2 * D, T, 3 * D, -1, scale, nullptr, 0, 0, fragO, st));
+        // bidirectional attention of each request over [its context rows ++ its block rows]
+        for (int b = 0; b < B; ++b) {
+            float* qb = qkv + (size_t)b * G * 3 * D;
+            QPrep qp{};
+            qp.q = qb;
+            qp.q_ld = 3 * D;
+            qp.q_hs = hd;
+            CHK(attend(ds[b], qp, G, i, 0, ds[b]->length, qb + D, qb + 2 * D, G, 3 * D, -1, scale, nullptr, 0, 0, fragO,
+                       st, b * G));
+        }
         CHK(skinny(d, {{d->W(BB(i, "o")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}}, D, T, SK_PARTIAL, 0,
                    &S, st));
         {
@@ -973,7 +984,7 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
             r.part = part;
             r.S = S;
             r.part_stride = pstr;
-            if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)i * T * D;
+            if (debug_layers) r.debug_x = debug_layers + (size_t)i * T * D;
             r.norm = ROW_RMS;
             r.w_bf16 = i + 1 < c.layers ? d->B(BB(i + 1, "attn_norm")) : d->B("out_norm");
             r.eps = c.rms_eps;
@@ -988,6 +999,11 @@ fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_o
     CHK(skinny(d, {{d->W("out_proj"), nullptr, nullptr, nullptr, nullptr, fragH, hidden_out, Ht, Ht}}, D, T, SK_F32, 0,
                nullptr, st));
     return FM_OK;
+}
+
+fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    fm_drafter* ds[1] = {d};
+    return kvinject_draft_batch(ds, 1, ba->anchor, hidden_out, ba->debug_layers, st);
 }
 
 // ── MTP ─────────────────────────────────────────────────────────────────────────────────────────
@@ -1230,7 +1246,7 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits, void* stream) {
     g_err.clear();
     if (!d || !hidden || !tokens) return fail(FM_E_INVALID, "null argument");
-    if (rows < 1 || rows > d->c.block) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, d->c.block);
+    if (rows < 1 || rows > TMAX) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, TMAX);
     hipStream_t st = (hipStream_t)stream;
     const int K = d->c.target_dim;
     uint8_t* fr = d->at<uint8_t>(d->p.fragH);
@@ -1363,6 +1379,36 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     a.table = (float*)d->F("mod");   // the caller's modulation table, overwritten in place
     HIPCHK(launch_time_condition(a, (hipStream_t)stream));
     return FM_OK;
+}
+
+fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const int32_t* anchors, float* hidden_out, void* stream) {
+    g_err.clear();
+    if (!ds || !anchors || !hidden_out || B < 1) return fail(FM_E_INVALID, "null argument or B < 1");
+    for (int b = 0; b < B; ++b)
+        if (!ds[b]) return fail(FM_E_INVALID, "null handle %d", b);
+    const auto& c = ds[0]->c;
+    if (c.variant != FM_VARIANT_KVINJECT) return fail(FM_E_UNSUPPORTED, "batched drafts: KV-injection drafters only");
+    if (B * c.block > TMAX) return fail(FM_E_INVALID, "B %d x block %d > %d rows", B, c.block, TMAX);
+    for (int b = 1; b < B; ++b) {
+        const fm_drafter* e = ds[b];
+        const auto& f = e->c;   // the shape of the block computation (max_ctx may differ: each cache is its own)
+        if (f.variant != c.variant || f.dim != c.dim || f.heads != c.heads || f.head_dim != c.head_dim ||
+            f.kv_heads != c.kv_heads || f.layers != c.layers || f.ffn != c.ffn || f.block != c.block ||
+            f.target_dim != c.target_dim || f.n_taps != c.n_taps || f.vocab != c.vocab || f.mlp != c.mlp ||
+            f.kv_dtype != c.kv_dtype || f.wtype != c.wtype || f.rms_eps != c.rms_eps || ds[b]->perm != ds[0]->perm)
+            return fail(FM_E_INVALID, "handle %d: another configuration", b);
+        for (const auto& n : required_names(c)) {
+            const auto& w0 = ds[0]->w;
+            const auto& w1 = e->w;
+            auto i0 = w0.find(n);
+            auto i1 = w1.find(n);
+            if (i0 == w0.end() || i1 == w1.end() || i0->second != i1->second)
+                return fail(FM_E_INVALID, "handle %d: weight %s is not the same tensor", b, n.c_str());
+        }
+        for (int a = 0; a < b; ++a)
+            if (ds[a] == e) return fail(FM_E_INVALID, "handle %d appears twice", b);
+    }
+    return kvinject_draft_batch(ds, B, anchors, hidden_out, nullptr, (hipStream_t)stream);
 }
 
 int32_t fm_context_length(const fm_drafter* d) { return d ? d->length : -1; }

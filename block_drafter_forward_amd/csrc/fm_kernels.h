@@ -76,6 +76,7 @@ struct RowArgs {
     const uint16_t* row_bias_bf16;  // bf16 [T][D] added to row t (or null)
     const float* zeros;    // a zero row of >= D floats (absent inputs read it; required)
     int frag_perm;         // k order of frag_out
+    int row0;              // row t of the launch is row row0 + t of x, debug_x, frag_out and f32_out (batched blocks)
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
@@ -83,7 +84,7 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, int perm, hipStream_t st);
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
-                              hipStream_t st);
+                              hipStream_t st, int row = 0);
 // Time conditioning of a jump s -> t: the modulation table [nnorm][rows] (rows = 3 D: scale | shift | gate) from the
 // time MLPs ([0] time_embed, [1] jump_embed: linear_1 bf16 [cd][td], linear_2 [cd][cd], biases) and one adaLN
 // linear per norm (bf16 [rows][cd] + bias [rows]). cond is a [cd] f32 scratch vector.
@@ -177,8 +178,9 @@ struct MergeArgs {
     int heads, nchunks, nq, hd;
     const float* gate;     // optional: o *= sigmoid(gate[t*gate_ld + h*gate_hs + d])
     int gate_ld, gate_hs;
-    uint8_t* o_frag;       // o row t, k = h*hd + d
+    uint8_t* o_frag;       // o row row0 + t, k = h*hd + d
     int perm;
+    int row0;
 };
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st);
 

@@ -813,7 +813,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
             o[e] *= il;
             if (gp) o[e] *= sigmoidf(gt[e]);
         }
-        frag_store8(a.o_frag, t, h * HD + d0, o, a.perm);
+        frag_store8(a.o_frag, a.row0 + t, h * HD + d0, o, a.perm);
     }
 }
 

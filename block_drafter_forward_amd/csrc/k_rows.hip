@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     size_t base_ld;
     if (a.init) { basef = a.init; base_ld = 0; }
     else if (a.in_rows) { basef = a.in_rows; base_ld = a.in_ld; }
-    else if (a.x && !a.base_zero) { basef = a.x; base_ld = D; }
+    else if (a.x && !a.base_zero) { basef = a.x + (size_t)a.row0 * D; base_ld = D; }
     else { basef = zf; base_ld = 0; }
     const uint16_t* baseb = a.base_bf16 ? a.base_bf16 + (size_t)(use_b16 ? t - a.base_from : 0) * D : zb;
     const bool has_part = !(a.part_rows > 0 && t >= a.part_rows);
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
         if (slot < nslot) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sum += v[j][e];
-            if (a.x) st8(a.x + (size_t)t * D + slot * 8, v[j]);
-            if (a.debug_x) st8(a.debug_x + (size_t)t * D + slot * 8, v[j]);
+            if (a.x) st8(a.x + (size_t)(t + a.row0) * D + slot * 8, v[j]);
+            if (a.debug_x) st8(a.debug_x + (size_t)(t + a.row0) * D + slot * 8, v[j]);
         }
     }
     if (a.norm == ROW_NONE && !a.frag_out && !a.f32_out) return;
@@ -131,8 +131,8 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
                 else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * p0[j][e];
                 else h[e] = v[j][e];
             }
-            if (a.frag_out) frag_store8(a.frag_out, t, a.frag_koff + i0, h, a.frag_perm);
-            if (a.f32_out) st8(a.f32_out + (size_t)t * a.out_ld + i0, h);
+            if (a.frag_out) frag_store8(a.frag_out, t + a.row0, a.frag_koff + i0, h, a.frag_perm);
+            if (a.f32_out) st8(a.f32_out + (size_t)(t + a.row0) * a.out_ld + i0, h);
         }
     }
 }
@@ -151,14 +151,15 @@ __global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag,
 // Token ids outside [0, V) are clamped into the table (a device-side id cannot be validated by the host).
 __device__ __forceinline__ size_t clamp_row(int32_t id, int V) { return (size_t)(id < 0 ? 0 : (id >= V ? V - 1 : id)); }
 
-__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm) {
+__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
+                                   int frow) {
     const int slot = blockIdx.x * 256 + threadIdx.x;
     if (slot * 8 >= K) return;
     const size_t row = clamp_row(idx[0], V);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(E[row * K + slot * 8 + e]);
-    frag_store8(frag, 0, slot * 8, v, perm);
+    frag_store8(frag, frow, slot * 8, v, perm);
 }
 
 __global__ void gather_f32_kernel(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add,
@@ -339,8 +340,9 @@ hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* fra
 }
 
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
-                              hipStream_t st) {
-    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, perm);
+                              hipStream_t st, int row) {
+    if (row < 0 || row >= 16) return hipErrorInvalidValue;
+    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, perm, row);
     return hipGetLastError();
 }
 

@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.fm_markov_argmax.restype = ctypes.c_int
         L.fm_time_condition.argtypes = [vp, ctypes.c_float, ctypes.c_float, i32, i32, ctypes.c_float, vp]
         L.fm_time_condition.restype = ctypes.c_int
+        L.fm_draft_batch.argtypes = [ctypes.POINTER(vp), i32, vp, vp, vp]
+        L.fm_draft_batch.restype = ctypes.c_int
         L.fm_context_length.argtypes = [vp]
         L.fm_context_length.restype = i32
         L.fm_destroy.argtypes = [vp]
@@ -198,6 +200,13 @@ class Drafter:
 
     def fm_time_condition(self, s: float, t: float, time_dim: int, cond_dim: int, time_scale: float, stream=None):
         check(self.L.fm_time_condition(self.h, s, t, time_dim, cond_dim, time_scale, _stream_ptr(stream)))
+
+    @staticmethod
+    def fm_draft_batch(drafters, anchors, hidden_out, stream=None):
+        """One KV-injection block forward for len(drafters) requests (each drafter holds its own context)."""
+        L = lib()
+        arr = (ctypes.c_void_p * len(drafters))(*[dr.h for dr in drafters])
+        check(L.fm_draft_batch(arr, len(drafters), anchors.data_ptr(), hidden_out.data_ptr(), _stream_ptr(stream)))
 
     # views of the caller-owned cache (layout documented in include/fm.h)
     def kv_layer(self, l: int, which: int):

@@ -155,7 +155,7 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
 
 /* tokens[r] = argmax_v (hidden[r] . lm_head[v]) for r < rows (ties to the lowest index), int32 on the device.
  * logits, if not NULL, receives the full [rows][vocab] f32 logits (a debug path; the fused path never writes them).
- * Errors: FM_E_INVALID (rows < 1 or > block, null hidden / tokens). */
+ * Errors: FM_E_INVALID (rows < 1 or > 16, null hidden / tokens). */
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits,
                        void* stream);
 
@@ -198,6 +198,16 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
  * outside [1, 1024]), FM_E_UNSUPPORTED (more than 49 norms). */
 fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, int32_t cond_dim, float time_scale,
                             void* stream);
+
+/* Batched drafting (module-dflash.ts forwardRows over anchors[]): one KV-injection block forward for B requests at
+ * once. Handle ds[b] holds request b's context (its cache, appended with fm_context_append); all handles share the
+ * same weight tensors and block shape. Every projection streams its weights once for all B * block rows; request b
+ * attends over its own context rows ++ its own block rows. Writes hidden_out [B * block][target_dim] (request b's
+ * rows at b * block) in ds[0]'s workspace's stead; the lm_head over those rows is fm_lm_argmax(ds[0], hidden_out,
+ * B * block, ...). anchors: device int32 [B].
+ * Errors: FM_E_INVALID (null pointers, B < 1, B * block > 16, handles with other shapes or other weight tensors, a
+ * handle twice), FM_E_UNSUPPORTED (flow-map or MTP handles: their blocks are 16 and up to 8 rows). */
+fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const int32_t* anchors, float* hidden_out, void* stream);
 
 /* Current context length (rows appended and not rewound), or -1 for a null handle. */
 int32_t fm_context_length(const fm_drafter* d);

@@ -122,3 +122,56 @@ def test_kvinject_markov_decode(name):
     with pytest.raises(fm.FmError) as ex:
         d.fm_markov_argmax(hid, T + 1, a, cfg["markov_rank"], tok, conf)
     assert ex.value.status == fm.FM_E_INVALID
+
+
+@pytest.mark.parametrize("name", ["small", "kvinject"])
+def test_kvinject_batched_requests(name):
+    """Three requests with their own contexts (different lengths) drafted in one pass: each request's rows equal
+    its own oracle's block and the same handle's single-request draft; tokens by the top-2 gap rule."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL if name == "small" else configs.get("kvinject")
+    W = gen.make_weights(cfg)
+    dw = fm.upload_weights(W)
+    B, G, Ht = 3, cfg["block"], cfg["target_dim"]
+    n = cfg["ctx_rows"]
+    lens = [n, n - 37, n - 90]
+    ds, os_ = [], []
+    for b in range(B):
+        d = fm.Drafter(cfg, dw)
+        o = kvinject.KVInjectOracle(cfg, W)
+        taps = gen.taps(cfg, f"batch-{b}", lens[b])
+        o.context_append(taps, 0)
+        d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+        ds.append(d)
+        os_.append(o)
+    anchors = [int(a) for a in gen.anchors(cfg, name + "-batch", B)]
+    _say(f"{name}: batched draft of {B} requests, contexts {lens}, anchors {anchors}")
+    an = torch.tensor(anchors, dtype=torch.int32, device="cuda")
+    hid = torch.empty(B * G, Ht, dtype=torch.float32, device="cuda")
+    fm.Drafter.fm_draft_batch(ds, an, hid)
+    tok = torch.empty(B * G, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B * G, cfg["vocab"], dtype=torch.float32, device="cuda")
+    ds[0].fm_lm_argmax(hid, B * G, tok, logits)
+    torch.cuda.synchronize()
+    h, t, lg = hid.cpu().numpy(), tok.cpu().numpy(), logits.cpu().numpy()
+    for b in range(B):
+        out, _ = os_[b].draft_block(anchors[b])
+        _, z = os_[b].lm_argmax(out)
+        rows = slice(b * G, (b + 1) * G)
+        e = assert_rows_close(h[rows], out, what=f"request {b} hidden")
+        assert_rows_close(lg[rows], z, what=f"request {b} logits")
+        k = assert_tokens_match(t[rows], z)
+        single = torch.empty(G, Ht, dtype=torch.float32, device="cuda")
+        ds[b].fm_draft_block(single, anchor=an[b:b + 1])
+        torch.cuda.synchronize()
+        s = single.cpu().numpy()
+        assert np.max(np.abs(s - h[rows])) <= 1e-6 * np.max(np.abs(s)), "batched rows differ from the single draft"
+        _say(f"{name}: request {b}: hidden err {e:.2e}, tokens exact on {k}/{G}")
+    with pytest.raises(fm.FmError) as ex:
+        fm.Drafter.fm_draft_batch([ds[0], ds[0]], an, hid)
+    assert ex.value.status == fm.FM_E_INVALID
+    with pytest.raises(fm.FmError) as ex:
+        fm.Drafter.fm_draft_batch(ds * 2, torch.cat([an, an]), torch.empty(6 * G, Ht, device="cuda"))
+    assert ex.value.status == fm.FM_E_INVALID
