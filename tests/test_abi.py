@@ -76,3 +76,16 @@ def test_calls_on_a_null_handle():
     assert L.fm_lm_argmax(None, 0x1000, 1, 0x2000, None, None) == fm.FM_E_INVALID
     assert L.fm_context_length(None) == -1
     L.fm_destroy(None)
+
+
+def test_later_entry_points_reject_bad_arguments_on_the_host():
+    # chained MTP depth, Markov decode, time conditioning and batched drafts validate before any launch
+    L = _lib()
+    assert L.fm_mtp_chain(None, 0x1000, 0x2000, 3, 0, 0, 0x3000, None) == fm.FM_E_INVALID
+    assert L.fm_markov_argmax(None, 0x1000, 5, 0x2000, 256, 0x3000, 0x4000, None, None) == fm.FM_E_INVALID
+    assert L.fm_time_condition(None, 0.0, 1.0, 256, 256, 1000.0, None) == fm.FM_E_INVALID
+    arr = (ctypes.c_void_p * 1)(None)
+    assert L.fm_draft_batch(arr, 1, 0x1000, 0x2000, None) == fm.FM_E_INVALID
+    assert L.fm_draft_batch(None, 1, 0x1000, 0x2000, None) == fm.FM_E_INVALID
+    assert L.fm_draft_batch(arr, 0, 0x1000, 0x2000, None) == fm.FM_E_INVALID
+    assert L.fm_last_error()
