@@ -194,7 +194,7 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     tkb = torch.empty(Bq * g, dtype=torch.int32, device="cuda")
 
     def bstep():
-        fm.Drafter.fm_draft_batch(dks, akb, hkb)
+        fm.Drafter.fm_draft_batch(dks, [{"anchor": akb[b:b + 1]} for b in range(Bq)], hkb)
         dk.fm_lm_argmax(hkb, Bq * g, tkb)
     ms = _time_ms(torch, _graph_of(torch, bstep), 5, reps)
     r = _hbm_row(f"{Bq} KV-injection requests (own 2048-row contexts) drafted in one pass + lm_head argmax over "
@@ -207,7 +207,8 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     mc = configs.get("mtp")
     print("[bench] MTP weights", file=sys.stderr, flush=True)
     Wm = gen.make_weights(mc)
-    dm = fm.Drafter(mc, fm.upload_weights(Wm))
+    dwm = fm.upload_weights(Wm)
+    dm = fm.Drafter(mc, dwm)
     H, NKV, HD = mc["dim"], mc["kv_heads"], mc["head_dim"]
     dm.kv_layer(0, 0).normal_()
     dm.kv_layer(0, 1).normal_()
@@ -225,6 +226,29 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
         ms = _time_ms(torch, _graph_of(torch, mstep), 5, reps)
         rows[f"mtp_pass_M{M}"] = _hbm_row(f"MTP pass, M = {M} rows + Q8_0 lm_head argmax", ms,
                                           mw + 2 * (pos0 + M) * NKV * HD * 4, "passes/s")
+    # four sequences' 2-row passes in one batched pass (fm_draft_batch) + the lm_head over the 8 rows
+    Bm, Mb = 4, 2
+    dms = [dm] + [fm.Drafter(mc, dwm) for _ in range(Bm - 1)]
+    for b in range(1, Bm):
+        dms[b].kv_layer(0, 0).normal_()
+        dms[b].kv_layer(0, 1).normal_()
+    eb, hb = gen.mtp_inputs(mc, Bm * Mb)
+    eb, hb = torch.from_numpy(eb).cuda(), torch.from_numpy(hb).cuda()
+    posb = mc["max_ctx"] - Mb
+    reqs = [dict(rows=Mb, pos=posb, kv_lo=0, embed_rows=eb[b * Mb:(b + 1) * Mb], prev_hidden=hb[b * Mb:(b + 1) * Mb])
+            for b in range(Bm)]
+    hbm = torch.empty(Bm * Mb, H, dtype=torch.float32, device="cuda")
+    tbm = torch.empty(Bm * Mb, dtype=torch.int32, device="cuda")
+
+    def bmstep():
+        fm.Drafter.fm_draft_batch(dms, reqs, hbm)
+        dm.fm_lm_argmax(hbm, Bm * Mb, tbm)
+    ms = _time_ms(torch, _graph_of(torch, bmstep), 5, reps)
+    r = _hbm_row(f"{Bm} MTP sequences x {Mb} rows in one pass + Q8_0 lm_head argmax over {Bm * Mb} rows", ms,
+                 mw + Bm * 2 * (posb + Mb) * NKV * HD * 4, "passes/s")
+    r["value"] = Bm * 1e3 / ms   # sequences' passes per second
+    rows["mtp_batch4_M2"] = r
+    del dms
     # chained depth: 3 single-row passes, each on the previous draft's table row and h' (fm_mtp_chain)
     steps = 3
     posc = mc["max_ctx"] - steps
@@ -239,7 +263,7 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     cbytes = sum(mw + 2 * (posc + i + 1) * NKV * HD * 4 for i in range(steps))
     rows["mtp_chain_3"] = _hbm_row("MTP chained depth: 3 single-row passes (table row gather + pass + Q8_0 lm_head "
                                    "argmax each)", ms, cbytes, "chains/s")
-    del dm, Wm
+    del dm, Wm, dwm
     return rows
 
 

@@ -905,7 +905,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
 // B requests in one pass (B = 1: fm_draft_block): handle ds[b] holds request b's context cache, handle ds[0]'s
 // workspace holds the B * block rows; every projection streams its weights once for all rows, each request attends
 // over its own cache rows ++ its own block rows.
-fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* anchors, float* hidden_out,
+fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* const* anchors, float* hidden_out,
                                float* debug_layers, hipStream_t st) {
     fm_drafter* d = ds[0];
     const auto& c = d->c;
@@ -921,7 +921,7 @@ fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* anch
 
     // block rows of request b: H_d[0] = tok_proj(E[anchor_b]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]
     for (int b = 0; b < B; ++b)
-        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, anchors + b, fragA, d->perm, st, b));
+        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, anchors[b], fragA, d->perm, st, b));
     int S = 0;
     CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, B, SK_PARTIAL, 0,
                &S, st));
@@ -1003,14 +1003,24 @@ fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* anch
 
 fm_status kvinject_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
     fm_drafter* ds[1] = {d};
-    return kvinject_draft_batch(ds, 1, ba->anchor, hidden_out, ba->debug_layers, st);
+    const int32_t* an[1] = {ba->anchor};
+    return kvinject_draft_batch(ds, 1, an, hidden_out, ba->debug_layers, st);
 }
 
 // ── MTP ─────────────────────────────────────────────────────────────────────────────────────────
-fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+// B requests in one pass (B = 1: fm_draft_block): request b's M_b rows are rows off_b .. off_b + M_b - 1 of the
+// pass (off_b = M_0 + ... + M_(b-1)), handle ds[b] holds its KV cache; the projections run once over all rows, the
+// q/k preparation (with its cache write) and the causal attention run per request.
+fm_status mtp_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* const* as, float* hidden_out,
+                          hipStream_t st) {
+    fm_drafter* d = ds[0];
     const auto& c = d->c;
-    const int H = c.dim, M = ba->rows, NH = c.heads, NKV = c.kv_heads, HD = c.head_dim;
+    const int H = c.dim, NH = c.heads, NKV = c.kv_heads, HD = c.head_dim;
     const int qw = NH * 2 * HD, kw = NKV * HD, qkvw = qw + 2 * kw;
+    int off[TMAX + 1];
+    off[0] = 0;
+    for (int b = 0; b < B; ++b) off[b + 1] = off[b] + as[b]->rows;
+    const int M = off[B];
     float* part = d->at<float>(d->p.part);
     float* x = d->at<float>(d->p.x);
     uint8_t* fragA = d->at<uint8_t>(d->p.fragA);
@@ -1024,17 +1034,19 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
     auto Dd = [&](const char* n) { return d->W(std::string(n) + ".d"); };
 
     // x = eh_proj([enorm(e); hnorm(h)])
-    for (int side = 0; side < 2; ++side) {
-        RowArgs r = rows_base(d, H, M);
-        r.in_rows = side == 0 ? ba->embed_rows : ba->prev_hidden;
-        r.in_ld = H;
-        r.norm = ROW_RMS;
-        r.w_f32 = d->F(side == 0 ? "enorm" : "hnorm");
-        r.eps = c.rms_eps;
-        r.frag_out = fragA;
-        r.frag_koff = side * H;
-        CHK(rows(r, st));
-    }
+    for (int b = 0; b < B; ++b)
+        for (int side = 0; side < 2; ++side) {
+            RowArgs r = rows_base(d, H, as[b]->rows);
+            r.row0 = off[b];
+            r.in_rows = side == 0 ? as[b]->embed_rows : as[b]->prev_hidden;
+            r.in_ld = H;
+            r.norm = ROW_RMS;
+            r.w_f32 = d->F(side == 0 ? "enorm" : "hnorm");
+            r.eps = c.rms_eps;
+            r.frag_out = fragA;
+            r.frag_koff = side * H;
+            CHK(rows(r, st));
+        }
     int S = 0;
     CHK(skinny(d, {{Q("eh_proj"), Dd("eh_proj"), nullptr, nullptr, nullptr, fragA, part, H, H}}, 2 * H, M, SK_PARTIAL,
                0, &S, st));
@@ -1056,13 +1068,15 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
                 {Q("attn_k"), Dd("attn_k"), nullptr, nullptr, nullptr, fragH, qkv + qw, kw, qkvw},
                 {Q("attn_v"), Dd("attn_v"), nullptr, nullptr, nullptr, fragH, qkv + qw + kw, kw, qkvw}},
                H, M, SK_F32, 0, nullptr, st));
-    {
+    for (int b = 0; b < B; ++b) {
+        fm_drafter* e = ds[b];
+        float* qb = qkv + (size_t)off[b] * qkvw;
         MtpPrepArgs p{};
-        p.qf = qkv;
-        p.kt = qkv + qw;
-        p.vt = qkv + qw + kw;
+        p.qf = qb;
+        p.kt = qb + qw;
+        p.vt = qb + qw + kw;
         p.qf_ld = p.kt_ld = p.vt_ld = qkvw;
-        p.M = M;
+        p.M = as[b]->rows;
         p.NH = NH;
         p.NKV = NKV;
         p.HD = HD;
@@ -1070,20 +1084,18 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
         p.qn = d->F("attn_q_norm");
         p.kn = d->F("attn_k_norm");
         p.eps = c.rms_eps;
-        p.rope_tab = d->at<float>(d->p.rope);
-        p.pos0 = ba->pos;
-        p.qout = qout;
-        p.kc = (float*)d->kv;
-        p.vc = (float*)d->kv + (size_t)c.max_ctx * kw;
+        p.rope_tab = e->at<float>(e->p.rope);
+        p.pos0 = as[b]->pos;
+        p.qout = qout + (size_t)off[b] * NH * HD;
+        p.kc = (float*)e->kv;
+        p.vc = (float*)e->kv + (size_t)e->c.max_ctx * kw;
         HIPCHK(launch_mtp_prep(p, st));
-    }
-    {
         QPrep qp{};
-        qp.q = qout;
+        qp.q = qout + (size_t)off[b] * NH * HD;
         qp.q_ld = NH * HD;
         qp.q_hs = HD;
-        CHK(attend(d, qp, M, 0, ba->kv_lo, ba->pos + M, nullptr, nullptr, 0, 0, ba->pos, 1.f / sqrtf((float)HD),
-                   qkv + HD, qkvw, 2 * HD, fragO, st));
+        CHK(attend(e, qp, as[b]->rows, 0, as[b]->kv_lo, as[b]->pos + as[b]->rows, nullptr, nullptr, 0, 0, as[b]->pos,
+                   1.f / sqrtf((float)HD), qb + HD, qkvw, 2 * HD, fragO, st, off[b]));
     }
     CHK(skinny(d, {{Q("attn_output"), Dd("attn_output"), nullptr, nullptr, nullptr, fragO, part, H, H}}, NH * HD, M,
                SK_PARTIAL, 0, &S, st));
@@ -1109,7 +1121,7 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
         r.part = part;
         r.S = S;
         r.part_stride = pstr;
-        if (ba->debug_layers) r.debug_x = ba->debug_layers;
+        if (B == 1 && as[0]->debug_layers) r.debug_x = as[0]->debug_layers;
         r.norm = ROW_RMS;
         r.w_f32 = d->F("shared_head_norm");
         r.eps = c.rms_eps;
@@ -1118,6 +1130,12 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
         CHK(rows(r, st));
     }
     return FM_OK;
+}
+
+fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    fm_drafter* ds[1] = {d};
+    const fm_block_args* as[1] = {ba};
+    return mtp_draft_batch(ds, 1, as, hidden_out, st);
 }
 
 fm_status kvinject_create(fm_drafter*, hipStream_t) { return FM_OK; }
@@ -1381,21 +1399,23 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     return FM_OK;
 }
 
-fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const int32_t* anchors, float* hidden_out, void* stream) {
+fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out,
+                         void* stream) {
     g_err.clear();
-    if (!ds || !anchors || !hidden_out || B < 1) return fail(FM_E_INVALID, "null argument or B < 1");
+    if (!ds || !args || !hidden_out || B < 1) return fail(FM_E_INVALID, "null argument or B < 1");
+    if (B > TMAX) return fail(FM_E_INVALID, "B %d > %d", B, TMAX);
     for (int b = 0; b < B; ++b)
         if (!ds[b]) return fail(FM_E_INVALID, "null handle %d", b);
     const auto& c = ds[0]->c;
-    if (c.variant != FM_VARIANT_KVINJECT) return fail(FM_E_UNSUPPORTED, "batched drafts: KV-injection drafters only");
-    if (B * c.block > TMAX) return fail(FM_E_INVALID, "B %d x block %d > %d rows", B, c.block, TMAX);
+    if (c.variant == FM_VARIANT_FLOWMAP) return fail(FM_E_UNSUPPORTED, "batched drafts: KV-injection and MTP drafters");
     for (int b = 1; b < B; ++b) {
         const fm_drafter* e = ds[b];
         const auto& f = e->c;   // the shape of the block computation (max_ctx may differ: each cache is its own)
         if (f.variant != c.variant || f.dim != c.dim || f.heads != c.heads || f.head_dim != c.head_dim ||
             f.kv_heads != c.kv_heads || f.layers != c.layers || f.ffn != c.ffn || f.block != c.block ||
             f.target_dim != c.target_dim || f.n_taps != c.n_taps || f.vocab != c.vocab || f.mlp != c.mlp ||
-            f.kv_dtype != c.kv_dtype || f.wtype != c.wtype || f.rms_eps != c.rms_eps || ds[b]->perm != ds[0]->perm)
+            f.kv_dtype != c.kv_dtype || f.wtype != c.wtype || f.rms_eps != c.rms_eps || f.rope != c.rope ||
+            f.rope_dims != c.rope_dims || f.rope_theta != c.rope_theta || ds[b]->perm != ds[0]->perm)
             return fail(FM_E_INVALID, "handle %d: another configuration", b);
         for (const auto& n : required_names(c)) {
             const auto& w0 = ds[0]->w;
@@ -1408,7 +1428,33 @@ fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const int32_t* anchor
         for (int a = 0; a < b; ++a)
             if (ds[a] == e) return fail(FM_E_INVALID, "handle %d appears twice", b);
     }
-    return kvinject_draft_batch(ds, B, anchors, hidden_out, nullptr, (hipStream_t)stream);
+    hipStream_t st = (hipStream_t)stream;
+    if (c.variant == FM_VARIANT_KVINJECT) {
+        if (B * c.block > TMAX) return fail(FM_E_INVALID, "B %d x block %d > %d rows", B, c.block, TMAX);
+        const int32_t* an[TMAX];
+        for (int b = 0; b < B; ++b) {
+            if (!args[b].anchor) return fail(FM_E_INVALID, "request %d: null anchor", b);
+            an[b] = args[b].anchor;
+        }
+        return kvinject_draft_batch(ds, B, an, hidden_out, nullptr, st);
+    }
+    const fm_block_args* as[TMAX];
+    int rows_total = 0;
+    for (int b = 0; b < B; ++b) {
+        const fm_block_args* a = &args[b];
+        if (!a->embed_rows || !a->prev_hidden) return fail(FM_E_INVALID, "request %d: null embed_rows / prev_hidden", b);
+        if (a->rows < 1 || a->rows > c.block)
+            return fail(FM_E_INVALID, "request %d: rows %d outside [1, %d]", b, a->rows, c.block);
+        if (a->pos < 0 || a->kv_lo < 0 || a->kv_lo > a->pos)
+            return fail(FM_E_INVALID, "request %d: need 0 <= kv_lo (%d) <= pos (%d)", b, a->kv_lo, a->pos);
+        if ((long long)a->pos + a->rows > ds[b]->c.max_ctx)
+            return fail(FM_E_CONTEXT_FULL, "request %d: pos %d + rows %d > KV cache rows %d", b, a->pos, a->rows,
+                        ds[b]->c.max_ctx);
+        rows_total += a->rows;
+        as[b] = a;
+    }
+    if (rows_total > TMAX) return fail(FM_E_INVALID, "%d rows in all > %d", rows_total, TMAX);
+    return mtp_draft_batch(ds, B, as, hidden_out, st);
 }
 
 int32_t fm_context_length(const fm_drafter* d) { return d ? d->length : -1; }

@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.fm_markov_argmax.restype = ctypes.c_int
         L.fm_time_condition.argtypes = [vp, ctypes.c_float, ctypes.c_float, i32, i32, ctypes.c_float, vp]
         L.fm_time_condition.restype = ctypes.c_int
-        L.fm_draft_batch.argtypes = [ctypes.POINTER(vp), i32, vp, vp, vp]
+        L.fm_draft_batch.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(FmBlockArgs), vp, vp]
         L.fm_draft_batch.restype = ctypes.c_int
         L.fm_context_length.argtypes = [vp]
         L.fm_context_length.restype = i32
@@ -202,11 +202,18 @@ class Drafter:
         check(self.L.fm_time_condition(self.h, s, t, time_dim, cond_dim, time_scale, _stream_ptr(stream)))
 
     @staticmethod
-    def fm_draft_batch(drafters, anchors, hidden_out, stream=None):
-        """One KV-injection block forward for len(drafters) requests (each drafter holds its own context)."""
+    def fm_draft_batch(drafters, requests, hidden_out, stream=None):
+        """One block forward for len(drafters) requests, each drafter holding its own context; requests[b] holds
+        fm_draft_block's keyword arguments for request b (anchor; or rows, pos, kv_lo, embed_rows, prev_hidden)."""
         L = lib()
-        arr = (ctypes.c_void_p * len(drafters))(*[dr.h for dr in drafters])
-        check(L.fm_draft_batch(arr, len(drafters), anchors.data_ptr(), hidden_out.data_ptr(), _stream_ptr(stream)))
+        B = len(drafters)
+        arr = (ctypes.c_void_p * B)(*[dr.h for dr in drafters])
+        args = (FmBlockArgs * B)()
+        for b, r in enumerate(requests):
+            ptr = lambda k: r[k].data_ptr() if r.get(k) is not None else None
+            args[b] = FmBlockArgs(ptr("anchor"), r.get("pos", 0), r.get("rows", 0), r.get("kv_lo", 0),
+                                  ptr("embed_rows"), ptr("prev_hidden"), None)
+        check(L.fm_draft_batch(arr, B, args, hidden_out.data_ptr(), _stream_ptr(stream)))
 
     # views of the caller-owned cache (layout documented in include/fm.h)
     def kv_layer(self, l: int, which: int):

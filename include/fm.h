@@ -199,15 +199,18 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
 fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, int32_t cond_dim, float time_scale,
                             void* stream);
 
-/* Batched drafting (module-dflash.ts forwardRows over anchors[]): one KV-injection block forward for B requests at
- * once. Handle ds[b] holds request b's context (its cache, appended with fm_context_append); all handles share the
- * same weight tensors and block shape. Every projection streams its weights once for all B * block rows; request b
- * attends over its own context rows ++ its own block rows. Writes hidden_out [B * block][target_dim] (request b's
- * rows at b * block) in ds[0]'s workspace's stead; the lm_head over those rows is fm_lm_argmax(ds[0], hidden_out,
- * B * block, ...). anchors: device int32 [B].
- * Errors: FM_E_INVALID (null pointers, B < 1, B * block > 16, handles with other shapes or other weight tensors, a
- * handle twice), FM_E_UNSUPPORTED (flow-map or MTP handles: their blocks are 16 and up to 8 rows). */
-fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const int32_t* anchors, float* hidden_out, void* stream);
+/* Batched drafting (module-dflash.ts forwardRows over anchors[]; for the MTP head, several sequences' rows in one
+ * pass): one block forward for B requests. Handle ds[b] holds request b's context (its KV cache); all handles share
+ * the same weight tensors and block shape (max_ctx may differ). args[b] is request b's fm_draft_block argument
+ * (KV-injection: anchor; MTP: rows, pos, kv_lo, embed_rows, prev_hidden; debug_layers is ignored). Every projection
+ * streams its weights once for all rows; each request attends over its own cache (KV-injection: its context rows
+ * ++ its block rows; MTP: causal over [kv_lo, pos + m], after writing its rows' K/V at pos). hidden_out gets the
+ * rows in request order (KV-injection: block rows per request; MTP: args[b].rows each), at most 16 in all; the
+ * lm_head over them is fm_lm_argmax(ds[0], hidden_out, rows, ...).
+ * Errors: FM_E_INVALID (null pointers, B < 1, more than 16 rows, handles with other shapes or other weight
+ * tensors, a handle twice, a request's own fm_draft_block errors), FM_E_CONTEXT_FULL (an MTP request past its
+ * cache), FM_E_UNSUPPORTED (flow-map handles: a block alone is 16 rows). */
+fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out, void* stream);
 
 /* Current context length (rows appended and not rewound), or -1 for a null handle. */
 int32_t fm_context_length(const fm_drafter* d);

@@ -150,7 +150,7 @@ def test_kvinject_batched_requests(name):
     _say(f"{name}: batched draft of {B} requests, contexts {lens}, anchors {anchors}")
     an = torch.tensor(anchors, dtype=torch.int32, device="cuda")
     hid = torch.empty(B * G, Ht, dtype=torch.float32, device="cuda")
-    fm.Drafter.fm_draft_batch(ds, an, hid)
+    fm.Drafter.fm_draft_batch(ds, [{"anchor": an[b:b + 1]} for b in range(B)], hid)
     tok = torch.empty(B * G, dtype=torch.int32, device="cuda")
     logits = torch.empty(B * G, cfg["vocab"], dtype=torch.float32, device="cuda")
     ds[0].fm_lm_argmax(hid, B * G, tok, logits)
@@ -170,8 +170,9 @@ def test_kvinject_batched_requests(name):
         assert np.max(np.abs(s - h[rows])) <= 1e-6 * np.max(np.abs(s)), "batched rows differ from the single draft"
         _say(f"{name}: request {b}: hidden err {e:.2e}, tokens exact on {k}/{G}")
     with pytest.raises(fm.FmError) as ex:
-        fm.Drafter.fm_draft_batch([ds[0], ds[0]], an, hid)
+        fm.Drafter.fm_draft_batch([ds[0], ds[0]], [{"anchor": an[0:1]}, {"anchor": an[1:2]}], hid)
     assert ex.value.status == fm.FM_E_INVALID
     with pytest.raises(fm.FmError) as ex:
-        fm.Drafter.fm_draft_batch(ds * 2, torch.cat([an, an]), torch.empty(6 * G, Ht, device="cuda"))
+        fm.Drafter.fm_draft_batch(ds * 2, [{"anchor": an[b % B:b % B + 1]} for b in range(6)],
+                                  torch.empty(6 * G, Ht, device="cuda"))
     assert ex.value.status == fm.FM_E_INVALID

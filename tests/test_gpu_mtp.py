@@ -147,3 +147,62 @@ def test_mtp_chain(name):
     with pytest.raises(fm.FmError) as ex:
         d.fm_mtp_chain(tokens, hid[0], 0, 0, 0, hid)
     assert ex.value.status == fm.FM_E_INVALID
+
+
+@pytest.mark.parametrize("name", ["small", "mtp"])
+def test_mtp_batched_requests(name):
+    """Three MTP requests (2, 1 and 4 rows, their own caches, positions and kv_lo) in one pass: each request's rows
+    and new cache rows equal its own oracle's and the same handle's single-request pass; tokens by the gap rule."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL if name == "small" else configs.get("mtp")
+    W = gen.make_weights(cfg)
+    dw = fm.upload_weights(W)
+    H, mc = cfg["dim"], cfg["max_ctx"]
+    Ms = [2, 1, 4]
+    poss = [mc - 2, mc - 50, mc - 14]
+    kvlos = [0, 7, (mc - 14) // 3]
+    kc, vc = gen.mtp_cache_rows(cfg, mc)
+    e_all, h_all = gen.mtp_inputs(cfg, sum(Ms))
+    ds, reqs, outs, oks = [], [], [], []
+    r0 = 0
+    for b, (M, pos, kvl) in enumerate(zip(Ms, poss, kvlos)):
+        d = fm.Drafter(cfg, dw)
+        d.kv_layer(0, 0)[:pos].copy_(torch.from_numpy(kc[:pos]))
+        d.kv_layer(0, 1)[:pos].copy_(torch.from_numpy(vc[:pos]))
+        o = mtp.MTPOracle(cfg, W)
+        o.set_cache_rows(kc[:pos], vc[:pos])
+        e, h = e_all[r0:r0 + M], h_all[r0:r0 + M]
+        outs.append(o.forward(e, h, pos, kvl))
+        oks.append(o)
+        reqs.append(dict(rows=M, pos=pos, kv_lo=kvl, embed_rows=torch.from_numpy(e.copy()).cuda(),
+                         prev_hidden=torch.from_numpy(h.copy()).cuda()))
+        ds.append(d)
+        r0 += M
+    _say(f"{name}: batched pass of {len(Ms)} requests, rows {Ms}, positions {poss}, kv_lo {kvlos}")
+    hid = torch.empty(sum(Ms), H, dtype=torch.float32, device="cuda")
+    fm.Drafter.fm_draft_batch(ds, reqs, hid)
+    tok = torch.empty(sum(Ms), dtype=torch.int32, device="cuda")
+    logits = torch.empty(sum(Ms), cfg["vocab"], dtype=torch.float32, device="cuda")
+    ds[0].fm_lm_argmax(hid, sum(Ms), tok, logits)
+    torch.cuda.synchronize()
+    hg, tg, lg = hid.cpu().numpy(), tok.cpu().numpy(), logits.cpu().numpy()
+    r0 = 0
+    for b, M in enumerate(Ms):
+        rows = slice(r0, r0 + M)
+        pos = poss[b]
+        err = assert_rows_close(hg[rows], outs[b], what=f"request {b} hidden")
+        _, z = oks[b].lm_argmax(outs[b])
+        assert_rows_close(lg[rows], z, what=f"request {b} logits")
+        k = assert_tokens_match(tg[rows], z)
+        assert_rows_close(ds[b].kv_layer(0, 0)[pos:pos + M].cpu().numpy(), oks[b].Kc[pos:pos + M], what="new K")
+        assert_rows_close(ds[b].kv_layer(0, 1)[pos:pos + M].cpu().numpy(), oks[b].Vc[pos:pos + M], what="new V")
+        single = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        ds[b].fm_draft_block(single, pos=pos, rows=M, kv_lo=kvlos[b], embed_rows=reqs[b]["embed_rows"],
+                             prev_hidden=reqs[b]["prev_hidden"])
+        torch.cuda.synchronize()
+        s = single.cpu().numpy()
+        assert np.max(np.abs(s - hg[rows])) <= 1e-6 * np.max(np.abs(s)), "batched rows differ from the single pass"
+        _say(f"{name}: request {b}: hidden err {err:.2e}, tokens exact on {k}/{M}")
+        r0 += M
