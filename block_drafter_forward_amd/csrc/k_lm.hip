@@ -484,101 +484,7 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
     }
 }
 
-// ── DSpark Markov correction (KV-injection page, forwardRows' greedy loop) ────────────────────────
-// One decode step k: scores[v] = z_k[v] + sum_j e1[j] w2[j][v] with e1 = w1[prev] (bf16 [V][r] rows, w2 bf16
-// [r][V]), then the argmax over v into a 64-bit key (same order as the lm_head kernel). Each thread owns 4
-// consecutive columns (one 8-byte load per w2 row), 16 rows' loads in flight; e1 goes through LDS as f32.
-// V % 4 == 0; columns past V (the last work-group) are clamped and left out of the argmax.
-__global__ __launch_bounds__(256) void markov_step_kernel(MarkovArgs a, int k) {
-    __shared__ float e1[MARKOV_MAX_RANK];
-    __shared__ float wb[4];
-    __shared__ int wi[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int prev = (int)min(max(k == 0 ? a.anchor[0] : a.tokens[k - 1], 0), a.V - 1);
-    for (int j = tid; j < a.r; j += 256) e1[j] = bf16_to_f32(a.w1[(size_t)prev * a.r + j]);
-    __syncthreads();
-    const int c0 = (blockIdx.x * 256 + tid) * 4;
-    const bool own = c0 < a.V;
-    const int cc = own ? c0 : a.V - 4;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* w = a.w2 + cc;
-    int j = 0;
-    for (; j + 16 <= a.r; j += 16) {
-        uint2 q[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) q[u] = *(const uint2*)(w + (size_t)(j + u) * a.V);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const float e = e1[j + u];
-            acc[0] += e * bf16_lo(q[u].x); acc[1] += e * bf16_hi(q[u].x);
-            acc[2] += e * bf16_lo(q[u].y); acc[3] += e * bf16_hi(q[u].y);
-        }
-    }
-    for (; j < a.r; ++j) {
-        const uint2 q = *(const uint2*)(w + (size_t)j * a.V);
-        const float e = e1[j];
-        acc[0] += e * bf16_lo(q.x); acc[1] += e * bf16_hi(q.x);
-        acc[2] += e * bf16_lo(q.y); acc[3] += e * bf16_hi(q.y);
-    }
-    const float4 zb = *(const float4*)(a.z + (size_t)k * a.V + cc);
-    const float sc[4] = {zb.x + acc[0], zb.y + acc[1], zb.z + acc[2], zb.w + acc[3]};
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
-    if (own) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (a.scores) a.scores[(size_t)k * a.V + cc + c] = sc[c];
-            if (sc[c] > best) { best = sc[c]; bidx = cc + c; }
-        }
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float ob = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bidx, o, 64);
-        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
-    }
-    if (lane == 0) { wb[wave] = best; wi[wave] = bidx; }
-    __syncthreads();
-    if (tid == 0) {
-        float b = wb[0];
-        int bi = wi[0];
-        for (int w2i = 1; w2i < 4; ++w2i)
-            if (wb[w2i] > b || (wb[w2i] == b && wi[w2i] < bi)) { b = wb[w2i]; bi = wi[w2i]; }
-        if (bi != 0x7fffffff) {
-            const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
-            atomicMax(&a.key[0], key);
-        }
-    }
-}
-
-// Step k's token from the key (the key is cleared for the next step) and its confidence
-// sigmoid([block_k; e1] conf.w + conf.b) with the same e1 as the step (the w1 row of the previous token).
-__global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs a, int k) {
-    __shared__ float red[4];
-    const int tid = threadIdx.x;
-    const int prev = (int)min(max(k == 0 ? a.anchor[0] : a.tokens[k - 1], 0), a.V - 1);
-    float s = 0.f;
-    for (int j = tid; j < a.D; j += 256) s += a.block[(size_t)k * a.D + j] * bf16_to_f32(a.cw[j]);
-    for (int j = tid; j < a.r; j += 256) s += bf16_to_f32(a.w1[(size_t)prev * a.r + j]) * bf16_to_f32(a.cw[a.D + j]);
-    s = block_sum256(s, red);
-    if (tid == 0) {
-        const unsigned long long key = a.key[0];
-        a.tokens[k] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-        a.key[0] = 0ull;
-        a.conf[k] = 1.f / (1.f + expf(-(s + bf16_to_f32(a.cb[0]))));
-    }
-}
-
 }  // namespace
-
-hipError_t launch_markov_step(const MarkovArgs& a, int k, hipStream_t st) {
-    if (a.r < 1 || a.r > MARKOV_MAX_RANK || a.V < 4 || a.V % 4 || k < 0) return hipErrorInvalidValue;
-    markov_step_kernel<<<(a.V / 4 + 255) / 256, 256, 0, st>>>(a, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    markov_finalize_kernel<<<1, 256, 0, st>>>(a, k);
-    return hipGetLastError();
-}
 
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
     if (a.T > 16) return hipErrorInvalidValue;
