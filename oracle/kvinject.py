@@ -50,7 +50,9 @@ class KVInjectOracle:
         n = taps.shape[0]
         if start < 0 or start > self.length:
             raise ValueError("start beyond the current context length")
-        if start + n + cfg["block"] > cfg["max_ctx"]:
+        # capacity: the flow-map page's extendContext rule (room for a block and one more row), taken for every
+        # variant; the KV-injection page grows its arrays and states no limit
+        if start + n + cfg["block"] + 1 > cfg["max_ctx"]:
             raise ContextFull("context full")
         hc = self.build_context(taps)
         for i in range(cfg["layers"]):
