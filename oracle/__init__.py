@@ -16,8 +16,8 @@ Modules
   loops     a pure-Python-loop second implementation of the flow-map forward for tiny shapes
 
 Parity pins: every function is checked in tests/test_oracle_*.py against closed forms, invariants, hand-worked
-values from the pages' formulas or brute-force loops.  One reading is not pinned by any of these: the tanh form
-of the gated-GELU activation of the KV-injection drafter (the page only names it) -- parity unpinned beyond its
-stated formula.
+values from the pages' formulas or brute-force loops.  One reading is not pinned by any of these: that the
+gated-GELU activation of the KV-injection drafter (the page only names it) is the tanh form -- parity unpinned
+beyond that reading; the tanh formula itself is pinned against PyTorch's tanh-approximate GELU.
 """
 from . import prims, flowmap, kvinject, mtp, loops  # noqa: F401

@@ -9,7 +9,7 @@ Follows page "mlx-bun 0.4.0 -> 1.0.0", src/spec/dspark/module-dflash.ts: the fil
 
 Readings: no RoPE, no q/k norm, no mask (batch of one); the head output is not cast before the lm_head; the lm_head
 table E is also the embedding table. The activation the page calls geluApprox is read as the tanh form (parity
-unpinned beyond that formula).
+unpinned beyond that reading; the formula is pinned against PyTorch's tanh-approximate GELU).
 
 Markov decode (forwardRows' greedy loop with the Markov head, #markov, #confidence): with block = RMSNorm(H_d;
 out_norm) and base logits z = (block out_proj) E^T, step k takes e1 = w1[prev] (prev = the anchor, then the

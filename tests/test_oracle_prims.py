@@ -229,6 +229,17 @@ def test_gelu_tanh_is_close_to_exact_gelu():
     assert P.gelu_tanh(np.array([0.0]))[0] == 0.0
 
 
+def test_gelu_tanh_matches_an_independent_implementation():
+    # The tanh form (Hendrycks & Gimpel) as PyTorch implements it, in float64 on the CPU: a second, independent
+    # implementation of the published formula; plus its odd-part identity gelu(x) - gelu(-x) = x.
+    torch = pytest.importorskip("torch")
+    x = np.concatenate([np.linspace(-12, 12, 4801), [1e-8, -3e-5, 0.5, 1.0, 2.0, 40.0, -40.0]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    # relative 1e-13 where the value is not tiny; on the far negative side 1 + tanh cancels, so absolute there
+    assert np.all(np.abs(P.gelu_tanh(x) - ref) <= 1e-13 * np.abs(ref) + 1e-15)
+    assert np.max(np.abs(P.gelu_tanh(x) - P.gelu_tanh(-x) - x)) < 1e-13 * 40
+
+
 def test_silu_sigmoid_values():
     assert P.sigmoid(np.array([0.0]))[0] == 0.5
     assert math.isclose(P.silu(np.array([2.0]))[0], 2.0 / (1.0 + math.exp(-2.0)), rel_tol=1e-15)
