@@ -307,8 +307,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline, lm_head and 8192-row prefill only")
     ap.add_argument("--pmc-probe", action="store_true",
-                    help="for a rocprofv3 --pmc pass: set up, run fm_lm_argmax 5 times and one elementwise kernel that "
-                         "reads 1 GiB and writes 1 GiB (the counters' scale reference), then exit")
+                    help="for a rocprofv3 --pmc pass: set up, run fm_lm_argmax 5 times on the FlashMap and 5 times on "
+                         "the MTP head's Q8_0 table, and one elementwise kernel that reads 1 GiB and writes 1 GiB (the "
+                         "counters' scale reference), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -341,12 +342,21 @@ def main():
         step()
         for _ in range(5):
             d.fm_lm_argmax(hidden, T, tokens)
+        # the MTP head's Q8_0 lm_head (248320 x 5120), 8 rows
+        mc = configs.get("mtp")
+        dm = fm.Drafter(mc, fm.upload_weights(gen.make_weights(mc)))
+        _, hm = gen.mtp_inputs(mc, 8)
+        hm = torch.from_numpy(hm).cuda()
+        tm = torch.empty(8, dtype=torch.int32, device="cuda")
+        for _ in range(5):
+            dm.fm_lm_argmax(hm, 8, tm)
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         src.fill_(1.0)
         dst = torch.empty_like(src)
         torch.mul(src, 2.0, out=dst)   # one elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-        print("[bench] pmc probe done: 5 x fm_lm_argmax, one 1 GiB elementwise pass", file=sys.stderr, flush=True)
+        print("[bench] pmc probe done: 5 x fm_lm_argmax (bf16), 5 x fm_lm_argmax (Q8_0), one 1 GiB elementwise pass",
+              file=sys.stderr, flush=True)
         return
 
     stream = torch.cuda.current_stream()
