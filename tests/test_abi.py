@@ -90,3 +90,13 @@ def test_later_entry_points_reject_bad_arguments_on_the_host():
     assert L.fm_draft_batch(None, 1, args, 0x2000, None) == fm.FM_E_INVALID
     assert L.fm_draft_batch(arr, 0, args, 0x2000, None) == fm.FM_E_INVALID
     assert L.fm_last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # bench.py measures one GPU; asking for more exits with a message before any GPU work
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
