@@ -273,7 +273,8 @@ std::vector<std::string> required_names(const fm_config& c) {
             }
         }
     } else if (c.variant == FM_VARIANT_KVINJECT) {
-        n = {"W_c", "ctx_norm", "tok_proj", "mask_emb", "block_pos", "out_norm", "out_proj", "lm_head.weight"};
+        n = {"W_c", "ctx_norm", "tok_proj", "block_pos", "out_norm", "out_proj", "lm_head.weight"};
+        if (c.block > 1) n.push_back("mask_emb");   // [block - 1][dim]: no rows in a one-row block
         for (int i = 0; i < c.layers; ++i)
             for (const char* p : {"attn_norm", "q", "k", "v", "o", "ff_norm", "gate", "up", "down"}) {
                 snprintf(b, sizeof b, "bb.%d.%s", i, p);

@@ -156,7 +156,7 @@ class Drafter:
             raise FmError(FM_E_INVALID, last_error())
         self.kv = torch.empty(kvb, dtype=torch.uint8, device="cuda")
         self.ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-        names = list(dev_weights.keys())
+        names = [n for n in dev_weights if dev_weights[n].numel() > 0]   # a tensor with no elements has no memory
         self._names = (ctypes.c_char_p * len(names))(*[n.encode() for n in names])
         self._ptrs = (ctypes.c_void_p * len(names))(*[dev_weights[n].data_ptr() for n in names])
         h = ctypes.c_void_p()

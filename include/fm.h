@@ -146,6 +146,7 @@ typedef struct fm_block_args {
  *             cross-attention over cache rows [0, pos], GELU MLP), final modulation and head. Needs pos <= length.
  *   KV-inject (module-dflash.ts forwardRows / #backbone): block = [tok_proj(E[anchor]) + block_pos[0];
  *             mask_emb + block_pos[1..]], every layer attends over [cache rows [0, length) ++ block], out_proj.
+ *             A one-row block (block = 1) is the anchor row alone and needs no mask_emb in the weight table.
  *   MTP       (ternary_bonsai_2_mtp.js MTPHead.forward): rows M at positions pos .. pos+M-1, writes their K/V to
  *             the cache there, causal grouped-query attention over rows [kv_lo, pos+m]; output shared_head_norm(x).
  * Anchor ids outside [0, vocab) are clamped into the table (a device-side id cannot be checked by the host).

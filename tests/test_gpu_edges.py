@@ -189,3 +189,32 @@ def test_kvinject_full_context():
         o.context_append(one, full)
     assert d.length == full and o.length == full
     _say(f"kvinject: full-context draft ok, hidden err {e:.2e}")
+
+
+@pytest.mark.parametrize("gamma", [1, 16])
+def test_kvinject_block_sizes(gamma):
+    """KV-injection blocks of one row (the anchor alone) and of 16 rows (the most a draft takes): hidden rows, logits
+    and tokens against the oracle after a ragged prefill."""
+    fm = _fm()
+    cfg = dict(KV_SMALL, block=gamma, name=f"kvinject_g{gamma}")
+    W = gen.make_weights(cfg)
+    d = fm.Drafter(cfg, fm.upload_weights(W))
+    o = kvinject.KVInjectOracle(cfg, W)
+    n = 77
+    taps = gen.taps(cfg, "prefill", n)
+    o.context_append(taps, 0)
+    d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+    an = 1234
+    _say(f"kvinject: block of {gamma} rows over {n} context rows")
+    hid = torch.empty(gamma, cfg["target_dim"], dtype=torch.float32, device="cuda")
+    d.fm_draft_block(hid, anchor=torch.tensor([an], dtype=torch.int32, device="cuda"))
+    tok = torch.empty(gamma, dtype=torch.int32, device="cuda")
+    logits = torch.empty(gamma, cfg["vocab"], dtype=torch.float32, device="cuda")
+    d.fm_lm_argmax(hid, gamma, tok, logits)
+    torch.cuda.synchronize()
+    out, _ = o.draft_block(an)
+    _, z = o.lm_argmax(out)
+    e = assert_rows_close(hid.cpu().numpy(), out, what=f"hidden, block {gamma}")
+    assert_rows_close(logits.cpu().numpy(), z, what=f"logits, block {gamma}")
+    k = assert_tokens_match(tok.cpu().numpy(), z)
+    _say(f"kvinject: block {gamma} hidden err {e:.2e}, tokens exact on {k}/{gamma}")
