@@ -288,3 +288,30 @@ def test_tiny_time_conditioning():
     with pytest.raises(fm.FmError) as ex:
         d.fm_time_condition(0.0, 1.0, 255, 256, 1000.0)
     assert ex.value.status == fm.FM_E_INVALID
+
+
+def test_flashmap_time_conditioning_table():
+    """The adaLN table at the FlashMap shape (dim 2048, 6 layers, time and condition widths 256, time scale 1000:
+    the page's configuration), for the page's jump 0 -> 1 and one more, against the oracle. Only the time MLPs and
+    the 19 adaLN linears take part, so the other weights are zeros."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = configs.get("flashmap", time_dim=256, cond_dim=256, time_scale=1000.0)
+    W = {}
+    for name, shape, kind in gen.weight_specs(cfg):
+        if "time_embed" in name or "jump_embed" in name or "adaln" in name:
+            W[name] = gen.make_tensor(cfg, name, shape, kind)
+        else:
+            W[name] = np.zeros(shape, np.float32 if kind == "mod" else np.uint16)
+    dw = fm.upload_weights(W)
+    d = fm.Drafter(cfg, dw)
+    o = flowmap.FlowMapOracle(cfg, W)
+    L, D = cfg["layers"], cfg["dim"]
+    for s_, t_ in ((0.0, 1.0), (0.3, 0.85)):
+        d.fm_time_condition(s_, t_, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"])
+        torch.cuda.synchronize()
+        got = dw["mod"].cpu().numpy().reshape(3 * L + 1, 3 * D)
+        ref = o.time_conditioning(s_, t_).reshape(3 * L + 1, 3 * D)
+        e = assert_rows_close(got, ref, tol=1e-4, what=f"flashmap table {s_}->{t_}")
+        _say(f"flashmap: time conditioning {s_} -> {t_}: table err {e:.2e}")
