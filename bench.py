@@ -148,6 +148,22 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     rows["flashmap_prefill_512"] = _mfma_row("512-row context prefill", ms, n,
                                              2.0 * n * D * (cfg["n_taps"] * Ht + 2 * Lyr * D))
 
+    # time conditioning of the jump 0 -> 1 at the FlashMap shape (time / condition widths 256, scale 1000): the time
+    # MLPs and 19 adaLN linears, written into a copy of the modulation table (the other rows keep theirs)
+    ct = configs.get("flashmap", time_dim=256, cond_dim=256, time_scale=1000.0)
+    tnames = [(nm, sh, k) for nm, sh, k in gen.weight_specs(ct) if "time_embed" in nm or "jump_embed" in nm or "adaln" in nm]
+    Wt = {nm: gen.make_tensor(ct, nm, sh, k) for nm, sh, k in tnames}
+    dwt = dict(d.weights)
+    dwt.update(fm.upload_weights(Wt))
+    dwt["mod"] = d.weights["mod"].clone()
+    dt = fm.Drafter(ct, dwt)
+    ms = _time_ms(torch, _graph_of(torch, lambda: dt.fm_time_condition(0.0, 1.0, 256, 256, 1000.0)), 5, reps)
+    rows["flashmap_time_condition"] = _hbm_row("time conditioning of a jump (time MLPs + 19 adaLN linears -> the "
+                                               "modulation table)", ms,
+                                               weight_bytes(Wt, [nm for nm, _, _ in tnames]) + dwt["mod"].numel() * 4,
+                                               "tables/s")
+    del dt, dwt
+
     # KV-injection: 2048-row prefill, then the gamma = 5 draft + lm_head argmax
     kc = configs.get("kvinject")
     print("[bench] KV-injection weights", file=sys.stderr, flush=True)

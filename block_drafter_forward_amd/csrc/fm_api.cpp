@@ -173,7 +173,7 @@ Plan make_plan(const fm_config& c) {
     const bool kvi = c.variant == FM_VARIANT_KVINJECT;
     p.blockn = take(kvi ? (size_t)TMAX * c.dim * 4 : 0);
     p.zbase = take(kvi ? (size_t)c.block * c.vocab * 4 : 0);
-    p.tcond = take(fmv ? (size_t)TC_MAX_DIM * 4 : 0);   // time conditioning: the cond vector
+    p.tcond = take(fmv ? (size_t)3 * TC_MAX_DIM * 4 : 0);   // time conditioning: cond, then the two hidden layers
     p.total = off;
     return p;
 }

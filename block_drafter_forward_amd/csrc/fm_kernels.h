@@ -96,7 +96,7 @@ struct TimeCondArgs {
     float times[2];        // s, t
     float time_scale;
     int td, cd, rows, nnorm;
-    float* cond;
+    float* cond;           // [3 * TC_MAX_DIM]: the condition vector, then the time MLPs' hidden layers
     float* table;
 };
 hipError_t launch_time_condition(const TimeCondArgs& a, hipStream_t st);

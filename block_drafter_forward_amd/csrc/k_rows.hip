@@ -226,6 +226,81 @@ __global__ __launch_bounds__(256) void tc_adaln_kernel(TimeCondArgs a) {
     a.table[(size_t)n * a.rows + m] = acc;
 }
 
+// Stage 2 with coalesced weight reads, for cond_dim a power of two in [16, 1024]: a row's dot product is split over
+// LPR = cond_dim / 16 adjacent threads, each reading 16 consecutive bf16 weights (two 16-byte loads) against the
+// matching 16 condition values, then summed by LPR-lane shuffles; a work-group covers 256 / LPR whole rows, so it
+// reads contiguous rows (the table's 19 x 6144 x 256 weights stream at ~5 TB/s instead of one 512-byte row per
+// thread read 2 bytes at a time).
+template <int LPR>
+__device__ __forceinline__ float tc_row_dot(const uint16_t* __restrict__ W, int K, int row, int seg, const float* x,
+                                            bool live) {
+    float acc = 0.f;
+    if (live) {
+        const uint4* p = (const uint4*)(W + (size_t)row * K + seg * 16);
+        const uint4 w0 = p[0], w1 = p[1];
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float* xs = x + seg * 16;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += bf16_lo(w[i]) * xs[2 * i] + bf16_hi(w[i]) * xs[2 * i + 1];
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+    return acc;
+}
+
+// Stage 1 over many work-groups, coalesced like stage 2 (time_dim and cond_dim powers of two in [16, 1024]):
+// work-group (row block, w) embeds time w and computes its 256 / LT rows of h_w = SiLU(linear_1 e_w) into the
+// scratch after the condition vector; then work-group (row block) computes its rows of both linear_2 outputs and
+// cond = SiLU(y_0 + y_1).
+template <int LT>
+__global__ __launch_bounds__(256) void tc_hidden_kernel(TimeCondArgs a) {
+    __shared__ __attribute__((aligned(16))) float e[TC_MAX_DIM];
+    constexpr int RPI = 256 / LT;
+    const int tid = threadIdx.x, w = blockIdx.y, half = a.td / 2, seg = tid % LT;
+    for (int i = tid; i < half; i += 256) {
+        const float f = (float)exp(-log(10000.0) * (double)i / (double)half);
+        const float ang = (a.times[w] * a.time_scale) * f;
+        e[i] = (float)cos((double)ang);
+        e[half + i] = (float)sin((double)ang);
+    }
+    __syncthreads();
+    const int m = blockIdx.x * RPI + tid / LT;
+    const bool live = m < a.cd;
+    const float acc = tc_row_dot<LT>(a.l1w[w], a.td, m, seg, e, live);
+    if (live && seg == 0) a.cond[(size_t)(1 + w) * TC_MAX_DIM + m] = silu(acc + bf16_to_f32(a.l1b[w][m]));
+}
+
+template <int LC>
+__global__ __launch_bounds__(256) void tc_cond_kernel(TimeCondArgs a) {
+    __shared__ __attribute__((aligned(16))) float h[2][TC_MAX_DIM];
+    constexpr int RPI = 256 / LC;
+    const int tid = threadIdx.x, seg = tid % LC;
+    for (int k = tid; k < a.cd; k += 256) {
+        h[0][k] = a.cond[TC_MAX_DIM + k];
+        h[1][k] = a.cond[2 * TC_MAX_DIM + k];
+    }
+    __syncthreads();
+    const int m = blockIdx.x * RPI + tid / LC;
+    const bool live = m < a.cd;
+    const float y0 = tc_row_dot<LC>(a.l2w[0], a.cd, m, seg, h[0], live);
+    const float y1 = tc_row_dot<LC>(a.l2w[1], a.cd, m, seg, h[1], live);
+    if (live && seg == 0)
+        a.cond[m] = silu((y0 + bf16_to_f32(a.l2b[0][m])) + (y1 + bf16_to_f32(a.l2b[1][m])));
+}
+
+template <int LC>
+__global__ __launch_bounds__(256) void tc_adaln_seg_kernel(TimeCondArgs a) {
+    __shared__ __attribute__((aligned(16))) float c[TC_MAX_DIM];
+    constexpr int RPI = 256 / LC;
+    const int n = blockIdx.y, tid = threadIdx.x, seg = tid % LC;
+    for (int k = tid; k < a.cd; k += 256) c[k] = a.cond[k];
+    __syncthreads();
+    const int m = blockIdx.x * RPI + tid / LC;
+    const bool live = m < a.rows;
+    const float acc = tc_row_dot<LC>(a.aw[n], a.cd, m, seg, c, live);
+    if (live && seg == 0) a.table[(size_t)n * a.rows + m] = acc + bf16_to_f32(a.ab[n][m]);
+}
+
 __global__ void colmean_stage1(const uint16_t* E, int V, int H, int R, float* scratch) {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= H) return;
@@ -350,10 +425,54 @@ hipError_t launch_time_condition(const TimeCondArgs& a, hipStream_t st) {
     if (a.td < 2 || a.td % 2 || a.td > TC_MAX_DIM || a.cd < 1 || a.cd > TC_MAX_DIM || a.rows < 1 || a.nnorm < 1 ||
         a.nnorm > TC_MAX_NORMS)
         return hipErrorInvalidValue;
-    tc_embed_kernel<<<1, 256, 0, st>>>(a);
+    // threads per row of the coalesced kernels (width / 16), 0 if the width does not fit them
+    auto lanes = [](int k) { return (k >= 16 && k <= 1024 && (k & (k - 1)) == 0) ? k / 16 : 0; };
+    const int lt = lanes(a.td), lc = lanes(a.cd);
+    bool aligned = true;   // the coalesced kernels read 16-byte pieces of every weight row
+    auto al = [&](const void* q) { aligned = aligned && ((uintptr_t)q & 15) == 0; };
+    for (int w = 0; w < 2; ++w) { al(a.l1w[w]); al(a.l2w[w]); }
+    for (int n = 0; n < a.nnorm; ++n) al(a.aw[n]);
+    if (lt == 0 || lc == 0 || !aligned) {
+        tc_embed_kernel<<<1, 256, 0, st>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        tc_adaln_kernel<<<dim3((a.rows + 255) / 256, a.nnorm), 256, 0, st>>>(a);
+        return hipGetLastError();
+    }
+    const dim3 hgrid((a.cd + 256 / lt - 1) / (256 / lt), 2);
+    switch (lt) {
+    case 1: tc_hidden_kernel<1><<<hgrid, 256, 0, st>>>(a); break;
+    case 2: tc_hidden_kernel<2><<<hgrid, 256, 0, st>>>(a); break;
+    case 4: tc_hidden_kernel<4><<<hgrid, 256, 0, st>>>(a); break;
+    case 8: tc_hidden_kernel<8><<<hgrid, 256, 0, st>>>(a); break;
+    case 16: tc_hidden_kernel<16><<<hgrid, 256, 0, st>>>(a); break;
+    case 32: tc_hidden_kernel<32><<<hgrid, 256, 0, st>>>(a); break;
+    default: tc_hidden_kernel<64><<<hgrid, 256, 0, st>>>(a); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    tc_adaln_kernel<<<dim3((a.rows + 255) / 256, a.nnorm), 256, 0, st>>>(a);
+    const int cgrid = (a.cd + 256 / lc - 1) / (256 / lc);
+    switch (lc) {
+    case 1: tc_cond_kernel<1><<<cgrid, 256, 0, st>>>(a); break;
+    case 2: tc_cond_kernel<2><<<cgrid, 256, 0, st>>>(a); break;
+    case 4: tc_cond_kernel<4><<<cgrid, 256, 0, st>>>(a); break;
+    case 8: tc_cond_kernel<8><<<cgrid, 256, 0, st>>>(a); break;
+    case 16: tc_cond_kernel<16><<<cgrid, 256, 0, st>>>(a); break;
+    case 32: tc_cond_kernel<32><<<cgrid, 256, 0, st>>>(a); break;
+    default: tc_cond_kernel<64><<<cgrid, 256, 0, st>>>(a); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid((a.rows + 256 / lc - 1) / (256 / lc), a.nnorm);
+    switch (lc) {
+    case 1: tc_adaln_seg_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: tc_adaln_seg_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 4: tc_adaln_seg_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 8: tc_adaln_seg_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    case 16: tc_adaln_seg_kernel<16><<<grid, 256, 0, st>>>(a); break;
+    case 32: tc_adaln_seg_kernel<32><<<grid, 256, 0, st>>>(a); break;
+    default: tc_adaln_seg_kernel<64><<<grid, 256, 0, st>>>(a); break;
+    }
     return hipGetLastError();
 }
 
