@@ -253,14 +253,15 @@ def test_longctx_workload(flashmap):
     _say(f"longctx: 64 steps, worst hidden err {worst:.2e}, tokens exact on {exact}/{64 * cfg['block']} rows")
 
 
-def test_tiny_time_conditioning():
+@pytest.mark.parametrize("widths", [(256, 256), (96, 80)])
+def test_tiny_time_conditioning(widths):
     """The adaLN table of a jump s -> t from the time MLPs, written into the drafter's modulation table: equal to
     the oracle's (two jumps), then a prefill and a draft that use it, against the oracle drafting with its own
-    table."""
+    table. Power-of-two widths take the coalesced kernels, others the one-row-per-thread ones."""
     from block_drafter_forward_amd import fm
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    cfg = configs.get("tiny", time_dim=256, cond_dim=256, time_scale=1000.0)
+    cfg = configs.get("tiny", time_dim=widths[0], cond_dim=widths[1], time_scale=1000.0)
     W = gen.make_weights(cfg)
     dw = fm.upload_weights(W)
     d = fm.Drafter(cfg, dw)
@@ -286,7 +287,7 @@ def test_tiny_time_conditioning():
     k = assert_tokens_match(tok, z)
     _say(f"tiny: draft with the derived table: hidden err {e:.2e}, tokens exact on {k}/{cfg['block']}")
     with pytest.raises(fm.FmError) as ex:
-        d.fm_time_condition(0.0, 1.0, 255, 256, 1000.0)
+        d.fm_time_condition(0.0, 1.0, cfg["time_dim"] - 1, cfg["cond_dim"], 1000.0)
     assert ex.value.status == fm.FM_E_INVALID
 
 
