@@ -1349,7 +1349,7 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
     a.V = c.vocab;
     a.r = rank;
     a.D = c.dim;
-    for (int k = 0; k < rows; ++k) HIPCHK(launch_markov_step(a, k, st));
+    HIPCHK(launch_markov(a, rows, st));   // the keys of rows [0, rows) were cleared by the lm_head's finalize
     return FM_OK;
 }
 

@@ -244,10 +244,12 @@ struct MarkovArgs {
     int32_t* tokens;       // device [rows]
     float* conf;           // device [rows]
     float* scores;         // optional [rows][V]
-    unsigned long long* key;  // [1], zero between steps
+    unsigned long long* key;  // [rows]: step k's argmax key; zero between calls
     int V, r, D;
 };
-hipError_t launch_markov_step(const MarkovArgs& a, int k, hipStream_t st);
+// The decode steps 0 .. rows - 1 (rows <= 16), step k's argmax in key[k] (key[0 .. rows) zero on entry, zero again
+// on exit).
+hipError_t launch_markov(const MarkovArgs& a, int rows, hipStream_t st);
 
 // ── K2: MFMA prefill GEMM (f16 operands, f32 accumulate) ──────────────────────────────────────
 // C[r][n] = sum_k A[r][k] B[n][k]; A f32 or f16 rows, B bf16 weights converted to f16 on the way into LDS.

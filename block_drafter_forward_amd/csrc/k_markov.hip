@@ -1,6 +1,8 @@
 // k_markov.hip — the DSpark Markov correction and confidence head of the KV-injection drafter (the DFlash
-// page, forwardRows' greedy loop): one launch pair per decode step, sequential over the block's rows because each
-// step conditions on the token the previous step chose.
+// page, forwardRows' greedy loop): one launch per decode step, sequential over the block's rows because each step
+// conditions on the token the previous step chose, plus one closing launch. Step k keeps its argmax in its own
+// 64-bit key slot; step k + 1 reads its token from there, and its first work-group writes step k's token and
+// confidence, so no step needs a launch of its own to finish.
 #include "fm_device.h"
 #include "fm_kernels.h"
 
@@ -18,12 +20,38 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // [r][V]), then the argmax over v into a 64-bit key (same order as the lm_head kernel). Each thread owns 4
 // consecutive columns (one 8-byte load per w2 row), 16 rows' loads in flight; e1 goes through LDS as f32.
 // V % 4 == 0; columns past V (the last work-group) are clamped and left out of the argmax.
+__device__ __forceinline__ int key_token(unsigned long long key) {
+    return (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+}
+
+// the token step k conditions on: the anchor, then the token step k - 1 chose
+__device__ __forceinline__ int markov_prev(const MarkovArgs& a, int k) {
+    const int p = k == 0 ? a.anchor[0] : key_token(a.key[k - 1]);
+    return min(max(p, 0), a.V - 1);
+}
+
+// step j's token (from its key) and confidence sigmoid([block_j; e1] conf.w + conf.b), e1 the w1 row of the token
+// step j conditioned on; the whole work-group takes part
+__device__ void markov_close(const MarkovArgs& a, int j, float* red) {
+    const int tid = threadIdx.x;
+    const int prev = markov_prev(a, j);
+    float s = 0.f;
+    for (int i = tid; i < a.D; i += 256) s += a.block[(size_t)j * a.D + i] * bf16_to_f32(a.cw[i]);
+    for (int i = tid; i < a.r; i += 256) s += bf16_to_f32(a.w1[(size_t)prev * a.r + i]) * bf16_to_f32(a.cw[a.D + i]);
+    s = block_sum256(s, red);
+    if (tid == 0) {
+        a.tokens[j] = key_token(a.key[j]);
+        a.conf[j] = 1.f / (1.f + expf(-(s + bf16_to_f32(a.cb[0]))));
+    }
+}
+
 __global__ __launch_bounds__(256) void markov_step_kernel(MarkovArgs a, int k) {
     __shared__ float e1[MARKOV_MAX_RANK];
     __shared__ float wb[4];
     __shared__ int wi[4];
+    __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int prev = (int)min(max(k == 0 ? a.anchor[0] : a.tokens[k - 1], 0), a.V - 1);
+    const int prev = markov_prev(a, k);
     for (int j = tid; j < a.r; j += 256) e1[j] = bf16_to_f32(a.w1[(size_t)prev * a.r + j]);
     __syncthreads();
     const int c0 = (blockIdx.x * 256 + tid) * 4;
@@ -75,36 +103,29 @@ __global__ __launch_bounds__(256) void markov_step_kernel(MarkovArgs a, int k) {
             if (wb[w2i] > b || (wb[w2i] == b && wi[w2i] < bi)) { b = wb[w2i]; bi = wi[w2i]; }
         if (bi != 0x7fffffff) {
             const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
-            atomicMax(&a.key[0], key);
+            atomicMax(&a.key[k], key);
         }
     }
+    if (k > 0 && blockIdx.x == 0) markov_close(a, k - 1, red);   // the previous step's token and confidence
 }
 
-// Step k's token from the key (the key is cleared for the next step) and its confidence
-// sigmoid([block_k; e1] conf.w + conf.b) with the same e1 as the step (the w1 row of the previous token).
-__global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs a, int k) {
+// The last step's token and confidence, then every step's key cleared for the next call.
+__global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs a, int last) {
     __shared__ float red[4];
-    const int tid = threadIdx.x;
-    const int prev = (int)min(max(k == 0 ? a.anchor[0] : a.tokens[k - 1], 0), a.V - 1);
-    float s = 0.f;
-    for (int j = tid; j < a.D; j += 256) s += a.block[(size_t)k * a.D + j] * bf16_to_f32(a.cw[j]);
-    for (int j = tid; j < a.r; j += 256) s += bf16_to_f32(a.w1[(size_t)prev * a.r + j]) * bf16_to_f32(a.cw[a.D + j]);
-    s = block_sum256(s, red);
-    if (tid == 0) {
-        const unsigned long long key = a.key[0];
-        a.tokens[k] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-        a.key[0] = 0ull;
-        a.conf[k] = 1.f / (1.f + expf(-(s + bf16_to_f32(a.cb[0]))));
-    }
+    markov_close(a, last, red);
+    __syncthreads();
+    if ((int)threadIdx.x <= last) a.key[threadIdx.x] = 0ull;
 }
 
 }  // namespace
 
-hipError_t launch_markov_step(const MarkovArgs& a, int k, hipStream_t st) {
-    if (a.r < 1 || a.r > MARKOV_MAX_RANK || a.V < 4 || a.V % 4 || k < 0) return hipErrorInvalidValue;
-    markov_step_kernel<<<(a.V / 4 + 255) / 256, 256, 0, st>>>(a, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    markov_finalize_kernel<<<1, 256, 0, st>>>(a, k);
+hipError_t launch_markov(const MarkovArgs& a, int rows, hipStream_t st) {
+    if (a.r < 1 || a.r > MARKOV_MAX_RANK || a.V < 4 || a.V % 4 || rows < 1 || rows > 16) return hipErrorInvalidValue;
+    for (int k = 0; k < rows; ++k) {
+        markov_step_kernel<<<(a.V / 4 + 255) / 256, 256, 0, st>>>(a, k);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    markov_finalize_kernel<<<1, 256, 0, st>>>(a, rows - 1);
     return hipGetLastError();
 }
