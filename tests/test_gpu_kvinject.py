@@ -119,6 +119,14 @@ def test_kvinject_markov_decode(name):
     # the correction acts: the Markov tokens differ from the plain argmax somewhere, or the scores do
     _, z = o.lm_argmax(out)
     assert np.max(np.abs(osc - z)) > 1e-4
+    # a second call over the first 3 rows (greedy and sequential, so a prefix of the same decode): every step's key
+    # slot starts from zero again, so tokens and confidences repeat exactly
+    tok3 = torch.empty(3, dtype=torch.int32, device="cuda")
+    conf3 = torch.empty(3, dtype=torch.float32, device="cuda")
+    d.fm_markov_argmax(hid, 3, a, cfg["markov_rank"], tok3, conf3)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok3.cpu().numpy(), gt[:3])
+    assert np.array_equal(conf3.cpu().numpy(), conf.cpu().numpy()[:3])
     with pytest.raises(fm.FmError) as ex:
         d.fm_markov_argmax(hid, T + 1, a, cfg["markov_rank"], tok, conf)
     assert ex.value.status == fm.FM_E_INVALID
