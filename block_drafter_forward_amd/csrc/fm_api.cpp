@@ -612,7 +612,6 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     float* part = d->at<float>(d->p.part);
     float* x = d->at<float>(d->p.x);
     const float* mod = d->F("mod");
-    uint8_t* fragA = d->at<uint8_t>(d->p.fragA);
     uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
     uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
     uint8_t* fragU = d->at<uint8_t>(d->p.fragU);

@@ -26,10 +26,6 @@ constexpr int MAX_QSLABS = 4;   // split-K slabs of q (and of the self-attention
 // native 4 x u32 vector: arrays of it stay in registers where arrays of the HIP uint4 class may not
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float ld_kv(const void* p, size_t i, int dt) {
-    return dt == 0 ? f16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
-}
-
 // ── self-attention ───────────────────────────────────────────────────────────────────────────────
 // One work-group per head, built for latency (the whole op is 16 x 16 x hd): every global load (q, k, v rows, the
 // norm weights and the slots' RoPE rows) is issued up front; thread (row, segment) holds hd/8 consecutive values of

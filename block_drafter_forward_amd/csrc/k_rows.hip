@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
         float q = 0.f;
 #pragma unroll
         for (int j = 0; j < NS; ++j)
-            if (threadIdx.x + j * 256 < nslot)
+            if ((int)threadIdx.x + j * 256 < nslot)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) { const float d = v[j][e] - mean; q += d * d; }
         const float var = block_sum256(q, red) / (float)D;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
         float q = 0.f;
 #pragma unroll
         for (int j = 0; j < NS; ++j)
-            if (threadIdx.x + j * 256 < nslot)
+            if ((int)threadIdx.x + j * 256 < nslot)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) q += v[j][e] * v[j][e];
         const float ms = block_sum256(q, red) / (float)D;
