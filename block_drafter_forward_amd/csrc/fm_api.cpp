@@ -161,7 +161,7 @@ Plan make_plan(const fm_config& c) {
     // the prefill K epilogue's copy of the RoPE table (flow-map): each lane's cos / sin as two 16-byte loads
     p.rope_pf = take(c.variant == FM_VARIANT_FLOWMAP ? (size_t)p.rope_rows * p.rope_dims * 4 : 0);
     p.qout = take(c.variant == FM_VARIANT_MTP ? (size_t)TMAX * c.heads * c.head_dim * 4 : 0);
-    // the flow-map anchor path runs on a side stream next to the first layer: it has buffers of its own
+    // the flow-map anchor path's own buffers (its partials, the anchor row and the slot row as fragments)
     const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
     p.apart = take(fmv ? p.part_floats * 4 : 0);
     p.afrag = take(fmv ? (size_t)c.target_dim * 64 : 0);
@@ -233,8 +233,6 @@ struct fm_drafter {
     uint8_t* kv;
     int length;
     int perm;                          // k order of activation fragments (fm_device.h); natural (0) everywhere
-    hipStream_t side = nullptr;        // default-priority stream for work that overlaps the caller's stream
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
     template <class T> T* at(size_t off) const { return (T*)(ws + off); }
     const void* W(const std::string& n) const { auto it = w.find(n); return it == w.end() ? nullptr : it->second; }
@@ -620,13 +618,11 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     const long long pstr = (long long)TMAX * D;
     const int Sq = pick_qsplit(D);
 
-    // anchor slot: anchor_norm(anchor_proj(E[anchor])) through every layer's k/v path at pos. It only has to be in
-    // the cache before the first cross-attention, so it runs on the side stream next to layer 0's self-attention
-    // branch (fork / join events; inside a graph capture these become parallel branches).
+    // anchor slot: anchor_norm(anchor_proj(E[anchor])) through every layer's k/v path at pos, on the caller's stream
+    // before layer 0. (Beside layer 0 on a second stream it was 37 us slower per step: its 1,536-work-group K/V
+    // projections took the CUs layer 0's latency-bound kernels needed, and the join cost another ~9 us.)
     {
-        hipStream_t as = d->side;
-        HIPCHK(hipEventRecord(d->ev_fork, st));
-        HIPCHK(hipStreamWaitEvent(as, d->ev_fork, 0));
+        hipStream_t as = st;
         uint8_t* afrag = d->at<uint8_t>(d->p.afrag);
         uint8_t* cfrag = d->at<uint8_t>(d->p.cfrag);
         float* apart = d->at<float>(d->p.apart);
@@ -645,7 +641,6 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         r.frag_out = cfrag;
         CHK(rows(r, as));
         CHK(fm_kv_rows_small(d, 1, pos, cfrag, as));
-        HIPCHK(hipEventRecord(d->ev_join, as));
     }
     int S = 0;
     const int L = pos + 1;
@@ -720,7 +715,6 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         // per-head q_norm + RoPE inside the attention kernel
         CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, D}},
                    D, T, SK_PARTIAL, Sq, nullptr, st, (long long)TMAX * D, d->p.qkv_floats));
-        if (l == 0) HIPCHK(hipStreamWaitEvent(st, d->ev_join, 0));   // the anchor slot is in the cache
         {
             QPrep qp{};
             qp.q = qkv;
@@ -1189,12 +1183,6 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
     hipStream_t st = (hipStream_t)stream;
     fm_status s = FM_OK;
     do {
-        if (cfg->variant == FM_VARIANT_FLOWMAP) {
-            hipError_t e = hipStreamCreateWithFlags(&d->side, hipStreamNonBlocking);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_fork, hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_join, hipEventDisableTiming);
-            if (e != hipSuccess) { s = fail(FM_E_HIP, "side stream: %s", hipGetErrorString(e)); break; }
-        }
         if (launch_fill_u32(d->at<uint32_t>(d->p.best), 32, 0u, st) != hipSuccess) { s = fail(FM_E_HIP, "fill"); break; }
         if (launch_fill_u32(d->at<uint32_t>(d->p.zeros), d->p.zeros_bytes / 4, 0u, st) != hipSuccess) {
             s = fail(FM_E_HIP, "fill");
@@ -1461,9 +1449,6 @@ int32_t fm_context_length(const fm_drafter* d) { return d ? d->length : -1; }
 
 void fm_destroy(fm_drafter* d) {
     if (!d) return;
-    if (d->ev_fork) (void)hipEventDestroy(d->ev_fork);
-    if (d->ev_join) (void)hipEventDestroy(d->ev_join);
-    if (d->side) (void)hipStreamDestroy(d->side);
     delete d;
 }
 
