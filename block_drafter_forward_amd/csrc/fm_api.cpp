@@ -82,7 +82,7 @@ int pick_split(int M_total, int K, bool q8 = false) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -174,6 +174,7 @@ Plan make_plan(const fm_config& c) {
     p.blockn = take(kvi ? (size_t)TMAX * c.dim * 4 : 0);
     p.zbase = take(kvi ? (size_t)c.block * c.vocab * 4 : 0);
     p.tcond = take(fmv ? (size_t)3 * TC_MAX_DIM * 4 : 0);   // time conditioning: cond, then the two hidden layers
+    p.qkv0 = take(fmv ? (size_t)TMAX * 3 * c.dim * 4 : 0);   // layer 0's q | k | v of the zero-noise slot rows
     p.total = off;
     return p;
 }
@@ -649,36 +650,35 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         const float* m_sa = mod + (size_t)(3 * l) * 3 * D;
         const float* m_ca = mod + (size_t)(3 * l + 1) * 3 * D;
         const float* m_ml = mod + (size_t)(3 * l + 2) * 3 * D;
-        // residual (previous layer's MLP) + self-attention modulation
-        {
+        // residual (previous layer's MLP) + self-attention modulation, then q | k | v; layer 0's are the same for
+        // every draft (flowmap_layer0_qkv)
+        if (l > 0) {
             RowArgs r = rows_base(d, D, T);
             r.x = x;
-            if (l == 0) {
-                r.init = d->at<float>(d->p.h0);
-            } else {
-                r.part = part;
-                r.S = S_prev;
-                r.part_stride = pstr;
-                r.bias = d->B(LW(l - 1, "mlp.fc2.bias"));
-                r.gate = mod + (size_t)(3 * (l - 1) + 2) * 3 * D + 2 * D;
-                if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)(l - 1) * T * D;
-            }
+            r.part = part;
+            r.S = S_prev;
+            r.part_stride = pstr;
+            r.bias = d->B(LW(l - 1, "mlp.fc2.bias"));
+            r.gate = mod + (size_t)(3 * (l - 1) + 2) * 3 * D + 2 * D;
+            if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)(l - 1) * T * D;
             r.norm = ROW_LN_MOD;
             r.scale = m_sa;
             r.shift = m_sa + D;
             r.eps = c.ln_eps;
             r.frag_out = fragH;
             CHK(rows(r, st));
+            CHK(skinny(d,
+                       {{d->W(LW(l, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D,
+                         3 * D},
+                        {d->W(LW(l, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D,
+                         3 * D},
+                        {d->W(LW(l, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D,
+                         D, 3 * D}},
+                       D, T, SK_F32, 0, nullptr, st));
         }
-        CHK(skinny(d,
-                   {{d->W(LW(l, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, 3 * D},
-                    {d->W(LW(l, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
-                    {d->W(LW(l, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D, D,
-                     3 * D}},
-                   D, T, SK_F32, 0, nullptr, st));
         {
             SelfAttnArgs a{};
-            a.qkv = qkv;
+            a.qkv = l == 0 ? d->at<float>(d->p.qkv0) : qkv;
             a.parts = 1;
             a.pstride = 0;
             a.T = T;
@@ -700,6 +700,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         {
             RowArgs r = rows_base(d, D, T);
             r.x = x;
+            if (l == 0) r.init = d->at<float>(d->p.h0);   // every slot's residual starts at h0
             r.part = part;
             r.S = S;
             r.part_stride = pstr;
@@ -775,6 +776,32 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     return FM_OK;
 }
 
+// Layer 0 of a draft starts every slot from the same row h0 with the same modulation, so its LN-mod and its q / k /
+// v projections (before the head norms and RoPE, which the self-attention kernel applies at the slots' positions)
+// are the same for every draft: computed here, at create and whenever the modulation table changes.
+fm_status flowmap_layer0_qkv(fm_drafter* d, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim, T = c.block;
+    const float* m_sa = d->F("mod");
+    uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
+    float* q0 = d->at<float>(d->p.qkv0);
+    RowArgs r = rows_base(d, D, T);
+    r.init = d->at<float>(d->p.h0);
+    r.norm = ROW_LN_MOD;
+    r.scale = m_sa;
+    r.shift = m_sa + D;
+    r.eps = c.ln_eps;
+    r.frag_out = fragH;
+    CHK(rows(r, st));
+    CHK(skinny(d,
+               {{d->W(LW(0, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, q0, D, 3 * D},
+                {d->W(LW(0, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, q0 + D, D, 3 * D},
+                {d->W(LW(0, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, q0 + 2 * D, D,
+                 3 * D}},
+               D, T, SK_F32, 0, nullptr, st));
+    return FM_OK;
+}
+
 fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int Ht = c.target_dim, D = c.dim;
@@ -791,7 +818,7 @@ fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     CHK(skinny(d, {{d->W("x_embed.weight"), nullptr, nullptr, nullptr, d->B("x_embed.bias"), d->at<uint8_t>(d->p.fragA),
                     d->at<float>(d->p.h0), D, D}},
                Ht, 1, SK_F32, 0, nullptr, st));
-    return FM_OK;
+    return flowmap_layer0_qkv(d, st);
 }
 
 // ── KV-injection ────────────────────────────────────────────────────────────────────────────────
@@ -1384,7 +1411,7 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     a.cond = d->at<float>(d->p.tcond);
     a.table = (float*)d->F("mod");   // the caller's modulation table, overwritten in place
     HIPCHK(launch_time_condition(a, (hipStream_t)stream));
-    return FM_OK;
+    return flowmap_layer0_qkv(d, (hipStream_t)stream);   // layer 0's projections follow the new table
 }
 
 fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out,

@@ -112,7 +112,8 @@ size_t fm_workspace_bytes(const fm_config* cfg);
  * Enqueues the create-time work on `stream`: clearing the workspace's counters, the RoPE table (angles in f64,
  * stored f32, and its permuted prefill copy), f16 copies of the context-projection and per-layer K/V weights
  * (flow-map and KV-inject) and, for the flow-map, the zero-noise slot input x_embed(state_norm(mean row of
- * lm_head)) + bias (flashmap_drafter.js, init). The weights must keep their values while the handle lives.
+ * lm_head)) + bias (flashmap_drafter.js, init), and that row's layer-0 modulation and q / k / v projections (the
+ * same for every draft). The weights must keep their values while the handle lives.
  * Context length starts at 0.
  * Errors: FM_E_INVALID (null pointer, dim % heads, sizes not multiples of 32/256, block > 16 ...),
  * FM_E_MISSING_WEIGHT, FM_E_UNSUPPORTED, FM_E_HIP. */
@@ -193,7 +194,8 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
  * (linear_1 [cond_dim][time_dim], SiLU, linear_2 [cond_dim][cond_dim], bf16, with biases), cond = SiLU(sum), then
  * every norm's [scale | shift | gate] = its adaLN linear (layers.<l>.{self_attn,cross_attn,mlp}_adaln.linear and
  * final_adaln.linear, bf16 [3 dim][cond_dim] + bias) of cond. The table is written IN PLACE into the f32 buffer
- * registered as "mod" at fm_create (the caller's memory), so later drafts use it. Create-time work: the page
+ * registered as "mod" at fm_create (the caller's memory), so later drafts use it, and recomputes the draft's
+ * layer-0 projections of the zero-noise slot row, which depend on that table. Create-time work: the page
  * computes it once per jump (zero noise to tokens: s = 0, t = 1).
  * Errors: FM_E_INVALID (not a flow-map drafter, missing weights, time_dim odd or outside [2, 1024], cond_dim
  * outside [1, 1024]), FM_E_UNSUPPORTED (more than 49 norms). */
