@@ -82,7 +82,8 @@ int pick_split(int M_total, int K, bool q8 = false) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, total;
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
+        total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -175,6 +176,8 @@ Plan make_plan(const fm_config& c) {
     p.zbase = take(kvi ? (size_t)c.block * c.vocab * 4 : 0);
     p.tcond = take(fmv ? (size_t)3 * TC_MAX_DIM * 4 : 0);   // time conditioning: cond, then the two hidden layers
     p.qkv0 = take(fmv ? (size_t)TMAX * 3 * c.dim * 4 : 0);   // layer 0's q | k | v of the zero-noise slot rows
+    p.x1 = take(fmv ? (size_t)TMAX * c.dim * 4 : 0);          // layer 0's residual after its self-attention
+    p.q0c = take(fmv ? (size_t)QKV_SLABS * TMAX * c.dim * 4 : 0);   // layer 0's cross-attention q (split-K slabs)
     p.total = off;
     return p;
 }
@@ -651,7 +654,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         const float* m_ca = mod + (size_t)(3 * l + 1) * 3 * D;
         const float* m_ml = mod + (size_t)(3 * l + 2) * 3 * D;
         // residual (previous layer's MLP) + self-attention modulation, then q | k | v; layer 0's are the same for
-        // every draft (flowmap_layer0_qkv)
+        // every draft (flowmap_layer0)
         if (l > 0) {
             RowArgs r = rows_base(d, D, T);
             r.x = x;
@@ -676,49 +679,51 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
                          D, 3 * D}},
                        D, T, SK_F32, 0, nullptr, st));
         }
-        {
-            SelfAttnArgs a{};
-            a.qkv = l == 0 ? d->at<float>(d->p.qkv0) : qkv;
-            a.parts = 1;
-            a.pstride = 0;
-            a.T = T;
-            a.D = D;
-            a.heads = H;
-            a.hd = hd;
-            a.qn = d->B(LW(l, "self_attn.q_norm.weight"));
-            a.kn = d->B(LW(l, "self_attn.k_norm.weight"));
-            a.eps = c.qk_eps;
-            a.rope_tab = rope;
-            a.pos_base = pos + 1;
-            a.scale = 1.f / sqrtf((float)hd);
-            a.o_frag = fragO;
-            a.perm = d->perm;
-            HIPCHK(launch_self_attn(a, st));
+        // layer 0 from here to the cross-attention's q is the same for every draft (flowmap_layer0)
+        if (l > 0) {
+            {
+                SelfAttnArgs a{};
+                a.qkv = qkv;
+                a.parts = 1;
+                a.pstride = 0;
+                a.T = T;
+                a.D = D;
+                a.heads = H;
+                a.hd = hd;
+                a.qn = d->B(LW(l, "self_attn.q_norm.weight"));
+                a.kn = d->B(LW(l, "self_attn.k_norm.weight"));
+                a.eps = c.qk_eps;
+                a.rope_tab = rope;
+                a.pos_base = pos + 1;
+                a.scale = 1.f / sqrtf((float)hd);
+                a.o_frag = fragO;
+                a.perm = d->perm;
+                HIPCHK(launch_self_attn(a, st));
+            }
+            CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
+                       D, T, SK_PARTIAL, 0, &S, st));
+            {
+                RowArgs r = rows_base(d, D, T);
+                r.x = x;
+                r.part = part;
+                r.S = S;
+                r.part_stride = pstr;
+                r.gate = m_sa + 2 * D;
+                r.norm = ROW_LN_MOD;
+                r.scale = m_ca;
+                r.shift = m_ca + D;
+                r.eps = c.ln_eps;
+                r.frag_out = fragH;
+                CHK(rows(r, st));
+            }
+            // cross-attention over cache rows [0, pos]: q = cross q_proj(h) (whole k-range per work-group), then
+            // per-head q_norm + RoPE inside the attention kernel
+            CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, D}},
+                       D, T, SK_PARTIAL, Sq, nullptr, st, (long long)TMAX * D, d->p.qkv_floats));
         }
-        CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
-                   D, T, SK_PARTIAL, 0, &S, st));
-        {
-            RowArgs r = rows_base(d, D, T);
-            r.x = x;
-            if (l == 0) r.init = d->at<float>(d->p.h0);   // every slot's residual starts at h0
-            r.part = part;
-            r.S = S;
-            r.part_stride = pstr;
-            r.gate = m_sa + 2 * D;
-            r.norm = ROW_LN_MOD;
-            r.scale = m_ca;
-            r.shift = m_ca + D;
-            r.eps = c.ln_eps;
-            r.frag_out = fragH;
-            CHK(rows(r, st));
-        }
-        // cross-attention over cache rows [0, pos]: q = cross q_proj(h) (whole k-range per work-group), then
-        // per-head q_norm + RoPE inside the attention kernel
-        CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, D}},
-                   D, T, SK_PARTIAL, Sq, nullptr, st, (long long)TMAX * D, d->p.qkv_floats));
         {
             QPrep qp{};
-            qp.q = qkv;
+            qp.q = l == 0 ? d->at<float>(d->p.q0c) : qkv;
             qp.q_ld = D;
             qp.q_hs = hd;
             qp.norm_bf16 = d->B(LW(l, "cross_attn.q_norm.weight"));
@@ -736,6 +741,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         {
             RowArgs r = rows_base(d, D, T);
             r.x = x;
+            if (l == 0) r.init = d->at<float>(d->p.x1);   // layer 0's residual after its self-attention (every row)
             r.part = part;
             r.S = S;
             r.part_stride = pstr;
@@ -779,7 +785,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
 // Layer 0 of a draft starts every slot from the same row h0 with the same modulation, so its LN-mod and its q / k /
 // v projections (before the head norms and RoPE, which the self-attention kernel applies at the slots' positions)
 // are the same for every draft: computed here, at create and whenever the modulation table changes.
-fm_status flowmap_layer0_qkv(fm_drafter* d, hipStream_t st) {
+fm_status flowmap_layer0(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int D = c.dim, T = c.block;
     const float* m_sa = d->F("mod");
@@ -799,6 +805,33 @@ fm_status flowmap_layer0_qkv(fm_drafter* d, hipStream_t st) {
                 {d->W(LW(0, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, q0 + 2 * D, D,
                  3 * D}},
                D, T, SK_F32, 0, nullptr, st));
+    // Every slot's v row is the same and each query's softmax weights sum to 1, so layer 0's self-attention output
+    // is v itself whatever the positions: o_proj(v), the residual x1 = h0 + gate * o_proj(v), its cross-attention
+    // LN-mod and the cross-attention q projection (before its head norm and RoPE) are the same for every draft too.
+    const float* m_ca = m_sa + 3 * D;
+    uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
+    float* part = d->at<float>(d->p.part);
+    const long long pstr = (long long)TMAX * D;
+    HIPCHK(launch_f32_to_frag(q0 + 2 * D, 3 * D, T, D, fragO, d->perm, st));
+    int S = 0;
+    CHK(skinny(d, {{d->W(LW(0, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}}, D,
+               T, SK_PARTIAL, 0, &S, st));
+    RowArgs r2 = rows_base(d, D, T);
+    r2.x = d->at<float>(d->p.x1);
+    r2.init = d->at<float>(d->p.h0);
+    r2.part = part;
+    r2.S = S;
+    r2.part_stride = pstr;
+    r2.gate = m_sa + 2 * D;
+    r2.norm = ROW_LN_MOD;
+    r2.scale = m_ca;
+    r2.shift = m_ca + D;
+    r2.eps = c.ln_eps;
+    r2.frag_out = fragH;
+    CHK(rows(r2, st));
+    CHK(skinny(d, {{d->W(LW(0, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH,
+                    d->at<float>(d->p.q0c), D, D}},
+               D, T, SK_PARTIAL, pick_qsplit(D), nullptr, st, pstr, (size_t)QKV_SLABS * TMAX * D));
     return FM_OK;
 }
 
@@ -818,7 +851,7 @@ fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     CHK(skinny(d, {{d->W("x_embed.weight"), nullptr, nullptr, nullptr, d->B("x_embed.bias"), d->at<uint8_t>(d->p.fragA),
                     d->at<float>(d->p.h0), D, D}},
                Ht, 1, SK_F32, 0, nullptr, st));
-    return flowmap_layer0_qkv(d, st);
+    return flowmap_layer0(d, st);
 }
 
 // ── KV-injection ────────────────────────────────────────────────────────────────────────────────
@@ -1411,7 +1444,7 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     a.cond = d->at<float>(d->p.tcond);
     a.table = (float*)d->F("mod");   // the caller's modulation table, overwritten in place
     HIPCHK(launch_time_condition(a, (hipStream_t)stream));
-    return flowmap_layer0_qkv(d, (hipStream_t)stream);   // layer 0's projections follow the new table
+    return flowmap_layer0(d, (hipStream_t)stream);   // layer 0's projections follow the new table
 }
 
 fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out,
