@@ -48,11 +48,12 @@ def traffic_record(kernel_file: str, record: str):
 def draft_step_bytes(cfg, L: int) -> int:
     """Algorithmic HBM bytes of one flow-map draft block: every weight the step reads once (the anchor path, the
     DiT layers, the head, the lm_head table, the modulation table) plus the f16 K/V rows [0, L) cross-attention
-    reads. Create-time work is not part of the step: fc, hidden_norm, state_norm, x_embed, and layer 0's q / k / v
-    projections of the zero-noise slot row (the same for every draft, computed at create)."""
+    reads. Create-time work is not part of the step: fc, hidden_norm, state_norm, x_embed, and layer 0 from the
+    zero-noise slot row up to the cross-attention's q (q / k / v, o_proj and the cross q_proj: the same for every
+    draft, computed at create; its few small norm and modulation rows, ~41 KB, stay counted)."""
     D, Ht, F, hd, Lyr, V = cfg["dim"], cfg["target_dim"], cfg["ffn"], cfg["head_dim"], cfg["layers"], cfg["vocab"]
     w = D * Ht + 2 * D + Ht                       # anchor_proj (+bias), anchor_norm, E[anchor]
-    w += Lyr * (8 * D * D + 4 * hd + 2 * F * D + F + D) - 3 * D * D
+    w += Lyr * (8 * D * D + 4 * hd + 2 * F * D + F + D) - 5 * D * D
     w += Ht * D + Ht + V * Ht                     # head (+bias), lm_head
     b = 2 * w + 4 * (3 * Lyr + 1) * 3 * D         # bf16 weights, f32 modulation table
     return b + 2 * Lyr * L * D * 2
