@@ -285,8 +285,11 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     return rows
 
 
-def cpu_baseline(cfg, W, budget_s: float):
-    """The oracle (float64 NumPy) on the host cores: draft block + lm_head argmax at the same position."""
+def cpu_baseline(cfg, W):
+    """The oracle (float64 NumPy) on the host cores, timed as a fixed protocol: one warm-up, then the median of 3
+    timed runs, of (a) the draft block -- fm_draft_block + fm_lm_argmax at the same position as the GPU step -- and
+    (b) the 512-row context prefill (fm_context_append)."""
+    import statistics
     from inputs import gen
     from oracle import flowmap
     try:
@@ -296,22 +299,37 @@ def cpu_baseline(cfg, W, budget_s: float):
         cores = os.cpu_count()
     o = flowmap.FlowMapOracle(cfg, W)
     n = cfg["ctx_rows"]
-    o.context_append(gen.taps(cfg, "prefill", n), 0)
+    taps = gen.taps(cfg, "prefill", n)
     an = int(gen.anchors(cfg, "bench", 1)[0])
-    out, _ = o.draft_block(an, n)       # warm-up: decodes the weights to float64
-    o.lm_argmax(out)
-    t0 = time.perf_counter()
-    k = 0
-    while True:
+
+    def timed(fn):
+        fn()   # warm-up (the first call also decodes the weights to float64)
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    pf_s = timed(lambda: o.context_append(taps, 0))
+
+    def draft():
         out, _ = o.draft_block(an, n)
         o.lm_argmax(out)
-        k += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": k / dt, "unit": "draft blocks/s", "cores": cores, "kind": "oracle",
-            "sample": f"{k} draft blocks (fm_draft_block + fm_lm_argmax) of the same 512-row-context workload, "
-                      f"float64 NumPy, {dt:.1f} s"}
+    dr_s = timed(draft)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": 1.0 / dr_s, "unit": "draft blocks/s", "cores": cores, "kind": "oracle",
+            "prefill_tokens_per_s": n / pf_s, "cpu": cpu,
+            "sample": f"median of 3 timed runs after 1 warm-up: the draft block (fm_draft_block + fm_lm_argmax, "
+                      f"{dr_s * 1e3:.0f} ms) and the {n}-row context prefill ({pf_s * 1e3:.0f} ms) of the "
+                      f"512-row-context FlashMap workload, float64 NumPy"}
 
 
 def main():
@@ -321,7 +339,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--graph", choices=["on", "off"], default="on")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline, lm_head and 8192-row prefill only")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -464,7 +481,7 @@ def main():
         res["rows"] = other_rows(torch, fm, configs, gen, W, d, dl, max(20, args.steps // 4))
     if not args.no_cpu:
         print("[bench] oracle on the host cores", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, W, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(cfg, W)
     print(json.dumps(res))
 
 

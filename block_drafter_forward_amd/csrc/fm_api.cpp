@@ -83,7 +83,7 @@ int pick_split(int M_total, int K, bool q8 = false) {
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
         pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
-        total;
+        rscale, modc, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -178,6 +178,10 @@ Plan make_plan(const fm_config& c) {
     p.qkv0 = take(fmv ? (size_t)TMAX * 3 * c.dim * 4 : 0);   // layer 0's q | k | v of the zero-noise slot rows
     p.x1 = take(fmv ? (size_t)TMAX * c.dim * 4 : 0);          // layer 0's residual after its self-attention
     p.q0c = take(fmv ? (size_t)QKV_SLABS * TMAX * c.dim * 4 : 0);   // layer 0's cross-attention q (split-K slabs)
+    p.rscale = take(prefill ? (size_t)c.max_ctx * 4 : 0);   // the power-of-two scale of each f16 tap row of an append
+    // the handle's own modulation table (copied from the caller's at create, rewritten by time conditioning): the
+    // layer-0 projections cached at create follow this table, so no other handle can change it under them
+    p.modc = take(fmv ? (size_t)(3 * c.layers + 1) * 3 * c.dim * 4 : 0);
     p.total = off;
     return p;
 }
@@ -198,6 +202,10 @@ fm_status validate_config(const fm_config* c) {
     if (c->dim % 256 || c->target_dim % 256 || c->ffn % (c->wtype == FM_W_BF16 ? 256 : 128))
         return fail(FM_E_INVALID, "dim and target_dim must be multiples of 256, ffn of 256 (bf16) or 128 (Q8_0)");
     if (c->vocab % 16) return fail(FM_E_INVALID, "vocab must be a multiple of 16");
+    if (c->target_dim % 512)   // the lm_head kernel walks its rows in pairs of 256-column chunks
+        return fail(FM_E_UNSUPPORTED, "target_dim %d: the lm_head takes rows of a multiple of 512", c->target_dim);
+    if (c->kv_dtype == FM_KV_F32 && c->head_dim != 128 && c->head_dim != 256)   // the f32-cache attention kernel
+        return fail(FM_E_UNSUPPORTED, "head_dim %d with an f32 cache (128 or 256 supported)", c->head_dim);
     if (c->dim > 8 * 256 * 3) return fail(FM_E_UNSUPPORTED, "dim too large for the row kernels");
     switch (c->variant) {
     case FM_VARIANT_FLOWMAP:
@@ -206,16 +214,19 @@ fm_status validate_config(const fm_config* c) {
             return fail(FM_E_UNSUPPORTED, "flow-map needs interleaved RoPE, exact GELU, bf16, f16 cache, hd <= 128");
         if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
         if (c->max_ctx % 32) return fail(FM_E_INVALID, "an f16 cache needs max_ctx %% 32 == 0 (V is tiled by 32)");
+        if (c->kv_heads != c->heads) return fail(FM_E_UNSUPPORTED, "the flow-map drafter has one K/V head per head");
         break;
     case FM_VARIANT_KVINJECT:
         if (c->rope != FM_ROPE_NONE || c->mlp != FM_MLP_GEGLU_TANH || c->wtype != FM_W_BF16 ||
             c->kv_dtype != FM_KV_F32 || c->head_dim > 128)
             return fail(FM_E_UNSUPPORTED, "KV-inject needs no RoPE, tanh GeGLU, bf16, f32 cache, hd <= 128");
         if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
+        if (c->kv_heads != c->heads) return fail(FM_E_UNSUPPORTED, "KV-inject attends with every head's own K/V");
         break;
     case FM_VARIANT_MTP:
         if (c->rope != FM_ROPE_NEOX || c->mlp != FM_MLP_SWIGLU || c->wtype != FM_W_Q8_0 || c->kv_dtype != FM_KV_F32)
             return fail(FM_E_UNSUPPORTED, "MTP needs NEOX RoPE, SwiGLU, Q8_0, f32 cache");
+        if (c->head_dim != 256) return fail(FM_E_UNSUPPORTED, "MTP head_dim %d (256 supported)", c->head_dim);
         if (c->rope_dims <= 0 || c->rope_dims > c->head_dim || c->rope_dims % 2)
             return fail(FM_E_INVALID, "rope_dims");
         if (c->target_dim != c->dim) return fail(FM_E_INVALID, "MTP target_dim must equal dim");
@@ -236,7 +247,6 @@ struct fm_drafter {
     uint8_t* ws;
     uint8_t* kv;
     int length;
-    int perm;                          // k order of activation fragments (fm_device.h); natural (0) everywhere
 
     template <class T> T* at(size_t off) const { return (T*)(ws + off); }
     const void* W(const std::string& n) const { auto it = w.find(n); return it == w.end() ? nullptr : it->second; }
@@ -330,7 +340,6 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     a.S = S;
     a.KW = K / 128 / S;
     a.mode = mode;
-    a.perm = d->perm;
     int begin = 0;
     for (size_t i = 0; i < gs.size(); ++i) {
         const auto& g = gs[i];
@@ -353,7 +362,6 @@ RowArgs rows_base(const fm_drafter* d, int D, int T) {
     r.D = D;
     r.T = T;
     r.zeros = d->at<float>(d->p.zeros);
-    r.frag_perm = d->perm;
     return r;
 }
 
@@ -429,15 +437,15 @@ fm_status attend(fm_drafter* d, const QPrep& qp, int nq, int layer_kv, int key_l
     m.gate_ld = gate_ld;
     m.gate_hs = gate_hs;
     m.o_frag = o_frag;
-    m.perm = d->perm;
     m.row0 = o_row0;
     HIPCHK(launch_attn_merge(m, st));
     return FM_OK;
 }
 
 // ── flow-map ────────────────────────────────────────────────────────────────────────────────────
-// A operand of the context projection: the f32 taps as they are for 128-tiles (rounded to f16 on the way into LDS),
-// an f16 copy for 256-tiles (which stream f16 operands straight into LDS; same rounding).
+// A operand of the context projection: the taps of the append as f16 rows, each scaled by a power of two that brings
+// its largest magnitude into [2^14, 2^15) (launch_taps_f16); the scale is undone on the f32 output rows
+// (d->p.rscale), so f16's range does not limit the taps.
 // The context projection [n][K] x [K][D]: 128-tiles that fill less than one round of work-groups (two per CU) split
 // their k-range over up to 4 work-groups per tile; the slabs go to ctx + s * n * D and the RMSNorm that follows
 // sums them. Returns the slab count.
@@ -445,16 +453,9 @@ fm_status prefill_context(fm_drafter* d, const float* taps, int n, const uint16_
                           int* nslab, hipStream_t st);
 
 fm_status prefill_taps(fm_drafter* d, const float* taps, int n, PrefillArgs& a, hipStream_t st) {
-    const size_t KT = d->tap_width();
-    if (prefill_tile(n, d->c.dim, 1) == 256) {
-        uint16_t* t16 = d->at<uint16_t>(d->p.taps16);
-        HIPCHK(launch_f32_to_f16(taps, (size_t)n * KT, t16, st));
-        a.A = t16;
-        a.a_f32 = 0;
-    } else {
-        a.A = taps;
-        a.a_f32 = 1;
-    }
+    uint16_t* t16 = d->at<uint16_t>(d->p.taps16);
+    HIPCHK(launch_taps_f16(taps, n, (int)d->tap_width(), t16, d->at<float>(d->p.rscale), st));
+    a.A = t16;
     return FM_OK;
 }
 
@@ -549,7 +550,7 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     const auto& c = d->c;
     const int D = c.dim, KT = c.n_taps * c.target_dim;
     if (n <= TMAX) {
-        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), d->perm, st));
+        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), st));
         int S = 0;
         float* part = d->at<float>(d->p.part);
         CHK(skinny(d, {{d->W("fc.weight"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}},
@@ -570,7 +571,8 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
     int nslab = 1;
     CHK(prefill_context(d, taps, n, d->B("fc.weight"), d->w16_ctx(), ctx, &nslab, st));
-    HIPCHK(launch_rms_f16(ctx, n, D, d->B("hidden_norm.weight"), c.rms_eps, ctxn, nslab, (long long)n * D, st));
+    HIPCHK(launch_rms_f16(ctx, n, D, d->B("hidden_norm.weight"), c.rms_eps, ctxn, nslab, (long long)n * D,
+                          d->at<float>(d->p.rscale), st));
     for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
         PrefillArgs a{};
         const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
@@ -587,7 +589,6 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
         }
         a.ngroups = 2 * nl;
         a.A = ctxn;
-        a.a_f32 = 0;
         a.rows = n;
         a.N = D;
         a.K = D;
@@ -613,7 +614,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     const int pos = ba->pos;
     float* part = d->at<float>(d->p.part);
     float* x = d->at<float>(d->p.x);
-    const float* mod = d->F("mod");
+    const float* mod = d->at<float>(d->p.modc);
     uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
     uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
     uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
@@ -630,7 +631,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         uint8_t* afrag = d->at<uint8_t>(d->p.afrag);
         uint8_t* cfrag = d->at<uint8_t>(d->p.cfrag);
         float* apart = d->at<float>(d->p.apart);
-        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, afrag, d->perm, as));
+        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, afrag, as));
         int Sa = 0;
         CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, afrag, apart, D, D}}, Ht, 1,
                    SK_PARTIAL, 0, &Sa, as));
@@ -697,7 +698,6 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
                 a.pos_base = pos + 1;
                 a.scale = 1.f / sqrtf((float)hd);
                 a.o_frag = fragO;
-                a.perm = d->perm;
                 HIPCHK(launch_self_attn(a, st));
             }
             CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
@@ -788,7 +788,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
 fm_status flowmap_layer0(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int D = c.dim, T = c.block;
-    const float* m_sa = d->F("mod");
+    const float* m_sa = d->at<float>(d->p.modc);
     uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
     float* q0 = d->at<float>(d->p.qkv0);
     RowArgs r = rows_base(d, D, T);
@@ -812,7 +812,7 @@ fm_status flowmap_layer0(fm_drafter* d, hipStream_t st) {
     uint8_t* fragO = d->at<uint8_t>(d->p.fragO);
     float* part = d->at<float>(d->p.part);
     const long long pstr = (long long)TMAX * D;
-    HIPCHK(launch_f32_to_frag(q0 + 2 * D, 3 * D, T, D, fragO, d->perm, st));
+    HIPCHK(launch_f32_to_frag(q0 + 2 * D, 3 * D, T, D, fragO, st));
     int S = 0;
     CHK(skinny(d, {{d->W(LW(0, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}}, D,
                T, SK_PARTIAL, 0, &S, st));
@@ -838,6 +838,8 @@ fm_status flowmap_layer0(fm_drafter* d, hipStream_t st) {
 fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int Ht = c.target_dim, D = c.dim;
+    HIPCHK(hipMemcpyAsync(d->at<float>(d->p.modc), d->F("mod"), (size_t)(3 * c.layers + 1) * 3 * D * 4,
+                          hipMemcpyDeviceToDevice, st));
     // zero-noise slot input h0 = x_embed(state_norm(mean row of E)) + b
     HIPCHK(launch_colmean(d->B("lm_head.weight"), c.vocab, Ht, d->at<float>(d->p.colsc), d->p.colR,
                           d->at<float>(d->p.cmean), st));
@@ -865,7 +867,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     const auto& c = d->c;
     const int D = c.dim, KT = c.n_taps * c.target_dim;
     if (n <= TMAX) {
-        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), d->perm, st));
+        HIPCHK(launch_f32_to_frag(taps, KT, n, KT, d->at<uint8_t>(d->p.fragA), st));
         int S = 0;
         float* part = d->at<float>(d->p.part);
         CHK(skinny(d, {{d->W("W_c"), nullptr, nullptr, nullptr, nullptr, d->at<uint8_t>(d->p.fragA), part, D, D}}, KT, n,
@@ -905,17 +907,14 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     uint16_t* ctxn = d->at<uint16_t>(d->p.pctxn);
     int nslab = 1;
     CHK(prefill_context(d, taps, n, d->B("W_c"), d->w16_ctx(), ctx, &nslab, st));
-    // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32; split slabs summed into slab 0's rows), then per layer
-    // RMSNorm(H_ctx; attn_norm) -> f16
+    // H_ctx = RMSNorm(ctx; ctx_norm) in place (f32; split slabs summed into slab 0's rows, times the taps' row scales),
+    // then per layer RMSNorm(H_ctx; attn_norm) -> f16
     {
         RowArgs r = rows_base(d, D, n);
-        if (nslab > 1) {
-            r.part = ctx;
-            r.S = nslab;
-            r.part_stride = (long long)n * D;
-        } else {
-            r.x = ctx;
-        }
+        r.part = ctx;
+        r.S = nslab;
+        r.part_stride = (long long)n * D;
+        r.row_scale = d->at<float>(d->p.rscale);
         r.norm = ROW_RMS;
         r.w_bf16 = d->B("ctx_norm");
         r.eps = c.rms_eps;
@@ -925,7 +924,7 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
     }
     for (int i = 0; i < c.layers; ++i)
         HIPCHK(launch_rms_f16(ctx, n, D, d->B(BB(i, "attn_norm")), c.rms_eps, ctxn + (size_t)i * c.max_ctx * D, 1, 0,
-                              st));
+                              nullptr, st));
     for (int l0 = 0; l0 < c.layers; l0 += PF_MAX_GROUPS / 2) {
         PrefillArgs a{};
         const int nl = std::min(c.layers - l0, PF_MAX_GROUPS / 2);
@@ -941,7 +940,6 @@ fm_status kvinject_append(fm_drafter* d, const float* taps, int n, int start, hi
                                           (2 * j + 1) * per};
         }
         a.ngroups = 2 * nl;
-        a.a_f32 = 0;
         a.rows = n;
         a.N = D;
         a.K = D;
@@ -975,7 +973,7 @@ fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* cons
 
     // block rows of request b: H_d[0] = tok_proj(E[anchor_b]) + block_pos[0]; H_d[k] = mask_emb[k-1] + block_pos[k]
     for (int b = 0; b < B; ++b)
-        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, anchors[b], fragA, d->perm, st, b));
+        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, anchors[b], fragA, st, b));
     int S = 0;
     CHK(skinny(d, {{d->W("tok_proj"), nullptr, nullptr, nullptr, nullptr, fragA, part, D, D}}, Ht, B, SK_PARTIAL, 0,
                &S, st));
@@ -1032,19 +1030,24 @@ fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* cons
                    D, T, SK_FRAG_GEGLU, 0, nullptr, st));
         CHK(skinny(d, {{d->W(BB(i, "down")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
                    SK_PARTIAL, 0, &S, st));
-        {
-            RowArgs r = rows_base(d, D, T);
+        // residual + the next norm; after the last layer each request's block = RMSNorm(H_d; out_norm) rows are also
+        // kept in its own handle for the confidence head (fm_markov_argmax on that handle)
+        const bool last = i + 1 == c.layers;
+        for (int b = 0; b < (last ? B : 1); ++b) {
+            RowArgs r = rows_base(d, D, last ? G : T);
+            r.row0 = last ? b * G : 0;
             r.x = x;
-            r.part = part;
+            r.part = part + (size_t)r.row0 * D;
             r.S = S;
             r.part_stride = pstr;
             if (debug_layers) r.debug_x = debug_layers + (size_t)i * T * D;
             r.norm = ROW_RMS;
-            r.w_bf16 = i + 1 < c.layers ? d->B(BB(i + 1, "attn_norm")) : d->B("out_norm");
+            r.w_bf16 = last ? d->B("out_norm") : d->B(BB(i + 1, "attn_norm"));
             r.eps = c.rms_eps;
             r.frag_out = fragH;
-            if (i + 1 == c.layers) {   // keep block = RMSNorm(H_d; out_norm) for the confidence head
-                r.f32_out = d->at<float>(d->p.blockn);
+            if (last) {
+                r.f32_out = ds[b]->at<float>(ds[b]->p.blockn);
+                r.f32_local = 1;
                 r.out_ld = D;
             }
             CHK(rows(r, st));
@@ -1228,7 +1231,6 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
     d->ws = (uint8_t*)workspace;
     d->kv = (uint8_t*)kv_cache;
     d->length = 0;
-    d->perm = 0;
     for (int i = 0; i < n_weights; ++i) {
         if (!names[i]) { delete d; return fail(FM_E_INVALID, "null weight name at %d", i); }
         if (!ptrs[i]) { delete d; return fail(FM_E_INVALID, "null pointer for weight %s", names[i]); }
@@ -1316,7 +1318,7 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     hipStream_t st = (hipStream_t)stream;
     const int K = d->c.target_dim;
     uint8_t* fr = d->at<uint8_t>(d->p.fragH);
-    HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, d->perm, st));
+    HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
     LmArgs a{};
     const bool q8 = d->c.wtype == FM_W_Q8_0;
     a.E = q8 ? d->W("lm_head.q") : d->W("lm_head.weight");
@@ -1328,7 +1330,6 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     a.best = d->at<unsigned long long>(d->p.best);
     a.tokens = tokens;
     a.logits = logits;
-    a.perm = d->perm;
     HIPCHK(launch_lm_argmax(a, q8 ? 1 : 0, st));
     return FM_OK;
 }
@@ -1401,7 +1402,7 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
 }
 
 fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, int32_t cond_dim, float time_scale,
-                            void* stream) {
+                            float* table_out, void* stream) {
     g_err.clear();
     if (!d) return fail(FM_E_INVALID, "null handle");
     const auto& c = d->c;
@@ -1442,8 +1443,11 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     a.rows = 3 * c.dim;
     a.nnorm = nn;
     a.cond = d->at<float>(d->p.tcond);
-    a.table = (float*)d->F("mod");   // the caller's modulation table, overwritten in place
+    a.table = d->at<float>(d->p.modc);   // the handle's own table: other handles sharing the weights keep theirs
     HIPCHK(launch_time_condition(a, (hipStream_t)stream));
+    if (table_out)
+        HIPCHK(hipMemcpyAsync(table_out, a.table, (size_t)nn * 3 * c.dim * 4, hipMemcpyDeviceToDevice,
+                              (hipStream_t)stream));
     return flowmap_layer0(d, (hipStream_t)stream);   // layer 0's projections follow the new table
 }
 
@@ -1463,7 +1467,7 @@ fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* 
             f.kv_heads != c.kv_heads || f.layers != c.layers || f.ffn != c.ffn || f.block != c.block ||
             f.target_dim != c.target_dim || f.n_taps != c.n_taps || f.vocab != c.vocab || f.mlp != c.mlp ||
             f.kv_dtype != c.kv_dtype || f.wtype != c.wtype || f.rms_eps != c.rms_eps || f.rope != c.rope ||
-            f.rope_dims != c.rope_dims || f.rope_theta != c.rope_theta || ds[b]->perm != ds[0]->perm)
+            f.rope_dims != c.rope_dims || f.rope_theta != c.rope_theta)
             return fail(FM_E_INVALID, "handle %d: another configuration", b);
         for (const auto& n : required_names(c)) {
             const auto& w0 = ds[0]->w;

@@ -33,36 +33,20 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
 // A skinny activation matrix X[T <= 16][K] (K a multiple of 32) is stored as the B operand of
 // v_mfma_f32_16x16x32_bf16, split into two bf16 terms x = hi + lo (|x - hi - lo| <= 2^-17 |x|):
 //   k-step s = 2048 bytes = hi[64 lanes][8 bf16] then lo[64 lanes][8 bf16]; lane l = t + 16 g holds row t = l % 16.
-// Which 8 columns a lane holds in step s is the k order, shared by the producer and the weight loads of the
-// consumer (an MFMA sums over its 32 k, so any bijection works as long as both operands use it):
-//   natural  (perm 0): k = 32 s + 8 g + e                              (Q8_0 weights: a step is one Q8_0 block)
-//   blocked  (perm 1): k = 256 (s / 8) + 64 g + 8 (s % 8) + e, K % 256 == 0
-// The blocked order makes a lane's 8 consecutive steps 128 contiguous bytes of a weight row, but each load
-// instruction then touches 64 cache lines instead of 16; measured on MI355X it streams ~3x slower, so every path
-// uses the natural order (the blocked one is kept for reference).
+// Column k = 32 s + 8 g + e of step s sits in lane group g, element e (the MFMA's own k order); Q8_0 weights: a step
+// is one Q8_0 block.
 // Rows t >= T are never read back by any consumer (MFMA columns are independent), so they need no clearing.
 #define FRAG_STEP_BYTES 2048
 
 // Column offset (within a weight row) of lane group g's 8 elements in k-step s.
-__device__ __forceinline__ int kcol(int s, int g, int perm) {
-    return perm ? ((s >> 3) << 8) + (g << 6) + ((s & 7) << 3) : (s << 5) + (g << 3);
-}
+__device__ __forceinline__ int kcol(int s, int g) { return (s << 5) + (g << 3); }
 
-__device__ __forceinline__ size_t frag_offset(int t, int k, int perm) {   // byte offset of (t, k), k % 8 == 0
-    int s, g;
-    if (perm) {
-        const int o = k & 255;
-        g = o >> 6;
-        s = ((k >> 8) << 3) + ((o >> 3) & 7);
-    } else {
-        s = k >> 5;
-        g = (k & 31) >> 3;
-    }
-    return (size_t)s * FRAG_STEP_BYTES + (size_t)(t + 16 * g) * 16;
+__device__ __forceinline__ size_t frag_offset(int t, int k) {   // byte offset of (t, k), k % 8 == 0
+    return (size_t)(k >> 5) * FRAG_STEP_BYTES + (size_t)(t + 16 * ((k & 31) >> 3)) * 16;
 }
 
 // Store 8 consecutive values x[t][k .. k+7] (k % 8 == 0) as their hi/lo bf16 fragments.
-__device__ __forceinline__ void frag_store8(uint8_t* frag, int t, int k, const float* v, int perm) {
+__device__ __forceinline__ void frag_store8(uint8_t* frag, int t, int k, const float* v) {
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -72,7 +56,7 @@ __device__ __forceinline__ void frag_store8(uint8_t* frag, int t, int k, const f
         hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
-    uint8_t* p = frag + frag_offset(t, k, perm);
+    uint8_t* p = frag + frag_offset(t, k);
     *(uint4*)p = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     *(uint4*)(p + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }

@@ -40,7 +40,6 @@ struct SkinnyArgs {
     int KW;               // k-steps per wave (K / 32 == S * 4 * KW), any value >= 1
     int mode;
     long long part_stride;
-    int perm;             // k order of the fragments and weight loads (fm_device.h)
 };
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int n_workgroups, hipStream_t st);
 
@@ -75,15 +74,16 @@ struct RowArgs {
     int base_from;
     const uint16_t* row_bias_bf16;  // bf16 [T][D] added to row t (or null)
     const float* zeros;    // a zero row of >= D floats (absent inputs read it; required)
-    int frag_perm;         // k order of frag_out
+    const float* row_scale;// if set, the partial sum of row t (slabs + biases) is multiplied by row_scale[t]
+    int f32_local;         // 1: f32_out row t is at f32_out + t * out_ld (not row0 + t)
     int row0;              // row t of the launch is row row0 + t of x, debug_x, frag_out and f32_out (batched blocks)
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
 // f32 rows [T][K] (row stride ld) -> fragments. T <= 16, K % 32 == 0.
-hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, int perm, hipStream_t st);
+hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st);
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
-hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
+hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag,
                               hipStream_t st, int row = 0);
 // Time conditioning of a jump s -> t: the modulation table [nnorm][rows] (rows = 3 D: scale | shift | gate) from the
 // time MLPs ([0] time_embed, [1] jump_embed: linear_1 bf16 [cd][td], linear_2 [cd][cd], biases) and one adaLN
@@ -144,7 +144,6 @@ struct SelfAttnArgs {
     int pos_base;
     float scale;
     uint8_t* o_frag;
-    int perm;
 };
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st);
 
@@ -179,7 +178,6 @@ struct MergeArgs {
     const float* gate;     // optional: o *= sigmoid(gate[t*gate_ld + h*gate_hs + d])
     int gate_ld, gate_hs;
     uint8_t* o_frag;       // o row row0 + t, k = h*hd + d
-    int perm;
     int row0;
 };
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st);
@@ -222,11 +220,8 @@ struct LmArgs {
     const uint8_t* X;      // fragments of the rows
     int V, K, T;
     unsigned long long* best;  // [16] packed (value, index) maxima, zero between calls
-    unsigned int* counter;     // work-groups done, zero between calls
     int32_t* tokens;
     float* logits;         // optional [T][V]
-    int n_wg;
-    int perm;
 };
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
 
@@ -252,7 +247,7 @@ struct MarkovArgs {
 hipError_t launch_markov(const MarkovArgs& a, int rows, hipStream_t st);
 
 // ── K2: MFMA prefill GEMM (f16 operands, f32 accumulate) ──────────────────────────────────────
-// C[r][n] = sum_k A[r][k] B[n][k]; A f32 or f16 rows, B bf16 weights converted to f16 on the way into LDS.
+// C[r][n] = sum_k A[r][k] B[n][k]; A f16 rows, B bf16 weights converted to f16 on the way into LDS (or their f16 copies).
 enum PrefillEpi {
     PF_F32 = 0,     // C f32 [rows][ld]
     PF_CACHE_K = 1, // head RMSNorm + RoPE at position start + r, stored to the cache (f16/f32)
@@ -272,8 +267,7 @@ struct PrefillGroup {
 struct PrefillArgs {
     PrefillGroup g[PF_MAX_GROUPS];
     int ngroups;
-    const void* A;         // [rows][K]
-    int a_f32;             // 1: A is f32, 0: A is f16
+    const void* A;         // f16 [rows][K]
     int rows, N, K, ld;
     int hd;
     float eps;
@@ -288,17 +282,19 @@ struct PrefillArgs {
     long long slab_stride; //   tile; split s writes its partial product to out + s * slab_stride (floats)
 };
 // Tile edge (128 or 256) the launcher uses for rows x N x ngroups; the host sizes m_tiles, n_tiles and the
-// groups' tile_begin with it. 256-tiles need f16 A (a_f32 == 0), every group's B16, and K % 64 == 0.
+// groups' tile_begin with it. 256-tiles need every group's B16 and K % 64 == 0.
 int prefill_tile(int rows, int N, int ngroups);
 hipError_t launch_prefill(const PrefillArgs& a, int n_workgroups, hipStream_t st);
 // Prefill copy of the interleaved-RoPE table [P][rdim] (rdim % 64 == 0): per position, per block of 32 pairs, per
 // c = 0..7 the cos then the sin of pairs c, c + 8, c + 16, c + 24 of the block.
 hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hipStream_t st);
-// y = f16(x) element-wise (round to nearest even), n % 4 == 0: f32 taps, bf16 weights.
-hipError_t launch_f32_to_f16(const float* x, size_t n, uint16_t* y, hipStream_t st);
+// n rows of f32 taps [n][KT] -> f16 rows y = f16(x s) with s = 2^k per row (the row's largest magnitude times s in
+// [2^14, 2^15)); rscale[row] = 1 / s. KT % 4 == 0.
+hipError_t launch_taps_f16(const float* x, int n, int KT, uint16_t* y, float* rscale, hipStream_t st);
+// y = f16(x) element-wise (exact for bf16 above f16's subnormal range), n % 4 == 0.
 hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStream_t st);
 
-// Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context); the rows are the sum of nslab (1, 2 or 4)
-// partial slabs slab_stride floats apart.
+// Row RMSNorm of f32 rows [n][D] -> f16 rows [n][D] (prefill context); row t is rscale[t] times the sum of nslab
+// (1, 2 or 4) partial slabs slab_stride floats apart (rscale: the taps' row scales, launch_taps_f16).
 hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, int nslab,
-                          long long slab_stride, hipStream_t st);
+                          long long slab_stride, const float* rscale, hipStream_t st);

@@ -5,8 +5,8 @@
 //                (flashmap_drafter.js: headNormRope, attnF32), in f32 registers with two LDS exchanges;
 //                o leaves as fragments for the o_proj GEMM.
 //  attn_split    up to 16 query rows of one head against one chunk of keys (cache rows, then optional extra f32
-//                rows): scores, chunk max, exp-sum and the unnormalised P·V, written as a partial; f16 caches run
-//                both products on the matrix cores, f32 caches on the vector ALU. Splitting the key
+//                rows): scores, chunk max, exp-sum and the unnormalised P·V, written as a partial; both products run
+//                on the matrix cores (f32 caches split into f16 hi + lo). Splitting the key
 //                range across work-groups (flash-decoding) removes the page's 4096-key shared-memory cap and gives
 //                long contexts enough work-groups; the queries' own head-norm + RoPE (or the sum of their split-K
 //                partials) is rebuilt per work-group so it needs no extra launch.
@@ -133,230 +133,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
             o[0] += p * v0.x; o[1] += p * v0.y; o[2] += p * v0.z; o[3] += p * v0.w;
             o[4] += p * v1.x; o[5] += p * v1.y; o[6] += p * v1.z; o[7] += p * v1.w;
         }
-        if (ot < T) frag_store8(a.o_frag, ot, h * HD + d0, o, a.perm);
-    }
-}
-
-// ── split-L attention ────────────────────────────────────────────────────────────────────────────
-// Keys per work-group: K and V chunks of C rows each take 16 KB in LDS in their storage type.
-template <int HD, int KVT>
-struct SplitShape {
-    static constexpr int ES = KVT == 0 ? 2 : 4;
-    static constexpr int C = 16384 / (HD * ES);          // 64 (f16, 128), 128 (f16, 64), 32 (f32, 128), 16 (f32, 256)
-    static constexpr int PAD = 16 / ES;                   // one 16-byte pad per row: conflict-free row reads
-    static constexpr int ROW = HD + PAD;                  // elements per LDS row
-    static constexpr int V16 = HD * ES / 16;              // 16-byte pieces per key row
-    static constexpr int LD16 = C * V16 / 256;            // 16-byte pieces per thread per tensor
-    static constexpr int NTG = 256 / C;                   // query groups in the score pass
-    static constexpr int G = 256 / HD;                    // key groups in the P.V pass
-};
-
-// Every global load (queries or their split-K partials, the head-norm weight, the queries' RoPE rows, the chunk's
-// K and V rows) is issued before the first use: one memory round trip per work-group; the rest runs from LDS.
-template <int HD, int KVT>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
-    using SS = SplitShape<HD, KVT>;
-    constexpr int C = SS::C, ROW = SS::ROW;
-    typedef typename std::conditional<KVT == 0, uint16_t, float>::type kv_t;
-    const int c = blockIdx.x, h = blockIdx.y;
-    const int nq = a.nq;
-    const int kh = h / (a.heads / a.kv_heads);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    __shared__ float qs[16][HD];
-    __shared__ __attribute__((aligned(16))) kv_t Ks[C * ROW];
-    __shared__ __attribute__((aligned(16))) kv_t Vs[C * ROW];
-    __shared__ float sc[16][C];
-    __shared__ float mrow[16], lrow[16];
-    const QPrep& qp = a.qp;
-
-    const int ncache = a.key_hi - a.key_lo;
-    const int ntot = ncache + a.nx;
-    const int k0 = c * C;
-    const int cnt = min(C, ntot - k0);
-
-    // 1. prefetch: the chunk's K and V rows first, then the queries (every load unconditional; absent inputs
-    //    read the zero row), all in flight before the first use
-    uint4 kr[SS::LD16], vr[SS::LD16];
-#pragma unroll
-    for (int j = 0; j < SS::LD16; ++j) {
-        const int u = tid + 256 * j;
-        const int row = u / SS::V16, p16 = u % SS::V16;
-        int kidx = k0 + row;
-        kidx = kidx < ntot ? kidx : ntot - 1;
-        const bool fc = kidx < ncache;
-        const kv_t* kb = fc ? (const kv_t*)a.kc + (size_t)(a.key_lo + kidx) * a.kv_ld
-                            : (const kv_t*)a.kx + (size_t)(kidx - ncache) * a.x_ld;
-        const kv_t* vb = fc ? (const kv_t*)a.vc + (size_t)(a.key_lo + kidx) * a.kv_ld
-                            : (const kv_t*)a.vx + (size_t)(kidx - ncache) * a.x_ld;
-        kr[j] = *((const uint4*)(kb + (size_t)kh * HD) + p16);
-        vr[j] = *((const uint4*)(vb + (size_t)kh * HD) + p16);
-    }
-    constexpr int QPT = 16 * HD / 256;          // query values per thread (nq <= 16)
-    float qv[QPT], ropev[QPT];
-    const float* ropep = qp.rope ? qp.rope_tab : qp.zeros;
-    const int rd = qp.rope ? qp.rope_dims : 0;
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + 256 * j;
-        const int t = i / HD, d = i % HD;
-        const int tt = t < nq ? t : 0;
-        qv[j] = qp.q[(size_t)tt * qp.q_ld + (size_t)h * qp.q_hs + d];
-        const int dd = d < rd ? d : 0;
-        ropev[j] = ropep[(size_t)(qp.rope ? qp.pos_base + tt : 0) * rd + dd];
-    }
-    const bool has_norm = qp.norm_bf16 || qp.norm_f32;
-    const float nw16 = bf16_to_f32((qp.norm_bf16 ? qp.norm_bf16 : (const uint16_t*)qp.zeros)[tid % HD]);
-    const float nw32 = (qp.norm_f32 ? qp.norm_f32 : qp.zeros)[tid % HD];
-    const float nwv = qp.norm_bf16 ? nw16 : nw32;
-    // 2. to LDS
-    constexpr int RTW = HD <= 128 ? HD : 128;   // RoPE'd dims of a query head (NEOX rotates at most 128 here)
-    __shared__ float nws[HD], rts[16][RTW];
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + 256 * j;
-        qs[i / HD][i % HD] = qv[j];
-        if (qp.rope && i % HD < RTW) rts[i / HD][i % HD] = ropev[j];
-    }
-    if (tid < HD) nws[tid] = nwv;
-    (void)has_norm;
-#pragma unroll
-    for (int j = 0; j < SS::LD16; ++j) {
-        const int u = tid + 256 * j;
-        const int row = u / SS::V16, p16 = u % SS::V16;
-        *((uint4*)(Ks + row * ROW) + p16) = kr[j];
-        *((uint4*)(Vs + row * ROW) + p16) = vr[j];
-    }
-    __syncthreads();
-    // 3. query head-norm and RoPE in LDS
-    if (qp.norm_bf16 || qp.norm_f32) {
-        for (int t = wave; t < nq; t += 4) {
-            float ss = 0.f;
-            for (int d = lane; d < HD; d += 64) ss += qs[t][d] * qs[t][d];
-            ss = wave_sum(ss);
-            const float r = 1.f / sqrtf(ss / (float)HD + qp.eps);
-            for (int d = lane; d < HD; d += 64) qs[t][d] *= nws[d] * r;
-        }
-        __syncthreads();
-    }
-    if (qp.rope == 1) {
-        const int half = HD / 2;
-        for (int i = tid; i < nq * half; i += 256) {
-            const int t = i / half, pi = i % half;
-            const float cs = rts[t][pi], sn = rts[t][half + pi];
-            const float x0 = qs[t][2 * pi], x1 = qs[t][2 * pi + 1];
-            qs[t][2 * pi] = x0 * cs - x1 * sn;
-            qs[t][2 * pi + 1] = x1 * cs + x0 * sn;
-        }
-        __syncthreads();
-    } else if (qp.rope == 2) {
-        const int half = qp.rope_dims / 2;
-        for (int i = tid; i < nq * half; i += 256) {
-            const int t = i / half, pi = i % half;
-            const float cs = rts[t][pi], sn = rts[t][half + pi];
-            const float x0 = qs[t][pi], x1 = qs[t][pi + half];
-            qs[t][pi] = x0 * cs - x1 * sn;
-            qs[t][pi + half] = x1 * cs + x0 * sn;
-        }
-        __syncthreads();
-    }
-    // 4. scores: thread (key j, query group tg)
-    {
-        const int j = tid % C, tg = tid / C;
-        const bool valid = j < cnt;
-        const int kidx = k0 + j;
-        const bool from_cache = kidx < ncache;
-        float acc[16 / SS::NTG];
-#pragma unroll
-        for (int q = 0; q < 16 / SS::NTG; ++q) acc[q] = 0.f;
-        for (int d0 = 0; d0 < HD; d0 += 8) {
-            float kk[8];
-            if constexpr (KVT == 0) {
-                const uint4 raw = *(const uint4*)(Ks + j * ROW + d0);
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kk[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
-                    kk[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
-                }
-            } else {
-                const float4 x0 = *(const float4*)(Ks + j * ROW + d0);
-                const float4 x1 = *(const float4*)(Ks + j * ROW + d0 + 4);
-                kk[0] = x0.x; kk[1] = x0.y; kk[2] = x0.z; kk[3] = x0.w;
-                kk[4] = x1.x; kk[5] = x1.y; kk[6] = x1.z; kk[7] = x1.w;
-            }
-#pragma unroll
-            for (int q = 0; q < 16 / SS::NTG; ++q) {
-                const int t = tg + q * SS::NTG;
-                if (t < nq) {
-                    float s2 = acc[q];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s2 += qs[t][d0 + e] * kk[e];
-                    acc[q] = s2;
-                }
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 16 / SS::NTG; ++q) {
-            const int t = tg + q * SS::NTG;
-            if (t < nq) {
-                float v = acc[q] * a.scale;
-                if (!valid) v = -INFINITY;
-                if (a.causal_base >= 0 && from_cache && a.key_lo + kidx > a.causal_base + t) v = -INFINITY;
-                sc[t][j] = v;
-            }
-        }
-    }
-    __syncthreads();
-    // 5. per-query max and exp-sum over the chunk (one wave per query row)
-    for (int t = wave; t < nq; t += 4) {
-        float m = -INFINITY;
-        for (int j = lane; j < C; j += 64) m = fmaxf(m, sc[t][j]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < C; j += 64) {
-            const float p = (m == -INFINITY) ? 0.f : expf(sc[t][j] - m);
-            sc[t][j] = p;
-            l += p;
-        }
-        l = wave_sum(l);
-        if (lane == 0) { mrow[t] = m; lrow[t] = l; }
-    }
-    __syncthreads();
-    // 6. P.V: thread (d, key group kg)
-    float o[16];
-    {
-        const int d = tid % HD, kg = tid / HD;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) o[t] = 0.f;
-        for (int j = kg; j < C; j += SS::G) {
-            float vv;
-            if constexpr (KVT == 0) vv = f16_to_f32(Vs[j * ROW + d]);
-            else vv = Vs[j * ROW + d];
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                if (t < nq) o[t] += sc[t][j] * vv;
-        }
-    }
-    __syncthreads();   // Ks is reused below for the key-group reduction
-    float* red = (float*)Ks;   // [G][16][HD]
-    {
-        const int d = tid % HD, kg = tid / HD;
-#pragma unroll
-        for (int t = 0; t < 16; ++t)
-            if (t < nq) red[(kg * 16 + t) * HD + d] = o[t];
-    }
-    __syncthreads();
-    float* out = a.part + ((size_t)h * a.nchunks + c) * nq * (HD + 2);
-    for (int i = tid; i < nq * HD; i += 256) {
-        const int t = i / HD, d = i % HD;
-        float v = 0.f;
-#pragma unroll
-        for (int g = 0; g < SS::G; ++g) v += red[(g * 16 + t) * HD + d];
-        out[(size_t)t * (HD + 2) + d] = v;
-    }
-    if (tid < nq) {
-        out[(size_t)tid * (HD + 2) + HD] = mrow[tid];
-        out[(size_t)tid * (HD + 2) + HD + 1] = lrow[tid];
+        if (ot < T) frag_store8(a.o_frag, ot, h * HD + d0, o);
     }
 }
 
@@ -809,7 +586,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
             o[e] *= il;
             if (gp) o[e] *= sigmoidf(gt[e]);
         }
-        frag_store8(a.o_frag, a.row0 + t, h * HD + d0, o, a.perm);
+        frag_store8(a.o_frag, a.row0 + t, h * HD + d0, o);
     }
 }
 
@@ -927,10 +704,11 @@ static bool f32_mfma_fits(const AttnArgs& a) {
 }
 
 int attn_chunk_size(int hd, int kv_dtype, int nkeys, int heads) {
+    (void)hd;
+    (void)kv_dtype;
     (void)nkeys;
     (void)heads;
-    if (kv_dtype == 0) return 32;   // the wave kernel's 32-key step
-    return (hd == 128 || hd == 256) ? 32 : 16384 / (hd * 4);
+    return 32;   // the 32-key step of both matrix-core kernels
 }
 
 hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
@@ -947,7 +725,6 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
     if (a.qp.rope && a.qp.rope_dims > (a.hd <= 128 ? a.hd : 128)) return hipErrorInvalidValue;
     if (a.nx > 0 && a.kv_dtype == 0) return hipErrorInvalidValue;   // extra rows are f32: f32 caches only
     if (a.qp.parts > MAX_QSLABS || (a.kv_dtype != 0 && a.qp.parts > 1)) return hipErrorInvalidValue;
-    dim3 grid(a.nchunks, a.heads);
     if (a.kv_dtype == 0) {
         if (a.qp.rope == 2 || (a.qp.rope == 1 && a.qp.rope_dims != a.hd) || a.nx > 0 || (a.key_lo & 31))
             return hipErrorInvalidValue;
@@ -961,21 +738,16 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
     } else if (f32_mfma_fits(a)) {
         const int rows = (a.heads / a.kv_heads) * a.nq;
         dim3 g2(a.nchunks, a.kv_heads);
-        if (a.hd == 128) {
-            if (rows <= 16) attn_split_f32_mfma_kernel<128, 1><<<g2, 256, 0, st>>>(a);
-            else if (rows <= 32) attn_split_f32_mfma_kernel<128, 2><<<g2, 256, 0, st>>>(a);
-            else attn_split_f32_mfma_kernel<128, 3><<<g2, 256, 0, st>>>(a);
+        if (a.hd == 128) {   // the KV-injection drafter: no grouped queries, at most 16 rows
+            if (rows > 16) return hipErrorInvalidValue;
+            attn_split_f32_mfma_kernel<128, 1><<<g2, 256, 0, st>>>(a);
         } else {
             if (rows <= 16) attn_split_f32_mfma_kernel<256, 1><<<g2, 256, 0, st>>>(a);
             else if (rows <= 32) attn_split_f32_mfma_kernel<256, 2><<<g2, 256, 0, st>>>(a);
             else attn_split_f32_mfma_kernel<256, 3><<<g2, 256, 0, st>>>(a);
         }
     } else {
-        if (a.hd == 256 || a.hd == 128) return hipErrorInvalidValue;   // the vector-ALU kernel's chunk is not 32
-        switch (a.hd) {
-        case 64: attn_split_kernel<64, 1><<<grid, 256, 0, st>>>(a); break;
-        default: return hipErrorInvalidValue;
-        }
+        return hipErrorInvalidValue;   // f32 caches: head widths 128 / 256 with ready-made queries
     }
     return hipGetLastError();
 }

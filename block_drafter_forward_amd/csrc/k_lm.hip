@@ -3,11 +3,11 @@
 // z[t][v] = sum_k X[t][k] E[v][k] over the whole vocabulary, for the T <= 16 rows of one draft, and
 // tok[t] = argmax_v z[t][v] (lowest index on ties). The flow-map page runs the target's verify-block matvec
 // ("one read of the table") and then argmaxRows over materialised logits; here the logits never leave registers:
-//   * a wave owns 32 vocabulary rows (two 16-row A tiles of v_mfma_f32_16x16x32_bf16) over the full K and streams
-//     them once from HBM (non-temporal, software-pipelined in chunks of 4 k-steps); the 16 draft rows are the MFMA's
-//     N, as hi/lo bf16 fragments (read through L2 by every wave);
+//   * the waves of a work-group own adjacent 16-row vocabulary tiles (the A operand of v_mfma_f32_16x16x32_bf16)
+//     and walk the k-range in lockstep, streaming the table once from HBM; the 16 draft rows are the MFMA's N, as
+//     hi/lo bf16 fragments staged once per work-group in LDS;
 //   * the wave's best (value, index) per row is reduced across lanes with shuffles, then across the work-group's
-//     4 waves in LDS, then across work-groups with one 64-bit atomicMax per row on an order-preserving key
+//     waves in LDS, then across work-groups with one 64-bit atomicMax per row on an order-preserving key
 //     (value bits, ~index), so ties resolve to the lowest index independent of scheduling;
 //   * a one-work-group finalize kernel turns the keys into token ids and clears them for the next call.
 // Q8_0 tables (the MTP head's lm_head): each k-step is one Q8_0 block; codes go exactly through the bf16 MFMA and
@@ -19,16 +19,10 @@
 
 namespace {
 
-constexpr int CH = 4;   // k-steps per pipeline stage
-
 __device__ __forceinline__ uint32_t nt32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ uint4 ldg_nt(const void* p) {
     const uint32_t* q = (const uint32_t*)p;
     return make_uint4(nt32(q), nt32(q + 1), nt32(q + 2), nt32(q + 3));
-}
-__device__ __forceinline__ uint2 ldg_nt2(const void* p) {
-    const uint32_t* q = (const uint32_t*)p;
-    return make_uint2(nt32(q), nt32(q + 1));
 }
 __device__ __forceinline__ bf16x8_t as_bf(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -51,235 +45,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int WT>
-struct Stage {
-    uint4 a[2][CH];      // bf16 weights, or (WT == 1) codes in .x/.y
-    uint4 bh[CH], bl[CH];
-    float sc[2][CH][4];
-};
-
-// Loads are unconditional (rows past the table are clamped to its last row and discarded later): a conditional
-// load would make the compiler wait for every outstanding load before the next MFMA.
-template <int WT>
-__device__ __forceinline__ void load_stage(Stage<WT>& st, const LmArgs& a, int v0, int s, int r, int g, int lane) {
-    const int K = a.K;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const uint8_t* xb = a.X + (size_t)(s + i) * FRAG_STEP_BYTES + lane * 16;
-        st.bh[i] = *(const uint4*)xb;
-        st.bl[i] = *(const uint4*)(xb + 1024);
-    }
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const size_t row = (size_t)min(v0 + 16 * n + r, a.V - 1);
-        if constexpr (WT == 0) {
-            const uint16_t* E = (const uint16_t*)a.E + row * K;
-#pragma unroll
-            for (int i = 0; i < CH; ++i) st.a[n][i] = ldg_nt(E + kcol(s + i, g, a.perm));
-        } else {
-            const int8_t* C = (const int8_t*)a.E + row * K + (size_t)s * 32 + g * 8;
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                uint2 c = ldg_nt2(C + i * 32);
-                st.a[n][i] = make_uint4(c.x, c.y, 0, 0);
-            }
-            const int nb = K >> 5;
-            const uint16_t* Dd = (const uint16_t*)a.Ed;
-#pragma unroll
-            for (int i = 0; i < CH; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    st.sc[n][i][j] = f16_to_f32(Dd[(size_t)min(v0 + 16 * n + 4 * g + j, a.V - 1) * nb + s + i]);
-        }
-    }
-}
-
-template <int WT>
-__device__ __forceinline__ void compute_stage(const Stage<WT>& st, f32x4_t* acc) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            if constexpr (WT == 0) {
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(st.a[n][i]), as_bf(st.bh[i]), acc[n], 0, 0, 0);
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(st.a[n][i]), as_bf(st.bl[i]), acc[n], 0, 0, 0);
-            } else {
-                const bf16x8_t A = as_bf(i8x8_bf16(make_uint2(st.a[n][i].x, st.a[n][i].y)));
-                f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf(st.bh[i]), p, 0, 0, 0);
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf(st.bl[i]), p, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[n][j] += st.sc[n][i][j] * p[j];
-            }
-        }
-    }
-}
-
-template <int WT>
-__global__ __launch_bounds__(256) void lm_argmax_kernel(LmArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, g = lane >> 4;
-    const int v0 = (blockIdx.x * 4 + wave) * 32;
-    const bool active = v0 < a.V;
-    const bool tile1 = v0 + 16 < a.V;
-    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    if (active) {
-        const int nsteps = a.K >> 5;   // a multiple of 2 * CH
-        Stage<WT> s0, s1;
-        load_stage<WT>(s0, a, v0, 0, r, g, lane);
-        int s = 0;
-        for (; s + 2 * CH < nsteps; s += 2 * CH) {
-            load_stage<WT>(s1, a, v0, s + CH, r, g, lane);
-            compute_stage<WT>(s0, acc);
-            load_stage<WT>(s0, a, v0, s + 2 * CH, r, g, lane);
-            compute_stage<WT>(s1, acc);
-        }
-        load_stage<WT>(s1, a, v0, s + CH, r, g, lane);
-        compute_stage<WT>(s0, acc);
-        compute_stage<WT>(s1, acc);
-    }
-    // lane holds z[t = lane % 16][v0 + 16 n + 4 g + j]
-    const int t = lane & 15;
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
-    if (active) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            if (n == 1 && !tile1) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int v = v0 + 16 * n + 4 * g + j;
-                const float z = acc[n][j];
-                if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
-                if (z > best) { best = z; bidx = v; }   // v increases with (n, j): first max kept
-            }
-        }
-    }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-        const float ob = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bidx, o, 64);
-        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
-    }
-    __shared__ float wb[4][16];
-    __shared__ int wi[4][16];
-    if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
-    __syncthreads();
-    if (threadIdx.x < 16 && threadIdx.x < a.T) {
-        const int tt = threadIdx.x;
-        float b = wb[0][tt];
-        int bi = wi[0][tt];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (wb[w][tt] > b || (wb[w][tt] == b && wi[w][tt] < bi)) { b = wb[w][tt]; bi = wi[w][tt]; }
-        if (bi != 0x7fffffff) {
-            const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
-            atomicMax(&a.best[tt], key);
-        }
-    }
-}
-
-// bf16 tables, row-staged: a wave owns 16 vocabulary rows. Each chunk of 8 k-steps (256 columns) is read as
-// 8 row-contiguous instructions (2 rows x 512 bytes), parked in a wave-private LDS tile and read back in the MFMA A
-// layout -- whole cache lines per instruction instead of the A layout's 16 half lines. The next chunk (weights and
-// activation fragments) is in flight while the current one multiplies.
+// Weights are row-staged: each chunk of 8 k-steps (256 columns) of a wave's 16 vocabulary rows is read as 8
+// row-contiguous instructions (2 rows x 512 bytes), parked in a wave-private LDS tile and read back in the MFMA A
+// layout -- whole cache lines per instruction instead of the A layout's 16 half lines.
 constexpr int RS_PITCH = 33;   // uint4 per LDS row: 32 + 1 pad (conflict-free A reads)
-
-struct RsChunk {
-    uint4 a[8];
-    uint4 bh[8], bl[8];
-};
-
-__device__ __forceinline__ void rs_load(RsChunk& c, const LmArgs& a, int v0, int s, int lane) {
-    const uint8_t* xb = a.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        c.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
-        c.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
-    }
-    // V is a multiple of 16, so a wave's 16 rows are all inside the table
-    const uint16_t* E = (const uint16_t*)a.E + (size_t)(v0 + (lane >> 5)) * a.K + s * 32 + (lane & 31) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c.a[i] = ldg_nt(E + (size_t)(2 * i) * a.K);
-}
-
-__device__ __forceinline__ void rs_compute(const RsChunk& c, uint4* lds, f32x4_t& acc, int lane) {
-    const int hr = lane >> 5, piece = lane & 31, r = lane & 15, g = lane >> 4;
-    __builtin_amdgcn_wave_barrier();   // the previous chunk's LDS reads stay before these writes
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds[(2 * i + hr) * RS_PITCH + piece] = c.a[i];
-    __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint4 av = lds[r * RS_PITCH + 4 * i + g];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(c.bh[i]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(c.bl[i]), acc, 0, 0, 0);
-    }
-}
-
-__global__ __launch_bounds__(256) void lm_argmax_rs_kernel(LmArgs a) {
-    __shared__ uint4 rs_lds[4][16 * RS_PITCH];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int g = lane >> 4;
-    const int v0 = (blockIdx.x * 4 + wave) * 16;
-    const bool active = v0 < a.V;
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (active) {
-        uint4* lds = rs_lds[wave];
-        const int nch = a.K >> 8;   // chunks of 8 k-steps
-        RsChunk c0, c1;
-        rs_load(c0, a, v0, 0, lane);
-        int ch = 0;
-        for (; ch + 2 < nch; ch += 2) {
-            rs_load(c1, a, v0, 8 * (ch + 1), lane);
-            rs_compute(c0, lds, acc, lane);
-            rs_load(c0, a, v0, 8 * (ch + 2), lane);
-            rs_compute(c1, lds, acc, lane);
-        }
-        if (ch + 1 < nch) {
-            rs_load(c1, a, v0, 8 * (ch + 1), lane);
-            rs_compute(c0, lds, acc, lane);
-            rs_compute(c1, lds, acc, lane);
-        } else {
-            rs_compute(c0, lds, acc, lane);
-        }
-    }
-    // lane holds z[t = lane % 16][v0 + 4 g + j]
-    const int t = lane & 15;
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
-    if (active) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int v = v0 + 4 * g + j;
-            const float z = acc[j];
-            if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
-            if (z > best) { best = z; bidx = v; }
-        }
-    }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-        const float ob = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bidx, o, 64);
-        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
-    }
-    __shared__ float wb[4][16];
-    __shared__ int wi[4][16];
-    if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
-    __syncthreads();
-    if (threadIdx.x < 16 && threadIdx.x < a.T) {
-        const int tt = threadIdx.x;
-        float b = wb[0][tt];
-        int bi = wi[0][tt];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (wb[w][tt] > b || (wb[w][tt] == b && wi[w][tt] < bi)) { b = wb[w][tt]; bi = wi[w][tt]; }
-        if (bi != 0x7fffffff) {
-            const unsigned long long key = ((unsigned long long)order_key(b) << 32) | (0xffffffffu - (uint32_t)bi);
-            atomicMax(&a.best[tt], key);
-        }
-    }
-}
 
 // bf16 tables, row-staged weights + work-group-shared activations: the 4 waves of a work-group own 4 adjacent
 // 16-row vocabulary tiles and walk the k-range in lockstep, so each chunk's activation fragments (8 k-steps,
@@ -487,18 +256,10 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
 }  // namespace
 
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
-    if (a.T > 16) return hipErrorInvalidValue;
-    if (a.perm == 0 && a.K % 512 == 0) {
-        if (wtype == 0) lm_argmax_ws_kernel<0, 4><<<(a.V + 63) / 64, 256, 0, st>>>(a);
-        else lm_argmax_ws_kernel<1, 8><<<(a.V + 127) / 128, 512, 0, st>>>(a);
-    } else if (wtype == 0 && a.perm == 0 && a.K % 256 == 0) {
-        lm_argmax_rs_kernel<<<(a.V + 63) / 64, 256, 0, st>>>(a);
-    } else {
-        if ((a.K >> 5) % (2 * CH) != 0) return hipErrorInvalidValue;
-        const int nwg = (a.V + 127) / 128;
-        if (wtype == 0) lm_argmax_kernel<0><<<nwg, 256, 0, st>>>(a);
-        else lm_argmax_kernel<1><<<nwg, 256, 0, st>>>(a);
-    }
+    // rows of a multiple of 512 (an even number of 8-step chunks) and whole 16-row vocabulary tiles
+    if (a.T > 16 || a.K % 512 || a.V % 16) return hipErrorInvalidValue;
+    if (wtype == 0) lm_argmax_ws_kernel<0, 4><<<(a.V + 63) / 64, 256, 0, st>>>(a);
+    else lm_argmax_ws_kernel<1, 8><<<(a.V + 127) / 128, 512, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     lm_finalize_kernel<<<1, 64, 0, st>>>(a.best, a.T, a.tokens);

@@ -2,20 +2,21 @@
 //
 // The one truly dense contraction of the path: the fusion of many context rows (fc / W_c over the concatenated
 // taps, flashmap_drafter.js extendContext; module-dflash.ts #buildContext) and the per-layer K/V projections of the
-// fused rows. Operands are f16 on v_mfma_f32_16x16x32_f16 with f32 accumulation: f32 taps are rounded to f16
-// (2^-11 relative, four times finer than bf16), bf16 weights are widened to f16 exactly (up to f16's subnormal
-// range, |error| <= 2^-25).
+// fused rows. Operands are f16 on v_mfma_f32_16x16x32_f16 with f32 accumulation: each row of f32 taps is scaled by a
+// power of two that brings its largest magnitude into [2^14, 2^15) and rounded to f16 (2^-11 relative, four times
+// finer than bf16; the scale is exact and undone on the f32 output row, so f16's range never limits the taps), bf16
+// weights are widened to f16 exactly (up to f16's subnormal range, |error| <= 2^-25).
 //
 // Large problems (at least one 256 x 256 tile per CU) run prefill_dma_kernel: A and B are both f16 in HBM (the
-// weights converted once when the drafter is created, the taps by one pass before the product) and are streamed
+// weights converted once when the drafter is created, the taps by the scaling pass before the product) and are streamed
 // into LDS by the LDS-direct load (global_load_lds_dwordx4: no registers, no conversion on the way). A k-stage is 64
 // k-values, so every row slice a load touches is one whole 128-byte line (measured: half-line slices moved half the
 // bytes per second); in LDS a row is 8 chunks of 16 bytes with chunk c at slot c ^ (row & 7), which makes the
 // 16 x 32 fragment reads conflict-free (measured with a read microbenchmark: 4 LDS cycles per 1 KB read). Two stage
 // buffers (128 KB); 8 waves as 2 x 4 of 128 x 64; each wave reads the fragments of the next 32-k substep while the
 // current one multiplies, so one barrier per stage is the only synchronisation.
-// Small problems run prefill_kernel: 128 x 128 tiles of 4 waves, operands staged through registers (f32 taps
-// rounded, bf16 weights widened on the way into LDS), two k-stages of loads in flight.
+// Small problems run prefill_kernel: 128 x 128 tiles of 4 waves, operands staged through registers (f16 rows, bf16
+// weights widened on the way into LDS), two k-stages of loads in flight.
 // Work-groups are remapped so each XCD owns a contiguous run of tiles, taken 8 row tiles at a time (the 8 row
 // tiles of a group share B tiles and each A tile is shared by the group's column tiles, in that XCD's L2).
 // Epilogues: f32 rows; a cache store (f16 / f32) at rows start + r, or into the f16 V cache's 32-position tiles
@@ -232,10 +233,10 @@ __device__ __forceinline__ void prefill_epilogue(f32x4_t (&acc)[TI][TJ], const P
 }
 
 // Tile T x T (T = 128: 4 waves as 2 x 2 of 64 x 64; T = 256: 8 waves as 2 x 4 of 128 x 64). Every thread stages
-// 16 k-values of one A row and one B row per k-stage; rows past the end of A are clamped (their results dropped).
+// 16 k-values of one f16 A row and one B row per k-stage; rows past the end of A are clamped (their results dropped).
 // Two work-groups per CU (2 waves per SIMD, <= 256 registers a wave): without the bound the compiler keeps the
 // accumulators in AGPRs next to 151 VGPRs and the kernel runs at one wave per SIMD, 25% slower.
-template <int AF32, int T>
+template <int T>
 __global__ __launch_bounds__(T * 2, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int BM = T, BN = T, NWN = T / 64, TI = T == 128 ? 4 : 8, TJ = 4;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
@@ -268,37 +269,20 @@ __global__ __launch_bounds__(T * 2, 2) void prefill_kernel(PrefillArgs a) {
     const int arow = min(r0 + ldrow, a.rows - 1);
 
     struct PStage {
-        float4 ra[4];
         uint4 rah[2], rb[2];
     };
     auto gload = [&](PStage& r, int kt) {
         const int k = kb + kt * BK + kofs;
-        if constexpr (AF32) {
-            const float4* p = (const float4*)((const float*)Ap + (size_t)arow * K + k);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r.ra[i] = p[i];
-        } else {
-            const uint4* p = (const uint4*)((const uint16_t*)Ap + (size_t)arow * K + k);
-            r.rah[0] = p[0];
-            r.rah[1] = p[1];
-        }
+        const uint4* p = (const uint4*)((const uint16_t*)Ap + (size_t)arow * K + k);
+        r.rah[0] = p[0];
+        r.rah[1] = p[1];
         const uint4* pb = (const uint4*)(G.B + (size_t)(n0 + ldrow) * K + k);
         r.rb[0] = pb[0];
         r.rb[1] = pb[1];
     };
     auto lstore = [&](const PStage& r, int buf) {
-        uint4 h0, h1;
-        if constexpr (AF32) {
-            h0 = make_uint4(pack_f16x2(r.ra[0].x, r.ra[0].y), pack_f16x2(r.ra[0].z, r.ra[0].w),
-                            pack_f16x2(r.ra[1].x, r.ra[1].y), pack_f16x2(r.ra[1].z, r.ra[1].w));
-            h1 = make_uint4(pack_f16x2(r.ra[2].x, r.ra[2].y), pack_f16x2(r.ra[2].z, r.ra[2].w),
-                            pack_f16x2(r.ra[3].x, r.ra[3].y), pack_f16x2(r.ra[3].z, r.ra[3].w));
-        } else {
-            h0 = r.rah[0];
-            h1 = r.rah[1];
-        }
-        *(uint4*)&As[buf][ldrow][kofs] = h0;
-        *(uint4*)&As[buf][ldrow][kofs + 8] = h1;
+        *(uint4*)&As[buf][ldrow][kofs] = r.rah[0];
+        *(uint4*)&As[buf][ldrow][kofs + 8] = r.rah[1];
         uint32_t w[8] = {r.rb[0].x, r.rb[0].y, r.rb[0].z, r.rb[0].w, r.rb[1].x, r.rb[1].y, r.rb[1].z, r.rb[1].w};
         uint32_t o[8];
 #pragma unroll
@@ -462,10 +446,37 @@ __global__ void rope_prefill_kernel(const float* __restrict__ tab, int P, int rd
     o[4 + j] = tab[(size_t)p * rdim + half + i];
 }
 
-__global__ void f32_to_f16_kernel(const float* __restrict__ x, size_t n4, uint2* __restrict__ y) {
-    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        const float4 v = ((const float4*)x)[i];
-        y[i] = make_uint2(pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w));
+// Taps of one append -> f16, one work-group per row: the row's largest magnitude m picks a power of two s = 2^k with
+// m s in [2^14, 2^15), the row is stored as f16(x s) (an exact scaling, then one rounding, so f16's range can
+// neither overflow nor flush the row whatever its magnitude) and 1 / s goes to rscale[row], by which the consumer
+// of the context projection multiplies that row's f32 output. A row whose largest magnitude is 0 or not finite
+// keeps s = 1.
+__global__ __launch_bounds__(256) void taps_f16_kernel(const float* __restrict__ x, int KT, uint2* __restrict__ y,
+                                                       float* __restrict__ rscale) {
+    const int row = blockIdx.x, n4 = KT >> 2;
+    const float4* p = (const float4*)(x + (size_t)row * KT);
+    float m = 0.f;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        const float4 v = p[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    __shared__ float red[4];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int k = 0;
+    if (m > 0.f && m <= 3.4028234e38f) {
+        int ex;
+        frexpf(m, &ex);   // m = f 2^ex, f in [0.5, 1): m 2^(15 - ex) in [2^14, 2^15)
+        k = min(max(15 - ex, -100), 100);
+    }
+    const float s = ldexpf(1.f, k);
+    if (threadIdx.x == 0) rscale[row] = ldexpf(1.f, -k);
+    uint2* q = y + (size_t)row * n4;
+    for (int i = threadIdx.x; i < n4; i += 256) {   // the second pass reads the row back from L2
+        const float4 v = p[i];
+        q[i] = make_uint2(pack_f16x2(v.x * s, v.y * s), pack_f16x2(v.z * s, v.w * s));
     }
 }
 
@@ -498,13 +509,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int nwg, hipStream_t st) {
         if (a.g[i].epi == PF_CACHE_K && a.g[i].knorm && (!a.rope_pf || a.rope_dims != a.hd || a.hd % 64))
             return hipErrorInvalidValue;
     if (T == 256) {   // f16 A and f16 copies of every group's B; 64-k stages
-        if (a.a_f32 || a.K % 64) return hipErrorInvalidValue;
+        if (a.K % 64) return hipErrorInvalidValue;
         for (int i = 0; i < a.ngroups; ++i)
             if (!a.g[i].B16) return hipErrorInvalidValue;
         prefill_dma_kernel<1><<<nwg, 512, 0, st>>>(a);
     } else {
-        if (a.a_f32) prefill_kernel<1, 128><<<nwg, 256, 0, st>>>(a);
-        else prefill_kernel<0, 128><<<nwg, 256, 0, st>>>(a);
+        prefill_kernel<128><<<nwg, 256, 0, st>>>(a);
     }
     return hipGetLastError();
 }
@@ -516,12 +526,9 @@ hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hi
     return hipGetLastError();
 }
 
-hipError_t launch_f32_to_f16(const float* x, size_t n, uint16_t* y, hipStream_t st) {
-    if (n % 4 || ((uintptr_t)x & 15) || ((uintptr_t)y & 7)) return hipErrorInvalidValue;
-    if (n == 0) return hipSuccess;
-    const size_t n4 = n / 4;
-    const int grid = (int)std::min<size_t>((n4 + 255) / 256, 4096);
-    f32_to_f16_kernel<<<grid, 256, 0, st>>>(x, n4, (uint2*)y);
+hipError_t launch_taps_f16(const float* x, int n, int KT, uint16_t* y, float* rscale, hipStream_t st) {
+    if (n < 1 || KT % 4 || ((uintptr_t)x & 15) || ((uintptr_t)y & 7)) return hipErrorInvalidValue;
+    taps_f16_kernel<<<n, 256, 0, st>>>(x, KT, (uint2*)y, rscale);
     return hipGetLastError();
 }
 

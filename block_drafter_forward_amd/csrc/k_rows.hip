@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     const float* p1f = a.norm == ROW_LN_MOD ? a.shift : zf;
     const uint16_t* wb = a.w_bf16 ? a.w_bf16 : zb;
     const bool w_is_b16 = a.norm == ROW_RMS && a.w_bf16 != nullptr;
+    const float rsc = a.row_scale ? a.row_scale[t] : 1.f;
 
     float v[NS][8], u[NS][8], gv[NS][8], p0[NS][8], p1[NS][8];
 #pragma unroll
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
 #pragma unroll
                 for (int s = 0; s < S; ++s) uu += pp[s][e];
             }
-            u[j][e] = uu;
+            u[j][e] = uu * rsc;
             v[j][e] = use_b16 ? bb[e] : bf[e];
             if (!a.gate) gv[j][e] = 1.f;
             if (w_is_b16) p0[j][e] = w16[e];
@@ -131,13 +132,13 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
                 else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * p0[j][e];
                 else h[e] = v[j][e];
             }
-            if (a.frag_out) frag_store8(a.frag_out, t + a.row0, a.frag_koff + i0, h, a.frag_perm);
-            if (a.f32_out) st8(a.f32_out + (size_t)(t + a.row0) * a.out_ld + i0, h);
+            if (a.frag_out) frag_store8(a.frag_out, t + a.row0, a.frag_koff + i0, h);
+            if (a.f32_out) st8(a.f32_out + (size_t)(t + (a.f32_local ? 0 : a.row0)) * a.out_ld + i0, h);
         }
     }
 }
 
-__global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag, int perm) {
+__global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag) {
     const int t = blockIdx.y;
     const int slot = blockIdx.x * 256 + threadIdx.x;
     if (slot * 8 >= K) return;
@@ -145,13 +146,13 @@ __global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag,
     const float* p = x + (size_t)t * ld + slot * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = p[e];
-    frag_store8(frag, t, slot * 8, v, perm);
+    frag_store8(frag, t, slot * 8, v);
 }
 
 // Token ids outside [0, V) are clamped into the table (a device-side id cannot be validated by the host).
 __device__ __forceinline__ size_t clamp_row(int32_t id, int V) { return (size_t)(id < 0 ? 0 : (id >= V ? V - 1 : id)); }
 
-__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
+__global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag,
                                    int frow) {
     const int slot = blockIdx.x * 256 + threadIdx.x;
     if (slot * 8 >= K) return;
@@ -159,7 +160,7 @@ __global__ void gather_frag_kernel(const uint16_t* E, int V, int K, const int32_
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(E[row * K + slot * 8 + e]);
-    frag_store8(frag, frow, slot * 8, v, perm);
+    frag_store8(frag, frow, slot * 8, v);
 }
 
 __global__ void gather_f32_kernel(const uint16_t* E, int V, int K, const int32_t* idx, const uint16_t* add,
@@ -337,12 +338,13 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 
 template <int NS, int NSLAB>
 __global__ __launch_bounds__(256) void rms_f16_kernel(const float* x, int D, const uint16_t* w, float eps,
-                                                      uint16_t* out, long long slab_stride) {
+                                                      uint16_t* out, long long slab_stride, const float* rscale) {
     const int t = blockIdx.x;
     const int nslot = D >> 3;
     __shared__ float red[4];
     float v[NS][8];
     float q = 0.f;
+    const float rs = rscale ? rscale[t] : 1.f;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int slot = threadIdx.x + j * 256;
@@ -357,7 +359,10 @@ __global__ __launch_bounds__(256) void rms_f16_kernel(const float* x, int D, con
                 v[j][4] += a1.x; v[j][5] += a1.y; v[j][6] += a1.z; v[j][7] += a1.w;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q += v[j][e] * v[j][e];
+            for (int e = 0; e < 8; ++e) {
+                v[j][e] *= rs;
+                q += v[j][e] * v[j][e];
+            }
         }
     }
     const float r = 1.f / sqrtf(block_sum256(q, red) / (float)D + eps);
@@ -408,16 +413,16 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
     }
 }
 
-hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, int perm, hipStream_t st) {
+hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st) {
     dim3 grid((K / 8 + 255) / 256, T);
-    f32_to_frag_kernel<<<grid, 256, 0, st>>>(x, ld, K, frag, perm);
+    f32_to_frag_kernel<<<grid, 256, 0, st>>>(x, ld, K, frag);
     return hipGetLastError();
 }
 
-hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag, int perm,
+hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag,
                               hipStream_t st, int row) {
     if (row < 0 || row >= 16) return hipErrorInvalidValue;
-    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, perm, row);
+    gather_frag_kernel<<<(K / 8 + 255) / 256, 256, 0, st>>>(E, V, K, idx, frag, row);
     return hipGetLastError();
 }
 
@@ -511,24 +516,24 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
 
 template <int NSLAB>
 hipError_t launch_rms_f16_s(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out,
-                            long long slab_stride, hipStream_t st) {
+                            long long slab_stride, const float* rscale, hipStream_t st) {
     const int ns = (D / 8 + 255) / 256;
     switch (ns) {
-    case 1: rms_f16_kernel<1, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride); break;
-    case 2: rms_f16_kernel<2, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride); break;
-    case 3: rms_f16_kernel<3, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride); break;
+    case 1: rms_f16_kernel<1, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride, rscale); break;
+    case 2: rms_f16_kernel<2, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride, rscale); break;
+    case 3: rms_f16_kernel<3, NSLAB><<<n, 256, 0, st>>>(x, D, w, eps, out, slab_stride, rscale); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, int nslab,
-                          long long slab_stride, hipStream_t st) {
+                          long long slab_stride, const float* rscale, hipStream_t st) {
     if (nslab > 1 && slab_stride < (long long)n * D) return hipErrorInvalidValue;
     switch (nslab) {
-    case 1: return launch_rms_f16_s<1>(x, n, D, w, eps, out, 0, st);
-    case 2: return launch_rms_f16_s<2>(x, n, D, w, eps, out, slab_stride, st);
-    case 4: return launch_rms_f16_s<4>(x, n, D, w, eps, out, slab_stride, st);
+    case 1: return launch_rms_f16_s<1>(x, n, D, w, eps, out, 0, rscale, st);
+    case 2: return launch_rms_f16_s<2>(x, n, D, w, eps, out, slab_stride, rscale, st);
+    case 4: return launch_rms_f16_s<4>(x, n, D, w, eps, out, slab_stride, rscale, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -67,7 +67,7 @@ struct SkStage {
 
 template <int NT, int WT, int SKC>
 __device__ __forceinline__ void sk_load(SkStage<NT, WT, SKC>& st, const SkinnyGroup& G, int K, int m0, int s, int r,
-                                        int g, int lane, int perm) {
+                                        int g, int lane) {
     const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
 #pragma unroll
     for (int i = 0; i < SKC; ++i) {
@@ -79,7 +79,7 @@ __device__ __forceinline__ void sk_load(SkStage<NT, WT, SKC>& st, const SkinnyGr
         if constexpr (WT == SKW_BF16) {
             const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + r) * K;
 #pragma unroll
-            for (int i = 0; i < SKC; ++i) st.a[n][i] = ldg_nt((const uint4*)(W + kcol(s + i, g, perm)));
+            for (int i = 0; i < SKC; ++i) st.a[n][i] = ldg_nt((const uint4*)(W + kcol(s + i, g)));
         } else {
             const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2);
             const uint16_t* Dd = (const uint16_t*)(n == 0 ? G.Wd : G.W2d);
@@ -308,19 +308,19 @@ __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skin
         }
     } else if constexpr (UP == 1) {
         SkStage<NT, WT, SKC> st;
-        sk_load<NT, WT, SKC>(st, G, K, m0, s0, r, g, lane, a.perm);
+        sk_load<NT, WT, SKC>(st, G, K, m0, s0, r, g, lane);
         sk_compute<NT, WT, SKC>(st, acc);
     } else {
         SkStage<NT, WT, SKC> st0, st1;
-        sk_load<NT, WT, SKC>(st0, G, K, m0, s0, r, g, lane, a.perm);
+        sk_load<NT, WT, SKC>(st0, G, K, m0, s0, r, g, lane);
         int s = 0;
         for (; s + 2 * SKC < KW; s += 2 * SKC) {
-            sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane, a.perm);
+            sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane);
             sk_compute<NT, WT, SKC>(st0, acc);
-            sk_load<NT, WT, SKC>(st0, G, K, m0, s0 + s + 2 * SKC, r, g, lane, a.perm);
+            sk_load<NT, WT, SKC>(st0, G, K, m0, s0 + s + 2 * SKC, r, g, lane);
             sk_compute<NT, WT, SKC>(st1, acc);
         }
-        sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane, a.perm);
+        sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane);
         sk_compute<NT, WT, SKC>(st0, acc);
         sk_compute<NT, WT, SKC>(st1, acc);
     }
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skin
             float vals[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) vals[e] = tile[tt][8 * h + e];
-            frag_store8((uint8_t*)G.out, tt, m0 + 8 * h, vals, a.perm);
+            frag_store8((uint8_t*)G.out, tt, m0 + 8 * h, vals);
         }
     }
 }
@@ -378,12 +378,12 @@ template <int NT, int WT>
 hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
     const int KW = a.KW;
     dim3 grid(nwg), block(256);
-    if (WT == SKW_BF16 && a.perm == 0 && KW % 4 == 0) {
+    if (WT == SKW_BF16 && KW % 4 == 0) {
         if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
         else skinny_kernel<NT, WT, 2, 4><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }
-    if (WT == SKW_Q8_0 && a.perm == 0 && KW % 8 == 0) {
+    if (WT == SKW_Q8_0 && KW % 8 == 0) {
         skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }

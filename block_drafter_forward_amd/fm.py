@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.fm_mtp_chain.restype = ctypes.c_int
         L.fm_markov_argmax.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp]
         L.fm_markov_argmax.restype = ctypes.c_int
-        L.fm_time_condition.argtypes = [vp, ctypes.c_float, ctypes.c_float, i32, i32, ctypes.c_float, vp]
+        L.fm_time_condition.argtypes = [vp, ctypes.c_float, ctypes.c_float, i32, i32, ctypes.c_float, vp, vp]
         L.fm_time_condition.restype = ctypes.c_int
         L.fm_draft_batch.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(FmBlockArgs), vp, vp]
         L.fm_draft_batch.restype = ctypes.c_int
@@ -198,8 +198,10 @@ class Drafter:
                                       conf.data_ptr(), scores.data_ptr() if scores is not None else None,
                                       _stream_ptr(stream)))
 
-    def fm_time_condition(self, s: float, t: float, time_dim: int, cond_dim: int, time_scale: float, stream=None):
-        check(self.L.fm_time_condition(self.h, s, t, time_dim, cond_dim, time_scale, _stream_ptr(stream)))
+    def fm_time_condition(self, s: float, t: float, time_dim: int, cond_dim: int, time_scale: float, table_out=None,
+                          stream=None):
+        check(self.L.fm_time_condition(self.h, s, t, time_dim, cond_dim, time_scale,
+                                       table_out.data_ptr() if table_out is not None else None, _stream_ptr(stream)))
 
     @staticmethod
     def fm_draft_batch(drafters, requests, hidden_out, stream=None):

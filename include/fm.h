@@ -63,7 +63,9 @@ enum fm_wtype { FM_W_BF16 = 0, FM_W_Q8_0 = 1 };
  *   max_ctx    cache rows (positions) held per layer
  *   rope       FM_ROPE_*; rope_dims rotated dims per head (NEOX partial); rope_theta the base
  *   ln_eps / rms_eps / qk_eps   LayerNorm, RMSNorm and q/k head-norm epsilons
- *   mlp        FM_MLP_*; kv_dtype FM_KV_* (cache element type); wtype FM_W_* (matrix storage)           */
+ *   mlp        FM_MLP_*; kv_dtype FM_KV_* (cache element type); wtype FM_W_* (matrix storage)
+ * Supported shapes (FM_E_UNSUPPORTED otherwise): target_dim a multiple of 512; head_dim 64 or 128 (flow-map), 128 or
+ * 256 (KV-inject), 256 (MTP); kv_heads == heads except for the MTP head.                                      */
 typedef struct fm_config {
     int32_t variant;
     int32_t dim;
@@ -111,9 +113,11 @@ size_t fm_workspace_bytes(const fm_config* cfg);
  * workspace must be at least fm_kv_bytes / fm_workspace_bytes and 256-byte aligned.
  * Enqueues the create-time work on `stream`: clearing the workspace's counters, the RoPE table (angles in f64,
  * stored f32, and its permuted prefill copy), f16 copies of the context-projection and per-layer K/V weights
- * (flow-map and KV-inject) and, for the flow-map, the zero-noise slot input x_embed(state_norm(mean row of
- * lm_head)) + bias (flashmap_drafter.js, init), and that row's layer-0 modulation and q / k / v projections (the
- * same for every draft). The weights must keep their values while the handle lives.
+ * (flow-map and KV-inject) and, for the flow-map, a private copy of the modulation table "mod", the zero-noise slot
+ * input x_embed(state_norm(mean row of lm_head)) + bias (flashmap_drafter.js, init), and layer 0 of a draft from
+ * that row up to the cross-attention's q projection (the same for every draft: each slot starts from that row, and
+ * the self-attention of identical v rows returns v, so this holds at zero noise, the only slot input built here).
+ * The weights must keep their values while the handle lives.
  * Context length starts at 0.
  * Errors: FM_E_INVALID (null pointer, dim % heads, sizes not multiples of 32/256, block > 16 ...),
  * FM_E_MISSING_WEIGHT, FM_E_UNSUPPORTED, FM_E_HIP. */
@@ -125,7 +129,9 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
  *   flow-map   c = RMSNorm(fc(taps); hidden_norm), per layer K = RoPE(headRMSNorm(k_proj c; k_norm)), V = v_proj c
  *   KV-inject  c = RMSNorm(W_c taps; ctx_norm), per layer K = W_k RMSNorm(c; attn_norm), V likewise
  * written to the cache (f16 or f32). Any start <= current length may be rewritten (a rewind); the length becomes
- * start + n. taps must be 16-byte aligned (it is read in 16-byte pieces).
+ * start + n. taps must be 16-byte aligned (it is read in 16-byte pieces). Appends of more than 16 rows round the
+ * taps to f16 for the matrix cores after scaling each row by a power of two into f16's range (undone in f32), so
+ * any finite magnitude is accepted; smaller appends keep f32 range (hi + lo bf16 operands).
  * Errors: FM_E_INVALID (n < 1, start < 0, start > length, null or misaligned taps, MTP handle),
  * FM_E_CONTEXT_FULL when start + n + block + 1 > max_ctx (extendContext's own check). */
 fm_status fm_context_append(fm_drafter* d, const float* taps, int32_t n, int32_t start, void* stream);
@@ -155,7 +161,12 @@ typedef struct fm_block_args {
  * (pos + rows (+1) > max_ctx). */
 fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_out, void* stream);
 
-/* tokens[r] = argmax_v (hidden[r] . lm_head[v]) for r < rows (ties to the lowest index), int32 on the device.
+/* tokens[r] = argmax_v (hidden[r] . lm_head[v]) for r < rows (ties to the lowest index), int32 on the device: the
+ * target's lm_head applied to the draft's head output and a greedy argmax per row (flashmap_drafter.js draft: the
+ * verify-block matvec over the target's head (mvT_ / mm_) and argmaxRows; module-dflash.ts #baseLogits and
+ * argmaxAxis; ternary_bonsai_2_mtp.js MTPRunner's lm micro-graph), fused so the [rows][vocab] logits are never
+ * stored. hidden is device f32 [rows][target_dim]; the table is the "lm_head.weight" (bf16 [vocab][target_dim]) or
+ * "lm_head" (Q8_0) tensor named at fm_create.
  * logits, if not NULL, receives the full [rows][vocab] f32 logits (a debug path; the fused path never writes them).
  * Errors: FM_E_INVALID (rows < 1 or > 16, null hidden / tokens). */
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits,
@@ -193,14 +204,16 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
  * angles of time * time_scale rounded to f32 as the page rounds them) through the time_embed / jump_embed MLPs
  * (linear_1 [cond_dim][time_dim], SiLU, linear_2 [cond_dim][cond_dim], bf16, with biases), cond = SiLU(sum), then
  * every norm's [scale | shift | gate] = its adaLN linear (layers.<l>.{self_attn,cross_attn,mlp}_adaln.linear and
- * final_adaln.linear, bf16 [3 dim][cond_dim] + bias) of cond. The table is written IN PLACE into the f32 buffer
- * registered as "mod" at fm_create (the caller's memory), so later drafts use it, and recomputes the draft's
- * layer-0 projections of the zero-noise slot row, which depend on that table. Create-time work: the page
- * computes it once per jump (zero noise to tokens: s = 0, t = 1).
+ * final_adaln.linear, bf16 [3 dim][cond_dim] + bias) of cond. Create-time work: the page computes it once per jump
+ * (zero noise to tokens: s = 0, t = 1).
+ * The table goes into this handle's own copy of the modulation table (taken from the "mod" tensor at fm_create;
+ * the caller's "mod" tensor is never written, so other handles created on the same weights keep their tables), and
+ * the draft's cached layer-0 projections of the zero-noise slot row, which depend on it, are recomputed.
+ * table_out, if not NULL, receives a copy of the new table (device f32 [3 layers + 1][3 dim]).
  * Errors: FM_E_INVALID (not a flow-map drafter, missing weights, time_dim odd or outside [2, 1024], cond_dim
  * outside [1, 1024]), FM_E_UNSUPPORTED (more than 49 norms). */
 fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, int32_t cond_dim, float time_scale,
-                            void* stream);
+                            float* table_out, void* stream);
 
 /* Batched drafting (module-dflash.ts forwardRows over anchors[]; for the MTP head, several sequences' rows in one
  * pass): one block forward for B requests. Handle ds[b] holds request b's context (its KV cache); all handles share
@@ -209,7 +222,8 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
  * streams its weights once for all rows; each request attends over its own cache (KV-injection: its context rows
  * ++ its block rows; MTP: causal over [kv_lo, pos + m], after writing its rows' K/V at pos). hidden_out gets the
  * rows in request order (KV-injection: block rows per request; MTP: args[b].rows each), at most 16 in all; the
- * lm_head over them is fm_lm_argmax(ds[0], hidden_out, rows, ...).
+ * lm_head over them is fm_lm_argmax(ds[0], hidden_out, rows, ...). KV-injection: each handle keeps its own request's
+ * normed backbone rows, so fm_markov_argmax(ds[b], request b's rows of hidden_out, ...) decodes request b.
  * Errors: FM_E_INVALID (null pointers, B < 1, more than 16 rows, handles with other shapes or other weight
  * tensors, a handle twice, a request's own fm_draft_block errors), FM_E_CONTEXT_FULL (an MTP request past its
  * cache), FM_E_UNSUPPORTED (flow-map handles: a block alone is 16 rows). */

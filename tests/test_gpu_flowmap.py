@@ -267,14 +267,17 @@ def test_tiny_time_conditioning(widths):
     d = fm.Drafter(cfg, dw)
     o = flowmap.FlowMapOracle(cfg, W)
     L, D = cfg["layers"], cfg["dim"]
+    mod0 = dw["mod"].cpu().numpy()
+    tab = torch.empty(3 * L + 1, 3 * D, dtype=torch.float32, device="cuda")
     for s_, t_ in ((0.25, 0.5), (0.0, 1.0)):
         _say(f"tiny: time conditioning {s_} -> {t_}")
-        d.fm_time_condition(s_, t_, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"])
+        d.fm_time_condition(s_, t_, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"], table_out=tab)
         torch.cuda.synchronize()
-        got = dw["mod"].cpu().numpy().reshape(3 * L + 1, 3 * D)
+        got = tab.cpu().numpy()
         ref = o.time_conditioning(s_, t_).reshape(3 * L + 1, 3 * D)
         e = assert_rows_close(got, ref, tol=1e-4, what=f"table {s_}->{t_}")
         _say(f"tiny: table err {e:.2e}")
+    assert np.array_equal(dw["mod"].cpu().numpy(), mod0), "the caller's modulation table was written"
     o.use_table(ref.reshape(-1))
     taps = gen.taps(cfg, "prefill", cfg["ctx_rows"])
     o.context_append(taps, 0)
@@ -309,10 +312,84 @@ def test_flashmap_time_conditioning_table():
     d = fm.Drafter(cfg, dw)
     o = flowmap.FlowMapOracle(cfg, W)
     L, D = cfg["layers"], cfg["dim"]
+    tab = torch.empty(3 * L + 1, 3 * D, dtype=torch.float32, device="cuda")
     for s_, t_ in ((0.0, 1.0), (0.3, 0.85)):
-        d.fm_time_condition(s_, t_, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"])
+        d.fm_time_condition(s_, t_, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"], table_out=tab)
         torch.cuda.synchronize()
-        got = dw["mod"].cpu().numpy().reshape(3 * L + 1, 3 * D)
+        got = tab.cpu().numpy()
         ref = o.time_conditioning(s_, t_).reshape(3 * L + 1, 3 * D)
         e = assert_rows_close(got, ref, tol=1e-4, what=f"flashmap table {s_}->{t_}")
         _say(f"flashmap: time conditioning {s_} -> {t_}: table err {e:.2e}")
+
+
+def test_tiny_handles_sharing_weights_keep_their_own_tables():
+    """Two drafters created on the same weight tensors: time conditioning of one changes that handle's modulation
+    table only. The other still drafts with the table it was created with, and each matches an oracle drafting
+    with its own table."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = configs.get("tiny", time_dim=256, cond_dim=256, time_scale=1000.0)
+    W = gen.make_weights(cfg)
+    dw = fm.upload_weights(W)
+    da, db = fm.Drafter(cfg, dw), fm.Drafter(cfg, dw)
+    oa, ob = flowmap.FlowMapOracle(cfg, W), flowmap.FlowMapOracle(cfg, W)
+    _say("tiny: two handles on one weight set, time conditioning on the first")
+    da.fm_time_condition(0.0, 1.0, cfg["time_dim"], cfg["cond_dim"], cfg["time_scale"])
+    oa.use_table(oa.time_conditioning(0.0, 1.0).reshape(-1))
+    taps = gen.taps(cfg, "shared", cfg["ctx_rows"])
+    pos = cfg["ctx_rows"]
+    for d, o, what in ((da, oa, "conditioned handle"), (db, ob, "other handle")):
+        o.context_append(taps, 0)
+        d.fm_context_append(torch.from_numpy(taps).cuda(), 0)
+        hid, tok, _, _ = _draft(fm, d, cfg, anchor=99, pos=pos, debug=False)
+        out, _ = o.draft_block(99, pos)
+        _, z = o.lm_argmax(out)
+        e = assert_rows_close(hid, out, what=what)
+        assert_tokens_match(tok, z)
+        _say(f"tiny: {what}: hidden err {e:.2e}")
+
+
+@pytest.mark.parametrize("n", [40, 16, 5])
+def test_tiny_taps_over_f16_range(n):
+    """Tap rows whose magnitudes span 1e-3 .. 1e6 (rows far outside f16's range and rows near its subnormals, and
+    within each row values spread over three decades): an append of more than 16 rows (f16 matrix-core route, rows
+    scaled by powers of two) and appends of 16 rows or fewer (hi + lo bf16 route) both match the oracle's cache rows
+    and draft, and the two routes agree with each other."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = configs.get("tiny")
+    W = gen.make_weights(cfg)
+    dw = fm.upload_weights(W)
+    rows = 40
+    taps = gen.taps(cfg, "wide-range", rows)
+    rng = np.random.default_rng(7)
+    row_mag = np.logspace(-3, 6, rows)
+    rng.shuffle(row_mag)
+    taps = (taps * row_mag[:, None] * 10.0 ** rng.uniform(-1.5, 1.5, taps.shape)).astype(np.float32)
+    d = fm.Drafter(cfg, dw)
+    o = flowmap.FlowMapOracle(cfg, W)
+    _say(f"tiny: {rows} wide-range tap rows appended {n} at a time")
+    for r0 in range(0, rows, n):
+        t = taps[r0:r0 + n]
+        o.context_append(t, r0)
+        d.fm_context_append(torch.from_numpy(np.ascontiguousarray(t)).cuda(), r0)
+    torch.cuda.synchronize()
+    w = _check_cache(d, o, cfg, 0, rows, f"wide-range appends of {n}")
+    hid, tok, _, _ = _draft(fm, d, cfg, anchor=11, pos=rows, debug=False)
+    out, _ = o.draft_block(11, rows)
+    _, z = o.lm_argmax(out)
+    e = assert_rows_close(hid, out, what="hidden")
+    assert_tokens_match(tok, z)
+    _say(f"tiny: appends of {n}: cache err {w:.2e}, hidden err {e:.2e}")
+    # the other route over the same rows: one append of all 40 (n = 16, 5) or 16-row pieces (n = 40)
+    d2 = fm.Drafter(cfg, dw)
+    m = 16 if n > 16 else rows
+    for r0 in range(0, rows, m):
+        d2.fm_context_append(torch.from_numpy(np.ascontiguousarray(taps[r0:r0 + m])).cuda(), r0)
+    torch.cuda.synchronize()
+    for l in range(cfg["layers"]):
+        for which in (0, 1):
+            assert_rows_close(_cache_rows(d, l, which, 0, rows), _cache_rows(d2, l, which, 0, rows),
+                              what=f"routes agree, layer {l} {'KV'[which]}")

@@ -177,6 +177,23 @@ def test_kvinject_batched_requests(name):
         s = single.cpu().numpy()
         assert np.max(np.abs(s - h[rows])) <= 1e-6 * np.max(np.abs(s)), "batched rows differ from the single draft"
         _say(f"{name}: request {b}: hidden err {e:.2e}, tokens exact on {k}/{G}")
+    # each request's Markov-corrected decode on its own handle reads that request's normed backbone rows
+    if "markov_rank" in cfg:
+        rk = cfg["markov_rank"]
+        for b in range(B):
+            rows = slice(b * G, (b + 1) * G)
+            tk = torch.empty(G, dtype=torch.int32, device="cuda")
+            cf = torch.empty(G, dtype=torch.float32, device="cuda")
+            sc = torch.empty(G, cfg["vocab"], dtype=torch.float32, device="cuda")
+            ds[b].fm_markov_argmax(hid[rows], G, an[b:b + 1], rk, tk, cf, sc)
+            torch.cuda.synchronize()
+            gt = tk.cpu().numpy()
+            out, _ = os_[b].draft_block(anchors[b])
+            _, osc, oconf = os_[b].markov_decode(os_[b].block_n, out, anchors[b], follow=gt)
+            assert_tokens_match(gt, osc)
+            assert_rows_close(sc.cpu().numpy(), osc, what=f"request {b} Markov scores")
+            assert np.max(np.abs(cf.cpu().numpy() - oconf)) < 1e-4, (b, cf.cpu().numpy(), oconf)
+            _say(f"{name}: request {b}: Markov decode on its own handle, conf {np.round(oconf, 4).tolist()}")
     with pytest.raises(fm.FmError) as ex:
         fm.Drafter.fm_draft_batch([ds[0], ds[0]], [{"anchor": an[0:1]}, {"anchor": an[1:2]}], hid)
     assert ex.value.status == fm.FM_E_INVALID
