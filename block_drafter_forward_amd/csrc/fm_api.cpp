@@ -1334,6 +1334,36 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     return FM_OK;
 }
 
+fm_status fm_lm_argmax_static(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, void* stream) {
+    g_err.clear();
+    if (!d || !hidden || !tokens) return fail(FM_E_INVALID, "null argument");
+    if (rows < 1 || rows > TMAX) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, TMAX);
+    const int K = d->c.target_dim;
+    if ((size_t)256 + (size_t)K * 64 > STATIC_SCRATCH_BYTES)
+        return fail(FM_E_INVALID, "target_dim %d: the static scratch holds fragments of rows up to %d wide", K,
+                    (int)((STATIC_SCRATCH_BYTES - 256) / 64));
+    hipError_t e = hipSuccess;
+    uint8_t* s = (uint8_t*)static_scratch(&e);
+    if (!s) return fail(FM_E_HIP, "static scratch: %s", hipGetErrorString(e));
+    hipStream_t st = (hipStream_t)stream;
+    unsigned long long* keys = (unsigned long long*)s;   // must start at zero: cleared by a kernel on every call
+    uint8_t* fr = s + 256;
+    HIPCHK(launch_fill_u32((uint32_t*)keys, 32, 0u, st));
+    HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
+    LmArgs a{};
+    const bool q8 = d->c.wtype == FM_W_Q8_0;
+    a.E = q8 ? d->W("lm_head.q") : d->W("lm_head.weight");
+    a.Ed = q8 ? d->W("lm_head.d") : nullptr;
+    a.X = fr;
+    a.V = d->c.vocab;
+    a.K = K;
+    a.T = rows;
+    a.best = keys;
+    a.tokens = tokens;
+    HIPCHK(launch_lm_argmax(a, q8 ? 1 : 0, st));
+    return FM_OK;
+}
+
 fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t steps, int32_t pos, int32_t kv_lo,
                        float* hidden_out, void* stream) {
     g_err.clear();

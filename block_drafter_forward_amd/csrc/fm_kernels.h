@@ -225,6 +225,12 @@ struct LmArgs {
 };
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
 
+// The library's static scratch (fm_static.hip): a file-scope device array of STATIC_SCRATCH_BYTES on each GPU, for
+// the entry point that allocates nothing. Returns its device address on the current device (looked up once per
+// device with hipGetSymbolAddress), or null with *err set.
+#define STATIC_SCRATCH_BYTES ((size_t)256 + (size_t)16 * 8192 * 4)   // 16 argmax keys, then fragments of K <= 8192
+void* static_scratch(hipError_t* err);
+
 // DSpark Markov decode step k (KV-injection drafter): scores = z_k + w1[prev] w2, argmax -> tokens[k], confidence
 // sigmoid([block_k; w1[prev]] conf.w + conf.b) -> conf[k]; prev = anchor (k = 0) or tokens[k - 1].
 #define MARKOV_MAX_RANK 1024
@@ -298,3 +304,4 @@ hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStrea
 // (1, 2 or 4) partial slabs slab_stride floats apart (rscale: the taps' row scales, launch_taps_f16).
 hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, int nslab,
                           long long slab_stride, const float* rscale, hipStream_t st);
+

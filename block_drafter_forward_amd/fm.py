@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.fm_draft_block.restype = ctypes.c_int
         L.fm_lm_argmax.argtypes = [vp, vp, i32, vp, vp, vp]
         L.fm_lm_argmax.restype = ctypes.c_int
+        L.fm_lm_argmax_static.argtypes = [vp, vp, i32, vp, vp]
+        L.fm_lm_argmax_static.restype = ctypes.c_int
         L.fm_mtp_chain.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         L.fm_mtp_chain.restype = ctypes.c_int
         L.fm_markov_argmax.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp]
@@ -188,6 +190,9 @@ class Drafter:
     def fm_lm_argmax(self, hidden, rows: int, tokens, logits=None, stream=None):
         check(self.L.fm_lm_argmax(self.h, hidden.data_ptr(), rows, tokens.data_ptr(),
                                   logits.data_ptr() if logits is not None else None, _stream_ptr(stream)))
+
+    def fm_lm_argmax_static(self, hidden, rows: int, tokens, stream=None):
+        check(self.L.fm_lm_argmax_static(self.h, hidden.data_ptr(), rows, tokens.data_ptr(), _stream_ptr(stream)))
 
     def fm_mtp_chain(self, tokens, h, steps: int, pos: int, kv_lo: int, hidden_out, stream=None):
         check(self.L.fm_mtp_chain(self.h, tokens.data_ptr(), h.data_ptr(), steps, pos, kv_lo, hidden_out.data_ptr(),

@@ -172,6 +172,15 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits,
                        void* stream);
 
+/* fm_lm_argmax without the handle's workspace, for callers that cannot allocate device memory where they call it
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same product and
+ * argmax, the same tokens, with its scratch -- 16 argmax keys and the fragments of the rows -- in the library's own
+ * static device array (256 B + 16 x 8192 x 4 B on each GPU, held until the process ends). No allocation, no host
+ * synchronisation. Every call on one GPU shares that array: calls that overlap on one GPU (two streams, two host
+ * threads) race and must be serialised by the caller; each call clears the keys it needs first.
+ * Errors: FM_E_INVALID (rows < 1 or > 16, null hidden / tokens, target_dim > 8192), FM_E_HIP. */
+fm_status fm_lm_argmax_static(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, void* stream);
+
 /* Chained MTP depth (ternary_bonsai_2_mtp.js: the file header's "Depth N chains the head", MTPRunner's draft loop):
  * `steps` further single-row passes, pass i at position pos + i, each on the embedding row of the previous draft
  * token (tokens[i]: the row of the lm_head table, dequantised) and the previous pass's output h' (h for pass 0),
