@@ -14,7 +14,7 @@ ARCH = "gfx950"
 # Packed-FP32 instructions stay off (hipcc's host pass warns that it does not know the feature: harmless).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result"]
-SOURCES = ["k_skinny.hip", "k_rows.hip", "k_attn.hip", "k_lm.hip", "k_markov.hip", "k_prefill.hip", "fm_static.hip", "fm_api.cpp"]
+SOURCES = ["k_skinny.hip", "k_rows.hip", "k_attn.hip", "k_lm.hip", "k_markov.hip", "k_prefill.hip", "k_draft.hip", "fm_static.hip", "fm_api.cpp"]
 
 
 def build(verbose: bool = False) -> str:

@@ -79,11 +79,84 @@ int pick_split(int M_total, int K, bool q8 = false) {
     return any_enough > 0 ? any_enough : largest;
 }
 
+// ── the persistent draft kernel (k_draft.hip): which shapes it takes, its k-splits and its arena ─────
+// Flow-map drafters with 128-wide heads, 16 slots, widths multiples of 256 up to 2048 (fc1 / head / the anchor's
+// K and V take their whole k-range, at most 8 chunks of 256 per work-item).
+bool draft_supported(const fm_config& c) {
+    return c.variant == FM_VARIANT_FLOWMAP && c.head_dim == 128 && c.block == TMAX && c.dim % 256 == 0 &&
+           c.dim <= 2048 && c.dim == c.heads * 128 && c.ffn % 256 == 0 && c.target_dim % 256 == 0;
+}
+
+// k-split of a projection in the persistent kernel: the split that minimises the chunks of the busiest work-group
+// (items dealt round-robin over G), with at most 8 chunks (two per consumer wave) per item; ties to fewer slabs.
+int pick_dsplit(int K, int tiles, int G) {
+    const int nk = K / 256;
+    int best = -1, best_cost = 0;
+    for (int S = 1; S <= nk; ++S) {
+        if (nk % S || nk / S > 8) continue;
+        const int cost = ((tiles * S + G - 1) / G) * (nk / S);
+        if (best < 0 || cost < best_cost) { best = S; best_cost = cost; }
+    }
+    return best;
+}
+
+struct DraftLayout {
+    uint32_t a3, xpart, mfrag, ocs, xm, hm, u, f2s, x0, h0, qkv, sao, os, xs, hc, qcs;   // within a layer block
+    uint32_t layer_bytes, a1, xf, hf, total, xpart_cap;
+    int S_a1, S_qkv, S_o, S_qc, S_oc, S_f2;
+};
+
+DraftLayout draft_layout(const fm_config& c, int G) {
+    DraftLayout L{};
+    const int D = c.dim, tD = D / 16;
+    L.S_a1 = pick_dsplit(c.target_dim, tD, G);
+    L.S_qkv = pick_dsplit(D, 3 * tD, G);
+    L.S_o = L.S_qc = L.S_oc = pick_dsplit(D, tD, G);
+    L.S_f2 = pick_dsplit(c.ffn, tD, G);
+    // the most cross-attention runs per head any position up to the last draftable one needs
+    int cap = 4;
+    const int pmax = c.max_ctx - c.block - 1;
+    for (int pos = 0; pos <= pmax; pos += 32) {
+        int ns, cpw, xg;
+        draft_xsplit(pos, c.heads, G, ns, cpw, xg);
+        cap = std::max(cap, 4 * xg);
+        draft_xsplit(std::min(pos + 31, pmax), c.heads, G, ns, cpw, xg);
+        cap = std::max(cap, 4 * xg);
+    }
+    L.xpart_cap = (uint32_t)cap;
+    size_t off = 0;
+    auto take = [&](size_t b) { const size_t o = off; off = align256(off + b); return (uint32_t)o; };
+    const size_t rowf = (size_t)TMAX * D * 4, frag = (size_t)D * 64;
+    L.a3 = take((size_t)2 * D * 4);
+    L.xpart = take((size_t)c.heads * cap * TMAX * (c.head_dim + 2) * 4);
+    L.mfrag = take(frag);
+    L.ocs = take(L.S_oc * rowf);
+    L.xm = take(rowf);
+    L.hm = take(frag);
+    L.u = take((size_t)c.ffn * 64);
+    L.f2s = take(L.S_f2 * rowf);
+    L.x0 = take(rowf);
+    L.h0 = take(frag);
+    L.qkv = take(L.S_qkv * 3 * rowf);
+    L.sao = take(frag);
+    L.os = take(L.S_o * rowf);
+    L.xs = take(rowf);
+    L.hc = take(frag);
+    L.qcs = take(L.S_qc * rowf);
+    L.layer_bytes = (uint32_t)off;
+    off = (size_t)c.layers * L.layer_bytes;
+    L.a1 = take((size_t)L.S_a1 * D * 4);
+    L.xf = take(rowf);
+    L.hf = take(frag);
+    L.total = (uint32_t)off;
+    return L;
+}
+
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
         pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
-        rscale, modc, total;
+        rscale, modc, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
@@ -182,6 +255,13 @@ Plan make_plan(const fm_config& c) {
     // the handle's own modulation table (copied from the caller's at create, rewritten by time conditioning): the
     // layer-0 projections cached at create follow this table, so no other handle can change it under them
     p.modc = take(fmv ? (size_t)(3 * c.layers + 1) * 3 * c.dim * 4 : 0);
+    // the persistent draft kernel: its arguments and per-layer table (device copies), its barrier counters and its
+    // activation arena (sized for the most work-groups it may run with)
+    const bool pk = draft_supported(c);
+    p.dargs = take(pk ? sizeof(DraftArgs) : 0);
+    p.dlayers = take(pk ? (size_t)c.layers * sizeof(DraftLayer) : 0);
+    p.dsync = take(pk ? (size_t)DR_SYNC_WORDS * 4 : 0);
+    p.arena = take(pk ? draft_layout(c, DR_MAX_WG).total : 0);
     p.total = off;
     return p;
 }
@@ -247,6 +327,11 @@ struct fm_drafter {
     uint8_t* ws;
     uint8_t* kv;
     int length;
+    int draft_path = 0;       // 0 (automatic) and 1: one launch per phase, 2: the persistent kernel
+    bool draft_ready = false; // the persistent kernel is set up for this handle (shape supported, grid resident)
+    int G = 0;                // its work-groups
+    DraftArgs dh{};           // host copies of its device-resident arguments (the sources of their uploads)
+    DraftLayer dl[DR_MAX_LAYERS]{};
 
     template <class T> T* at(size_t off) const { return (T*)(ws + off); }
     const void* W(const std::string& n) const { auto it = w.find(n); return it == w.end() ? nullptr : it->second; }
@@ -835,6 +920,75 @@ fm_status flowmap_layer0(fm_drafter* d, hipStream_t st) {
     return FM_OK;
 }
 
+// Arguments of the persistent draft kernel, uploaded once: weights, cache rows, the handle's buffers and the arena
+// layout for this device's work-group count. Leaves draft_ready false (the launches path serves the handle) when
+// one work-group per CU does not fit.
+fm_status draft_setup(fm_drafter* d, hipStream_t st) {
+    const auto& c = d->c;
+    if (!draft_supported(c)) return FM_OK;
+    int dev = 0, ncu = 0;
+    HIPCHK(hipGetDevice(&dev));
+    HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    if (draft_occupancy() < 1 || ncu < 1) return FM_OK;
+    d->G = std::min(ncu, DR_MAX_WG);
+    const DraftLayout lay = draft_layout(c, d->G);
+    const DraftLayout cap = draft_layout(c, DR_MAX_WG);   // the arena was sized with this one
+    if (lay.total > cap.total) return FM_OK;
+    const int D = c.dim;
+    for (int l = 0; l < c.layers; ++l) {
+        DraftLayer& L = d->dl[l];
+        auto w = [&](const char* n) { return d->B(LW(l, n)); };
+        L.wq = w("self_attn.q_proj.weight"); L.wk = w("self_attn.k_proj.weight"); L.wv = w("self_attn.v_proj.weight");
+        L.wo = w("self_attn.o_proj.weight"); L.qn = w("self_attn.q_norm.weight"); L.kn = w("self_attn.k_norm.weight");
+        L.wqc = w("cross_attn.q_proj.weight"); L.woc = w("cross_attn.o_proj.weight");
+        L.cqn = w("cross_attn.q_norm.weight"); L.ckn = w("cross_attn.k_norm.weight");
+        L.wck = w("cross_attn.k_proj.weight"); L.wcv = w("cross_attn.v_proj.weight");
+        L.w1 = w("mlp.fc1.weight"); L.b1 = w("mlp.fc1.bias"); L.w2 = w("mlp.fc2.weight"); L.b2 = w("mlp.fc2.bias");
+        L.kc = (uint16_t*)d->kv_layer(l, 0);
+        L.vc = (uint16_t*)d->kv_layer(l, 1);
+        const uint32_t b = (uint32_t)l * lay.layer_bytes;
+        L.a3 = b + lay.a3; L.xpart = b + lay.xpart; L.mfrag = b + lay.mfrag; L.ocs = b + lay.ocs; L.xm = b + lay.xm;
+        L.hm = b + lay.hm; L.u = b + lay.u; L.f2s = b + lay.f2s; L.x0 = b + lay.x0; L.h0 = b + lay.h0;
+        L.qkv = b + lay.qkv; L.sao = b + lay.sao; L.os = b + lay.os; L.xs = b + lay.xs; L.hc = b + lay.hc;
+        L.qcs = b + lay.qcs;
+    }
+    DraftArgs& a = d->dh;
+    a.L = d->at<DraftLayer>(d->p.dlayers);
+    a.layers = c.layers; a.D = D; a.H = c.heads; a.hd = c.head_dim; a.F = c.ffn; a.Ht = c.target_dim; a.V = c.vocab;
+    a.mod = d->at<float>(d->p.modc);
+    a.rope = d->at<float>(d->p.rope);
+    a.wap = d->B("anchor_proj.weight"); a.bap = d->B("anchor_proj.bias"); a.anorm = d->B("anchor_norm.weight");
+    a.E = d->B("lm_head.weight"); a.whead = d->B("head.weight"); a.bhead = d->B("head.bias");
+    a.q0c = d->at<float>(d->p.q0c);
+    a.q0c_slabs = pick_qsplit(D);
+    a.q0c_stride = (long long)TMAX * D;
+    a.x1 = d->at<float>(d->p.x1);
+    a.ln_eps = c.ln_eps; a.rms_eps = c.rms_eps; a.qk_eps = c.qk_eps; a.scale = 1.f / sqrtf((float)c.head_dim);
+    a.arena = d->at<uint8_t>(d->p.arena);
+    a.a1 = lay.a1; a.xf = lay.xf; a.hf = lay.hf; a.xpart_cap = lay.xpart_cap;
+    a.S_a1 = lay.S_a1; a.S_qkv = lay.S_qkv; a.S_o = lay.S_o; a.S_qc = lay.S_qc; a.S_oc = lay.S_oc; a.S_f2 = lay.S_f2;
+    a.sync = d->at<uint32_t>(d->p.dsync);
+    a.limit = 20000000;   // 0.2 s at the 100 MHz real-time clock: far beyond any draft; only a broken launch reaches it
+    a.G = d->G;
+    HIPCHK(hipMemcpyAsync(d->at<uint8_t>(d->p.dlayers), d->dl, (size_t)c.layers * sizeof(DraftLayer),
+                          hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(d->at<uint8_t>(d->p.dargs), &d->dh, sizeof(DraftArgs), hipMemcpyHostToDevice, st));
+    HIPCHK(launch_fill_u32(a.sync, DR_SYNC_WORDS, 0u, st));
+    d->draft_ready = true;
+    return FM_OK;
+}
+
+// The draft as one persistent kernel: clear its arrival counters (a fill kernel, so the pair can be captured in a
+// graph), then one launch.
+fm_status flowmap_draft_persistent(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    int ns, cpw, xg;
+    draft_xsplit(ba->pos, d->c.heads, d->G, ns, cpw, xg);
+    if ((uint32_t)(4 * xg) > d->dh.xpart_cap) return fail(FM_E_INVALID, "cross-attention runs exceed the arena");
+    HIPCHK(launch_fill_u32(d->dh.sync, 8 * 64, 0u, st));
+    HIPCHK(launch_draft(d->at<DraftArgs>(d->p.dargs), d->G, ba->pos, ba->anchor, hidden_out, ba->debug_layers, st));
+    return FM_OK;
+}
+
 fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int Ht = c.target_dim, D = c.dim;
@@ -853,7 +1007,8 @@ fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     CHK(skinny(d, {{d->W("x_embed.weight"), nullptr, nullptr, nullptr, d->B("x_embed.bias"), d->at<uint8_t>(d->p.fragA),
                     d->at<float>(d->p.h0), D, D}},
                Ht, 1, SK_F32, 0, nullptr, st));
-    return flowmap_layer0(d, st);
+    CHK(flowmap_layer0(d, st));
+    return draft_setup(d, st);
 }
 
 // ── KV-injection ────────────────────────────────────────────────────────────────────────────────
@@ -1296,6 +1451,7 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
         if (!a->anchor) return fail(FM_E_INVALID, "null anchor");
         if (a->pos < 0 || a->pos > d->length) return fail(FM_E_INVALID, "pos %d outside [0, length %d]", a->pos, d->length);
         if ((long long)a->pos + c.block + 1 > c.max_ctx) return fail(FM_E_CONTEXT_FULL, "pos %d + block + 1 > max_ctx", a->pos);
+        if (d->draft_ready && d->draft_path == 2) return flowmap_draft_persistent(d, a, hidden_out, st);
         return flowmap_draft(d, a, hidden_out, st);
     }
     if (c.variant == FM_VARIANT_KVINJECT) {
@@ -1537,6 +1693,37 @@ fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* 
     }
     if (rows_total > TMAX) return fail(FM_E_INVALID, "%d rows in all > %d", rows_total, TMAX);
     return mtp_draft_batch(ds, B, as, hidden_out, st);
+}
+
+fm_status fm_set_draft_path(fm_drafter* d, int32_t path) {
+    g_err.clear();
+    if (!d) return fail(FM_E_INVALID, "null handle");
+    if (path < 0 || path > 2) return fail(FM_E_INVALID, "draft path %d (0 auto, 1 launches, 2 persistent)", path);
+    if (path == 2 && !d->draft_ready)
+        return fail(FM_E_UNSUPPORTED, "no persistent draft kernel for this drafter (shape or device)");
+    d->draft_path = path;
+    return FM_OK;
+}
+
+int32_t fm_draft_path(const fm_drafter* d) {
+    if (!d) return -1;
+    return (d->draft_ready && d->draft_path == 2) ? 2 : 1;
+}
+
+fm_status fm_device_status(fm_drafter* d, void* stream) {
+    g_err.clear();
+    if (!d) return fail(FM_E_INVALID, "null handle");
+    if (!d->draft_ready) return FM_OK;
+    HIPCHK(hipStreamSynchronize((hipStream_t)stream));
+    uint32_t e = 0;
+    uint32_t* w = d->dh.sync + 8 * 64;
+    HIPCHK(hipMemcpy(&e, w, 4, hipMemcpyDeviceToHost));
+    if (e) {
+        const uint32_t z = 0;
+        HIPCHK(hipMemcpy(w, &z, 4, hipMemcpyHostToDevice));
+        return fail(FM_E_DEVICE, "a persistent draft launch gave up waiting (its results are not valid)");
+    }
+    return FM_OK;
 }
 
 int32_t fm_context_length(const fm_drafter* d) { return d ? d->length : -1; }

@@ -305,3 +305,57 @@ hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStrea
 hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float eps, uint16_t* out, int nslab,
                           long long slab_stride, const float* rscale, hipStream_t st);
 
+// ── K8: the flow-map draft block as one persistent kernel ──────────────────────────────────────
+// One work-group per CU (DR_WAVES consumer waves + one producer wave). The producer streams every weight tile and the
+// context K/V of the cross-attention through an LDS ring, running ahead of the consumers across phase boundaries;
+// the consumers run the phases in order (anchor slot, the DiT layers, the head), exchanging activations through a
+// write-once arena with device-coherent (sc1) stores and loads and per-XCD arrival counters between phases.
+#define DR_MAX_LAYERS 16
+#define DR_RING 16              // 8 KB ring slots
+#define DR_CHUNK 8192
+#define DR_WAVES 4              // consumer waves
+#define DR_SCRATCH 27136        // consumer scratch bytes (the largest phase's)
+#define DR_LDS (DR_RING * DR_CHUNK + 256 + DR_SCRATCH)
+#define DR_MAX_WG 256
+#define DR_SYNC_WORDS (8 * 64 + 64)   // 8 arrival counters 64 words apart, then the error word
+struct DraftLayer {
+    const uint16_t *wq, *wk, *wv, *wo, *qn, *kn;      // self-attention: projections [D][D], head norms [hd]
+    const uint16_t *wqc, *woc, *cqn, *ckn, *wck, *wcv; // cross-attention: q / o projections, q / k head norms, k / v
+    const uint16_t *w1, *b1, *w2, *b2;                 // MLP: fc1 [F][D] + bias, fc2 [D][F] + bias
+    uint16_t* kc;                                      // f16 K cache [max_ctx][D]
+    uint16_t* vc;                                      // f16 V cache, tiled [max_ctx / 32][D][32]
+    // arena byte offsets of this layer's activations (each written once per launch)
+    uint32_t a3, xpart, mfrag, ocs, xm, hm, u, f2s, x0, h0, qkv, sao, os, xs, hc, qcs;
+};
+struct DraftArgs {             // per handle, in device memory (written at create)
+    const DraftLayer* L;       // device [layers]: the per-layer table
+    int layers, D, H, hd, F, Ht, V;
+    const float* mod;          // the handle's modulation table [(3 layers + 1)][scale D | shift D | gate D]
+    const float* rope;         // [pos][cos hd/2 | sin hd/2]
+    const uint16_t *wap, *bap, *anorm, *E, *whead, *bhead;
+    const float* q0c;          // layer 0's cross-attention q (create time): q0c_slabs slabs q0c_stride floats apart
+    int q0c_slabs;
+    long long q0c_stride;
+    const float* x1;           // layer 0's residual after its self-attention (create time), [16][D]
+    float ln_eps, rms_eps, qk_eps, scale;
+    uint8_t* arena;
+    uint32_t a1, xf, hf;       // arena offsets: anchor_proj slabs, final residual, final LN-mod fragments
+    uint32_t xpart_cap;        // cross-attention partial runs the arena holds per head
+    int S_a1, S_qkv, S_o, S_qc, S_oc, S_f2;   // k-splits of the projections
+    uint32_t* sync;            // DR_SYNC_WORDS: arrival counters (zero at launch), then the error word
+    long long limit;           // wall-clock ticks (100 MHz) any wait may take before the launch gives up
+    int G;                     // work-groups
+};
+// Split of the cross-attention over the context keys [0, pos) (nsteps 32-key steps): runs of cpw steps, four runs
+// per work-group, xgroups work-groups per head, so that heads x xgroups fills about one work-group per CU.
+__host__ __device__ inline void draft_xsplit(int pos, int H, int G, int& nsteps, int& cpw, int& xgroups) {
+    nsteps = (pos + 31) / 32;
+    cpw = (nsteps * H + 4 * G - 1) / (4 * G);
+    if (cpw < 1) cpw = 1;
+    xgroups = (nsteps + 4 * cpw - 1) / (4 * cpw);
+}
+// Work-groups of the persistent draft kernel one CU holds at once (0: it does not fit).
+int draft_occupancy();
+// args: device copy of the handle's DraftArgs; pos the anchor's position (cross-attention over [0, pos]).
+hipError_t launch_draft(const DraftArgs* args, int G, int pos, const int32_t* anchor, float* hidden_out, float* debug,
+                        hipStream_t st);

@@ -14,9 +14,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfm.so")
 
-FM_OK, FM_E_INVALID, FM_E_CONTEXT_FULL, FM_E_HIP, FM_E_UNSUPPORTED, FM_E_MISSING_WEIGHT = range(6)
+FM_OK, FM_E_INVALID, FM_E_CONTEXT_FULL, FM_E_HIP, FM_E_UNSUPPORTED, FM_E_MISSING_WEIGHT, FM_E_DEVICE = range(7)
 STATUS_NAMES = {0: "FM_OK", 1: "FM_E_INVALID", 2: "FM_E_CONTEXT_FULL", 3: "FM_E_HIP", 4: "FM_E_UNSUPPORTED",
-                5: "FM_E_MISSING_WEIGHT"}
+                5: "FM_E_MISSING_WEIGHT", 6: "FM_E_DEVICE"}
+DRAFT_PATH = {"auto": 0, "launches": 1, "persistent": 2}
 VARIANT = {"flowmap": 0, "kvinject": 1, "mtp": 2}
 ROPE = {"none": 0, "interleaved": 1, "neox": 2}
 MLP = {"gelu_erf": 0, "geglu_tanh": 1, "swiglu": 2}
@@ -80,6 +81,12 @@ def lib() -> ctypes.CDLL:
         L.fm_time_condition.restype = ctypes.c_int
         L.fm_draft_batch.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(FmBlockArgs), vp, vp]
         L.fm_draft_batch.restype = ctypes.c_int
+        L.fm_set_draft_path.argtypes = [vp, i32]
+        L.fm_set_draft_path.restype = ctypes.c_int
+        L.fm_draft_path.argtypes = [vp]
+        L.fm_draft_path.restype = i32
+        L.fm_device_status.argtypes = [vp, vp]
+        L.fm_device_status.restype = ctypes.c_int
         L.fm_context_length.argtypes = [vp]
         L.fm_context_length.restype = i32
         L.fm_destroy.argtypes = [vp]
@@ -175,6 +182,16 @@ class Drafter:
     @property
     def length(self) -> int:
         return self.L.fm_context_length(self.h)
+
+    def set_draft_path(self, path: str):
+        check(self.L.fm_set_draft_path(self.h, DRAFT_PATH[path]))
+
+    @property
+    def draft_path(self) -> str:
+        return {1: "launches", 2: "persistent"}.get(self.L.fm_draft_path(self.h), "?")
+
+    def device_status(self, stream=None):
+        check(self.L.fm_device_status(self.h, _stream_ptr(stream)))
 
     def fm_context_append(self, taps, start: int, stream=None):
         check(self.L.fm_context_append(self.h, taps.data_ptr(), taps.shape[0], start, _stream_ptr(stream)))

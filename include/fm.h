@@ -42,7 +42,8 @@ typedef enum fm_status {
     FM_E_CONTEXT_FULL = 2,   /* the append (or draft) would run past max_ctx */
     FM_E_HIP = 3,            /* a HIP runtime call failed (message holds hipGetErrorString) */
     FM_E_UNSUPPORTED = 4,    /* a config combination this build does not implement */
-    FM_E_MISSING_WEIGHT = 5  /* a weight the variant needs is not in the name table */
+    FM_E_MISSING_WEIGHT = 5, /* a weight the variant needs is not in the name table */
+    FM_E_DEVICE = 6          /* reported by fm_device_status: a persistent draft launch gave up waiting */
 } fm_status;
 
 enum fm_variant { FM_VARIANT_FLOWMAP = 0, FM_VARIANT_KVINJECT = 1, FM_VARIANT_MTP = 2 };
@@ -237,6 +238,28 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
  * tensors, a handle twice, a request's own fm_draft_block errors), FM_E_CONTEXT_FULL (an MTP request past its
  * cache), FM_E_UNSUPPORTED (flow-map handles: a block alone is 16 rows). */
 fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out, void* stream);
+
+/* How fm_draft_block runs a flow-map draft. The draft is one forward pass either way (the same arithmetic, results
+ * within rounding); this only chooses how its phases are scheduled on the GPU:
+ *   0  automatic (the default): one launch per phase, the faster of the two on MI355X at every shape the persistent
+ *      kernel takes (its phases are latency-bound, and a launch spreads each over more work-groups)
+ *   1  one launch per phase
+ *   2  the persistent kernel: every phase of the draft in one launch, one work-group per CU, weights and context K/V
+ *      streamed ahead of the arithmetic into LDS, activations passed between work-groups through device-coherent
+ *      memory with grid barriers between phases; it applies to 128-wide heads, 16 slots and widths that are
+ *      multiples of 256 up to 2048 with one work-group per CU resident (FM_E_UNSUPPORTED elsewhere)
+ * The persistent kernel needs its whole grid resident: a caller that runs other work on the GPU at the same time may
+ * delay it (each of its waits gives up after 0.2 s, leaving the draft's outputs invalid; fm_device_status reports
+ * it). Errors: FM_E_INVALID (null handle, path outside [0, 2]), FM_E_UNSUPPORTED. */
+fm_status fm_set_draft_path(fm_drafter* d, int32_t path);
+
+/* The path fm_draft_block takes now: 1 (one launch per phase) or 2 (persistent); -1 for a null handle. */
+int32_t fm_draft_path(const fm_drafter* d);
+
+/* Synchronises `stream` (the one call that does) and reports whether a persistent draft launch on this handle gave up
+ * waiting since the last check (FM_E_DEVICE; the flag is then cleared). FM_OK for handles without the persistent
+ * kernel. For tests and diagnostics. */
+fm_status fm_device_status(fm_drafter* d, void* stream);
 
 /* Current context length (rows appended and not rewound), or -1 for a null handle. */
 int32_t fm_context_length(const fm_drafter* d);

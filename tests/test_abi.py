@@ -85,6 +85,9 @@ def test_later_entry_points_reject_bad_arguments_on_the_host():
     assert L.fm_markov_argmax(None, 0x1000, 5, 0x2000, 256, 0x3000, 0x4000, None, None) == fm.FM_E_INVALID
     assert L.fm_time_condition(None, 0.0, 1.0, 256, 256, 1000.0, None, None) == fm.FM_E_INVALID
     assert L.fm_lm_argmax_static(None, 0x1000, 5, 0x2000, None) == fm.FM_E_INVALID
+    assert L.fm_set_draft_path(None, 0) == fm.FM_E_INVALID
+    assert L.fm_draft_path(None) == -1
+    assert L.fm_device_status(None, None) == fm.FM_E_INVALID
     arr = (ctypes.c_void_p * 1)(None)
     args = (fm.FmBlockArgs * 1)()
     assert L.fm_draft_batch(arr, 1, args, 0x2000, None) == fm.FM_E_INVALID
