@@ -7,9 +7,10 @@ vocab 151936, random-init bf16 weights, synthetic f32 taps):
   * the same drafter's context prefill of 8192 rows (fm_context_append: fc 12800 -> 2048 on the matrix cores,
     RMSNorm, 12 K/V projections with head-norm + RoPE + f16 cache stores) is timed as a second line item.
 
-Prints one JSON line: draft blocks/s (value), the lm_head+argmax kernel against the HBM roofline (timed live with
-HIP events on the stream it runs on), the prefill against the bf16/f16 MFMA roofline, and the float64 oracle timed
-on the host cores on a bounded sample of the same draft step.
+Prints one JSON line: draft blocks/s (value); the skinny weight-streaming GEMM (K1, the step's largest kernel time)
+and the lm_head+argmax kernel against the HBM roofline, both timed live with HIP events on the stream they run on;
+the prefill against the bf16/f16 MFMA roofline; and the float64 oracle timed on the host cores on a bounded sample
+of the same draft step.
 """
 from __future__ import annotations
 
@@ -57,6 +58,24 @@ def draft_step_bytes(cfg, L: int) -> int:
     w += Ht * D + Ht + V * Ht                     # head (+bias), lm_head
     b = 2 * w + 4 * (3 * Lyr + 1) * 3 * D         # bf16 weights, f32 modulation table
     return b + 2 * Lyr * L * D * 2
+
+
+def skinny_step_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of the skinny GEMM launches (K1) of one flow-map draft: each launch's bf16 weights and
+    biases once, its activation rows once (hi/lo bf16 pairs: 4 bytes an element) and its f32 result once. The
+    launches: anchor_proj (1 row); the 12 cross K / V projections of the anchor row (one launch); layer 0 from its
+    cross o_proj (cross o_proj, fc1, fc2); every further layer's q | k | v, self o_proj, cross q_proj, cross o_proj,
+    fc1, fc2 (16 rows); the head."""
+    D, Ht, F, Lyr, T = cfg["dim"], cfg["target_dim"], cfg["ffn"], cfg["layers"], cfg["block"]
+
+    def g(M, K, rows, bias=0, groups=1):   # one launch: `groups` M x K matrices over the same rows
+        return groups * (2 * M * K + 2 * bias + 4 * rows * M) + 4 * rows * K
+    b = g(D, Ht, 1) + g(D, D, 1, groups=2 * Lyr)
+    mlp = g(F, D, T, bias=F) + g(D, F, T)
+    b += g(D, D, T) + mlp
+    b += (Lyr - 1) * (g(D, D, T, groups=3) + 3 * g(D, D, T) + mlp)
+    b += g(Ht, D, T, bias=Ht)
+    return b
 
 
 def weight_bytes(W, names) -> int:
@@ -343,8 +362,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline, lm_head and 8192-row prefill only")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for a rocprofv3 --pmc pass: set up, run fm_lm_argmax 5 times on the FlashMap and 5 times on "
-                         "the MTP head's Q8_0 table, and one elementwise kernel that reads 1 GiB and writes 1 GiB (the "
-                         "counters' scale reference), then exit")
+                         "the MTP head's Q8_0 table, 3 FlashMap draft steps, one 8192-row context prefill, and one "
+                         "elementwise kernel that reads 1 GiB and writes 1 GiB (the counters' scale reference), then "
+                         "exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -385,13 +405,20 @@ def main():
         tm = torch.empty(8, dtype=torch.int32, device="cuda")
         for _ in range(5):
             dm.fm_lm_argmax(hm, 8, tm)
+        # three draft steps (the skinny GEMM launches) and one 8192-row context prefill (the MFMA GEMMs)
+        for _ in range(3):
+            step()
+        dlp = fm.Drafter(lcfg, dw)
+        dlp.fm_context_append(torch.from_numpy(gen.taps(lcfg, "prefill", lcfg["ctx_rows"])).cuda(), 0)
+        torch.cuda.synchronize()
+        del dlp
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         src.fill_(1.0)
         dst = torch.empty_like(src)
         torch.mul(src, 2.0, out=dst)   # one elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-        print("[bench] pmc probe done: 5 x fm_lm_argmax (bf16), 5 x fm_lm_argmax (Q8_0), one 1 GiB elementwise pass",
-              file=sys.stderr, flush=True)
+        print("[bench] pmc probe done: 5 x fm_lm_argmax (bf16), 5 x fm_lm_argmax (Q8_0), 3 draft steps, one 8192-row "
+              "prefill, one 1 GiB elementwise pass", file=sys.stderr, flush=True)
         return
 
     stream = torch.cuda.current_stream()
@@ -425,7 +452,15 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] draft step {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
-    # dominant kernel: the lm_head GEMM fused with the argmax, timed alone with events on its stream
+    # dominant kernel by step time: the skinny weight-streaming GEMM (K1); a draft's K1 launches replayed alone,
+    # back to back, between HIP events on the stream they run on (fm_profile_draft, 8 passes); median of 5 calls
+    prof = sorted((d.profile_draft(hidden, anchor, n, 8) for _ in range(5)), key=lambda r: r[0])
+    k1_us, k1_n, k1_draft_us = prof[len(prof) // 2]
+    k1_bytes = skinny_step_bytes(cfg)
+    k1_gbs = k1_bytes / (k1_us * 1e-6) / 1e9
+    k1_traffic = traffic_record("k_skinny.hip", "skinny_flashmap_traffic.json")
+
+    # second kernel: the lm_head GEMM fused with the argmax, timed alone with events on its stream
     lm_reps = max(20, args.steps // 2)
     for _ in range(3):
         d.fm_lm_argmax(hidden, T, tokens)
@@ -467,10 +502,17 @@ def main():
                    "graph": graph is not None, "step_hbm_bytes": step_bytes,
                    "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
                    "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"kernel": "lm_argmax (lm_head GEMM + fused argmax, V=151936 x 2560 bf16, 16 rows)",
-                     "bound": "hbm", "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": lm_gbs / HBM_PEAK_GBS, "traffic": traffic, "us_per_launch": lm_us,
-                     "algorithmic_bytes_per_launch": lm_bytes},
+        "roofline": {"kernel": f"skinny_kernel (K1: the draft's {k1_n} weight-streaming GEMM launches, bf16 "
+                               "weights, 1 or 16 activation rows)",
+                     "bound": "hbm", "achieved": k1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": k1_gbs / HBM_PEAK_GBS, "traffic": k1_traffic, "launches_per_step": k1_n,
+                     "us_per_step": k1_us, "us_per_launch": k1_us / k1_n,
+                     "algorithmic_bytes_per_step": k1_bytes, "algorithmic_bytes_per_launch": k1_bytes / k1_n,
+                     "draft_us_profiled": k1_draft_us},
+        "roofline_lm_head": {"kernel": "lm_argmax (lm_head GEMM + fused argmax, V=151936 x 2560 bf16, 16 rows)",
+                             "bound": "hbm", "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": lm_gbs / HBM_PEAK_GBS, "traffic": traffic, "us_per_launch": lm_us,
+                             "algorithmic_bytes_per_launch": lm_bytes},
         "prefill": {"value": P / (pf_ms * 1e-3), "unit": "tokens/s", "rows": P, "ms": pf_ms,
                     "roofline": {"bound": "mfma", "achieved": pf_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": pf_tflops / MFMA_F16_PEAK_TFLOPS, "flop": pf_flop,

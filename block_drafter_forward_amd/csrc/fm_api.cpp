@@ -332,6 +332,13 @@ struct fm_drafter {
     int G = 0;                // its work-groups
     DraftArgs dh{};           // host copies of its device-resident arguments (the sources of their uploads)
     DraftLayer dl[DR_MAX_LAYERS]{};
+    // fm_profile_draft: while `rec` is set, every skinny launch's arguments are appended to it (and launched)
+    std::vector<std::pair<SkinnyArgs, int>>* rec = nullptr;
+    hipEvent_t ev[4] = {};
+    ~fm_drafter() {
+        for (hipEvent_t e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
 
     template <class T> T* at(size_t off) const { return (T*)(ws + off); }
     const void* W(const std::string& n) const { auto it = w.find(n); return it == w.end() ? nullptr : it->second; }
@@ -438,6 +445,7 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         if ((size_t)S * a.part_stride > cap) return fail(FM_E_INVALID, "skinny: partial buffer too small");
     }
     if (S_out) *S_out = S;
+    if (d->rec) d->rec->push_back({a, begin});
     HIPCHK(launch_skinny(a, d->c.wtype == FM_W_Q8_0 ? SKW_Q8_0 : SKW_BF16, begin, st));
     return FM_OK;
 }
@@ -1723,6 +1731,47 @@ fm_status fm_device_status(fm_drafter* d, void* stream) {
         HIPCHK(hipMemcpy(w, &z, 4, hipMemcpyHostToDevice));
         return fail(FM_E_DEVICE, "a persistent draft launch gave up waiting (its results are not valid)");
     }
+    return FM_OK;
+}
+
+fm_status fm_profile_draft(fm_drafter* d, const fm_block_args* a, float* hidden_out, int32_t reps, float* skinny_us,
+                           int32_t* skinny_launches, float* draft_us, void* stream) {
+    g_err.clear();
+    if (!d || !a || !hidden_out || !skinny_us || !skinny_launches || !draft_us)
+        return fail(FM_E_INVALID, "null argument");
+    if (d->c.variant != FM_VARIANT_FLOWMAP) return fail(FM_E_UNSUPPORTED, "profile: flow-map drafters only");
+    if (a->pos < 0 || a->pos + 1 > d->c.max_ctx) return fail(FM_E_INVALID, "pos %d outside the cache", a->pos);
+    if (!a->anchor) return fail(FM_E_INVALID, "null anchor");
+    if (reps < 1 || reps > 64) return fail(FM_E_INVALID, "reps %d outside [1, 64]", reps);
+    hipStream_t st = (hipStream_t)stream;
+    for (hipEvent_t& e : d->ev)
+        if (!e) HIPCHK(hipEventCreate(&e));
+    const int wt = d->c.wtype == FM_W_Q8_0 ? SKW_Q8_0 : SKW_BF16;
+    // 1. one draft, recording its skinny launches
+    std::vector<std::pair<SkinnyArgs, int>> rec;
+    d->rec = &rec;
+    const fm_status s = flowmap_draft(d, a, hidden_out, st);
+    d->rec = nullptr;
+    if (s != FM_OK) return s;
+    // 2. the recorded skinny launches alone, `reps` times over, between two events; a hold kernel ahead of them
+    // keeps the GPU busy while the host queues them, so they run back to back as in a draft
+    HIPCHK(launch_hold(200000, st));   // 2 ms
+    HIPCHK(hipEventRecord(d->ev[0], st));
+    for (int r = 0; r < reps; ++r)
+        for (const auto& l : rec) HIPCHK(launch_skinny(l.first, wt, l.second, st));
+    HIPCHK(hipEventRecord(d->ev[1], st));
+    // 3. the whole draft once more, the same way (its outputs are the call's outputs)
+    HIPCHK(launch_hold(200000, st));
+    HIPCHK(hipEventRecord(d->ev[2], st));
+    CHK(flowmap_draft(d, a, hidden_out, st));
+    HIPCHK(hipEventRecord(d->ev[3], st));
+    HIPCHK(hipStreamSynchronize(st));
+    float k1 = 0.f, tot = 0.f;
+    HIPCHK(hipEventElapsedTime(&k1, d->ev[0], d->ev[1]));
+    HIPCHK(hipEventElapsedTime(&tot, d->ev[2], d->ev[3]));
+    *skinny_us = k1 * 1e3f / (float)reps;
+    *skinny_launches = (int32_t)rec.size();
+    *draft_us = tot * 1e3f;
     return FM_OK;
 }
 

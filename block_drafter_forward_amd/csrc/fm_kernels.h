@@ -114,6 +114,8 @@ hipError_t launch_colmean(const uint16_t* E, int V, int H, float* scratch, int R
 hipError_t launch_rope_table(float* tab, int P, int r, double theta, hipStream_t st);
 // Fill n 32-bit words with v.
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
+// a one-wave kernel that returns after `ticks` of the 100 MHz wall clock
+hipError_t launch_hold(uint64_t ticks, hipStream_t st);
 
 // ── K4: attention ──────────────────────────────────────────────────────────────────────────────
 struct QPrep {             // how a work-group builds its query rows for one head

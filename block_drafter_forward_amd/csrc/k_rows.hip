@@ -331,6 +331,13 @@ __global__ void rope_table_kernel(float* tab, int P, int rdim, double theta) {
     tab[(size_t)p * rdim + half + i] = (float)sin(a);
 }
 
+// One wave that returns once `ticks` of the 100 MHz wall clock have passed since it started: queued ahead of a
+// sequence of launches, it keeps the GPU busy while the host enqueues them, so they later run back to back.
+__global__ void hold_kernel(uint64_t ticks) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = v;
@@ -505,6 +512,11 @@ hipError_t launch_colmean(const uint16_t* E, int V, int H, float* scratch, int R
 hipError_t launch_rope_table(float* tab, int P, int rdim, double theta, hipStream_t st) {
     const size_t n = (size_t)P * (rdim / 2);
     rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(tab, P, rdim, theta);
+    return hipGetLastError();
+}
+
+hipError_t launch_hold(uint64_t ticks, hipStream_t st) {
+    hold_kernel<<<1, 64, 0, st>>>(ticks);
     return hipGetLastError();
 }
 

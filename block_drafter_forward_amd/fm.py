@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.fm_draft_path.restype = i32
         L.fm_device_status.argtypes = [vp, vp]
         L.fm_device_status.restype = ctypes.c_int
+        L.fm_profile_draft.argtypes = [vp, vp, vp, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
+                                       ctypes.POINTER(ctypes.c_float), vp]
+        L.fm_profile_draft.restype = ctypes.c_int
         L.fm_context_length.argtypes = [vp]
         L.fm_context_length.restype = i32
         L.fm_destroy.argtypes = [vp]
@@ -203,6 +206,15 @@ class Drafter:
                         prev_hidden.data_ptr() if prev_hidden is not None else None,
                         debug_layers.data_ptr() if debug_layers is not None else None)
         check(self.L.fm_draft_block(self.h, ctypes.byref(a), hidden_out.data_ptr(), _stream_ptr(stream)))
+
+    def profile_draft(self, hidden_out, anchor, pos: int, reps: int = 8, stream=None):
+        """A flow-map draft's skinny GEMM launches timed alone and the draft timed whole, with HIP events:
+        (skinny_us per draft, skinny_launches, draft_us)."""
+        a = FmBlockArgs(anchor.data_ptr(), pos, 0, 0, None, None, None)
+        k1, n, tot = ctypes.c_float(), ctypes.c_int32(), ctypes.c_float()
+        check(self.L.fm_profile_draft(self.h, ctypes.byref(a), hidden_out.data_ptr(), reps, ctypes.byref(k1),
+                                      ctypes.byref(n), ctypes.byref(tot), _stream_ptr(stream)))
+        return k1.value, n.value, tot.value
 
     def fm_lm_argmax(self, hidden, rows: int, tokens, logits=None, stream=None):
         check(self.L.fm_lm_argmax(self.h, hidden.data_ptr(), rows, tokens.data_ptr(),

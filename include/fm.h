@@ -256,7 +256,18 @@ fm_status fm_set_draft_path(fm_drafter* d, int32_t path);
 /* The path fm_draft_block takes now: 1 (one launch per phase) or 2 (persistent); -1 for a null handle. */
 int32_t fm_draft_path(const fm_drafter* d);
 
-/* Synchronises `stream` (the one call that does) and reports whether a persistent draft launch on this handle gave up
+/* Diagnostics: the time of a flow-map draft's skinny weight-streaming GEMM launches (K1) and of the whole draft,
+ * with HIP events on `stream`. Runs the draft (one launch per phase) once while recording its K1 launches; then
+ * those launches alone, in order, `reps` times over between two events; then the draft once more between two events
+ * (its outputs and cache writes are those of fm_draft_block; hidden_out holds them on return). A 2 ms one-wave hold
+ * kernel goes ahead of each timed sequence so the host has queued it before the GPU reaches it. Synchronises
+ * `stream` and returns, on the host: *skinny_us, the time of one pass over the K1 launches (microseconds);
+ * *skinny_launches, their count; *draft_us, the timed draft. Errors: FM_E_INVALID (null pointer, pos outside the
+ * cache, null anchor, reps outside [1, 64]), FM_E_UNSUPPORTED (not a flow-map drafter). */
+fm_status fm_profile_draft(fm_drafter* d, const fm_block_args* a, float* hidden_out, int32_t reps, float* skinny_us,
+                           int32_t* skinny_launches, float* draft_us, void* stream);
+
+/* Synchronises `stream` and reports whether a persistent draft launch on this handle gave up
  * waiting since the last check (FM_E_DEVICE; the flag is then cleared). FM_OK for handles without the persistent
  * kernel. For tests and diagnostics. */
 fm_status fm_device_status(fm_drafter* d, void* stream);

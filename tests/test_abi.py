@@ -88,6 +88,9 @@ def test_later_entry_points_reject_bad_arguments_on_the_host():
     assert L.fm_set_draft_path(None, 0) == fm.FM_E_INVALID
     assert L.fm_draft_path(None) == -1
     assert L.fm_device_status(None, None) == fm.FM_E_INVALID
+    k1, n, tot = ctypes.c_float(), ctypes.c_int32(), ctypes.c_float()
+    assert L.fm_profile_draft(None, None, 0x1000, 4, ctypes.byref(k1), ctypes.byref(n), ctypes.byref(tot),
+                              None) == fm.FM_E_INVALID
     arr = (ctypes.c_void_p * 1)(None)
     args = (fm.FmBlockArgs * 1)()
     assert L.fm_draft_batch(arr, 1, args, 0x2000, None) == fm.FM_E_INVALID
