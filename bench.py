@@ -162,8 +162,27 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
                                          "appends/s")
     dl.fm_context_append(t16, P)   # leave the context at 8192 + 16 rows
 
-    # 512-row prefill on the FlashMap shape
+    # two FlowMap requests in one pass (fm_draft_batch, 32 rows): each over its own 512-row context, the lm_head
+    # argmax over both blocks' rows; the weights and the table stream once for both
     n = cfg["ctx_rows"]
+    d2 = fm.Drafter(cfg, d.weights)
+    d2.fm_context_append(torch.from_numpy(gen.taps(cfg, "bench-b2", n)).cuda(), 0)
+    an2 = torch.tensor([int(gen.anchors(cfg, "bench-b2", 1)[0])], dtype=torch.int32, device="cuda")
+    hid2 = torch.empty(2 * T, Ht, dtype=torch.float32, device="cuda")
+    tok2 = torch.empty(2 * T, dtype=torch.int32, device="cuda")
+
+    def b2step():
+        fm.Drafter.fm_draft_batch([d, d2], [{"anchor": an, "pos": n}, {"anchor": an2, "pos": n}], hid2)
+        d.fm_lm_argmax(hid2, 2 * T, tok2)
+    ms = _time_ms(torch, _graph_of(torch, b2step), 5, reps)
+    row = _hbm_row("two flow-map requests in one pass (fm_draft_batch B = 2, 32 rows, each over its own 512-row "
+                   "context) + lm_head argmax over the 32 rows", ms,
+                   draft_step_bytes(cfg, n + 1) + 2 * Lyr * (n + 1) * D * 2, "draft blocks/s")
+    row["value"] *= 2   # two blocks per pass
+    rows["flashmap_batch2"] = row
+    del d2
+
+    # 512-row prefill on the FlashMap shape
     tp = torch.from_numpy(gen.taps(cfg, "prefill", n)).cuda()
     ms = _time_ms(torch, lambda: d.fm_context_append(tp, 0), 2, 10)
     rows["flashmap_prefill_512"] = _mfma_row("512-row context prefill", ms, n,

@@ -38,6 +38,7 @@ fm_status fail(fm_status s, const char* fmt, ...) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int TMAX = 16;          // rows of one skinny activation matrix
+constexpr int FM_BATCH = 2;       // flow-map requests one batched draft takes (16 rows each)
 constexpr int QKV_SLABS = 4;      // split-K slabs the attention kernels sum while building q (and k, v)
 constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
 constexpr int PF_SPLIT_WGS = 512; // a k-split prefill launch stays within one round (two 128-tile work-groups per CU)
@@ -193,23 +194,25 @@ Plan make_plan(const fm_config& c) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     const int D = c.dim;
-    p.best = take(16 * sizeof(unsigned long long));
+    const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
+    const int RB = fmv ? FM_BATCH * TMAX : TMAX;   // rows of the block buffers (flow-map: two batched requests)
+    p.best = take((size_t)RB * sizeof(unsigned long long));
     p.zeros_bytes = (size_t)std::max({kmax_frag(c), 2 * c.dim, c.target_dim, 256}) * 4;
     p.zeros = take(p.zeros_bytes);
     p.rope_dims = c.rope == FM_ROPE_NEOX ? c.rope_dims : c.head_dim;
     p.rope_rows = c.max_ctx + c.block + 2;
     p.rope = take(c.rope == FM_ROPE_NONE ? 0 : (size_t)p.rope_rows * p.rope_dims * 4);
-    const size_t fragK = (size_t)kmax_frag(c) * 64;   // 2 KB per 32 k
+    const size_t fragK = (size_t)kmax_frag(c) * 64;   // 2 KB per 32 k, per block of 16 rows
     p.fragA = take(fragK);
-    p.fragH = take(fragK);
-    p.fragO = take(fragK);
-    p.fragU = take(fragK);
-    p.x = take((size_t)TMAX * D * 4);
-    p.part_floats = (size_t)TMAX * part_need(c);
+    p.fragH = take(fragK * (RB / TMAX));
+    p.fragO = take(fragK * (RB / TMAX));
+    p.fragU = take(fragK * (RB / TMAX));
+    p.x = take((size_t)RB * D * 4);
+    p.part_floats = (size_t)RB * part_need(c);
     p.part = take(p.part_floats * 4);
     int qkvw = 3 * D;
     if (c.variant == FM_VARIANT_MTP) qkvw = c.heads * 2 * c.head_dim + 2 * c.kv_heads * c.head_dim;
-    p.qkv_floats = (size_t)QKV_SLABS * TMAX * qkvw;
+    p.qkv_floats = (size_t)QKV_SLABS * RB * qkvw;
     p.qkv = take(p.qkv_floats * 4);
     const int Lmax = c.max_ctx + c.block + 1;
     p.nchunk_max = (Lmax + 15) / 16;
@@ -236,7 +239,6 @@ Plan make_plan(const fm_config& c) {
     p.rope_pf = take(c.variant == FM_VARIANT_FLOWMAP ? (size_t)p.rope_rows * p.rope_dims * 4 : 0);
     p.qout = take(c.variant == FM_VARIANT_MTP ? (size_t)TMAX * c.heads * c.head_dim * 4 : 0);
     // the flow-map anchor path's own buffers (its partials, the anchor row and the slot row as fragments)
-    const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
     p.apart = take(fmv ? p.part_floats * 4 : 0);
     p.afrag = take(fmv ? (size_t)c.target_dim * 64 : 0);
     p.cfrag = take(fmv ? (size_t)c.dim * 64 : 0);
@@ -334,6 +336,10 @@ struct fm_drafter {
     DraftLayer dl[DR_MAX_LAYERS]{};
     // fm_profile_draft: while `rec` is set, every skinny launch's arguments are appended to it (and launched)
     std::vector<std::pair<SkinnyArgs, int>>* rec = nullptr;
+    // the jump (s, t, time_dim, cond_dim, time_scale) the modulation table was last conditioned on (tc_set), else
+    // the table is the one given at create: handles with the same weights and the same key hold the same table
+    float tc_key[5] = {};
+    bool tc_set = false;
     hipEvent_t ev[4] = {};
     ~fm_drafter() {
         for (hipEvent_t e : ev)
@@ -414,8 +420,10 @@ struct SkGroupDesc {
 // runs with S = 1 (the whole k-range in one work-group).
 // Partial slabs go to the groups' own outputs; by default they are the shared partial buffer with slabs TMAX * M
 // apart (M of the first group). A caller writing elsewhere passes the slab stride and the capacity (floats) there.
+// nb = 2: two blocks of 16 activation rows (rows 16 b + t of the outputs; fragments of block b at X + b * K * 64),
+// each weight tile multiplied against both; the k-split then keeps k-steps per wave a multiple of 4.
 fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K, int T, int mode, int S_force,
-                 int* S_out, hipStream_t st, long long pstride = 0, size_t cap_floats = 0) {
+                 int* S_out, hipStream_t st, long long pstride = 0, size_t cap_floats = 0, int nb = 1) {
     if (gs.empty() || gs.size() > SK_MAX_GROUPS) return fail(FM_E_INVALID, "skinny: %zu groups", gs.size());
     if (K % 128) return fail(FM_E_INVALID, "skinny: K %d not a multiple of 128", K);
     SkinnyArgs a{};
@@ -424,6 +432,13 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     int S = 1;
     if (mode == SK_PARTIAL)
         S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K, d->c.wtype == FM_W_Q8_0);
+    if (nb == 2) {
+        if (T != 16 || d->c.wtype != FM_W_BF16) return fail(FM_E_UNSUPPORTED, "skinny: two row blocks need bf16, T 16");
+        while (S > 1 && ((K / 128) % S || (K / 128 / S) % 4)) --S;
+        if ((K / 128 / S) % 4) return fail(FM_E_UNSUPPORTED, "skinny: two row blocks need K %% 512 == 0 (K %d)", K);
+    } else if (nb != 1) {
+        return fail(FM_E_INVALID, "skinny: %d row blocks", nb);
+    }
     if (S < 1 || (K / 128) % S || !kw_ok(K / 128 / S))
         return fail(FM_E_UNSUPPORTED, "skinny: no supported k-split for K %d (S %d)", K, S);
     a.ngroups = (int)gs.size();
@@ -432,6 +447,7 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     a.S = S;
     a.KW = K / 128 / S;
     a.mode = mode;
+    a.nb = nb;
     int begin = 0;
     for (size_t i = 0; i < gs.size(); ++i) {
         const auto& g = gs[i];
@@ -440,7 +456,7 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         begin += (g.M / 16) * S;
     }
     if (mode == SK_PARTIAL) {
-        a.part_stride = pstride > 0 ? pstride : (long long)TMAX * gs[0].M;
+        a.part_stride = pstride > 0 ? pstride : (long long)TMAX * nb * gs[0].M;
         const size_t cap = cap_floats > 0 ? cap_floats : d->p.part_floats;
         if ((size_t)S * a.part_stride > cap) return fail(FM_E_INVALID, "skinny: partial buffer too small");
     }
@@ -602,8 +618,10 @@ std::string LW(int l, const char* s) {
     return b;
 }
 
-// c rows (fragments in fragH, T rows) -> every layer's K/V at rows start.. (skinny path, T <= 16)
-fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, const uint8_t* cfrag, hipStream_t st) {
+// c rows (fragments in fragH, T rows) -> every layer's K/V at rows start.. (skinny path, T <= 16). With `caches`
+// (batched drafts), row t goes to the cache of handle caches[t] at its row starts[t] instead.
+fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, const uint8_t* cfrag, hipStream_t st,
+                           fm_drafter* const* caches = nullptr, const int* starts = nullptr) {
     const auto& c = d->c;
     const int D = c.dim;
     std::vector<SkGroupDesc> gs;
@@ -635,7 +653,20 @@ fm_status fm_kv_rows_small(fm_drafter* d, int T, int start, const uint8_t* cfrag
     k.max_ctx = c.max_ctx;
     k.kv_dtype = c.kv_dtype;
     k.zeros = d->at<float>(d->p.zeros);
-    HIPCHK(launch_kv_final(k, st));
+    if (!caches) {
+        HIPCHK(launch_kv_final(k, st));
+        return FM_OK;
+    }
+    for (int t = 0; t < T; ++t) {   // one row into each request's own cache
+        KVFinalArgs kt = k;
+        kt.n = 1;
+        kt.stage_n = T;
+        kt.stage_t0 = t;
+        kt.start = starts[t];
+        kt.cache = caches[t]->kv;
+        kt.max_ctx = caches[t]->c.max_ctx;
+        HIPCHK(launch_kv_final(kt, st));
+    }
     return FM_OK;
 }
 
@@ -701,10 +732,18 @@ fm_status flowmap_append(fm_drafter* d, const float* taps, int n, int start, hip
     return FM_OK;
 }
 
-fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+// B (1 or 2) flow-map drafts in one pass: request b's anchor, position and context cache are handle ds[b]'s; its 16
+// slots are rows 16 b .. 16 b + 15 of the pass (of hidden_out too). Every projection streams its weights once for
+// all rows (two blocks of 16 activation rows against each weight tile); self-attention runs within each request's
+// rows, cross-attention over each request's own cache, and each anchor slot goes into its own request's cache. The
+// handles share the weights and the modulation table (checked by the caller), so the row kernels and layer 0's
+// cached rows serve every request.
+fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* const* bas, float* hidden_out,
+                              hipStream_t st) {
+    fm_drafter* d = ds[0];
     const auto& c = d->c;
     const int D = c.dim, T = c.block, Ht = c.target_dim, H = c.heads, hd = c.head_dim;
-    const int pos = ba->pos;
+    const int R = B * T;   // rows of the pass
     float* part = d->at<float>(d->p.part);
     float* x = d->at<float>(d->p.x);
     const float* mod = d->at<float>(d->p.modc);
@@ -713,36 +752,44 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
     uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
     float* qkv = d->at<float>(d->p.qkv);
     const float* rope = d->at<float>(d->p.rope);
-    const long long pstr = (long long)TMAX * D;
+    const long long pstr = (long long)TMAX * B * D;   // partial slab stride: the pass's rows
     const int Sq = pick_qsplit(D);
+    float* debug = B == 1 ? bas[0]->debug_layers : nullptr;
 
-    // anchor slot: anchor_norm(anchor_proj(E[anchor])) through every layer's k/v path at pos, on the caller's stream
-    // before layer 0. (Beside layer 0 on a second stream it was 37 us slower per step: its 1,536-work-group K/V
-    // projections took the CUs layer 0's latency-bound kernels needed, and the join cost another ~9 us.)
+    // anchor slots: anchor_norm(anchor_proj(E[anchor_b])) as row b, through every layer's k/v path into request b's
+    // cache at its pos, on the caller's stream before layer 0. (Beside layer 0 on a second stream it was 37 us slower
+    // per step: its 1,536-work-group K/V projections took the CUs layer 0's latency-bound kernels needed, and the
+    // join cost another ~9 us.)
     {
-        hipStream_t as = st;
         uint8_t* afrag = d->at<uint8_t>(d->p.afrag);
         uint8_t* cfrag = d->at<uint8_t>(d->p.cfrag);
         float* apart = d->at<float>(d->p.apart);
-        HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, ba->anchor, afrag, as));
+        for (int b = 0; b < B; ++b)
+            HIPCHK(launch_gather_frag(d->B("lm_head.weight"), c.vocab, Ht, bas[b]->anchor, afrag, st, b));
         int Sa = 0;
-        CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, afrag, apart, D, D}}, Ht, 1,
-                   SK_PARTIAL, 0, &Sa, as));
-        RowArgs r = rows_base(d, D, 1);
+        CHK(skinny(d, {{d->W("anchor_proj.weight"), nullptr, nullptr, nullptr, nullptr, afrag, apart, D, D}}, Ht, B,
+                   SK_PARTIAL, 0, &Sa, st));
+        RowArgs r = rows_base(d, D, B);
         r.part = apart;
         r.S = Sa;
-        r.part_stride = pstr;
+        r.part_stride = (long long)TMAX * D;
         r.bias = d->B("anchor_proj.bias");
         r.norm = ROW_RMS;
         r.w_bf16 = d->B("anchor_norm.weight");
         r.eps = c.rms_eps;
         r.frag_out = cfrag;
-        CHK(rows(r, as));
-        CHK(fm_kv_rows_small(d, 1, pos, cfrag, as));
+        CHK(rows(r, st));
+        if (B == 1) {
+            CHK(fm_kv_rows_small(d, 1, bas[0]->pos, cfrag, st));
+        } else {
+            int starts[FM_BATCH];
+            for (int b = 0; b < B; ++b) starts[b] = bas[b]->pos;
+            CHK(fm_kv_rows_small(d, B, 0, cfrag, st, ds, starts));
+        }
     }
     int S = 0;
-    const int L = pos + 1;
     int S_prev = 0;           // split count of the pending residual update (fc2 of the previous layer)
+    int Sqb = Sq;             // split count of the cross q of layers >= 1 (two row blocks may take fewer)
     for (int l = 0; l < c.layers; ++l) {
         const float* m_sa = mod + (size_t)(3 * l) * 3 * D;
         const float* m_ca = mod + (size_t)(3 * l + 1) * 3 * D;
@@ -750,14 +797,14 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         // residual (previous layer's MLP) + self-attention modulation, then q | k | v; layer 0's are the same for
         // every draft (flowmap_layer0)
         if (l > 0) {
-            RowArgs r = rows_base(d, D, T);
+            RowArgs r = rows_base(d, D, R);
             r.x = x;
             r.part = part;
             r.S = S_prev;
             r.part_stride = pstr;
             r.bias = d->B(LW(l - 1, "mlp.fc2.bias"));
             r.gate = mod + (size_t)(3 * (l - 1) + 2) * 3 * D + 2 * D;
-            if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)(l - 1) * T * D;
+            if (debug) r.debug_x = debug + (size_t)(l - 1) * T * D;
             r.norm = ROW_LN_MOD;
             r.scale = m_sa;
             r.shift = m_sa + D;
@@ -771,10 +818,7 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
                          3 * D},
                         {d->W(LW(l, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D,
                          D, 3 * D}},
-                       D, T, SK_F32, 0, nullptr, st));
-        }
-        // layer 0 from here to the cross-attention's q is the same for every draft (flowmap_layer0)
-        if (l > 0) {
+                       D, T, SK_F32, 0, nullptr, st, 0, 0, B));
             {
                 SelfAttnArgs a{};
                 a.qkv = qkv;
@@ -788,15 +832,17 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
                 a.kn = d->B(LW(l, "self_attn.k_norm.weight"));
                 a.eps = c.qk_eps;
                 a.rope_tab = rope;
-                a.pos_base = pos + 1;
+                a.pos_base = bas[0]->pos + 1;
+                a.pos_base1 = bas[B - 1]->pos + 1;
+                a.nb = B;
                 a.scale = 1.f / sqrtf((float)hd);
                 a.o_frag = fragO;
                 HIPCHK(launch_self_attn(a, st));
             }
             CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
-                       D, T, SK_PARTIAL, 0, &S, st));
+                       D, T, SK_PARTIAL, 0, &S, st, pstr, 0, B));
             {
-                RowArgs r = rows_base(d, D, T);
+                RowArgs r = rows_base(d, D, R);
                 r.x = x;
                 r.part = part;
                 r.S = S;
@@ -812,11 +858,11 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
             // cross-attention over cache rows [0, pos]: q = cross q_proj(h) (whole k-range per work-group), then
             // per-head q_norm + RoPE inside the attention kernel
             CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, D}},
-                       D, T, SK_PARTIAL, Sq, nullptr, st, (long long)TMAX * D, d->p.qkv_floats));
+                       D, T, SK_PARTIAL, Sq, &Sqb, st, (long long)TMAX * B * D, d->p.qkv_floats, B));
         }
-        {
+        for (int b = 0; b < B; ++b) {   // each request over its own cache rows [0, pos_b]
             QPrep qp{};
-            qp.q = l == 0 ? d->at<float>(d->p.q0c) : qkv;
+            qp.q = l == 0 ? d->at<float>(d->p.q0c) : qkv + (size_t)b * T * D;
             qp.q_ld = D;
             qp.q_hs = hd;
             qp.norm_bf16 = d->B(LW(l, "cross_attn.q_norm.weight"));
@@ -824,15 +870,16 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
             qp.rope = 1;
             qp.rope_dims = d->p.rope_dims;
             qp.rope_tab = rope;
-            qp.pos_base = pos + 1;
-            qp.parts = Sq;
-            qp.pstride = (long long)TMAX * D;
-            CHK(attend(d, qp, T, l, 0, L, nullptr, nullptr, 0, 0, -1, 1.f / sqrtf((float)hd), nullptr, 0, 0, fragO, st));
+            qp.pos_base = bas[b]->pos + 1;
+            qp.parts = l == 0 ? Sq : Sqb;
+            qp.pstride = l == 0 ? (long long)TMAX * D : (long long)TMAX * B * D;
+            CHK(attend(ds[b], qp, T, l, 0, bas[b]->pos + 1, nullptr, nullptr, 0, 0, -1, 1.f / sqrtf((float)hd), nullptr,
+                       0, 0, fragO, st, b * T));
         }
         CHK(skinny(d, {{d->W(LW(l, "cross_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
-                   D, T, SK_PARTIAL, 0, &S, st));
+                   D, T, SK_PARTIAL, 0, &S, st, pstr, 0, B));
         {
-            RowArgs r = rows_base(d, D, T);
+            RowArgs r = rows_base(d, D, R);
             r.x = x;
             if (l == 0) r.init = d->at<float>(d->p.x1);   // layer 0's residual after its self-attention (every row)
             r.part = part;
@@ -849,20 +896,20 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         // MLP: fc1 + exact GELU (fused), fc2 (its residual is applied by the next row kernel)
         CHK(skinny(d, {{d->W(LW(l, "mlp.fc1.weight")), nullptr, nullptr, nullptr, d->B(LW(l, "mlp.fc1.bias")), fragH,
                         fragU, c.ffn, 0}},
-                   D, T, SK_FRAG_GELU, 0, nullptr, st));
+                   D, T, SK_FRAG_GELU, 0, nullptr, st, 0, 0, B));
         CHK(skinny(d, {{d->W(LW(l, "mlp.fc2.weight")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
-                   SK_PARTIAL, 0, &S_prev, st));
+                   SK_PARTIAL, 0, &S_prev, st, pstr, 0, B));
     }
     {
         const float* m_f = mod + (size_t)(3 * c.layers) * 3 * D;
-        RowArgs r = rows_base(d, D, T);
+        RowArgs r = rows_base(d, D, R);
         r.x = x;
         r.part = part;
         r.S = S_prev;
         r.part_stride = pstr;
         r.bias = d->B(LW(c.layers - 1, "mlp.fc2.bias"));
         r.gate = mod + (size_t)(3 * (c.layers - 1) + 2) * 3 * D + 2 * D;
-        if (ba->debug_layers) r.debug_x = ba->debug_layers + (size_t)(c.layers - 1) * T * D;
+        if (debug) r.debug_x = debug + (size_t)(c.layers - 1) * T * D;
         r.norm = ROW_LN_MOD;
         r.scale = m_f;
         r.shift = m_f + D;
@@ -871,8 +918,14 @@ fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_ou
         CHK(rows(r, st));
     }
     CHK(skinny(d, {{d->W("head.weight"), nullptr, nullptr, nullptr, d->B("head.bias"), fragH, hidden_out, Ht, Ht}}, D, T,
-               SK_F32, 0, nullptr, st));
+               SK_F32, 0, nullptr, st, 0, 0, B));
     return FM_OK;
+}
+
+fm_status flowmap_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, hipStream_t st) {
+    fm_drafter* ds[1] = {d};
+    const fm_block_args* as[1] = {ba};
+    return flowmap_draft_batch(ds, 1, as, hidden_out, st);
 }
 
 // Layer 0 of a draft starts every slot from the same row h0 with the same modulation, so its LN-mod and its q / k /
@@ -1478,7 +1531,9 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits, void* stream) {
     g_err.clear();
     if (!d || !hidden || !tokens) return fail(FM_E_INVALID, "null argument");
-    if (rows < 1 || rows > TMAX) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, TMAX);
+    // flow-map handles (bf16 tables) take the rows of a two-request batch
+    const int rmax = d->c.variant == FM_VARIANT_FLOWMAP && d->c.wtype == FM_W_BF16 ? FM_BATCH * TMAX : TMAX;
+    if (rows < 1 || rows > rmax) return fail(FM_E_INVALID, "rows %d outside [1, %d]", rows, rmax);
     hipStream_t st = (hipStream_t)stream;
     const int K = d->c.target_dim;
     uint8_t* fr = d->at<uint8_t>(d->p.fragH);
@@ -1642,7 +1697,13 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     if (table_out)
         HIPCHK(hipMemcpyAsync(table_out, a.table, (size_t)nn * 3 * c.dim * 4, hipMemcpyDeviceToDevice,
                               (hipStream_t)stream));
-    return flowmap_layer0(d, (hipStream_t)stream);   // layer 0's projections follow the new table
+    const fm_status r = flowmap_layer0(d, (hipStream_t)stream);   // layer 0's projections follow the new table
+    if (r == FM_OK) {
+        const float key[5] = {s, t, (float)time_dim, (float)cond_dim, time_scale};
+        memcpy(d->tc_key, key, sizeof key);
+        d->tc_set = true;
+    }
+    return r;
 }
 
 fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out,
@@ -1653,7 +1714,8 @@ fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* 
     for (int b = 0; b < B; ++b)
         if (!ds[b]) return fail(FM_E_INVALID, "null handle %d", b);
     const auto& c = ds[0]->c;
-    if (c.variant == FM_VARIANT_FLOWMAP) return fail(FM_E_UNSUPPORTED, "batched drafts: KV-injection and MTP drafters");
+    if (c.variant == FM_VARIANT_FLOWMAP && B > FM_BATCH)
+        return fail(FM_E_UNSUPPORTED, "flow-map batches take at most %d requests", FM_BATCH);
     for (int b = 1; b < B; ++b) {
         const fm_drafter* e = ds[b];
         const auto& f = e->c;   // the shape of the block computation (max_ctx may differ: each cache is its own)
@@ -1675,6 +1737,24 @@ fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* 
             if (ds[a] == e) return fail(FM_E_INVALID, "handle %d appears twice", b);
     }
     hipStream_t st = (hipStream_t)stream;
+    if (c.variant == FM_VARIANT_FLOWMAP) {
+        if (B > 1 && (c.block != TMAX || c.wtype != FM_W_BF16 || c.dim % 512 || c.ffn % 512))
+            return fail(FM_E_UNSUPPORTED, "flow-map batches need 16-slot blocks, bf16 weights, dim and ffn %% 512 == 0");
+        const fm_block_args* as[FM_BATCH];
+        for (int b = 0; b < B; ++b) {
+            const fm_block_args* a = &args[b];
+            const fm_drafter* e = ds[b];
+            if (!a->anchor) return fail(FM_E_INVALID, "request %d: null anchor", b);
+            if (a->pos < 0 || a->pos > e->length)
+                return fail(FM_E_INVALID, "request %d: pos %d outside [0, length %d]", b, a->pos, e->length);
+            if ((long long)a->pos + c.block + 1 > e->c.max_ctx)
+                return fail(FM_E_CONTEXT_FULL, "request %d: pos %d + block + 1 > max_ctx", b, a->pos);
+            if (e->tc_set != ds[0]->tc_set || (e->tc_set && memcmp(e->tc_key, ds[0]->tc_key, sizeof e->tc_key)))
+                return fail(FM_E_INVALID, "handle %d: another modulation table (time conditioning)", b);
+            as[b] = a;
+        }
+        return flowmap_draft_batch(ds, B, as, hidden_out, st);
+    }
     if (c.variant == FM_VARIANT_KVINJECT) {
         if (B * c.block > TMAX) return fail(FM_E_INVALID, "B %d x block %d > %d rows", B, c.block, TMAX);
         const int32_t* an[TMAX];

@@ -61,6 +61,12 @@ __device__ __forceinline__ void frag_store8(uint8_t* frag, int t, int k, const f
     *(uint4*)(p + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
+// A fragment matrix of T <= 32 rows is two of the above, one per 16 rows: rows 16 b .. 16 b + 15 of X[T][K] at byte
+// offset b * K * 64 (K / 32 steps of 2 KB each).
+__device__ __forceinline__ void frag_store8_rows(uint8_t* frag, int K, int t, int k, const float* v) {
+    frag_store8(frag + (size_t)(t >> 4) * K * 64, t & 15, k, v);
+}
+
 // ── reductions ─────────────────────────────────────────────────────────────────────────────────
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -4,10 +4,12 @@
 #include <stdint.h>
 
 // ── K1: skinny-T weight-streaming GEMM ─────────────────────────────────────────────────────────
-// Y[t][m] = sum_k X[t][k] W[m][k] for t < T <= 16: weights streamed once from HBM straight into the A operand of
-// v_mfma_f32_16x16x32_bf16 (16 rows x 32 k per step), activations read as hi/lo bf16 fragments (fm_device.h).
+// Y[t][m] = sum_k X[t][k] W[m][k] for t < T <= 16 (or, with nb = 2 blocks of activation rows, t < 32): weights
+// streamed once from HBM straight into the A operand of v_mfma_f32_16x16x32_bf16 (16 rows x 32 k per step),
+// activations read as hi/lo bf16 fragments (fm_device.h; block b of the rows at X + b * K * 64).
 // A work-group is 4 waves on one 16-row tile, each wave a quarter of the group's k-range; the 4 partial tiles are
-// summed in LDS. S > 1 splits k across work-groups; those write partial slabs the consumer sums in order.
+// summed in LDS. S > 1 splits k across work-groups; those write partial slabs the consumer sums in order. Output row
+// t of block b is row 16 b + t of out (SK_F32, SK_PARTIAL) or of the output fragments (block b at out + b * M * 64).
 enum SkinnyOut {
     SK_F32 = 0,        // out[t*ld + m] = acc + bias[m]
     SK_PARTIAL = 1,    // out[split*part_stride + t*ld + m] = acc
@@ -40,6 +42,7 @@ struct SkinnyArgs {
     int KW;               // k-steps per wave (K / 32 == S * 4 * KW), any value >= 1
     int mode;
     long long part_stride;
+    int nb;               // blocks of 16 activation rows: 1, or 2 (bf16, KW % 4 == 0; T = 16 rows per block)
 };
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int n_workgroups, hipStream_t st);
 
@@ -77,10 +80,11 @@ struct RowArgs {
     const float* row_scale;// if set, the partial sum of row t (slabs + biases) is multiplied by row_scale[t]
     int f32_local;         // 1: f32_out row t is at f32_out + t * out_ld (not row0 + t)
     int row0;              // row t of the launch is row row0 + t of x, debug_x, frag_out and f32_out (batched blocks)
+    int frag_kw;           // width of the fragment matrix frag_out (0: D); rows >= 16 sit in its second block
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
-// f32 rows [T][K] (row stride ld) -> fragments. T <= 16, K % 32 == 0.
+// f32 rows [T][K] (row stride ld) -> fragments. T <= 32 (rows 16.. in the second block), K % 32 == 0.
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st);
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag,
@@ -146,6 +150,8 @@ struct SelfAttnArgs {
     int pos_base;
     float scale;
     uint8_t* o_frag;
+    int nb;                // blocks of T rows attending each within itself (1 or 2): block b's rows are rows 16 b + t
+    int pos_base1;         //   of qkv (T = 16) and of the o fragments (K = D); its RoPE positions start at pos_base1
 };
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st);
 
@@ -179,7 +185,7 @@ struct MergeArgs {
     int heads, nchunks, nq, hd;
     const float* gate;     // optional: o *= sigmoid(gate[t*gate_ld + h*gate_hs + d])
     int gate_ld, gate_hs;
-    uint8_t* o_frag;       // o row row0 + t, k = h*hd + d
+    uint8_t* o_frag;       // o row row0 + t, k = h*hd + d (rows >= 16 in the second block of K = heads * hd)
     int row0;
 };
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st);
@@ -198,6 +204,8 @@ struct KVFinalArgs {
     int max_ctx;
     int kv_dtype;
     const float* zeros;    // zero row (absent norm weights / RoPE read it)
+    int stage_n;           // rows per group of stage (0: n), of which this launch takes rows stage_t0 ..
+    int stage_t0;
 };
 hipError_t launch_kv_final(const KVFinalArgs& a, hipStream_t st);
 
@@ -219,9 +227,9 @@ hipError_t launch_mtp_prep(const MtpPrepArgs& a, hipStream_t st);
 struct LmArgs {
     const void* E;         // bf16 [V][K] or Q8_0 codes
     const void* Ed;        // Q8_0 scales or null
-    const uint8_t* X;      // fragments of the rows
-    int V, K, T;
-    unsigned long long* best;  // [16] packed (value, index) maxima, zero between calls
+    const uint8_t* X;      // fragments of the rows (rows 16.. in a second block at X + K * 64)
+    int V, K, T;           // T <= 16, or <= 32 for bf16 tables
+    unsigned long long* best;  // [T] packed (value, index) maxima, zero between calls
     int32_t* tokens;
     float* logits;         // optional [T][V]
 };

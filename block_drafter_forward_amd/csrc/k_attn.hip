@@ -38,13 +38,15 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     __shared__ __attribute__((aligned(16))) float QK[32 * QP];
     __shared__ __attribute__((aligned(16))) float Vs[16 * QP];
     __shared__ float Ps[16][17];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int h = blockIdx.x, blk = blockIdx.y, tid = threadIdx.x;
     const int T = a.T, D = a.D;
+    const float* qkv = a.qkv + (size_t)blk * 16 * 3 * D;   // this block's rows
+    const int pos_base = blk ? a.pos_base1 : a.pos_base;
     const int row = tid >> 3, seg = tid & 7;            // q rows 0..15, k rows 16..31
     const int w = row >> 4, t = row & 15, tc = min(t, T - 1);
     float x[SEG], cs[SEG / 2], sn[SEG / 2], nw[SEG], v[VPT];
     {
-        const float* src = a.qkv + (size_t)tc * 3 * D + (size_t)w * D + (size_t)h * HD + seg * SEG;
+        const float* src = qkv + (size_t)tc * 3 * D + (size_t)w * D + (size_t)h * HD + seg * SEG;
 #pragma unroll
         for (int j = 0; j < SEG; ++j) x[j] = 0.f;
 #pragma unroll
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
                 x[4 * j] += m * f.x; x[4 * j + 1] += m * f.y; x[4 * j + 2] += m * f.z; x[4 * j + 3] += m * f.w;
             }
         }
-        const float* rt = a.rope_tab + (size_t)(a.pos_base + tc) * HD + seg * (SEG / 2);
+        const float* rt = a.rope_tab + (size_t)(pos_base + tc) * HD + seg * (SEG / 2);
 #pragma unroll
         for (int j = 0; j < SEG / 8; ++j) {
             const float4 c = ((const float4*)rt)[j], sv = ((const float4*)(rt + HD / 2))[j];
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
 #pragma unroll
         for (int j = 0; j < SEG; ++j) nw[j] = bf16_to_f32(n[j]);
         const int vt = min(tid >> 4, T - 1), vp = tid & 15;
-        const float* vs = a.qkv + (size_t)vt * 3 * D + 2 * (size_t)D + (size_t)h * HD + vp * VPT;
+        const float* vs = qkv + (size_t)vt * 3 * D + 2 * (size_t)D + (size_t)h * HD + vp * VPT;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) v[j] = 0.f;
 #pragma unroll
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
             o[0] += p * v0.x; o[1] += p * v0.y; o[2] += p * v0.z; o[3] += p * v0.w;
             o[4] += p * v1.x; o[5] += p * v1.y; o[6] += p * v1.z; o[7] += p * v1.w;
         }
-        if (ot < T) frag_store8(a.o_frag, ot, h * HD + d0, o);
+        if (ot < T) frag_store8(a.o_frag + (size_t)blk * D * 64, ot, h * HD + d0, o);
     }
 }
 
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
             o[e] *= il;
             if (gp) o[e] *= sigmoidf(gt[e]);
         }
-        frag_store8(a.o_frag, a.row0 + t, h * HD + d0, o);
+        frag_store8_rows(a.o_frag, a.heads * HD, a.row0 + t, h * HD + d0, o);
     }
 }
 
@@ -594,8 +596,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
 __global__ __launch_bounds__(256) void kv_final_kernel(KVFinalArgs a) {
     const int t = blockIdx.x, l = blockIdx.y;
     const int D = a.D, hd = a.hd, per = hd >> 3;   // threads per head
-    const float* krow = a.stage + ((size_t)(2 * l) * a.n + t) * D;
-    const float* vrow = a.stage + ((size_t)(2 * l + 1) * a.n + t) * D;
+    const int sn = a.stage_n ? a.stage_n : a.n;   // stage rows per group; this launch's rows start at stage_t0
+    const float* krow = a.stage + ((size_t)(2 * l) * sn + a.stage_t0 + t) * D;
+    const float* vrow = a.stage + ((size_t)(2 * l + 1) * sn + a.stage_t0 + t) * D;
     const size_t row = (size_t)(a.start + t) * D;
     const size_t kbase = (size_t)(2 * l) * a.max_ctx * D + row;
     const size_t vbase = (size_t)(2 * l + 1) * a.max_ctx * D + row;
@@ -687,10 +690,12 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
 }  // namespace
 
 hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
-    if (a.T < 1 || a.T > 16 || a.parts < 1 || a.parts > MAX_QSLABS) return hipErrorInvalidValue;
+    if (a.T < 1 || a.T > 16 || a.parts < 1 || a.parts > MAX_QSLABS || a.nb < 0 || a.nb > 2 || (a.nb == 2 && a.T != 16))
+        return hipErrorInvalidValue;
+    const dim3 grid(a.heads, a.nb > 1 ? a.nb : 1);
     switch (a.hd) {
-    case 64: self_attn_kernel<64><<<a.heads, 256, 0, st>>>(a); break;
-    case 128: self_attn_kernel<128><<<a.heads, 256, 0, st>>>(a); break;
+    case 64: self_attn_kernel<64><<<grid, 256, 0, st>>>(a); break;
+    case 128: self_attn_kernel<128><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

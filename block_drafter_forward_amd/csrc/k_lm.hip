@@ -5,7 +5,8 @@
 // ("one read of the table") and then argmaxRows over materialised logits; here the logits never leave registers:
 //   * the waves of a work-group own adjacent 16-row vocabulary tiles (the A operand of v_mfma_f32_16x16x32_bf16)
 //     and walk the k-range in lockstep, streaming the table once from HBM; the 16 draft rows are the MFMA's N, as
-//     hi/lo bf16 fragments staged once per work-group in LDS;
+//     hi/lo bf16 fragments staged once per work-group in LDS (32 rows of two batched drafts: two 16-row blocks,
+//     each weight tile multiplied against both);
 //   * the wave's best (value, index) per row is reduced across lanes with shuffles, then across the work-group's
 //     waves in LDS, then across work-groups with one 64-bit atomicMax per row on an order-preserving key
 //     (value bits, ~index), so ties resolve to the lowest index independent of scheduling;
@@ -54,40 +55,52 @@ constexpr int RS_PITCH = 33;   // uint4 per LDS row: 32 + 1 pad (conflict-free A
 // 16-row vocabulary tiles and walk the k-range in lockstep, so each chunk's activation fragments (8 k-steps,
 // 16 KB) are read from L2 once per work-group (each thread one quarter of it) into a double-buffered LDS slab
 // instead of once per wave. Weights and fragments of the next two chunks are in flight while one multiplies.
+// NB blocks of 16 rows (bf16 tables): each chunk's fragments of every block go to the slab, block b at b * 1024
+// (uint4), and each weight tile is multiplied against every block.
+template <int NW, int NB>
 struct WsRegs {
-    uint4 a[8];   // this wave's 16 rows x 256 columns
-    uint4 b[4];   // this thread's quarter of the chunk's fragments
+    uint4 a[8];             // this wave's 16 rows x 256 columns
+    uint4 b[NB * 16 / NW];  // this thread's share of the chunk's fragments
 };
 
-template <int NW>
-__device__ __forceinline__ void ws_load(WsRegs& r, const LmArgs& a, int v0, int ch, int tid) {
+template <int NW, int NB>
+__device__ __forceinline__ void ws_load(WsRegs<NW, NB>& r, const LmArgs& a, int v0, int ch, int tid) {
     const int lane = tid & 63;
     const uint16_t* E = (const uint16_t*)a.E + (size_t)(v0 + (lane >> 5)) * a.K + ch * 256 + (lane & 31) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) r.a[i] = ldg_nt(E + (size_t)(2 * i) * a.K);
-    const uint4* xb = (const uint4*)(a.X + (size_t)ch * 8 * FRAG_STEP_BYTES);
 #pragma unroll
-    for (int j = 0; j < 16 / NW; ++j) r.b[j] = xb[tid + 64 * NW * j];
+    for (int b = 0; b < NB; ++b) {
+        const uint4* xb = (const uint4*)(a.X + (size_t)b * a.K * 64 + (size_t)ch * 8 * FRAG_STEP_BYTES);
+#pragma unroll
+        for (int j = 0; j < 16 / NW; ++j) r.b[b * (16 / NW) + j] = xb[tid + 64 * NW * j];
+    }
 }
 
-template <int NW>
-__device__ __forceinline__ void ws_stage(const WsRegs& r, uint4* alds, uint4* blds, int tid) {
+template <int NW, int NB>
+__device__ __forceinline__ void ws_stage(const WsRegs<NW, NB>& r, uint4* alds, uint4* blds, int tid) {
     const int lane = tid & 63;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 8; ++i) alds[(2 * i + (lane >> 5)) * RS_PITCH + (lane & 31)] = r.a[i];
 #pragma unroll
-    for (int j = 0; j < 16 / NW; ++j) blds[tid + 64 * NW * j] = r.b[j];
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 16 / NW; ++j) blds[b * 1024 + tid + 64 * NW * j] = r.b[b * (16 / NW) + j];
 }
 
-__device__ __forceinline__ void ws_compute(const uint4* alds, const uint4* blds, f32x4_t& acc, int lane) {
+template <int NB>
+__device__ __forceinline__ void ws_compute(const uint4* alds, const uint4* blds, f32x4_t* acc, int lane) {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint4 av = alds[r * RS_PITCH + 4 * i + g];
-        const uint4 bh = blds[i * 128 + lane], bl = blds[i * 128 + 64 + lane];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bh), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bl), acc, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint4 bh = blds[b * 1024 + i * 128 + lane], bl = blds[b * 1024 + i * 128 + 64 + lane];
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bh), acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bl), acc[b], 0, 0, 0);
+        }
     }
 }
 
@@ -156,23 +169,27 @@ __device__ __forceinline__ void ws_compute_q8(const uint4* alds, const uint16_t*
 }
 
 // K % 512 == 0 (an even number of chunks), V % 16 == 0 (a tail work-group's extra waves redo the last tile).
-template <int WT, int NW>
+// NB = 2 (bf16 only): rows 16 b + t of block b, every weight tile multiplied against both blocks.
+template <int WT, int NW, int NB = 1>
 __global__ __launch_bounds__(NW * 64) void lm_argmax_ws_kernel(LmArgs a) {
+    static_assert(NB == 1 || WT == 0, "two row blocks: bf16 tables only");
     constexpr int APITCH = WT == 0 ? RS_PITCH : Q8_PITCH;
     __shared__ uint4 alds_all[NW][16 * APITCH];
     __shared__ uint16_t slds_all[NW][8 * 16];
-    __shared__ uint4 blds_all[2][1024];
+    __shared__ uint4 blds_all[2][NB * 1024];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4;
     const int v0 = min((blockIdx.x * NW + wave) * 16, a.V - 16);   // tail waves redo the last tile (discarded)
     const bool own = (blockIdx.x * NW + wave) * 16 < a.V;
     uint4* alds = alds_all[wave];
     uint16_t* slds = slds_all[wave];
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int nch = a.K >> 8;
-    using Regs = typename std::conditional<WT == 0, WsRegs, WsRegsQ8>::type;
+    using Regs = typename std::conditional<WT == 0, WsRegs<NW, NB>, WsRegsQ8>::type;
     auto load = [&](Regs& r, int ch) {
-        if constexpr (WT == 0) ws_load<NW>(r, a, v0, ch, tid);
+        if constexpr (WT == 0) ws_load<NW, NB>(r, a, v0, ch, tid);
         else ws_load_q8<NW>(r, a, v0, ch, tid);
         // each chunk's loads stay together, in the prologue as in the loop: the wait before a chunk is staged is
         // the stricter of the loop header's two entries, and a prologue that interleaves the two chunks' loads
@@ -180,12 +197,12 @@ __global__ __launch_bounds__(NW * 64) void lm_argmax_ws_kernel(LmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     };
     auto stage = [&](const Regs& r, int buf) {
-        if constexpr (WT == 0) ws_stage<NW>(r, alds, blds_all[buf], tid);
+        if constexpr (WT == 0) ws_stage<NW, NB>(r, alds, blds_all[buf], tid);
         else ws_stage_q8<NW>(r, alds, slds, blds_all[buf], tid);
     };
     auto compute = [&](int buf) {
-        if constexpr (WT == 0) ws_compute(alds, blds_all[buf], acc, lane);
-        else ws_compute_q8(alds, slds, blds_all[buf], acc, lane);
+        if constexpr (WT == 0) ws_compute<NB>(alds, blds_all[buf], acc, lane);
+        else ws_compute_q8(alds, slds, blds_all[buf], acc[0], lane);
     };
     Regs r0, r1;
     load(r0, 0);
@@ -208,30 +225,33 @@ __global__ __launch_bounds__(NW * 64) void lm_argmax_ws_kernel(LmArgs a) {
     __syncthreads();
     compute(1);
 
-    // lane holds z[t = lane % 16][v0 + 4 g + j]
-    const int t = lane & 15;
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
-    if (own) {
+    // lane holds z[row 16 b + lane % 16][v0 + 4 g + j] of block b
+    __shared__ float wb[NW][NB * 16];
+    __shared__ int wi[NW][NB * 16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int v = v0 + 4 * g + j;
-            const float z = acc[j];
-            if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
-            if (z > best) { best = z; bidx = v; }
+    for (int b = 0; b < NB; ++b) {
+        const int t = 16 * b + (lane & 15);
+        float best = -INFINITY;
+        int bidx = 0x7fffffff;
+        if (own) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int v = v0 + 4 * g + j;
+                const float z = acc[b][j];
+                if (a.logits && t < a.T) a.logits[(size_t)t * a.V + v] = z;
+                if (z > best) { best = z; bidx = v; }
+            }
         }
-    }
 #pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-        const float ob = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bidx, o, 64);
-        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+        for (int o = 16; o < 64; o <<= 1) {
+            const float ob = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(bidx, o, 64);
+            if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+        }
+        if (lane < 16) { wb[wave][16 * b + lane] = best; wi[wave][16 * b + lane] = bidx; }
     }
-    __shared__ float wb[NW][16];
-    __shared__ int wi[NW][16];
-    if (lane < 16) { wb[wave][lane] = best; wi[wave][lane] = bidx; }
     __syncthreads();
-    if (tid < 16 && tid < a.T) {
+    if (tid < NB * 16 && tid < a.T) {
         float b = wb[0][tid];
         int bi = wi[0][tid];
 #pragma unroll
@@ -256,9 +276,11 @@ __global__ void lm_finalize_kernel(unsigned long long* best, int T, int32_t* tok
 }  // namespace
 
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st) {
-    // rows of a multiple of 512 (an even number of 8-step chunks) and whole 16-row vocabulary tiles
-    if (a.T > 16 || a.K % 512 || a.V % 16) return hipErrorInvalidValue;
-    if (wtype == 0) lm_argmax_ws_kernel<0, 4><<<(a.V + 63) / 64, 256, 0, st>>>(a);
+    // rows of a multiple of 512 (an even number of 8-step chunks) and whole 16-row vocabulary tiles; more than 16
+    // activation rows (two blocks) on bf16 tables only
+    if (a.T < 1 || a.T > 32 || (a.T > 16 && wtype != 0) || a.K % 512 || a.V % 16) return hipErrorInvalidValue;
+    if (wtype == 0 && a.T > 16) lm_argmax_ws_kernel<0, 8, 2><<<(a.V + 127) / 128, 512, 0, st>>>(a);
+    else if (wtype == 0) lm_argmax_ws_kernel<0, 4><<<(a.V + 63) / 64, 256, 0, st>>>(a);
     else lm_argmax_ws_kernel<1, 8><<<(a.V + 127) / 128, 512, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

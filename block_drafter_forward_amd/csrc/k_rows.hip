@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
                 else if (a.norm == ROW_RMS) h[e] = v[j][e] * r * p0[j][e];
                 else h[e] = v[j][e];
             }
-            if (a.frag_out) frag_store8(a.frag_out, t + a.row0, a.frag_koff + i0, h);
+            if (a.frag_out) frag_store8_rows(a.frag_out, a.frag_kw ? a.frag_kw : D, t + a.row0, a.frag_koff + i0, h);
             if (a.f32_out) st8(a.f32_out + (size_t)(t + (a.f32_local ? 0 : a.row0)) * a.out_ld + i0, h);
         }
     }
@@ -146,7 +146,7 @@ __global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag)
     const float* p = x + (size_t)t * ld + slot * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = p[e];
-    frag_store8(frag, t, slot * 8, v);
+    frag_store8_rows(frag, K, t, slot * 8, v);
 }
 
 // Token ids outside [0, V) are clamped into the table (a device-side id cannot be validated by the host).
@@ -421,6 +421,7 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st) {
+    if (T < 1 || T > 32 || K % 32) return hipErrorInvalidValue;
     dim3 grid((K / 8 + 255) / 256, T);
     f32_to_frag_kernel<<<grid, 256, 0, st>>>(x, ld, K, frag);
     return hipGetLastError();

@@ -122,19 +122,23 @@ __device__ __forceinline__ void sk_compute(const SkStage<NT, WT, SKC>& st, f32x4
 // (32 RC columns) of the wave's 16-row tile is loaded as RC row-contiguous instructions (16 / RC rows x 64 RC bytes
 // each: whole cache lines), parked in a wave-private LDS tile (row pitch padded by 16 bytes) and read back in the
 // A layout; the next chunk's weights and activation fragments are in flight while the current one multiplies.
-template <int NT, int RC>
+template <int NT, int RC, int NB>
 struct RsStage {
     uint4 a[NT][RC];
-    uint4 bh[RC], bl[RC];
+    uint4 bh[NB][RC], bl[NB][RC];
 };
 
-template <int NT, int RC>
-__device__ __forceinline__ void rs_load(RsStage<NT, RC>& st, const SkinnyGroup& G, int K, int m0, int s, int lane) {
-    const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
+template <int NT, int RC, int NB>
+__device__ __forceinline__ void rs_load(RsStage<NT, RC, NB>& st, const SkinnyGroup& G, int K, int m0, int s,
+                                        int lane) {
 #pragma unroll
-    for (int i = 0; i < RC; ++i) {
-        st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
-        st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
+    for (int b = 0; b < NB; ++b) {
+        const uint8_t* xb = G.X + (size_t)b * K * 64 + (size_t)s * FRAG_STEP_BYTES + lane * 16;
+#pragma unroll
+        for (int i = 0; i < RC; ++i) {
+            st.bh[b][i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
+            st.bl[b][i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
+        }
     }
     constexpr int RPI = 16 / RC, LPR = 64 / RPI;   // rows per instruction, lanes per row
     const int sub = lane / LPR, piece = lane % LPR;
@@ -146,8 +150,8 @@ __device__ __forceinline__ void rs_load(RsStage<NT, RC>& st, const SkinnyGroup& 
     }
 }
 
-template <int NT, int RC>
-__device__ __forceinline__ void rs_compute(const RsStage<NT, RC>& st, uint4* lds, f32x4_t* acc, int lane) {
+template <int NT, int RC, int NB>
+__device__ __forceinline__ void rs_compute(const RsStage<NT, RC, NB>& st, uint4* lds, f32x4_t (*acc)[NB], int lane) {
     constexpr int RPI = 16 / RC, LPR = 64 / RPI, PITCH = 4 * RC + 1;
     const int sub = lane / LPR, piece = lane % LPR, r = lane & 15, g = lane >> 4;
     __builtin_amdgcn_wave_barrier();   // the previous chunk's LDS reads stay before these writes
@@ -161,8 +165,13 @@ __device__ __forceinline__ void rs_compute(const RsStage<NT, RC>& st, uint4* lds
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const uint4 av = lds[(n * 16 + r) * PITCH + 4 * i + g];
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(st.bh[i]), acc[n], 0, 0, 0);
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(st.bl[i]), acc[n], 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                acc[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(st.bh[b][i]), acc[n][b],
+                                                                    0, 0, 0);
+                acc[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(st.bl[b][i]), acc[n][b],
+                                                                    0, 0, 0);
+            }
         }
     }
 }
@@ -242,8 +251,10 @@ __device__ __forceinline__ void rs_compute_q8(const RsStageQ8<NT>& st, uint4* ld
 // stage i computes), with the last pair peeled so the loop body carries no conditions.
 // A single Q8_0 matrix fits two work-groups per CU (<= 256 registers a wave, no scratch); without the bound the
 // compiler spends AGPRs and runs one wave per SIMD. Two matrices at once would spill, so they keep one.
-template <int NT, int WT, int UP, int SKC>
+// NB = 2 (two blocks of 16 activation rows against each weight tile) exists for bf16 with UP = 2 only.
+template <int NT, int WT, int UP, int SKC, int NB = 1>
 __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skinny_kernel(SkinnyArgs a) {
+    static_assert(NB == 1 || (WT == SKW_BF16 && UP == 2), "two row blocks: row-staged bf16 only");
     const int bid = blockIdx.x;
     int gi = 0;
 #pragma unroll 1
@@ -260,9 +271,12 @@ __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skin
     const int r = lane & 15, g = lane >> 4;
     const int K = a.K;
 
-    f32x4_t acc[NT];
+    f32x4_t accb[NT][NB];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) accb[n][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t* acc = &accb[0][0];   // the one-block paths (NB == 1): accb[n][0] is acc[n]
 
     if constexpr (UP == 2 && WT == SKW_Q8_0) {
         __shared__ uint4 q8_lds[4][NT * 16 * Q8_PITCH];
@@ -289,22 +303,22 @@ __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skin
     } else if constexpr (UP == 2) {
         __shared__ uint4 rs_lds[4][NT * 16 * (4 * SKC + 1)];
         uint4* lds = rs_lds[wave];
-        RsStage<NT, SKC> c0, c1;
+        RsStage<NT, SKC, NB> c0, c1;
         const int nch = KW / SKC;
-        rs_load<NT, SKC>(c0, G, K, m0, s0, lane);
+        rs_load<NT, SKC, NB>(c0, G, K, m0, s0, lane);
         int ch = 0;
         for (; ch + 2 < nch; ch += 2) {
-            rs_load<NT, SKC>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
-            rs_compute<NT, SKC>(c0, lds, acc, lane);
-            rs_load<NT, SKC>(c0, G, K, m0, s0 + SKC * (ch + 2), lane);
-            rs_compute<NT, SKC>(c1, lds, acc, lane);
+            rs_load<NT, SKC, NB>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
+            rs_compute<NT, SKC, NB>(c0, lds, accb, lane);
+            rs_load<NT, SKC, NB>(c0, G, K, m0, s0 + SKC * (ch + 2), lane);
+            rs_compute<NT, SKC, NB>(c1, lds, accb, lane);
         }
         if (ch + 1 < nch) {
-            rs_load<NT, SKC>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
-            rs_compute<NT, SKC>(c0, lds, acc, lane);
-            rs_compute<NT, SKC>(c1, lds, acc, lane);
+            rs_load<NT, SKC, NB>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
+            rs_compute<NT, SKC, NB>(c0, lds, accb, lane);
+            rs_compute<NT, SKC, NB>(c1, lds, accb, lane);
         } else {
-            rs_compute<NT, SKC>(c0, lds, acc, lane);
+            rs_compute<NT, SKC, NB>(c0, lds, accb, lane);
         }
     } else if constexpr (UP == 1) {
         SkStage<NT, WT, SKC> st;
@@ -325,51 +339,57 @@ __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skin
         sk_compute<NT, WT, SKC>(st1, acc);
     }
 
-    // ── sum the four waves' tiles (fixed order) ──
-    __shared__ f32x4_t red[NT][4][64];
-    __shared__ float tile[16][17];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) red[n][wave][lane] = acc[n];
-    __syncthreads();
-    const int el = threadIdx.x & 63, rr = threadIdx.x >> 6;
-    float v[NT];
+    // ── sum the four waves' tiles (fixed order), per block of rows ──
+    __shared__ f32x4_t red[NT * NB][4][64];
+    __shared__ float tile[NB][16][17];
 #pragma unroll
     for (int n = 0; n < NT; ++n)
-        v[n] = ((red[n][0][el][rr] + red[n][1][el][rr]) + red[n][2][el][rr]) + red[n][3][el][rr];
-    const int ml = 4 * (el >> 4) + rr;   // row of the tile
-    const int t = el & 15;               // activation row (slot)
-    const int m = m0 + ml;
-
-    switch (a.mode) {
-    case SK_F32:
-        if (t < a.T) {
-            float b = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
-            ((float*)G.out)[(size_t)t * G.ld + m] = v[0] + b;
-        }
-        return;
-    case SK_PARTIAL:
-        if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)t * G.ld + m] = v[0];
-        return;
-    default: break;
-    }
-    float o;
-    if (a.mode == SK_FRAG_GELU) {
-        float b = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
-        o = gelu_erf(v[0] + b);
-    } else if (a.mode == SK_FRAG_GEGLU) {
-        o = gelu_tanh(v[0]) * v[NT - 1];
-    } else {
-        o = silu(v[0]) * v[NT - 1];
-    }
-    tile[t][ml] = o;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[n * NB + b][wave][lane] = accb[n][b];
     __syncthreads();
-    if (threadIdx.x < 32) {
-        const int tt = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const int el = threadIdx.x & 63, rr = threadIdx.x >> 6;
+    const int ml = 4 * (el >> 4) + rr;   // row of the tile
+    const int t = el & 15;               // activation row (slot) within the block
+    const int m = m0 + ml;
+    const bool frag_mode = a.mode != SK_F32 && a.mode != SK_PARTIAL;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float v[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int q = n * NB + b;
+            v[n] = ((red[q][0][el][rr] + red[q][1][el][rr]) + red[q][2][el][rr]) + red[q][3][el][rr];
+        }
+        const int row = 16 * b + t;
+        if (a.mode == SK_F32) {
+            if (t < a.T) {
+                float bi = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
+                ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + bi;
+            }
+        } else if (a.mode == SK_PARTIAL) {
+            if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)row * G.ld + m] = v[0];
+        } else {
+            float o;
+            if (a.mode == SK_FRAG_GELU) {
+                float bi = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
+                o = gelu_erf(v[0] + bi);
+            } else if (a.mode == SK_FRAG_GEGLU) {
+                o = gelu_tanh(v[0]) * v[NT - 1];
+            } else {
+                o = silu(v[0]) * v[NT - 1];
+            }
+            tile[b][t][ml] = o;
+        }
+    }
+    if (!frag_mode) return;
+    __syncthreads();
+    if (threadIdx.x < 32 * NB) {
+        const int b = threadIdx.x >> 5, tt = (threadIdx.x >> 1) & 15, h = threadIdx.x & 1;
         if (tt < a.T) {
             float vals[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] = tile[tt][8 * h + e];
-            frag_store8((uint8_t*)G.out, tt, m0 + 8 * h, vals);
+            for (int e = 0; e < 8; ++e) vals[e] = tile[b][tt][8 * h + e];
+            frag_store8((uint8_t*)G.out + (size_t)b * G.M * 64, tt, m0 + 8 * h, vals);
         }
     }
 }
@@ -378,6 +398,15 @@ template <int NT, int WT>
 hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
     const int KW = a.KW;
     dim3 grid(nwg), block(256);
+    if (a.nb == 2) {   // two blocks of rows: chunks of 4 k-steps (the registers of two blocks' fragments)
+        if constexpr (WT == SKW_BF16) {
+            if (KW % 4 || a.T != 16) return hipErrorInvalidValue;
+            skinny_kernel<NT, WT, 2, 4, 2><<<grid, block, 0, st>>>(a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    if (a.nb != 1) return hipErrorInvalidValue;
     if (WT == SKW_BF16 && KW % 4 == 0) {
         if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
         else skinny_kernel<NT, WT, 2, 4><<<grid, block, 0, st>>>(a);

@@ -169,7 +169,9 @@ fm_status fm_draft_block(fm_drafter* d, const fm_block_args* a, float* hidden_ou
  * stored. hidden is device f32 [rows][target_dim]; the table is the "lm_head.weight" (bf16 [vocab][target_dim]) or
  * "lm_head" (Q8_0) tensor named at fm_create.
  * logits, if not NULL, receives the full [rows][vocab] f32 logits (a debug path; the fused path never writes them).
- * Errors: FM_E_INVALID (rows < 1 or > 16, null hidden / tokens). */
+ * rows <= 16; a flow-map handle (bf16 table) takes up to 32, the rows of a two-request fm_draft_batch, and streams
+ * the table once for all of them.
+ * Errors: FM_E_INVALID (rows < 1 or above that limit, null hidden / tokens). */
 fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t* tokens, float* logits,
                        void* stream);
 
@@ -228,15 +230,20 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
 /* Batched drafting (module-dflash.ts forwardRows over anchors[]; for the MTP head, several sequences' rows in one
  * pass): one block forward for B requests. Handle ds[b] holds request b's context (its KV cache); all handles share
  * the same weight tensors and block shape (max_ctx may differ). args[b] is request b's fm_draft_block argument
- * (KV-injection: anchor; MTP: rows, pos, kv_lo, embed_rows, prev_hidden; debug_layers is ignored). Every projection
- * streams its weights once for all rows; each request attends over its own cache (KV-injection: its context rows
- * ++ its block rows; MTP: causal over [kv_lo, pos + m], after writing its rows' K/V at pos). hidden_out gets the
- * rows in request order (KV-injection: block rows per request; MTP: args[b].rows each), at most 16 in all; the
- * lm_head over them is fm_lm_argmax(ds[0], hidden_out, rows, ...). KV-injection: each handle keeps its own request's
- * normed backbone rows, so fm_markov_argmax(ds[b], request b's rows of hidden_out, ...) decodes request b.
- * Errors: FM_E_INVALID (null pointers, B < 1, more than 16 rows, handles with other shapes or other weight
- * tensors, a handle twice, a request's own fm_draft_block errors), FM_E_CONTEXT_FULL (an MTP request past its
- * cache), FM_E_UNSUPPORTED (flow-map handles: a block alone is 16 rows). */
+ * (flow-map and KV-injection: anchor, and for flow-map pos; MTP: rows, pos, kv_lo, embed_rows, prev_hidden;
+ * debug_layers is ignored). Every projection streams its weights once for all rows; each request attends over its
+ * own cache (flow-map: cross-attention over its cache rows [0, pos], self-attention among its own slots, its anchor
+ * slot written into its own cache at pos; KV-injection: its context rows ++ its block rows; MTP: causal over
+ * [kv_lo, pos + m], after writing its rows' K/V at pos). hidden_out gets the rows in request order (flow-map and
+ * KV-injection: block rows per request; MTP: args[b].rows each); the lm_head over them is
+ * fm_lm_argmax(ds[0], hidden_out, rows, ...). KV-injection and MTP take at most 16 rows in all; flow-map takes
+ * B <= 2 requests (32 rows: each weight tile multiplied against two 16-row blocks), with 16-slot blocks, bf16
+ * weights, dim and ffn multiples of 512, and handles whose modulation tables agree (the same fm_time_condition
+ * jump, or none). KV-injection: each handle keeps its own request's normed backbone rows, so
+ * fm_markov_argmax(ds[b], request b's rows of hidden_out, ...) decodes request b.
+ * Errors: FM_E_INVALID (null pointers, B < 1, more than 16 rows, handles with other shapes, other weight tensors or
+ * (flow-map) another modulation table, a handle twice, a request's own fm_draft_block errors), FM_E_CONTEXT_FULL (a
+ * request past its cache), FM_E_UNSUPPORTED (a flow-map batch of more than 2 requests or of another shape). */
 fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* args, float* hidden_out, void* stream);
 
 /* How fm_draft_block runs a flow-map draft. The draft is one forward pass either way (the same arithmetic, results
