@@ -295,6 +295,8 @@ fm_status validate_config(const fm_config* c) {
             c->kv_dtype != FM_KV_F16 || c->head_dim > 128)
             return fail(FM_E_UNSUPPORTED, "flow-map needs interleaved RoPE, exact GELU, bf16, f16 cache, hd <= 128");
         if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
+        if (c->n_taps * c->target_dim > TAPS_MAX_WIDTH)
+            return fail(FM_E_UNSUPPORTED, "tap width %d > %d", c->n_taps * c->target_dim, TAPS_MAX_WIDTH);
         if (c->max_ctx % 32) return fail(FM_E_INVALID, "an f16 cache needs max_ctx %% 32 == 0 (V is tiled by 32)");
         if (c->kv_heads != c->heads) return fail(FM_E_UNSUPPORTED, "the flow-map drafter has one K/V head per head");
         break;
@@ -303,6 +305,8 @@ fm_status validate_config(const fm_config* c) {
             c->kv_dtype != FM_KV_F32 || c->head_dim > 128)
             return fail(FM_E_UNSUPPORTED, "KV-inject needs no RoPE, tanh GeGLU, bf16, f32 cache, hd <= 128");
         if ((c->n_taps * c->target_dim) % 128) return fail(FM_E_INVALID, "tap width must be a multiple of 128");
+        if (c->n_taps * c->target_dim > TAPS_MAX_WIDTH)
+            return fail(FM_E_UNSUPPORTED, "tap width %d > %d", c->n_taps * c->target_dim, TAPS_MAX_WIDTH);
         if (c->kv_heads != c->heads) return fail(FM_E_UNSUPPORTED, "KV-inject attends with every head's own K/V");
         break;
     case FM_VARIANT_MTP:

@@ -305,7 +305,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int n_workgroups, hipStream_t st
 // c = 0..7 the cos then the sin of pairs c, c + 8, c + 16, c + 24 of the block.
 hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hipStream_t st);
 // n rows of f32 taps [n][KT] -> f16 rows y = f16(x s) with s = 2^k per row (the row's largest magnitude times s in
-// [2^14, 2^15)); rscale[row] = 1 / s. KT % 4 == 0.
+// [2^14, 2^15)); rscale[row] = 1 / s. KT % 4 == 0, KT <= TAPS_MAX_WIDTH.
+#define TAPS_MAX_WIDTH 16384
 hipError_t launch_taps_f16(const float* x, int n, int KT, uint16_t* y, float* rscale, hipStream_t st);
 // y = f16(x) element-wise (exact for bf16 above f16's subnormal range), n % 4 == 0.
 hipError_t launch_bf16_to_f16(const uint16_t* x, size_t n, uint16_t* y, hipStream_t st);

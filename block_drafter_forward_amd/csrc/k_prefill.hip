@@ -451,15 +451,23 @@ __global__ void rope_prefill_kernel(const float* __restrict__ tab, int P, int rd
 // neither overflow nor flush the row whatever its magnitude) and 1 / s goes to rscale[row], by which the consumer
 // of the context projection multiplies that row's f32 output. A row whose largest magnitude is 0 or not finite
 // keeps s = 1.
+// The row is held in registers (NPT float4 per thread, all its loads in flight together), so it is read from HBM once
+// (KT <= 1024 NPT).
+template <int NPT>
 __global__ __launch_bounds__(256) void taps_f16_kernel(const float* __restrict__ x, int KT, uint2* __restrict__ y,
-                                                       float* __restrict__ rscale) {
+                                                           float* __restrict__ rscale) {
     const int row = blockIdx.x, n4 = KT >> 2;
     const float4* p = (const float4*)(x + (size_t)row * KT);
-    float m = 0.f;
-    for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = p[i];
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    float4 v[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        v[j] = i < n4 ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
     __shared__ float red[4];
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -474,9 +482,10 @@ __global__ __launch_bounds__(256) void taps_f16_kernel(const float* __restrict__
     const float s = ldexpf(1.f, k);
     if (threadIdx.x == 0) rscale[row] = ldexpf(1.f, -k);
     uint2* q = y + (size_t)row * n4;
-    for (int i = threadIdx.x; i < n4; i += 256) {   // the second pass reads the row back from L2
-        const float4 v = p[i];
-        q[i] = make_uint2(pack_f16x2(v.x * s, v.y * s), pack_f16x2(v.z * s, v.w * s));
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        if (i < n4) q[i] = make_uint2(pack_f16x2(v[j].x * s, v[j].y * s), pack_f16x2(v[j].z * s, v[j].w * s));
     }
 }
 
@@ -528,7 +537,8 @@ hipError_t launch_rope_prefill(const float* tab, int P, int rdim, float* out, hi
 
 hipError_t launch_taps_f16(const float* x, int n, int KT, uint16_t* y, float* rscale, hipStream_t st) {
     if (n < 1 || KT % 4 || ((uintptr_t)x & 15) || ((uintptr_t)y & 7)) return hipErrorInvalidValue;
-    taps_f16_kernel<<<n, 256, 0, st>>>(x, KT, (uint2*)y, rscale);
+    if (KT > TAPS_MAX_WIDTH) return hipErrorInvalidValue;
+    taps_f16_kernel<16><<<n, 256, 0, st>>>(x, KT, (uint2*)y, rscale);
     return hipGetLastError();
 }
 
