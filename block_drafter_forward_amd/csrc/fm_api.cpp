@@ -60,24 +60,38 @@ int pick_qsplit(int K) {
     return 1;
 }
 
-// k-split of a partial-output skinny GEMM (at most 8 slabs, the consumers' limit). Preference: enough work-groups
-// (tiles * S >= TARGET_WGS) with a per-wave range that is a whole number of row-staged chunks (KW % 8 == 0);
-// then enough work-groups with any supported range; else the largest supported S. Q8_0 weights (q8): the
-// single-matrix kernel runs two work-groups per CU, so twice the work-groups are wanted, and only whole chunks.
-int pick_split(int M_total, int K, bool q8 = false) {
-    const int target = q8 ? 2 * TARGET_WGS : TARGET_WGS;
+// k-split of a partial-output bf16 skinny GEMM (at most 8 slabs, the consumers' limit). Preference: enough
+// work-groups (tiles * S >= TARGET_WGS) with a per-wave range that is a whole number of row-staged chunks
+// (KW % 8 == 0); then enough work-groups with any supported range; else the largest supported S.
+int pick_split(int M_total, int K) {
     const int n4 = K / 128, tiles = M_total / 16;
     int any_enough = -1, largest = -1;
     for (int S = 1; S <= std::min(8, n4); ++S) {
         if (n4 % S || !kw_ok(n4 / S)) continue;
-        if (q8 && (n4 / S) % 8) continue;   // the row-staged Q8_0 path takes whole chunks of 8 k-steps
         largest = S;
-        if (tiles * S >= target) {
+        if (tiles * S >= TARGET_WGS) {
             if ((n4 / S) % 8 == 0) return S;
             if (any_enough < 0) any_enough = S;
         }
     }
     return any_enough > 0 ? any_enough : largest;
+}
+
+// k-split of a Q8_0 projection (the tile-owning skinny variant): whole 256-column chunks per split, at most 8 slabs;
+// the fewest splits that give twice TARGET_WGS work-groups, else the most.
+int pick_split_ws(int groups, int K) {
+    const int nch = K / 256;
+    int S = 1;
+    for (int s = 1; s <= std::min(8, nch); ++s) {
+        if (nch % s) continue;
+        S = s;
+        if (groups * s >= 2 * TARGET_WGS) break;
+    }
+    return S;
+}
+int ws_groups(int M, bool glu = false) {
+    const int tpw = glu ? SK_WS_WAVES / 2 : SK_WS_WAVES;   // tiles per work-group (of each matrix of a gated unit)
+    return (M / 16 + tpw - 1) / tpw;
 }
 
 // ── the persistent draft kernel (k_draft.hip): which shapes it takes, its k-splits and its arena ─────
@@ -177,7 +191,7 @@ int kmax_frag(const fm_config& c) {
 int part_need(const fm_config& c) {   // floats per split slab row-set: max over partial uses of S * M
     int need = 0;
     const bool q8 = c.wtype == FM_W_Q8_0;
-    auto use = [&](int M, int K) { need = std::max(need, pick_split(M, K, q8) * M); };
+    auto use = [&](int M, int K) { need = std::max(need, (q8 ? pick_split_ws(ws_groups(M), K) : pick_split(M, K)) * M); };
     const int D = c.dim, Ht = c.target_dim;
     if (c.variant == FM_VARIANT_FLOWMAP) {
         use(D, c.n_taps * Ht); use(D, Ht); use(D, D); use(D, c.ffn);
@@ -281,8 +295,8 @@ fm_status validate_config(const fm_config* c) {
         return fail(FM_E_INVALID, "dim %d != heads * head_dim", c->dim);
     if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
         return fail(FM_E_UNSUPPORTED, "head_dim %d (64, 128 or 256 supported)", c->head_dim);
-    if (c->dim % 256 || c->target_dim % 256 || c->ffn % (c->wtype == FM_W_BF16 ? 256 : 128))
-        return fail(FM_E_INVALID, "dim and target_dim must be multiples of 256, ffn of 256 (bf16) or 128 (Q8_0)");
+    if (c->dim % 256 || c->target_dim % 256 || c->ffn % 256)
+        return fail(FM_E_INVALID, "dim, target_dim and ffn must be multiples of 256");
     if (c->vocab % 16) return fail(FM_E_INVALID, "vocab must be a multiple of 16");
     if (c->target_dim % 512)   // the lm_head kernel walks its rows in pairs of 256-column chunks
         return fail(FM_E_UNSUPPORTED, "target_dim %d: the lm_head takes rows of a multiple of 512", c->target_dim);
@@ -316,7 +330,7 @@ fm_status validate_config(const fm_config* c) {
         if (c->rope_dims <= 0 || c->rope_dims > c->head_dim || c->rope_dims % 2)
             return fail(FM_E_INVALID, "rope_dims");
         if (c->target_dim != c->dim) return fail(FM_E_INVALID, "MTP target_dim must equal dim");
-        if ((c->heads * c->head_dim) % 128 || (c->kv_heads * c->head_dim) % 16)
+        if ((c->heads * c->head_dim) % 256 || (c->kv_heads * c->head_dim) % 16)   // o_proj's k-range: whole chunks
             return fail(FM_E_INVALID, "MTP head widths");
         break;
     }
@@ -431,25 +445,37 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     if (gs.empty() || gs.size() > SK_MAX_GROUPS) return fail(FM_E_INVALID, "skinny: %zu groups", gs.size());
     if (K % 128) return fail(FM_E_INVALID, "skinny: K %d not a multiple of 128", K);
     SkinnyArgs a{};
-    int tiles_total = 0;
-    for (auto& g : gs) tiles_total += g.M / 16;
+    const bool q8 = d->c.wtype == FM_W_Q8_0;
+    const bool glu = mode == SK_FRAG_GEGLU || mode == SK_FRAG_SWIGLU;
+    int tiles_total = 0, groups_total = 0;
+    for (auto& g : gs) {
+        tiles_total += g.M / 16;
+        groups_total += ws_groups(g.M, glu);
+    }
     int S = 1;
-    if (mode == SK_PARTIAL)
-        S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K, d->c.wtype == FM_W_Q8_0);
-    if (nb == 2) {
+    if (q8) {   // the tile-owning variant: whole 256-column chunks per split
+        if (nb != 1 || T > TMAX) return fail(FM_E_UNSUPPORTED, "skinny: Q8_0 takes one block of <= %d rows", TMAX);
+        if (K % 256) return fail(FM_E_UNSUPPORTED, "skinny: Q8_0 needs K %% 256 == 0 (K %d)", K);
+        if (mode == SK_PARTIAL) S = S_force > 0 ? S_force : pick_split_ws(groups_total, K);
+        if (S < 1 || (K / 256) % S) return fail(FM_E_UNSUPPORTED, "skinny: no Q8_0 k-split %d for K %d", S, K);
+    } else if (mode == SK_PARTIAL) {
+        S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K);
+    }
+    if (q8) {
+    } else if (nb == 2) {
         if (T != 16 || d->c.wtype != FM_W_BF16) return fail(FM_E_UNSUPPORTED, "skinny: two row blocks need bf16, T 16");
         while (S > 1 && ((K / 128) % S || (K / 128 / S) % 4)) --S;
         if ((K / 128 / S) % 4) return fail(FM_E_UNSUPPORTED, "skinny: two row blocks need K %% 512 == 0 (K %d)", K);
     } else if (nb != 1) {
         return fail(FM_E_INVALID, "skinny: %d row blocks", nb);
     }
-    if (S < 1 || (K / 128) % S || !kw_ok(K / 128 / S))
+    if (!q8 && (S < 1 || (K / 128) % S || !kw_ok(K / 128 / S)))
         return fail(FM_E_UNSUPPORTED, "skinny: no supported k-split for K %d (S %d)", K, S);
     a.ngroups = (int)gs.size();
     a.K = K;
     a.T = T;
     a.S = S;
-    a.KW = K / 128 / S;
+    a.KW = q8 ? 0 : K / 128 / S;
     a.mode = mode;
     a.nb = nb;
     int begin = 0;
@@ -457,7 +483,7 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         const auto& g = gs[i];
         if (g.M % 16) return fail(FM_E_INVALID, "skinny: M %d not a multiple of 16", g.M);
         a.g[i] = SkinnyGroup{g.W, g.Wd, g.W2, g.W2d, g.bias, g.X, g.out, g.M, g.ld, begin, 0};
-        begin += (g.M / 16) * S;
+        begin += (q8 ? ws_groups(g.M, glu) : g.M / 16) * S;   // work-groups of this group
     }
     if (mode == SK_PARTIAL) {
         a.part_stride = pstride > 0 ? pstride : (long long)TMAX * nb * gs[0].M;

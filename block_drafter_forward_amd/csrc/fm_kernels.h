@@ -44,6 +44,11 @@ struct SkinnyArgs {
     long long part_stride;
     int nb;               // blocks of 16 activation rows: 1, or 2 (bf16, KW % 4 == 0; T = 16 rows per block)
 };
+// Q8_0 weights run the tile-owning variant: a work-group of SK_WS_WAVES waves owns that many adjacent 16-row tiles
+// of a group, or for a gated unit half as many tiles of each of its two matrices (tile_begin then counts work-groups:
+// ceil(M / (16 SK_WS_WAVES)) x S per group, twice that for a gated unit) over a k-range of K / S columns (a multiple
+// of 256), sharing one LDS copy of the activation fragments.
+#define SK_WS_WAVES 4
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int n_workgroups, hipStream_t st);
 
 // ── K3: row kernels (residual update + norm + fragment store) ─────────────────────────────────

@@ -2,22 +2,24 @@
 //
 // Computes Y[t][m] = sum_k X[t][k] W[m][k] for the draft's 16 slots (or fewer rows), the product the flow-map page's
 // gemvT17 / gemvT1 kernels and the MTP page's WG_Q8 compute: every weight byte is read from HBM exactly once.
-// Design for CDNA4:
-//   * the weight tile (16 rows x 32 k, 1 KB) is loaded straight into the A operand of v_mfma_f32_16x16x32_bf16:
-//     lane l reads 16 contiguous bytes of row l % 16, so a wave reads 16 rows x 64 contiguous bytes per step;
-//     loads are non-temporal (streamed, never reused);
+// Design for CDNA4, bf16 weights (skinny_kernel):
+//   * the weight tile (16 rows x 32 k, 1 KB) is the A operand of v_mfma_f32_16x16x32_bf16, row-staged through a
+//     wave-private LDS tile (whole cache lines per load instruction); loads are non-temporal (streamed, never reused);
 //   * the activations are the B operand (16 slots = the MFMA's N), pre-split into bf16 hi + lo fragments by their
 //     producer, so one k-step is two MFMAs and the f32 activations keep ~17 significant bits;
-//   * a work-group is 4 waves on one 16-row tile, each wave a contiguous quarter of the k-range; up to 16 k-steps
-//     a wave loads its whole range at once (all of it in flight), longer ranges stream in double-buffered stages;
-//     the four 16x16 partial tiles are summed in LDS in a fixed order (deterministic), then the epilogue runs per
-//     element;
+//   * a work-group is 4 waves on one 16-row tile, each wave a contiguous quarter of the k-range, its next chunk's
+//     weights and fragments in flight while one multiplies; the four 16x16 partial tiles are summed in LDS in a fixed
+//     order (deterministic), then the epilogue runs per element;
 //   * k is split across S work-groups when M alone gives too few work-groups to fill 256 CUs; the S partial slabs
 //     are summed by the consumer kernel in a fixed order.
-// Q8_0 weights (int8 codes + one f16 scale per 32 codes): a k-step is exactly one Q8_0 block, so the codes go
-// through the MFMA exactly (int8 is exact in bf16) and each row's scale multiplies that step's partial product.
+// Q8_0 weights (int8 codes + one f16 scale per 32 codes: the MTP head), skinny_ws_kernel: a k-step is exactly one
+// Q8_0 block, so the codes go through the MFMA exactly (int8 is exact in bf16) and each row's scale multiplies that
+// step's partial product. Here the waves of a work-group own adjacent 16-row tiles and walk their k-range in lockstep,
+// sharing one LDS copy of each chunk's activation fragments (fm_ws.h): a wave reads 4 KB of codes per chunk next to
+// the 16 KB of fragments, so per-wave fragment reads would be four times the HBM bytes.
 #include "fm_device.h"
 #include "fm_kernels.h"
+#include "fm_ws.h"
 
 namespace {
 
@@ -29,40 +31,14 @@ __device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
     v.w = __builtin_nontemporal_load(&((const uint32_t*)p)[3]);
     return v;
 }
-__device__ __forceinline__ uint2 ldg_nt2(const uint2* p) {
-    uint2 v;
-    v.x = __builtin_nontemporal_load(&((const uint32_t*)p)[0]);
-    v.y = __builtin_nontemporal_load(&((const uint32_t*)p)[1]);
-    return v;
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// 8 int8 codes -> 8 bf16 (exact).
-__device__ __forceinline__ uint4 i8x8_to_bf16x8(uint2 c) {
-    uint32_t w[2] = {c.x, c.y};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            int b0 = ((int)(w[i] << (24 - 16 * j))) >> 24;
-            int b1 = ((int)(w[i] << (16 - 16 * j))) >> 24;
-            uint32_t f0 = __float_as_uint((float)b0) >> 16;
-            uint32_t f1 = __float_as_uint((float)b1) & 0xffff0000u;
-            o[2 * i + j] = f0 | f1;
-        }
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
 
 // One pipeline stage: SKC k-steps of the wave's A tiles and B fragments, loaded without any condition (a
 // conditional load makes the compiler wait for every outstanding load before the next MFMA).
 template <int NT, int WT, int SKC>
 struct SkStage {
-    uint4 a[NT][SKC];    // bf16 weights; Q8_0 codes in .x/.y
+    uint4 a[NT][SKC];    // bf16 weights
     uint4 bh[SKC], bl[SKC];
-    float sc[NT][SKC][4];
 };
 
 template <int NT, int WT, int SKC>
@@ -76,23 +52,9 @@ __device__ __forceinline__ void sk_load(SkStage<NT, WT, SKC>& st, const SkinnyGr
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        if constexpr (WT == SKW_BF16) {
-            const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + r) * K;
+        const uint16_t* W = (const uint16_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + r) * K;
 #pragma unroll
-            for (int i = 0; i < SKC; ++i) st.a[n][i] = ldg_nt((const uint4*)(W + kcol(s + i, g)));
-        } else {
-            const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2);
-            const uint16_t* Dd = (const uint16_t*)(n == 0 ? G.Wd : G.W2d);
-            const uint2* cp = (const uint2*)(C + (size_t)(m0 + r) * K + (size_t)s * 32 + g * 8);
-            const int nb = K >> 5;
-#pragma unroll
-            for (int i = 0; i < SKC; ++i) {
-                const uint2 c = ldg_nt2(cp + i * 4);
-                st.a[n][i] = make_uint4(c.x, c.y, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) st.sc[n][i][j] = f16_to_f32(Dd[(size_t)(m0 + 4 * g + j) * nb + s + i]);
-            }
-        }
+        for (int i = 0; i < SKC; ++i) st.a[n][i] = ldg_nt((const uint4*)(W + kcol(s + i, g)));
     }
 }
 
@@ -102,17 +64,8 @@ __device__ __forceinline__ void sk_compute(const SkStage<NT, WT, SKC>& st, f32x4
     for (int i = 0; i < SKC; ++i) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            if constexpr (WT == SKW_BF16) {
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[n][i]), as_bf16x8(st.bh[i]), acc[n], 0, 0, 0);
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[n][i]), as_bf16x8(st.bl[i]), acc[n], 0, 0, 0);
-            } else {
-                const bf16x8_t A = as_bf16x8(i8x8_to_bf16x8(make_uint2(st.a[n][i].x, st.a[n][i].y)));
-                f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bh[i]), p, 0, 0, 0);
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bl[i]), p, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[n][j] += st.sc[n][i][j] * p[j];
-            }
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[n][i]), as_bf16x8(st.bh[i]), acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[n][i]), as_bf16x8(st.bl[i]), acc[n], 0, 0, 0);
         }
     }
 }
@@ -176,85 +129,15 @@ __device__ __forceinline__ void rs_compute(const RsStage<NT, RC, NB>& st, uint4*
     }
 }
 
-// Q8_0 row staging (KW a multiple of 8): a chunk of 8 k-steps is 8 Q8_0 blocks per row -- 256 code bytes (4 rows
-// per 1 KB load instruction) and 8 f16 scales per row (lanes 0-15, one 16-byte load). Codes return from a
-// wave-private LDS tile as the A operand (8 bytes per lane, widened exactly to bf16); the scales sit transposed
-// [step][row] so a lane reads the scales of its 4 output rows for a step in one 8-byte read.
-constexpr int Q8_PITCH = 17;   // uint4 per LDS code row: 16 + 1 pad
-
-template <int NT>
-struct RsStageQ8 {
-    uint4 a[NT][4];
-    uint4 sc[NT];
-    uint4 bh[8], bl[8];
-};
-
-template <int NT>
-__device__ __forceinline__ void rs_load_q8(RsStageQ8<NT>& st, const SkinnyGroup& G, int K, int m0, int s, int lane) {
-    const uint8_t* xb = G.X + (size_t)s * FRAG_STEP_BYTES + lane * 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        st.bh[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES);
-        st.bl[i] = *(const uint4*)(xb + (size_t)i * FRAG_STEP_BYTES + 1024);
-    }
-    const int nb = K >> 5;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int8_t* C = (const int8_t*)(n == 0 ? G.W : G.W2) + (size_t)(m0 + (lane >> 4)) * K + s * 32 + (lane & 15) * 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.a[n][i] = ldg_nt((const uint4*)(C + (size_t)(4 * i) * K));
-        // scales with an ordinary load: a 128-byte line of them serves 8 chunks and must stay in L2 meanwhile
-        st.sc[n] = *(const uint4*)((const uint16_t*)(n == 0 ? G.Wd : G.W2d) + (size_t)(m0 + (lane & 15)) * nb + s);
-    }
-}
-
-template <int NT>
-__device__ __forceinline__ void rs_compute_q8(const RsStageQ8<NT>& st, uint4* lds, uint16_t* slds, f32x4_t* acc,
-                                              int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    __builtin_amdgcn_wave_barrier();   // the previous chunk's LDS reads stay before these writes
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lds[(n * 16 + 4 * i + (lane >> 4)) * Q8_PITCH + (lane & 15)] = st.a[n][i];
-        if (lane < 16) {
-            const uint32_t w[4] = {st.sc[n].x, st.sc[n].y, st.sc[n].z, st.sc[n].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                slds[(n * 8 + 2 * e) * 16 + lane] = (uint16_t)(w[e] & 0xffffu);
-                slds[(n * 8 + 2 * e + 1) * 16 + lane] = (uint16_t)(w[e] >> 16);
-            }
-        }
-    }
-    __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const uint2 cv = ((const uint2*)(lds + (n * 16 + r) * Q8_PITCH))[4 * i + g];
-            const bf16x8_t A = as_bf16x8(i8x8_to_bf16x8(cv));
-            f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bh[i]), p, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(st.bl[i]), p, 0, 0, 0);
-            const uint2 sv = *(const uint2*)(slds + (n * 8 + i) * 16 + 4 * g);
-            acc[n][0] += f16_to_f32((uint16_t)(sv.x & 0xffffu)) * p[0];
-            acc[n][1] += f16_to_f32((uint16_t)(sv.x >> 16)) * p[1];
-            acc[n][2] += f16_to_f32((uint16_t)(sv.y & 0xffffu)) * p[2];
-            acc[n][3] += f16_to_f32((uint16_t)(sv.y >> 16)) * p[3];
-        }
-    }
-}
-
 // UP = 2: row-staged chunks of SKC (8 or 4) k-steps (bf16, KW % SKC == 0), double-buffered, last chunk peeled.
 // UP = 1: the wave's whole k-range (SKC == KW steps) is loaded at once, then multiplied -- every byte of the wave
 // in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
 // stage i computes), with the last pair peeled so the loop body carries no conditions.
-// A single Q8_0 matrix fits two work-groups per CU (<= 256 registers a wave, no scratch); without the bound the
-// compiler spends AGPRs and runs one wave per SIMD. Two matrices at once would spill, so they keep one.
-// NB = 2 (two blocks of 16 activation rows against each weight tile) exists for bf16 with UP = 2 only.
+// NB = 2 (two blocks of 16 activation rows against each weight tile) exists with UP = 2 only.
 template <int NT, int WT, int UP, int SKC, int NB = 1>
-__global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skinny_kernel(SkinnyArgs a) {
-    static_assert(NB == 1 || (WT == SKW_BF16 && UP == 2), "two row blocks: row-staged bf16 only");
+__global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
+    static_assert(WT == SKW_BF16, "bf16 weights (Q8_0: skinny_ws_kernel)");
+    static_assert(NB == 1 || UP == 2, "two row blocks: row-staged only");
     const int bid = blockIdx.x;
     int gi = 0;
 #pragma unroll 1
@@ -278,29 +161,7 @@ __global__ __launch_bounds__(256, (NT == 1 && WT == SKW_Q8_0) ? 2 : 1) void skin
         for (int b = 0; b < NB; ++b) accb[n][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t* acc = &accb[0][0];   // the one-block paths (NB == 1): accb[n][0] is acc[n]
 
-    if constexpr (UP == 2 && WT == SKW_Q8_0) {
-        __shared__ uint4 q8_lds[4][NT * 16 * Q8_PITCH];
-        __shared__ uint16_t q8_slds[4][NT * 8 * 16];
-        uint4* lds = q8_lds[wave];
-        uint16_t* slds = q8_slds[wave];
-        RsStageQ8<NT> c0, c1;
-        const int nch = KW / 8;
-        rs_load_q8<NT>(c0, G, K, m0, s0, lane);
-        int ch = 0;
-        for (; ch + 2 < nch; ch += 2) {
-            rs_load_q8<NT>(c1, G, K, m0, s0 + 8 * (ch + 1), lane);
-            rs_compute_q8<NT>(c0, lds, slds, acc, lane);
-            rs_load_q8<NT>(c0, G, K, m0, s0 + 8 * (ch + 2), lane);
-            rs_compute_q8<NT>(c1, lds, slds, acc, lane);
-        }
-        if (ch + 1 < nch) {
-            rs_load_q8<NT>(c1, G, K, m0, s0 + 8 * (ch + 1), lane);
-            rs_compute_q8<NT>(c0, lds, slds, acc, lane);
-            rs_compute_q8<NT>(c1, lds, slds, acc, lane);
-        } else {
-            rs_compute_q8<NT>(c0, lds, slds, acc, lane);
-        }
-    } else if constexpr (UP == 2) {
+    if constexpr (UP == 2) {
         __shared__ uint4 rs_lds[4][NT * 16 * (4 * SKC + 1)];
         uint4* lds = rs_lds[wave];
         RsStage<NT, SKC, NB> c0, c1;
@@ -407,27 +268,126 @@ hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
         return hipErrorInvalidValue;
     }
     if (a.nb != 1) return hipErrorInvalidValue;
-    if (WT == SKW_BF16 && KW % 4 == 0) {
+    if (KW % 4 == 0) {
         if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
         else skinny_kernel<NT, WT, 2, 4><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }
-    if (WT == SKW_Q8_0 && KW % 8 == 0) {
-        skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
-        return hipGetLastError();
-    }
 #define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n><<<grid, block, 0, st>>>(a); return hipGetLastError();
     switch (KW) {
-        SK_UP(1) SK_UP(2) SK_UP(3) SK_UP(4) SK_UP(5) SK_UP(6) SK_UP(8) SK_UP(10) SK_UP(12) SK_UP(16)
+        SK_UP(1) SK_UP(2) SK_UP(3) SK_UP(5) SK_UP(6) SK_UP(10)
     default: break;
     }
 #undef SK_UP
-    if (KW % 16 == 0) skinny_kernel<NT, WT, 0, 8><<<grid, block, 0, st>>>(a);
-    else if (KW % 8 == 0) skinny_kernel<NT, WT, 0, 4><<<grid, block, 0, st>>>(a);
-    else if (KW % 4 == 0) skinny_kernel<NT, WT, 0, 2><<<grid, block, 0, st>>>(a);
-    else if (KW % 2 == 0) skinny_kernel<NT, WT, 0, 1><<<grid, block, 0, st>>>(a);
+    if (KW > 16 && KW % 2 == 0) skinny_kernel<NT, WT, 0, 1><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+// ── Q8_0: the tile-owning variant ──────────────────────────────────────────────────────────────
+// A work-group is SK_WS_WAVES waves walking columns [split K / S, (split + 1) K / S) in chunks of 256, each chunk's
+// fragments staged once per work-group (fm_ws.h), three chunks in flight per wave. Wave w owns one 16-row tile:
+// tile NW tg + w of its group, or for a gated unit (GLU) tile NW / 2 tg + w / 2 of the gate (w even) or of the up
+// matrix (w odd), the pair combined through LDS at the end. Tail waves of a group's last work-group redo its last
+// tile, their results dropped. Each wave's 16 x 16 tile is complete for its k-range, so no sum over waves: the
+// epilogue goes straight from the accumulator (SK_PARTIAL: the split's slab).
+template <bool GLU>
+__global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyArgs a) {
+    constexpr int NW = SK_WS_WAVES, TPW = GLU ? NW / 2 : NW;   // tiles per work-group (of each matrix)
+    __shared__ uint4 alds_all[NW][16 * ws::Q8_PITCH];
+    __shared__ uint16_t slds_all[NW][128];
+    __shared__ uint4 blds_all[3][1024];
+    __shared__ float tile_all[NW][16][17];
+    const int bid = blockIdx.x;
+    int gi = 0;
+#pragma unroll 1
+    for (int i = 1; i < a.ngroups; ++i)
+        if (bid >= a.g[i].tile_begin) gi = i;
+    const SkinnyGroup& G = a.g[gi];
+    const int local = bid - G.tile_begin;
+    const int tg = local / a.S, split = local - tg * a.S;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ntile = G.M / 16, mt = tg * TPW + (GLU ? wave >> 1 : wave);
+    const bool own = mt < ntile;
+    const int m0 = min(mt, ntile - 1) * 16;
+    const bool up = GLU && (wave & 1);
+    const int K = a.K, kc = K / a.S, c0 = split * kc, nch = kc >> 8;
+    const int8_t* const Ct[1] = {(const int8_t*)(up ? G.W2 : G.W) + (size_t)m0 * K + c0};
+    const uint16_t* const Dt[1] = {(const uint16_t*)(up ? G.W2d : G.Wd) + (size_t)m0 * (K >> 5) + (c0 >> 5)};
+    const uint8_t* X = G.X + (size_t)(c0 >> 5) * FRAG_STEP_BYTES;
+    uint4* alds = alds_all[wave];
+    uint16_t* slds = slds_all[wave];
+    f32x4_t acc[1][1] = {{f32x4_t{0.f, 0.f, 0.f, 0.f}}};
+    using Regs = ws::RegsQ8<NW, 1>;
+    auto load = [&](Regs& r, int ch) {   // nothing past the last chunk (a uniform branch)
+        if (ch < nch) ws::load_q8<NW, 1>(r, Ct, Dt, K, X, ch, tid);
+        __builtin_amdgcn_sched_barrier(0);   // each chunk's loads stay together (one wait per chunk)
+    };
+    // chunk c is staged into slab c % 3: written after the barrier that follows the multiply of chunk c - 3
+    auto step = [&](Regs& r, int c, int buf) {
+        ws::stage_q8<NW, 1>(r, alds, slds, blds_all[buf], tid);
+        load(r, c + 3);
+        __syncthreads();
+        ws::compute_q8<1>(alds, slds, blds_all[buf], acc, lane);
+    };
+    Regs r0, r1, r2;
+    load(r0, 0);
+    load(r1, 1);
+    load(r2, 2);
+    int ch = 0;
+    for (; ch + 3 <= nch; ch += 3) {
+        step(r0, ch, 0);
+        step(r1, ch + 1, 1);
+        step(r2, ch + 2, 2);
+    }
+    if (ch < nch) step(r0, ch, 0);
+    if (ch + 1 < nch) step(r1, ch + 1, 1);
+
+    // lane holds Y[t = lane % 16][m0 + 4 g + j]
+    const int t = lane & 15, g = lane >> 4, mc = m0 + 4 * g;
+    if (!GLU && (a.mode == SK_F32 || a.mode == SK_PARTIAL)) {
+        if (!own || t >= a.T) return;
+        float4 o = make_float4(acc[0][0][0], acc[0][0][1], acc[0][0][2], acc[0][0][3]);
+        float* dst = (float*)G.out + (size_t)t * G.ld + mc;
+        if (a.mode == SK_PARTIAL) {
+            dst += (size_t)split * a.part_stride;
+        } else if (G.bias) {
+            o.x += bf16_to_f32(G.bias[mc]);
+            o.y += bf16_to_f32(G.bias[mc + 1]);
+            o.z += bf16_to_f32(G.bias[mc + 2]);
+            o.w += bf16_to_f32(G.bias[mc + 3]);
+        }
+        *(float4*)dst = o;
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile_all[wave][t][4 * g + j] = acc[0][0][j];
+    if constexpr (GLU) {
+        __syncthreads();   // the up tile of the pair is in its wave's LDS
+        if (up) return;
+        const float(*ut)[17] = tile_all[wave + 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = tile_all[wave][t][4 * g + j], u = ut[t][4 * g + j];
+            tile_all[wave][t][4 * g + j] = a.mode == SK_FRAG_GEGLU ? gelu_tanh(v) * u : silu(v) * u;
+        }
+    } else {   // SK_FRAG_GELU
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = tile_all[wave][t][4 * g + j];
+            tile_all[wave][t][4 * g + j] = gelu_erf(v + (G.bias ? bf16_to_f32(G.bias[mc + j]) : 0.f));
+        }
+    }
+    __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
+    if (lane < 32 && own) {
+        const int tt = lane >> 1, h = lane & 1;
+        if (tt < a.T) {
+            float vals[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vals[e] = tile_all[wave][tt][8 * h + e];
+            frag_store8((uint8_t*)G.out, tt, m0 + 8 * h, vals);
+        }
+    }
 }
 
 }  // namespace
@@ -435,5 +395,13 @@ hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st) {
     const bool glu = (a.mode == SK_FRAG_GEGLU || a.mode == SK_FRAG_SWIGLU);
     if (wtype == SKW_BF16) return glu ? launch_nt<2, SKW_BF16>(a, nwg, st) : launch_nt<1, SKW_BF16>(a, nwg, st);
-    return glu ? launch_nt<2, SKW_Q8_0>(a, nwg, st) : launch_nt<1, SKW_Q8_0>(a, nwg, st);
+    // Q8_0: whole chunks of 256 columns per split, one block of at most 16 rows, whole slabs (SK_F32 / FRAG: S = 1)
+    if (a.nb != 1 || a.T < 1 || a.T > 16 || a.S < 1 || a.K % (256 * a.S) ||
+        (a.mode != SK_PARTIAL && a.S != 1))
+        return hipErrorInvalidValue;
+    for (int i = 0; i < a.ngroups; ++i)
+        if (a.g[i].M % 16 || !a.g[i].Wd || (glu && !a.g[i].W2d)) return hipErrorInvalidValue;
+    if (glu) skinny_ws_kernel<true><<<nwg, SK_WS_WAVES * 64, 0, st>>>(a);
+    else skinny_ws_kernel<false><<<nwg, SK_WS_WAVES * 64, 0, st>>>(a);
+    return hipGetLastError();
 }
