@@ -182,6 +182,24 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     rows["flashmap_batch2"] = row
     del d2
 
+    # the same draft step on the persistent schedule (every phase of the draft in one launch; the automatic schedule
+    # is one launch per phase, the faster of the two)
+    if d.draft_path == "launches":
+        try:
+            d.set_draft_path("persistent")
+        except fm.FmError:
+            pass
+    if d.draft_path == "persistent":
+        def pstep():
+            d.fm_draft_block(hid, anchor=an, pos=n)
+            d.fm_lm_argmax(hid, T, tok)
+        ms = _time_ms(torch, _graph_of(torch, pstep), 5, reps)
+        d.device_status()
+        rows["flashmap_draft_persistent"] = _hbm_row("FlashMap draft block + lm_head argmax, the draft as one persistent "
+                                                     "launch (fm_set_draft_path 2)", ms, draft_step_bytes(cfg, n + 1),
+                                                     "draft blocks/s")
+        d.set_draft_path("auto")
+
     # 512-row prefill on the FlashMap shape
     tp = torch.from_numpy(gen.taps(cfg, "prefill", n)).cuda()
     ms = _time_ms(torch, lambda: d.fm_context_append(tp, 0), 2, 10)
