@@ -14,7 +14,9 @@ unpinned beyond that reading; the formula is pinned against PyTorch's tanh-appro
 Markov decode (forwardRows' greedy loop with the Markov head, #markov, #confidence): with block = RMSNorm(H_d;
 out_norm) and base logits z = (block out_proj) E^T, step k takes e1 = w1[prev] (prev = the anchor, then the
 previous step's token), scores_k = z_k + e1 w2, token_k = argmax scores_k and conf_k = sigmoid([block_k; e1] conf.w
-+ conf.b). draft_block/lm_argmax alone are the page's parallel route (w2 = 0, its initialisation).
++ conf.b). draft_block/lm_argmax alone are the page's parallel route (w2 = 0, its initialisation). Confidence pruning
+(forwardRows' thresholds / minConf): a step k >= 1 whose confidence is below its threshold drops position k and ends
+the block.
 """
 from __future__ import annotations
 
@@ -109,11 +111,14 @@ class KVInjectOracle:
         z = P.linear(hidden, self.w("lm_head.weight"))
         return P.argmax_rows(z), z
 
-    def markov_decode(self, block_n: np.ndarray, hidden: np.ndarray, anchor: int, follow=None):
+    def markov_decode(self, block_n: np.ndarray, hidden: np.ndarray, anchor: int, follow=None, thresholds=None):
         """Greedy decode with the Markov correction and the confidence head over the rows of one block: block_n the
         normed backbone rows [gamma][dDraft], hidden = out_proj(block_n) [gamma][Ht]. follow (optional): tokens to
         condition the next step on instead of this oracle's own argmax (a device run that took the other side of a
-        near-tie). Returns (tokens, scores [gamma][V], conf [gamma])."""
+        near-tie). thresholds (optional, gamma values): confidence pruning as DF forwardRows does it with
+        thresholds / minConf -- after step k >= 1 has its token and confidence, a confidence below thresholds[k]
+        drops position k and ends the block (position 0 is always kept). Returns (tokens, scores, conf) over the
+        positions kept."""
         z = P.linear(hidden, self.w("lm_head.weight"))
         w1, w2 = self.w("markov.w1"), self.w("markov.w2")
         cw, cb = self.w("conf.w")[:, 0], self.w("conf.b")[0]
@@ -126,5 +131,7 @@ class KVInjectOracle:
             toks.append(t)
             scores.append(s)
             conf.append(P.sigmoid(np.concatenate([block_n[k], e1]) @ cw + cb))
+            if thresholds is not None and k > 0 and conf[k] < thresholds[k]:
+                return np.array(toks[:k]), np.stack(scores[:k]), np.array(conf[:k])
             prev = t if follow is None else int(follow[k])
         return np.array(toks), np.stack(scores), np.array(conf)

@@ -322,6 +322,30 @@ def test_markov_decode_identical_rows_remove_the_chain():
     assert np.array_equal(t2, t) and np.array_equal(sc2, sc)
 
 
+def test_markov_decode_pruning_cuts_at_the_first_low_confidence():
+    # DF forwardRows' pruning only shortens the block: the kept positions are the unpruned decode's first positions,
+    # cut at the first k >= 1 whose confidence is below thresholds[k]; position 0 is never cut; thresholds that no
+    # sigmoid reaches cut where they stand, thresholds of zero never cut.
+    cfg, W, o, out = _markov_setup()
+    g = cfg["block"]
+    t, sc, conf = o.markov_decode(o.block_n, out, anchor=11)
+    assert len(t) == g
+    tz, _, _ = o.markov_decode(o.block_n, out, anchor=11, thresholds=[0.0] * g)
+    assert np.array_equal(tz, t)
+    for j in range(1, g):
+        thr = [0.0] * g
+        thr[j] = 1.0   # above any sigmoid
+        tj, scj, cj = o.markov_decode(o.block_n, out, anchor=11, thresholds=thr)
+        assert len(tj) == j and np.array_equal(tj, t[:j]) and np.array_equal(scj, sc[:j]) and np.array_equal(cj, conf[:j])
+    t0, _, _ = o.markov_decode(o.block_n, out, anchor=11, thresholds=[1.0] + [0.0] * (g - 1))
+    assert len(t0) == g   # a threshold at position 0 is never applied
+    for m in sorted(set(conf[1:])):   # a uniform minConf at each confidence value and just above it
+        for thrv in (m, np.nextafter(m, 2.0)):
+            want = next((k for k in range(1, g) if conf[k] < thrv), g)
+            tm, _, _ = o.markov_decode(o.block_n, out, anchor=11, thresholds=[thrv] * g)
+            assert len(tm) == want and np.array_equal(tm, t[:want])
+
+
 def test_kvinject_cached_route_equals_reprojection():
     # The page: the context projection is independent of the block and can be retained.
     cfg = KV_MICRO
