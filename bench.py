@@ -257,6 +257,18 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
     rows["kvinject_draft_markov"] = _hbm_row("KV-injection draft + Markov-corrected greedy decode and confidence "
                                              "(gamma 5, rank 256)", ms,
                                              kbytes + g * (rk * Vk * 2 + 2 * Vk * 4 + rk * 2), "draft blocks/s")
+    # the same with confidence pruning that ends the block at position 2 (thresholds 0, 0, 1, 0, 0): the decode
+    # steps of the dropped positions do no work
+    thr = [0.0, 0.0, 1.0] + [0.0] * (g - 3)
+    lenk = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def mpstep():
+        dk.fm_draft_block(hk, anchor=ak)
+        dk.fm_markov_argmax(hk, g, ak, rk, tkk, cfk, thresholds=thr, length=lenk)
+    ms = _time_ms(torch, _graph_of(torch, mpstep), 5, reps)
+    rows["kvinject_draft_markov_pruned_at_2"] = _hbm_row(
+        "KV-injection draft + Markov decode with confidence pruning that keeps 2 of 5 positions (the other steps "
+        "skip the correction table)", ms, kbytes + 2 * (rk * Vk * 2 + 2 * Vk * 4 + rk * 2), "draft blocks/s")
     # three requests with their own 2048-row contexts drafted in one pass (fm_draft_batch) + the lm_head over the 15
     # rows: the weights stream once for all three blocks
     Bq = 3

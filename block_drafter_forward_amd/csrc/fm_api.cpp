@@ -169,10 +169,11 @@ DraftLayout draft_layout(const fm_config& c, int G) {
 
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
-    size_t best, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
+    size_t best, mcut, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
         pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
         rscale, modc, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
+    int best_rows;           // argmax keys (one per row)
     size_t part_floats;      // capacity of the partial buffer
     size_t attnp_bytes;      // capacity of the attention partial buffer
     int rope_rows, rope_dims;
@@ -210,7 +211,9 @@ Plan make_plan(const fm_config& c) {
     const int D = c.dim;
     const bool fmv = c.variant == FM_VARIANT_FLOWMAP;
     const int RB = fmv ? FM_BATCH * TMAX : TMAX;   // rows of the block buffers (flow-map: two batched requests)
+    p.best_rows = RB;
     p.best = take((size_t)RB * sizeof(unsigned long long));
+    p.mcut = take(c.variant == FM_VARIANT_KVINJECT ? 4 : 0);   // the Markov decode's pruning cut (zero between calls)
     p.zeros_bytes = (size_t)std::max({kmax_frag(c), 2 * c.dim, c.target_dim, 256}) * 4;
     p.zeros = take(p.zeros_bytes);
     p.rope_dims = c.rope == FM_ROPE_NEOX ? c.rope_dims : c.head_dim;
@@ -1491,7 +1494,14 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
     hipStream_t st = (hipStream_t)stream;
     fm_status s = FM_OK;
     do {
-        if (launch_fill_u32(d->at<uint32_t>(d->p.best), 32, 0u, st) != hipSuccess) { s = fail(FM_E_HIP, "fill"); break; }
+        if (launch_fill_u32(d->at<uint32_t>(d->p.best), 2 * (size_t)d->p.best_rows, 0u, st) != hipSuccess) {
+            s = fail(FM_E_HIP, "fill");
+            break;
+        }
+        if (cfg->variant == FM_VARIANT_KVINJECT && launch_fill_u32(d->at<uint32_t>(d->p.mcut), 1, 0u, st) != hipSuccess) {
+            s = fail(FM_E_HIP, "fill");
+            break;
+        }
         if (launch_fill_u32(d->at<uint32_t>(d->p.zeros), d->p.zeros_bytes / 4, 0u, st) != hipSuccess) {
             s = fail(FM_E_HIP, "fill");
             break;
@@ -1647,7 +1657,8 @@ fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t s
 }
 
 fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, const int32_t* anchor, int32_t rank,
-                           int32_t* tokens, float* conf, float* scores, void* stream) {
+                           int32_t* tokens, float* conf, float* scores, const float* thresholds, int32_t* length,
+                           void* stream) {
     g_err.clear();
     if (!d || !hidden || !anchor || !tokens || !conf) return fail(FM_E_INVALID, "null argument");
     const auto& c = d->c;
@@ -1676,6 +1687,10 @@ fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, con
     a.V = c.vocab;
     a.r = rank;
     a.D = c.dim;
+    a.prune = thresholds ? 1 : 0;
+    for (int k = 0; thresholds && k < rows; ++k) a.thr[k] = thresholds[k];
+    a.cut = d->at<int32_t>(d->p.mcut);
+    a.length = length;
     HIPCHK(launch_markov(a, rows, st));   // the keys of rows [0, rows) were cleared by the lm_head's finalize
     return FM_OK;
 }

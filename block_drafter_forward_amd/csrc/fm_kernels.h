@@ -262,9 +262,14 @@ struct MarkovArgs {
     float* scores;         // optional [rows][V]
     unsigned long long* key;  // [rows]: step k's argmax key; zero between calls
     int V, r, D;
+    int prune;             // 1: confidence pruning with thr[] (positions k >= 1 with conf < thr[k] end the block)
+    float thr[16];
+    int32_t* cut;          // device [1]: the step that ended the block, 0 while none has; zero between calls
+    int32_t* length;       // optional device [1]: positions kept
 };
 // The decode steps 0 .. rows - 1 (rows <= 16), step k's argmax in key[k] (key[0 .. rows) zero on entry, zero again
-// on exit).
+// on exit). With pruning, a step whose confidence falls below its threshold ends the block there: it and every later
+// step do no work, their tokens are -1 and their confidences 0.
 hipError_t launch_markov(const MarkovArgs& a, int rows, hipStream_t st);
 
 // ── K2: MFMA prefill GEMM (f16 operands, f32 accumulate) ──────────────────────────────────────

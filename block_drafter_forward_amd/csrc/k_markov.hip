@@ -30,18 +30,24 @@ __device__ __forceinline__ int markov_prev(const MarkovArgs& a, int k) {
     return min(max(p, 0), a.V - 1);
 }
 
-// step j's token (from its key) and confidence sigmoid([block_j; e1] conf.w + conf.b), e1 the w1 row of the token
-// step j conditioned on; the whole work-group takes part
-__device__ void markov_close(const MarkovArgs& a, int j, float* red) {
+// step j's confidence sigmoid([block_j; e1] conf.w + conf.b), e1 the w1 row of the token step j conditioned on;
+// the whole work-group takes part and every thread gets it (the same value in every work-group: same order of sums)
+__device__ float markov_conf(const MarkovArgs& a, int j, float* red) {
     const int tid = threadIdx.x;
     const int prev = markov_prev(a, j);
     float s = 0.f;
     for (int i = tid; i < a.D; i += 256) s += a.block[(size_t)j * a.D + i] * bf16_to_f32(a.cw[i]);
     for (int i = tid; i < a.r; i += 256) s += bf16_to_f32(a.w1[(size_t)prev * a.r + i]) * bf16_to_f32(a.cw[a.D + i]);
     s = block_sum256(s, red);
-    if (tid == 0) {
+    return 1.f / (1.f + expf(-(s + bf16_to_f32(a.cb[0]))));
+}
+
+// step j's token (from its key) and confidence
+__device__ void markov_close(const MarkovArgs& a, int j, float* red) {
+    const float c = markov_conf(a, j, red);
+    if (threadIdx.x == 0) {
         a.tokens[j] = key_token(a.key[j]);
-        a.conf[j] = 1.f / (1.f + expf(-(s + bf16_to_f32(a.cb[0]))));
+        a.conf[j] = c;
     }
 }
 
@@ -51,6 +57,18 @@ __global__ __launch_bounds__(256) void markov_step_kernel(MarkovArgs a, int k) {
     __shared__ int wi[4];
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (a.prune && k > 0) {
+        // DFlash pruning: position k is dropped, and the block ends, when its confidence (which needs only the token
+        // step k - 1 chose) is below thr[k]; then neither this step nor a later one streams the correction table
+        if (*a.cut) return;   // an earlier step ended the block
+        if (markov_conf(a, k, red) < a.thr[k]) {
+            if (blockIdx.x == 0) {
+                markov_close(a, k - 1, red);   // position k - 1 is kept
+                if (tid == 0) *a.cut = k;
+            }
+            return;
+        }
+    }
     const int prev = markov_prev(a, k);
     for (int j = tid; j < a.r; j += 256) e1[j] = bf16_to_f32(a.w1[(size_t)prev * a.r + j]);
     __syncthreads();
@@ -109,18 +127,28 @@ __global__ __launch_bounds__(256) void markov_step_kernel(MarkovArgs a, int k) {
     if (k > 0 && blockIdx.x == 0) markov_close(a, k - 1, red);   // the previous step's token and confidence
 }
 
-// The last step's token and confidence, then every step's key cleared for the next call.
+// The last step's token and confidence (unless pruning ended the block earlier: then the dropped positions get
+// token -1 and confidence 0), the kept length, then every step's key and the cut cleared for the next call.
 __global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs a, int last) {
     __shared__ float red[4];
-    markov_close(a, last, red);
+    const int cut = a.prune ? *a.cut : 0;   // uniform
+    if (cut == 0) markov_close(a, last, red);
     __syncthreads();
-    if ((int)threadIdx.x <= last) a.key[threadIdx.x] = 0ull;
+    const int t = threadIdx.x;
+    if (cut > 0 && t >= cut && t <= last) {
+        a.tokens[t] = -1;
+        a.conf[t] = 0.f;
+    }
+    if (t == 0 && a.length) *a.length = cut > 0 ? cut : last + 1;
+    if (t <= last) a.key[t] = 0ull;
+    if (t == 0 && a.prune) *a.cut = 0;
 }
 
 }  // namespace
 
 hipError_t launch_markov(const MarkovArgs& a, int rows, hipStream_t st) {
-    if (a.r < 1 || a.r > MARKOV_MAX_RANK || a.V < 4 || a.V % 4 || rows < 1 || rows > 16) return hipErrorInvalidValue;
+    if (a.r < 1 || a.r > MARKOV_MAX_RANK || a.V < 4 || a.V % 4 || rows < 1 || rows > 16 || (a.prune && !a.cut))
+        return hipErrorInvalidValue;
     for (int k = 0; k < rows; ++k) {
         markov_step_kernel<<<(a.V / 4 + 255) / 256, 256, 0, st>>>(a, k);
         const hipError_t e = hipGetLastError();

@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.fm_lm_argmax_static.restype = ctypes.c_int
         L.fm_mtp_chain.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         L.fm_mtp_chain.restype = ctypes.c_int
-        L.fm_markov_argmax.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp]
+        L.fm_markov_argmax.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_float), vp, vp]
         L.fm_markov_argmax.restype = ctypes.c_int
         L.fm_time_condition.argtypes = [vp, ctypes.c_float, ctypes.c_float, i32, i32, ctypes.c_float, vp, vp]
         L.fm_time_condition.restype = ctypes.c_int
@@ -227,10 +227,16 @@ class Drafter:
         check(self.L.fm_mtp_chain(self.h, tokens.data_ptr(), h.data_ptr(), steps, pos, kv_lo, hidden_out.data_ptr(),
                                   _stream_ptr(stream)))
 
-    def fm_markov_argmax(self, hidden, rows: int, anchor, rank: int, tokens, conf, scores=None, stream=None):
+    def fm_markov_argmax(self, hidden, rows: int, anchor, rank: int, tokens, conf, scores=None, thresholds=None,
+                         length=None, stream=None):
+        """thresholds: None, or rows floats (host): the minimum confidence to keep each position (pruning);
+        length: None, or a device int32 tensor [1] that receives the positions kept."""
+        thr = None
+        if thresholds is not None:
+            thr = (ctypes.c_float * rows)(*[float(v) for v in thresholds])
         check(self.L.fm_markov_argmax(self.h, hidden.data_ptr(), rows, anchor.data_ptr(), rank, tokens.data_ptr(),
                                       conf.data_ptr(), scores.data_ptr() if scores is not None else None,
-                                      _stream_ptr(stream)))
+                                      thr, length.data_ptr() if length is not None else None, _stream_ptr(stream)))
 
     def fm_time_condition(self, s: float, t: float, time_dim: int, cond_dim: int, time_scale: float, table_out=None,
                           stream=None):

@@ -206,11 +206,17 @@ fm_status fm_mtp_chain(fm_drafter* d, int32_t* tokens, const float* h, int32_t s
  *   weights (named at fm_create): markov.w1 bf16 [vocab][rank], markov.w2 bf16 [rank][vocab],
  *            conf.w bf16 [dim + rank], conf.b bf16 [1]
  *   anchor   device int32 [1]; tokens, conf device [rows]; scores nullable device f32 [rows][vocab] (debug)
- * Confidence pruning (truncating the block where conf drops below a threshold) is the caller's decision.
+ * Confidence pruning (forwardRows with thresholds / minConf): thresholds, if not NULL, is a host float [rows], the
+ * minimum confidence to keep each position (a uniform minConf is every entry equal). Position 0 is always kept;
+ * at the first r >= 1 with conf[r] < thresholds[r] the block ends: positions r .. rows - 1 are dropped (tokens -1,
+ * conf 0) and their decode steps do no work (the correction table is not streamed for them; the decision is taken
+ * on the device, no host synchronisation). length, if not NULL, receives on the device the positions kept (rows
+ * without a cut). With thresholds NULL every position is decoded.
  * Errors: FM_E_INVALID (null pointers, not a KV-injection drafter, rows outside [1, block], rank outside [1, 1024],
  * missing weights), FM_E_UNSUPPORTED (vocab % 4 != 0). */
 fm_status fm_markov_argmax(fm_drafter* d, const float* hidden, int32_t rows, const int32_t* anchor, int32_t rank,
-                           int32_t* tokens, float* conf, float* scores, void* stream);
+                           int32_t* tokens, float* conf, float* scores, const float* thresholds, int32_t* length,
+                           void* stream);
 
 /* Time conditioning of the flow-map jump s -> t (flashmap_drafter.js timeConditioning, the model's
  * time_conditioning): sinusoidal embeddings of s and t (time_dim values, frequencies 10000^(-i / (time_dim / 2)),

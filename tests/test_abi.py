@@ -82,7 +82,7 @@ def test_later_entry_points_reject_bad_arguments_on_the_host():
     # chained MTP depth, Markov decode, time conditioning and batched drafts validate before any launch
     L = _lib()
     assert L.fm_mtp_chain(None, 0x1000, 0x2000, 3, 0, 0, 0x3000, None) == fm.FM_E_INVALID
-    assert L.fm_markov_argmax(None, 0x1000, 5, 0x2000, 256, 0x3000, 0x4000, None, None) == fm.FM_E_INVALID
+    assert L.fm_markov_argmax(None, 0x1000, 5, 0x2000, 256, 0x3000, 0x4000, None, None, None, None) == fm.FM_E_INVALID
     assert L.fm_time_condition(None, 0.0, 1.0, 256, 256, 1000.0, None, None) == fm.FM_E_INVALID
     assert L.fm_lm_argmax_static(None, 0x1000, 5, 0x2000, None) == fm.FM_E_INVALID
     assert L.fm_set_draft_path(None, 0) == fm.FM_E_INVALID

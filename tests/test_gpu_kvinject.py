@@ -131,6 +131,35 @@ def test_kvinject_markov_decode(name):
         d.fm_markov_argmax(hid, T + 1, a, cfg["markov_rank"], tok, conf)
     assert ex.value.status == fm.FM_E_INVALID
 
+    # confidence pruning (DF forwardRows' thresholds / minConf), decided on the device: the kept positions are the
+    # unpruned decode's prefix; dropped ones read token -1 and confidence 0; the kept count lands in `length`.
+    # Thresholds of 0 never cut and 1.0 (above any sigmoid) always cuts where it stands, so the cut does not hinge on
+    # rounding; a uniform minConf halfway between two well-separated device confidences cuts where the oracle's
+    # confidences (within 1e-4 of the device's) say it does.
+    gc = conf.cpu().numpy()
+    length = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cases = [[0.0] * T] + [[0.0] * j + [1.0] + [0.0] * (T - j - 1) for j in range(1, T)]
+    srt = sorted(set(gc[1:].tolist()))
+    for lo, hi in zip(srt, srt[1:]):
+        if hi - lo > 1e-3:
+            cases.append([(lo + hi) / 2] * T)
+    for thr in cases:
+        tp = torch.full((T,), 7, dtype=torch.int32, device="cuda")
+        cp = torch.full((T,), 7.0, dtype=torch.float32, device="cuda")
+        d.fm_markov_argmax(hid, T, a, cfg["markov_rank"], tp, cp, thresholds=thr, length=length)
+        torch.cuda.synchronize()
+        ot_p, _, oc_p = o.markov_decode(o.block_n, out, an, follow=gt, thresholds=thr)
+        n_keep = int(length.item())
+        assert n_keep == len(ot_p), (thr, n_keep, len(ot_p))
+        assert np.array_equal(tp.cpu().numpy()[:n_keep], gt[:n_keep])
+        assert np.array_equal(cp.cpu().numpy()[:n_keep], gc[:n_keep])
+        assert np.all(tp.cpu().numpy()[n_keep:] == -1) and np.all(cp.cpu().numpy()[n_keep:] == 0.0)
+    _say(f"{name}: pruning: {len(cases)} threshold sets, kept lengths checked against the oracle")
+    # after pruned calls, an unpruned call decodes every position again
+    d.fm_markov_argmax(hid, T, a, cfg["markov_rank"], tok, conf, length=length)
+    torch.cuda.synchronize()
+    assert int(length.item()) == T and np.array_equal(tok.cpu().numpy(), gt)
+
 
 @pytest.mark.parametrize("name", ["small", "kvinject"])
 def test_kvinject_batched_requests(name):
