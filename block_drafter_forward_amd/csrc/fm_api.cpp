@@ -167,11 +167,18 @@ DraftLayout draft_layout(const fm_config& c, int G) {
     return L;
 }
 
+// c1 / c2 of the LayerNorm fold (flow-map): per layer [q, k, v, cross q: 2 dim each][fc1: 2 ffn], then the head
+// (2 target_dim); layer 0's first four are unused (its self-attention and cross q are cached at create)
+size_t c12_floats(const fm_config& c) { return (size_t)c.layers * 2 * (4 * c.dim + c.ffn) + 2 * (size_t)c.target_dim; }
+size_t c12_off(const fm_config& c, int l, int which) {   // which 0..3: q k v cross-q, 4: fc1; l == layers: head
+    return (size_t)l * 2 * (4 * c.dim + c.ffn) + (size_t)2 * c.dim * which;
+}
+
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, mcut, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
         pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
-        rscale, modc, dargs, dlayers, dsync, arena, total;
+        rscale, modc, lnstats, c12, lnfrag, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
     int best_rows;           // argmax keys (one per row)
     size_t part_floats;      // capacity of the partial buffer
@@ -274,6 +281,12 @@ Plan make_plan(const fm_config& c) {
     // the handle's own modulation table (copied from the caller's at create, rewritten by time conditioning): the
     // layer-0 projections cached at create follow this table, so no other handle can change it under them
     p.modc = take(fmv ? (size_t)(3 * c.layers + 1) * 3 * c.dim * 4 : 0);
+    // the LayerNorm fold of the flow-map draft: (mean, M2) of each 16-column tile of the residual rows (written by
+    // each residual update, read by the next product), c1 / c2 of every product that takes a LayerNorm-modulated
+    // row (layer l: q, k, v, cross q, fc1; then the head), and the fragments of the modulation rows they come from
+    p.lnstats = take(fmv ? (size_t)(c.dim / 16) * FM_BATCH * TMAX * 8 : 0);
+    p.c12 = take(fmv ? c12_floats(c) * 4 : 0);
+    p.lnfrag = take(fmv ? (size_t)(3 * c.layers + 1) * c.dim * 64 : 0);
     // the persistent draft kernel: its arguments and per-layer table (device copies), its barrier counters and its
     // activation arena (sized for the most work-groups it may run with)
     const bool pk = draft_supported(c);
@@ -316,6 +329,8 @@ fm_status validate_config(const fm_config* c) {
             return fail(FM_E_UNSUPPORTED, "tap width %d > %d", c->n_taps * c->target_dim, TAPS_MAX_WIDTH);
         if (c->max_ctx % 32) return fail(FM_E_INVALID, "an f16 cache needs max_ctx %% 32 == 0 (V is tiled by 32)");
         if (c->kv_heads != c->heads) return fail(FM_E_UNSUPPORTED, "the flow-map drafter has one K/V head per head");
+        if (c->dim > 16 * LN_MAX_TILES)   // the LayerNorm fold's statistics: at most LN_MAX_TILES tiles per row
+            return fail(FM_E_UNSUPPORTED, "flow-map dim %d > %d", c->dim, 16 * LN_MAX_TILES);
         break;
     case FM_VARIANT_KVINJECT:
         if (c->rope != FM_ROPE_NONE || c->mlp != FM_MLP_GEGLU_TANH || c->wtype != FM_W_BF16 ||
@@ -435,6 +450,23 @@ struct SkGroupDesc {
     void* out;
     int M;
     int ld;
+    const float* c12 = nullptr;   // the LayerNorm fold's c1 / c2 of this group
+};
+
+// Optional epilogue work of a skinny launch (SkinnyArgs): the LayerNorm fold of a product whose input is a
+// LayerNorm-modulated row (ln_stats), or the residual update of SK_RESID.
+struct SkExtra {
+    const float* ln_stats = nullptr;
+    int ln_tiles = 0;
+    float ln_eps = 0.f;
+    float* rx = nullptr;
+    int rx_ld = 0;
+    const float* rbase = nullptr;
+    int rbase_ld = 0;
+    const float* rgate = nullptr;
+    const float* ryscale = nullptr;
+    float* rstats = nullptr;
+    float* rdebug = nullptr;
 };
 
 // Enqueue one skinny launch. For SK_PARTIAL the k-split is chosen here (returned through S_out); every other mode
@@ -444,7 +476,8 @@ struct SkGroupDesc {
 // nb = 2: two blocks of 16 activation rows (rows 16 b + t of the outputs; fragments of block b at X + b * K * 64),
 // each weight tile multiplied against both; the k-split then keeps k-steps per wave a multiple of 4.
 fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K, int T, int mode, int S_force,
-                 int* S_out, hipStream_t st, long long pstride = 0, size_t cap_floats = 0, int nb = 1) {
+                 int* S_out, hipStream_t st, long long pstride = 0, size_t cap_floats = 0, int nb = 1,
+                 const SkExtra* ex = nullptr) {
     if (gs.empty() || gs.size() > SK_MAX_GROUPS) return fail(FM_E_INVALID, "skinny: %zu groups", gs.size());
     if (K % 128) return fail(FM_E_INVALID, "skinny: K %d not a multiple of 128", K);
     SkinnyArgs a{};
@@ -481,11 +514,27 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
     a.KW = q8 ? 0 : K / 128 / S;
     a.mode = mode;
     a.nb = nb;
+    a.zeros = d->at<float>(d->p.zeros);
+    if (ex) {
+        a.ln_stats = ex->ln_stats;
+        a.ln_tiles = ex->ln_tiles;
+        a.ln_inv = ex->ln_tiles > 0 ? 1.f / (float)ex->ln_tiles : 0.f;
+        a.ln_eps = ex->ln_eps;
+        a.rx = ex->rx;
+        a.rx_ld = ex->rx_ld;
+        a.rbase = ex->rbase;
+        a.rbase_ld = ex->rbase_ld;
+        a.rgate = ex->rgate;
+        a.ryscale = ex->ryscale;
+        a.rstats = ex->rstats;
+        a.rdebug = ex->rdebug;
+    }
+    if (mode == SK_RESID && (S != 1 || !ex)) return fail(FM_E_INVALID, "skinny: a residual update runs unsplit");
     int begin = 0;
     for (size_t i = 0; i < gs.size(); ++i) {
         const auto& g = gs[i];
         if (g.M % 16) return fail(FM_E_INVALID, "skinny: M %d not a multiple of 16", g.M);
-        a.g[i] = SkinnyGroup{g.W, g.Wd, g.W2, g.W2d, g.bias, g.X, g.out, g.M, g.ld, begin, 0};
+        a.g[i] = SkinnyGroup{g.W, g.Wd, g.W2, g.W2d, g.bias, g.X, g.out, g.M, g.ld, begin, 0, g.c12};
         begin += (q8 ? ws_groups(g.M, glu) : g.M / 16) * S;   // work-groups of this group
     }
     if (mode == SK_PARTIAL) {
@@ -776,8 +825,6 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
     fm_drafter* d = ds[0];
     const auto& c = d->c;
     const int D = c.dim, T = c.block, Ht = c.target_dim, H = c.heads, hd = c.head_dim;
-    const int R = B * T;   // rows of the pass
-    float* part = d->at<float>(d->p.part);
     float* x = d->at<float>(d->p.x);
     const float* mod = d->at<float>(d->p.modc);
     uint8_t* fragH = d->at<uint8_t>(d->p.fragH);
@@ -785,7 +832,6 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
     uint8_t* fragU = d->at<uint8_t>(d->p.fragU);
     float* qkv = d->at<float>(d->p.qkv);
     const float* rope = d->at<float>(d->p.rope);
-    const long long pstr = (long long)TMAX * B * D;   // partial slab stride: the pass's rows
     const int Sq = pick_qsplit(D);
     float* debug = B == 1 ? bas[0]->debug_layers : nullptr;
 
@@ -820,38 +866,48 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
             CHK(fm_kv_rows_small(d, B, 0, cfrag, st, ds, starts));
         }
     }
-    int S = 0;
-    int S_prev = 0;           // split count of the pending residual update (fc2 of the previous layer)
+    // The layers, with every LayerNorm folded into the product that takes its row (SkinnyArgs): each residual
+    // update (o_proj, cross o_proj, fc2: unsplit, SK_RESID) writes x, the fragments of y = x (1 + scale) for the next
+    // product and x's per-tile statistics; the next product (q | k | v, cross q, fc1, the head) applies
+    // rstd (acc - mean c1) + c2. No row kernel runs between the layers.
+    float2* stats = d->at<float2>(d->p.lnstats);
+    const float* c12 = d->at<float>(d->p.c12);
+    auto fold = [&]() {
+        SkExtra e;
+        e.ln_stats = (const float*)stats;
+        e.ln_tiles = D / 16;
+        e.ln_eps = c.ln_eps;
+        return e;
+    };
+    auto resid = [&](const float* base, int base_ld, const float* gate, const float* next_mod, float* dbg) {
+        SkExtra e;
+        e.rx = x;
+        e.rx_ld = D;
+        e.rbase = base;
+        e.rbase_ld = base_ld;
+        e.rgate = gate;
+        e.ryscale = next_mod;   // the next LayerNorm's scale row
+        e.rstats = (float*)stats;
+        e.rdebug = dbg;
+        return e;
+    };
+    auto C12 = [&](int l, int which) { return c12 + c12_off(c, l, which); };
     int Sqb = Sq;             // split count of the cross q of layers >= 1 (two row blocks may take fewer)
     for (int l = 0; l < c.layers; ++l) {
         const float* m_sa = mod + (size_t)(3 * l) * 3 * D;
         const float* m_ca = mod + (size_t)(3 * l + 1) * 3 * D;
         const float* m_ml = mod + (size_t)(3 * l + 2) * 3 * D;
-        // residual (previous layer's MLP) + self-attention modulation, then q | k | v; layer 0's are the same for
-        // every draft (flowmap_layer0)
+        // q | k | v of the self-attention LN-mod (x and its fragments from the previous layer's fc2); layer 0's are
+        // the same for every draft (flowmap_layer0)
         if (l > 0) {
-            RowArgs r = rows_base(d, D, R);
-            r.x = x;
-            r.part = part;
-            r.S = S_prev;
-            r.part_stride = pstr;
-            r.bias = d->B(LW(l - 1, "mlp.fc2.bias"));
-            r.gate = mod + (size_t)(3 * (l - 1) + 2) * 3 * D + 2 * D;
-            if (debug) r.debug_x = debug + (size_t)(l - 1) * T * D;
-            r.norm = ROW_LN_MOD;
-            r.scale = m_sa;
-            r.shift = m_sa + D;
-            r.eps = c.ln_eps;
-            r.frag_out = fragH;
-            CHK(rows(r, st));
-            CHK(skinny(d,
-                       {{d->W(LW(l, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D,
-                         3 * D},
-                        {d->W(LW(l, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D,
-                         3 * D},
-                        {d->W(LW(l, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D,
-                         D, 3 * D}},
-                       D, T, SK_F32, 0, nullptr, st, 0, 0, B));
+            const SkExtra ef = fold();
+            std::vector<SkGroupDesc> g = {
+                {d->W(LW(l, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, 3 * D},
+                {d->W(LW(l, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
+                {d->W(LW(l, "self_attn.v_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D, D,
+                 3 * D}};
+            for (int i = 0; i < 3; ++i) g[i].c12 = C12(l, i);
+            CHK(skinny(d, g, D, T, SK_F32, 0, nullptr, st, 0, 0, B, &ef));
             {
                 SelfAttnArgs a{};
                 a.qkv = qkv;
@@ -872,26 +928,17 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
                 a.o_frag = fragO;
                 HIPCHK(launch_self_attn(a, st));
             }
-            CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
-                       D, T, SK_PARTIAL, 0, &S, st, pstr, 0, B));
-            {
-                RowArgs r = rows_base(d, D, R);
-                r.x = x;
-                r.part = part;
-                r.S = S;
-                r.part_stride = pstr;
-                r.gate = m_sa + 2 * D;
-                r.norm = ROW_LN_MOD;
-                r.scale = m_ca;
-                r.shift = m_ca + D;
-                r.eps = c.ln_eps;
-                r.frag_out = fragH;
-                CHK(rows(r, st));
-            }
-            // cross-attention over cache rows [0, pos]: q = cross q_proj(h) (whole k-range per work-group), then
-            // per-head q_norm + RoPE inside the attention kernel
-            CHK(skinny(d, {{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, D}},
-                       D, T, SK_PARTIAL, Sq, &Sqb, st, (long long)TMAX * B * D, d->p.qkv_floats, B));
+            // o_proj and the gated residual; fragments of the cross-attention LN-mod's x (1 + scale)
+            const SkExtra er = resid(x, D, m_sa + 2 * D, m_ca, nullptr);
+            CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, fragH, D,
+                            0}},
+                       D, T, SK_RESID, 0, nullptr, st, 0, 0, B, &er));
+            // cross-attention q = cross q_proj(LN-mod(x)) (k-split slabs), per-head q_norm + RoPE inside the
+            // attention kernel
+            SkGroupDesc gq{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D,
+                           D};
+            gq.c12 = C12(l, 3);
+            CHK(skinny(d, {gq}, D, T, SK_PARTIAL, Sq, &Sqb, st, (long long)TMAX * B * D, d->p.qkv_floats, B, &ef));
         }
         for (int b = 0; b < B; ++b) {   // each request over its own cache rows [0, pos_b]
             QPrep qp{};
@@ -909,49 +956,37 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
             CHK(attend(ds[b], qp, T, l, 0, bas[b]->pos + 1, nullptr, nullptr, 0, 0, -1, 1.f / sqrtf((float)hd), nullptr,
                        0, 0, fragO, st, b * T));
         }
-        CHK(skinny(d, {{d->W(LW(l, "cross_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}},
-                   D, T, SK_PARTIAL, 0, &S, st, pstr, 0, B));
+        // cross o_proj and the gated residual (layer 0: on x1, the residual after its self-attention, the same row
+        // for every slot); fragments of the MLP LN-mod's x (1 + scale)
         {
-            RowArgs r = rows_base(d, D, R);
-            r.x = x;
-            if (l == 0) r.init = d->at<float>(d->p.x1);   // layer 0's residual after its self-attention (every row)
-            r.part = part;
-            r.S = S;
-            r.part_stride = pstr;
-            r.gate = m_ca + 2 * D;
-            r.norm = ROW_LN_MOD;
-            r.scale = m_ml;
-            r.shift = m_ml + D;
-            r.eps = c.ln_eps;
-            r.frag_out = fragH;
-            CHK(rows(r, st));
+            const SkExtra er = l == 0 ? resid(d->at<float>(d->p.x1), 0, m_ca + 2 * D, m_ml, nullptr)
+                                      : resid(x, D, m_ca + 2 * D, m_ml, nullptr);
+            CHK(skinny(d, {{d->W(LW(l, "cross_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, fragH,
+                            D, 0}},
+                       D, T, SK_RESID, 0, nullptr, st, 0, 0, B, &er));
         }
-        // MLP: fc1 + exact GELU (fused), fc2 (its residual is applied by the next row kernel)
-        CHK(skinny(d, {{d->W(LW(l, "mlp.fc1.weight")), nullptr, nullptr, nullptr, d->B(LW(l, "mlp.fc1.bias")), fragH,
-                        fragU, c.ffn, 0}},
-                   D, T, SK_FRAG_GELU, 0, nullptr, st, 0, 0, B));
-        CHK(skinny(d, {{d->W(LW(l, "mlp.fc2.weight")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
-                   SK_PARTIAL, 0, &S_prev, st, pstr, 0, B));
+        // MLP: fc1 of the LN-mod + exact GELU (fused), fc2 + bias and the gated residual; fragments of the next
+        // LayerNorm's x (1 + scale): the next layer's self-attention, or the final modulation
+        {
+            const SkExtra ef = fold();
+            SkGroupDesc g1{d->W(LW(l, "mlp.fc1.weight")), nullptr, nullptr, nullptr, d->B(LW(l, "mlp.fc1.bias")), fragH,
+                           fragU, c.ffn, 0};
+            g1.c12 = C12(l, 4);
+            CHK(skinny(d, {g1}, D, T, SK_FRAG_GELU, 0, nullptr, st, 0, 0, B, &ef));
+            const float* next = l + 1 < c.layers ? mod + (size_t)(3 * (l + 1)) * 3 * D : mod + (size_t)(3 * c.layers) * 3 * D;
+            const SkExtra er = resid(x, D, m_ml + 2 * D, next, debug ? debug + (size_t)l * T * D : nullptr);
+            CHK(skinny(d, {{d->W(LW(l, "mlp.fc2.weight")), nullptr, nullptr, nullptr, d->B(LW(l, "mlp.fc2.bias")),
+                            fragU, fragH, D, 0}},
+                       c.ffn, T, SK_RESID, 0, nullptr, st, 0, 0, B, &er));
+        }
     }
+    // the head of the final LN-mod, + bias
     {
-        const float* m_f = mod + (size_t)(3 * c.layers) * 3 * D;
-        RowArgs r = rows_base(d, D, R);
-        r.x = x;
-        r.part = part;
-        r.S = S_prev;
-        r.part_stride = pstr;
-        r.bias = d->B(LW(c.layers - 1, "mlp.fc2.bias"));
-        r.gate = mod + (size_t)(3 * (c.layers - 1) + 2) * 3 * D + 2 * D;
-        if (debug) r.debug_x = debug + (size_t)(c.layers - 1) * T * D;
-        r.norm = ROW_LN_MOD;
-        r.scale = m_f;
-        r.shift = m_f + D;
-        r.eps = c.ln_eps;
-        r.frag_out = fragH;
-        CHK(rows(r, st));
+        const SkExtra ef = fold();
+        SkGroupDesc gh{d->W("head.weight"), nullptr, nullptr, nullptr, d->B("head.bias"), fragH, hidden_out, Ht, Ht};
+        gh.c12 = C12(c.layers, 0);
+        CHK(skinny(d, {gh}, D, T, SK_F32, 0, nullptr, st, 0, 0, B, &ef));
     }
-    CHK(skinny(d, {{d->W("head.weight"), nullptr, nullptr, nullptr, d->B("head.bias"), fragH, hidden_out, Ht, Ht}}, D, T,
-               SK_F32, 0, nullptr, st, 0, 0, B));
     return FM_OK;
 }
 
@@ -1012,6 +1047,40 @@ fm_status flowmap_layer0(fm_drafter* d, hipStream_t st) {
                     d->at<float>(d->p.q0c), D, D}},
                D, T, SK_PARTIAL, pick_qsplit(D), nullptr, st, pstr, (size_t)QKV_SLABS * TMAX * D));
     return FM_OK;
+}
+
+// c1 = sum_k (1 + scale_k) W[m][k] and c2 = sum_k shift_k W[m][k] of every product that takes a LayerNorm-modulated
+// row in the draft, under the handle's modulation table (at create and whenever the table changes): each is one
+// group of a two-row skinny product over the fragments of (1 + scale, shift).
+fm_status flowmap_ln_fold(fm_drafter* d, hipStream_t st) {
+    const auto& c = d->c;
+    const int D = c.dim, L = c.layers;
+    const float* mod = d->at<float>(d->p.modc);
+    uint8_t* lf = d->at<uint8_t>(d->p.lnfrag);
+    float* c12 = d->at<float>(d->p.c12);
+    HIPCHK(launch_ln_fold_rows(mod, D, 3 * L + 1, lf, st));
+    std::vector<SkGroupDesc> gs;
+    auto flush = [&]() -> fm_status {
+        if (!gs.empty()) CHK(skinny(d, gs, D, 2, SK_F32, 0, nullptr, st));
+        gs.clear();
+        return FM_OK;
+    };
+    auto add = [&](const std::string& w, int j, size_t off, int M) -> fm_status {
+        if (gs.size() == SK_MAX_GROUPS) CHK(flush());
+        gs.push_back({d->W(w), nullptr, nullptr, nullptr, nullptr, lf + (size_t)j * D * 64, c12 + off, M, M});
+        return FM_OK;
+    };
+    for (int l = 0; l < L; ++l) {
+        if (l > 0) {
+            CHK(add(LW(l, "self_attn.q_proj.weight"), 3 * l, c12_off(c, l, 0), D));
+            CHK(add(LW(l, "self_attn.k_proj.weight"), 3 * l, c12_off(c, l, 1), D));
+            CHK(add(LW(l, "self_attn.v_proj.weight"), 3 * l, c12_off(c, l, 2), D));
+            CHK(add(LW(l, "cross_attn.q_proj.weight"), 3 * l + 1, c12_off(c, l, 3), D));
+        }
+        CHK(add(LW(l, "mlp.fc1.weight"), 3 * l + 2, c12_off(c, l, 4), c.ffn));
+    }
+    CHK(add("head.weight", 3 * L, c12_off(c, L, 0), c.target_dim));
+    return flush();
 }
 
 // Arguments of the persistent draft kernel, uploaded once: weights, cache rows, the handle's buffers and the arena
@@ -1102,6 +1171,7 @@ fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
                     d->at<float>(d->p.h0), D, D}},
                Ht, 1, SK_F32, 0, nullptr, st));
     CHK(flowmap_layer0(d, st));
+    CHK(flowmap_ln_fold(d, st));
     return draft_setup(d, st);
 }
 
@@ -1742,7 +1812,8 @@ fm_status fm_time_condition(fm_drafter* d, float s, float t, int32_t time_dim, i
     if (table_out)
         HIPCHK(hipMemcpyAsync(table_out, a.table, (size_t)nn * 3 * c.dim * 4, hipMemcpyDeviceToDevice,
                               (hipStream_t)stream));
-    const fm_status r = flowmap_layer0(d, (hipStream_t)stream);   // layer 0's projections follow the new table
+    fm_status r = flowmap_layer0(d, (hipStream_t)stream);   // layer 0's projections follow the new table
+    if (r == FM_OK) r = flowmap_ln_fold(d, (hipStream_t)stream);   // and so do the LayerNorm fold's c1 / c2
     if (r == FM_OK) {
         const float key[5] = {s, t, (float)time_dim, (float)cond_dim, time_scale};
         memcpy(d->tc_key, key, sizeof key);
@@ -1783,8 +1854,10 @@ fm_status fm_draft_batch(fm_drafter* const* ds, int32_t B, const fm_block_args* 
     }
     hipStream_t st = (hipStream_t)stream;
     if (c.variant == FM_VARIANT_FLOWMAP) {
-        if (B > 1 && (c.block != TMAX || c.wtype != FM_W_BF16 || c.dim % 512 || c.ffn % 512))
-            return fail(FM_E_UNSUPPORTED, "flow-map batches need 16-slot blocks, bf16 weights, dim and ffn %% 512 == 0");
+        if (B > 1 && (c.block != TMAX || c.wtype != FM_W_BF16 || c.dim % 512 || c.ffn % 512 ||
+                      c.dim > 16 * LN_MAX_TILES / FM_BATCH))
+            return fail(FM_E_UNSUPPORTED, "flow-map batches need 16-slot blocks, bf16 weights, dim and ffn %% 512 == 0, "
+                                          "dim <= %d", 16 * LN_MAX_TILES / FM_BATCH);
         const fm_block_args* as[FM_BATCH];
         for (int b = 0; b < B; ++b) {
             const fm_block_args* a = &args[b];

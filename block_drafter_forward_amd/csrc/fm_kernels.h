@@ -15,7 +15,9 @@ enum SkinnyOut {
     SK_PARTIAL = 1,    // out[split*part_stride + t*ld + m] = acc
     SK_FRAG_GELU = 2,  // frag(out)[t][m] = gelu_erf(acc + bias[m])
     SK_FRAG_GEGLU = 3, // frag(out)[t][m] = gelu_tanh(acc_gate) * acc_up        (two weight tiles)
-    SK_FRAG_SWIGLU = 4 // frag(out)[t][m] = silu(acc_gate) * acc_up             (two weight tiles)
+    SK_FRAG_SWIGLU = 4, // frag(out)[t][m] = silu(acc_gate) * acc_up            (two weight tiles)
+    SK_RESID = 5        // residual update (bf16, one matrix, S = 1): x[t][m] = base[t][m] + gate[m] (acc + bias[m]);
+                        // frag(out)[t][m] = x[t][m] (1 + yscale[m]); (mean, M2) of x over each 16-column tile
 };
 enum SkinnyWType { SKW_BF16 = 0, SKW_Q8_0 = 1 };
 
@@ -32,6 +34,7 @@ struct SkinnyGroup {
     int ld;               // output row stride (elements)
     int tile_begin;       // first work-group of this group
     int pad;
+    const float* c12;     // LayerNorm fold: c1 = c12[m], c2 = c12[M + m] (see SkinnyArgs), or null
 };
 struct SkinnyArgs {
     SkinnyGroup g[SK_MAX_GROUPS];
@@ -43,7 +46,27 @@ struct SkinnyArgs {
     int mode;
     long long part_stride;
     int nb;               // blocks of 16 activation rows: 1, or 2 (bf16, KW % 4 == 0; T = 16 rows per block)
+    const float* zeros;   // a zero row (the target of loads an epilogue does not use)
+    // LayerNorm fold (bf16, one matrix): the activation fragments hold y = x (1 + s) of rows x whose LayerNorm with
+    // modulation (x - mean) rstd (1 + s) + shift is the product's real input. ln_stats (float2 [ln_tiles][16 nb])
+    // holds (mean, M2) of each 16-column tile of x (an SK_RESID epilogue's output); with c1 = sum_k (1 + s_k) W[m][k]
+    // and c2 = sum_k shift_k W[m][k] (the group's c12), the epilogue takes rstd (acc - mean c1[m]) + c2[m] as the
+    // product (SK_PARTIAL: split 0 adds the constant part, every split scales by rstd).
+    const float* ln_stats;
+    int ln_tiles;         // x's width / 16 (at most LN_MAX_TILES / nb)
+    float ln_inv;         // 1 / ln_tiles
+    float ln_eps;
+    // SK_RESID
+    float* rx;            // residual stream [rows][rx_ld], written (x above)
+    int rx_ld;
+    const float* rbase;   // base rows [rows][rbase_ld] (rbase_ld 0: one row for every row); may be rx
+    int rbase_ld;
+    const float* rgate;   // f32 [M] or null (gate 1)
+    const float* ryscale; // f32 [M]: the next LayerNorm's modulation scale s
+    float* rstats;        // float2 [M / 16][16 nb]: (mean, M2) of x over each 16-column tile, per row
+    float* rdebug;        // optional copy of x (same layout)
 };
+#define LN_MAX_TILES 256   // LayerNorm fold: x at most 4096 wide (2048 with two blocks of rows)
 // Q8_0 weights run the tile-owning variant: a work-group of SK_WS_WAVES waves owns that many adjacent 16-row tiles
 // of a group, or for a gated unit half as many tiles of each of its two matrices (tile_begin then counts work-groups:
 // ceil(M / (16 SK_WS_WAVES)) x S per group, twice that for a gated unit) over a k-range of K / S columns (a multiple
@@ -91,6 +114,8 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t st);
 
 // f32 rows [T][K] (row stride ld) -> fragments. T <= 32 (rows 16.. in the second block), K % 32 == 0.
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st);
+// fragments of (1 + scale, shift) of each of nmod modulations (scale, shift, gate rows of D) for the LayerNorm fold
+hipError_t launch_ln_fold_rows(const float* mod, int D, int nmod, uint8_t* frag, hipStream_t st);
 // bf16 row E[*idx] of a [V][K] table -> fragments (T = 1, lo = 0); ids are clamped to [0, V).
 hipError_t launch_gather_frag(const uint16_t* E, int V, int K, const int32_t* idx, uint8_t* frag,
                               hipStream_t st, int row = 0);

@@ -138,6 +138,27 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     }
 }
 
+// The rows whose products with a matrix W give the LayerNorm fold's c1 = sum_k (1 + s_k) W[m][k] and
+// c2 = sum_k shift_k W[m][k]: for modulation j of the table (scale, shift, gate at mod + 3 j D), row 0 = 1 + scale
+// and row 1 = shift as fragments at frag + j D 64 (a 16-row block; rows 2..15 zero).
+__global__ void ln_fold_rows_kernel(const float* mod, int D, uint8_t* frag) {
+    const int j = blockIdx.y;
+    const int slot = blockIdx.x * 256 + threadIdx.x;
+    if (slot * 8 >= D) return;
+    const float* m = mod + (size_t)j * 3 * D + slot * 8;
+    float v0[8], v1[8], z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        v0[e] = 1.f + m[e];
+        v1[e] = m[D + e];
+        z[e] = 0.f;
+    }
+    uint8_t* f = frag + (size_t)j * D * 64;
+    frag_store8(f, 0, slot * 8, v0);
+    frag_store8(f, 1, slot * 8, v1);
+    for (int t = 2; t < 16; ++t) frag_store8(f, t, slot * 8, z);
+}
+
 __global__ void f32_to_frag_kernel(const float* x, int ld, int K, uint8_t* frag) {
     const int t = blockIdx.y;
     const int slot = blockIdx.x * 256 + threadIdx.x;
@@ -418,6 +439,12 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t st) {
     case 3: return launch_rows_ns<3>(a, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_ln_fold_rows(const float* mod, int D, int nmod, uint8_t* frag, hipStream_t st) {
+    if (D % 32 || nmod < 1) return hipErrorInvalidValue;
+    ln_fold_rows_kernel<<<dim3((D / 8 + 255) / 256, nmod), 256, 0, st>>>(mod, D, frag);
+    return hipGetLastError();
 }
 
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st) {

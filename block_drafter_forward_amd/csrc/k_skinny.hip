@@ -33,6 +33,15 @@ __device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// LDS-direct load: lane l's 16 bytes from g land at lds + 16 l (lds wave-uniform, through m0). In inline asm, so
+// the compiler's wait bookkeeping does not see it (a tracked LDS-direct load would make it wait for every load in
+// flight at the next LDS read); its reader waits explicitly.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+    const unsigned la =
+        __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((__attribute__((address_space(3))) void*)lds));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory", "m0");
+}
+
 // One pipeline stage: SKC k-steps of the wave's A tiles and B fragments, loaded without any condition (a
 // conditional load makes the compiler wait for every outstanding load before the next MFMA).
 template <int NT, int WT, int SKC>
@@ -134,10 +143,14 @@ __device__ __forceinline__ void rs_compute(const RsStage<NT, RC, NB>& st, uint4*
 // in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
 // stage i computes), with the last pair peeled so the loop body carries no conditions.
 // NB = 2 (two blocks of 16 activation rows against each weight tile) exists with UP = 2 only.
-template <int NT, int WT, int UP, int SKC, int NB = 1>
+// LN: the LayerNorm fold of SkinnyArgs (one matrix). Every operand of the epilogue (bias, LayerNorm statistics and
+// c1 / c2, the residual update's base, gate and scale) is loaded before the main loop, so the epilogue waits on no
+// memory round trip of its own.
+template <int NT, int WT, int UP, int SKC, int NB = 1, bool LN = false>
 __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     static_assert(WT == SKW_BF16, "bf16 weights (Q8_0: skinny_ws_kernel)");
     static_assert(NB == 1 || UP == 2, "two row blocks: row-staged only");
+    static_assert(!LN || NT == 1, "the LayerNorm fold takes one matrix");
     const int bid = blockIdx.x;
     int gi = 0;
 #pragma unroll 1
@@ -154,6 +167,36 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     const int r = lane & 15, g = lane >> 4;
     const int K = a.K;
 
+    // ── epilogue operands, in flight with the first weights ──
+    constexpr int R = 16 * NB;              // activation rows of the launch
+    constexpr int NGQ = 256 / R;            // LayerNorm statistics: threads per row
+    const int e_el = threadIdx.x & 63, e_rr = threadIdx.x >> 6;
+    const int e_ml = 4 * (e_el >> 4) + e_rr;   // the element this thread finishes: tile row e_ml, activation row e_t
+    const int e_t = e_el & 15, e_m = m0 + e_ml;
+    const bool resid = a.mode == SK_RESID;
+    const float e_bias = bf16_to_f32(*(G.bias ? G.bias + e_m : (const uint16_t*)a.zeros));   // no branch: no wait
+    float e_base[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) e_base[b] = *(resid ? a.rbase + (size_t)(16 * b + e_t) * a.rbase_ld + e_m : a.zeros);
+    const float e_gate = *(resid && a.rgate ? a.rgate + e_m : a.zeros);
+    const float e_ys = *(resid ? a.ryscale + e_m : a.zeros);
+    // LayerNorm statistics (float2 [ln_tiles][R], ln_tiles R / 128 KB) straight into LDS, 1 KB per wave instruction,
+    // issued right after the first chunk's loads: loads complete in issue order, so the first chunk's wait covers
+    // them too, and the statistics are reduced (ln_reduce) between the first chunk's products and the next chunk's
+    __shared__ float2 lnlds[LN ? LN_MAX_TILES * 16 : 1];
+    float e_c1 = 0.f, e_c2 = 0.f;
+    if constexpr (LN) {
+        e_c1 = G.c12[e_m];
+        e_c2 = G.c12[G.M + e_m];
+    }
+    auto ln_prefetch = [&]() {
+        if constexpr (LN) {
+            const int nin = a.ln_tiles * R / 128;   // 1 KB pieces
+            for (int i = wave; i < nin; i += 4)
+                lds_dma16((const uint8_t*)a.ln_stats + (size_t)i * 1024 + lane * 16, (uint8_t*)lnlds + (size_t)i * 1024);
+        }
+    };
+
     f32x4_t accb[NT][NB];
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -161,57 +204,124 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
         for (int b = 0; b < NB; ++b) accb[n][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t* acc = &accb[0][0];   // the one-block paths (NB == 1): accb[n][0] is acc[n]
 
+    // ── LayerNorm fold: each row's mean and rstd from its tiles' (mean, M2) in one pass, in a fixed order
+    // (deterministic). Sums are taken about K = the row's first tile mean (Chan et al. with a shift):
+    //   sum_j mean_j and S = sum_j (M2_j + 16 (mean_j - K)^2) = sum (x - K)^2;  M2 = S - n (mean - K)^2.
+    // Thread (row, gq) takes tiles gq, gq + NGQ, ... (every LDS read in bounds and unconditional, the tiles past the
+    // row's end masked); wave shuffles, then the four waves' sums through LDS. Run once, right after the first
+    // chunk's products, while the next chunk's loads are in flight: its LDS reads take their base address from an
+    // asm that consumes those products, so they cannot be scheduled before the wait for the first chunk, which (in
+    // issue order) covers the statistics' LDS-direct loads. ──
+    float e_mu[NB], e_rs[NB];
+    __shared__ float lnred[LN ? 2 : 1][4][R];
+    auto ln_reduce = [&]() {
+        if constexpr (LN) {
+            constexpr int NPT = LN_MAX_TILES / NB / NGQ;   // tiles per thread at most (16)
+            int lbase = 0;
+            float dep = accb[0][0][0];
+            asm volatile("" : "+v"(lbase) : "v"(dep));
+            __syncthreads();   // every wave's statistics have landed
+            const float2* lp = lnlds + lbase;
+            const int row = threadIdx.x % R, gq = threadIdx.x / R;
+            const float kr = lp[row].x;
+            float2 sv[NPT];
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) sv[i] = lp[(gq + NGQ * i) * R + row];   // in bounds, past-the-row tiles too
+            // every value an operand of an (empty) asm: the reads are issued together, none sunk into a branch
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) asm volatile("" : "+v"(sv[i].x), "+v"(sv[i].y));
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) {
+                const bool ok = gq + NGQ * i < a.ln_tiles;
+                const float dd = sv[i].x - kr;
+                const float t2 = sv[i].y + 16.f * dd * dd;
+                s1 += ok ? sv[i].x : 0.f;
+                s2 += ok ? t2 : 0.f;
+            }
+            // lanes of one row within a wave: lane = gq_local R + row
+#pragma unroll
+            for (int o = R; o < 64; o <<= 1) {
+                s1 += __shfl_xor(s1, o, 64);
+                s2 += __shfl_xor(s2, o, 64);
+            }
+            if (lane < R) {
+                lnred[0][wave][lane] = s1;
+                lnred[1][wave][lane] = s2;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int rw = 16 * b + e_t;
+                const float mu =
+                    (((lnred[0][0][rw] + lnred[0][1][rw]) + lnred[0][2][rw]) + lnred[0][3][rw]) * a.ln_inv;
+                const float sq = ((lnred[1][0][rw] + lnred[1][1][rw]) + lnred[1][2][rw]) + lnred[1][3][rw];
+                const float dk = mu - lp[rw].x;
+                const float var = (sq * a.ln_inv - 16.f * dk * dk) * (1.f / 16.f);
+                e_mu[b] = mu;
+                e_rs[b] = 1.f / sqrtf(fmaxf(var, 0.f) + a.ln_eps);
+            }
+        }
+    };
+
     if constexpr (UP == 2) {
         __shared__ uint4 rs_lds[4][NT * 16 * (4 * SKC + 1)];
         uint4* lds = rs_lds[wave];
         RsStage<NT, SKC, NB> c0, c1;
         const int nch = KW / SKC;
         rs_load<NT, SKC, NB>(c0, G, K, m0, s0, lane);
+        ln_prefetch();
         int ch = 0;
         for (; ch + 2 < nch; ch += 2) {
             rs_load<NT, SKC, NB>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
             rs_compute<NT, SKC, NB>(c0, lds, accb, lane);
+            if (ch == 0) ln_reduce();
             rs_load<NT, SKC, NB>(c0, G, K, m0, s0 + SKC * (ch + 2), lane);
             rs_compute<NT, SKC, NB>(c1, lds, accb, lane);
         }
         if (ch + 1 < nch) {
             rs_load<NT, SKC, NB>(c1, G, K, m0, s0 + SKC * (ch + 1), lane);
             rs_compute<NT, SKC, NB>(c0, lds, accb, lane);
+            if (ch == 0) ln_reduce();
             rs_compute<NT, SKC, NB>(c1, lds, accb, lane);
         } else {
             rs_compute<NT, SKC, NB>(c0, lds, accb, lane);
+            if (ch == 0) ln_reduce();
         }
     } else if constexpr (UP == 1) {
         SkStage<NT, WT, SKC> st;
         sk_load<NT, WT, SKC>(st, G, K, m0, s0, r, g, lane);
+        ln_prefetch();
         sk_compute<NT, WT, SKC>(st, acc);
+        ln_reduce();
     } else {
         SkStage<NT, WT, SKC> st0, st1;
         sk_load<NT, WT, SKC>(st0, G, K, m0, s0, r, g, lane);
+        ln_prefetch();
         int s = 0;
         for (; s + 2 * SKC < KW; s += 2 * SKC) {
             sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane);
             sk_compute<NT, WT, SKC>(st0, acc);
+            if (s == 0) ln_reduce();
             sk_load<NT, WT, SKC>(st0, G, K, m0, s0 + s + 2 * SKC, r, g, lane);
             sk_compute<NT, WT, SKC>(st1, acc);
         }
         sk_load<NT, WT, SKC>(st1, G, K, m0, s0 + s + SKC, r, g, lane);
         sk_compute<NT, WT, SKC>(st0, acc);
+        if (s == 0) ln_reduce();
         sk_compute<NT, WT, SKC>(st1, acc);
     }
 
     // ── sum the four waves' tiles (fixed order), per block of rows ──
     __shared__ f32x4_t red[NT * NB][4][64];
     __shared__ float tile[NB][16][17];
+    __shared__ float xt[NB][16][17];   // SK_RESID: the tile's updated residual
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int b = 0; b < NB; ++b) red[n * NB + b][wave][lane] = accb[n][b];
     __syncthreads();
-    const int el = threadIdx.x & 63, rr = threadIdx.x >> 6;
-    const int ml = 4 * (el >> 4) + rr;   // row of the tile
-    const int t = el & 15;               // activation row (slot) within the block
-    const int m = m0 + ml;
+    const int el = e_el, rr = e_rr, ml = e_ml, t = e_t, m = e_m;
     const bool frag_mode = a.mode != SK_F32 && a.mode != SK_PARTIAL;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -222,18 +332,24 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
             v[n] = ((red[q][0][el][rr] + red[q][1][el][rr]) + red[q][2][el][rr]) + red[q][3][el][rr];
         }
         const int row = 16 * b + t;
+        if constexpr (LN)   // rstd (acc - mean c1) + c2; the constant part once (split 0)
+            v[0] = split == 0 ? e_rs[b] * (v[0] - e_mu[b] * e_c1) + e_c2 : e_rs[b] * v[0];
         if (a.mode == SK_F32) {
-            if (t < a.T) {
-                float bi = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
-                ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + bi;
-            }
+            if (t < a.T) ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + e_bias;
         } else if (a.mode == SK_PARTIAL) {
             if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)row * G.ld + m] = v[0];
+        } else if (a.mode == SK_RESID) {
+            const float xn = e_base[b] + (a.rgate ? e_gate : 1.f) * (v[0] + e_bias);
+            if (t < a.T) {
+                a.rx[(size_t)row * a.rx_ld + m] = xn;
+                if (a.rdebug) a.rdebug[(size_t)row * a.rx_ld + m] = xn;
+            }
+            xt[b][t][ml] = xn;
+            tile[b][t][ml] = xn * (1.f + e_ys);
         } else {
             float o;
             if (a.mode == SK_FRAG_GELU) {
-                float bi = G.bias ? bf16_to_f32(G.bias[m]) : 0.f;
-                o = gelu_erf(v[0] + bi);
+                o = gelu_erf(v[0] + e_bias);
             } else if (a.mode == SK_FRAG_GEGLU) {
                 o = gelu_tanh(v[0]) * v[NT - 1];
             } else {
@@ -244,6 +360,20 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     }
     if (!frag_mode) return;
     __syncthreads();
+    if (resid && threadIdx.x < R) {   // (mean, M2) of each row of x over the tile's 16 columns
+        const int b = threadIdx.x >> 4, tt = threadIdx.x & 15;
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sm += xt[b][tt][j];
+        const float mean = sm * (1.f / 16.f);
+        float q = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float dd = xt[b][tt][j] - mean;
+            q += dd * dd;
+        }
+        ((float2*)a.rstats)[(size_t)(m0 >> 4) * R + threadIdx.x] = make_float2(mean, q);
+    }
     if (threadIdx.x < 32 * NB) {
         const int b = threadIdx.x >> 5, tt = (threadIdx.x >> 1) & 15, h = threadIdx.x & 1;
         if (tt < a.T) {
@@ -255,33 +385,42 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     }
 }
 
-template <int NT, int WT>
-hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
+template <int NT, int WT, bool LN>
+hipError_t launch_nt_ln(const SkinnyArgs& a, int nwg, hipStream_t st) {
     const int KW = a.KW;
     dim3 grid(nwg), block(256);
     if (a.nb == 2) {   // two blocks of rows: chunks of 4 k-steps (the registers of two blocks' fragments)
         if constexpr (WT == SKW_BF16) {
             if (KW % 4 || a.T != 16) return hipErrorInvalidValue;
-            skinny_kernel<NT, WT, 2, 4, 2><<<grid, block, 0, st>>>(a);
+            skinny_kernel<NT, WT, 2, 4, 2, LN><<<grid, block, 0, st>>>(a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
     if (a.nb != 1) return hipErrorInvalidValue;
     if (KW % 4 == 0) {
-        if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8><<<grid, block, 0, st>>>(a);
-        else skinny_kernel<NT, WT, 2, 4><<<grid, block, 0, st>>>(a);
+        if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8, 1, LN><<<grid, block, 0, st>>>(a);
+        else skinny_kernel<NT, WT, 2, 4, 1, LN><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }
-#define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n><<<grid, block, 0, st>>>(a); return hipGetLastError();
+#define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n, 1, LN><<<grid, block, 0, st>>>(a); return hipGetLastError();
     switch (KW) {
         SK_UP(1) SK_UP(2) SK_UP(3) SK_UP(5) SK_UP(6) SK_UP(10)
     default: break;
     }
 #undef SK_UP
-    if (KW > 16 && KW % 2 == 0) skinny_kernel<NT, WT, 0, 1><<<grid, block, 0, st>>>(a);
+    if (KW > 16 && KW % 2 == 0) skinny_kernel<NT, WT, 0, 1, 1, LN><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+template <int NT, int WT>
+hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
+    if (a.ln_stats) {
+        if constexpr (NT == 1) return launch_nt_ln<1, WT, true>(a, nwg, st);
+        return hipErrorInvalidValue;
+    }
+    return launch_nt_ln<NT, WT, false>(a, nwg, st);
 }
 
 // ── Q8_0: the tile-owning variant ──────────────────────────────────────────────────────────────
@@ -394,7 +533,17 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyAr
 
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st) {
     const bool glu = (a.mode == SK_FRAG_GEGLU || a.mode == SK_FRAG_SWIGLU);
+    if (!a.zeros) return hipErrorInvalidValue;
+    if (a.ln_stats) {   // the LayerNorm fold: bf16, one matrix, every group with its c1 / c2
+        if (wtype != SKW_BF16 || glu || a.ln_tiles < 1 || a.ln_tiles > LN_MAX_TILES / a.nb) return hipErrorInvalidValue;
+        for (int i = 0; i < a.ngroups; ++i)
+            if (!a.g[i].c12) return hipErrorInvalidValue;
+    }
+    if (a.mode == SK_RESID &&
+        (wtype != SKW_BF16 || a.S != 1 || !a.rx || !a.rbase || !a.ryscale || !a.rstats || a.ngroups != 1))
+        return hipErrorInvalidValue;
     if (wtype == SKW_BF16) return glu ? launch_nt<2, SKW_BF16>(a, nwg, st) : launch_nt<1, SKW_BF16>(a, nwg, st);
+    if (a.mode == SK_RESID) return hipErrorInvalidValue;
     // Q8_0: whole chunks of 256 columns per split, one block of at most 16 rows, whole slabs (SK_F32 / FRAG: S = 1)
     if (a.nb != 1 || a.T < 1 || a.T > 16 || a.S < 1 || a.K % (256 * a.S) ||
         (a.mode != SK_PARTIAL && a.S != 1))
