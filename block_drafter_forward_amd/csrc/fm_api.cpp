@@ -39,6 +39,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int TMAX = 16;          // rows of one skinny activation matrix
 constexpr int FM_BATCH = 2;       // flow-map requests one batched draft takes (16 rows each)
+constexpr int RTICK_MAX = 256;    // tiles of a split residual update (its output width / 16)
 constexpr int QKV_SLABS = 4;      // split-K slabs the attention kernels sum while building q (and k, v)
 constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
 constexpr int PF_SPLIT_WGS = 512; // a k-split prefill launch stays within one round (two 128-tile work-groups per CU)
@@ -178,7 +179,7 @@ size_t c12_off(const fm_config& c, int l, int which) {   // which 0..3: q k v cr
 struct Plan {
     size_t best, mcut, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
         pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
-        rscale, modc, lnstats, c12, lnfrag, dargs, dlayers, dsync, arena, total;
+        rscale, modc, lnstats, c12, lnfrag, rtick, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
     int best_rows;           // argmax keys (one per row)
     size_t part_floats;      // capacity of the partial buffer
@@ -287,6 +288,7 @@ Plan make_plan(const fm_config& c) {
     p.lnstats = take(fmv ? (size_t)(c.dim / 16) * FM_BATCH * TMAX * 8 : 0);
     p.c12 = take(fmv ? c12_floats(c) * 4 : 0);
     p.lnfrag = take(fmv ? (size_t)(3 * c.layers + 1) * c.dim * 64 : 0);
+    p.rtick = take(fmv ? (size_t)RTICK_MAX * 4 : 0);   // a split residual update's per-tile arrival counters
     // the persistent draft kernel: its arguments and per-layer table (device copies), its barrier counters and its
     // activation arena (sized for the most work-groups it may run with)
     const bool pk = draft_supported(c);
@@ -496,6 +498,8 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         if (S < 1 || (K / 256) % S) return fail(FM_E_UNSUPPORTED, "skinny: no Q8_0 k-split %d for K %d", S, K);
     } else if (mode == SK_PARTIAL) {
         S = S_force > 0 ? S_force : pick_split(tiles_total * 16, K);
+    } else if (mode == SK_RESID && S_force > 0) {
+        S = S_force;   // the last split of each tile to arrive finishes it
     }
     if (q8) {
     } else if (nb == 2) {
@@ -529,7 +533,14 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         a.rstats = ex->rstats;
         a.rdebug = ex->rdebug;
     }
-    if (mode == SK_RESID && (S != 1 || !ex)) return fail(FM_E_INVALID, "skinny: a residual update runs unsplit");
+    if (mode == SK_RESID && !ex) return fail(FM_E_INVALID, "skinny: a residual update needs its operands");
+    if (mode == SK_RESID && S > 1) {
+        a.rpart = d->at<float>(d->p.part);
+        a.rtick = d->at<uint32_t>(d->p.rtick);
+        a.part_stride = (long long)TMAX * nb * gs[0].M;
+        if ((size_t)S * a.part_stride > d->p.part_floats) return fail(FM_E_INVALID, "skinny: partial buffer too small");
+        if (gs[0].M / 16 > RTICK_MAX) return fail(FM_E_INVALID, "skinny: %d tiles > %d counters", gs[0].M / 16, RTICK_MAX);
+    }
     int begin = 0;
     for (size_t i = 0; i < gs.size(); ++i) {
         const auto& g = gs[i];
@@ -977,7 +988,7 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
             const SkExtra er = resid(x, D, m_ml + 2 * D, next, debug ? debug + (size_t)l * T * D : nullptr);
             CHK(skinny(d, {{d->W(LW(l, "mlp.fc2.weight")), nullptr, nullptr, nullptr, d->B(LW(l, "mlp.fc2.bias")),
                             fragU, fragH, D, 0}},
-                       c.ffn, T, SK_RESID, 0, nullptr, st, 0, 0, B, &er));
+                       c.ffn, T, SK_RESID, 2, nullptr, st, 0, 0, B, &er));
         }
     }
     // the head of the final LN-mod, + bias
@@ -1155,6 +1166,7 @@ fm_status flowmap_draft_persistent(fm_drafter* d, const fm_block_args* ba, float
 fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int Ht = c.target_dim, D = c.dim;
+    HIPCHK(launch_fill_u32(d->at<uint32_t>(d->p.rtick), RTICK_MAX, 0u, st));   // each last arrival resets its own
     HIPCHK(hipMemcpyAsync(d->at<float>(d->p.modc), d->F("mod"), (size_t)(3 * c.layers + 1) * 3 * D * 4,
                           hipMemcpyDeviceToDevice, st));
     // zero-noise slot input h0 = x_embed(state_norm(mean row of E)) + b

@@ -16,8 +16,9 @@ enum SkinnyOut {
     SK_FRAG_GELU = 2,  // frag(out)[t][m] = gelu_erf(acc + bias[m])
     SK_FRAG_GEGLU = 3, // frag(out)[t][m] = gelu_tanh(acc_gate) * acc_up        (two weight tiles)
     SK_FRAG_SWIGLU = 4, // frag(out)[t][m] = silu(acc_gate) * acc_up            (two weight tiles)
-    SK_RESID = 5        // residual update (bf16, one matrix, S = 1): x[t][m] = base[t][m] + gate[m] (acc + bias[m]);
-                        // frag(out)[t][m] = x[t][m] (1 + yscale[m]); (mean, M2) of x over each 16-column tile
+    SK_RESID = 5        // residual update (bf16, one matrix): x[t][m] = base[t][m] + gate[m] (acc + bias[m]);
+                        // frag(out)[t][m] = x[t][m] (1 + yscale[m]); (mean, M2) of x over each 16-column tile. With
+                        // S > 1 the last split of a tile to arrive (an arrival counter) sums the splits and finishes it
 };
 enum SkinnyWType { SKW_BF16 = 0, SKW_Q8_0 = 1 };
 
@@ -65,6 +66,8 @@ struct SkinnyArgs {
     const float* ryscale; // f32 [M]: the next LayerNorm's modulation scale s
     float* rstats;        // float2 [M / 16][16 nb]: (mean, M2) of x over each 16-column tile, per row
     float* rdebug;        // optional copy of x (same layout)
+    float* rpart;         // S > 1: the splits' partial tiles [S][rows][M] (slab stride part_stride)
+    uint32_t* rtick;      // S > 1: one arrival counter per 16-row tile, zero between launches
 };
 #define LN_MAX_TILES 256   // LayerNorm fold: x at most 4096 wide (2048 with two blocks of rows)
 // Q8_0 weights run the tile-owning variant: a work-group of SK_WS_WAVES waves owns that many adjacent 16-row tiles

@@ -323,6 +323,37 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     __syncthreads();
     const int el = e_el, rr = e_rr, ml = e_ml, t = e_t, m = e_m;
     const bool frag_mode = a.mode != SK_F32 && a.mode != SK_PARTIAL;
+    // A residual update split over S work-groups: each split writes its partial tile with device-coherent stores
+    // (written through to memory), waits until they are performed, then takes a ticket on the tile's counter. The
+    // split that draws the last ticket adds the S partials in split order (deterministic), resets the counter for
+    // the next launch and finishes the tile; the others are done. Nothing ever waits on another work-group.
+    float vsum[NB];
+    if (resid && a.S > 1) {
+        __shared__ int ticket;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int q = b;
+            vsum[b] = ((red[q][0][el][rr] + red[q][1][el][rr]) + red[q][2][el][rr]) + red[q][3][el][rr];
+            __hip_atomic_store(a.rpart + (size_t)split * a.part_stride + (size_t)(16 * b + t) * G.M + m, vsum[b],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores are performed
+        __syncthreads();                                    // and every thread's
+        if (threadIdx.x == 0)
+            ticket = (int)__hip_atomic_fetch_add(a.rtick + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket != a.S - 1) return;   // another split finishes the tile
+        if (threadIdx.x == 0) __hip_atomic_store(a.rtick + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float tot = 0.f;
+            for (int sp = 0; sp < a.S; ++sp)
+                tot += sp == split ? vsum[b]
+                                   : __hip_atomic_load(a.rpart + (size_t)sp * a.part_stride + (size_t)(16 * b + t) * G.M + m,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            vsum[b] = tot;
+        }
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         float v[NT];
@@ -331,6 +362,7 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
             const int q = n * NB + b;
             v[n] = ((red[q][0][el][rr] + red[q][1][el][rr]) + red[q][2][el][rr]) + red[q][3][el][rr];
         }
+        if (resid && a.S > 1) v[0] = vsum[b];
         const int row = 16 * b + t;
         if constexpr (LN)   // rstd (acc - mean c1) + c2; the constant part once (split 0)
             v[0] = split == 0 ? e_rs[b] * (v[0] - e_mu[b] * e_c1) + e_c2 : e_rs[b] * v[0];
@@ -534,13 +566,14 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyAr
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st) {
     const bool glu = (a.mode == SK_FRAG_GEGLU || a.mode == SK_FRAG_SWIGLU);
     if (!a.zeros) return hipErrorInvalidValue;
-    if (a.ln_stats) {   // the LayerNorm fold: bf16, one matrix, every group with its c1 / c2
-        if (wtype != SKW_BF16 || glu || a.ln_tiles < 1 || a.ln_tiles > LN_MAX_TILES / a.nb) return hipErrorInvalidValue;
+    if (a.ln_stats) {   // the LayerNorm fold: bf16, one matrix, every group with its c1 / c2, not a residual update
+        if (wtype != SKW_BF16 || glu || a.ln_tiles < 1 || a.ln_tiles > LN_MAX_TILES / a.nb || a.mode == SK_RESID)
+            return hipErrorInvalidValue;
         for (int i = 0; i < a.ngroups; ++i)
             if (!a.g[i].c12) return hipErrorInvalidValue;
     }
-    if (a.mode == SK_RESID &&
-        (wtype != SKW_BF16 || a.S != 1 || !a.rx || !a.rbase || !a.ryscale || !a.rstats || a.ngroups != 1))
+    if (a.mode == SK_RESID && (wtype != SKW_BF16 || a.S < 1 || !a.rx || !a.rbase || !a.ryscale || !a.rstats ||
+                               a.ngroups != 1 || (a.S > 1 && (!a.rpart || !a.rtick))))
         return hipErrorInvalidValue;
     if (wtype == SKW_BF16) return glu ? launch_nt<2, SKW_BF16>(a, nwg, st) : launch_nt<1, SKW_BF16>(a, nwg, st);
     if (a.mode == SK_RESID) return hipErrorInvalidValue;
