@@ -40,6 +40,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int TMAX = 16;          // rows of one skinny activation matrix
 constexpr int FM_BATCH = 2;       // flow-map requests one batched draft takes (16 rows each)
 constexpr int RTICK_MAX = 256;    // tiles of a split residual update (its output width / 16)
+constexpr int SATICK_MAX = 64;    // heads of the self-attention tail
 constexpr int QKV_SLABS = 4;      // split-K slabs the attention kernels sum while building q (and k, v)
 constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
 constexpr int PF_SPLIT_WGS = 512; // a k-split prefill launch stays within one round (two 128-tile work-groups per CU)
@@ -288,7 +289,8 @@ Plan make_plan(const fm_config& c) {
     p.lnstats = take(fmv ? (size_t)(c.dim / 16) * FM_BATCH * TMAX * 8 : 0);
     p.c12 = take(fmv ? c12_floats(c) * 4 : 0);
     p.lnfrag = take(fmv ? (size_t)(3 * c.layers + 1) * c.dim * 64 : 0);
-    p.rtick = take(fmv ? (size_t)RTICK_MAX * 4 : 0);   // a split residual update's per-tile arrival counters
+    // arrival counters: a split residual update's per tile, then the self-attention tail's per head
+    p.rtick = take(fmv ? (size_t)(RTICK_MAX + SATICK_MAX) * 4 : 0);
     // the persistent draft kernel: its arguments and per-layer table (device copies), its barrier counters and its
     // activation arena (sized for the most work-groups it may run with)
     const bool pk = draft_supported(c);
@@ -469,6 +471,7 @@ struct SkExtra {
     const float* ryscale = nullptr;
     float* rstats = nullptr;
     float* rdebug = nullptr;
+    SelfAttnArgs sa{};   // q | k | v with the self-attention tail (sa.qkv set)
 };
 
 // Enqueue one skinny launch. For SK_PARTIAL the k-split is chosen here (returned through S_out); every other mode
@@ -532,6 +535,8 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         a.ryscale = ex->ryscale;
         a.rstats = ex->rstats;
         a.rdebug = ex->rdebug;
+        a.sa = ex->sa;
+        if (a.sa.qkv) a.satick = d->at<uint32_t>(d->p.rtick) + RTICK_MAX;
     }
     if (mode == SK_RESID && !ex) return fail(FM_E_INVALID, "skinny: a residual update needs its operands");
     if (mode == SK_RESID && S > 1) {
@@ -911,7 +916,22 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
         // q | k | v of the self-attention LN-mod (x and its fragments from the previous layer's fc2); layer 0's are
         // the same for every draft (flowmap_layer0)
         if (l > 0) {
-            const SkExtra ef = fold();
+            SkExtra ef = fold();   // with the self-attention tail: the head's last q | k | v tile runs it
+            ef.sa.qkv = qkv;
+            ef.sa.T = T;
+            ef.sa.D = D;
+            ef.sa.heads = H;
+            ef.sa.hd = hd;
+            ef.sa.qn = d->B(LW(l, "self_attn.q_norm.weight"));
+            ef.sa.kn = d->B(LW(l, "self_attn.k_norm.weight"));
+            ef.sa.eps = c.qk_eps;
+            ef.sa.rope_tab = rope;
+            ef.sa.pos_base = bas[0]->pos + 1;
+            ef.sa.pos_base1 = bas[B - 1]->pos + 1;
+            ef.sa.nb = B;
+            ef.sa.scale = 1.f / sqrtf((float)hd);
+            ef.sa.o_frag = fragO;
+            if (H > SATICK_MAX) return fail(FM_E_UNSUPPORTED, "more than %d heads", SATICK_MAX);
             std::vector<SkGroupDesc> g = {
                 {d->W(LW(l, "self_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, 3 * D},
                 {d->W(LW(l, "self_attn.k_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
@@ -919,26 +939,6 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
                  3 * D}};
             for (int i = 0; i < 3; ++i) g[i].c12 = C12(l, i);
             CHK(skinny(d, g, D, T, SK_F32, 0, nullptr, st, 0, 0, B, &ef));
-            {
-                SelfAttnArgs a{};
-                a.qkv = qkv;
-                a.parts = 1;
-                a.pstride = 0;
-                a.T = T;
-                a.D = D;
-                a.heads = H;
-                a.hd = hd;
-                a.qn = d->B(LW(l, "self_attn.q_norm.weight"));
-                a.kn = d->B(LW(l, "self_attn.k_norm.weight"));
-                a.eps = c.qk_eps;
-                a.rope_tab = rope;
-                a.pos_base = bas[0]->pos + 1;
-                a.pos_base1 = bas[B - 1]->pos + 1;
-                a.nb = B;
-                a.scale = 1.f / sqrtf((float)hd);
-                a.o_frag = fragO;
-                HIPCHK(launch_self_attn(a, st));
-            }
             // o_proj and the gated residual; fragments of the cross-attention LN-mod's x (1 + scale)
             const SkExtra er = resid(x, D, m_sa + 2 * D, m_ca, nullptr);
             CHK(skinny(d, {{d->W(LW(l, "self_attn.o_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragO, fragH, D,
@@ -949,7 +949,8 @@ fm_status flowmap_draft_batch(fm_drafter* const* ds, int B, const fm_block_args*
             SkGroupDesc gq{d->W(LW(l, "cross_attn.q_proj.weight")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D,
                            D};
             gq.c12 = C12(l, 3);
-            CHK(skinny(d, {gq}, D, T, SK_PARTIAL, Sq, &Sqb, st, (long long)TMAX * B * D, d->p.qkv_floats, B, &ef));
+            const SkExtra efq = fold();
+            CHK(skinny(d, {gq}, D, T, SK_PARTIAL, Sq, &Sqb, st, (long long)TMAX * B * D, d->p.qkv_floats, B, &efq));
         }
         for (int b = 0; b < B; ++b) {   // each request over its own cache rows [0, pos_b]
             QPrep qp{};
@@ -1166,7 +1167,8 @@ fm_status flowmap_draft_persistent(fm_drafter* d, const fm_block_args* ba, float
 fm_status flowmap_create(fm_drafter* d, hipStream_t st) {
     const auto& c = d->c;
     const int Ht = c.target_dim, D = c.dim;
-    HIPCHK(launch_fill_u32(d->at<uint32_t>(d->p.rtick), RTICK_MAX, 0u, st));   // each last arrival resets its own
+    HIPCHK(launch_fill_u32(d->at<uint32_t>(d->p.rtick), RTICK_MAX + SATICK_MAX, 0u, st));   // each last arrival
+                                                                                            // resets its own
     HIPCHK(hipMemcpyAsync(d->at<float>(d->p.modc), d->F("mod"), (size_t)(3 * c.layers + 1) * 3 * D * 4,
                           hipMemcpyDeviceToDevice, st));
     // zero-noise slot input h0 = x_embed(state_norm(mean row of E)) + b

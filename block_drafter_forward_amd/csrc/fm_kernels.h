@@ -23,6 +23,22 @@ enum SkinnyOut {
 enum SkinnyWType { SKW_BF16 = 0, SKW_Q8_0 = 1 };
 
 #define SK_MAX_GROUPS 12
+// Flow-map self-attention over the T slots of each block of rows, one head at a time (fm_selfattn.h): run by the
+// q | k | v product's last work-group of each head (SkinnyArgs.sa); writes o as fragments.
+struct SelfAttnArgs {
+    const float* qkv;      // [rows][3D]: q | k | v (null: no self-attention)
+    int T, D, heads, hd;
+    const uint16_t* qn;    // q_norm, k_norm (bf16 [hd])
+    const uint16_t* kn;
+    float eps;
+    const float* rope_tab;
+    int pos_base;          // RoPE position of row 0 of block 0
+    float scale;
+    uint8_t* o_frag;
+    int nb;                // blocks of T rows attending each within itself (1 or 2): block b's rows are rows 16 b + t
+    int pos_base1;         //   of qkv (T = 16) and of the o fragments (K = D); its RoPE positions start at pos_base1
+};
+
 struct SkinnyGroup {
     const void* W;        // bf16 [M][K], or Q8_0 codes int8 [M][K]
     const void* Wd;       // Q8_0 scales f16 [M][K/32] (else null)
@@ -68,6 +84,11 @@ struct SkinnyArgs {
     float* rdebug;        // optional copy of x (same layout)
     float* rpart;         // S > 1: the splits' partial tiles [S][rows][M] (slab stride part_stride)
     uint32_t* rtick;      // S > 1: one arrival counter per 16-row tile, zero between launches
+    // q | k | v followed by the self-attention (SK_F32, the LayerNorm fold, three groups q, k, v of D rows each,
+    // S = 1): the outputs are stored device-coherent, each tile's work-group takes a ticket on its head's counter
+    // (satick[head], zero between launches), and the head's last arrival (3 hd / 16 of them) runs its attention
+    SelfAttnArgs sa;
+    uint32_t* satick;
 };
 #define LN_MAX_TILES 256   // LayerNorm fold: x at most 4096 wide (2048 with two blocks of rows)
 // Q8_0 weights run the tile-owning variant: a work-group of SK_WS_WAVES waves owns that many adjacent 16-row tiles
@@ -170,23 +191,6 @@ struct QPrep {             // how a work-group builds its query rows for one hea
     int parts;             // q is the sum of this many split-K slabs (0 or 1: one), slab i at q + i * pstride
     long long pstride;     //   (honoured by the f16-cache kernel; the f32-cache kernel takes one slab)
 };
-// Flow-map self-attention over the T slots (one work-group per head); writes o as fragments.
-struct SelfAttnArgs {
-    const float* qkv;      // [T][3D]: q | k | v, the sum of `parts` split-K slabs pstride floats apart
-    int parts;
-    long long pstride;
-    int T, D, heads, hd;
-    const uint16_t* qn;    // q_norm, k_norm (bf16 [hd])
-    const uint16_t* kn;
-    float eps;
-    const float* rope_tab;
-    int pos_base;
-    float scale;
-    uint8_t* o_frag;
-    int nb;                // blocks of T rows attending each within itself (1 or 2): block b's rows are rows 16 b + t
-    int pos_base1;         //   of qkv (T = 16) and of the o fragments (K = D); its RoPE positions start at pos_base1
-};
-hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st);
 
 struct AttnArgs {
     QPrep qp;

@@ -1,9 +1,5 @@
 // k_attn.hip — K4: the drafter's attention kernels.
 //
-//  self_attn     flow-map self-attention over the T slots (one work-group per head): per-head q/k RMSNorm,
-//                interleaved RoPE at the slots' positions, softmax(q kᵀ / sqrt(hd)) v with no mask
-//                (flashmap_drafter.js: headNormRope, attnF32), in f32 registers with two LDS exchanges;
-//                o leaves as fragments for the o_proj GEMM.
 //  attn_split    up to 16 query rows of one head against one chunk of keys (cache rows, then optional extra f32
 //                rows): scores, chunk max, exp-sum and the unnormalised P·V, written as a partial; both products run
 //                on the matrix cores (f32 caches split into f16 hi + lo). Splitting the key
@@ -21,123 +17,10 @@
 
 namespace {
 
-constexpr int MAX_QSLABS = 4;   // split-K slabs of q (and of the self-attention's k, v) summed in the prologue
+constexpr int MAX_QSLABS = 4;   // split-K slabs of q summed in the prologue
 
 // native 4 x u32 vector: arrays of it stay in registers where arrays of the HIP uint4 class may not
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// ── self-attention ───────────────────────────────────────────────────────────────────────────────
-// One work-group per head, built for latency (the whole op is 16 x 16 x hd): every global load (q, k, v rows, the
-// norm weights and the slots' RoPE rows) is issued up front; thread (row, segment) holds hd/8 consecutive values of
-// one q or k row, so the head-RMSNorm is an 8-lane shuffle reduction and the interleaved RoPE pairs stay inside the
-// thread; then one LDS exchange for the scores (thread = (query, key), 16-lane softmax by shuffles) and one for
-// P·V, whose 8 consecutive outputs per thread go straight out as fragments. All arithmetic in f32.
-template <int HD>
-__global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
-    constexpr int SEG = HD / 8, VPT = HD / 16, QP = HD + 4;
-    __shared__ __attribute__((aligned(16))) float QK[32 * QP];
-    __shared__ __attribute__((aligned(16))) float Vs[16 * QP];
-    __shared__ float Ps[16][17];
-    const int h = blockIdx.x, blk = blockIdx.y, tid = threadIdx.x;
-    const int T = a.T, D = a.D;
-    const float* qkv = a.qkv + (size_t)blk * 16 * 3 * D;   // this block's rows
-    const int pos_base = blk ? a.pos_base1 : a.pos_base;
-    const int row = tid >> 3, seg = tid & 7;            // q rows 0..15, k rows 16..31
-    const int w = row >> 4, t = row & 15, tc = min(t, T - 1);
-    float x[SEG], cs[SEG / 2], sn[SEG / 2], nw[SEG], v[VPT];
-    {
-        const float* src = qkv + (size_t)tc * 3 * D + (size_t)w * D + (size_t)h * HD + seg * SEG;
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) x[j] = 0.f;
-#pragma unroll
-        for (int p = 0; p < MAX_QSLABS; ++p) {   // every slab load issued together; absent slabs re-read slab 0
-            const float m = p < a.parts ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < SEG / 4; ++j) {
-                const float4 f = ((const float4*)(src + (p < a.parts ? p : 0) * a.pstride))[j];
-                x[4 * j] += m * f.x; x[4 * j + 1] += m * f.y; x[4 * j + 2] += m * f.z; x[4 * j + 3] += m * f.w;
-            }
-        }
-        const float* rt = a.rope_tab + (size_t)(pos_base + tc) * HD + seg * (SEG / 2);
-#pragma unroll
-        for (int j = 0; j < SEG / 8; ++j) {
-            const float4 c = ((const float4*)rt)[j], sv = ((const float4*)(rt + HD / 2))[j];
-            cs[4 * j] = c.x; cs[4 * j + 1] = c.y; cs[4 * j + 2] = c.z; cs[4 * j + 3] = c.w;
-            sn[4 * j] = sv.x; sn[4 * j + 1] = sv.y; sn[4 * j + 2] = sv.z; sn[4 * j + 3] = sv.w;
-        }
-        const uint16_t* n = (w ? a.kn : a.qn) + seg * SEG;
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) nw[j] = bf16_to_f32(n[j]);
-        const int vt = min(tid >> 4, T - 1), vp = tid & 15;
-        const float* vs = qkv + (size_t)vt * 3 * D + 2 * (size_t)D + (size_t)h * HD + vp * VPT;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) v[j] = 0.f;
-#pragma unroll
-        for (int p = 0; p < MAX_QSLABS; ++p) {
-            const float m = p < a.parts ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < VPT / 4; ++j) {
-                const float4 f = ((const float4*)(vs + (p < a.parts ? p : 0) * a.pstride))[j];
-                v[4 * j] += m * f.x; v[4 * j + 1] += m * f.y; v[4 * j + 2] += m * f.z; v[4 * j + 3] += m * f.w;
-            }
-        }
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < SEG; ++j) ss += x[j] * x[j];
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    const float r = 1.f / sqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-    for (int j = 0; j < SEG / 2; ++j) {
-        const float x0 = x[2 * j] * (nw[2 * j] * r), x1 = x[2 * j + 1] * (nw[2 * j + 1] * r);
-        x[2 * j] = x0 * cs[j] - x1 * sn[j];
-        x[2 * j + 1] = x1 * cs[j] + x0 * sn[j];
-    }
-#pragma unroll
-    for (int j = 0; j < SEG / 4; ++j)
-        *(float4*)(QK + row * QP + seg * SEG + 4 * j) = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
-#pragma unroll
-    for (int j = 0; j < VPT / 4; ++j)
-        *(float4*)(Vs + (tid >> 4) * QP + (tid & 15) * VPT + 4 * j) =
-            make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-    __syncthreads();
-    {
-        const int qt = tid >> 4, u = tid & 15;
-        const float* q = QK + qt * QP;
-        const float* k = QK + (16 + u) * QP;
-        float s = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < HD; d += 4) {
-            const float4 qa = *(const float4*)(q + d), kb = *(const float4*)(k + d);
-            s += qa.x * kb.x + qa.y * kb.y + qa.z * kb.z + qa.w * kb.w;
-        }
-        s = u < T ? s * a.scale : -INFINITY;
-        float m = s;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        const float e = u < T ? expf(s - m) : 0.f;
-        float z = e;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
-        Ps[qt][u] = e / z;
-    }
-    __syncthreads();
-    if (tid < 2 * HD) {
-        const int ot = tid / (HD / 8), d0 = (tid % (HD / 8)) * 8;
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
-        for (int u = 0; u < T; ++u) {
-            const float p = Ps[ot][u];
-            const float4 v0 = *(const float4*)(Vs + u * QP + d0), v1 = *(const float4*)(Vs + u * QP + d0 + 4);
-            o[0] += p * v0.x; o[1] += p * v0.y; o[2] += p * v0.z; o[3] += p * v0.w;
-            o[4] += p * v1.x; o[5] += p * v1.y; o[6] += p * v1.z; o[7] += p * v1.w;
-        }
-        if (ot < T) frag_store8(a.o_frag + (size_t)blk * D * 64, ot, h * HD + d0, o);
-    }
-}
 
 // ── split-L attention on the matrix cores, one key run per wave (f16 cache, V tiled by 32 positions) ─
 // A work-group of 4 waves builds the head's queries once (thread (query t, segment) holds hd/16 consecutive values:
@@ -689,17 +572,6 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
 
 }  // namespace
 
-hipError_t launch_self_attn(const SelfAttnArgs& a, hipStream_t st) {
-    if (a.T < 1 || a.T > 16 || a.parts < 1 || a.parts > MAX_QSLABS || a.nb < 0 || a.nb > 2 || (a.nb == 2 && a.T != 16))
-        return hipErrorInvalidValue;
-    const dim3 grid(a.heads, a.nb > 1 ? a.nb : 1);
-    switch (a.hd) {
-    case 64: self_attn_kernel<64><<<grid, 256, 0, st>>>(a); break;
-    case 128: self_attn_kernel<128><<<grid, 256, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
 
 // The f32-cache matrix-core kernel: head widths 128 / 256, queries ready-made, G * nq <= 48.
 static bool f32_mfma_fits(const AttnArgs& a) {

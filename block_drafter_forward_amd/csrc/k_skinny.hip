@@ -20,6 +20,7 @@
 #include "fm_device.h"
 #include "fm_kernels.h"
 #include "fm_ws.h"
+#include "fm_selfattn.h"
 
 namespace {
 
@@ -183,7 +184,8 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     // LayerNorm statistics (float2 [ln_tiles][R], ln_tiles R / 128 KB) straight into LDS, 1 KB per wave instruction,
     // issued right after the first chunk's loads: loads complete in issue order, so the first chunk's wait covers
     // them too, and the statistics are reduced (ln_reduce) between the first chunk's products and the next chunk's
-    __shared__ float2 lnlds[LN ? LN_MAX_TILES * 16 : 1];
+    // (after the statistics are reduced, the q | k | v product's self-attention tail reuses this LDS)
+    __shared__ __attribute__((aligned(16))) float2 lnlds[LN ? LN_MAX_TILES * 16 : 1];
     float e_c1 = 0.f, e_c2 = 0.f;
     if constexpr (LN) {
         e_c1 = G.c12[e_m];
@@ -367,7 +369,11 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
         if constexpr (LN)   // rstd (acc - mean c1) + c2; the constant part once (split 0)
             v[0] = split == 0 ? e_rs[b] * (v[0] - e_mu[b] * e_c1) + e_c2 : e_rs[b] * v[0];
         if (a.mode == SK_F32) {
-            if (t < a.T) ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + e_bias;
+            if (t < a.T) {
+                float* dst = (float*)G.out + (size_t)row * G.ld + m;
+                if (LN && a.sa.qkv) __hip_atomic_store(dst, v[0] + e_bias, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else *dst = v[0] + e_bias;
+            }
         } else if (a.mode == SK_PARTIAL) {
             if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)row * G.ld + m] = v[0];
         } else if (a.mode == SK_RESID) {
@@ -390,7 +396,30 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
             tile[b][t][ml] = o;
         }
     }
-    if (!frag_mode) return;
+    if (!frag_mode) {
+        if constexpr (LN) {
+            if (a.sa.qkv) {   // q | k | v stored device-coherent: the head's last tile to arrive runs its attention
+                __shared__ int sticket;
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are performed
+                __syncthreads();                                    // and every thread's
+                const int head = m0 / a.sa.hd;
+                if (threadIdx.x == 0)
+                    sticket = (int)__hip_atomic_fetch_add(a.satick + head, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                if (sticket != 3 * (a.sa.hd / 16) - 1) return;   // another tile of the head finishes it
+                if (threadIdx.x == 0) __hip_atomic_store(a.satick + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                float* QK = (float*)lnlds;   // the statistics are reduced: the LDS is free
+                float* Vs = QK + 32 * (a.sa.hd + 4);
+                float(*Ps)[17] = (float(*)[17])(Vs + 16 * (a.sa.hd + 4));
+                for (int b = 0; b < a.sa.nb; ++b) {
+                    if (a.sa.hd == 128) sattn::head<128>(a.sa, head, b, QK, Vs, Ps);
+                    else sattn::head<64>(a.sa, head, b, QK, Vs, Ps);
+                }
+            }
+        }
+        return;
+    }
     __syncthreads();
     if (resid && threadIdx.x < R) {   // (mean, M2) of each row of x over the tile's 16 columns
         const int b = threadIdx.x >> 4, tt = threadIdx.x & 15;
@@ -572,6 +601,11 @@ hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st
         for (int i = 0; i < a.ngroups; ++i)
             if (!a.g[i].c12) return hipErrorInvalidValue;
     }
+    if (a.sa.qkv &&   // the self-attention tail: a LayerNorm-folded unsplit q | k | v product of whole heads
+        (!a.ln_stats || a.mode != SK_F32 || a.S != 1 || a.ngroups != 3 || !a.satick || a.nb != a.sa.nb ||
+         (a.sa.hd != 64 && a.sa.hd != 128) || a.sa.T < 1 || a.sa.T > 16 || a.sa.D % a.sa.hd ||
+         32 * (a.sa.hd + 4) * 4 + 16 * (a.sa.hd + 4) * 4 + 16 * 17 * 4 > LN_MAX_TILES * 16 * 8))
+        return hipErrorInvalidValue;
     if (a.mode == SK_RESID && (wtype != SKW_BF16 || a.S < 1 || !a.rx || !a.rbase || !a.ryscale || !a.rstats ||
                                a.ngroups != 1 || (a.S > 1 && (!a.rpart || !a.rtick))))
         return hipErrorInvalidValue;
