@@ -62,19 +62,36 @@ def draft_step_bytes(cfg, L: int) -> int:
 
 def skinny_step_bytes(cfg) -> int:
     """Algorithmic HBM bytes of the skinny GEMM launches (K1) of one flow-map draft: each launch's bf16 weights and
-    biases once, its activation rows once (hi/lo bf16 pairs: 4 bytes an element) and its f32 result once. The
-    launches: anchor_proj (1 row); the 12 cross K / V projections of the anchor row (one launch); layer 0 from its
-    cross o_proj (cross o_proj, fc1, fc2); every further layer's q | k | v, self o_proj, cross q_proj, cross o_proj,
-    fc1, fc2 (16 rows); the head."""
-    D, Ht, F, Lyr, T = cfg["dim"], cfg["target_dim"], cfg["ffn"], cfg["layers"], cfg["block"]
+    biases once, its activation rows once (hi/lo bf16 pairs: 4 bytes an element) and its result once, plus what its
+    fused epilogue moves. The launches: anchor_proj (1 row); the 12 cross K / V projections of the anchor row (one
+    launch); layer 0 from its cross o_proj (cross o_proj, fc1, fc2); every further layer's q | k | v, self o_proj,
+    cross q_proj, cross o_proj, fc1, fc2 (16 rows); the head.
+      * residual update (o_proj, cross o_proj, fc2): reads the residual rows x (layer 0's cross o_proj one broadcast
+        row), the gate and the next modulation's scale row; writes x, the next product's fragments and x's
+        (mean, M2) per 16-column tile;
+      * LayerNorm fold (q | k | v, cross q_proj, fc1, head): reads those tile statistics and each matrix's c1 / c2;
+      * self-attention in the q | k | v launch: reads the head-norm weights and the slots' RoPE rows, writes o as
+        fragments (q, k, v themselves are its f32 result, counted once)."""
+    D, Ht, F, Lyr, T, hd = cfg["dim"], cfg["target_dim"], cfg["ffn"], cfg["layers"], cfg["block"], cfg["head_dim"]
 
     def g(M, K, rows, bias=0, groups=1):   # one launch: `groups` M x K matrices over the same rows
         return groups * (2 * M * K + 2 * bias + 4 * rows * M) + 4 * rows * K
+
+    def resid(M, rows, base_rows):         # x read (base rows) and written, gate + scale rows, tile statistics
+        return 4 * base_rows * M + 4 * rows * M + 8 * M + 8 * rows * (M // 16)
+
+    def ln(K, rows, M, groups=1):          # the statistics of the input rows, c1 / c2 of each matrix
+        return 8 * rows * (K // 16) + groups * 8 * M
+
+    sa = 2 * 2 * hd + 4 * T * hd + 4 * T * D   # q / k norm weights, RoPE rows, o fragments
     b = g(D, Ht, 1) + g(D, D, 1, groups=2 * Lyr)
-    mlp = g(F, D, T, bias=F) + g(D, F, T)
-    b += g(D, D, T) + mlp
-    b += (Lyr - 1) * (g(D, D, T, groups=3) + 3 * g(D, D, T) + mlp)
-    b += g(Ht, D, T, bias=Ht)
+    mlp = g(F, D, T, bias=F) + ln(D, T, F) + g(D, F, T, bias=D) + resid(D, T, T)
+    b += g(D, D, T) + resid(D, T, 1) + mlp                                   # layer 0
+    b += (Lyr - 1) * (g(D, D, T, groups=3) + ln(D, T, D, 3) + sa           # q | k | v + self-attention
+                      + g(D, D, T) + resid(D, T, T)                         # o_proj
+                      + g(D, D, T) + ln(D, T, D)                            # cross q_proj
+                      + g(D, D, T) + resid(D, T, T) + mlp)                  # cross o_proj, MLP
+    b += g(Ht, D, T, bias=Ht) + ln(D, T, Ht)
     return b
 
 

@@ -34,6 +34,24 @@ __device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Device-coherent 16-byte store / load (written through / read past the non-coherent caches): buffer instructions
+// with the device-coherent cache policy bit.
+// base is wave-uniform (the buffer resource lives in scalar registers), idx the lane's float offset from it.
+constexpr int SC1 = 16;
+__device__ __forceinline__ void cst16(float* base, size_t idx, float4 v) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)}, r,
+        (unsigned)(idx * 4), 0, SC1);
+}
+__device__ __forceinline__ float4 cld16(const float* base, size_t idx) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (unsigned)(idx * 4), 0, SC1);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
 // LDS-direct load: lane l's 16 bytes from g land at lds + 16 l (lds wave-uniform, through m0). In inline asm, so
 // the compiler's wait bookkeeping does not see it (a tracked LDS-direct load would make it wait for every load in
 // flight at the next LDS read); its reader waits explicitly.
@@ -329,15 +347,21 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     // (written through to memory), waits until they are performed, then takes a ticket on the tile's counter. The
     // split that draws the last ticket adds the S partials in split order (deterministic), resets the counter for
     // the next launch and finishes the tile; the others are done. Nothing ever waits on another work-group.
+    // The partial tiles go out and come back as 16-byte rows (thread q of a block: row q / 4, columns 4 (q % 4) ..),
+    // staged through LDS: one write-through transaction per 16 bytes rather than one per element.
     float vsum[NB];
     if (resid && a.S > 1) {
         __shared__ int ticket;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int q = b;
-            vsum[b] = ((red[q][0][el][rr] + red[q][1][el][rr]) + red[q][2][el][rr]) + red[q][3][el][rr];
-            __hip_atomic_store(a.rpart + (size_t)split * a.part_stride + (size_t)(16 * b + t) * G.M + m, vsum[b],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            vsum[b] = ((red[b][0][el][rr] + red[b][1][el][rr]) + red[b][2][el][rr]) + red[b][3][el][rr];
+            tile[b][t][ml] = vsum[b];
+        }
+        __syncthreads();
+        if (threadIdx.x < 64 * NB) {
+            const int b = threadIdx.x >> 6, q = threadIdx.x & 63, tr = q >> 2, c4 = 4 * (q & 3);
+            cst16(a.rpart, (size_t)split * a.part_stride + (size_t)(16 * b + tr) * G.M + m0 + c4,
+                  make_float4(tile[b][tr][c4], tile[b][tr][c4 + 1], tile[b][tr][c4 + 2], tile[b][tr][c4 + 3]));
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores are performed
         __syncthreads();                                    // and every thread's
@@ -346,15 +370,27 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
         __syncthreads();
         if (ticket != a.S - 1) return;   // another split finishes the tile
         if (threadIdx.x == 0) __hip_atomic_store(a.rtick + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float tot[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            float tot = 0.f;
-            for (int sp = 0; sp < a.S; ++sp)
-                tot += sp == split ? vsum[b]
-                                   : __hip_atomic_load(a.rpart + (size_t)sp * a.part_stride + (size_t)(16 * b + t) * G.M + m,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            vsum[b] = tot;
+        for (int b = 0; b < NB; ++b) tot[b] = 0.f;
+        for (int sp = 0; sp < a.S; ++sp) {   // split order: the sum is the same whichever split finishes
+            if (sp == split) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) tot[b] += vsum[b];
+                continue;
+            }
+            if (threadIdx.x < 64 * NB) {   // the other split's tile, through LDS (xt: free until the epilogue)
+                const int b = threadIdx.x >> 6, q = threadIdx.x & 63, tr = q >> 2, c4 = 4 * (q & 3);
+                const float4 f = cld16(a.rpart, (size_t)sp * a.part_stride + (size_t)(16 * b + tr) * G.M + m0 + c4);
+                xt[b][tr][c4] = f.x; xt[b][tr][c4 + 1] = f.y; xt[b][tr][c4 + 2] = f.z; xt[b][tr][c4 + 3] = f.w;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < NB; ++b) tot[b] += xt[b][t][ml];
+            __syncthreads();
         }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) vsum[b] = tot[b];
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -369,11 +405,8 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
         if constexpr (LN)   // rstd (acc - mean c1) + c2; the constant part once (split 0)
             v[0] = split == 0 ? e_rs[b] * (v[0] - e_mu[b] * e_c1) + e_c2 : e_rs[b] * v[0];
         if (a.mode == SK_F32) {
-            if (t < a.T) {
-                float* dst = (float*)G.out + (size_t)row * G.ld + m;
-                if (LN && a.sa.qkv) __hip_atomic_store(dst, v[0] + e_bias, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else *dst = v[0] + e_bias;
-            }
+            if (LN && a.sa.qkv) tile[b][t][ml] = v[0] + e_bias;   // stored device-coherent below, 16 bytes a thread
+            else if (t < a.T) ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + e_bias;
         } else if (a.mode == SK_PARTIAL) {
             if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)row * G.ld + m] = v[0];
         } else if (a.mode == SK_RESID) {
@@ -400,6 +433,13 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
         if constexpr (LN) {
             if (a.sa.qkv) {   // q | k | v stored device-coherent: the head's last tile to arrive runs its attention
                 __shared__ int sticket;
+                __syncthreads();
+                if (threadIdx.x < 64 * NB) {
+                    const int b = threadIdx.x >> 6, q = threadIdx.x & 63, tr = q >> 2, c4 = 4 * (q & 3);
+                    if (tr < a.T)
+                        cst16((float*)G.out, (size_t)(16 * b + tr) * G.ld + m0 + c4,
+                              make_float4(tile[b][tr][c4], tile[b][tr][c4 + 1], tile[b][tr][c4 + 2], tile[b][tr][c4 + 3]));
+                }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are performed
                 __syncthreads();                                    // and every thread's
                 const int head = m0 / a.sa.hd;
