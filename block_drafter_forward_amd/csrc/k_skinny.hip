@@ -162,14 +162,16 @@ __device__ __forceinline__ void rs_compute(const RsStage<NT, RC, NB>& st, uint4*
 // in flight together. UP = 0: KW is a multiple of 2*SKC and stages are double-buffered (stage i+1 in flight while
 // stage i computes), with the last pair peeled so the loop body carries no conditions.
 // NB = 2 (two blocks of 16 activation rows against each weight tile) exists with UP = 2 only.
-// LN: the LayerNorm fold of SkinnyArgs (one matrix). Every operand of the epilogue (bias, LayerNorm statistics and
-// c1 / c2, the residual update's base, gate and scale) is loaded before the main loop, so the epilogue waits on no
-// memory round trip of its own.
-template <int NT, int WT, int UP, int SKC, int NB = 1, bool LN = false>
+// EP, the epilogue's kind: EP_PLAIN, EP_LN (the LayerNorm fold of SkinnyArgs, one matrix) or EP_RESID (SK_RESID,
+// one matrix). Every operand of the epilogue (bias, LayerNorm statistics and c1 / c2, the residual update's base,
+// gate and scale) is loaded before the main loop, so the epilogue waits on no memory round trip of its own.
+enum SkEpilogue { EP_PLAIN = 0, EP_LN = 1, EP_RESID = 2 };
+template <int NT, int WT, int UP, int SKC, int NB = 1, int EP = EP_PLAIN>
 __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     static_assert(WT == SKW_BF16, "bf16 weights (Q8_0: skinny_ws_kernel)");
     static_assert(NB == 1 || UP == 2, "two row blocks: row-staged only");
-    static_assert(!LN || NT == 1, "the LayerNorm fold takes one matrix");
+    static_assert(EP == EP_PLAIN || NT == 1, "the LayerNorm fold and the residual update take one matrix");
+    constexpr bool LN = EP == EP_LN;
     const int bid = blockIdx.x;
     int gi = 0;
 #pragma unroll 1
@@ -192,13 +194,15 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     const int e_el = threadIdx.x & 63, e_rr = threadIdx.x >> 6;
     const int e_ml = 4 * (e_el >> 4) + e_rr;   // the element this thread finishes: tile row e_ml, activation row e_t
     const int e_t = e_el & 15, e_m = m0 + e_ml;
-    const bool resid = a.mode == SK_RESID;
+    constexpr bool resid = EP == EP_RESID;   // mode SK_RESID (checked by the launcher)
     const float e_bias = bf16_to_f32(*(G.bias ? G.bias + e_m : (const uint16_t*)a.zeros));   // no branch: no wait
-    float e_base[NB];
+    float e_base[NB], e_gate = 1.f, e_ys = 0.f;
+    if constexpr (resid) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) e_base[b] = *(resid ? a.rbase + (size_t)(16 * b + e_t) * a.rbase_ld + e_m : a.zeros);
-    const float e_gate = *(resid && a.rgate ? a.rgate + e_m : a.zeros);
-    const float e_ys = *(resid ? a.ryscale + e_m : a.zeros);
+        for (int b = 0; b < NB; ++b) e_base[b] = a.rbase[(size_t)(16 * b + e_t) * a.rbase_ld + e_m];
+        e_gate = *(a.rgate ? a.rgate + e_m : a.zeros);
+        e_ys = a.ryscale[e_m];
+    }
     // LayerNorm statistics (float2 [ln_tiles][R], ln_tiles R / 128 KB) straight into LDS, 1 KB per wave instruction,
     // issued right after the first chunk's loads: loads complete in issue order, so the first chunk's wait covers
     // them too, and the statistics are reduced (ln_reduce) between the first chunk's products and the next chunk's
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     // The partial tiles go out and come back as 16-byte rows (thread q of a block: row q / 4, columns 4 (q % 4) ..),
     // staged through LDS: one write-through transaction per 16 bytes rather than one per element.
     float vsum[NB];
-    if (resid && a.S > 1) {
+    if (resid && a.S > 1) {   // (resid: compile-time)
         __shared__ int ticket;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
             else if (t < a.T) ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + e_bias;
         } else if (a.mode == SK_PARTIAL) {
             if (t < a.T) ((float*)G.out)[(size_t)split * a.part_stride + (size_t)row * G.ld + m] = v[0];
-        } else if (a.mode == SK_RESID) {
+        } else if (resid) {
             const float xn = e_base[b] + (a.rgate ? e_gate : 1.f) * (v[0] + e_bias);
             if (t < a.T) {
                 a.rx[(size_t)row * a.rx_ld + m] = xn;
@@ -486,42 +490,43 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     }
 }
 
-template <int NT, int WT, bool LN>
-hipError_t launch_nt_ln(const SkinnyArgs& a, int nwg, hipStream_t st) {
+template <int NT, int WT, int EP>
+hipError_t launch_nt_ep(const SkinnyArgs& a, int nwg, hipStream_t st) {
     const int KW = a.KW;
     dim3 grid(nwg), block(256);
     if (a.nb == 2) {   // two blocks of rows: chunks of 4 k-steps (the registers of two blocks' fragments)
         if constexpr (WT == SKW_BF16) {
             if (KW % 4 || a.T != 16) return hipErrorInvalidValue;
-            skinny_kernel<NT, WT, 2, 4, 2, LN><<<grid, block, 0, st>>>(a);
+            skinny_kernel<NT, WT, 2, 4, 2, EP><<<grid, block, 0, st>>>(a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
     if (a.nb != 1) return hipErrorInvalidValue;
     if (KW % 4 == 0) {
-        if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8, 1, LN><<<grid, block, 0, st>>>(a);
-        else skinny_kernel<NT, WT, 2, 4, 1, LN><<<grid, block, 0, st>>>(a);
+        if (KW % 8 == 0) skinny_kernel<NT, WT, 2, 8, 1, EP><<<grid, block, 0, st>>>(a);
+        else skinny_kernel<NT, WT, 2, 4, 1, EP><<<grid, block, 0, st>>>(a);
         return hipGetLastError();
     }
-#define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n, 1, LN><<<grid, block, 0, st>>>(a); return hipGetLastError();
+#define SK_UP(n) case n: skinny_kernel<NT, WT, 1, n, 1, EP><<<grid, block, 0, st>>>(a); return hipGetLastError();
     switch (KW) {
         SK_UP(1) SK_UP(2) SK_UP(3) SK_UP(5) SK_UP(6) SK_UP(10)
     default: break;
     }
 #undef SK_UP
-    if (KW > 16 && KW % 2 == 0) skinny_kernel<NT, WT, 0, 1, 1, LN><<<grid, block, 0, st>>>(a);
+    if (KW > 16 && KW % 2 == 0) skinny_kernel<NT, WT, 0, 1, 1, EP><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 template <int NT, int WT>
 hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
-    if (a.ln_stats) {
-        if constexpr (NT == 1) return launch_nt_ln<1, WT, true>(a, nwg, st);
+    if (a.ln_stats || a.mode == SK_RESID) {
+        if constexpr (NT == 1)
+            return a.ln_stats ? launch_nt_ep<1, WT, EP_LN>(a, nwg, st) : launch_nt_ep<1, WT, EP_RESID>(a, nwg, st);
         return hipErrorInvalidValue;
     }
-    return launch_nt_ln<NT, WT, false>(a, nwg, st);
+    return launch_nt_ep<NT, WT, EP_PLAIN>(a, nwg, st);
 }
 
 // ── Q8_0: the tile-owning variant ──────────────────────────────────────────────────────────────
