@@ -13,11 +13,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Two values split into their hi / lo bf16 terms, packed by pairs: hi = RNE(x), lo = RNE(x - hi) (x - hi is exact
+// in f32), both rounded to nearest even by gfx950's v_cvt_pk_bf16_f32, one instruction per pair.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const f32x2_t v = {a, b};
+    const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    const f32x2_t r = v - __builtin_convertvector(h, f32x2_t);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
@@ -49,13 +54,7 @@ __device__ __forceinline__ size_t frag_offset(int t, int k) {   // byte offset o
 __device__ __forceinline__ void frag_store8(uint8_t* frag, int t, int k, const float* v) {
     uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-        uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
-        uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
+    for (int i = 0; i < 4; ++i) split_pair(v[2 * i], v[2 * i + 1], hi[i], lo[i]);
     uint8_t* p = frag + frag_offset(t, k);
     *(uint4*)p = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     *(uint4*)(p + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);

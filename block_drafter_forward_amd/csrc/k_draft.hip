@@ -245,10 +245,10 @@ __device__ __forceinline__ void afrag8(__amdgpu_buffer_rsrc_t r, uint32_t base, 
     u32x4 hi, lo;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-        const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        uint32_t h, l;
+        split_pair(v[2 * i], v[2 * i + 1], h, l);
+        hi[i] = h;
+        lo[i] = l;
     }
     const uint32_t off = base + (uint32_t)frag_offset(t, k);
     ast16(r, off, hi);
@@ -516,13 +516,8 @@ __device__ __forceinline__ bool gemm_run(Ctx& x, const DraftArgs& a, int k, int 
                 const float* cv = cvec + (s0 + i) * 32 + 8 * g4;
                 uint32_t hh[4], ll[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v0 = r == 0 ? cv[2 * e] : 0.f, v1 = r == 0 ? cv[2 * e + 1] : 0.f;
-                    const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-                    hh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                    ll[e] = (uint32_t)f32_to_bf16(v0 - bf16_to_f32(h0)) |
-                            ((uint32_t)f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
-                }
+                for (int e = 0; e < 4; ++e)
+                    split_pair(r == 0 ? cv[2 * e] : 0.f, r == 0 ? cv[2 * e + 1] : 0.f, hh[e], ll[e]);
                 h[i] = u32x4{hh[0], hh[1], hh[2], hh[3]};
                 lo[i] = u32x4{ll[0], ll[1], ll[2], ll[3]};
             }
