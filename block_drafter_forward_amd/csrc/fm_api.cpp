@@ -41,6 +41,9 @@ constexpr int TMAX = 16;          // rows of one skinny activation matrix
 constexpr int FM_BATCH = 2;       // flow-map requests one batched draft takes (16 rows each)
 constexpr int RTICK_MAX = 256;    // tiles of a split residual update (its output width / 16)
 constexpr int SATICK_MAX = 64;    // heads of the self-attention tail
+// the KV-injection residual updates run unsplit (64 work-groups at its width 1024: 435.9 us per draft against
+// 445.8 us split in two with an arrival ticket and 452.8 us split in four)
+constexpr int KVI_RESID_SPLIT = 1;
 constexpr int QKV_SLABS = 4;      // split-K slabs the attention kernels sum while building q (and k, v)
 constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
 constexpr int PF_SPLIT_WGS = 512; // a k-split prefill launch stays within one round (two 128-tile work-groups per CU)
@@ -286,11 +289,12 @@ Plan make_plan(const fm_config& c) {
     // the LayerNorm fold of the flow-map draft: (mean, M2) of each 16-column tile of the residual rows (written by
     // each residual update, read by the next product), c1 / c2 of every product that takes a LayerNorm-modulated
     // row (layer l: q, k, v, cross q, fc1; then the head), and the fragments of the modulation rows they come from
-    p.lnstats = take(fmv ? (size_t)(c.dim / 16) * FM_BATCH * TMAX * 8 : 0);
+    // (the KV-injection draft folds its RMSNorms the same way: statistics and arrival counters only)
+    p.lnstats = take(fmv || kvi ? (size_t)(c.dim / 16) * FM_BATCH * TMAX * 8 : 0);
     p.c12 = take(fmv ? c12_floats(c) * 4 : 0);
     p.lnfrag = take(fmv ? (size_t)(3 * c.layers + 1) * c.dim * 64 : 0);
     // arrival counters: a split residual update's per tile, then the self-attention tail's per head
-    p.rtick = take(fmv ? (size_t)(RTICK_MAX + SATICK_MAX) * 4 : 0);
+    p.rtick = take(fmv || kvi ? (size_t)(RTICK_MAX + SATICK_MAX) * 4 : 0);
     // the persistent draft kernel: its arguments and per-layer table (device copies), its barrier counters and its
     // activation arena (sized for the most work-groups it may run with)
     const bool pk = draft_supported(c);
@@ -471,6 +475,8 @@ struct SkExtra {
     const float* ryscale = nullptr;
     float* rstats = nullptr;
     float* rdebug = nullptr;
+    int ln_rms = 0;                  // the RMSNorm fold (no c1 / c2)
+    const uint16_t* ryw = nullptr;   // SK_RESID: fragments of x w (the next RMSNorm's weight) instead of x (1 + s)
     SelfAttnArgs sa{};   // q | k | v with the self-attention tail (sa.qkv set)
 };
 
@@ -533,6 +539,8 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         a.rbase_ld = ex->rbase_ld;
         a.rgate = ex->rgate;
         a.ryscale = ex->ryscale;
+        a.ryw = ex->ryw;
+        a.ln_rms = ex->ln_rms;
         a.rstats = ex->rstats;
         a.rdebug = ex->rdebug;
         a.sa = ex->sa;
@@ -1329,12 +1337,34 @@ fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* cons
         CHK(rows(r, st));
     }
     const float scale = 1.f / sqrtf((float)hd);
+    // Every RMSNorm inside the stack is folded (SkinnyArgs ln_rms): the residual updates of o and down (SK_RESID, gate
+    // 1) write x, the fragments of x w for the next product (w: the next norm's weight) and x's per-tile statistics;
+    // that product (the gate | up pair, the next layer's q | k | v) scales its rows by rstd. Layer 0's q | k | v takes
+    // the normalised rows of the row kernel above, and the last layer's out_norm stays a row kernel (its f32 rows
+    // feed the confidence head).
+    float2* stats = d->at<float2>(d->p.lnstats);
+    SkExtra fold;
+    fold.ln_stats = (const float*)stats;
+    fold.ln_tiles = D / 16;
+    fold.ln_eps = c.rms_eps;
+    fold.ln_rms = 1;
+    auto resid = [&](const uint16_t* w_next, float* dbg) {
+        SkExtra e;
+        e.rx = x;
+        e.rx_ld = D;
+        e.rbase = x;
+        e.rbase_ld = D;
+        e.ryw = w_next;
+        e.rstats = (float*)stats;
+        e.rdebug = dbg;
+        return e;
+    };
     for (int i = 0; i < c.layers; ++i) {
         CHK(skinny(d,
                    {{d->W(BB(i, "q")), nullptr, nullptr, nullptr, nullptr, fragH, qkv, D, 3 * D},
                     {d->W(BB(i, "k")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + D, D, 3 * D},
                     {d->W(BB(i, "v")), nullptr, nullptr, nullptr, nullptr, fragH, qkv + 2 * D, D, 3 * D}},
-                   D, T, SK_F32, 0, nullptr, st));
+                   D, T, SK_F32, 0, nullptr, st, 0, 0, 1, i > 0 ? &fold : nullptr));
         // bidirectional attention of each request over [its context rows ++ its block rows]
         for (int b = 0; b < B; ++b) {
             float* qb = qkv + (size_t)b * G * 3 * D;
@@ -1345,44 +1375,39 @@ fm_status kvinject_draft_batch(fm_drafter* const* ds, int B, const int32_t* cons
             CHK(attend(ds[b], qp, G, i, 0, ds[b]->length, qb + D, qb + 2 * D, G, 3 * D, -1, scale, nullptr, 0, 0, fragO,
                        st, b * G));
         }
-        CHK(skinny(d, {{d->W(BB(i, "o")), nullptr, nullptr, nullptr, nullptr, fragO, part, D, D}}, D, T, SK_PARTIAL, 0,
-                   &S, st));
-        {
-            RowArgs r = rows_base(d, D, T);
-            r.x = x;
-            r.part = part;
-            r.S = S;
-            r.part_stride = pstr;
-            r.norm = ROW_RMS;
-            r.w_bf16 = d->B(BB(i, "ff_norm"));
-            r.eps = c.rms_eps;
-            r.frag_out = fragH;
-            CHK(rows(r, st));
-        }
+        // o and the residual; fragments of x ff_norm for the gated unit
+        const SkExtra eo = resid(d->B(BB(i, "ff_norm")), nullptr);
+        CHK(skinny(d, {{d->W(BB(i, "o")), nullptr, nullptr, nullptr, nullptr, fragO, fragH, D, 0}}, D, T, SK_RESID,
+                   KVI_RESID_SPLIT, nullptr, st, 0, 0, 1, &eo));
         CHK(skinny(d, {{d->W(BB(i, "gate")), nullptr, d->W(BB(i, "up")), nullptr, nullptr, fragH, fragU, c.ffn, 0}},
-                   D, T, SK_FRAG_GEGLU, 0, nullptr, st));
+                   D, T, SK_FRAG_GEGLU, 0, nullptr, st, 0, 0, 1, &fold));
+        const bool last = i + 1 == c.layers;
+        float* dbg = debug_layers ? debug_layers + (size_t)i * T * D : nullptr;
+        if (!last) {   // down and the residual; fragments of x attn_norm of the next layer
+            const SkExtra ed = resid(d->B(BB(i + 1, "attn_norm")), dbg);
+            CHK(skinny(d, {{d->W(BB(i, "down")), nullptr, nullptr, nullptr, nullptr, fragU, fragH, D, 0}}, c.ffn, T,
+                       SK_RESID, KVI_RESID_SPLIT, nullptr, st, 0, 0, 1, &ed));
+            continue;
+        }
         CHK(skinny(d, {{d->W(BB(i, "down")), nullptr, nullptr, nullptr, nullptr, fragU, part, D, D}}, c.ffn, T,
                    SK_PARTIAL, 0, &S, st));
-        // residual + the next norm; after the last layer each request's block = RMSNorm(H_d; out_norm) rows are also
-        // kept in its own handle for the confidence head (fm_markov_argmax on that handle)
-        const bool last = i + 1 == c.layers;
-        for (int b = 0; b < (last ? B : 1); ++b) {
-            RowArgs r = rows_base(d, D, last ? G : T);
-            r.row0 = last ? b * G : 0;
+        // residual + out_norm; each request's normed block rows are also kept in its own handle for the confidence
+        // head (fm_markov_argmax on that handle)
+        for (int b = 0; b < B; ++b) {
+            RowArgs r = rows_base(d, D, G);
+            r.row0 = b * G;
             r.x = x;
             r.part = part + (size_t)r.row0 * D;
             r.S = S;
             r.part_stride = pstr;
-            if (debug_layers) r.debug_x = debug_layers + (size_t)i * T * D;
+            if (dbg) r.debug_x = dbg;
             r.norm = ROW_RMS;
-            r.w_bf16 = last ? d->B("out_norm") : d->B(BB(i + 1, "attn_norm"));
+            r.w_bf16 = d->B("out_norm");
             r.eps = c.rms_eps;
             r.frag_out = fragH;
-            if (last) {
-                r.f32_out = ds[b]->at<float>(ds[b]->p.blockn);
-                r.f32_local = 1;
-                r.out_ld = D;
-            }
+            r.f32_out = ds[b]->at<float>(ds[b]->p.blockn);
+            r.f32_local = 1;
+            r.out_ld = D;
             CHK(rows(r, st));
         }
     }
@@ -1528,7 +1553,10 @@ fm_status mtp_draft(fm_drafter* d, const fm_block_args* ba, float* hidden_out, h
     return mtp_draft_batch(ds, 1, as, hidden_out, st);
 }
 
-fm_status kvinject_create(fm_drafter*, hipStream_t) { return FM_OK; }
+fm_status kvinject_create(fm_drafter* d, hipStream_t st) {
+    HIPCHK(launch_fill_u32(d->at<uint32_t>(d->p.rtick), RTICK_MAX + SATICK_MAX, 0u, st));   // each last arrival
+    return FM_OK;                                                                              // resets its own
+}
 
 }  // namespace
 

@@ -69,17 +69,21 @@ struct SkinnyArgs {
     // holds (mean, M2) of each 16-column tile of x (an SK_RESID epilogue's output); with c1 = sum_k (1 + s_k) W[m][k]
     // and c2 = sum_k shift_k W[m][k] (the group's c12), the epilogue takes rstd (acc - mean c1[m]) + c2[m] as the
     // product (SK_PARTIAL: split 0 adds the constant part, every split scales by rstd).
+    // ln_rms: the fold of an RMSNorm instead (one or two matrices, no c12): the fragments hold y = x w (w the norm's
+    // weight), and the epilogue takes rstd acc with rstd = 1 / sqrt(mean(x^2) + eps) from the same statistics.
     const float* ln_stats;
     int ln_tiles;         // x's width / 16 (at most LN_MAX_TILES / nb)
     float ln_inv;         // 1 / ln_tiles
     float ln_eps;
+    int ln_rms;
     // SK_RESID
     float* rx;            // residual stream [rows][rx_ld], written (x above)
     int rx_ld;
     const float* rbase;   // base rows [rows][rbase_ld] (rbase_ld 0: one row for every row); may be rx
     int rbase_ld;
     const float* rgate;   // f32 [M] or null (gate 1)
-    const float* ryscale; // f32 [M]: the next LayerNorm's modulation scale s
+    const float* ryscale; // f32 [M]: the next LayerNorm's modulation scale s (fragments of x (1 + s))
+    const uint16_t* ryw;  // or bf16 [M]: the next RMSNorm's weight w (fragments of x w)
     float* rstats;        // float2 [M / 16][16 nb]: (mean, M2) of x over each 16-column tile, per row
     float* rdebug;        // optional copy of x (same layout)
     float* rpart;         // S > 1: the splits' partial tiles [S][rows][M] (slab stride part_stride)

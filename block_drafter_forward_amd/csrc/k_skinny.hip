@@ -170,7 +170,7 @@ template <int NT, int WT, int UP, int SKC, int NB = 1, int EP = EP_PLAIN>
 __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     static_assert(WT == SKW_BF16, "bf16 weights (Q8_0: skinny_ws_kernel)");
     static_assert(NB == 1 || UP == 2, "two row blocks: row-staged only");
-    static_assert(EP == EP_PLAIN || NT == 1, "the LayerNorm fold and the residual update take one matrix");
+    static_assert(EP == EP_PLAIN || EP == EP_LN || NT == 1, "the residual update takes one matrix");
     constexpr bool LN = EP == EP_LN;
     const int bid = blockIdx.x;
     int gi = 0;
@@ -196,12 +196,14 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     const int e_t = e_el & 15, e_m = m0 + e_ml;
     constexpr bool resid = EP == EP_RESID;   // mode SK_RESID (checked by the launcher)
     const float e_bias = bf16_to_f32(*(G.bias ? G.bias + e_m : (const uint16_t*)a.zeros));   // no branch: no wait
-    float e_base[NB], e_gate = 1.f, e_ys = 0.f;
+    float e_base[NB], e_gate = 1.f, e_yf = 1.f;   // e_yf: x's factor in the next product's fragments
     if constexpr (resid) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) e_base[b] = a.rbase[(size_t)(16 * b + e_t) * a.rbase_ld + e_m];
         e_gate = *(a.rgate ? a.rgate + e_m : a.zeros);
-        e_ys = a.ryscale[e_m];
+        const float ys = *(a.ryscale ? a.ryscale + e_m : a.zeros);
+        const float yw = bf16_to_f32(*(a.ryw ? a.ryw + e_m : (const uint16_t*)a.zeros));
+        e_yf = a.ryw ? yw : 1.f + ys;
     }
     // LayerNorm statistics (float2 [ln_tiles][R], ln_tiles R / 128 KB) straight into LDS, 1 KB per wave instruction,
     // issued right after the first chunk's loads: loads complete in issue order, so the first chunk's wait covers
@@ -209,9 +211,9 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
     // (after the statistics are reduced, the q | k | v product's self-attention tail reuses this LDS)
     __shared__ __attribute__((aligned(16))) float2 lnlds[LN ? LN_MAX_TILES * 16 : 1];
     float e_c1 = 0.f, e_c2 = 0.f;
-    if constexpr (LN) {
-        e_c1 = G.c12[e_m];
-        e_c2 = G.c12[G.M + e_m];
+    if constexpr (LN) {   // (an RMSNorm fold has no c12: zeros)
+        e_c1 = *(G.c12 ? G.c12 + e_m : a.zeros);
+        e_c2 = *(G.c12 ? G.c12 + G.M + e_m : a.zeros);
     }
     auto ln_prefetch = [&]() {
         if constexpr (LN) {
@@ -281,9 +283,9 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
                     (((lnred[0][0][rw] + lnred[0][1][rw]) + lnred[0][2][rw]) + lnred[0][3][rw]) * a.ln_inv;
                 const float sq = ((lnred[1][0][rw] + lnred[1][1][rw]) + lnred[1][2][rw]) + lnred[1][3][rw];
                 const float dk = mu - lp[rw].x;
-                const float var = (sq * a.ln_inv - 16.f * dk * dk) * (1.f / 16.f);
-                e_mu[b] = mu;
-                e_rs[b] = 1.f / sqrtf(fmaxf(var, 0.f) + a.ln_eps);
+                const float var = fmaxf((sq * a.ln_inv - 16.f * dk * dk) * (1.f / 16.f), 0.f);
+                e_mu[b] = a.ln_rms ? 0.f : mu;
+                e_rs[b] = 1.f / sqrtf((a.ln_rms ? var + mu * mu : var) + a.ln_eps);
             }
         }
     };
@@ -406,8 +408,11 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
         }
         if (resid && a.S > 1) v[0] = vsum[b];
         const int row = 16 * b + t;
-        if constexpr (LN)   // rstd (acc - mean c1) + c2; the constant part once (split 0)
+        if constexpr (LN) {   // rstd (acc - mean c1) + c2; the constant part once (split 0)
             v[0] = split == 0 ? e_rs[b] * (v[0] - e_mu[b] * e_c1) + e_c2 : e_rs[b] * v[0];
+#pragma unroll
+            for (int n = 1; n < NT; ++n) v[n] = e_rs[b] * v[n];   // (RMSNorm fold: no c1 / c2)
+        }
         if (a.mode == SK_F32) {
             if (LN && a.sa.qkv) tile[b][t][ml] = v[0] + e_bias;   // stored device-coherent below, 16 bytes a thread
             else if (t < a.T) ((float*)G.out)[(size_t)row * G.ld + m] = v[0] + e_bias;
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void skinny_kernel(SkinnyArgs a) {
                 if (a.rdebug) a.rdebug[(size_t)row * a.rx_ld + m] = xn;
             }
             xt[b][t][ml] = xn;
-            tile[b][t][ml] = xn * (1.f + e_ys);
+            tile[b][t][ml] = xn * e_yf;
         } else {
             float o;
             if (a.mode == SK_FRAG_GELU) {
@@ -524,6 +529,8 @@ hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
     if (a.ln_stats || a.mode == SK_RESID) {
         if constexpr (NT == 1)
             return a.ln_stats ? launch_nt_ep<1, WT, EP_LN>(a, nwg, st) : launch_nt_ep<1, WT, EP_RESID>(a, nwg, st);
+        else if (a.ln_stats && a.ln_rms)
+            return launch_nt_ep<NT, WT, EP_LN>(a, nwg, st);
         return hipErrorInvalidValue;
     }
     return launch_nt_ep<NT, WT, EP_PLAIN>(a, nwg, st);
@@ -640,18 +647,20 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyAr
 hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st) {
     const bool glu = (a.mode == SK_FRAG_GEGLU || a.mode == SK_FRAG_SWIGLU);
     if (!a.zeros) return hipErrorInvalidValue;
-    if (a.ln_stats) {   // the LayerNorm fold: bf16, one matrix, every group with its c1 / c2, not a residual update
-        if (wtype != SKW_BF16 || glu || a.ln_tiles < 1 || a.ln_tiles > LN_MAX_TILES / a.nb || a.mode == SK_RESID)
+    if (a.ln_stats) {   // the LayerNorm fold: bf16, one matrix, every group with its c1 / c2, not a residual update;
+                        // the RMSNorm fold: bf16, one or two matrices (a gated unit), no c1 / c2
+        if (wtype != SKW_BF16 || (glu && !a.ln_rms) || a.ln_tiles < 1 || a.ln_tiles > LN_MAX_TILES / a.nb ||
+            a.mode == SK_RESID)
             return hipErrorInvalidValue;
         for (int i = 0; i < a.ngroups; ++i)
-            if (!a.g[i].c12) return hipErrorInvalidValue;
+            if (!a.g[i].c12 != (a.ln_rms != 0)) return hipErrorInvalidValue;
     }
     if (a.sa.qkv &&   // the self-attention tail: a LayerNorm-folded unsplit q | k | v product of whole heads
         (!a.ln_stats || a.mode != SK_F32 || a.S != 1 || a.ngroups != 3 || !a.satick || a.nb != a.sa.nb ||
          (a.sa.hd != 64 && a.sa.hd != 128) || a.sa.T < 1 || a.sa.T > 16 || a.sa.D % a.sa.hd ||
          32 * (a.sa.hd + 4) * 4 + 16 * (a.sa.hd + 4) * 4 + 16 * 17 * 4 > LN_MAX_TILES * 16 * 8))
         return hipErrorInvalidValue;
-    if (a.mode == SK_RESID && (wtype != SKW_BF16 || a.S < 1 || !a.rx || !a.rbase || !a.ryscale || !a.rstats ||
+    if (a.mode == SK_RESID && (wtype != SKW_BF16 || a.S < 1 || !a.rx || !a.rbase || !a.ryscale == !a.ryw || !a.rstats ||
                                a.ngroups != 1 || (a.S > 1 && (!a.rpart || !a.rtick))))
         return hipErrorInvalidValue;
     if (wtype == SKW_BF16) return glu ? launch_nt<2, SKW_BF16>(a, nwg, st) : launch_nt<1, SKW_BF16>(a, nwg, st);
