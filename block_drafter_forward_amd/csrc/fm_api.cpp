@@ -348,6 +348,8 @@ fm_status validate_config(const fm_config* c) {
         if (c->n_taps * c->target_dim > TAPS_MAX_WIDTH)
             return fail(FM_E_UNSUPPORTED, "tap width %d > %d", c->n_taps * c->target_dim, TAPS_MAX_WIDTH);
         if (c->kv_heads != c->heads) return fail(FM_E_UNSUPPORTED, "KV-inject attends with every head's own K/V");
+        if (c->dim > 16 * LN_MAX_TILES)   // the RMSNorm fold's statistics: at most LN_MAX_TILES tiles per row
+            return fail(FM_E_UNSUPPORTED, "KV-inject dim %d > %d", c->dim, 16 * LN_MAX_TILES);
         break;
     case FM_VARIANT_MTP:
         if (c->rope != FM_ROPE_NEOX || c->mlp != FM_MLP_SWIGLU || c->wtype != FM_W_Q8_0 || c->kv_dtype != FM_KV_F32)

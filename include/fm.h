@@ -65,8 +65,10 @@ enum fm_wtype { FM_W_BF16 = 0, FM_W_Q8_0 = 1 };
  *   rope       FM_ROPE_*; rope_dims rotated dims per head (NEOX partial); rope_theta the base
  *   ln_eps / rms_eps / qk_eps   LayerNorm, RMSNorm and q/k head-norm epsilons
  *   mlp        FM_MLP_*; kv_dtype FM_KV_* (cache element type); wtype FM_W_* (matrix storage)
- * Supported shapes (FM_E_UNSUPPORTED otherwise): target_dim a multiple of 512; head_dim 64 or 128 (flow-map), 128 or
- * 256 (KV-inject), 256 (MTP); kv_heads == heads except for the MTP head; n_taps * target_dim at most 16384.
+ * Supported shapes (FM_E_UNSUPPORTED otherwise): target_dim a multiple of 512; head_dim 64 or 128 (flow-map), 128
+ * (KV-inject), 256 (MTP); kv_heads == heads except for the MTP head; n_taps * target_dim at most 16384; dim at most
+ * 4096 for the flow-map and KV-inject drafters (their norms are folded into the products, whose statistics cover at
+ * most 256 tiles of 16 columns), 6144 for the MTP head.
  * dim, target_dim and ffn must be multiples of 256, and for the MTP head heads * head_dim too (FM_E_INVALID). */
 typedef struct fm_config {
     int32_t variant;

@@ -49,6 +49,16 @@ def test_invalid_configs_report_zero_size(field, value):
     assert fm.last_error() != ""
 
 
+@pytest.mark.parametrize("name", ["flashmap", "kvinject"])
+def test_norm_fold_width_limit(name):
+    # the LayerNorm / RMSNorm fold reduces at most 256 tiles of 16 columns per row
+    _lib()
+    cfg = configs.get(name)
+    cfg.update(dim=4352, heads=34, kv_heads=34)
+    assert fm.kv_bytes(cfg) == 0
+    assert "4096" in fm.last_error()
+
+
 def test_create_rejects_null_and_missing_weights_before_any_launch():
     L = _lib()
     c = fm.make_config(configs.get("tiny"))
