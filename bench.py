@@ -179,6 +179,27 @@ def other_rows(torch, fm, configs, gen, W, d, dl, reps: int):
                                          "appends/s")
     dl.fm_context_append(t16, P)   # leave the context at 8192 + 16 rows
 
+    # the long-context workload's own schedule after its 8192-row prefill: 64 steps, each a draft block + lm_head
+    # argmax at pos_s, then an append of U{1..16} rows at pos_s (the first rewinds the 16 rows above). Every call's
+    # arguments are fixed by the schedule, so the 64 steps replay as one graph; a replay rewrites the same rows.
+    sched = gen.longctx_schedule(lcfg)
+    s_an = torch.tensor([a for a, _, _ in sched], dtype=torch.int32, device="cuda")
+    s_taps = [torch.from_numpy(gen.taps(lcfg, f"step{i}", ns)).cuda() for i, (_, _, ns) in enumerate(sched)]
+
+    def sched_run():
+        for i, (_, pos, ns) in enumerate(sched):
+            dl.fm_draft_block(hid, anchor=s_an[i:i + 1], pos=pos)
+            dl.fm_lm_argmax(hid, T, tok)
+            dl.fm_context_append(s_taps[i], pos)
+    ms = _time_ms(torch, _graph_of(torch, sched_run), 1, 3)
+    s_bytes = sum(draft_step_bytes(lcfg, pos + 1) + weight_bytes(W, app_w) + ns * lcfg["n_taps"] * Ht * 4 +
+                  2 * Lyr * ns * D * 2 for _, pos, ns in sched)
+    r = _hbm_row(f"the long-context schedule: {len(sched)} x (draft block + lm_head argmax at L = {sched[0][1] + 1} .. "
+                 f"{sched[-1][1] + 1}, then an append of 1-16 rows)", ms, s_bytes, "schedules/s")
+    r["draft_blocks_per_s"] = len(sched) / (ms * 1e-3)
+    r["us_per_step"] = ms * 1e3 / len(sched)
+    rows["longctx_schedule_64"] = r
+
     # two FlowMap requests in one pass (fm_draft_batch, 32 rows): each over its own 512-row context, the lm_head
     # argmax over both blocks' rows; the weights and the table stream once for both
     n = cfg["ctx_rows"]
