@@ -41,7 +41,7 @@ typedef enum fm_status {
     FM_E_INVALID = 1,        /* bad argument: null pointer, out-of-range size/position, inconsistent config */
     FM_E_CONTEXT_FULL = 2,   /* the append (or draft) would run past max_ctx */
     FM_E_HIP = 3,            /* a HIP runtime call failed (message holds hipGetErrorString) */
-    FM_E_UNSUPPORTED = 4,    /* a config combination this build does not implement */
+    FM_E_UNSUPPORTED = 4,    /* a config combination the library does not implement */
     FM_E_MISSING_WEIGHT = 5, /* a weight the variant needs is not in the name table */
     FM_E_DEVICE = 6          /* reported by fm_device_status: a persistent draft launch gave up waiting */
 } fm_status;
