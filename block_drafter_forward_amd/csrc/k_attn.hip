@@ -406,10 +406,12 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
 }
 
 // One work-group per (head, query row): thread (4-dim group, chunk group) folds its chunks with the online
-// rescale, four chunks' loads in flight at a time; the chunk groups are then folded in LDS.
-template <int HD>
-__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-    constexpr int DV = HD / 4, G = 256 / DV;
+// rescale, four chunks' loads in flight at a time; the chunk groups are then folded in LDS, one thread per
+// dimension. NTH threads: 1024 when 256 would leave a thread more than two rounds of four chunks (many partials),
+// so that every partial's load is in flight at once.
+template <int HD, int NTH>
+__global__ __launch_bounds__(NTH) void attn_merge_kernel(MergeArgs a) {
+    constexpr int DV = HD / 4, G = NTH / DV;
     const int h = blockIdx.x, t = blockIdx.y;
     const int d4 = threadIdx.x % DV, cg = threadIdx.x / DV;
     const int nc = a.nchunks;
@@ -442,33 +444,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
     }
     __shared__ float sm[G], sl[G];
     __shared__ float so[G][HD];
+    __shared__ float fo[HD];
     if (d4 == 0) { sm[cg] = M; sl[cg] = Ls; }
     so[cg][4 * d4] = O.x; so[cg][4 * d4 + 1] = O.y; so[cg][4 * d4 + 2] = O.z; so[cg][4 * d4 + 3] = O.w;
     __syncthreads();
-    const int per = HD / 8;
-    if (threadIdx.x < per) {
-        const int d0 = threadIdx.x * 8;
+    if (threadIdx.x < HD) {   // dimension d over the chunk groups, in group order
+        const int d = threadIdx.x;
         float MM = -INFINITY;
 #pragma unroll
         for (int g = 0; g < G; ++g) MM = fmaxf(MM, sm[g]);
-        float L = 0.f, o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        float L = 0.f, od = 0.f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float w = sm[g] == -INFINITY ? 0.f : expf(sm[g] - MM);
             L += w * sl[g];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += w * so[g][d0 + e];
+            od += w * so[g][d];
         }
-        const float il = 1.f / L;
-        float gt[8];
+        fo[d] = od * (1.f / L);
+    }
+    __syncthreads();
+    if (threadIdx.x < HD / 8) {
+        const int d0 = threadIdx.x * 8;
+        float o[8], gt[8];
         const float* gp = a.gate ? a.gate + (size_t)t * a.gate_ld + (size_t)h * a.gate_hs + d0 : nullptr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) gt[e] = gp ? gp[e] : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            o[e] *= il;
+            o[e] = fo[d0 + e];
             if (gp) o[e] *= sigmoidf(gt[e]);
         }
         frag_store8_rows(a.o_frag, a.heads * HD, a.row0 + t, h * HD + d0, o);
@@ -631,11 +634,15 @@ hipError_t launch_attn_split(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st) {
     dim3 grid(a.heads, a.nq);
+    if (a.hd != 64 && a.hd != 128 && a.hd != 256) return hipErrorInvalidValue;
+    // more than two rounds of four chunks per thread at 256 threads (measured: the MTP pass over a 4096-row cache
+    // 531 -> 526 us, the KV-injection draft 434 -> 432 us; at two rounds, the flow-map draft at L = 8193, 1024
+    // threads were 4 us slower)
+    const bool wide = a.nchunks > 8 * (256 / (a.hd / 4));
     switch (a.hd) {
-    case 64: attn_merge_kernel<64><<<grid, 256, 0, st>>>(a); break;
-    case 128: attn_merge_kernel<128><<<grid, 256, 0, st>>>(a); break;
-    case 256: attn_merge_kernel<256><<<grid, 256, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
+    case 64: wide ? attn_merge_kernel<64, 1024><<<grid, 1024, 0, st>>>(a) : attn_merge_kernel<64, 256><<<grid, 256, 0, st>>>(a); break;
+    case 128: wide ? attn_merge_kernel<128, 1024><<<grid, 1024, 0, st>>>(a) : attn_merge_kernel<128, 256><<<grid, 256, 0, st>>>(a); break;
+    default: wide ? attn_merge_kernel<256, 1024><<<grid, 1024, 0, st>>>(a) : attn_merge_kernel<256, 256><<<grid, 256, 0, st>>>(a); break;
     }
     return hipGetLastError();
 }
