@@ -647,10 +647,14 @@ hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st) {
     // 531 -> 526 us, the KV-injection draft 434 -> 432 us; at two rounds, the flow-map draft at L = 8193, 1024
     // threads were 4 us slower)
     const bool wide = a.nchunks > 8 * (256 / (a.hd / 4));
-    switch (a.hd) {
-    case 64: wide ? attn_merge_kernel<64, 1024><<<grid, 1024, 0, st>>>(a) : attn_merge_kernel<64, 256><<<grid, 256, 0, st>>>(a); break;
-    case 128: wide ? attn_merge_kernel<128, 1024><<<grid, 1024, 0, st>>>(a) : attn_merge_kernel<128, 256><<<grid, 256, 0, st>>>(a); break;
-    default: wide ? attn_merge_kernel<256, 1024><<<grid, 1024, 0, st>>>(a) : attn_merge_kernel<256, 256><<<grid, 256, 0, st>>>(a); break;
+    if (wide) {
+        if (a.hd == 64) attn_merge_kernel<64, 1024><<<grid, 1024, 0, st>>>(a);
+        else if (a.hd == 128) attn_merge_kernel<128, 1024><<<grid, 1024, 0, st>>>(a);
+        else attn_merge_kernel<256, 1024><<<grid, 1024, 0, st>>>(a);
+    } else {
+        if (a.hd == 64) attn_merge_kernel<64, 256><<<grid, 256, 0, st>>>(a);
+        else if (a.hd == 128) attn_merge_kernel<128, 256><<<grid, 256, 0, st>>>(a);
+        else attn_merge_kernel<256, 256><<<grid, 256, 0, st>>>(a);
     }
     return hipGetLastError();
 }
