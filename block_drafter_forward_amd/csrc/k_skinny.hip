@@ -538,18 +538,21 @@ hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
 
 // ── Q8_0: the tile-owning variant ──────────────────────────────────────────────────────────────
 // A work-group is SK_WS_WAVES waves walking columns [split K / S, (split + 1) K / S) in chunks of 256, each chunk's
-// fragments staged once per work-group (fm_ws.h), three chunks in flight per wave. Wave w owns one 16-row tile:
+// fragments staged once per work-group (fm_ws.h), two chunks in flight per wave, three work-groups per CU (50 KB of
+// LDS, at most 168 VGPRs; the epilogue's tile reuses the fragment slabs). Against three chunks in flight and two
+// work-groups per CU the MTP pass went from 524 to 515 us: the launches of 544 and 640 work-groups no longer leave a
+// second, mostly empty round. Wave w owns one 16-row tile:
 // tile NW tg + w of its group, or for a gated unit (GLU) tile NW / 2 tg + w / 2 of the gate (w even) or of the up
 // matrix (w odd), the pair combined through LDS at the end. Tail waves of a group's last work-group redo its last
 // tile, their results dropped. Each wave's 16 x 16 tile is complete for its k-range, so no sum over waves: the
 // epilogue goes straight from the accumulator (SK_PARTIAL: the split's slab).
 template <bool GLU>
-__global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(SK_WS_WAVES * 64, 3) void skinny_ws_kernel(SkinnyArgs a) {
     constexpr int NW = SK_WS_WAVES, TPW = GLU ? NW / 2 : NW;   // tiles per work-group (of each matrix)
     __shared__ uint4 alds_all[NW][16 * ws::Q8_PITCH];
     __shared__ uint16_t slds_all[NW][128];
-    __shared__ uint4 blds_all[3][1024];
-    __shared__ float tile_all[NW][16][17];
+    __shared__ uint4 blds_all[2][1024];
+    float(*tile_all)[16][17] = (float(*)[16][17])&blds_all[0][0];   // after the last product
     const int bid = blockIdx.x;
     int gi = 0;
 #pragma unroll 1
@@ -575,25 +578,22 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyAr
         if (ch < nch) ws::load_q8<NW, 1>(r, Ct, Dt, K, X, ch, tid);
         __builtin_amdgcn_sched_barrier(0);   // each chunk's loads stay together (one wait per chunk)
     };
-    // chunk c is staged into slab c % 3: written after the barrier that follows the multiply of chunk c - 3
+    // chunk c is staged into slab c % 2: written after the barrier that follows the multiply of chunk c - 2
     auto step = [&](Regs& r, int c, int buf) {
         ws::stage_q8<NW, 1>(r, alds, slds, blds_all[buf], tid);
-        load(r, c + 3);
+        load(r, c + 2);
         __syncthreads();
         ws::compute_q8<1>(alds, slds, blds_all[buf], acc, lane);
     };
-    Regs r0, r1, r2;
+    Regs r0, r1;
     load(r0, 0);
     load(r1, 1);
-    load(r2, 2);
     int ch = 0;
-    for (; ch + 3 <= nch; ch += 3) {
+    for (; ch + 2 <= nch; ch += 2) {
         step(r0, ch, 0);
         step(r1, ch + 1, 1);
-        step(r2, ch + 2, 2);
     }
     if (ch < nch) step(r0, ch, 0);
-    if (ch + 1 < nch) step(r1, ch + 1, 1);
 
     // lane holds Y[t = lane % 16][m0 + 4 g + j]
     const int t = lane & 15, g = lane >> 4, mc = m0 + 4 * g;
@@ -612,6 +612,7 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 2) void skinny_ws_kernel(SkinnyAr
         *(float4*)dst = o;
         return;
     }
+    __syncthreads();   // every wave is done with the fragment slabs that tile_all reuses
 #pragma unroll
     for (int j = 0; j < 4; ++j) tile_all[wave][t][4 * g + j] = acc[0][0][j];
     if constexpr (GLU) {
