@@ -646,10 +646,10 @@ hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t st) {
     // more than two rounds of four chunks per thread at 256 threads (measured: the MTP pass over a 4096-row cache
     // 531 -> 526 us, the KV-injection draft 434 -> 432 us; at two rounds, the flow-map draft at L = 8193, 1024
     // threads were 4 us slower)
-    const bool wide = a.nchunks > 8 * (256 / (a.hd / 4));
+    // (head width 64 keeps the 256-thread kernel: no configuration reaches that many partials with it)
+    const bool wide = a.hd >= 128 && a.nchunks > 8 * (256 / (a.hd / 4));
     if (wide) {
-        if (a.hd == 64) attn_merge_kernel<64, 1024><<<grid, 1024, 0, st>>>(a);
-        else if (a.hd == 128) attn_merge_kernel<128, 1024><<<grid, 1024, 0, st>>>(a);
+        if (a.hd == 128) attn_merge_kernel<128, 1024><<<grid, 1024, 0, st>>>(a);
         else attn_merge_kernel<256, 1024><<<grid, 1024, 0, st>>>(a);
     } else {
         if (a.hd == 64) attn_merge_kernel<64, 256><<<grid, 256, 0, st>>>(a);
