@@ -182,7 +182,7 @@ size_t c12_off(const fm_config& c, int l, int which) {   // which 0..3: q k v cr
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, mcut, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, blockn, zbase, tcond, qkv0, x1, q0c,
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, lmq, lmqd, blockn, zbase, tcond, qkv0, x1, q0c,
         rscale, modc, lnstats, c12, lnfrag, rtick, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
     int best_rows;           // argmax keys (one per row)
@@ -273,6 +273,10 @@ Plan make_plan(const fm_config& c) {
     p.cfrag = take(fmv ? (size_t)c.dim * 64 : 0);
     // MTP chained passes: the embedding row of the previous draft token
     p.echain = take(c.variant == FM_VARIANT_MTP ? (size_t)c.dim * 4 : 0);
+    // the Q8_0 lm_head in the MFMA operand layout its kernel streams (codes, then scales), copied at create
+    const bool lmq8 = c.wtype == FM_W_Q8_0;
+    p.lmq = take(lmq8 ? (size_t)c.vocab * c.target_dim : 0);
+    p.lmqd = take(lmq8 ? (size_t)c.vocab * (c.target_dim / 32) * 2 : 0);
     // KV-injection: the normed backbone rows of the last draft (the confidence head's input) and the base logits
     // of the Markov decode
     const bool kvi = c.variant == FM_VARIANT_KVINJECT;
@@ -1631,6 +1635,12 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
             s = prefill_weight_copies(d, st);
             if (s != FM_OK) break;
         }
+        if (cfg->wtype == FM_W_Q8_0) {
+            const hipError_t e = launch_q8_tile_copy((const int8_t*)d->W("lm_head.q"), (const uint16_t*)d->W("lm_head.d"),
+                                                     cfg->vocab, cfg->target_dim, d->at<uint8_t>(d->p.lmq),
+                                                     d->at<uint16_t>(d->p.lmqd), st);
+            if (e != hipSuccess) { s = fail(FM_E_HIP, "Q8_0 lm_head copy: %s", hipGetErrorString(e)); break; }
+        }
         if (cfg->variant == FM_VARIANT_FLOWMAP) s = flowmap_create(d, st);
         else if (cfg->variant == FM_VARIANT_KVINJECT) s = kvinject_create(d, st);
     } while (0);
@@ -1694,8 +1704,8 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
     LmArgs a{};
     const bool q8 = d->c.wtype == FM_W_Q8_0;
-    a.E = q8 ? d->W("lm_head.q") : d->W("lm_head.weight");
-    a.Ed = q8 ? d->W("lm_head.d") : nullptr;
+    a.E = q8 ? (const void*)d->at<uint8_t>(d->p.lmq) : d->W("lm_head.weight");
+    a.Ed = q8 ? (const void*)d->at<uint16_t>(d->p.lmqd) : nullptr;
     a.X = fr;
     a.V = d->c.vocab;
     a.K = K;
@@ -1725,8 +1735,8 @@ fm_status fm_lm_argmax_static(fm_drafter* d, const float* hidden, int32_t rows, 
     HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
     LmArgs a{};
     const bool q8 = d->c.wtype == FM_W_Q8_0;
-    a.E = q8 ? d->W("lm_head.q") : d->W("lm_head.weight");
-    a.Ed = q8 ? d->W("lm_head.d") : nullptr;
+    a.E = q8 ? (const void*)d->at<uint8_t>(d->p.lmq) : d->W("lm_head.weight");
+    a.Ed = q8 ? (const void*)d->at<uint16_t>(d->p.lmqd) : nullptr;
     a.X = fr;
     a.V = d->c.vocab;
     a.K = K;

@@ -266,8 +266,8 @@ hipError_t launch_mtp_prep(const MtpPrepArgs& a, hipStream_t st);
 
 // ── K5: lm_head + argmax ───────────────────────────────────────────────────────────────────────
 struct LmArgs {
-    const void* E;         // bf16 [V][K] or Q8_0 codes
-    const void* Ed;        // Q8_0 scales or null
+    const void* E;         // bf16 [V][K], or Q8_0 codes in the MFMA operand layout of launch_q8_tile_copy
+    const void* Ed;        // Q8_0 scales in that layout, or null
     const uint8_t* X;      // fragments of the rows (rows 16.. in a second block at X + K * 64)
     int V, K, T;           // T <= 16, or <= 32 for bf16 tables
     unsigned long long* best;  // [T] packed (value, index) maxima, zero between calls
@@ -275,6 +275,12 @@ struct LmArgs {
     float* logits;         // optional [T][V]
 };
 hipError_t launch_lm_argmax(const LmArgs& a, int wtype, hipStream_t st);
+// A Q8_0 table (codes [M][K], f16 scales [M][K / 32]) copied into the layout the Q8_0 lm_head kernel streams: per
+// 16-row tile and 256-column chunk, 4 KB of codes in the order the MFMA's operand registers take them, then (in the
+// scale array) 16 rows x 8 scales. oq: M K bytes, od: M K / 32 halves. M % 16 == 0, K % 256 == 0; q 8-byte aligned,
+// oq and od 16-byte aligned.
+hipError_t launch_q8_tile_copy(const int8_t* q, const uint16_t* d, int M, int K, uint8_t* oq, uint16_t* od,
+                               hipStream_t st);
 
 // The library's static scratch (fm_static.hip): a file-scope device array of STATIC_SCRATCH_BYTES on each GPU, for
 // the entry point that allocates nothing. Returns its device address on the current device (looked up once per
