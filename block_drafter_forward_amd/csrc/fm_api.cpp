@@ -179,10 +179,24 @@ size_t c12_off(const fm_config& c, int l, int which) {   // which 0..3: q k v cr
     return (size_t)l * 2 * (4 * c.dim + c.ffn) + (size_t)2 * c.dim * which;
 }
 
+// The Q8_0 matrices of a configuration (the MTP head's) with their shapes [M][K]: each is copied at create into the
+// MFMA operand layout (launch_q8_tile_copy) and registered under its name + ".qt" (codes) and ".dt" (scales).
+struct Q8Mat {
+    const char* name;
+    int M, K;
+};
+std::vector<Q8Mat> q8_mats(const fm_config& c) {
+    if (c.wtype != FM_W_Q8_0) return {};
+    const int H = c.dim, qw = c.heads * 2 * c.head_dim, kw = c.kv_heads * c.head_dim;
+    return {{"eh_proj", H, 2 * H},     {"attn_q", qw, H},       {"attn_k", kw, H},     {"attn_v", kw, H},
+            {"attn_output", H, c.heads * c.head_dim},           {"ffn_gate", c.ffn, H}, {"ffn_up", c.ffn, H},
+            {"ffn_down", H, c.ffn},    {"lm_head", c.vocab, c.target_dim}};
+}
+
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, mcut, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, lmq, lmqd, blockn, zbase, tcond, qkv0, x1, q0c,
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, q8t, blockn, zbase, tcond, qkv0, x1, q0c,
         rscale, modc, lnstats, c12, lnfrag, rtick, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
     int best_rows;           // argmax keys (one per row)
@@ -273,10 +287,11 @@ Plan make_plan(const fm_config& c) {
     p.cfrag = take(fmv ? (size_t)c.dim * 64 : 0);
     // MTP chained passes: the embedding row of the previous draft token
     p.echain = take(c.variant == FM_VARIANT_MTP ? (size_t)c.dim * 4 : 0);
-    // the Q8_0 lm_head in the MFMA operand layout its kernel streams (codes, then scales), copied at create
-    const bool lmq8 = c.wtype == FM_W_Q8_0;
-    p.lmq = take(lmq8 ? (size_t)c.vocab * c.target_dim : 0);
-    p.lmqd = take(lmq8 ? (size_t)c.vocab * (c.target_dim / 32) * 2 : 0);
+    // every Q8_0 matrix in the MFMA operand layout its kernels stream (codes, then scales, per matrix), copied at
+    // create
+    size_t q8b = 0;
+    for (const Q8Mat& m : q8_mats(c)) q8b += align256((size_t)m.M * m.K) + align256((size_t)m.M * (m.K / 32) * 2);
+    p.q8t = take(q8b);
     // KV-injection: the normed backbone rows of the last draft (the confidence head's input) and the base logits
     // of the Markov decode
     const bool kvi = c.variant == FM_VARIANT_KVINJECT;
@@ -1451,8 +1466,8 @@ fm_status mtp_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* con
     float* qkv = d->at<float>(d->p.qkv);
     float* qout = d->at<float>(d->p.qout);
     const long long pstr = (long long)TMAX * H;
-    auto Q = [&](const char* n) { return d->W(std::string(n) + ".q"); };
-    auto Dd = [&](const char* n) { return d->W(std::string(n) + ".d"); };
+    auto Q = [&](const char* n) { return d->W(std::string(n) + ".qt"); };   // the copies in the MFMA operand layout
+    auto Dd = [&](const char* n) { return d->W(std::string(n) + ".dt"); };
 
     // x = eh_proj([enorm(e); hnorm(h)])
     for (int b = 0; b < B; ++b)
@@ -1635,12 +1650,23 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
             s = prefill_weight_copies(d, st);
             if (s != FM_OK) break;
         }
-        if (cfg->wtype == FM_W_Q8_0) {
-            const hipError_t e = launch_q8_tile_copy((const int8_t*)d->W("lm_head.q"), (const uint16_t*)d->W("lm_head.d"),
-                                                     cfg->vocab, cfg->target_dim, d->at<uint8_t>(d->p.lmq),
-                                                     d->at<uint16_t>(d->p.lmqd), st);
-            if (e != hipSuccess) { s = fail(FM_E_HIP, "Q8_0 lm_head copy: %s", hipGetErrorString(e)); break; }
+        size_t q8o = d->p.q8t;
+        for (const Q8Mat& m : q8_mats(*cfg)) {
+            const std::string n = m.name;
+            uint8_t* oq = d->at<uint8_t>(q8o);
+            q8o += align256((size_t)m.M * m.K);
+            uint16_t* od = d->at<uint16_t>(q8o);
+            q8o += align256((size_t)m.M * (m.K / 32) * 2);
+            const hipError_t e = launch_q8_tile_copy((const int8_t*)d->W(n + ".q"), (const uint16_t*)d->W(n + ".d"),
+                                                     m.M, m.K, oq, od, st);
+            if (e != hipSuccess) {
+                s = fail(FM_E_HIP, "Q8_0 copy of %s: %s (codes 8-byte aligned?)", m.name, hipGetErrorString(e));
+                break;
+            }
+            d->w[n + ".qt"] = oq;
+            d->w[n + ".dt"] = od;
         }
+        if (s != FM_OK) break;
         if (cfg->variant == FM_VARIANT_FLOWMAP) s = flowmap_create(d, st);
         else if (cfg->variant == FM_VARIANT_KVINJECT) s = kvinject_create(d, st);
     } while (0);
@@ -1704,8 +1730,8 @@ fm_status fm_lm_argmax(fm_drafter* d, const float* hidden, int32_t rows, int32_t
     HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
     LmArgs a{};
     const bool q8 = d->c.wtype == FM_W_Q8_0;
-    a.E = q8 ? (const void*)d->at<uint8_t>(d->p.lmq) : d->W("lm_head.weight");
-    a.Ed = q8 ? (const void*)d->at<uint16_t>(d->p.lmqd) : nullptr;
+    a.E = q8 ? d->W("lm_head.qt") : d->W("lm_head.weight");
+    a.Ed = q8 ? d->W("lm_head.dt") : nullptr;
     a.X = fr;
     a.V = d->c.vocab;
     a.K = K;
@@ -1735,8 +1761,8 @@ fm_status fm_lm_argmax_static(fm_drafter* d, const float* hidden, int32_t rows, 
     HIPCHK(launch_f32_to_frag(hidden, K, rows, K, fr, st));
     LmArgs a{};
     const bool q8 = d->c.wtype == FM_W_Q8_0;
-    a.E = q8 ? (const void*)d->at<uint8_t>(d->p.lmq) : d->W("lm_head.weight");
-    a.Ed = q8 ? (const void*)d->at<uint16_t>(d->p.lmqd) : nullptr;
+    a.E = q8 ? d->W("lm_head.qt") : d->W("lm_head.weight");
+    a.Ed = q8 ? d->W("lm_head.dt") : nullptr;
     a.X = fr;
     a.V = d->c.vocab;
     a.K = K;

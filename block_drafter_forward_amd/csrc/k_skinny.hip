@@ -537,21 +537,23 @@ hipError_t launch_nt(const SkinnyArgs& a, int nwg, hipStream_t st) {
 }
 
 // ── Q8_0: the tile-owning variant ──────────────────────────────────────────────────────────────
-// A work-group is SK_WS_WAVES waves walking columns [split K / S, (split + 1) K / S) in chunks of 256, each chunk's
-// fragments staged once per work-group (fm_ws.h), two chunks in flight per wave, three work-groups per CU (50 KB of
-// LDS, at most 168 VGPRs; the epilogue's tile reuses the fragment slabs). Against three chunks in flight and two
-// work-groups per CU the MTP pass went from 524 to 515 us: the launches of 544 and 640 work-groups no longer leave a
-// second, mostly empty round. Wave w owns one 16-row tile:
-// tile NW tg + w of its group, or for a gated unit (GLU) tile NW / 2 tg + w / 2 of the gate (w even) or of the up
-// matrix (w odd), the pair combined through LDS at the end. Tail waves of a group's last work-group redo its last
-// tile, their results dropped. Each wave's 16 x 16 tile is complete for its k-range, so no sum over waves: the
-// epilogue goes straight from the accumulator (SK_PARTIAL: the split's slab).
+// The weights come in the MFMA operand layout (launch_q8_tile_copy: per 16-row tile and 256-column chunk, each lane's
+// 64 bytes of codes contiguous, then its row's 8 scales), so codes go from HBM straight into the operand registers.
+// A work-group is SK_WS_WAVES waves walking columns [split K / S, (split + 1) K / S) in chunks of 256, two chunks in
+// flight per wave, each chunk's activation fragments staged once per work-group in a double-buffered LDS slab;
+// three work-groups per CU (at most 168 VGPRs), so that the launches of 544 and 640 work-groups of the MTP head fit
+// one round. The fragments are the MFMA's A operand and the codes its B operand: a lane's output column is its own
+// code row, each k-step's scale one of its own 8. Wave w owns one 16-row tile: tile NW tg + w of its group, or for a
+// gated unit (GLU) tile NW / 2 tg + w / 2 of the gate (w even) or of the up matrix (w odd), the pair combined
+// through LDS at the end. Tail waves of a group's last work-group redo its last tile, their results dropped. Each
+// wave's 16 x 16 tile is complete for its k-range, so no sum over waves: the epilogue goes straight from the
+// accumulator (SK_PARTIAL: the split's slab).
 template <bool GLU>
 __global__ __launch_bounds__(SK_WS_WAVES * 64, 3) void skinny_ws_kernel(SkinnyArgs a) {
     constexpr int NW = SK_WS_WAVES, TPW = GLU ? NW / 2 : NW;   // tiles per work-group (of each matrix)
-    __shared__ uint4 alds_all[NW][16 * ws::Q8_PITCH];
-    __shared__ uint16_t slds_all[NW][128];
+    constexpr int ST = 2;                                      // chunks in flight per wave
     __shared__ uint4 blds_all[2][1024];
+    static_assert(sizeof(float) * NW * 16 * 17 <= sizeof(blds_all), "epilogue tile");
     float(*tile_all)[16][17] = (float(*)[16][17])&blds_all[0][0];   // after the last product
     const int bid = blockIdx.x;
     int gi = 0;
@@ -562,59 +564,87 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 3) void skinny_ws_kernel(SkinnyAr
     const int local = bid - G.tile_begin;
     const int tg = local / a.S, split = local - tg * a.S;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
     const int ntile = G.M / 16, mt = tg * TPW + (GLU ? wave >> 1 : wave);
     const bool own = mt < ntile;
     const int m0 = min(mt, ntile - 1) * 16;
     const bool up = GLU && (wave & 1);
-    const int K = a.K, kc = K / a.S, c0 = split * kc, nch = kc >> 8;
-    const int8_t* const Ct[1] = {(const int8_t*)(up ? G.W2 : G.W) + (size_t)m0 * K + c0};
-    const uint16_t* const Dt[1] = {(const uint16_t*)(up ? G.W2d : G.Wd) + (size_t)m0 * (K >> 5) + (c0 >> 5)};
-    const uint8_t* X = G.X + (size_t)(c0 >> 5) * FRAG_STEP_BYTES;
-    uint4* alds = alds_all[wave];
-    uint16_t* slds = slds_all[wave];
-    f32x4_t acc[1][1] = {{f32x4_t{0.f, 0.f, 0.f, 0.f}}};
-    using Regs = ws::RegsQ8<NW, 1>;
-    auto load = [&](Regs& r, int ch) {   // nothing past the last chunk (a uniform branch)
-        if (ch < nch) ws::load_q8<NW, 1>(r, Ct, Dt, K, X, ch, tid);
+    const int K = a.K, ncht = K >> 8, nch = ncht / a.S, c0 = split * nch;   // chunks: per row, per split, first
+    const size_t tc0 = (size_t)(m0 >> 4) * ncht + c0;
+    const uint8_t* Tq = (const uint8_t*)(up ? G.W2 : G.W) + tc0 * 4096 + lane * 16;
+    const uint16_t* Ts = (const uint16_t*)(up ? G.W2d : G.Wd) + tc0 * 128 + r * 8;
+    const uint8_t* X = G.X + (size_t)c0 * 8 * FRAG_STEP_BYTES;
+    struct Regs {
+        uint4 c[4];            // codes of k-steps 2i, 2i + 1 (8 each) in c[i]
+        uint4 s;               // the row's 8 scales
+        uint4 b[16 / NW];      // this thread's share of the chunk's fragments
+    };
+    auto load = [&](Regs& q, int ch) {   // nothing past the last chunk (a uniform branch)
+        if (ch < nch) {
+            const uint8_t* p = Tq + (size_t)ch * 4096;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q.c[i] = ws::ldg_nt(p + i * 1024);
+            q.s = *(const uint4*)(Ts + (size_t)ch * 128);
+            const uint4* xb = (const uint4*)(X + (size_t)ch * 8 * FRAG_STEP_BYTES);
+#pragma unroll
+            for (int j = 0; j < 16 / NW; ++j) q.b[j] = xb[tid + 64 * NW * j];
+        }
         __builtin_amdgcn_sched_barrier(0);   // each chunk's loads stay together (one wait per chunk)
     };
-    // chunk c is staged into slab c % 2: written after the barrier that follows the multiply of chunk c - 2
-    auto step = [&](Regs& r, int c, int buf) {
-        ws::stage_q8<NW, 1>(r, alds, slds, blds_all[buf], tid);
-        load(r, c + 2);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // chunk c's fragments go to slab c % 2: written after the barrier that follows the multiply of chunk c - 2
+    auto step = [&](const Regs& q, int ch) {
+        uint4* blds = blds_all[ch & 1];
+#pragma unroll
+        for (int j = 0; j < 16 / NW; ++j) blds[tid + 64 * NW * j] = q.b[j];
         __syncthreads();
-        ws::compute_q8<1>(alds, slds, blds_all[buf], acc, lane);
-    };
-    Regs r0, r1;
-    load(r0, 0);
-    load(r1, 1);
-    int ch = 0;
-    for (; ch + 2 <= nch; ch += 2) {
-        step(r0, ch, 0);
-        step(r1, ch + 1, 1);
-    }
-    if (ch < nch) step(r0, ch, 0);
-
-    // lane holds Y[t = lane % 16][m0 + 4 g + j]
-    const int t = lane & 15, g = lane >> 4, mc = m0 + 4 * g;
-    if (!GLU && (a.mode == SK_F32 || a.mode == SK_PARTIAL)) {
-        if (!own || t >= a.T) return;
-        float4 o = make_float4(acc[0][0][0], acc[0][0][1], acc[0][0][2], acc[0][0][3]);
-        float* dst = (float*)G.out + (size_t)t * G.ld + mc;
-        if (a.mode == SK_PARTIAL) {
-            dst += (size_t)split * a.part_stride;
-        } else if (G.bias) {
-            o.x += bf16_to_f32(G.bias[mc]);
-            o.y += bf16_to_f32(G.bias[mc + 1]);
-            o.z += bf16_to_f32(G.bias[mc + 2]);
-            o.w += bf16_to_f32(G.bias[mc + 3]);
+        const uint32_t sw[4] = {q.s.x, q.s.y, q.s.z, q.s.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 xh = blds[i * 128 + lane], xl = blds[i * 128 + 64 + lane];
+            const uint4 cc = q.c[i >> 1];
+            const bf16x8_t B = ws::as_bf(ws::i8x8_bf16((i & 1) ? make_uint2(cc.z, cc.w) : make_uint2(cc.x, cc.y)));
+            f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws::as_bf(xh), B, p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws::as_bf(xl), B, p, 0, 0, 0);
+            const float sc = f16_to_f32((uint16_t)((i & 1) ? (sw[i >> 1] >> 16) : (sw[i >> 1] & 0xffffu)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += sc * p[j];
         }
-        *(float4*)dst = o;
+    };
+    Regs q[ST];
+#pragma unroll
+    for (int u = 0; u < ST; ++u) load(q[u], u);
+    int ch = 0;
+    for (; ch + ST <= nch; ch += ST) {
+#pragma unroll
+        for (int u = 0; u < ST; ++u) {
+            step(q[u], ch + u);
+            load(q[u], ch + u + ST);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < ST - 1; ++u)
+        if (ch + u < nch) step(q[u], ch + u);
+
+    // lane holds Y[t = 4 g + j][m0 + r]
+    if (!GLU && (a.mode == SK_F32 || a.mode == SK_PARTIAL)) {
+        if (!own) return;
+        const int m = m0 + r;
+        float* dst = (float*)G.out + m;
+        float bias = 0.f;
+        if (a.mode == SK_PARTIAL) dst += (size_t)split * a.part_stride;
+        else if (G.bias) bias = bf16_to_f32(G.bias[m]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * g + j < a.T) dst[(size_t)(4 * g + j) * G.ld] = acc[j] + bias;
         return;
     }
     __syncthreads();   // every wave is done with the fragment slabs that tile_all reuses
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile_all[wave][t][4 * g + j] = acc[0][0][j];
+    for (int j = 0; j < 4; ++j) tile_all[wave][4 * g + j][r] = acc[j];
+    // from here the tile is read as [t = lane % 16][column 4 (lane / 16) + j]: other lanes' writes
+    const int t = lane & 15, mc = m0 + 4 * g;
     if constexpr (GLU) {
         __syncthreads();   // the up tile of the pair is in its wave's LDS
         if (up) return;
@@ -625,6 +655,7 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 3) void skinny_ws_kernel(SkinnyAr
             tile_all[wave][t][4 * g + j] = a.mode == SK_FRAG_GEGLU ? gelu_tanh(v) * u : silu(v) * u;
         }
     } else {   // SK_FRAG_GELU
+        __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave: the reads below see the writes
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float v = tile_all[wave][t][4 * g + j];
