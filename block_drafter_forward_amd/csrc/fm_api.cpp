@@ -196,7 +196,7 @@ std::vector<Q8Mat> q8_mats(const fm_config& c) {
 // ── workspace plan ──────────────────────────────────────────────────────────────────────────────
 struct Plan {
     size_t best, mcut, zeros, rope, fragA, fragH, fragO, fragU, x, part, qkv, attnp, stage, h0, colsc, cmean, hc, pctx,
-        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, q8t, blockn, zbase, tcond, qkv0, x1, q0c,
+        pctxn, qout, apart, afrag, cfrag, w16, taps16, rope_pf, echain, q8t, ssq, blockn, zbase, tcond, qkv0, x1, q0c,
         rscale, modc, lnstats, c12, lnfrag, rtick, dargs, dlayers, dsync, arena, total;
     size_t zeros_bytes;
     int best_rows;           // argmax keys (one per row)
@@ -292,6 +292,8 @@ Plan make_plan(const fm_config& c) {
     size_t q8b = 0;
     for (const Q8Mat& m : q8_mats(c)) q8b += align256((size_t)m.M * m.K) + align256((size_t)m.M * (m.K / 32) * 2);
     p.q8t = take(q8b);
+    // the MTP head's RMSNorm folds: sums of squares per 512-column slice, [2 segments][16 rows][slices]
+    p.ssq = take(c.variant == FM_VARIANT_MTP ? (size_t)2 * 16 * ((c.dim + 511) / 512) * 4 : 0);
     // KV-injection: the normed backbone rows of the last draft (the confidence head's input) and the base logits
     // of the Markov decode
     const bool kvi = c.variant == FM_VARIANT_KVINJECT;
@@ -499,6 +501,12 @@ struct SkExtra {
     int ln_rms = 0;                  // the RMSNorm fold (no c1 / c2)
     const uint16_t* ryw = nullptr;   // SK_RESID: fragments of x w (the next RMSNorm's weight) instead of x (1 + s)
     SelfAttnArgs sa{};   // q | k | v with the self-attention tail (sa.qkv set)
+    // Q8_0: the RMSNorm fold (SkinnyArgs.rms_*)
+    const float* rms_ssq = nullptr;
+    int rms_nsl = 0;
+    int rms_seg = 0;
+    float rms_inv = 0.f;
+    float rms_eps = 0.f;
 };
 
 // Enqueue one skinny launch. For SK_PARTIAL the k-split is chosen here (returned through S_out); every other mode
@@ -565,6 +573,11 @@ fm_status skinny(const fm_drafter* d, const std::vector<SkGroupDesc>& gs, int K,
         a.rstats = ex->rstats;
         a.rdebug = ex->rdebug;
         a.sa = ex->sa;
+        a.rms_ssq = ex->rms_ssq;
+        a.rms_nsl = ex->rms_nsl;
+        a.rms_seg = ex->rms_seg;
+        a.rms_inv = ex->rms_inv;
+        a.rms_eps = ex->rms_eps;
         if (a.sa.qkv) a.satick = d->at<uint32_t>(d->p.rtick) + RTICK_MAX;
     }
     if (mode == SK_RESID && !ex) return fail(FM_E_INVALID, "skinny: a residual update needs its operands");
@@ -1469,41 +1482,58 @@ fm_status mtp_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* con
     auto Q = [&](const char* n) { return d->W(std::string(n) + ".qt"); };   // the copies in the MFMA operand layout
     auto Dd = [&](const char* n) { return d->W(std::string(n) + ".dt"); };
 
+    // The three RMSNorms that feed a Q8_0 product (enorm | hnorm before eh_proj, attn_norm, post_attention_norm)
+    // are folded into it: a row kernel writes the fragments of w x and each 512-column slice's sum of squares, the
+    // product scales its rows by their rstd. ssq holds one or two segments' sums ([segment][16][nsl]).
+    float* ssq = d->at<float>(d->p.ssq);
+    const int nsl = (H + 511) / 512;
+    SkExtra fold{};
+    fold.rms_ssq = ssq;
+    fold.rms_nsl = nsl;
+    fold.rms_seg = H;
+    fold.rms_inv = 1.f / (float)H;
+    fold.rms_eps = c.rms_eps;
+    auto rms = [&](int nseg, const float* in0, const float* in1, int row0, int T, bool x_in, const float* w0,
+                   const float* w1, int S, uint8_t* frag, int frag_kw) -> fm_status {
+        RmsSegArgs r{};
+        r.in[0] = in0;
+        r.in[1] = in1;
+        r.in_ld = H;
+        r.x_in = x_in ? 1 : 0;
+        r.x = nseg == 1 ? x : nullptr;
+        r.part = S > 0 ? part : nullptr;
+        r.part_stride = pstr;
+        r.S = S;
+        r.w[0] = w0;
+        r.w[1] = w1;
+        r.frag = frag;
+        r.frag_kw = frag_kw;
+        r.ssq = ssq;
+        r.nsl = nsl;
+        r.D = H;
+        r.T = T;
+        r.row0 = row0;
+        r.nseg = nseg;
+        HIPCHK(launch_rms_seg(r, st));
+        return FM_OK;
+    };
     // x = eh_proj([enorm(e); hnorm(h)])
     for (int b = 0; b < B; ++b)
-        for (int side = 0; side < 2; ++side) {
-            RowArgs r = rows_base(d, H, as[b]->rows);
-            r.row0 = off[b];
-            r.in_rows = side == 0 ? as[b]->embed_rows : as[b]->prev_hidden;
-            r.in_ld = H;
-            r.norm = ROW_RMS;
-            r.w_f32 = d->F(side == 0 ? "enorm" : "hnorm");
-            r.eps = c.rms_eps;
-            r.frag_out = fragA;
-            r.frag_koff = side * H;
-            CHK(rows(r, st));
-        }
-    int S = 0;
+        CHK(rms(2, as[b]->embed_rows, as[b]->prev_hidden, off[b], as[b]->rows, false, d->F("enorm"), d->F("hnorm"), 0,
+                fragA, 2 * H));
+    // eh_proj's splits each take columns of one norm's segment: an even split of the 2H columns
+    int S = pick_split_ws(ws_groups(H), 2 * H);
+    for (int s2 = S; S % 2 && s2 <= 8; ++s2)
+        if ((2 * H / 256) % s2 == 0 && s2 % 2 == 0) S = s2;
+    if (S % 2) S = 2;
     CHK(skinny(d, {{Q("eh_proj"), Dd("eh_proj"), nullptr, nullptr, nullptr, fragA, part, H, H}}, 2 * H, M, SK_PARTIAL,
-               0, &S, st));
-    {
-        RowArgs r = rows_base(d, H, M);
-        r.x = x;
-        r.base_zero = 1;
-        r.part = part;
-        r.S = S;
-        r.part_stride = pstr;
-        r.norm = ROW_RMS;
-        r.w_f32 = d->F("attn_norm");
-        r.eps = c.rms_eps;
-        r.frag_out = fragH;
-        CHK(rows(r, st));
-    }
+               S, &S, st, 0, 0, 1, &fold));
+    CHK(rms(1, nullptr, nullptr, 0, M, false, d->F("attn_norm"), nullptr, S, fragH, H));
     CHK(skinny(d,
                {{Q("attn_q"), Dd("attn_q"), nullptr, nullptr, nullptr, fragH, qkv, qw, qkvw},
                 {Q("attn_k"), Dd("attn_k"), nullptr, nullptr, nullptr, fragH, qkv + qw, kw, qkvw},
                 {Q("attn_v"), Dd("attn_v"), nullptr, nullptr, nullptr, fragH, qkv + qw + kw, kw, qkvw}},
-               H, M, SK_F32, 0, nullptr, st));
+               H, M, SK_F32, 0, nullptr, st, 0, 0, 1, &fold));
     for (int b = 0; b < B; ++b) {
         fm_drafter* e = ds[b];
         float* qb = qkv + (size_t)off[b] * qkvw;
@@ -1535,20 +1565,9 @@ fm_status mtp_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* con
     }
     CHK(skinny(d, {{Q("attn_output"), Dd("attn_output"), nullptr, nullptr, nullptr, fragO, part, H, H}}, NH * HD, M,
                SK_PARTIAL, 0, &S, st));
-    {
-        RowArgs r = rows_base(d, H, M);
-        r.x = x;
-        r.part = part;
-        r.S = S;
-        r.part_stride = pstr;
-        r.norm = ROW_RMS;
-        r.w_f32 = d->F("post_attention_norm");
-        r.eps = c.rms_eps;
-        r.frag_out = fragH;
-        CHK(rows(r, st));
-    }
+    CHK(rms(1, nullptr, nullptr, 0, M, true, d->F("post_attention_norm"), nullptr, S, fragH, H));
     CHK(skinny(d, {{Q("ffn_gate"), Dd("ffn_gate"), Q("ffn_up"), Dd("ffn_up"), nullptr, fragH, fragU, c.ffn, 0}}, H, M,
-               SK_FRAG_SWIGLU, 0, nullptr, st));
+               SK_FRAG_SWIGLU, 0, nullptr, st, 0, 0, 1, &fold));
     CHK(skinny(d, {{Q("ffn_down"), Dd("ffn_down"), nullptr, nullptr, nullptr, fragU, part, H, H}}, c.ffn, M,
                SK_PARTIAL, 0, &S, st));
     {

@@ -93,6 +93,14 @@ struct SkinnyArgs {
     // (satick[head], zero between launches), and the head's last arrival (3 hd / 16 of them) runs its attention
     SelfAttnArgs sa;
     uint32_t* satick;
+    // RMSNorm fold of the Q8_0 variant: the fragments hold w x of rows x whose RMSNorm is the real input, rms_ssq the
+    // sums of squares of x per 512-column slice (launch_rms_seg: [segment][16][rms_nsl]); a split's columns lie in
+    // segment c / rms_seg, and the product of row t is scaled by 1 / sqrt(sum ssq * rms_inv + rms_eps)
+    const float* rms_ssq;
+    int rms_nsl;
+    int rms_seg;
+    float rms_inv;
+    float rms_eps;
 };
 #define LN_MAX_TILES 256   // LayerNorm fold: x at most 4096 wide (2048 with two blocks of rows)
 // Q8_0 weights run the tile-owning variant: a work-group of SK_WS_WAVES waves owns that many adjacent 16-row tiles
@@ -139,6 +147,29 @@ struct RowArgs {
     int frag_kw;           // width of the fragment matrix frag_out (0: D); rows >= 16 sit in its second block
 };
 hipError_t launch_rows(const RowArgs& a, hipStream_t st);
+
+// The RMSNorm fold's producer: for rows row0 .. row0 + T - 1 (at most 16 in all) and nseg (1 or 2) segments of D
+// columns, segment s's row v = in[s] row t (in_ld apart; null: x's row if x_in, else 0), plus with one segment the
+// S split partials (row row0 + t of each [16][D] slab, part_stride floats apart); x (one segment) receives v; the
+// fragments (width frag_kw) receive w[s] * v at k offset s D; ssq[(s 16 + row) nsl + slice] the sum of v^2 over
+// each 512-column slice (nsl = ceil(D / 512)). The consumer (SkinnyArgs.rms_*) scales its product by
+// 1 / sqrt(sum ssq / D + eps).
+struct RmsSegArgs {
+    const float* in[2];
+    int in_ld;
+    int x_in;              // 1: the base is x's row (segment 0, no in[0])
+    float* x;
+    const float* part;
+    long long part_stride;
+    int S;
+    const float* w[2];     // f32 RMSNorm weights
+    uint8_t* frag;
+    int frag_kw;
+    float* ssq;
+    int nsl;
+    int D, T, row0, nseg;
+};
+hipError_t launch_rms_seg(const RmsSegArgs& a, hipStream_t st);
 
 // f32 rows [T][K] (row stride ld) -> fragments. T <= 32 (rows 16.. in the second block), K % 32 == 0.
 hipError_t launch_f32_to_frag(const float* x, int ld, int T, int K, uint8_t* frag, hipStream_t st);

@@ -138,6 +138,42 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     }
 }
 
+// The RMSNorm fold's producer (the MTP head): one wave per (row, 512-column slice, segment). Segment s's row is
+// in[s] (or zero) plus, with one segment, the sum of the split partials; it is written to x if set, w[s] * row goes
+// out as fragments at k offset s D, and the slice's sum of squares to ssq[s][row0 + t][slice]. The consumer takes
+// rstd = 1 / sqrt(sum ssq / D + eps) of each row and segment and multiplies its product by it.
+__global__ __launch_bounds__(64) void rms_seg_kernel(RmsSegArgs a) {
+    const int t = blockIdx.x, sl = blockIdx.y, sg = blockIdx.z;
+    const int D = a.D, row = a.row0 + t;
+    const int i0 = (sl * 64 + (int)threadIdx.x) * 8;
+    float q = 0.f;
+    if (i0 < D) {
+        float v[8], w[8];
+        if (a.in[sg]) ld8(a.in[sg] + (size_t)t * a.in_ld + i0, v);
+        else if (a.x_in) ld8(a.x + (size_t)row * D + i0, v);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        for (int sp = 0; sp < a.S; ++sp) {
+            float pp[8];
+            ld8(a.part + (size_t)sp * a.part_stride + (size_t)row * D + i0, pp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += pp[e];
+        }
+        if (a.x) st8(a.x + (size_t)row * D + i0, v);
+        ld8(a.w[sg] + i0, w);
+        float h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            q += v[e] * v[e];
+            h[e] = v[e] * w[e];
+        }
+        frag_store8_rows(a.frag, a.frag_kw, row, sg * D + i0, h);
+    }
+    q = wave_sum(q);
+    if (threadIdx.x == 0) a.ssq[((size_t)sg * 16 + row) * gridDim.y + sl] = q;
+}
+
 // The rows whose products with a matrix W give the LayerNorm fold's c1 = sum_k (1 + s_k) W[m][k] and
 // c2 = sum_k shift_k W[m][k]: for modulation j of the table (scale, shift, gate at mod + 3 j D), row 0 = 1 + scale
 // and row 1 = shift as fragments at frag + j D 64 (a 16-row block; rows 2..15 zero).
@@ -576,4 +612,14 @@ hipError_t launch_rms_f16(const float* x, int n, int D, const uint16_t* w, float
     case 4: return launch_rms_f16_s<4>(x, n, D, w, eps, out, slab_stride, rscale, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_rms_seg(const RmsSegArgs& a, hipStream_t st) {
+    const int nsl = (a.D + 511) / 512;
+    if (a.D % 32 || a.T < 1 || a.row0 < 0 || a.row0 + a.T > 16 || a.nseg < 1 || a.nseg > 2 || !a.w[0] ||
+        (a.nseg == 2 && !a.w[1]) || !a.frag || !a.ssq || a.frag_kw < a.nseg * a.D || a.S < 0 || (a.S > 0 && !a.part) ||
+        (a.x_in && !a.x) || ((a.S > 0 || a.x) && a.nseg != 1) || nsl != a.nsl)
+        return hipErrorInvalidValue;
+    rms_seg_kernel<<<dim3(a.T, nsl, a.nseg), 64, 0, st>>>(a);
+    return hipGetLastError();
 }

@@ -612,6 +612,14 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 3) void skinny_ws_kernel(SkinnyAr
             for (int j = 0; j < 4; ++j) acc[j] += sc * p[j];
         }
     };
+    // the RMSNorm fold: lane t < 16 takes row t's rstd over the segment holding this split's columns
+    float rstd = 0.f;
+    if (a.rms_ssq && r < a.T) {
+        const float* qs = a.rms_ssq + ((size_t)((c0 * 256) / a.rms_seg) * 16 + r) * a.rms_nsl;
+        float sum = 0.f;
+        for (int i = 0; i < a.rms_nsl; ++i) sum += qs[i];
+        rstd = 1.f / sqrtf(sum * a.rms_inv + a.rms_eps);
+    }
     Regs q[ST];
 #pragma unroll
     for (int u = 0; u < ST; ++u) load(q[u], u);
@@ -626,6 +634,9 @@ __global__ __launch_bounds__(SK_WS_WAVES * 64, 3) void skinny_ws_kernel(SkinnyAr
 #pragma unroll
     for (int u = 0; u < ST - 1; ++u)
         if (ch + u < nch) step(q[u], ch + u);
+    if (a.rms_ssq)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] *= __shfl(rstd, 4 * g + j, 64);
 
     // lane holds Y[t = 4 g + j][m0 + r]
     if (!GLU && (a.mode == SK_F32 || a.mode == SK_PARTIAL)) {
@@ -694,6 +705,9 @@ hipError_t launch_skinny(const SkinnyArgs& a, int wtype, int nwg, hipStream_t st
         return hipErrorInvalidValue;
     if (a.mode == SK_RESID && (wtype != SKW_BF16 || a.S < 1 || !a.rx || !a.rbase || !a.ryscale == !a.ryw || !a.rstats ||
                                a.ngroups != 1 || (a.S > 1 && (!a.rpart || !a.rtick))))
+        return hipErrorInvalidValue;
+    if (a.rms_ssq && (wtype != SKW_Q8_0 || a.rms_nsl < 1 || a.rms_seg < 256 || a.rms_seg % 256 ||
+                      a.K % a.rms_seg || a.K / a.rms_seg > 2 || a.rms_seg % (a.K / a.S)))   // a split in one segment
         return hipErrorInvalidValue;
     if (wtype == SKW_BF16) return glu ? launch_nt<2, SKW_BF16>(a, nwg, st) : launch_nt<1, SKW_BF16>(a, nwg, st);
     if (a.mode == SK_RESID) return hipErrorInvalidValue;
