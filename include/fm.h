@@ -107,7 +107,9 @@ size_t fm_kv_bytes(const fm_config* cfg);
 
 /* Bytes of the device workspace the caller allocates for `cfg` (0 if cfg is invalid): activations, split-K
  * partials, the RoPE table (and its prefill copy), the zero-noise slot row, argmax scratch, prefill buffers (an f16
- * copy of one append's taps; f16 copies of the context-projection and K/V weights, made at create).
+ * copy of one append's taps; f16 copies of the context-projection and K/V weights, made at create); for Q8_0
+ * weights (the MTP head) a copy of every Q8_0 matrix, the lm_head included, in the order its matrix-core kernels
+ * read it (made at create: 1.79 GB at the MTP head shape).
  * Owned by the caller; reserved for one handle. */
 size_t fm_workspace_bytes(const fm_config* cfg);
 
@@ -117,7 +119,8 @@ size_t fm_workspace_bytes(const fm_config* cfg);
  * workspace must be at least fm_kv_bytes / fm_workspace_bytes and 256-byte aligned.
  * Enqueues the create-time work on `stream`: clearing the workspace's counters, the RoPE table (angles in f64,
  * stored f32, and its permuted prefill copy), f16 copies of the context-projection and per-layer K/V weights
- * (flow-map and KV-inject) and, for the flow-map, a private copy of the modulation table "mod", the zero-noise slot
+ * (flow-map and KV-inject), copies of the Q8_0 matrices in the matrix-core operand order (MTP: Q8_0 codes must be
+ * 8-byte aligned; a misaligned table fails with FM_E_HIP) and, for the flow-map, a private copy of the modulation table "mod", the zero-noise slot
  * input x_embed(state_norm(mean row of lm_head)) + bias (flashmap_drafter.js, init), and layer 0 of a draft from
  * that row up to the cross-attention's q projection (the same for every draft: each slot starts from that row, and
  * the self-attention of identical v rows returns v, so this holds at zero noise, the only slot input built here).
