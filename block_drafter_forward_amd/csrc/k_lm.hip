@@ -117,15 +117,16 @@ __global__ __launch_bounds__(NW * 64) void lm_argmax_ws_kernel(LmArgs a) {
 }
 
 // Q8_0 tables in the MFMA operand layout (q8_tile_copy_kernel): a wave owns one 16-row vocabulary tile and walks
-// the k-range in chunks of 256 columns (8 Q8_0 blocks), three chunks in flight. Per chunk a lane loads the 64 bytes
+// the k-range in chunks of 256 columns (8 Q8_0 blocks), two chunks in flight. Per chunk a lane loads the 64 bytes
 // of codes it multiplies (four 16-byte loads, each instruction 1 KB contiguous) and the 8 scales of its row; the
 // chunk's activation fragments go through a double-buffered LDS slab shared by the work-group's 4 waves. The
 // fragments are the MFMA's A operand and the codes its B operand, so a lane's output column is its own code row and
-// each step's scale is one of the lane's own 8. Two work-groups per CU (242 VGPRs): against the row-major table
-// staged through LDS (8 waves, one work-group per CU) the MTP head's 248320 x 5120 table went from 303 to 271 us.
-constexpr int LMQ_NW = 4, LMQ_ST = 3;
+// each step's scale is one of the lane's own 8. Three work-groups per CU (at most 168 VGPRs). The MTP head's
+// 248320 x 5120 table: 303 us per call row-major and staged through LDS (8 waves, one work-group per CU); from the
+// copy, 267 us with three chunks in flight and two work-groups per CU, 252 us with two chunks and three.
+constexpr int LMQ_NW = 4, LMQ_ST = 2;
 
-__global__ __launch_bounds__(LMQ_NW * 64, 2) void lm_argmax_q8t_kernel(LmArgs a) {
+__global__ __launch_bounds__(LMQ_NW * 64, 3) void lm_argmax_q8t_kernel(LmArgs a) {
     constexpr int NW = LMQ_NW, ST = LMQ_ST;
     __shared__ uint4 blds_all[2][1024];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
