@@ -1643,6 +1643,11 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
             return fail(FM_E_MISSING_WEIGHT, "missing weight '%s'", n.c_str());
         }
     if (cfg->variant == FM_VARIANT_KVINJECT && cfg->block < 1) { delete d; return fail(FM_E_INVALID, "gamma"); }
+    for (const Q8Mat& m : q8_mats(*cfg))   // checked before any work is enqueued: the copies read codes 8 bytes a lane
+        if (((uintptr_t)d->W(std::string(m.name) + ".q") & 7) || ((uintptr_t)d->W(std::string(m.name) + ".d") & 1)) {
+            delete d;
+            return fail(FM_E_INVALID, "%s.q must be 8-byte aligned and %s.d 2-byte aligned", m.name, m.name);
+        }
     hipStream_t st = (hipStream_t)stream;
     fm_status s = FM_OK;
     do {
@@ -1679,7 +1684,7 @@ fm_status fm_create(const fm_config* cfg, int32_t n_weights, const char* const* 
             const hipError_t e = launch_q8_tile_copy((const int8_t*)d->W(n + ".q"), (const uint16_t*)d->W(n + ".d"),
                                                      m.M, m.K, oq, od, st);
             if (e != hipSuccess) {
-                s = fail(FM_E_HIP, "Q8_0 copy of %s: %s (codes 8-byte aligned?)", m.name, hipGetErrorString(e));
+                s = fail(FM_E_HIP, "Q8_0 copy of %s: %s", m.name, hipGetErrorString(e));
                 break;
             }
             d->w[n + ".qt"] = oq;

@@ -119,8 +119,9 @@ size_t fm_workspace_bytes(const fm_config* cfg);
  * workspace must be at least fm_kv_bytes / fm_workspace_bytes and 256-byte aligned.
  * Enqueues the create-time work on `stream`: clearing the workspace's counters, the RoPE table (angles in f64,
  * stored f32, and its permuted prefill copy), f16 copies of the context-projection and per-layer K/V weights
- * (flow-map and KV-inject), copies of the Q8_0 matrices in the matrix-core operand order (MTP: Q8_0 codes must be
- * 8-byte aligned; a misaligned table fails with FM_E_HIP) and, for the flow-map, a private copy of the modulation table "mod", the zero-noise slot
+ * (flow-map and KV-inject), copies of the Q8_0 matrices in the matrix-core operand order (MTP: every "<name>.q"
+ * must be 8-byte aligned and every "<name>.d" 2-byte aligned, else FM_E_INVALID before any work is enqueued) and,
+ * for the flow-map, a private copy of the modulation table "mod", the zero-noise slot
  * input x_embed(state_norm(mean row of lm_head)) + bias (flashmap_drafter.js, init), and layer 0 of a draft from
  * that row up to the cross-attention's q projection (the same for every draft: each slot starts from that row, and
  * the self-attention of identical v rows returns v, so this holds at zero noise, the only slot input built here).

@@ -81,6 +81,24 @@ def test_mtp_bad_rows():
     assert ex.value.status == fm.FM_E_INVALID
 
 
+def test_mtp_misaligned_codes_refused():
+    """The create-time copies read Q8_0 codes 8 bytes at a time: a misaligned table is refused on the host."""
+    from block_drafter_forward_amd import fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = SMALL
+    dev = fm.upload_weights(gen.make_weights(cfg))
+    q = dev["lm_head.q"]
+    buf = torch.zeros(q.numel() + 16, dtype=q.dtype, device="cuda")
+    buf[1:1 + q.numel()].copy_(q.reshape(-1))
+    dev["lm_head.q"] = buf[1:1 + q.numel()].view(q.shape)
+    assert dev["lm_head.q"].data_ptr() % 8 != 0
+    with pytest.raises(fm.FmError) as ex:
+        fm.Drafter(cfg, dev)
+    assert ex.value.status == fm.FM_E_INVALID and "aligned" in str(ex.value)
+    torch.cuda.synchronize()
+
+
 def test_mtp_lm_head_row_scales():
     """The Q8_0 lm_head alone on rows whose magnitudes span 1e-30 .. 1e30 (each row is brought into the f16 range
     by a power of two inside the library): logits within the row tolerance, tokens by the top-2 gap rule."""
