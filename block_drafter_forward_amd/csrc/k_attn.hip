@@ -265,6 +265,11 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
     constexpr int LDK = C * V4 / 256;            // float4 of K (and of V) per thread
     constexpr int LDQ = NQR * V4 / 256;          // float4 of q per thread
     static_assert(LDK >= 1 && LDQ >= 1, "shape");
+    // hd = 256 with one query tile: the two waves that compute scores read their query operands straight into
+    // registers, and the query tiles leave LDS (96 -> 79 KB: two work-groups per CU instead of one; the MTP pass at
+    // M = 1 over a 4096-row cache 419 -> 416 us). At hd = 128 (already three per CU) it cost 0.7 us per draft.
+    constexpr bool QREG = QT == 1 && HD == 256;
+    constexpr int NSQ = HD / 32;
     const int c = blockIdx.x, kh = blockIdx.y;
     const int nq = a.nq;
     const int G = a.heads / a.kv_heads;
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
     const QPrep& qp = a.qp;
     __shared__ __attribute__((aligned(16))) _Float16 Kh[C * KROW], Kl[C * KROW];
     __shared__ __attribute__((aligned(16))) _Float16 Vth[HD * VROW], Vtl[HD * VROW];
-    __shared__ __attribute__((aligned(16))) _Float16 Qh[NQR * QROW], Ql[NQR * QROW];
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[QREG ? 8 : NQR * QROW], Ql[QREG ? 8 : NQR * QROW];
     __shared__ __attribute__((aligned(16))) _Float16 Ph[NQR * PROW], Pl[NQR * PROW];
     __shared__ float S[NQR][C + 1];
 
@@ -295,12 +300,25 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
         kr[i] = *((const float4*)(kb + (size_t)kh * HD) + c4);
         vr[i] = *((const float4*)(vb + (size_t)kh * HD) + c4);
     }
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    float4 qf[QREG ? 2 * NSQ : 1];   // QREG: this lane's query operand values (row fr, columns 32 s + fk .. + 7)
+    if constexpr (QREG) {
+        const int hl = fr / nq, m = fr - hl * nq;
+        const float* src = fr < Q ? qp.q + (size_t)m * qp.q_ld + (size_t)(kh * G + hl) * qp.q_hs : qp.zeros;
+        if (wave < 2)   // the score waves (a wave-uniform branch)
 #pragma unroll
-    for (int i = 0; i < LDQ; ++i) {
-        const int u = tid + 256 * i, t = u / V4, c4 = u % V4;
-        const int hl = t / nq, m = t - hl * nq;
-        const float* src = t < Q ? qp.q + (size_t)m * qp.q_ld + (size_t)(kh * G + hl) * qp.q_hs : qp.zeros;
-        qr[i] = *((const float4*)src + c4);
+            for (int s = 0; s < NSQ; ++s) {
+                qf[2 * s] = *(const float4*)(src + 32 * s + fk);
+                qf[2 * s + 1] = *(const float4*)(src + 32 * s + fk + 4);
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < LDQ; ++i) {
+            const int u = tid + 256 * i, t = u / V4, c4 = u % V4;
+            const int hl = t / nq, m = t - hl * nq;
+            const float* src = t < Q ? qp.q + (size_t)m * qp.q_ld + (size_t)(kh * G + hl) * qp.q_hs : qp.zeros;
+            qr[i] = *((const float4*)src + c4);
+        }
     }
     // 2. hi/lo f16 splits into LDS: K row-major, V transposed (dim-major), queries row-major
 #pragma unroll
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < LDQ; ++i) {
+    for (int i = 0; i < (QREG ? 0 : LDQ); ++i) {
         const int u = tid + 256 * i, t = u / V4, d = 4 * (u % V4);
         const float qv[4] = {qr[i].x, qr[i].y, qr[i].z, qr[i].w};
 #pragma unroll
@@ -332,7 +350,6 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
     // 3. scores Sᵀ[j][t]: (key tile, query tile) pairs over the waves
-    const int fr = lane & 15, fk = 8 * (lane >> 4);
     for (int pr = wave; pr < 2 * QT; pr += 4) {
         const int kt = pr & 1, qt = pr >> 1;
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -340,8 +357,20 @@ __global__ __launch_bounds__(256) void attn_split_f32_mfma_kernel(AttnArgs a) {
         for (int s = 0; s < HD / 32; ++s) {
             const f16x8_t Ah = *(const f16x8_t*)(Kh + (kt * 16 + fr) * KROW + s * 32 + fk);
             const f16x8_t Al = *(const f16x8_t*)(Kl + (kt * 16 + fr) * KROW + s * 32 + fk);
-            const f16x8_t Bh = *(const f16x8_t*)(Qh + (qt * 16 + fr) * QROW + s * 32 + fk);
-            const f16x8_t Bl = *(const f16x8_t*)(Ql + (qt * 16 + fr) * QROW + s * 32 + fk);
+            f16x8_t Bh, Bl;
+            if constexpr (QREG) {
+                const float x[8] = {qf[2 * s].x, qf[2 * s].y, qf[2 * s].z, qf[2 * s].w,
+                                    qf[2 * s + 1].x, qf[2 * s + 1].y, qf[2 * s + 1].z, qf[2 * s + 1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const _Float16 h = (_Float16)x[e];
+                    Bh[e] = h;
+                    Bl[e] = (_Float16)(x[e] - (float)h);
+                }
+            } else {
+                Bh = *(const f16x8_t*)(Qh + (qt * 16 + fr) * QROW + s * 32 + fk);
+                Bl = *(const f16x8_t*)(Ql + (qt * 16 + fr) * QROW + s * 32 + fk);
+            }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, acc, 0, 0, 0);
