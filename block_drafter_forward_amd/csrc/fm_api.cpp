@@ -45,7 +45,8 @@ constexpr int SATICK_MAX = 64;    // heads of the self-attention tail
 // 445.8 us split in two with an arrival ticket and 452.8 us split in four)
 constexpr int KVI_RESID_SPLIT = 1;
 constexpr int QKV_SLABS = 4;      // split-K slabs the attention kernels sum while building q (and k, v)
-constexpr int TARGET_WGS = 256;   // work-groups wanted per skinny launch (one per CU)
+constexpr int TARGET_WGS = 256;
+constexpr int MTP_QKV_SPLIT = 2;   // k-split of the MTP head's q | k | v product (K / 256 chunks must divide by it)   // work-groups wanted per skinny launch (one per CU)
 constexpr int PF_SPLIT_WGS = 512; // a k-split prefill launch stays within one round (two 128-tile work-groups per CU)
 constexpr int PF_SPLIT_ROWS = 4096;  // prefill context rows kept for k-split slabs
 
@@ -1529,11 +1530,14 @@ fm_status mtp_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* con
     CHK(skinny(d, {{Q("eh_proj"), Dd("eh_proj"), nullptr, nullptr, nullptr, fragA, part, H, H}}, 2 * H, M, SK_PARTIAL,
                S, &S, st, 0, 0, 1, &fold));
     CHK(rms(1, nullptr, nullptr, 0, M, false, d->F("attn_norm"), nullptr, S, fragH, H));
+    // q | gate, k, v as MTP_QKV_SPLIT partial slabs of [16][qkvw] (one work-group per four tiles would leave CUs
+    // idle: 224 at the MTP shape), summed by mtp_prep
+    int Sq = 0;
     CHK(skinny(d,
                {{Q("attn_q"), Dd("attn_q"), nullptr, nullptr, nullptr, fragH, qkv, qw, qkvw},
                 {Q("attn_k"), Dd("attn_k"), nullptr, nullptr, nullptr, fragH, qkv + qw, kw, qkvw},
                 {Q("attn_v"), Dd("attn_v"), nullptr, nullptr, nullptr, fragH, qkv + qw + kw, kw, qkvw}},
-               H, M, SK_F32, 0, nullptr, st, 0, 0, 1, &fold));
+               H, M, SK_PARTIAL, MTP_QKV_SPLIT, &Sq, st, (long long)TMAX * qkvw, d->p.qkv_floats, 1, &fold));
     for (int b = 0; b < B; ++b) {
         fm_drafter* e = ds[b];
         float* qb = qkv + (size_t)off[b] * qkvw;
@@ -1542,6 +1546,8 @@ fm_status mtp_draft_batch(fm_drafter* const* ds, int B, const fm_block_args* con
         p.kt = qb + qw;
         p.vt = qb + qw + kw;
         p.qf_ld = p.kt_ld = p.vt_ld = qkvw;
+        p.S = Sq;
+        p.slab = (long long)TMAX * qkvw;
         p.M = as[b]->rows;
         p.NH = NH;
         p.NKV = NKV;

@@ -285,6 +285,8 @@ hipError_t launch_kv_final(const KVFinalArgs& a, hipStream_t st);
 struct MtpPrepArgs {
     const float* qf; const float* kt; const float* vt;
     int qf_ld, kt_ld, vt_ld;   // row strides (elements)
+    int S;                 // q | gate, k, v arrive as S split-K partial slabs, slab floats apart: summed here, and each
+    long long slab;        // q head's summed gate written back into slab 0 (where the attention merge reads it)
     int M, NH, NKV, HD, rot;
     const float* qn; const float* kn;
     float eps;

@@ -582,15 +582,27 @@ __global__ __launch_bounds__(256) void mtp_prep_kernel(MtpPrepArgs a) {
     const int pos = a.pos0 + m;
     __shared__ float red[4];
     __shared__ float sh[256];
+    auto sum = [&](const float* p) {   // the S slabs of one element, in slab order
+        float v = p[0];
+        for (int s = 1; s < a.S; ++s) v += p[(size_t)s * a.slab];
+        return v;
+    };
     if (j >= NH + NKV) {
         const int vh = j - NH - NKV;
-        if (tid < HD) a.vc[(size_t)pos * NKV * HD + vh * HD + tid] = a.vt[(size_t)m * a.vt_ld + vh * HD + tid];
+        if (tid < HD) a.vc[(size_t)pos * NKV * HD + vh * HD + tid] = sum(a.vt + (size_t)m * a.vt_ld + vh * HD + tid);
         return;
     }
     float x = 0.f, w = 0.f;
     if (tid < HD) {
-        if (j < NH) { x = a.qf[(size_t)m * a.qf_ld + (size_t)j * 2 * HD + tid]; w = a.qn[tid]; }
-        else { x = a.kt[(size_t)m * a.kt_ld + (size_t)(j - NH) * HD + tid]; w = a.kn[tid]; }
+        if (j < NH) {
+            const size_t qi = (size_t)m * a.qf_ld + (size_t)j * 2 * HD + tid;
+            x = sum(a.qf + qi);
+            w = a.qn[tid];
+            if (a.S > 1) ((float*)a.qf)[qi + HD] = sum(a.qf + qi + HD);   // the gate, for the merge
+        } else {
+            x = sum(a.kt + (size_t)m * a.kt_ld + (size_t)(j - NH) * HD + tid);
+            w = a.kn[tid];
+        }
     }
     const float ss = block_sum256(x * x, red);
     const float y = x * (1.f / sqrtf(ss / (float)HD + a.eps)) * w;
@@ -695,7 +707,7 @@ hipError_t launch_kv_final(const KVFinalArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_mtp_prep(const MtpPrepArgs& a, hipStream_t st) {
-    if (a.HD > 256) return hipErrorInvalidValue;
+    if (a.HD > 256 || a.S < 1 || (a.S > 1 && a.slab < 1)) return hipErrorInvalidValue;
     mtp_prep_kernel<<<dim3(a.M, a.NH + 2 * a.NKV), 256, 0, st>>>(a);
     return hipGetLastError();
 }
